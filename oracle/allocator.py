@@ -1,0 +1,187 @@
+"""Oracle for the host block allocator (test infrastructure only).
+
+Policy, and where the pages fix it:
+
+* The pool starts as a queue of free block ids (0..NB-1, or a given
+  permutation).  Allocation takes the head of the queue ("PagedAttention
+  源码解析：KV Cache 怎么管理" §二/§三: `free_blocks.pop(0)`; its worked example
+  gives requests of 32, 16 and 48 tokens the blocks [0,1], [2], [3,4,5] and
+  leaves [6,7,8,...] free, which only first-in-first-out order produces).
+* A sequence of n tokens holds ceil(n / bs) blocks (same page §三; "Ascend C
+  算子开发高阶实战…" §1.2: 45 tokens -> 3 blocks, 100 -> 7).
+* Every block carries a reference count: 1 when allocated, +1 per extra
+  sharer, -1 when a sharer lets go; at 0 it returns to the tail of the free
+  queue (xdnf.cn PagedAttention article §3.4 and its §4.2 PhysicalBlockPool;
+  "PagedAttention 实现细节" §3.3).  A freed sequence releases its blocks in
+  block-table order.
+* Appending a token at position L (xdnf.cn article §4.2 append_token_kv):
+  if L % bs == 0 a fresh block is appended to the table; otherwise the token
+  goes to the last block at offset L % bs.  Copy-on-write is decided before
+  the write (xdnf.cn article §3.4; "PagedAttention 实现细节" §3.3): a last
+  block with refcount > 1 is replaced by a fresh block, the pair (old, new) is
+  emitted for a whole-block copy, the old count drops by one and the new one
+  is 1; a block with refcount 1 is written in place.  The slot is
+  table[L // bs] * bs + L % bs (xdnf.cn article §3.1 addressing).
+* Fork (parallel sampling, beam search: xdnf.cn article §3.4) gives the child
+  the parent's first ceil(n / bs) blocks and adds one reference to each.
+* Running out of blocks is an error that leaves the state unchanged
+  ("PagedAttention 源码解析…" §三 raises, xdnf.cn §4.2 asserts, "PagedAttention
+  实现细节" §3.3 fails the copy-on-write).
+* A batch of appends is processed in the order given, and all-or-nothing.
+"""
+from __future__ import annotations
+
+import copy
+from collections import deque
+
+
+class AllocatorError(Exception):
+    def __init__(self, code: str, msg: str = ""):
+        super().__init__(f"{code}: {msg}" if msg else code)
+        self.code = code
+
+
+NO_FREE_BLOCKS = "NO_FREE_BLOCKS"
+UNKNOWN_SEQ = "UNKNOWN_SEQ"
+SEQ_EXISTS = "SEQ_EXISTS"
+INVALID_ARG = "INVALID_ARG"
+
+
+class BlockAllocator:
+    def __init__(self, num_blocks: int, block_size: int, initial_free_order=None):
+        if num_blocks < 0 or block_size <= 0:
+            raise AllocatorError(INVALID_ARG, "num_blocks >= 0 and block_size > 0")
+        order = list(range(num_blocks)) if initial_free_order is None else [int(b) for b in initial_free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise AllocatorError(INVALID_ARG, "initial free order must be a permutation of 0..NB-1")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.free = deque(order)
+        self.refs = [0] * num_blocks
+        self.tables: dict[int, list[int]] = {}
+        self.lens: dict[int, int] = {}
+        self.stats = {"blocks_allocated": 0, "blocks_freed": 0, "cow_copies": 0}
+
+    # -- helpers -------------------------------------------------------------
+    def _blocks_for(self, n: int) -> int:
+        return (n + self.block_size - 1) // self.block_size
+
+    def _take(self) -> int:
+        if not self.free:
+            raise AllocatorError(NO_FREE_BLOCKS)
+        b = self.free.popleft()
+        self.refs[b] = 1
+        self.stats["blocks_allocated"] += 1
+        return b
+
+    def _release(self, b: int):
+        self.refs[b] -= 1
+        if self.refs[b] == 0:
+            self.free.append(b)
+            self.stats["blocks_freed"] += 1
+
+    def _need(self, seq_id: int):
+        if seq_id not in self.tables:
+            raise AllocatorError(UNKNOWN_SEQ, str(seq_id))
+
+    # -- public verbs ----------------------------------------------------------
+    def clone(self) -> "BlockAllocator":
+        return copy.deepcopy(self)
+
+    def seq_create(self, seq_id: int, num_tokens: int):
+        if seq_id in self.tables:
+            raise AllocatorError(SEQ_EXISTS, str(seq_id))
+        if num_tokens < 0:
+            raise AllocatorError(INVALID_ARG, "num_tokens < 0")
+        nb = self._blocks_for(num_tokens)
+        if nb > len(self.free):
+            raise AllocatorError(NO_FREE_BLOCKS)
+        self.tables[seq_id] = [self._take() for _ in range(nb)]
+        self.lens[seq_id] = num_tokens
+
+    def seq_fork(self, parent: int, child: int, num_tokens: int = -1):
+        self._need(parent)
+        if child in self.tables:
+            raise AllocatorError(SEQ_EXISTS, str(child))
+        n = self.lens[parent] if num_tokens < 0 else num_tokens
+        if n > self.lens[parent]:
+            raise AllocatorError(INVALID_ARG, "fork length beyond the parent")
+        shared = self.tables[parent][: self._blocks_for(n)]
+        for b in shared:
+            self.refs[b] += 1
+        self.tables[child] = list(shared)
+        self.lens[child] = n
+
+    def seq_append_slot(self, seq_id: int):
+        """Reserve the slot of the next token; returns (slot, cow_src, cow_dst), -1s when no copy."""
+        self._need(seq_id)
+        table = self.tables[seq_id]
+        L = self.lens[seq_id]
+        src = dst = -1
+        if L % self.block_size == 0:
+            table.append(self._take())
+        else:
+            last = table[L // self.block_size]
+            if self.refs[last] > 1:
+                new = self._take()
+                self.refs[last] -= 1
+                table[L // self.block_size] = new
+                src, dst = last, new
+                self.stats["cow_copies"] += 1
+        slot = table[L // self.block_size] * self.block_size + L % self.block_size
+        self.lens[seq_id] = L + 1
+        return slot, src, dst
+
+    def seq_append_slots(self, seq_ids):
+        """Append one token to each sequence, in order.  Returns (slots, pairs).  All-or-nothing."""
+        saved = copy.deepcopy((self.free, self.refs, self.tables, self.lens, self.stats))
+        try:
+            slots, pairs = [], []
+            for s in seq_ids:
+                slot, src, dst = self.seq_append_slot(s)
+                slots.append(slot)
+                if src >= 0:
+                    pairs.append((src, dst))
+            return slots, pairs
+        except AllocatorError:
+            self.free, self.refs, self.tables, self.lens, self.stats = saved
+            raise
+
+    def seq_free(self, seq_id: int):
+        self._need(seq_id)
+        for b in self.tables[seq_id]:
+            self._release(b)
+        del self.tables[seq_id]
+        del self.lens[seq_id]
+
+    def can_allocate(self, num_blocks: int) -> bool:
+        return num_blocks <= len(self.free)
+
+    def num_free_blocks(self) -> int:
+        return len(self.free)
+
+    def ref_count(self, block: int) -> int:
+        return self.refs[block] if 0 <= block < self.num_blocks else -1
+
+    def seq_len(self, seq_id: int) -> int:
+        self._need(seq_id)
+        return self.lens[seq_id]
+
+    def block_table(self, seq_id: int) -> list:
+        self._need(seq_id)
+        return list(self.tables[seq_id])
+
+    def free_list(self) -> list:
+        return list(self.free)
+
+    def build_block_tables(self, seq_ids, max_blocks: int):
+        """Rows of physical block ids, padded with -1 to `max_blocks`, and the context lengths."""
+        tables, lens = [], []
+        for s in seq_ids:
+            self._need(s)
+            t = self.tables[s]
+            if len(t) > max_blocks:
+                raise AllocatorError(INVALID_ARG, "block table longer than max_blocks")
+            tables.append(t + [-1] * (max_blocks - len(t)))
+            lens.append(self.lens[s])
+        return tables, lens

@@ -1,0 +1,188 @@
+"""Oracle for paged decode attention, in float64 (test infrastructure only).
+
+What is computed, and where the pages define it:
+
+* Gather, then attend.  "PagedAttention 实现细节" §3.1 first collects a
+  sequence's K/V rows from its physical blocks (block `table[j]` holds logical
+  tokens j*bs .. j*bs+bs-1; only the first `n` tokens are valid) into a
+  contiguous tensor, then runs exactly the same math as a contiguous cache.
+* The math is single-query scaled-dot-product attention,
+  out = softmax(scale * K q) V, with scale = 1/sqrt(head_dim): "PagedAttention
+  源码解析：KV Cache 怎么管理" §四 (standard_attention), "Ascend C算子开发高阶实战…"
+  §1.3, "PagedAttention 实现细节" §3.1.  The pages' own per-block and online
+  loops are not followed where they differ from this definition (one page
+  normalises each block separately, another never rescales its accumulator);
+  the oracle is the definition they all aim at.
+* Pool layout [num_blocks, num_kv_heads, block_size, head_dim] for each of K
+  and V ("PagedAttention 实现细节" §3.1 index-based kernel signature, §3.4
+  PagedAttention.forward).
+* Query heads share KV heads in contiguous groups: query head h reads KV head
+  h // (num_heads // num_kv_heads).  The pages name grouped-query attention
+  only as future work ("Ascend C算子开发高阶实战…" §十); contiguous grouping is
+  the plain reading.
+* Split partials and merge: the pages only say a second kernel exists for few,
+  very long sequences ("Ascend平台下的PageAttention优化实践" §2.3).  The oracle
+  cuts the context into partitions of `partition_size` tokens, keeps
+  (m_p = max logit, l_p = sum exp(z - m_p), o_p = normalised partial output)
+  per partition, and merges with the log-sum-exp rule.
+
+Inputs are NumPy arrays in storage type: float32, float16, or bf16 given as
+uint16 bit patterns.  Everything is upcast exactly to float64; the scale is
+taken as the float32 value the kernels receive.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def to_f64(x, dtype: str) -> np.ndarray:
+    """Exact upcast of a storage array to float64 (bf16: bits << 16 -> float32)."""
+    x = np.asarray(x)
+    if dtype == "bf16":
+        bits = x.astype(np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    if dtype in ("f32", "f16"):
+        return x.astype(np.float64)
+    raise ValueError(dtype)
+
+
+def scale_f64(scale: float) -> float:
+    """The float32 value of `scale`, as float64."""
+    return float(np.float32(scale))
+
+
+def blocks_for(num_tokens: int, block_size: int) -> int:
+    """Blocks a sequence of `num_tokens` occupies: ceil(n / bs)."""
+    return (num_tokens + block_size - 1) // block_size
+
+
+def gather_kv(key_cache, value_cache, table_row, num_tokens: int, kv_head: int, dtype: str):
+    """Collect the first `num_tokens` K and V rows of one sequence and KV head.
+
+    Logical block j of the sequence lives in physical block table_row[j]; its
+    rows are tokens j*bs .. j*bs + bs - 1, of which only those below
+    `num_tokens` are valid ("PagedAttention 实现细节" §3.1, the gather step).
+    Returns float64 arrays K, V of shape [num_tokens, head_dim].
+    """
+    num_blocks, _, block_size, head_dim = key_cache.shape
+    ks, vs = [], []
+    for j in range(blocks_for(num_tokens, block_size)):
+        phys = int(table_row[j])
+        if not 0 <= phys < num_blocks:
+            raise IndexError(f"block table entry {phys} outside the pool of {num_blocks}")
+        valid = min(block_size, num_tokens - j * block_size)
+        ks.append(to_f64(key_cache[phys, kv_head, :valid, :], dtype))
+        vs.append(to_f64(value_cache[phys, kv_head, :valid, :], dtype))
+    if not ks:
+        empty = np.zeros((0, head_dim), dtype=np.float64)
+        return empty, empty.copy()
+    return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
+
+
+def logits(q64: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:
+    """z_t = scale * <q, K_t> for every cached token t."""
+    return scale * (K @ q64)
+
+
+def softmax_weights(z: np.ndarray) -> np.ndarray:
+    """p_t = exp(z_t - max z) / sum_u exp(z_u - max z)."""
+    e = np.exp(z - np.max(z))
+    return e / np.sum(e)
+
+
+def attend(q64: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """Standard single-query attention softmax(scale*K q)^T V.  No tokens -> zeros."""
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[1], dtype=np.float64)
+    return softmax_weights(logits(q64, K, scale)) @ V
+
+
+def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scale: float,
+                 dtype: str) -> np.ndarray:
+    """out[s, h] = attention of query[s, h] over the first context_lens[s] tokens of
+    sequence s, gathered through block_tables[s] from the KV head h // G.
+
+    query [S, H, D]; key_cache, value_cache [NB, H_kv, bs, D]; block_tables [S, MB];
+    context_lens [S].  Returns float64 [S, H, D].
+    """
+    S, H, D = query.shape
+    H_kv = key_cache.shape[1]
+    if H % H_kv:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    G = H // H_kv
+    sig = scale_f64(scale)
+    out = np.zeros((S, H, D), dtype=np.float64)
+    for s in range(S):
+        n = int(context_lens[s])
+        for g in range(H_kv):
+            K, V = gather_kv(key_cache, value_cache, block_tables[s], n, g, dtype)
+            for h in range(g * G, (g + 1) * G):
+                out[s, h] = attend(to_f64(query[s, h], dtype), K, V, sig)
+    return out
+
+
+def decode_one(query, key_cache, value_cache, table_row, num_tokens: int, head: int,
+               num_heads: int, scale: float, dtype: str) -> np.ndarray:
+    """One output row out[s, head] (query = query[s], table_row = block_tables[s])."""
+    H_kv = key_cache.shape[1]
+    g = head // (num_heads // H_kv)
+    K, V = gather_kv(key_cache, value_cache, table_row, num_tokens, g, dtype)
+    return attend(to_f64(query[head], dtype), K, V, scale_f64(scale))
+
+
+# ----------------------------------------------------------------------------
+# split-context partials and their merge
+
+
+def partition_partials(q64: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+                       partition_size: int):
+    """Per partition p = tokens [p*PS, min((p+1)*PS, n)):
+    m_p = max z, l_p = sum exp(z - m_p), o_p = sum exp(z - m_p) V / l_p.
+    Returns float64 arrays m [P], l [P], o [P, D] with P = ceil(n / PS).
+    """
+    n = K.shape[0]
+    P = (n + partition_size - 1) // partition_size
+    D = V.shape[1]
+    m = np.zeros(P)
+    l = np.zeros(P)
+    o = np.zeros((P, D))
+    for p in range(P):
+        lo, hi = p * partition_size, min((p + 1) * partition_size, n)
+        z = logits(q64, K[lo:hi], scale)
+        m[p] = np.max(z)
+        e = np.exp(z - m[p])
+        l[p] = np.sum(e)
+        o[p] = (e @ V[lo:hi]) / l[p]
+    return m, l, o
+
+
+def lse_merge(m: np.ndarray, l: np.ndarray, o: np.ndarray) -> np.ndarray:
+    """Merge partition partials: M = max m_p, w_p = l_p exp(m_p - M),
+    out = sum_p w_p o_p / sum_p w_p.  No partitions -> zeros."""
+    if m.shape[0] == 0:
+        return np.zeros(o.shape[1], dtype=np.float64)
+    M = np.max(m)
+    w = l * np.exp(m - M)
+    return (w @ o) / np.sum(w)
+
+
+def split_decode_partials(query, key_cache, value_cache, block_tables, context_lens, scale: float,
+                          dtype: str, partition_size: int, seqs=None, heads=None):
+    """Partials (m, l, o) for every (seq, head) in `seqs` x `heads`: a dict keyed by (s, h)."""
+    S, H, D = query.shape
+    H_kv = key_cache.shape[1]
+    G = H // H_kv
+    sig = scale_f64(scale)
+    seqs = range(S) if seqs is None else seqs
+    heads = range(H) if heads is None else heads
+    res = {}
+    for s in seqs:
+        n = int(context_lens[s])
+        cache = {}
+        for h in heads:
+            g = h // G
+            if g not in cache:
+                cache[g] = gather_kv(key_cache, value_cache, block_tables[s], n, g, dtype)
+            K, V = cache[g]
+            res[(s, h)] = partition_partials(to_f64(query[s, h], dtype), K, V, sig, partition_size)
+    return res

@@ -1,0 +1,43 @@
+"""Oracle for the two pool-writing operations (test infrastructure only).
+
+* Slot-mapping write: token i's new K/V rows go to slot = slot_mapping[i],
+  i.e. physical block slot // bs at offset slot % bs ("Ascend C算子开发高阶实战…"
+  §3.1 params: slot_mapping maps a token to (block id, offset in block);
+  "PagedAttention 实现细节" §3.4, writing the new KV into its block after each
+  step).  A negative slot means "no write" (the pages are silent; plain
+  reading: padding tokens are skipped).
+* Block copy for copy-on-write: the whole source block, K and V, every KV head,
+  every row, is copied to the destination block ("PagedAttention 实现细节"
+  §3.3: copy the full contents of the original block to the new one).  Pairs
+  are applied in list order.
+
+Arrays are NumPy storage arrays (bf16 as uint16 bits), so the results are
+bit patterns and compare bit-exactly.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping):
+    """Return copies of the pools with key[i], value[i] ([H_kv, D]) written at slot_mapping[i]."""
+    kc = np.array(key_cache, copy=True)
+    vc = np.array(value_cache, copy=True)
+    block_size = kc.shape[2]
+    for i, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        if slot < 0:
+            continue
+        block, offset = divmod(int(slot), block_size)
+        kc[block, :, offset, :] = key[i]
+        vc[block, :, offset, :] = value[i]
+    return kc, vc
+
+
+def copy_blocks(key_cache, value_cache, pairs):
+    """Return copies of the pools after copying block src -> dst for each (src, dst) pair."""
+    kc = np.array(key_cache, copy=True)
+    vc = np.array(value_cache, copy=True)
+    for src, dst in np.asarray(pairs).reshape(-1, 2).tolist():
+        kc[dst] = kc[src]
+        vc[dst] = vc[src]
+    return kc, vc

@@ -1,0 +1,40 @@
+"""CPU pins of the pool-writing oracles: slot-mapping scatter and whole-block copy."""
+import numpy as np
+
+from oracle import cache_ops as C
+from tests import oracle_pins as P
+
+
+def test_reshape_hand_example():
+    # pool of 4 blocks x 2 KV heads x 4 rows x 2 dims, zeros; three new tokens
+    kc = np.zeros((4, 2, 4, 2), dtype=np.float32)
+    vc = np.zeros((4, 2, 4, 2), dtype=np.float32)
+    key = np.arange(12, dtype=np.float32).reshape(3, 2, 2) + 1
+    val = -key
+    kc2, vc2 = C.reshape_and_cache(key, val, kc, vc, [5, -1, 14])
+    exp_k = np.zeros_like(kc)
+    exp_k[1, :, 1, :] = key[0]     # slot 5 = block 1, offset 1
+    exp_k[3, :, 2, :] = key[2]     # slot 14 = block 3, offset 2; slot -1 skipped
+    assert np.array_equal(kc2, exp_k)
+    assert np.array_equal(vc2, -exp_k)
+    assert np.array_equal(kc, np.zeros_like(kc))  # inputs untouched
+
+
+def test_reshape_keeps_bf16_bits():
+    kc = np.zeros((2, 1, 16, 4), dtype=np.uint16)
+    key = np.array([[[0x7FC1, 0x0001, 0x8000, 0xFFFF]]], dtype=np.uint16)
+    kc2, _ = C.reshape_and_cache(key, key, kc, kc, [17])
+    assert np.array_equal(kc2[1, 0, 1], key[0, 0])
+
+
+def test_copy_blocks_hand_example():
+    kc = np.arange(4 * 2 * 2 * 2, dtype=np.float32).reshape(4, 2, 2, 2)
+    vc = -kc
+    kc2, vc2 = C.copy_blocks(kc, vc, [[0, 2], [1, 3]])
+    assert np.array_equal(kc2[2], kc[0]) and np.array_equal(kc2[3], kc[1])
+    assert np.array_equal(kc2[:2], kc[:2])
+    assert np.array_equal(vc2[2], vc[0]) and np.array_equal(vc2[3], vc[1])
+
+
+def test_cow_timeline_from_impl_page():
+    P.check_p4_cow_timeline()

@@ -1,0 +1,161 @@
+"""Planted mistakes in the oracle (on the CPU): each must be caught by a pin.
+
+Each case patches one piece of the oracle with a plausible error and checks
+that at least one of the pins in tests/oracle_pins.py then fails.
+"""
+import numpy as np
+import pytest
+
+from oracle import allocator as AL
+from oracle import attention as A
+from tests import oracle_pins as P
+
+
+def _softmax_no_shift_wrong_sign(z):
+    e = np.exp(-(z - np.max(z)))
+    return e / np.sum(e)
+
+
+def _softmax_unnormalised(z):
+    return np.exp(z - np.max(z))
+
+
+def _logits_no_scale(q64, K, scale):
+    return K @ q64
+
+
+def _logits_sqrt_scale(q64, K, scale):
+    return np.sqrt(scale) * (K @ q64)
+
+
+def _gather_drop_last_row(kc, vc, row, n, g, dtype, _orig=A.gather_kv):
+    K, V = _orig(kc, vc, row, n, g, dtype)
+    return (K[:-1], V[:-1]) if n > 1 else (K, V)
+
+
+def _gather_transposed_block(kc, vc, row, n, g, dtype, _orig=A.gather_kv):
+    # reads row t of a block from the wrong KV head when there is more than one
+    H_kv = kc.shape[1]
+    return _orig(kc, vc, row, n, (g + 1) % H_kv, dtype)
+
+
+def _merge_no_rescale(m, l, o, _orig=A.lse_merge):
+    return (l @ o) / np.sum(l)
+
+
+def _partials_unnormalised(q64, K, V, scale, ps, _orig=A.partition_partials):
+    m, l, o = _orig(q64, K, V, scale, ps)
+    return m, l, o * l[:, None]
+
+
+def _per_block_softmax_decode(query, kc, vc, tables, ctx, scale, dtype):
+    # one page's loop: a softmax per block, block outputs summed
+    S, H, D = query.shape
+    H_kv, bs = kc.shape[1], kc.shape[2]
+    G = H // H_kv
+    out = np.zeros((S, H, D))
+    for s in range(S):
+        n = int(ctx[s])
+        for h in range(H):
+            K, V = A.gather_kv(kc, vc, tables[s], n, h // G, dtype)
+            q = A.to_f64(query[s, h], dtype)
+            for j in range(0, n, bs):
+                out[s, h] += A.softmax_weights(A.scale_f64(scale) * (K[j:j + bs] @ q)) @ V[j:j + bs]
+    return out
+
+
+ATTENTION_MUTANTS = [
+    ("softmax_weights", _softmax_no_shift_wrong_sign),
+    ("softmax_weights", _softmax_unnormalised),
+    ("logits", _logits_no_scale),
+    ("logits", _logits_sqrt_scale),
+    ("gather_kv", _gather_drop_last_row),
+    ("gather_kv", _gather_transposed_block),
+    ("paged_decode", _per_block_softmax_decode),
+]
+
+ATTENTION_PINS = [
+    lambda: P.check_against_sdpa(),
+    lambda: P.check_against_sdpa(seed=5, S=2, H=8, Hkv=2, D=64, bs=16, ctx=(40, 70), dtype="f16"),
+    P.check_brute_force, P.check_two_token_closed_form, P.check_identical_keys_mean,
+    P.check_ctx1_is_v0, P.check_dominant_key, P.check_split_merge, P.check_p4_gather_demo,
+]
+
+
+def _caught(pins):
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("name,bad", ATTENTION_MUTANTS, ids=[f"{n}:{b.__name__}" for n, b in ATTENTION_MUTANTS])
+def test_attention_mutant_is_caught(monkeypatch, name, bad):
+    monkeypatch.setattr(A, name, bad)
+    assert _caught(ATTENTION_PINS), f"no pin caught the planted mistake in {name}"
+
+
+@pytest.mark.parametrize("name,bad", [("lse_merge", _merge_no_rescale),
+                                      ("partition_partials", _partials_unnormalised)])
+def test_split_mutant_is_caught(monkeypatch, name, bad):
+    monkeypatch.setattr(A, name, bad)
+    assert _caught([P.check_split_merge])
+
+
+class _LifoAllocator(AL.BlockAllocator):
+    def _take(self):
+        if not self.free:
+            raise AL.AllocatorError(AL.NO_FREE_BLOCKS)
+        b = self.free.pop()
+        self.refs[b] = 1
+        return b
+
+
+class _FreeToHeadAllocator(AL.BlockAllocator):
+    def _release(self, b):
+        self.refs[b] -= 1
+        if self.refs[b] == 0:
+            self.free.appendleft(b)
+
+
+class _CowNoDecrement(AL.BlockAllocator):
+    def seq_append_slot(self, seq_id):
+        L = self.lens[seq_id]
+        t = self.tables[seq_id]
+        if L % self.block_size and self.refs[t[L // self.block_size]] > 1:
+            self.refs[t[L // self.block_size]] += 1   # wrong: should drop by one after the copy
+            self.refs[t[L // self.block_size]] -= 1
+            old = t[L // self.block_size]
+            new = self._take()
+            t[L // self.block_size] = new
+            self.lens[seq_id] = L + 1
+            return new * self.block_size + L % self.block_size, old, new
+        return super().seq_append_slot(seq_id)
+
+
+class _CowInPlace(AL.BlockAllocator):
+    def seq_append_slot(self, seq_id):
+        L = self.lens[seq_id]
+        if L % self.block_size:
+            t = self.tables[seq_id]
+            self.lens[seq_id] = L + 1
+            return t[L // self.block_size] * self.block_size + L % self.block_size, -1, -1
+        return super().seq_append_slot(seq_id)
+
+
+class _CeilOffByOne(AL.BlockAllocator):
+    def _blocks_for(self, n):
+        return n // self.block_size + 1
+
+
+ALLOCATOR_PINS = [P.check_p1_block_mapping, P.check_block_counts, P.check_addressing,
+                  P.check_p4_cow_timeline, P.check_p2_lifecycle]
+
+
+@pytest.mark.parametrize("cls", [_LifoAllocator, _FreeToHeadAllocator, _CowNoDecrement, _CowInPlace,
+                                 _CeilOffByOne])
+def test_allocator_mutant_is_caught(monkeypatch, cls):
+    monkeypatch.setattr(AL, "BlockAllocator", cls)
+    assert _caught(ALLOCATOR_PINS), f"no pin caught {cls.__name__}"
