@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark for paged attention on one MI355X.
+
+One step = the whole hot path over one batch:
+  host allocator bookkeeping for one new token per sequence (slots, copy-on-write
+  pairs, block tables), the table/slot uploads, pa_copy_blocks (when pairs exist),
+  pa_reshape_and_cache of the new K/V, and the decode over every cached token
+  (pa_decode, or pa_decode_split + its LSE merge).
+
+Default workload: 64 sequences, 32 query / 32 KV heads of dimension 128, fp16,
+block size 16, contexts uniform in [256, 2048] (a LLaMA-7B-like layer), pool of
+8192 blocks in shuffled order.  Inputs are synthetic (seeded normals) and
+resident in HBM before the timed region.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload 1..5] [--path single|split]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_333_amd", "csrc", "decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--path", choices=["single", "split"], default=None,
+                    help="decode path (default: split for workload 4, single otherwise)")
+    ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for name in ("decode.hip", "device_common.hpp"):
+        with open(os.path.join(ROOT, "paged_kv_cache_333_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: int, path: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it was taken
+    on the current decode kernel source for this workload and path; else None."""
+    try:
+        with open(TRAFFIC_FILE, encoding="utf-8") as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(f"workload{workload}-{path}")
+    if not entry or entry.get("source_digest") != source_digest():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+class Bench:
+    def __init__(self, args):
+        import numpy as np
+        import torch
+
+        import paged_kv_cache_333_amd as pa
+        import synth
+
+        self.np, self.torch, self.pa, self.synth = np, torch, pa, synth
+        self.args = args
+        self.w = w = synth.workload(args.workload)
+        self.path = args.path or ("split" if args.workload == 4 else "single")
+        self.dev = torch.device("cuda:0")
+        self.stream = torch.cuda.current_stream()
+        seeds = synth.tensor_seeds(args.workload)
+        S, H, Hkv, D, bs = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size
+        total_steps = args.warmup + args.steps
+
+        # host allocator state (product path: the C++ allocator)
+        self.alloc = pa.Allocator(w.num_blocks, bs, w.free_order)
+        if args.workload == 5:
+            for g in range(w.groups):
+                parent = 10_000 + g
+                self.alloc.seq_create(parent, w.parent_len)
+                for b in range(w.branches):
+                    s = g * w.branches + b
+                    self.alloc.seq_fork(parent, s, w.context_lens[s])
+                self.alloc.seq_free(parent)
+            self.base = self.alloc.clone()  # every step starts from the post-fork state
+            growth = 1
+        else:
+            for s, n in enumerate(w.context_lens):
+                self.alloc.seq_create(s, n)
+            self.base = None
+            growth = total_steps
+        self.max_blocks = -(-(max(w.context_lens) + growth) // bs) + 1
+        self.max_ctx = self.max_blocks * bs
+
+        # device data, resident before timing
+        pool = (w.num_blocks, Hkv, bs, D)
+        self.kc = synth.normal_device(pool, seeds["key_cache"], w.dtype)
+        self.vc = synth.normal_device(pool, seeds["value_cache"], w.dtype)
+        self.q = synth.normal_device((S, H, D), seeds["query"], w.dtype)
+        R = 8  # distinct new-token K/V batches, cycled
+        self.newk = synth.normal_device((R, S, Hkv, D), seeds["new_key"], w.dtype)
+        self.newv = synth.normal_device((R, S, Hkv, D), seeds["new_value"], w.dtype)
+        self.out = torch.empty_like(self.q)
+        if self.path == "split":
+            nbytes = pa.pa_decode_split_workspace_bytes(S, H, D, self.max_ctx, args.partition)
+            self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.dev)
+
+        # double-buffered pinned staging and device index buffers
+        self.ids = torch.arange(S, dtype=torch.int64).pin_memory()
+        self.bufs = []
+        for _ in range(2):
+            b = {
+                "slots_h": torch.empty(S, dtype=torch.int32).pin_memory(),
+                "pairs_h": torch.empty((S, 2), dtype=torch.int32).pin_memory(),
+                "tab_h": torch.empty((S, self.max_blocks), dtype=torch.int32).pin_memory(),
+                "len_h": torch.empty(S, dtype=torch.int32).pin_memory(),
+                "slots_d": torch.empty(S, dtype=torch.int32, device=self.dev),
+                "pairs_d": torch.empty((S, 2), dtype=torch.int32, device=self.dev),
+                "tab_d": torch.empty((S, self.max_blocks), dtype=torch.int32, device=self.dev),
+                "len_d": torch.empty(S, dtype=torch.int32, device=self.dev),
+                "staged": torch.cuda.Event(),
+            }
+            b["staged"].record(self.stream)
+            self.bufs.append(b)
+        self.elem = synth.ELEM_BYTES[w.dtype]
+        torch.cuda.synchronize()
+
+    def step(self, k: int, timing: list | None):
+        pa, w = self.pa, self.w
+        b = self.bufs[k % 2]
+        b["staged"].synchronize()  # the uploads that last read this staging buffer are done
+        alloc = self.alloc
+        if self.base is not None:
+            alloc = self.alloc = self.base.clone()
+        S = w.num_seqs
+        npairs = alloc.seq_append_slots_into(self.ids.data_ptr(), S, b["slots_h"].data_ptr(), b["pairs_h"].data_ptr())
+        alloc.build_block_tables_into(self.ids.data_ptr(), S, self.max_blocks, b["tab_h"].data_ptr(),
+                                      b["len_h"].data_ptr())
+        b["slots_d"].copy_(b["slots_h"], non_blocking=True)
+        b["tab_d"].copy_(b["tab_h"], non_blocking=True)
+        b["len_d"].copy_(b["len_h"], non_blocking=True)
+        if npairs:
+            b["pairs_d"][:npairs].copy_(b["pairs_h"][:npairs], non_blocking=True)
+        b["staged"].record(self.stream)
+        if npairs:
+            pa.pa_copy_blocks(self.kc, self.vc, b["pairs_d"], num_pairs=npairs)
+        r = k % self.newk.shape[0]
+        pa.pa_reshape_and_cache(self.newk[r], self.newv[r], self.kc, self.vc, b["slots_d"])
+        if timing is not None:
+            e0, e1 = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+        if self.path == "single":
+            pa.pa_decode(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"], self.max_ctx, w.scale)
+        else:
+            pa.pa_decode_split(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"], self.max_ctx, w.scale,
+                               self.args.partition, self.ws)
+        if timing is not None:
+            e1.record(self.stream)
+            lens = b["len_h"].numpy()
+            timing.append((e0, e1, int(lens.sum()), int(((lens + w.block_size - 1) // w.block_size).sum()), npairs))
+
+    def run(self):
+        torch = self.torch
+        a = self.args
+        for k in range(a.warmup):
+            self.step(k, None)
+        torch.cuda.synchronize()
+        timing = []
+        t0 = time.perf_counter()
+        for k in range(a.warmup, a.warmup + a.steps):
+            self.step(k, timing)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall, timing
+
+    def cpu_baseline(self, min_seconds: float):
+        """The float64 oracle on the final step's inputs (all sequences, all heads), repeated
+        whole until min_seconds have passed; single-threaded BLAS."""
+        import numpy as np
+        from threadpoolctl import threadpool_limits
+
+        from oracle import attention as A
+        torch, synth, w = self.torch, self.synth, self.w
+        b = self.bufs[(self.args.warmup + self.args.steps - 1) % 2]
+        lens = b["len_h"].numpy().copy()
+        tabs = b["tab_h"].numpy().copy()
+        # copy just the used blocks back, renumbered 0..n-1 (a plain re-indexing of the inputs)
+        used = np.unique(tabs[tabs >= 0])
+        remap = -np.ones(w.num_blocks, dtype=np.int32)
+        remap[used] = np.arange(len(used), dtype=np.int32)
+        idx = torch.from_numpy(used.astype(np.int64)).to(self.dev)
+        kc = synth.to_numpy(self.kc.index_select(0, idx), w.dtype)
+        vc = synth.to_numpy(self.vc.index_select(0, idx), w.dtype)
+        q = synth.to_numpy(self.q, w.dtype)
+        t2 = np.where(tabs >= 0, remap[np.maximum(tabs, 0)], -1)
+        passes, tokens = 0, 0
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            while True:
+                A.paged_decode(q, kc, vc, t2, lens, w.scale, w.dtype)
+                passes += 1
+                tokens += int(lens.sum())
+                el = time.perf_counter() - t0
+                if el >= min_seconds:
+                    break
+        return {"value": tokens / el, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"float64 NumPy oracle, whole decode step ({w.num_seqs} seqs x {w.num_heads} heads, "
+                          f"{int(lens.sum())} KV tokens) repeated {passes}x in {el:.1f} s, 1 BLAS thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path shards by "
+              "sequence or KV head with no exchange; this build runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    bench = Bench(args)
+    wall, timing = bench.run()
+    w = bench.w
+    e = bench.elem
+    durs = [a.elapsed_time(b) * 1e-3 for a, b, *_ in timing]  # seconds
+    kv_tokens = sum(t[2] for t in timing)
+    kv_bytes_token = 2 * w.num_kv_heads * w.head_dim * e
+    qo_bytes = 2 * w.num_seqs * w.num_heads * w.head_dim * e
+    alg_bytes = [t[2] * kv_bytes_token + qo_bytes + 4 * t[3] + 4 * w.num_seqs for t in timing]
+    avg_dur = sum(durs) / len(durs)
+    avg_bytes = sum(alg_bytes) / len(alg_bytes)
+    achieved = avg_bytes / avg_dur / 1e9
+    traffic = measured_traffic(args.workload, bench.path)
+    res = {
+        "metric": "paged decode attention: KV GB/s achieved (% of HBM peak) and KV tokens/s",
+        "value": kv_tokens / wall,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "context_lens": "per workload definition, +1 token per step",
+                   "mean_kv_tokens_per_step": kv_tokens / len(timing), "decode_path": bench.path,
+                   "partition_size": args.partition if bench.path == "split" else None,
+                   "cow_pairs_per_step": sum(t[4] for t in timing) / len(timing)},
+        "decode_kernel_us": avg_dur * 1e6,
+        "kv_gbps_step": kv_tokens * kv_bytes_token / wall / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = bench.cpu_baseline(args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,255 @@
+/*
+ * pa.h — PagedAttention decode for AMD Instinct MI355X (gfx950): the C ABI.
+ *
+ * One shared library, libpa.so, exports everything declared here.  All calls
+ * are extern "C", take plain host or device pointers and sizes, never throw
+ * across the boundary, and report failure through pa_status.
+ *
+ * Sources (the pages this library implements):
+ *   [SRC-1] "PagedAttention 源码解析：KV Cache 怎么管理" (coreui.cn)
+ *   [XDNF]  xdnf.cn article on PagedAttention block mapping, dynamic allocation
+ *           and copy-on-write
+ *   [ASC]   "Ascend C算子开发高阶实战：实现高性能KV Cache管理与PagedAttention融合算子"
+ *           (cann.csdn.net)
+ *   [IMPL]  "PagedAttention 实现细节" (pyllm.pages.dev)
+ *   [ATB]   "Ascend平台下的PageAttention优化实践" (jsqmd.com)
+ *
+ * Data layout (device memory, all row-major, all owned by the caller):
+ *   query, out      [num_seqs, num_heads, head_dim]               element type `dtype`
+ *   key_cache,
+ *   value_cache     [num_blocks, num_kv_heads, block_size, head_dim]  element type `dtype`
+ *                   (the separate K and V pools of [IMPL] §3.1/§3.4; one
+ *                   (block, kv head) tile is contiguous, one token row is
+ *                   head_dim contiguous elements)
+ *   block_tables    [num_seqs, max_blocks_per_seq] int32; entry j of row s is
+ *                   the physical block of logical block j (tokens j*bs ..
+ *                   j*bs+bs-1) of sequence s; unused entries are -1 by
+ *                   convention and never read
+ *   context_lens    [num_seqs] int32, the number of cached tokens of each sequence
+ *   slot_mapping    [num_tokens] int32, slot = block * block_size + offset
+ *
+ * Query head h reads KV head h / (num_heads / num_kv_heads) (contiguous
+ * groups; num_heads must be a multiple of num_kv_heads).
+ *
+ * Supported shapes: dtype f32, f16, bf16; head_dim 64 or 128; block_size 16
+ * or 32.  Other values return PA_ERR_UNSUPPORTED.
+ *
+ * Streams: device calls enqueue work on `stream` (a hipStream_t; NULL is the
+ * null stream) and return without synchronising.  The library allocates no
+ * device memory; the split path's workspace is passed in by the caller.
+ *
+ * Debug mode: with the environment variable PA_DEBUG=1 set when the library
+ * is loaded, device calls first copy the index arrays back to the host
+ * (synchronising `stream`) and validate them, returning PA_ERR_BAD_TABLE on
+ * any violation, and synchronise after the launch to report kernel errors.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,        /* null pointer, negative size, bad combination */
+  PA_ERR_NO_FREE_BLOCKS = 2,     /* the pool cannot satisfy the request; state unchanged */
+  PA_ERR_UNKNOWN_SEQ = 3,        /* no sequence with this id */
+  PA_ERR_SEQ_EXISTS = 4,         /* a sequence with this id already exists */
+  PA_ERR_UNSUPPORTED = 5,        /* dtype / head_dim / block_size not built */
+  PA_ERR_BAD_TABLE = 6,          /* PA_DEBUG validation: index outside its range, or a write race */
+  PA_ERR_WORKSPACE_TOO_SMALL = 7,
+  PA_ERR_HIP = 8                 /* a HIP runtime call or kernel launch failed */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* ======================================================================== *
+ * Host block allocator                                                      *
+ * ======================================================================== *
+ * The pool's bookkeeping on the host ([SRC-1] §二/§三 PagedKVCache,
+ * [XDNF] §3.3/§3.4/§4.2, [IMPL] §3.3 and §3.4 BlockSpaceManager,
+ * [ASC] §7.1 BlockManager, [ATB] §4.2 BlockManager):
+ *   - free blocks form a first-in-first-out queue: allocation takes the head,
+ *     a block whose refcount reaches 0 goes to the tail ([SRC-1] §二 worked
+ *     example: 32, 16, 48 tokens -> [0,1], [2], [3,4,5], free [6,7,8,...]);
+ *   - a sequence of n tokens holds ceil(n / block_size) blocks;
+ *   - each block has a refcount: 1 when allocated, +1 per extra sharer;
+ *   - copy-on-write is decided before a write ([XDNF] §3.4, [IMPL] §3.3).
+ * Every call is all-or-nothing: on error the state is unchanged.  Calls on
+ * one handle are serialised by an internal mutex.  Sequence ids are arbitrary
+ * int64 values chosen by the caller.  The allocator touches no device memory.
+ */
+typedef struct pa_allocator pa_allocator;
+
+typedef struct pa_allocator_stats {
+  int64_t blocks_allocated;  /* blocks taken from the free queue */
+  int64_t blocks_freed;      /* blocks returned to the free queue */
+  int64_t cow_copies;        /* copy-on-write pairs emitted */
+} pa_allocator_stats;
+
+/* Create a pool of num_blocks blocks of block_size tokens.  initial_free_order:
+ * NULL for 0..num_blocks-1, else a host array of num_blocks ids that must be
+ * a permutation of 0..num_blocks-1 (PA_ERR_INVALID_ARG otherwise).  *out
+ * receives the handle; the caller destroys it with pa_allocator_destroy. */
+pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size,
+                              const int32_t* initial_free_order, pa_allocator** out);
+void pa_allocator_destroy(pa_allocator* a);
+/* Deep copy of the whole state (free queue order, refcounts, sequences, stats). */
+pa_status pa_allocator_clone(const pa_allocator* a, pa_allocator** out);
+
+/* New sequence holding num_tokens >= 0 tokens: ceil(num_tokens / bs) blocks
+ * from the head of the free queue, each with refcount 1 ([SRC-1] §三). */
+pa_status pa_seq_create(pa_allocator* a, int64_t seq_id, int32_t num_tokens);
+
+/* Fork for parallel sampling / beam search ([XDNF] §3.4): the child gets the
+ * parent's first ceil(n / bs) blocks, each gaining one reference, and length
+ * n = num_tokens (0 <= n <= parent length; -1 means the parent's length). */
+pa_status pa_seq_fork(pa_allocator* a, int64_t parent, int64_t child, int32_t num_tokens);
+
+/* Reserve the slot of the sequence's next token (position L = current length)
+ * ([XDNF] §4.2 append_token_kv, §3.1 addressing; [IMPL] §3.3):
+ *   L % bs == 0            -> a fresh block is appended to the table;
+ *   last block refcount >1 -> copy-on-write: a fresh block replaces it in the
+ *                             table, *cow_src / *cow_dst receive (old, new),
+ *                             the old refcount drops by one, the new is 1;
+ *   otherwise              -> the token is written in place.
+ * *slot = table[L / bs] * bs + L % bs; the length becomes L + 1.  *cow_src and
+ * *cow_dst are -1 when no copy is needed.  The caller must copy the whole
+ * block (pa_copy_blocks) before writing the token (pa_reshape_and_cache). */
+pa_status pa_seq_append_slot(pa_allocator* a, int64_t seq_id, int32_t* slot,
+                             int32_t* cow_src, int32_t* cow_dst);
+
+/* One decode step's bookkeeping: pa_seq_append_slot for seq_ids[0..n-1] in
+ * that order (so earlier sharers copy and the last remaining sharer writes in
+ * place).  slots: host [n]; cow_pairs: host [n, 2] (src, dst) capacity;
+ * *num_pairs receives the number of pairs written.  All-or-nothing. */
+pa_status pa_seq_append_slots(pa_allocator* a, const int64_t* seq_ids, int32_t n,
+                              int32_t* slots, int32_t* cow_pairs, int32_t* num_pairs);
+
+/* Release a sequence ([XDNF] §4.2 free_sequence): each block in table order
+ * loses one reference and goes to the tail of the free queue at 0. */
+pa_status pa_seq_free(pa_allocator* a, int64_t seq_id);
+
+pa_status pa_can_allocate(const pa_allocator* a, int32_t num_blocks, int32_t* ok);
+int32_t pa_num_free_blocks(const pa_allocator* a);
+/* Refcount of a block, or -1 when `block` is outside [0, num_blocks). */
+int32_t pa_ref_count(const pa_allocator* a, int32_t block);
+pa_status pa_seq_len(const pa_allocator* a, int64_t seq_id, int32_t* len);
+/* Copy a sequence's table into host out[0..capacity); *num_blocks receives its
+ * length (PA_ERR_INVALID_ARG if it exceeds capacity). */
+pa_status pa_seq_block_table(const pa_allocator* a, int64_t seq_id, int32_t* out,
+                             int32_t capacity, int32_t* num_blocks);
+/* Copy the free queue, head first, into host out[0..capacity). */
+pa_status pa_free_list(const pa_allocator* a, int32_t* out, int32_t capacity, int32_t* n);
+/* Fill host tables [n, max_blocks] (rows padded with -1) and context_lens [n]
+ * for the listed sequences ([ATB] §4.2 get_block_table / get_context_lens).
+ * PA_ERR_INVALID_ARG if a table is longer than max_blocks. */
+pa_status pa_build_block_tables(const pa_allocator* a, const int64_t* seq_ids, int32_t n,
+                                int32_t max_blocks, int32_t* tables, int32_t* context_lens);
+pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out);
+
+/* ======================================================================== *
+ * Device operations                                                         *
+ * ======================================================================== */
+
+/* Write new K/V rows into the pools through the slot mapping ([ASC] §3.1
+ * slot_mapping; [IMPL] §3.4 _add_kv_cache):
+ *   for i < num_tokens with 0 <= s = slot_mapping[i] < num_blocks*block_size:
+ *     key_cache[s / bs, h, s % bs, :] = key[i, h, :]  for every KV head h,
+ *     value_cache likewise from value.
+ * key, value: device [num_tokens, num_kv_heads, head_dim].  Negative slots are
+ * skipped (padding); slots past the pool are skipped too (and rejected under
+ * PA_DEBUG).  Two tokens with the same slot race: invalid input.  A pure copy,
+ * bit-exact. */
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                               void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, pa_dtype dtype, void* stream);
+
+/* Copy-on-write block copies ([IMPL] §3.3: the whole block is copied):
+ * for each pair p < num_pairs, block pairs[2p] (src) -> pairs[2p+1] (dst) in
+ * both pools, all KV heads, all rows.  pairs: device int32 [num_pairs, 2].
+ * Pairs run concurrently: a block that is the destination of one pair must
+ * not be the source or destination of another (rejected under PA_DEBUG).
+ * Pairs with an id outside [0, num_blocks) are skipped.  Bit-exact. */
+pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
+                         int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, pa_dtype dtype, void* stream);
+
+/* Single-pass paged decode attention ([IMPL] §3.1 index-based kernel and
+ * §3.4 PagedAttention.forward; [ATB] §3.2 PagedAttentionOperation.apply;
+ * [ASC] §三/§四 fused gather + QK^T + softmax + OV):
+ *   for each sequence s and query head h, with n = context_lens[s],
+ *   g = h / (num_heads / num_kv_heads), token t in block
+ *   block_tables[s, t / bs] at row t % bs:
+ *     z_t = scale * <query[s,h,:], K_t>,  out[s,h,:] = sum_t softmax(z)_t V_t
+ * accumulated in fp32 with an online softmax (running max and sum, both
+ * rescaled when the max grows), written in `dtype` (round to nearest even).
+ * n == 0 gives a zero row.  max_context_len bounds every n and is used to
+ * size the launch.
+ * Invalid device data never causes an out-of-bounds access: a context length
+ * outside [0, min(max_context_len, max_blocks_per_seq*bs)] or a block id
+ * outside [0, num_blocks) among the first ceil(n / bs) entries makes that
+ * sequence's output rows NaN (PA_ERR_BAD_TABLE under PA_DEBUG). */
+pa_status pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+                    float scale, pa_dtype dtype, void* stream);
+
+/* Split-context workspace.  For P = ceil(max_context_len / partition_size)
+ * partitions, the workspace holds three fp32 arrays, each starting at a
+ * 256-byte aligned offset:
+ *   m [num_seqs, num_heads, P]         m_p = max logit of partition p (natural units)
+ *   l [num_seqs, num_heads, P]         l_p = sum_t exp(z_t - m_p)
+ *   o [num_seqs, num_heads, P, head_dim] o_p = sum_t exp(z_t - m_p) V_t / l_p
+ * Partition p of sequence s covers tokens [p*PS, min((p+1)*PS, n)); only the
+ * first ceil(n / PS) partitions of a sequence are written.  Returns 0 on an
+ * invalid argument. */
+size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                       int32_t max_context_len, int32_t partition_size);
+
+/* Split-context decode for few, very long sequences ([ATB] §2.3 describes a
+ * second kernel for that case): one pass writes the per-partition partials
+ * (m_p, l_p, o_p) above into `workspace`, then pa_lse_reduce merges them into
+ * `out`.  Same arguments and error behaviour as pa_decode, plus
+ * partition_size (a multiple of block_size, at most 4096) and the
+ * caller-owned device workspace of workspace_bytes bytes. */
+pa_status pa_decode_split(void* out, const void* query, const void* key_cache,
+                          const void* value_cache, const int32_t* block_tables,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+                          float scale, pa_dtype dtype, int32_t partition_size, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Log-sum-exp merge of split partials (the standard rule; the pages do not
+ * spell it out): with M = max_p m_p and w_p = l_p * exp(m_p - M),
+ *   out[s,h,:] = sum_p w_p o_p / sum_p w_p   over p < ceil(n / partition_size),
+ * written in `dtype`; n == 0 gives zeros; an invalid n gives NaN rows.
+ * `workspace` is laid out as described for pa_decode_split_workspace_bytes
+ * with the same num_seqs, num_heads, head_dim, max_context_len and
+ * partition_size. */
+pa_status pa_lse_reduce(void* out, const void* workspace, size_t workspace_bytes,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                        int32_t head_dim, int32_t max_context_len, int32_t partition_size,
+                        pa_dtype dtype, void* stream);
+
+/* ======================================================================== *
+ * Errors and version                                                        *
+ * ======================================================================== */
+const char* pa_status_string(pa_status s);
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* pa_last_error(void);
+int32_t pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H_ */

@@ -1,0 +1,293 @@
+"""PagedAttention decode for MI355X (gfx950): Python binding of libpa.so.
+
+Argument marshalling only.  Every step runs in the C++ allocator or the HIP
+kernels of libpa.so; torch tensors supply device memory and the current
+stream.  Importing this package fails loudly when libpa.so has not been
+built (python -m paged_kv_cache_333_amd.build): there is no fallback.
+
+Names follow the C ABI in include/pa.h:
+  pa_reshape_and_cache, pa_copy_blocks, pa_decode, pa_decode_split,
+  pa_decode_split_workspace_bytes, pa_lse_reduce, and the allocator verbs as
+  methods of `Allocator` (pa_seq_create -> Allocator.seq_create, ...).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_333_amd.build`")
+lib = C.CDLL(LIB_PATH)
+
+PA_OK = 0
+STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_NO_FREE_BLOCKS", 3: "PA_ERR_UNKNOWN_SEQ",
+          4: "PA_ERR_SEQ_EXISTS", 5: "PA_ERR_UNSUPPORTED", 6: "PA_ERR_BAD_TABLE",
+          7: "PA_ERR_WORKSPACE_TOO_SMALL", 8: "PA_ERR_HIP"}
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
+
+_i32, _i64, _f32, _vp, _sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
+_pi32, _pi64 = C.POINTER(C.c_int32), C.POINTER(C.c_int64)
+
+
+class pa_allocator_stats(C.Structure):
+    _fields_ = [("blocks_allocated", C.c_int64), ("blocks_freed", C.c_int64), ("cow_copies", C.c_int64)]
+
+
+_PROTOS = {
+    "pa_allocator_create": (_i32, [_i32, _i32, _pi32, C.POINTER(_vp)]),
+    "pa_allocator_destroy": (None, [_vp]),
+    "pa_allocator_clone": (_i32, [_vp, C.POINTER(_vp)]),
+    "pa_seq_create": (_i32, [_vp, _i64, _i32]),
+    "pa_seq_fork": (_i32, [_vp, _i64, _i64, _i32]),
+    "pa_seq_append_slot": (_i32, [_vp, _i64, _pi32, _pi32, _pi32]),
+    "pa_seq_append_slots": (_i32, [_vp, _pi64, _i32, _pi32, _pi32, _pi32]),
+    "pa_seq_free": (_i32, [_vp, _i64]),
+    "pa_can_allocate": (_i32, [_vp, _i32, _pi32]),
+    "pa_num_free_blocks": (_i32, [_vp]),
+    "pa_ref_count": (_i32, [_vp, _i32]),
+    "pa_seq_len": (_i32, [_vp, _i64, _pi32]),
+    "pa_seq_block_table": (_i32, [_vp, _i64, _pi32, _i32, _pi32]),
+    "pa_free_list": (_i32, [_vp, _pi32, _i32, _pi32]),
+    "pa_build_block_tables": (_i32, [_vp, _pi64, _i32, _i32, _pi32, _pi32]),
+    "pa_allocator_get_stats": (_i32, [_vp, C.POINTER(pa_allocator_stats)]),
+    "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                         _f32, _i32, _vp]),
+    "pa_decode_split_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_split": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_lse_reduce": (_i32, [_vp, _vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_status_string": (C.c_char_p, [_i32]),
+    "pa_last_error": (C.c_char_p, []),
+    "pa_abi_version": (_i32, []),
+}
+for _name, (_res, _args) in _PROTOS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_PROTOS)
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.code = STATUS.get(status, str(status))
+        detail = lib.pa_last_error().decode()
+        super().__init__(f"{where}: {self.code} ({detail})")
+
+
+def _check(status: int, where: str):
+    if status != PA_OK:
+        raise PAError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# device operations (torch tensors in, nothing computed here)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    codes = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _ptr(t) -> int:
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libpa must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, stream=None):
+    """key, value [T, H_kv, D]; pools [NB, H_kv, bs, D]; slot_mapping int32 [T]."""
+    NB, H_kv, bs, D = key_cache.shape
+    _check(lib.pa_reshape_and_cache(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                    _ptr(slot_mapping), slot_mapping.numel(), NB, H_kv, D, bs,
+                                    _dtype_code(key_cache), _stream(stream)), "pa_reshape_and_cache")
+
+
+def pa_copy_blocks(key_cache, value_cache, pairs, stream=None, num_pairs=None):
+    """pairs int32 [P, 2] (src, dst) on the device; num_pairs may cover a prefix of it."""
+    NB, H_kv, bs, D = key_cache.shape
+    P = pairs.shape[0] if num_pairs is None else num_pairs
+    _check(lib.pa_copy_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(pairs), P, NB, H_kv, D, bs,
+                              _dtype_code(key_cache), _stream(stream)), "pa_copy_blocks")
+
+
+def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len: int,
+              scale: float, stream=None):
+    """out, query [S, H, D]; pools [NB, H_kv, bs, D]; block_tables [S, MB]; context_lens [S]."""
+    S, H, D = query.shape
+    NB, H_kv, bs, _ = key_cache.shape
+    _check(lib.pa_decode(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+                         _ptr(context_lens), S, H, H_kv, D, bs, block_tables.shape[1], NB, max_context_len,
+                         scale, _dtype_code(query), _stream(stream)), "pa_decode")
+
+
+def pa_decode_split_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
+                                    partition_size: int) -> int:
+    return lib.pa_decode_split_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size)
+
+
+def pa_decode_split(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len: int,
+                    scale: float, partition_size: int, workspace, stream=None):
+    """As pa_decode; workspace is a device tensor of at least pa_decode_split_workspace_bytes bytes."""
+    S, H, D = query.shape
+    NB, H_kv, bs, _ = key_cache.shape
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.pa_decode_split(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                               _ptr(block_tables), _ptr(context_lens), S, H, H_kv, D, bs,
+                               block_tables.shape[1], NB, max_context_len, scale, _dtype_code(query),
+                               partition_size, _ptr(workspace), nbytes, _stream(stream)), "pa_decode_split")
+
+
+def pa_lse_reduce(out, workspace, context_lens, max_context_len: int, partition_size: int, stream=None):
+    """out [S, H, D]; workspace holds the split partials for the same S, H, D."""
+    S, H, D = out.shape
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.pa_lse_reduce(_ptr(out), _ptr(workspace), nbytes, _ptr(context_lens), S, H, D,
+                             max_context_len, partition_size, _dtype_code(out), _stream(stream)),
+           "pa_lse_reduce")
+
+
+def split_layout(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int, partition_size: int):
+    """Byte offsets and partition count of the split workspace, as documented in include/pa.h."""
+    P = -(-max_context_len // partition_size)
+    units = num_seqs * num_heads * P
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    off_l = a256(units * 4)
+    off_o = off_l + a256(units * 4)
+    return {"parts": P, "off_m": 0, "off_l": off_l, "off_o": off_o, "total": off_o + units * head_dim * 4}
+
+
+# ---------------------------------------------------------------------------
+# host allocator
+
+
+class Allocator:
+    """Host block allocator (pa_allocator_* / pa_seq_* in include/pa.h)."""
+
+    def __init__(self, num_blocks: int, block_size: int, initial_free_order=None, _handle=None):
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        if _handle is not None:
+            self._h = _handle
+            return
+        h = _vp()
+        order = None
+        if initial_free_order is not None:
+            arr = (C.c_int32 * num_blocks)(*[int(x) for x in initial_free_order])
+            order = C.cast(arr, _pi32)
+        _check(lib.pa_allocator_create(num_blocks, block_size, order, C.byref(h)), "pa_allocator_create")
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib.pa_allocator_destroy(h)
+            self._h = None
+
+    def clone(self) -> "Allocator":
+        h = _vp()
+        _check(lib.pa_allocator_clone(self._h, C.byref(h)), "pa_allocator_clone")
+        return Allocator(self.num_blocks, self.block_size, _handle=h)
+
+    def seq_create(self, seq_id: int, num_tokens: int):
+        _check(lib.pa_seq_create(self._h, seq_id, num_tokens), "pa_seq_create")
+
+    def seq_fork(self, parent: int, child: int, num_tokens: int = -1):
+        _check(lib.pa_seq_fork(self._h, parent, child, num_tokens), "pa_seq_fork")
+
+    def seq_append_slot(self, seq_id: int):
+        slot, src, dst = C.c_int32(), C.c_int32(), C.c_int32()
+        _check(lib.pa_seq_append_slot(self._h, seq_id, C.byref(slot), C.byref(src), C.byref(dst)),
+               "pa_seq_append_slot")
+        return slot.value, src.value, dst.value
+
+    def seq_append_slots_into(self, seq_ids_ptr: int, n: int, slots_ptr: int, pairs_ptr: int) -> int:
+        """Raw form for pinned host buffers: pointers to int64 ids, int32 slots, int32 pairs."""
+        np_ = C.c_int32()
+        _check(lib.pa_seq_append_slots(self._h, C.cast(seq_ids_ptr, _pi64), n, C.cast(slots_ptr, _pi32),
+                                       C.cast(pairs_ptr, _pi32), C.byref(np_)), "pa_seq_append_slots")
+        return np_.value
+
+    def seq_append_slots(self, seq_ids):
+        n = len(seq_ids)
+        ids = (C.c_int64 * max(n, 1))(*seq_ids)
+        slots = (C.c_int32 * max(n, 1))()
+        pairs = (C.c_int32 * max(2 * n, 2))()
+        np_ = C.c_int32()
+        _check(lib.pa_seq_append_slots(self._h, ids, n, slots, pairs, C.byref(np_)), "pa_seq_append_slots")
+        return list(slots[:n]), [(pairs[2 * i], pairs[2 * i + 1]) for i in range(np_.value)]
+
+    def seq_free(self, seq_id: int):
+        _check(lib.pa_seq_free(self._h, seq_id), "pa_seq_free")
+
+    def can_allocate(self, num_blocks: int) -> bool:
+        ok = C.c_int32()
+        _check(lib.pa_can_allocate(self._h, num_blocks, C.byref(ok)), "pa_can_allocate")
+        return bool(ok.value)
+
+    def num_free_blocks(self) -> int:
+        return lib.pa_num_free_blocks(self._h)
+
+    def ref_count(self, block: int) -> int:
+        return lib.pa_ref_count(self._h, block)
+
+    def seq_len(self, seq_id: int) -> int:
+        n = C.c_int32()
+        _check(lib.pa_seq_len(self._h, seq_id, C.byref(n)), "pa_seq_len")
+        return n.value
+
+    def block_table(self, seq_id: int) -> list:
+        cap = self.num_blocks + 1
+        buf = (C.c_int32 * cap)()
+        n = C.c_int32()
+        _check(lib.pa_seq_block_table(self._h, seq_id, buf, cap, C.byref(n)), "pa_seq_block_table")
+        return list(buf[: n.value])
+
+    def free_list(self) -> list:
+        cap = max(self.num_blocks, 1)
+        buf = (C.c_int32 * cap)()
+        n = C.c_int32()
+        _check(lib.pa_free_list(self._h, buf, cap, C.byref(n)), "pa_free_list")
+        return list(buf[: n.value])
+
+    def build_block_tables(self, seq_ids, max_blocks: int):
+        n = len(seq_ids)
+        ids = (C.c_int64 * max(n, 1))(*seq_ids)
+        tabs = (C.c_int32 * max(n * max_blocks, 1))()
+        lens = (C.c_int32 * max(n, 1))()
+        _check(lib.pa_build_block_tables(self._h, ids, n, max_blocks, tabs, lens), "pa_build_block_tables")
+        return ([list(tabs[i * max_blocks:(i + 1) * max_blocks]) for i in range(n)], list(lens[:n]))
+
+    def build_block_tables_into(self, seq_ids_ptr: int, n: int, max_blocks: int, tables_ptr: int,
+                                lens_ptr: int):
+        """Raw form for pinned host buffers."""
+        _check(lib.pa_build_block_tables(self._h, C.cast(seq_ids_ptr, _pi64), n, max_blocks,
+                                         C.cast(tables_ptr, _pi32), C.cast(lens_ptr, _pi32)),
+               "pa_build_block_tables")
+
+    def stats(self) -> dict:
+        st = pa_allocator_stats()
+        _check(lib.pa_allocator_get_stats(self._h, C.byref(st)), "pa_allocator_get_stats")
+        return {"blocks_allocated": st.blocks_allocated, "blocks_freed": st.blocks_freed,
+                "cow_copies": st.cow_copies}

@@ -1,0 +1,366 @@
+// Host block allocator: a first-in-first-out queue of free blocks, per-block
+// reference counts, fork and append with copy-on-write.
+//
+// Policy ("PagedAttention 源码解析：KV Cache 怎么管理" §二/§三; xdnf.cn
+// PagedAttention article §3.1, §3.4, §4.2; "PagedAttention 实现细节" §3.3):
+//  * allocation takes the head of the free queue; a block whose count drops to
+//    zero is appended to the tail (the first page's worked example, requests of
+//    32/16/48 tokens getting [0,1], [2], [3,4,5], fixes the queue order);
+//  * n tokens occupy ceil(n / block_size) blocks;
+//  * appending at position L opens a fresh block when L % bs == 0, otherwise it
+//    writes into the last block, first replacing that block with a private copy
+//    if its count is above one (the copy is done on the device by the caller);
+//  * every call is all-or-nothing.
+//
+// The free queue is a ring buffer of num_blocks entries; a block is never in
+// it twice, so it never overflows.
+#include <cstring>
+#include <mutex>
+#include <unordered_map>
+#include <vector>
+
+#include "status.hpp"
+
+namespace {
+
+struct Seq {
+  std::vector<int32_t> table;
+  int32_t len = 0;
+};
+
+}  // namespace
+
+struct pa_allocator {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> ring;  // free queue storage
+  int32_t head = 0;           // index of the queue head in `ring`
+  int32_t count = 0;          // number of free blocks
+  std::vector<int32_t> refs;
+  std::unordered_map<int64_t, Seq> seqs;
+  pa_allocator_stats stats{0, 0, 0};
+  mutable std::mutex mu;
+
+  int32_t blocks_for(int64_t n) const {
+    return static_cast<int32_t>((n + block_size - 1) / block_size);
+  }
+  int32_t pop_head() {
+    int32_t b = ring[head];
+    head = head + 1 == num_blocks ? 0 : head + 1;
+    --count;
+    refs[b] = 1;
+    ++stats.blocks_allocated;
+    return b;
+  }
+  void push_tail(int32_t b) {
+    int64_t pos = static_cast<int64_t>(head) + count;
+    ring[pos % num_blocks] = b;
+    ++count;
+    ++stats.blocks_freed;
+  }
+  void release(int32_t b) {
+    if (--refs[b] == 0) push_tail(b);
+  }
+};
+
+namespace {
+
+using pa::fail;
+
+// Undo log for a batch of appends, so a batch that runs out of blocks half way
+// can be rolled back whole.
+struct Journal {
+  struct RefChange { int32_t block, old; };
+  struct SeqChange { Seq* seq; int32_t old_len; int32_t index; int32_t old_block; bool appended; };
+  std::vector<RefChange> refs;
+  std::vector<SeqChange> seqs;
+  int32_t head = 0, count = 0;
+  pa_allocator_stats stats{0, 0, 0};
+};
+
+// Append one token to `s`.  Needs at most one free block, checked before any
+// change.  With a journal, every change is logged for rollback.
+pa_status append_one(pa_allocator* a, Seq& s, int32_t* slot, int32_t* src, int32_t* dst,
+                     Journal* j) {
+  const int32_t bs = a->block_size;
+  const int32_t L = s.len;
+  if (L == INT32_MAX) return fail(PA_ERR_INVALID_ARG, "sequence length overflow");
+  const int32_t lb = L / bs;
+  *src = -1;
+  *dst = -1;
+  if (L % bs == 0) {
+    if (a->count == 0) return fail(PA_ERR_NO_FREE_BLOCKS, "no free block for a new token");
+    if (j) j->seqs.push_back({&s, L, lb, -1, true});
+    int32_t b = a->pop_head();
+    if (j) j->refs.push_back({b, 0});
+    s.table.push_back(b);
+  } else {
+    int32_t last = s.table[lb];
+    if (a->refs[last] > 1) {
+      if (a->count == 0) return fail(PA_ERR_NO_FREE_BLOCKS, "no free block for copy-on-write");
+      if (j) j->seqs.push_back({&s, L, lb, last, false});
+      int32_t b = a->pop_head();
+      if (j) {
+        j->refs.push_back({b, 0});
+        j->refs.push_back({last, a->refs[last]});
+      }
+      --a->refs[last];
+      s.table[lb] = b;
+      ++a->stats.cow_copies;
+      *src = last;
+      *dst = b;
+    } else if (j) {
+      j->seqs.push_back({&s, L, lb, -1, false});
+    }
+  }
+  *slot = s.table[lb] * bs + L % bs;
+  s.len = L + 1;
+  return PA_OK;
+}
+
+void rollback(pa_allocator* a, Journal& j) {
+  for (auto it = j.refs.rbegin(); it != j.refs.rend(); ++it) a->refs[it->block] = it->old;
+  for (auto it = j.seqs.rbegin(); it != j.seqs.rend(); ++it) {
+    Seq& s = *it->seq;
+    if (it->appended) s.table.pop_back();
+    else if (it->old_block >= 0) s.table[it->index] = it->old_block;
+    s.len = it->old_len;
+  }
+  a->head = j.head;
+  a->count = j.count;
+  a->stats = j.stats;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size,
+                              const int32_t* initial_free_order, pa_allocator** out) {
+  if (!out) return fail(PA_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  if (num_blocks < 0 || block_size <= 0)
+    return fail(PA_ERR_INVALID_ARG, "num_blocks must be >= 0 and block_size > 0");
+  auto* a = new (std::nothrow) pa_allocator();
+  if (!a) return fail(PA_ERR_INVALID_ARG, "out of host memory");
+  a->num_blocks = num_blocks;
+  a->block_size = block_size;
+  a->ring.resize(num_blocks);
+  a->refs.assign(num_blocks, 0);
+  if (initial_free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t b = initial_free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete a;
+        return fail(PA_ERR_INVALID_ARG, "initial free order is not a permutation of 0..num_blocks-1");
+      }
+      seen[b] = 1;
+      a->ring[i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) a->ring[i] = i;
+  }
+  a->head = 0;
+  a->count = num_blocks;
+  *out = a;
+  return PA_OK;
+}
+
+void pa_allocator_destroy(pa_allocator* a) { delete a; }
+
+pa_status pa_allocator_clone(const pa_allocator* a, pa_allocator** out) {
+  if (!a || !out) return fail(PA_ERR_INVALID_ARG, "null argument");
+  std::lock_guard<std::mutex> g(a->mu);
+  auto* c = new (std::nothrow) pa_allocator();
+  if (!c) return fail(PA_ERR_INVALID_ARG, "out of host memory");
+  c->num_blocks = a->num_blocks;
+  c->block_size = a->block_size;
+  c->ring = a->ring;
+  c->head = a->head;
+  c->count = a->count;
+  c->refs = a->refs;
+  c->seqs = a->seqs;
+  c->stats = a->stats;
+  *out = c;
+  return PA_OK;
+}
+
+pa_status pa_seq_create(pa_allocator* a, int64_t seq_id, int32_t num_tokens) {
+  if (!a) return fail(PA_ERR_INVALID_ARG, "null allocator");
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens < 0");
+  std::lock_guard<std::mutex> g(a->mu);
+  if (a->seqs.count(seq_id)) return fail(PA_ERR_SEQ_EXISTS, "sequence id already in use");
+  int32_t nb = a->blocks_for(num_tokens);
+  if (nb > a->count) return fail(PA_ERR_NO_FREE_BLOCKS, "not enough free blocks for the sequence");
+  Seq s;
+  s.table.reserve(nb + 1);
+  for (int32_t i = 0; i < nb; ++i) s.table.push_back(a->pop_head());
+  s.len = num_tokens;
+  a->seqs.emplace(seq_id, std::move(s));
+  return PA_OK;
+}
+
+pa_status pa_seq_fork(pa_allocator* a, int64_t parent, int64_t child, int32_t num_tokens) {
+  if (!a) return fail(PA_ERR_INVALID_ARG, "null allocator");
+  std::lock_guard<std::mutex> g(a->mu);
+  auto it = a->seqs.find(parent);
+  if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown parent sequence");
+  if (a->seqs.count(child)) return fail(PA_ERR_SEQ_EXISTS, "child id already in use");
+  const Seq& p = it->second;
+  int32_t n = num_tokens < 0 ? p.len : num_tokens;
+  if (n > p.len) return fail(PA_ERR_INVALID_ARG, "fork length beyond the parent's length");
+  Seq c;
+  int32_t nb = a->blocks_for(n);
+  c.table.assign(p.table.begin(), p.table.begin() + nb);
+  c.len = n;
+  for (int32_t b : c.table) ++a->refs[b];
+  a->seqs.emplace(child, std::move(c));
+  return PA_OK;
+}
+
+pa_status pa_seq_append_slot(pa_allocator* a, int64_t seq_id, int32_t* slot, int32_t* cow_src,
+                             int32_t* cow_dst) {
+  if (!a || !slot || !cow_src || !cow_dst) return fail(PA_ERR_INVALID_ARG, "null argument");
+  std::lock_guard<std::mutex> g(a->mu);
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence");
+  return append_one(a, it->second, slot, cow_src, cow_dst, nullptr);
+}
+
+pa_status pa_seq_append_slots(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t* slots,
+                              int32_t* cow_pairs, int32_t* num_pairs) {
+  if (!a || !num_pairs || n < 0 || (n > 0 && (!seq_ids || !slots || !cow_pairs)))
+    return fail(PA_ERR_INVALID_ARG, "null argument or negative count");
+  std::lock_guard<std::mutex> g(a->mu);
+  std::vector<Seq*> ptrs(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence in batch");
+    ptrs[i] = &it->second;
+  }
+  // Each append needs at most one block: with n free blocks nothing can fail
+  // for lack of blocks and the journal is skipped.
+  Journal journal;
+  Journal* j = nullptr;
+  if (a->count < n) {
+    journal.head = a->head;
+    journal.count = a->count;
+    journal.stats = a->stats;
+    j = &journal;
+  }
+  int32_t np = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t src, dst;
+    pa_status st = append_one(a, *ptrs[i], &slots[i], &src, &dst, j);
+    if (st != PA_OK) {
+      if (j) rollback(a, *j);
+      return st;
+    }
+    if (src >= 0) {
+      cow_pairs[2 * np] = src;
+      cow_pairs[2 * np + 1] = dst;
+      ++np;
+    }
+  }
+  *num_pairs = np;
+  return PA_OK;
+}
+
+pa_status pa_seq_free(pa_allocator* a, int64_t seq_id) {
+  if (!a) return fail(PA_ERR_INVALID_ARG, "null allocator");
+  std::lock_guard<std::mutex> g(a->mu);
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence");
+  for (int32_t b : it->second.table) a->release(b);
+  a->seqs.erase(it);
+  return PA_OK;
+}
+
+pa_status pa_can_allocate(const pa_allocator* a, int32_t num_blocks, int32_t* ok) {
+  if (!a || !ok) return fail(PA_ERR_INVALID_ARG, "null argument");
+  std::lock_guard<std::mutex> g(a->mu);
+  *ok = num_blocks <= a->count ? 1 : 0;
+  return PA_OK;
+}
+
+int32_t pa_num_free_blocks(const pa_allocator* a) {
+  if (!a) return -1;
+  std::lock_guard<std::mutex> g(a->mu);
+  return a->count;
+}
+
+int32_t pa_ref_count(const pa_allocator* a, int32_t block) {
+  if (!a) return -1;
+  std::lock_guard<std::mutex> g(a->mu);
+  if (block < 0 || block >= a->num_blocks) return -1;
+  return a->refs[block];
+}
+
+pa_status pa_seq_len(const pa_allocator* a, int64_t seq_id, int32_t* len) {
+  if (!a || !len) return fail(PA_ERR_INVALID_ARG, "null argument");
+  std::lock_guard<std::mutex> g(a->mu);
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence");
+  *len = it->second.len;
+  return PA_OK;
+}
+
+pa_status pa_seq_block_table(const pa_allocator* a, int64_t seq_id, int32_t* out, int32_t capacity,
+                             int32_t* num_blocks) {
+  if (!a || !num_blocks || capacity < 0 || (capacity > 0 && !out))
+    return fail(PA_ERR_INVALID_ARG, "null argument or negative capacity");
+  std::lock_guard<std::mutex> g(a->mu);
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence");
+  const auto& t = it->second.table;
+  if (static_cast<int64_t>(t.size()) > capacity) return fail(PA_ERR_INVALID_ARG, "capacity too small");
+  if (!t.empty()) std::memcpy(out, t.data(), t.size() * sizeof(int32_t));
+  *num_blocks = static_cast<int32_t>(t.size());
+  return PA_OK;
+}
+
+pa_status pa_free_list(const pa_allocator* a, int32_t* out, int32_t capacity, int32_t* n) {
+  if (!a || !n || capacity < 0 || (capacity > 0 && !out))
+    return fail(PA_ERR_INVALID_ARG, "null argument or negative capacity");
+  std::lock_guard<std::mutex> g(a->mu);
+  if (a->count > capacity) return fail(PA_ERR_INVALID_ARG, "capacity too small");
+  for (int32_t i = 0; i < a->count; ++i)
+    out[i] = a->ring[(static_cast<int64_t>(a->head) + i) % a->num_blocks];
+  *n = a->count;
+  return PA_OK;
+}
+
+pa_status pa_build_block_tables(const pa_allocator* a, const int64_t* seq_ids, int32_t n,
+                                int32_t max_blocks, int32_t* tables, int32_t* context_lens) {
+  if (!a || n < 0 || max_blocks < 0 ||
+      (n > 0 && (!seq_ids || !context_lens || (max_blocks > 0 && !tables))))
+    return fail(PA_ERR_INVALID_ARG, "null argument or negative size");
+  std::lock_guard<std::mutex> g(a->mu);
+  std::vector<const Seq*> ptrs(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence");
+    if (static_cast<int64_t>(it->second.table.size()) > max_blocks)
+      return fail(PA_ERR_INVALID_ARG, "a block table is longer than max_blocks");
+    ptrs[i] = &it->second;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const auto& t = ptrs[i]->table;
+    int32_t* row = tables + static_cast<int64_t>(i) * max_blocks;
+    const int32_t k = static_cast<int32_t>(t.size());
+    if (k) std::memcpy(row, t.data(), k * sizeof(int32_t));
+    for (int32_t j = k; j < max_blocks; ++j) row[j] = -1;
+    context_lens[i] = ptrs[i]->len;
+  }
+  return PA_OK;
+}
+
+pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out) {
+  if (!a || !out) return fail(PA_ERR_INVALID_ARG, "null argument");
+  std::lock_guard<std::mutex> g(a->mu);
+  *out = a->stats;
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,300 @@
+// C ABI for the device operations: argument validation, the optional
+// PA_DEBUG checks of device-side indices, and dispatch to the kernels.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "launch.hpp"
+#include "status.hpp"
+
+namespace {
+
+using pa::fail;
+
+bool debug_mode() {
+  static const bool on = [] {
+    const char* v = std::getenv("PA_DEBUG");
+    return v && std::strcmp(v, "0") != 0 && v[0] != '\0';
+  }();
+  return on;
+}
+
+int elem_bytes(pa_dtype dt) { return dt == PA_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pa_status hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+pa_status check_shape(pa_dtype dt, int32_t head_dim, int32_t block_size) {
+  if (dt != PA_F32 && dt != PA_F16 && dt != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype");
+  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (block_size != 16 && block_size != 32) return fail(PA_ERR_UNSUPPORTED, "block_size must be 16 or 32");
+  return PA_OK;
+}
+
+// After a launch: report launch errors; in debug mode also wait and report
+// execution errors.
+pa_status finish(hipError_t launch, hipStream_t st, const char* what) {
+  if (launch != hipSuccess) return hip_fail(launch, what);
+  if (debug_mode()) {
+    hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, what);
+  }
+  return PA_OK;
+}
+
+template <typename T>
+pa_status fetch(std::vector<T>& host, const T* dev, size_t n, hipStream_t st) {
+  host.resize(n);
+  if (n == 0) return PA_OK;
+  hipError_t e = hipStreamSynchronize(st);
+  if (e == hipSuccess) e = hipMemcpy(host.data(), dev, n * sizeof(T), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "PA_DEBUG copy-back");
+  return PA_OK;
+}
+
+pa_status check_decode_args(const pa::DecodeArgs& a) {
+  pa_status s = check_shape(a.dtype, a.head_dim, a.block_size);
+  if (s != PA_OK) return s;
+  if (a.num_seqs < 0 || a.num_heads <= 0 || a.num_kv_heads <= 0 || a.max_blocks_per_seq < 0 ||
+      a.num_blocks < 0 || a.max_context_len < 0)
+    return fail(PA_ERR_INVALID_ARG, "negative size or zero heads");
+  if (a.num_heads % a.num_kv_heads) return fail(PA_ERR_INVALID_ARG, "num_heads % num_kv_heads != 0");
+  if (a.num_seqs == 0) return PA_OK;
+  if (!a.out || !a.query || !a.key_cache || !a.value_cache || !a.block_tables || !a.context_lens)
+    return fail(PA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(a.out) || !aligned16(a.query) || !aligned16(a.key_cache) || !aligned16(a.value_cache))
+    return fail(PA_ERR_INVALID_ARG, "query, out and the pools must be 16-byte aligned");
+  if (static_cast<int64_t>(a.num_seqs) * a.num_heads > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "num_seqs * num_heads too large");
+  return PA_OK;
+}
+
+int64_t len_limit(const pa::DecodeArgs& a) {
+  const int64_t cap = static_cast<int64_t>(a.max_blocks_per_seq) * a.block_size;
+  return cap < a.max_context_len ? cap : a.max_context_len;
+}
+
+pa_status debug_check_tables(const pa::DecodeArgs& a, hipStream_t st) {
+  std::vector<int32_t> ctx, tab;
+  pa_status s = fetch(ctx, a.context_lens, a.num_seqs, st);
+  if (s == PA_OK) s = fetch(tab, a.block_tables, static_cast<size_t>(a.num_seqs) * a.max_blocks_per_seq, st);
+  if (s != PA_OK) return s;
+  const int64_t lim = len_limit(a);
+  for (int32_t i = 0; i < a.num_seqs; ++i) {
+    if (ctx[i] < 0 || ctx[i] > lim)
+      return fail(PA_ERR_BAD_TABLE, "context_lens[" + std::to_string(i) + "] = " + std::to_string(ctx[i]) +
+                                        " outside [0, " + std::to_string(lim) + "]");
+    const int32_t nb = (ctx[i] + a.block_size - 1) / a.block_size;
+    for (int32_t j = 0; j < nb; ++j) {
+      const int32_t b = tab[static_cast<size_t>(i) * a.max_blocks_per_seq + j];
+      if (b < 0 || b >= a.num_blocks)
+        return fail(PA_ERR_BAD_TABLE, "block_tables[" + std::to_string(i) + "][" + std::to_string(j) +
+                                          "] = " + std::to_string(b) + " outside the pool");
+    }
+  }
+  return PA_OK;
+}
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+struct SplitSizes {
+  int64_t off_l, off_o, total;
+  int32_t parts;
+};
+
+bool split_sizes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
+                 int32_t partition_size, SplitSizes* out) {
+  if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0 || partition_size <= 0)
+    return false;
+  const int64_t parts = (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
+  if (parts > 65535) return false;
+  const int64_t units = static_cast<int64_t>(num_seqs) * num_heads * parts;
+  out->parts = static_cast<int32_t>(parts);
+  out->off_l = align256(units * 4);
+  out->off_o = out->off_l + align256(units * 4);
+  out->total = out->off_o + units * head_dim * 4;
+  return true;
+}
+
+pa_status make_layout(void* workspace, size_t workspace_bytes, int32_t num_seqs, int32_t num_heads,
+                      int32_t head_dim, int32_t max_context_len, int32_t partition_size,
+                      pa::SplitLayout* ws) {
+  SplitSizes z;
+  if (!split_sizes(num_seqs, num_heads, head_dim, max_context_len, partition_size, &z))
+    return fail(PA_ERR_INVALID_ARG, "split sizes (at most 65535 partitions)");
+  if (static_cast<int64_t>(workspace_bytes) < z.total)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL,
+                "need " + std::to_string(z.total) + " bytes, got " + std::to_string(workspace_bytes));
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(PA_ERR_INVALID_ARG, "workspace must be non-null and 256-byte aligned");
+  char* base = static_cast<char*>(workspace);
+  ws->m = reinterpret_cast<float*>(base);
+  ws->l = reinterpret_cast<float*>(base + z.off_l);
+  ws->o = reinterpret_cast<float*>(base + z.off_o);
+  ws->partition_size = partition_size;
+  ws->num_parts = z.parts;
+  return PA_OK;
+}
+
+pa::DecodeArgs pack(void* out, const void* query, const void* key_cache, const void* value_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len, float scale,
+                    pa_dtype dtype) {
+  return pa::DecodeArgs{out, query, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                        num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                        max_context_len, scale, dtype};
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                               const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pa_dtype dtype,
+                               void* stream) {
+  pa_status s = check_shape(dtype, head_dim, block_size);
+  if (s != PA_OK) return s;
+  if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID_ARG, "negative size or zero heads");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PA_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_mode()) {
+    std::vector<int32_t> slots;
+    s = fetch(slots, slot_mapping, num_tokens, st);
+    if (s != PA_OK) return s;
+    const int64_t nslots = static_cast<int64_t>(num_blocks) * block_size;
+    std::unordered_set<int32_t> seen;
+    for (int32_t i = 0; i < num_tokens; ++i) {
+      if (slots[i] < 0) continue;
+      if (slots[i] >= nslots)
+        return fail(PA_ERR_BAD_TABLE, "slot_mapping[" + std::to_string(i) + "] past the pool");
+      if (!seen.insert(slots[i]).second)
+        return fail(PA_ERR_BAD_TABLE, "slot " + std::to_string(slots[i]) + " written twice");
+    }
+  }
+  return finish(pa::launch_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                                             num_blocks, num_kv_heads, head_dim * elem_bytes(dtype),
+                                             block_size, st),
+                st, "pa_reshape_and_cache");
+}
+
+pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs, int32_t num_pairs,
+                         int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         pa_dtype dtype, void* stream) {
+  pa_status s = check_shape(dtype, head_dim, block_size);
+  if (s != PA_OK) return s;
+  if (num_pairs < 0 || num_blocks < 0 || num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID_ARG, "negative size or zero heads");
+  if (num_pairs == 0) return PA_OK;
+  if (!key_cache || !value_cache || !pairs) return fail(PA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PA_ERR_INVALID_ARG, "pools must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_mode()) {
+    std::vector<int32_t> pr;
+    s = fetch(pr, pairs, static_cast<size_t>(num_pairs) * 2, st);
+    if (s != PA_OK) return s;
+    std::unordered_set<int32_t> dsts, srcs;
+    for (int32_t p = 0; p < num_pairs; ++p) {
+      const int32_t a = pr[2 * p], b = pr[2 * p + 1];
+      if (a < 0 || a >= num_blocks || b < 0 || b >= num_blocks)
+        return fail(PA_ERR_BAD_TABLE, "copy pair " + std::to_string(p) + " outside the pool");
+      if (!dsts.insert(b).second) return fail(PA_ERR_BAD_TABLE, "two copies into one block");
+      srcs.insert(a);
+    }
+    for (int32_t b : dsts)
+      if (srcs.count(b)) return fail(PA_ERR_BAD_TABLE, "a copy destination is also a source");
+  }
+  const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
+  return finish(pa::launch_copy_blocks(key_cache, value_cache, pairs, num_pairs, num_blocks, block_bytes, st),
+                st, "pa_copy_blocks");
+}
+
+pa_status pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len, float scale,
+                    pa_dtype dtype, void* stream) {
+  pa::DecodeArgs a = pack(out, query, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                          num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                          max_context_len, scale, dtype);
+  pa_status s = check_decode_args(a);
+  if (s != PA_OK || num_seqs == 0) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_mode() && (s = debug_check_tables(a, st)) != PA_OK) return s;
+  return finish(pa::launch_decode(a, st), st, "pa_decode");
+}
+
+size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                       int32_t max_context_len, int32_t partition_size) {
+  SplitSizes z;
+  if (!split_sizes(num_seqs, num_heads, head_dim, max_context_len, partition_size, &z)) return 0;
+  return static_cast<size_t>(z.total);
+}
+
+pa_status pa_decode_split(void* out, const void* query, const void* key_cache, const void* value_cache,
+                          const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+                          float scale, pa_dtype dtype, int32_t partition_size, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  pa::DecodeArgs a = pack(out, query, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                          num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                          max_context_len, scale, dtype);
+  pa_status s = check_decode_args(a);
+  if (s != PA_OK) return s;
+  if (partition_size <= 0 || partition_size % block_size || partition_size > 4096)
+    return fail(PA_ERR_INVALID_ARG, "partition_size must be a multiple of block_size, at most 4096");
+  if (num_seqs == 0) return PA_OK;
+  pa::SplitLayout ws;
+  s = make_layout(workspace, workspace_bytes, num_seqs, num_heads, head_dim, max_context_len,
+                  partition_size, &ws);
+  if (s != PA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_mode() && (s = debug_check_tables(a, st)) != PA_OK) return s;
+  return finish(pa::launch_decode_split(a, ws, st), st, "pa_decode_split");
+}
+
+pa_status pa_lse_reduce(void* out, const void* workspace, size_t workspace_bytes, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
+                        int32_t partition_size, pa_dtype dtype, void* stream) {
+  pa_status s = check_shape(dtype, head_dim, 16);
+  if (s != PA_OK) return s;
+  if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0 || partition_size <= 0)
+    return fail(PA_ERR_INVALID_ARG, "negative size");
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !context_lens) return fail(PA_ERR_INVALID_ARG, "null pointer");
+  if (static_cast<int64_t>(num_seqs) * num_heads > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "num_seqs * num_heads too large");
+  pa::SplitLayout ws;
+  s = make_layout(const_cast<void*>(workspace), workspace_bytes, num_seqs, num_heads, head_dim,
+                  max_context_len, partition_size, &ws);
+  if (s != PA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_mode()) {
+    std::vector<int32_t> ctx;
+    if ((s = fetch(ctx, context_lens, num_seqs, st)) != PA_OK) return s;
+    for (int32_t i = 0; i < num_seqs; ++i)
+      if (ctx[i] < 0 || ctx[i] > max_context_len)
+        return fail(PA_ERR_BAD_TABLE, "context_lens[" + std::to_string(i) + "] outside [0, max_context_len]");
+  }
+  return finish(pa::launch_lse_reduce(out, ws, context_lens, num_seqs, num_heads, head_dim, max_context_len,
+                                      dtype, st),
+                st, "pa_lse_reduce");
+}
+
+}  // extern "C"

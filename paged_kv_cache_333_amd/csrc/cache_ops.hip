@@ -1,0 +1,96 @@
+// Pool writes: the slot-mapping scatter of new K/V rows, and whole-block copies
+// for copy-on-write.  Both are pure 16-byte copies: every lane moves one chunk
+// of a token row, consecutive lanes move consecutive chunks, so a wave writes
+// whole rows with coalesced stores.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace pa {
+
+// Slot-mapping write ("Ascend C算子开发高阶实战…" §3.1: slot_mapping maps a
+// token to block slot / bs, offset slot % bs; "PagedAttention 实现细节" §3.4:
+// the new K/V of each step goes into its block).  One thread per 16-byte chunk
+// of one (token, KV head) row; it writes both the K and the V chunk.  Slots
+// outside [0, num_blocks * block_size) write nothing.
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const char* __restrict__ key, const char* __restrict__ value, char* __restrict__ key_cache,
+    char* __restrict__ value_cache, const int32_t* __restrict__ slot_mapping, int32_t num_tokens,
+    int64_t num_slots, int32_t num_kv_heads, int32_t chunks_per_row, int32_t block_size) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t per_token = static_cast<int64_t>(num_kv_heads) * chunks_per_row;
+  if (idx >= per_token * num_tokens) return;
+  const int64_t tok = idx / per_token;
+  const int64_t rem = idx - tok * per_token;  // = h * chunks_per_row + c
+  const int32_t h = static_cast<int32_t>(rem / chunks_per_row);
+  const int32_t c = static_cast<int32_t>(rem - static_cast<int64_t>(h) * chunks_per_row);
+  const int64_t slot = slot_mapping[tok];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / block_size;
+  const int64_t off = slot - blk * block_size;
+  const int64_t dst = (((blk * num_kv_heads + h) * block_size + off) * chunks_per_row + c) * 16;
+  const int64_t src = idx * 16;
+  store16(key_cache + dst, load16(key + src));
+  store16(value_cache + dst, load16(value + src));
+}
+
+// Whole-block copy ("PagedAttention 实现细节" §3.3: the full contents of the
+// original block go to the new one).  grid.x = pair * groups_per_pair + group,
+// grid.y = pool (K or V); each workgroup copies a stretch of the block's
+// 16-byte chunks.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ key_cache,
+                                                          char* __restrict__ value_cache,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int32_t num_blocks, int64_t chunks_per_block,
+                                                          int32_t groups_per_pair) {
+  const int32_t p = blockIdx.x / groups_per_pair;
+  const int32_t grp = blockIdx.x - p * groups_per_pair;
+  const int32_t src = pairs[2 * p];
+  const int32_t dst = pairs[2 * p + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  char* pool = blockIdx.y == 0 ? key_cache : value_cache;
+  const char* s = pool + static_cast<int64_t>(src) * chunks_per_block * 16;
+  char* d = pool + static_cast<int64_t>(dst) * chunks_per_block * 16;
+  constexpr int kUnroll = 4;
+  const int64_t stride = static_cast<int64_t>(groups_per_pair) * blockDim.x;
+  int64_t i = static_cast<int64_t>(grp) * blockDim.x + threadIdx.x;
+  for (; i + (kUnroll - 1) * stride < chunks_per_block; i += kUnroll * stride) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = load16(s + (i + u * stride) * 16);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) store16(d + (i + u * stride) * 16, v[u]);
+  }
+  for (; i < chunks_per_block; i += stride) store16(d + i * 16, load16(s + i * 16));
+}
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                                    void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                                    int32_t num_blocks, int32_t num_kv_heads, int32_t row_bytes,
+                                    int32_t block_size, hipStream_t stream) {
+  const int32_t cpr = row_bytes / 16;
+  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * cpr;
+  if (total == 0) return hipSuccess;
+  const int64_t grid = (total + 255) / 256;
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream,
+                     static_cast<const char*>(key), static_cast<const char*>(value),
+                     static_cast<char*>(key_cache), static_cast<char*>(value_cache), slot_mapping,
+                     num_tokens, static_cast<int64_t>(num_blocks) * block_size, num_kv_heads, cpr,
+                     block_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
+                              int32_t num_pairs, int32_t num_blocks, int64_t block_bytes,
+                              hipStream_t stream) {
+  if (num_pairs == 0) return hipSuccess;
+  const int64_t chunks = block_bytes / 16;
+  // about 4 chunks per thread per workgroup pass; at least one workgroup
+  int64_t gx = (chunks + 1023) / 1024;
+  if (gx < 1) gx = 1;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<uint32_t>(gx * num_pairs), 2), dim3(256), 0,
+                     stream, static_cast<char*>(key_cache), static_cast<char*>(value_cache), pairs,
+                     num_blocks, chunks, static_cast<int32_t>(gx));
+  return hipGetLastError();
+}
+
+}  // namespace pa

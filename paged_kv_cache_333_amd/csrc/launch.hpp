@@ -1,0 +1,47 @@
+// Internal interface between the C ABI layer (api.cpp) and the kernel
+// launchers.  Arguments reaching these functions have been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+struct DecodeArgs {
+  void* out;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_seqs, num_heads, num_kv_heads, head_dim, block_size;
+  int32_t max_blocks_per_seq, num_blocks, max_context_len;
+  float scale;
+  pa_dtype dtype;
+};
+
+// The three fp32 arrays of the split workspace (see pa_decode_split_workspace_bytes).
+struct SplitLayout {
+  float* m;
+  float* l;
+  float* o;
+  int32_t partition_size;
+  int32_t num_parts;
+};
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                                    void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                                    int32_t num_blocks, int32_t num_kv_heads, int32_t row_bytes,
+                                    int32_t block_size, hipStream_t stream);
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
+                              int32_t num_pairs, int32_t num_blocks, int64_t block_bytes,
+                              hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_split(const DecodeArgs& a, const SplitLayout& ws, hipStream_t stream);
+hipError_t launch_lse_reduce(void* out, const SplitLayout& ws, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t len_limit,
+                             pa_dtype dtype, hipStream_t stream);
+
+}  // namespace pa

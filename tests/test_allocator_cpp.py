@@ -1,0 +1,147 @@
+"""The C++ allocator behind the C ABI equals the oracle allocator bit for bit:
+tables, lengths, refcounts, free-queue order, slots, copy pairs, statistics and
+error codes, over the pages' examples and long random operation sequences."""
+import numpy as np
+import pytest
+
+import paged_kv_cache_333_amd as pa
+from oracle import allocator as AL
+from tests import oracle_pins as P
+
+CODE = {"PA_ERR_NO_FREE_BLOCKS": AL.NO_FREE_BLOCKS, "PA_ERR_UNKNOWN_SEQ": AL.UNKNOWN_SEQ,
+        "PA_ERR_SEQ_EXISTS": AL.SEQ_EXISTS, "PA_ERR_INVALID_ARG": AL.INVALID_ARG}
+
+
+def same_state(cpp, ora):
+    assert cpp.free_list() == ora.free_list()
+    assert [cpp.ref_count(b) for b in range(ora.num_blocks)] == ora.refs
+    for s in ora.tables:
+        assert cpp.block_table(s) == ora.tables[s]
+        assert cpp.seq_len(s) == ora.lens[s]
+    assert cpp.stats() == ora.stats
+
+
+def both(cpp_fn, ora_fn):
+    err_c = err_o = None
+    try:
+        rc = cpp_fn()
+    except pa.PAError as e:
+        err_c = CODE[e.code]
+    try:
+        ro = ora_fn()
+    except AL.AllocatorError as e:
+        err_o = e.code
+    assert err_c == err_o
+    if err_c is None:
+        assert rc == ro
+    return err_c
+
+
+class _Shim:
+    """Routes the oracle-pin checks to the C++ allocator."""
+
+    def __init__(self, num_blocks, block_size, initial_free_order=None):
+        self._a = pa.Allocator(num_blocks, block_size, initial_free_order)
+        self._ids = {}
+        self.num_blocks = num_blocks
+
+    def _id(self, s):
+        return self._ids.setdefault(s, len(self._ids) + 1) if isinstance(s, str) else s
+
+    def seq_create(self, s, n): self._a.seq_create(self._id(s), n)
+    def seq_fork(self, p, c, n=-1): self._a.seq_fork(self._id(p), self._id(c), n)
+    def seq_append_slot(self, s): return self._a.seq_append_slot(self._id(s))
+    def seq_free(self, s): self._a.seq_free(self._id(s))
+    def block_table(self, s): return self._a.block_table(self._id(s))
+    def free_list(self): return self._a.free_list()
+    def ref_count(self, b): return self._a.ref_count(b)
+    def num_free_blocks(self): return self._a.num_free_blocks()
+
+
+@pytest.mark.parametrize("check", [P.check_p1_block_mapping, P.check_block_counts, P.check_addressing,
+                                   P.check_p4_cow_timeline, P.check_p2_lifecycle])
+def test_page_examples_on_cpp(monkeypatch, check):
+    monkeypatch.setattr(AL, "BlockAllocator", _Shim)
+    check()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_ops_bit_exact(seed):
+    rng = np.random.default_rng(seed)
+    NB = int(rng.integers(8, 200))
+    bs = int(rng.choice([4, 8, 16, 32]))
+    order = rng.permutation(NB) if seed % 2 else None
+    cpp = pa.Allocator(NB, bs, order)
+    ora = AL.BlockAllocator(NB, bs, order)
+    live, nxt = [], 0
+    for step in range(1500):
+        op = int(rng.integers(0, 7))
+        if op == 0 or not live:
+            n = int(rng.integers(0, 5 * bs))
+            if both(lambda: cpp.seq_create(nxt, n), lambda: ora.seq_create(nxt, n)) is None:
+                live.append(nxt)
+            nxt += 1
+        elif op == 1:
+            p = live[int(rng.integers(len(live)))]
+            n = int(rng.integers(-1, ora.lens[p] + 2))
+            if both(lambda: cpp.seq_fork(p, nxt, n), lambda: ora.seq_fork(p, nxt, n)) is None:
+                live.append(nxt)
+            nxt += 1
+        elif op in (2, 3):
+            s = live[int(rng.integers(len(live)))]
+            both(lambda: cpp.seq_append_slot(s), lambda: ora.seq_append_slot(s))
+        elif op == 4:
+            ids = [live[i] for i in rng.integers(0, len(live), size=int(rng.integers(1, 8)))]
+            both(lambda: cpp.seq_append_slots(ids), lambda: ora.seq_append_slots(ids))
+        elif op == 5:
+            s = live.pop(int(rng.integers(len(live))))
+            both(lambda: cpp.seq_free(s), lambda: ora.seq_free(s))
+        else:
+            bad = nxt + 1000
+            both(lambda: cpp.seq_append_slot(bad), lambda: ora.seq_append_slot(bad))
+        if step % 25 == 0:
+            same_state(cpp, ora)
+            if live:
+                mb = max(len(ora.tables[s]) for s in live) + 2
+                assert cpp.build_block_tables(live, mb) == ora.build_block_tables(live, mb)
+    same_state(cpp, ora)
+    c2, o2 = cpp.clone(), ora.clone()
+    same_state(c2, o2)
+
+
+def test_parallel_sampling_cow_batch_matches_oracle():
+    # a parent of 2304 tokens, 5 branches forked at 2048 + s, parent freed; one batched step
+    rng = np.random.default_rng(5)
+    NB, bs = 400, 16
+    order = rng.permutation(NB)
+    cpp, ora = pa.Allocator(NB, bs, order), AL.BlockAllocator(NB, bs, order)
+    for al in (cpp, ora):
+        for g in range(2):
+            al.seq_create(1000 + g, 2304)
+            for b in range(5):
+                al.seq_fork(1000 + g, 5 * g + b, 2048 + int([0, 7, 7, 255, 256][b]))
+            al.seq_free(1000 + g)
+    ids = list(range(10))
+    rc, ro = cpp.seq_append_slots(ids), ora.seq_append_slots(ids)
+    assert rc == ro
+    assert len(ro[1]) > 0
+    same_state(cpp, ora)
+
+
+def test_batch_exhaustion_rolls_back():
+    for al in (pa.Allocator(3, 4), AL.BlockAllocator(3, 4)):
+        al.seq_create(1, 4)
+        al.seq_create(2, 4)
+        before = (al.free_list(), [al.ref_count(b) for b in range(3)], al.block_table(1), al.block_table(2))
+        with pytest.raises((pa.PAError, AL.AllocatorError)):
+            al.seq_append_slots([1, 2])     # two fresh blocks needed, one free
+        after = (al.free_list(), [al.ref_count(b) for b in range(3)], al.block_table(1), al.block_table(2))
+        assert before == after
+        assert al.seq_len(1) == 4
+
+
+def test_create_rejects_bad_free_order():
+    with pytest.raises(pa.PAError):
+        pa.Allocator(3, 16, [0, 0, 1])
+    with pytest.raises(pa.PAError):
+        pa.Allocator(3, 16, [0, 1, 3])
