@@ -20,7 +20,34 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_333_amd.build`")
+
+# torch ships its own HIP runtime.  Loading torch first makes the dynamic
+# linker satisfy libpa.so's libamdhip64.so.7 / libhsa-runtime64.so.1 with the
+# copies torch already mapped (same sonames), so torch's device memory and
+# streams and libpa.so's kernels live in one runtime.
+try:
+    import torch as _torch_runtime  # noqa: F401
+except ImportError:  # plain C use: libpa.so binds to the system runtime
+    _torch_runtime = None
 lib = C.CDLL(LIB_PATH)
+
+
+def _hip_runtimes_mapped():
+    paths = set()
+    try:
+        with open("/proc/self/maps", encoding="utf-8") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return sorted(paths)
+
+
+_RUNTIMES = _hip_runtimes_mapped()
+if len(_RUNTIMES) > 1:
+    raise ImportError("two HIP runtimes are mapped in this process (" + ", ".join(_RUNTIMES) + "); "
+                      "import torch before anything that loads another libamdhip64")
 
 PA_OK = 0
 STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_NO_FREE_BLOCKS", 3: "PA_ERR_UNKNOWN_SEQ",

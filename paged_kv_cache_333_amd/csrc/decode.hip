@@ -71,7 +71,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams a) {
   constexpr float kNegInf = -__builtin_huge_valf();
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform: keeps the block loop and the table lookups in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane / LPR;
   const int c = lane - r * LPR;
   const int groups = a.num_heads / GT;

@@ -33,15 +33,22 @@ __device__ __forceinline__ void store16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
 
+// Word i of a chunk as a scalar.  (Bit-casting a vector element in place is
+// not reliable: the element must be copied out first.)
+__device__ __forceinline__ uint32_t word(u32x4 w, int i) {
+  const uint32_t x = w[i];
+  return x;
+}
+
 // Unpack a 16-byte chunk into EPL floats (exact conversions).
 __device__ __forceinline__ void to_float(TF32, u32x4 w, float* f) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f[i] = __builtin_bit_cast(float, w[i]);
+  for (int i = 0; i < 4; ++i) f[i] = __builtin_bit_cast(float, word(w, i));
 }
 __device__ __forceinline__ void to_float(TF16, u32x4 w, float* f) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    f16x2 h = __builtin_bit_cast(f16x2, w[i]);
+    const f16x2 h = __builtin_bit_cast(f16x2, word(w, i));
     f[2 * i] = static_cast<float>(h[0]);
     f[2 * i + 1] = static_cast<float>(h[1]);
   }
@@ -49,8 +56,9 @@ __device__ __forceinline__ void to_float(TF16, u32x4 w, float* f) {
 __device__ __forceinline__ void to_float(TBF16, u32x4 w, float* f) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
-    f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+    const uint32_t x = word(w, i);
+    f[2 * i] = __builtin_bit_cast(float, x << 16);
+    f[2 * i + 1] = __builtin_bit_cast(float, x & 0xffff0000u);
   }
 }
 
@@ -60,23 +68,23 @@ __device__ __forceinline__ float dot16(TF32, u32x4 a, u32x4 b) {
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    s = __builtin_fmaf(__builtin_bit_cast(float, a[i]), __builtin_bit_cast(float, b[i]), s);
+    s = __builtin_fmaf(__builtin_bit_cast(float, word(a, i)), __builtin_bit_cast(float, word(b, i)), s);
   return s;
 }
 __device__ __forceinline__ float dot16(TF16, u32x4 a, u32x4 b) {
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a[i]), __builtin_bit_cast(f16x2, b[i]), s,
-                               false);
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, word(a, i)), __builtin_bit_cast(f16x2, word(b, i)),
+                               s, false);
   return s;
 }
 __device__ __forceinline__ float dot16(TBF16, u32x4 a, u32x4 b) {
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a[i]),
-                                        __builtin_bit_cast(bf16x2, b[i]), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word(a, i)),
+                                        __builtin_bit_cast(bf16x2, word(b, i)), s, false);
   return s;
 }
 

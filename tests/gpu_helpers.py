@@ -26,7 +26,7 @@ def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what=""):
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
     err = np.abs(gpu - ref)
-    tol = tolerance(ref, dtype)
+    tol = np.broadcast_to(tolerance(ref, dtype), err.shape)
     worst = np.unravel_index(np.argmax(err - tol), err.shape)
     assert np.all(err <= tol), f"{what}: max err {err.max():.3g} at {worst} (tol {tol[worst]:.3g})"
     return float(err.max())
