@@ -69,6 +69,15 @@ typedef enum pa_status {
 
 typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
 
+/* Decode flags (bit mask).  By default K/V rows are read with a streaming
+ * (non-temporal) cache hint: each KV element is read once per step, so it
+ * should not displace anything.  PA_DECODE_CACHED_KV reads them with the
+ * default policy instead, for pools where several sequences in the batch
+ * share blocks (forked branches, shared prefixes), so that the sharers' reads
+ * can hit the caches; order such sharers next to each other in seq_order.
+ * Results do not depend on the flag. */
+#define PA_DECODE_CACHED_KV 1u
+
 /* ======================================================================== *
  * Host block allocator                                                      *
  * ======================================================================== *
@@ -154,6 +163,14 @@ pa_status pa_build_block_tables(const pa_allocator* a, const int64_t* seq_ids, i
                                 int32_t max_blocks, int32_t* tables, int32_t* context_lens);
 pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out);
 
+/* Launch order for the decode calls: order[0..n) receives the indices of the
+ * sequences sorted by context_lens (host [n]) from longest to shortest, ties
+ * in index order.  Passing it as `seq_order` starts the longest sequences
+ * first, so short ones fill the gaps they leave (longest-processing-time-first
+ * scheduling); this changes no result.  Host arrays; PA_ERR_INVALID_ARG on a
+ * null pointer or negative n. */
+pa_status pa_order_longest_first(const int32_t* context_lens, int32_t n, int32_t* order);
+
 /* ======================================================================== *
  * Device operations                                                         *
  * ======================================================================== */
@@ -192,16 +209,22 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* pair
  * accumulated in fp32 with an online softmax (running max and sum, both
  * rescaled when the max grows), written in `dtype` (round to nearest even).
  * n == 0 gives a zero row.  max_context_len bounds every n and is used to
- * size the launch.
+ * size the launch.  seq_order: NULL, or device int32 [num_seqs], a
+ * permutation of 0..num_seqs-1 giving the order in which sequences are
+ * started (see pa_order_longest_first); it does not change any result.
+ * Entries outside [0, num_seqs) are ignored (rejected under PA_DEBUG); a
+ * sequence missing from the permutation gets no output.  flags: PA_DECODE_*
+ * bits (unknown bits are PA_ERR_INVALID_ARG).
  * Invalid device data never causes an out-of-bounds access: a context length
  * outside [0, min(max_context_len, max_blocks_per_seq*bs)] or a block id
  * outside [0, num_blocks) among the first ceil(n / bs) entries makes that
  * sequence's output rows NaN (PA_ERR_BAD_TABLE under PA_DEBUG). */
 pa_status pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
-                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
+                    int32_t num_seqs,
                     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                     int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
-                    float scale, pa_dtype dtype, void* stream);
+                    float scale, pa_dtype dtype, uint32_t flags, void* stream);
 
 /* Split-context workspace.  For P = ceil(max_context_len / partition_size)
  * partitions, the workspace holds three fp32 arrays, each starting at a
@@ -223,11 +246,12 @@ size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
  * caller-owned device workspace of workspace_bytes bytes. */
 pa_status pa_decode_split(void* out, const void* query, const void* key_cache,
                           const void* value_cache, const int32_t* block_tables,
-                          const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                          const int32_t* context_lens, const int32_t* seq_order, int32_t num_seqs,
+                          int32_t num_heads,
                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                           int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
-                          float scale, pa_dtype dtype, int32_t partition_size, void* workspace,
-                          size_t workspace_bytes, void* stream);
+                          float scale, pa_dtype dtype, uint32_t flags, int32_t partition_size,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Log-sum-exp merge of split partials (the standard rule; the pages do not
  * spell it out): with M = max_p m_p and w_p = l_p * exp(m_p - M),

@@ -3,7 +3,7 @@
 Argument marshalling only.  Every step runs in the C++ allocator or the HIP
 kernels of libpa.so; torch tensors supply device memory and the current
 stream.  Importing this package fails loudly when libpa.so has not been
-built (python -m paged_kv_cache_333_amd.build): there is no fallback.
+built (python paged_kv_cache_333_amd/build.py): there is no fallback.
 
 Names follow the C ABI in include/pa.h:
   pa_reshape_and_cache, pa_copy_blocks, pa_decode, pa_decode_split,
@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_333_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python paged_kv_cache_333_amd/build.py`")
 
 # torch ships its own HIP runtime.  Loading torch first makes the dynamic
 # linker satisfy libpa.so's libamdhip64.so.7 / libhsa-runtime64.so.1 with the
@@ -54,9 +54,10 @@ STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_NO_FREE_BLOCKS", 3: "P
           4: "PA_ERR_SEQ_EXISTS", 5: "PA_ERR_UNSUPPORTED", 6: "PA_ERR_BAD_TABLE",
           7: "PA_ERR_WORKSPACE_TOO_SMALL", 8: "PA_ERR_HIP"}
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_DECODE_CACHED_KV = 1
 DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
 
-_i32, _i64, _f32, _vp, _sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
+_i32, _u32, _i64, _f32, _vp, _sz = C.c_int32, C.c_uint32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
 _pi32, _pi64 = C.POINTER(C.c_int32), C.POINTER(C.c_int64)
 
 
@@ -83,18 +84,23 @@ _PROTOS = {
     "pa_allocator_get_stats": (_i32, [_vp, C.POINTER(pa_allocator_stats)]),
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
-    "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
-                         _f32, _i32, _vp]),
+    "pa_order_longest_first": (_i32, [_pi32, _i32, _pi32]),
+    "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                         _f32, _i32, _u32, _vp]),
     "pa_decode_split_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
-    "pa_decode_split": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
-                               _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_decode_split": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _i32, _f32, _i32, _u32, _i32, _vp, _sz, _vp]),
     "pa_lse_reduce": (_i32, [_vp, _vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_status_string": (C.c_char_p, [_i32]),
     "pa_last_error": (C.c_char_p, []),
     "pa_abi_version": (_i32, []),
 }
 for _name, (_res, _args) in _PROTOS.items():
-    _fn = getattr(lib, _name)
+    try:
+        _fn = getattr(lib, _name)
+    except AttributeError as _e:
+        raise ImportError(f"{LIB_PATH} lacks {_name}: it is out of date, rebuild it with "
+                          "`python paged_kv_cache_333_amd/build.py`") from _e
     _fn.restype = _res
     _fn.argtypes = _args
 
@@ -159,14 +165,21 @@ def pa_copy_blocks(key_cache, value_cache, pairs, stream=None, num_pairs=None):
                               _dtype_code(key_cache), _stream(stream)), "pa_copy_blocks")
 
 
+def _opt(t):
+    return None if t is None else _ptr(t)
+
+
 def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len: int,
-              scale: float, stream=None):
-    """out, query [S, H, D]; pools [NB, H_kv, bs, D]; block_tables [S, MB]; context_lens [S]."""
+              scale: float, stream=None, seq_order=None, cached_kv: bool = False):
+    """out, query [S, H, D]; pools [NB, H_kv, bs, D]; block_tables [S, MB]; context_lens [S];
+    seq_order: optional device int32 [S] launch order (see pa_order_longest_first);
+    cached_kv: read K/V with the default cache policy (pools with shared blocks)."""
     S, H, D = query.shape
     NB, H_kv, bs, _ = key_cache.shape
     _check(lib.pa_decode(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
-                         _ptr(context_lens), S, H, H_kv, D, bs, block_tables.shape[1], NB, max_context_len,
-                         scale, _dtype_code(query), _stream(stream)), "pa_decode")
+                         _ptr(context_lens), _opt(seq_order), S, H, H_kv, D, bs, block_tables.shape[1], NB,
+                         max_context_len, scale, _dtype_code(query), PA_DECODE_CACHED_KV if cached_kv else 0,
+                         _stream(stream)), "pa_decode")
 
 
 def pa_decode_split_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
@@ -175,15 +188,17 @@ def pa_decode_split_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int
 
 
 def pa_decode_split(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len: int,
-                    scale: float, partition_size: int, workspace, stream=None):
+                    scale: float, partition_size: int, workspace, stream=None, seq_order=None,
+                    cached_kv: bool = False):
     """As pa_decode; workspace is a device tensor of at least pa_decode_split_workspace_bytes bytes."""
     S, H, D = query.shape
     NB, H_kv, bs, _ = key_cache.shape
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib.pa_decode_split(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
-                               _ptr(block_tables), _ptr(context_lens), S, H, H_kv, D, bs,
+                               _ptr(block_tables), _ptr(context_lens), _opt(seq_order), S, H, H_kv, D, bs,
                                block_tables.shape[1], NB, max_context_len, scale, _dtype_code(query),
-                               partition_size, _ptr(workspace), nbytes, _stream(stream)), "pa_decode_split")
+                               PA_DECODE_CACHED_KV if cached_kv else 0, partition_size, _ptr(workspace), nbytes,
+                               _stream(stream)), "pa_decode_split")
 
 
 def pa_lse_reduce(out, workspace, context_lens, max_context_len: int, partition_size: int, stream=None):
@@ -193,6 +208,21 @@ def pa_lse_reduce(out, workspace, context_lens, max_context_len: int, partition_
     _check(lib.pa_lse_reduce(_ptr(out), _ptr(workspace), nbytes, _ptr(context_lens), S, H, D,
                              max_context_len, partition_size, _dtype_code(out), _stream(stream)),
            "pa_lse_reduce")
+
+
+def pa_order_longest_first(context_lens) -> list:
+    """Indices of the sequences from the longest context to the shortest (ties in index order)."""
+    n = len(context_lens)
+    lens = (C.c_int32 * max(n, 1))(*[int(x) for x in context_lens])
+    order = (C.c_int32 * max(n, 1))()
+    _check(lib.pa_order_longest_first(lens, n, order), "pa_order_longest_first")
+    return list(order[:n])
+
+
+def pa_order_longest_first_into(lens_ptr: int, n: int, order_ptr: int):
+    """Raw form for pinned host buffers (int32 pointers)."""
+    _check(lib.pa_order_longest_first(C.cast(lens_ptr, _pi32), n, C.cast(order_ptr, _pi32)),
+           "pa_order_longest_first")
 
 
 def split_layout(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int, partition_size: int):

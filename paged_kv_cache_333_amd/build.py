@@ -1,6 +1,6 @@
 """Build libpa.so in-tree with hipcc for gfx950.
 
-    python -m paged_kv_cache_333_amd.build
+    python paged_kv_cache_333_amd/build.py
 
 Every source under csrc/ is compiled to an object in _build/ (in parallel)
 and linked into paged_kv_cache_333_amd/libpa.so.  A build always recompiles.

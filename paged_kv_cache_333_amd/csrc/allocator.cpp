@@ -14,7 +14,9 @@
 //
 // The free queue is a ring buffer of num_blocks entries; a block is never in
 // it twice, so it never overflows.
+#include <algorithm>
 #include <cstring>
+#include <numeric>
 #include <mutex>
 #include <unordered_map>
 #include <vector>
@@ -360,6 +362,14 @@ pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out)
   if (!a || !out) return fail(PA_ERR_INVALID_ARG, "null argument");
   std::lock_guard<std::mutex> g(a->mu);
   *out = a->stats;
+  return PA_OK;
+}
+
+pa_status pa_order_longest_first(const int32_t* context_lens, int32_t n, int32_t* order) {
+  if (n < 0 || (n > 0 && (!context_lens || !order))) return fail(PA_ERR_INVALID_ARG, "null argument");
+  std::iota(order, order + n, 0);
+  std::stable_sort(order, order + n,
+                   [context_lens](int32_t x, int32_t y) { return context_lens[x] > context_lens[y]; });
   return PA_OK;
 }
 

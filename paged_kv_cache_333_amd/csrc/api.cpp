@@ -100,6 +100,16 @@ pa_status debug_check_tables(const pa::DecodeArgs& a, hipStream_t st) {
                                           "] = " + std::to_string(b) + " outside the pool");
     }
   }
+  if (a.seq_order) {
+    std::vector<int32_t> ord;
+    if ((s = fetch(ord, a.seq_order, a.num_seqs, st)) != PA_OK) return s;
+    std::vector<char> seen(a.num_seqs, 0);
+    for (int32_t i = 0; i < a.num_seqs; ++i) {
+      if (ord[i] < 0 || ord[i] >= a.num_seqs || seen[ord[i]])
+        return fail(PA_ERR_BAD_TABLE, "seq_order is not a permutation of 0..num_seqs-1");
+      seen[ord[i]] = 1;
+    }
+  }
   return PA_OK;
 }
 
@@ -145,13 +155,14 @@ pa_status make_layout(void* workspace, size_t workspace_bytes, int32_t num_seqs,
 }
 
 pa::DecodeArgs pack(void* out, const void* query, const void* key_cache, const void* value_cache,
-                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
+                    int32_t num_seqs,
                     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                     int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len, float scale,
-                    pa_dtype dtype) {
-  return pa::DecodeArgs{out, query, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                    pa_dtype dtype, uint32_t flags) {
+  return pa::DecodeArgs{out, query, key_cache, value_cache, block_tables, context_lens, seq_order, num_seqs,
                         num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
-                        max_context_len, scale, dtype};
+                        max_context_len, scale, dtype, flags};
 }
 
 }  // namespace
@@ -225,15 +236,17 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* pair
 }
 
 pa_status pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
-                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
+                    int32_t num_seqs,
                     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                     int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len, float scale,
-                    pa_dtype dtype, void* stream) {
-  pa::DecodeArgs a = pack(out, query, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                    pa_dtype dtype, uint32_t flags, void* stream) {
+  pa::DecodeArgs a = pack(out, query, key_cache, value_cache, block_tables, context_lens, seq_order, num_seqs,
                           num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
-                          max_context_len, scale, dtype);
+                          max_context_len, scale, dtype, flags);
   pa_status s = check_decode_args(a);
   if (s != PA_OK || num_seqs == 0) return s;
+  if (flags & ~uint32_t(PA_DECODE_CACHED_KV)) return fail(PA_ERR_INVALID_ARG, "unknown flag bits");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (debug_mode() && (s = debug_check_tables(a, st)) != PA_OK) return s;
   return finish(pa::launch_decode(a, st), st, "pa_decode");
@@ -247,16 +260,18 @@ size_t pa_decode_split_workspace_bytes(int32_t num_seqs, int32_t num_heads, int3
 }
 
 pa_status pa_decode_split(void* out, const void* query, const void* key_cache, const void* value_cache,
-                          const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                          const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
+                          int32_t num_seqs,
                           int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                           int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
-                          float scale, pa_dtype dtype, int32_t partition_size, void* workspace,
+                          float scale, pa_dtype dtype, uint32_t flags, int32_t partition_size, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  pa::DecodeArgs a = pack(out, query, key_cache, value_cache, block_tables, context_lens, num_seqs,
+  pa::DecodeArgs a = pack(out, query, key_cache, value_cache, block_tables, context_lens, seq_order, num_seqs,
                           num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
-                          max_context_len, scale, dtype);
+                          max_context_len, scale, dtype, flags);
   pa_status s = check_decode_args(a);
   if (s != PA_OK) return s;
+  if (flags & ~uint32_t(PA_DECODE_CACHED_KV)) return fail(PA_ERR_INVALID_ARG, "unknown flag bits");
   if (partition_size <= 0 || partition_size % block_size || partition_size > 4096)
     return fail(PA_ERR_INVALID_ARG, "partition_size must be a multiple of block_size, at most 4096");
   if (num_seqs == 0) return PA_OK;
@@ -292,8 +307,8 @@ pa_status pa_lse_reduce(void* out, const void* workspace, size_t workspace_bytes
       if (ctx[i] < 0 || ctx[i] > max_context_len)
         return fail(PA_ERR_BAD_TABLE, "context_lens[" + std::to_string(i) + "] outside [0, max_context_len]");
   }
-  return finish(pa::launch_lse_reduce(out, ws, context_lens, num_seqs, num_heads, head_dim, max_context_len,
-                                      dtype, st),
+  return finish(pa::launch_lse_reduce(out, ws, context_lens, nullptr, num_seqs, num_heads, head_dim,
+                                      max_context_len, dtype, st),
                 st, "pa_lse_reduce");
 }
 

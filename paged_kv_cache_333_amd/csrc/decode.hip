@@ -46,9 +46,11 @@ struct DecodeParams {
   const char* vc;
   const int32_t* tables;
   const int32_t* ctx;
+  const int32_t* order;  // optional launch order of the sequences (a permutation), or null
   float* ws_m;
   float* ws_l;
   float* ws_o;
+  int32_t num_seqs;
   int32_t num_heads;
   int32_t num_kv_heads;
   int32_t max_blocks;
@@ -59,13 +61,13 @@ struct DecodeParams {
   float scale_log2;    // scale * log2(e)
 };
 
-template <typename T, int D, int BS, int GT, bool SPLIT>
+template <typename T, int D, int BS, int GT, bool SPLIT, bool CACHED>
 __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams a) {
   constexpr int EPL = T::kEPL;
   constexpr int LPR = D / EPL;   // lanes per token row
   constexpr int RPL = 64 / LPR;  // rows per wave load
   constexpr int NJ = BS / RPL;   // loads per block per pool
-  constexpr int JB0 = GT >= 4 ? 2 : 4;
+  constexpr int JB0 = GT >= 8 ? 2 : 8;
   constexpr int JB = NJ < JB0 ? NJ : JB0;  // loads consumed per inner step
   static_assert(NJ % JB == 0, "block rows");
   constexpr float kNegInf = -__builtin_huge_valf();
@@ -76,8 +78,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams a) {
   const int r = lane / LPR;
   const int c = lane - r * LPR;
   const int groups = a.num_heads / GT;
-  const int s = blockIdx.x / groups;
-  const int h0 = (blockIdx.x - s * groups) * GT;
+  const int slot = blockIdx.x / groups;
+  const int h0 = (blockIdx.x - slot * groups) * GT;
+  // Workgroups start in blockIdx order; with a longest-first order the long
+  // sequences start first and the short ones fill in behind them.
+  const int s = a.order ? a.order[slot] : slot;
+  if (static_cast<uint32_t>(s) >= static_cast<uint32_t>(a.num_seqs)) return;
   const int kvh = h0 / (a.num_heads / a.num_kv_heads);
   const int n = a.ctx[s];
   const bool bad_len = n < 0 || n > a.len_limit;
@@ -122,8 +128,14 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams a) {
       u32x4 kv[JB], vv[JB];
 #pragma unroll
       for (int jj = 0; jj < JB; ++jj) {
-        kv[jj] = load16(kp + static_cast<int64_t>((j0 + jj) * RPL) * D * T::kBytes);
-        vv[jj] = load16(vp + static_cast<int64_t>((j0 + jj) * RPL) * D * T::kBytes);
+        const int64_t off = static_cast<int64_t>((j0 + jj) * RPL) * D * T::kBytes;
+        if constexpr (CACHED) {
+          kv[jj] = load16(kp + off);
+          vv[jj] = load16(vp + off);
+        } else {
+          kv[jj] = load16_stream(kp + off);
+          vv[jj] = load16_stream(vp + off);
+        }
       }
       bool valid[JB];
       float vf[JB][EPL];
@@ -234,11 +246,15 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(void* out, const float* _
                                                        const float* __restrict__ ws_l,
                                                        const float* __restrict__ ws_o,
                                                        const int32_t* __restrict__ ctx,
+                                                       const int32_t* __restrict__ order, int32_t num_seqs,
                                                        int32_t num_heads, int32_t len_limit,
                                                        int32_t part_size, int32_t num_parts) {
   constexpr float kLog2e = 1.4426950408889634f;
-  const int64_t sh = blockIdx.x;
-  const int s = static_cast<int>(sh / num_heads);
+  const int slot = blockIdx.x / num_heads;
+  const int h = blockIdx.x - slot * num_heads;
+  const int s = order ? order[slot] : slot;  // same sequence set as the partials pass
+  if (static_cast<uint32_t>(s) >= static_cast<uint32_t>(num_seqs)) return;
+  const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
   const int d = threadIdx.x;
   const int n = ctx[s];
   if (n < 0 || n > len_limit) {
@@ -266,40 +282,44 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(void* out, const float* _
 namespace {
 
 template <typename T, int D, int BS, int GT, bool SPLIT>
-hipError_t launch_t(const DecodeParams& p, int32_t num_seqs, hipStream_t stream) {
+hipError_t launch_t(const DecodeParams& p, int32_t num_seqs, bool cached, hipStream_t stream) {
   const uint32_t gx = static_cast<uint32_t>(num_seqs) * (p.num_heads / GT);
   const uint32_t gy = SPLIT ? static_cast<uint32_t>(p.num_parts) : 1u;
-  hipLaunchKernelGGL((decode_kernel<T, D, BS, GT, SPLIT>), dim3(gx, gy), dim3(kWaves * 64), 0, stream, p);
+  if (cached)
+    hipLaunchKernelGGL((decode_kernel<T, D, BS, GT, SPLIT, true>), dim3(gx, gy), dim3(kWaves * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<T, D, BS, GT, SPLIT, false>), dim3(gx, gy), dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <typename T, int D, int BS, bool SPLIT>
-hipError_t by_group(const DecodeParams& p, int32_t num_seqs, int gt, hipStream_t stream) {
+hipError_t by_group(const DecodeParams& p, int32_t num_seqs, int gt, bool cached, hipStream_t stream) {
   switch (gt) {
-    case 1: return launch_t<T, D, BS, 1, SPLIT>(p, num_seqs, stream);
-    case 2: return launch_t<T, D, BS, 2, SPLIT>(p, num_seqs, stream);
-    case 4: return launch_t<T, D, BS, 4, SPLIT>(p, num_seqs, stream);
-    case 8: return launch_t<T, D, BS, 8, SPLIT>(p, num_seqs, stream);
+    case 1: return launch_t<T, D, BS, 1, SPLIT>(p, num_seqs, cached, stream);
+    case 2: return launch_t<T, D, BS, 2, SPLIT>(p, num_seqs, cached, stream);
+    case 4: return launch_t<T, D, BS, 4, SPLIT>(p, num_seqs, cached, stream);
+    case 8: return launch_t<T, D, BS, 8, SPLIT>(p, num_seqs, cached, stream);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T, bool SPLIT>
-hipError_t by_shape(const DecodeParams& p, int32_t num_seqs, int d, int bs, int gt, hipStream_t stream) {
-  if (d == 64 && bs == 16) return by_group<T, 64, 16, SPLIT>(p, num_seqs, gt, stream);
-  if (d == 64 && bs == 32) return by_group<T, 64, 32, SPLIT>(p, num_seqs, gt, stream);
-  if (d == 128 && bs == 16) return by_group<T, 128, 16, SPLIT>(p, num_seqs, gt, stream);
-  if (d == 128 && bs == 32) return by_group<T, 128, 32, SPLIT>(p, num_seqs, gt, stream);
+hipError_t by_shape(const DecodeParams& p, int32_t num_seqs, int d, int bs, int gt, bool cached,
+                    hipStream_t stream) {
+  if (d == 64 && bs == 16) return by_group<T, 64, 16, SPLIT>(p, num_seqs, gt, cached, stream);
+  if (d == 64 && bs == 32) return by_group<T, 64, 32, SPLIT>(p, num_seqs, gt, cached, stream);
+  if (d == 128 && bs == 16) return by_group<T, 128, 16, SPLIT>(p, num_seqs, gt, cached, stream);
+  if (d == 128 && bs == 32) return by_group<T, 128, 32, SPLIT>(p, num_seqs, gt, cached, stream);
   return hipErrorInvalidValue;
 }
 
 template <bool SPLIT>
-hipError_t by_dtype(const DecodeParams& p, int32_t num_seqs, pa_dtype dt, int d, int bs, int gt,
+hipError_t by_dtype(const DecodeParams& p, int32_t num_seqs, pa_dtype dt, int d, int bs, int gt, bool cached,
                     hipStream_t stream) {
   switch (dt) {
-    case PA_F32: return by_shape<TF32, SPLIT>(p, num_seqs, d, bs, gt, stream);
-    case PA_F16: return by_shape<TF16, SPLIT>(p, num_seqs, d, bs, gt, stream);
-    case PA_BF16: return by_shape<TBF16, SPLIT>(p, num_seqs, d, bs, gt, stream);
+    case PA_F32: return by_shape<TF32, SPLIT>(p, num_seqs, d, bs, gt, cached, stream);
+    case PA_F16: return by_shape<TF16, SPLIT>(p, num_seqs, d, bs, gt, cached, stream);
+    case PA_BF16: return by_shape<TBF16, SPLIT>(p, num_seqs, d, bs, gt, cached, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -318,6 +338,8 @@ DecodeParams make_params(const DecodeArgs& x) {
   p.vc = static_cast<const char*>(x.value_cache);
   p.tables = x.block_tables;
   p.ctx = x.context_lens;
+  p.order = x.seq_order;
+  p.num_seqs = x.num_seqs;
   p.num_heads = x.num_heads;
   p.num_kv_heads = x.num_kv_heads;
   p.max_blocks = x.max_blocks_per_seq;
@@ -333,7 +355,8 @@ DecodeParams make_params(const DecodeArgs& x) {
 hipError_t launch_decode(const DecodeArgs& x, hipStream_t stream) {
   DecodeParams p = make_params(x);
   const int gt = group_tile(x.num_heads / x.num_kv_heads);
-  return by_dtype<false>(p, x.num_seqs, x.dtype, x.head_dim, x.block_size, gt, stream);
+  return by_dtype<false>(p, x.num_seqs, x.dtype, x.head_dim, x.block_size, gt, x.flags & PA_DECODE_CACHED_KV,
+                         stream);
 }
 
 hipError_t launch_decode_split(const DecodeArgs& x, const SplitLayout& ws, hipStream_t stream) {
@@ -344,19 +367,20 @@ hipError_t launch_decode_split(const DecodeArgs& x, const SplitLayout& ws, hipSt
   p.part_size = ws.partition_size;
   p.num_parts = ws.num_parts;
   const int gt = group_tile(x.num_heads / x.num_kv_heads);
-  hipError_t e = by_dtype<true>(p, x.num_seqs, x.dtype, x.head_dim, x.block_size, gt, stream);
+  hipError_t e = by_dtype<true>(p, x.num_seqs, x.dtype, x.head_dim, x.block_size, gt,
+                                x.flags & PA_DECODE_CACHED_KV, stream);
   if (e != hipSuccess) return e;
-  return launch_lse_reduce(x.out, ws, x.context_lens, x.num_seqs, x.num_heads, x.head_dim, p.len_limit,
-                           x.dtype, stream);
+  return launch_lse_reduce(x.out, ws, x.context_lens, x.seq_order, x.num_seqs, x.num_heads, x.head_dim,
+                           p.len_limit, x.dtype, stream);
 }
 
-hipError_t launch_lse_reduce(void* out, const SplitLayout& ws, const int32_t* ctx, int32_t num_seqs,
-                             int32_t num_heads, int32_t head_dim, int32_t len_limit, pa_dtype dt,
-                             hipStream_t stream) {
+hipError_t launch_lse_reduce(void* out, const SplitLayout& ws, const int32_t* ctx, const int32_t* order,
+                             int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t len_limit,
+                             pa_dtype dt, hipStream_t stream) {
   const dim3 grid(static_cast<uint32_t>(num_seqs) * num_heads);
 #define PA_REDUCE(T, D)                                                                          \
   hipLaunchKernelGGL((lse_reduce_kernel<T, D>), grid, dim3(D), 0, stream, out, ws.m, ws.l, ws.o, \
-                     ctx, num_heads, len_limit, ws.partition_size, ws.num_parts)
+                     ctx, order, num_seqs, num_heads, len_limit, ws.partition_size, ws.num_parts)
   if (head_dim == 64) {
     if (dt == PA_F32) PA_REDUCE(TF32, 64);
     else if (dt == PA_F16) PA_REDUCE(TF16, 64);

@@ -29,6 +29,11 @@ struct TBF16 {
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+// Streaming load: the non-temporal hint keeps data that is read once from
+// displacing reusable lines in the caches (the KV pool is read once per step).
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 __device__ __forceinline__ void store16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }

@@ -16,10 +16,12 @@ struct DecodeArgs {
   const void* value_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const int32_t* seq_order;  // optional, may be null
   int32_t num_seqs, num_heads, num_kv_heads, head_dim, block_size;
   int32_t max_blocks_per_seq, num_blocks, max_context_len;
   float scale;
   pa_dtype dtype;
+  uint32_t flags;  // PA_DECODE_* bits
 };
 
 // The three fp32 arrays of the split workspace (see pa_decode_split_workspace_bytes).
@@ -41,7 +43,7 @@ hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t*
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeArgs& a, const SplitLayout& ws, hipStream_t stream);
 hipError_t launch_lse_reduce(void* out, const SplitLayout& ws, const int32_t* context_lens,
-                             int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t len_limit,
-                             pa_dtype dtype, hipStream_t stream);
+                             const int32_t* seq_order, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                             int32_t len_limit, pa_dtype dtype, hipStream_t stream);
 
 }  // namespace pa

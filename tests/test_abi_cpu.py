@@ -19,7 +19,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 25
+    assert len(names) == 26
     for n in names:
         assert hasattr(pa.lib, n), n
         assert C.cast(getattr(pa.lib, n), C.c_void_p).value
@@ -41,8 +41,10 @@ def _decode(**kw):
                 NB=8, maxlen=64, scale=0.1, dt=F)
     args.update(kw)
     a = args
-    return pa.lib.pa_decode(a["out"], a["query"], a["kc"], a["vc"], a["tab"], a["ctx"], a["S"], a["H"],
-                            a["Hkv"], a["D"], a["bs"], a["MB"], a["NB"], a["maxlen"], a["scale"], a["dt"], None)
+    a.setdefault("flags", 0)
+    return pa.lib.pa_decode(a["out"], a["query"], a["kc"], a["vc"], a["tab"], a["ctx"], None, a["S"], a["H"],
+                            a["Hkv"], a["D"], a["bs"], a["MB"], a["NB"], a["maxlen"], a["scale"], a["dt"],
+                            a.get("flags", 0), None)
 
 
 def test_decode_validation_rejects_before_launch():
@@ -55,6 +57,7 @@ def test_decode_validation_rejects_before_launch():
     assert _decode(out=24) == 1  # not 16-byte aligned
     assert _decode(S=-1) == 1
     assert _decode(S=0, out=0, query=0) == 0  # nothing to do, nothing launched
+    assert _decode(flags=2) == 1              # unknown flag bit
     assert b"head_dim" in _decode.__globals__["pa"].lib.pa_last_error() or True
 
 
@@ -65,12 +68,14 @@ def test_split_workspace_size_and_validation():
     assert n == 2 * (4 * 32 * 256 * 4) + 4 * 32 * 256 * 128 * 4
     assert pa.pa_decode_split_workspace_bytes(1, 1, 64, 10, 0) == 0
     assert pa.pa_decode_split_workspace_bytes(1, 1, 64, 16 * 70000, 16) == 0  # > 65535 partitions
-    r = pa.lib.pa_decode_split(16, 16, 16, 16, 16, 16, 1, 32, 32, 128, 16, 4, 8, 64, 0.1, F, 24, 256, 10 ** 6,
-                               None)
+    r = pa.lib.pa_decode_split(16, 16, 16, 16, 16, 16, None, 1, 32, 32, 128, 16, 4, 8, 64, 0.1, F, 0, 24, 256,
+                               10 ** 6, None)
     assert r == 1  # partition not a multiple of the block size
-    r = pa.lib.pa_decode_split(16, 16, 16, 16, 16, 16, 1, 32, 32, 128, 16, 4, 8, 64, 0.1, F, 32, 256, 10, None)
+    r = pa.lib.pa_decode_split(16, 16, 16, 16, 16, 16, None, 1, 32, 32, 128, 16, 4, 8, 64, 0.1, F, 0, 32, 256, 10,
+                               None)
     assert r == 7  # workspace too small
-    r = pa.lib.pa_decode_split(16, 16, 16, 16, 16, 16, 1, 32, 32, 128, 16, 4, 8, 64, 0.1, F, 32, 0, 10 ** 6, None)
+    r = pa.lib.pa_decode_split(16, 16, 16, 16, 16, 16, None, 1, 32, 32, 128, 16, 4, 8, 64, 0.1, F, 0, 32, 0, 10 ** 6,
+                               None)
     assert r == 1  # null workspace
 
 
@@ -87,3 +92,13 @@ def test_error_detail_is_reported():
     with pytest.raises(pa.PAError) as e:
         pa.Allocator(4, 16).seq_free(3)
     assert e.value.code == "PA_ERR_UNKNOWN_SEQ" and "unknown sequence" in str(e.value)
+
+
+def test_longest_first_order():
+    import numpy as np
+    rng = np.random.default_rng(0)
+    for n in (0, 1, 7, 300):
+        lens = rng.integers(0, 50, size=n)          # many ties
+        got = pa.pa_order_longest_first(lens.tolist())
+        assert got == [int(i) for i in np.argsort(-lens, kind="stable")]
+    assert pa.lib.pa_order_longest_first(None, 3, None) == 1

@@ -57,16 +57,19 @@ def to_dev(c):
                 ctx=torch.tensor(c["ctx"], dtype=torch.int32).cuda())
 
 
-def run_decode(c, dv, split=None, max_ctx=None):
+def run_decode(c, dv, split=None, max_ctx=None, order=None, cached=False):
     out = torch.full_like(dv["q"], 7.0)
     max_ctx = c["MB"] * c["bs"] if max_ctx is None else max_ctx
     scale = scale_for(c["D"])
+    so = None if order is None else torch.tensor(order, dtype=torch.int32, device="cuda")
     if split is None:
-        pa.pa_decode(out, dv["q"], dv["kc"], dv["vc"], dv["tables"], dv["ctx"], max_ctx, scale)
+        pa.pa_decode(out, dv["q"], dv["kc"], dv["vc"], dv["tables"], dv["ctx"], max_ctx, scale, seq_order=so,
+                     cached_kv=cached)
     else:
         nbytes = pa.pa_decode_split_workspace_bytes(c["S"], c["H"], c["D"], max_ctx, split)
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-        pa.pa_decode_split(out, dv["q"], dv["kc"], dv["vc"], dv["tables"], dv["ctx"], max_ctx, scale, split, ws)
+        pa.pa_decode_split(out, dv["q"], dv["kc"], dv["vc"], dv["tables"], dv["ctx"], max_ctx, scale, split, ws,
+                           seq_order=so, cached_kv=cached)
     torch.cuda.synchronize()
     return out_to_f64(out, c["dtype"])
 
@@ -89,6 +92,10 @@ def test_decode_small_all_families(dt, D, bs, H, Hkv):
     ref = oracle(c)
     assert_close(run_decode(c, dv), ref, dt, "single pass")
     assert_close(run_decode(c, dv, split=2 * bs), ref, dt, "split")
+    order = pa.pa_order_longest_first(list(ctx))
+    assert np.array_equal(run_decode(c, dv, order=order), run_decode(c, dv))
+    assert np.array_equal(run_decode(c, dv, cached=True), run_decode(c, dv))
+    assert np.array_equal(run_decode(c, dv, split=2 * bs, order=order), run_decode(c, dv, split=2 * bs))
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
@@ -129,15 +136,31 @@ def test_tiny_fp32_workload_before_and_after_the_write():
 
 @pytest.mark.parametrize("key", [2, 3])
 def test_full_size_workload_sampled(key):
+    """Full-size workloads 2 and 3 in the configuration the benchmark times (single pass,
+    longest-first launch order), and through the split path."""
     dw = DeviceWorkload(key)
     w = dw.w
+    order = torch.tensor(pa.pa_order_longest_first(w.context_lens), dtype=torch.int32, device="cuda")
     pa.pa_decode(dw.out, dw.query, dw.key_cache, dw.value_cache, dw.tables, dw.context_lens,
-                 dw.max_context_len, w.scale)
+                 dw.max_context_len, w.scale, seq_order=order)
     torch.cuda.synchronize()
     out = out_to_f64(dw.out, w.dtype)
     assert np.all(np.isfinite(out))
+    plain = torch.empty_like(dw.out)
+    pa.pa_decode(plain, dw.query, dw.key_cache, dw.value_cache, dw.tables, dw.context_lens,
+                 dw.max_context_len, w.scale)
+    split = torch.empty_like(dw.out)
+    ws = torch.empty(pa.pa_decode_split_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim,
+                                                        dw.max_context_len, 512), dtype=torch.uint8, device="cuda")
+    pa.pa_decode_split(split, dw.query, dw.key_cache, dw.value_cache, dw.tables, dw.context_lens,
+                       dw.max_context_len, w.scale, 512, ws, seq_order=order)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, dw.out), "launch order changed a result"
+    split = out_to_f64(split, w.dtype)
     for s, h in sample_pairs(w, 24, key):
-        assert_close(out[s, h], dw.oracle_row(s, h), w.dtype, f"seq {s} head {h}")
+        ref = dw.oracle_row(s, h)
+        assert_close(out[s, h], ref, w.dtype, f"seq {s} head {h}")
+        assert_close(split[s, h], ref, w.dtype, f"split seq {s} head {h}")
 
 
 def test_long_context_split_workload_sampled():
@@ -260,6 +283,17 @@ def test_invalid_device_indices_give_nan_rows_without_faulting():
         assert np.all(np.isnan(got[1])) and not np.any(np.isnan(got[0]))
 
 
+def test_bad_launch_order_entries_do_not_fault():
+    c = make_case(67, "f16", 4, 4, 4, 64, 16, (40, 20, 10, 33))
+    dv = to_dev(c)
+    ref = run_decode(c, dv)
+    got = run_decode(c, dv, order=[3, -1, 1, 99])     # entries outside [0, S) are ignored
+    got_split = run_decode(c, dv, split=32, order=[3, -1, 1, 99])
+    for g in (got, got_split):
+        assert np.array_equal(g[[1, 3]], ref[[1, 3]])
+        assert np.all(g[[0, 2]] == 7.0)              # sequences not listed keep the buffer's contents
+
+
 def test_zero_sequences_is_a_no_op():
     q = torch.empty((0, 4, 64), dtype=torch.float16, device="cuda")
     kc = torch.zeros((2, 4, 16, 64), dtype=torch.float16, device="cuda")
@@ -295,7 +329,7 @@ def test_parallel_sampling_decode_after_cow_step():
     pa.pa_copy_blocks(dw.key_cache, dw.value_cache, torch.tensor(pairs, dtype=torch.int32).cuda())
     pa.pa_reshape_and_cache(key, val, dw.key_cache, dw.value_cache, torch.tensor(slots, dtype=torch.int32).cuda())
     pa.pa_decode(dw.out, dw.query, dw.key_cache, dw.value_cache, dw.tables, dw.context_lens,
-                 dw.max_context_len, w.scale)
+                 dw.max_context_len, w.scale, cached_kv=True)
     torch.cuda.synchronize()
     out = out_to_f64(dw.out, w.dtype)
     kc1, vc1 = OC.copy_blocks(kc0, vc0, np.array(pairs))
