@@ -50,6 +50,11 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain copy of known size instead (pa_copy_blocks, 1 GiB read + 1 GiB written "
                          "per launch), to scale HBM counters and give a measured copy bandwidth")
+    ap.add_argument("--profile-commands", metavar="OUTDIR",
+                    help="print the rocprofv3 commands that profile this workload into OUTDIR (no GPU needed)")
+    ap.add_argument("--summarize-profile", metavar="OUTDIR",
+                    help="read the rocprofv3 CSVs those commands wrote, print a markdown summary and record the "
+                         "decode kernel's HBM bytes per launch in profiles/decode_traffic.json (no GPU needed)")
     return ap.parse_args()
 
 
@@ -75,6 +80,109 @@ def calibrate_copy(launches: int = 10):
     print(json.dumps({"calibration": "pa_copy_blocks", "launches": launches + 1,
                       "bytes_read_per_launch": per_launch, "bytes_written_per_launch": per_launch,
                       "kernel_us": us, "copy_gbps_read_plus_write": 2 * per_launch / us / 1e3}), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3: kernel trace + HBM counters of the decode kernel, scaled by the same
+# counters read on a plain copy of known size (pa_copy_blocks moving 1 GiB).
+
+PROFILE_STEPS = {"trace": (20, 5), "counters": (3, 2)}  # (steps, warmup)
+
+
+def profile_commands(workload: int, outdir: str, path: str | None) -> list[str]:
+    bench = f"python3 {os.path.join(ROOT, 'bench.py')}"
+    sel = f" --workload {workload}" + (f" --path {path}" if path else "") + " --no-cpu-baseline"
+    ts, tw = PROFILE_STEPS["trace"]
+    cs, cw = PROFILE_STEPS["counters"]
+    cmds = [f"rocprofv3 --kernel-trace --stats -f csv -d {outdir}/trace -o run -- "
+            f"{bench}{sel} --steps {ts} --warmup {tw}"]
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        cmds.append(f"rocprofv3 --pmc {ctr} -f csv -d {outdir}/{ctr.lower()} -o run -- "
+                    f"{bench}{sel} --steps {cs} --warmup {cw}")
+        cmds.append(f"rocprofv3 --pmc {ctr} -f csv -d {outdir}/copy_{ctr.lower()} -o run -- "
+                    f"{bench} --calibrate-copy")
+    return cmds
+
+
+def _csv_rows(folder: str, suffix: str):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(folder, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {folder}")
+    rows = []
+    for fn in files:
+        with open(fn, newline="", encoding="utf-8") as f:
+            rows.extend({k.strip().lower(): v for k, v in r.items()} for r in csv.DictReader(f))
+    return rows
+
+
+def _counter_per_dispatch(folder: str, counter: str, kernel_substr: str) -> tuple[float, int]:
+    """Mean over dispatches of `counter` (summed over its rows per dispatch) for kernels whose
+    name contains kernel_substr."""
+    per = {}
+    for r in _csv_rows(folder, "counter_collection.csv"):
+        if r.get("counter_name") != counter or kernel_substr not in r.get("kernel_name", ""):
+            continue
+        d = r.get("dispatch_id") or r.get("correlation_id")
+        per[d] = per.get(d, 0.0) + float(r["counter_value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for *{kernel_substr}* under {folder}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
+    w_path = path or ("split" if workload == 4 else "single")
+    decode = "decode_kernel"
+    stats = _csv_rows(os.path.join(outdir, "trace"), "kernel_stats.csv")
+    stats.sort(key=lambda r: -float(r["totaldurationns"]))
+    dec = [r for r in stats if decode in r["name"]]
+    if not dec:
+        raise SystemExit("decode kernel missing from the kernel trace")
+    dec_avg_ns = float(dec[0]["averagens"])
+    copy_bytes = 8192 // 2 * 32 * 16 * 128 * 2 * 2   # calibrate_copy: read (= written) per launch
+    scale, meas = {}, {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        ck, cn = _counter_per_dispatch(os.path.join(outdir, f"copy_{ctr.lower()}"), ctr, "copy_blocks_kernel")
+        scale[ctr] = copy_bytes / (ck * 1024.0)
+        meas[ctr] = _counter_per_dispatch(os.path.join(outdir, ctr.lower()), ctr, decode)
+        meas[ctr] = (meas[ctr][0], meas[ctr][1], ck, cn)
+    traffic = sum(meas[c][0] * 1024.0 * scale[c] for c in meas)
+    key = f"workload{workload}-{w_path}"
+    try:
+        with open(TRAFFIC_FILE, encoding="utf-8") as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec[key] = {"bytes_per_launch": traffic, "source_digest": source_digest(),
+                "fetch_kib_per_dispatch": meas["FETCH_SIZE"][0], "write_kib_per_dispatch": meas["WRITE_SIZE"][0],
+                "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"],
+                "rocprof_decode_avg_us": dec_avg_ns / 1e3}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w", encoding="utf-8") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    out = [f"# rocprofv3: decode kernel, workload {workload} ({w_path} path)", "",
+           f"Decode kernel source digest (decode.hip + device_common.hpp): `{source_digest()}`", "",
+           "Commands (run from any directory with TMPDIR=/tmp; OUTDIR is a scratch folder):", "", "```"]
+    out += profile_commands(workload, "OUTDIR", path) + ["```", "", "## Kernel trace (--kernel-trace --stats)", "",
+                                                        "| kernel | calls | avg us | min us | max us | % time |",
+                                                        "|---|---|---|---|---|---|"]
+    for r in stats[:8]:
+        name = r["name"] if len(r["name"]) < 90 else r["name"][:87] + "..."
+        out.append(f"| `{name}` | {r['calls']} | {float(r['averagens']) / 1e3:.2f} | "
+                   f"{float(r['minns']) / 1e3:.2f} | {float(r['maxns']) / 1e3:.2f} | {float(r['percentage']):.1f} |")
+    out += ["", "## HBM counters (--pmc, one counter per run, KiB per dispatch)", "",
+            "| counter | decode kernel | dispatches | copy kernel (1 GiB each way) | dispatches | scale |",
+            "|---|---|---|---|---|---|"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        v, n, ck, cn = meas[c]
+        out.append(f"| {c} | {v:.1f} | {n} | {ck:.1f} | {cn} | {scale[c]:.4f} |")
+    out += ["", f"Scaled HBM traffic per decode launch: **{traffic / 1e6:.2f} MB** "
+                f"(fetch {meas['FETCH_SIZE'][0] * 1024 * scale['FETCH_SIZE'] / 1e6:.2f} MB + write "
+                f"{meas['WRITE_SIZE'][0] * 1024 * scale['WRITE_SIZE'] / 1e6:.2f} MB); "
+                f"average decode duration in the trace {dec_avg_ns / 1e3:.2f} us."]
+    print("\n".join(out))
 
 
 def source_digest() -> str:
@@ -122,6 +230,8 @@ class Bench:
 
         # host allocator state (product path: the C++ allocator)
         self.alloc = pa.Allocator(w.num_blocks, bs, w.free_order)
+        # Workloads 1 and 5 time one step from a fixed state: workload 1's 16-block pool
+        # holds a single step's growth, and workload 5's copies happen on the first append.
         if args.workload == 5:
             for g in range(w.groups):
                 parent = 10_000 + g
@@ -135,8 +245,8 @@ class Bench:
         else:
             for s, n in enumerate(w.context_lens):
                 self.alloc.seq_create(s, n)
-            self.base = None
-            growth = total_steps
+            self.base = self.alloc.clone() if args.workload == 1 else None
+            growth = 1 if args.workload == 1 else total_steps
         self.max_blocks = -(-(max(w.context_lens) + growth) // bs) + 1
         self.max_ctx = self.max_blocks * bs
 
@@ -259,6 +369,12 @@ class Bench:
 
 def main():
     args = parse()
+    if args.profile_commands:
+        print("\n".join(profile_commands(args.workload, args.profile_commands, args.path)))
+        return
+    if args.summarize_profile:
+        summarize_profile(args.workload, args.summarize_profile, args.path)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path shards by "
               "sequence or KV head with no exchange; this build runs on a single MI355X)", file=sys.stderr)
