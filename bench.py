@@ -64,7 +64,7 @@ def calibrate_copy(launches: int = 10):
     import paged_kv_cache_333_amd as pa
     NB, Hkv, bs, D = 8192, 32, 16, 128          # 128 KiB per block and pool, 1 GiB per pool
     kc = torch.zeros((NB, Hkv, bs, D), dtype=torch.float16, device="cuda")
-    vc = torch.zeros_like(kc)
+    vc = torch.zeros((NB, Hkv, D, bs), dtype=torch.float16, device="cuda")
     half = NB // 2
     pairs = torch.stack([torch.arange(half), torch.arange(half, NB)], dim=1).to(torch.int32).cuda()
     per_launch = half * Hkv * bs * D * 2 * 2     # bytes read (= bytes written), both pools
@@ -251,9 +251,9 @@ class Bench:
         self.max_ctx = self.max_blocks * bs
 
         # device data, resident before timing
-        pool = (w.num_blocks, Hkv, bs, D)
-        self.kc = synth.normal_device(pool, seeds["key_cache"], w.dtype)
-        self.vc = synth.normal_device(pool, seeds["value_cache"], w.dtype)
+        k_shape, v_shape = synth.pool_shapes(w)
+        self.kc = synth.normal_device(k_shape, seeds["key_cache"], w.dtype)
+        self.vc = synth.normal_device(v_shape, seeds["value_cache"], w.dtype)
         self.q = synth.normal_device((S, H, D), seeds["query"], w.dtype)
         R = 8  # distinct new-token K/V batches, cycled
         self.newk = synth.normal_device((R, S, Hkv, D), seeds["new_key"], w.dtype)

@@ -16,11 +16,17 @@
  *
  * Data layout (device memory, all row-major, all owned by the caller):
  *   query, out      [num_seqs, num_heads, head_dim]               element type `dtype`
- *   key_cache,
- *   value_cache     [num_blocks, num_kv_heads, block_size, head_dim]  element type `dtype`
- *                   (the separate K and V pools of [IMPL] §3.1/§3.4; one
- *                   (block, kv head) tile is contiguous, one token row is
- *                   head_dim contiguous elements)
+ *   key_cache       [num_blocks, num_kv_heads, block_size, head_dim]  element type `dtype`
+ *                   (the separate key pool of [IMPL] §3.1/§3.4: one token's
+ *                   key is head_dim contiguous elements)
+ *   value_cache     [num_blocks, num_kv_heads, head_dim, block_size]  element type `dtype`
+ *                   (block size innermost, the arrangement of [ASC] §3.1/§5.2:
+ *                   one dim of a block's block_size tokens is contiguous)
+ *                   In both pools one (block, kv head) tile is one contiguous
+ *                   block_size * head_dim run.  The two orientations give the
+ *                   decode kernel's matrix-core products 16-byte operand loads
+ *                   along their contraction axes (head_dim for q.K, tokens for
+ *                   P.V).
  *   block_tables    [num_seqs, max_blocks_per_seq] int32; entry j of row s is
  *                   the physical block of logical block j (tokens j*bs ..
  *                   j*bs+bs-1) of sequence s; unused entries are -1 by
@@ -53,7 +59,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -178,8 +184,8 @@ pa_status pa_order_longest_first(const int32_t* context_lens, int32_t n, int32_t
 /* Write new K/V rows into the pools through the slot mapping ([ASC] §3.1
  * slot_mapping; [IMPL] §3.4 _add_kv_cache):
  *   for i < num_tokens with 0 <= s = slot_mapping[i] < num_blocks*block_size:
- *     key_cache[s / bs, h, s % bs, :] = key[i, h, :]  for every KV head h,
- *     value_cache likewise from value.
+ *     key_cache[s / bs, h, s % bs, :]   = key[i, h, :]    for every KV head h,
+ *     value_cache[s / bs, h, :, s % bs] = value[i, h, :].
  * key, value: device [num_tokens, num_kv_heads, head_dim].  Negative slots are
  * skipped (padding); slots past the pool are skipped too (and rejected under
  * PA_DEBUG).  Two tokens with the same slot race: invalid input.  A pure copy,
@@ -191,7 +197,7 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cac
 
 /* Copy-on-write block copies ([IMPL] §3.3: the whole block is copied):
  * for each pair p < num_pairs, block pairs[2p] (src) -> pairs[2p+1] (dst) in
- * both pools, all KV heads, all rows.  pairs: device int32 [num_pairs, 2].
+ * both pools, all KV heads, all tokens (the whole tile of each pool).  pairs: device int32 [num_pairs, 2].
  * Pairs run concurrently: a block that is the destination of one pair must
  * not be the source or destination of another (rejected under PA_DEBUG).
  * Pairs with an id outside [0, num_blocks) are skipped.  Bit-exact. */
@@ -204,7 +210,8 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* pair
  * [ASC] §三/§四 fused gather + QK^T + softmax + OV):
  *   for each sequence s and query head h, with n = context_lens[s],
  *   g = h / (num_heads / num_kv_heads), token t in block
- *   block_tables[s, t / bs] at row t % bs:
+ *   b = block_tables[s, t / bs] at offset o = t % bs,
+ *   K_t = key_cache[b, g, o, :], V_t = value_cache[b, g, :, o]:
  *     z_t = scale * <query[s,h,:], K_t>,  out[s,h,:] = sum_t softmax(z)_t V_t
  * accumulated in fp32 with an online softmax (running max and sum, both
  * rescaled when the max grows), written in `dtype` (round to nearest even).

@@ -13,9 +13,12 @@ What is computed, and where the pages define it:
   loops are not followed where they differ from this definition (one page
   normalises each block separately, another never rescales its accumulator);
   the oracle is the definition they all aim at.
-* Pool layout [num_blocks, num_kv_heads, block_size, head_dim] for each of K
-  and V ("PagedAttention 实现细节" §3.1 index-based kernel signature, §3.4
-  PagedAttention.forward).
+* Pool layouts.  Keys: [num_blocks, num_kv_heads, block_size, head_dim], one
+  token row after another ("PagedAttention 实现细节" §3.1 index-based kernel
+  signature, §3.4 PagedAttention.forward).  Values: [num_blocks, num_kv_heads,
+  head_dim, block_size], the block-size-innermost arrangement of
+  "Ascend C算子开发高阶实战…" §3.1/§5.2, so value row t of a block is the
+  column [:, t % block_size] of its (block, KV head) tile.
 * Query heads share KV heads in contiguous groups: query head h reads KV head
   h // (num_heads // num_kv_heads).  The pages name grouped-query attention
   only as future work ("Ascend C算子开发高阶实战…" §十); contiguous grouping is
@@ -62,6 +65,7 @@ def gather_kv(key_cache, value_cache, table_row, num_tokens: int, kv_head: int, 
     Logical block j of the sequence lives in physical block table_row[j]; its
     rows are tokens j*bs .. j*bs + bs - 1, of which only those below
     `num_tokens` are valid ("PagedAttention 实现细节" §3.1, the gather step).
+    key_cache is [NB, H_kv, bs, D] and value_cache [NB, H_kv, D, bs].
     Returns float64 arrays K, V of shape [num_tokens, head_dim].
     """
     num_blocks, _, block_size, head_dim = key_cache.shape
@@ -72,7 +76,7 @@ def gather_kv(key_cache, value_cache, table_row, num_tokens: int, kv_head: int, 
             raise IndexError(f"block table entry {phys} outside the pool of {num_blocks}")
         valid = min(block_size, num_tokens - j * block_size)
         ks.append(to_f64(key_cache[phys, kv_head, :valid, :], dtype))
-        vs.append(to_f64(value_cache[phys, kv_head, :valid, :], dtype))
+        vs.append(to_f64(value_cache[phys, kv_head, :, :valid].T, dtype))
     if not ks:
         empty = np.zeros((0, head_dim), dtype=np.float64)
         return empty, empty.copy()
@@ -102,8 +106,8 @@ def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scal
     """out[s, h] = attention of query[s, h] over the first context_lens[s] tokens of
     sequence s, gathered through block_tables[s] from the KV head h // G.
 
-    query [S, H, D]; key_cache, value_cache [NB, H_kv, bs, D]; block_tables [S, MB];
-    context_lens [S].  Returns float64 [S, H, D].
+    query [S, H, D]; key_cache [NB, H_kv, bs, D]; value_cache [NB, H_kv, D, bs];
+    block_tables [S, MB]; context_lens [S].  Returns float64 [S, H, D].
     """
     S, H, D = query.shape
     H_kv = key_cache.shape[1]

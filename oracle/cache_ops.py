@@ -11,8 +11,11 @@
   §3.3: copy the full contents of the original block to the new one).  Pairs
   are applied in list order.
 
-Arrays are NumPy storage arrays (bf16 as uint16 bits), so the results are
-bit patterns and compare bit-exactly.
+Pools: key_cache [NB, H_kv, bs, D] (token rows), value_cache [NB, H_kv, D, bs]
+(block size innermost, "Ascend C算子开发高阶实战…" §3.1/§5.2), so a token's
+value vector is written down column `offset` of its tile.  Arrays are NumPy
+storage arrays (bf16 as uint16 bits), so the results are bit patterns and
+compare bit-exactly.
 """
 from __future__ import annotations
 
@@ -29,7 +32,7 @@ def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping):
             continue
         block, offset = divmod(int(slot), block_size)
         kc[block, :, offset, :] = key[i]
-        vc[block, :, offset, :] = value[i]
+        vc[block, :, :, offset] = value[i]
     return kc, vc
 
 

@@ -149,9 +149,20 @@ def _stream(stream):
     return _torch().cuda.current_stream().cuda_stream
 
 
-def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, stream=None):
-    """key, value [T, H_kv, D]; pools [NB, H_kv, bs, D]; slot_mapping int32 [T]."""
+def _pool_dims(key_cache, value_cache):
+    """(NB, H_kv, bs, D) from key_cache [NB, H_kv, bs, D]; value_cache must be [NB, H_kv, D, bs]."""
     NB, H_kv, bs, D = key_cache.shape
+    if tuple(value_cache.shape) != (NB, H_kv, D, bs) or value_cache.dtype != key_cache.dtype:
+        raise ValueError(f"value_cache must be [num_blocks, num_kv_heads, head_dim, block_size] = "
+                         f"{(NB, H_kv, D, bs)} of {key_cache.dtype}, got {tuple(value_cache.shape)} "
+                         f"of {value_cache.dtype}")
+    return NB, H_kv, bs, D
+
+
+def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, stream=None):
+    """key, value [T, H_kv, D]; key_cache [NB, H_kv, bs, D]; value_cache [NB, H_kv, D, bs];
+    slot_mapping int32 [T]."""
+    NB, H_kv, bs, D = _pool_dims(key_cache, value_cache)
     _check(lib.pa_reshape_and_cache(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
                                     _ptr(slot_mapping), slot_mapping.numel(), NB, H_kv, D, bs,
                                     _dtype_code(key_cache), _stream(stream)), "pa_reshape_and_cache")
@@ -159,7 +170,7 @@ def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, strea
 
 def pa_copy_blocks(key_cache, value_cache, pairs, stream=None, num_pairs=None):
     """pairs int32 [P, 2] (src, dst) on the device; num_pairs may cover a prefix of it."""
-    NB, H_kv, bs, D = key_cache.shape
+    NB, H_kv, bs, D = _pool_dims(key_cache, value_cache)
     P = pairs.shape[0] if num_pairs is None else num_pairs
     _check(lib.pa_copy_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(pairs), P, NB, H_kv, D, bs,
                               _dtype_code(key_cache), _stream(stream)), "pa_copy_blocks")
@@ -171,11 +182,12 @@ def _opt(t):
 
 def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len: int,
               scale: float, stream=None, seq_order=None, cached_kv: bool = False):
-    """out, query [S, H, D]; pools [NB, H_kv, bs, D]; block_tables [S, MB]; context_lens [S];
+    """out, query [S, H, D]; key_cache [NB, H_kv, bs, D]; value_cache [NB, H_kv, D, bs];
+    block_tables [S, MB]; context_lens [S];
     seq_order: optional device int32 [S] launch order (see pa_order_longest_first);
     cached_kv: read K/V with the default cache policy (pools with shared blocks)."""
     S, H, D = query.shape
-    NB, H_kv, bs, _ = key_cache.shape
+    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache)
     _check(lib.pa_decode(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
                          _ptr(context_lens), _opt(seq_order), S, H, H_kv, D, bs, block_tables.shape[1], NB,
                          max_context_len, scale, _dtype_code(query), PA_DECODE_CACHED_KV if cached_kv else 0,
@@ -192,7 +204,7 @@ def pa_decode_split(out, query, key_cache, value_cache, block_tables, context_le
                     cached_kv: bool = False):
     """As pa_decode; workspace is a device tensor of at least pa_decode_split_workspace_bytes bytes."""
     S, H, D = query.shape
-    NB, H_kv, bs, _ = key_cache.shape
+    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache)
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib.pa_decode_split(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
                                _ptr(block_tables), _ptr(context_lens), _opt(seq_order), S, H, H_kv, D, bs,

@@ -198,7 +198,7 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cac
     }
   }
   return finish(pa::launch_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, num_tokens,
-                                             num_blocks, num_kv_heads, head_dim * elem_bytes(dtype),
+                                             num_blocks, num_kv_heads, head_dim, elem_bytes(dtype),
                                              block_size, st),
                 st, "pa_reshape_and_cache");
 }

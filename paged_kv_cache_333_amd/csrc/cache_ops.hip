@@ -1,7 +1,8 @@
 // Pool writes: the slot-mapping scatter of new K/V rows, and whole-block copies
-// for copy-on-write.  Both are pure 16-byte copies: every lane moves one chunk
-// of a token row, consecutive lanes move consecutive chunks, so a wave writes
-// whole rows with coalesced stores.
+// for copy-on-write.  Both are pure copies, bit-exact.  Every lane reads one
+// 16-byte chunk of a row and consecutive lanes take consecutive chunks; key
+// rows are stored as whole chunks, value rows element by element down a
+// column of the dim-major value tile.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -10,27 +11,43 @@ namespace pa {
 // Slot-mapping write ("Ascend C算子开发高阶实战…" §3.1: slot_mapping maps a
 // token to block slot / bs, offset slot % bs; "PagedAttention 实现细节" §3.4:
 // the new K/V of each step goes into its block).  One thread per 16-byte chunk
-// of one (token, KV head) row; it writes both the K and the V chunk.  Slots
+// of one (token, KV head) row.  The key chunk is stored whole (keys are token
+// rows, [NB, H_kv, bs, D]); the value chunk's EPL elements go down column
+// `offset` of the value tile ([NB, H_kv, D, bs]), one element per dim.  Slots
 // outside [0, num_blocks * block_size) write nothing.
+template <int E>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const char* __restrict__ key, const char* __restrict__ value, char* __restrict__ key_cache,
     char* __restrict__ value_cache, const int32_t* __restrict__ slot_mapping, int32_t num_tokens,
-    int64_t num_slots, int32_t num_kv_heads, int32_t chunks_per_row, int32_t block_size) {
+    int64_t num_slots, int32_t num_kv_heads, int32_t head_dim, int32_t block_size) {
+  constexpr int EPL = 16 / E;
+  const int32_t cpr = head_dim / EPL;  // chunks per row
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t per_token = static_cast<int64_t>(num_kv_heads) * chunks_per_row;
+  const int64_t per_token = static_cast<int64_t>(num_kv_heads) * cpr;
   if (idx >= per_token * num_tokens) return;
   const int64_t tok = idx / per_token;
-  const int64_t rem = idx - tok * per_token;  // = h * chunks_per_row + c
-  const int32_t h = static_cast<int32_t>(rem / chunks_per_row);
-  const int32_t c = static_cast<int32_t>(rem - static_cast<int64_t>(h) * chunks_per_row);
+  const int64_t rem = idx - tok * per_token;  // = h * cpr + c
+  const int32_t h = static_cast<int32_t>(rem / cpr);
+  const int32_t c = static_cast<int32_t>(rem - static_cast<int64_t>(h) * cpr);
   const int64_t slot = slot_mapping[tok];
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / block_size;
   const int64_t off = slot - blk * block_size;
-  const int64_t dst = (((blk * num_kv_heads + h) * block_size + off) * chunks_per_row + c) * 16;
+  const int64_t tile = blk * num_kv_heads + h;  // (block, KV head) tile
   const int64_t src = idx * 16;
-  store16(key_cache + dst, load16(key + src));
-  store16(value_cache + dst, load16(value + src));
+  store16(key_cache + ((tile * block_size + off) * head_dim + static_cast<int64_t>(c) * EPL) * E,
+          load16(key + src));
+  const u32x4 v = load16(value + src);
+  char* vcol = value_cache + ((tile * head_dim + static_cast<int64_t>(c) * EPL) * block_size + off) * E;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const uint32_t w = word(v, e * E / 4);
+    if constexpr (E == 4)
+      *reinterpret_cast<uint32_t*>(vcol + static_cast<int64_t>(e) * block_size * E) = w;
+    else
+      *reinterpret_cast<uint16_t*>(vcol + static_cast<int64_t>(e) * block_size * E) =
+          static_cast<uint16_t>(e & 1 ? w >> 16 : w);
+  }
 }
 
 // Whole-block copy ("PagedAttention 实现细节" §3.3: the full contents of the
@@ -65,17 +82,22 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ key
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,
                                     void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
-                                    int32_t num_blocks, int32_t num_kv_heads, int32_t row_bytes,
-                                    int32_t block_size, hipStream_t stream) {
-  const int32_t cpr = row_bytes / 16;
-  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * cpr;
+                                    int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t elem_bytes, int32_t block_size, hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * (head_dim * elem_bytes / 16);
   if (total == 0) return hipSuccess;
   const int64_t grid = (total + 255) / 256;
-  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream,
-                     static_cast<const char*>(key), static_cast<const char*>(value),
-                     static_cast<char*>(key_cache), static_cast<char*>(value_cache), slot_mapping,
-                     num_tokens, static_cast<int64_t>(num_blocks) * block_size, num_kv_heads, cpr,
-                     block_size);
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
+#define PA_RESHAPE(E)                                                                                      \
+  hipLaunchKernelGGL(reshape_and_cache_kernel<E>, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream, \
+                     static_cast<const char*>(key), static_cast<const char*>(value),                      \
+                     static_cast<char*>(key_cache), static_cast<char*>(value_cache), slot_mapping,          \
+                     num_tokens, num_slots, num_kv_heads, head_dim, block_size)
+  if (elem_bytes == 4)
+    PA_RESHAPE(4);
+  else
+    PA_RESHAPE(2);
+#undef PA_RESHAPE
   return hipGetLastError();
 }
 

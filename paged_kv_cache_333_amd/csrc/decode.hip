@@ -1,5 +1,5 @@
-// Paged decode attention for gfx950: single pass, split partials, and the
-// log-sum-exp merge of partials.
+// Paged decode attention for gfx950 on the matrix cores: single pass, split
+// partials, and the log-sum-exp merge of partials.
 //
 // What is computed ("PagedAttention 实现细节" §3.1 index-based kernel: token t
 // of a sequence lives in block table[t / bs] at row t % bs, read in place;
@@ -8,29 +8,46 @@
 //   out[s,h] = sum_t softmax_t(scale * <q[s,h], K_t>) V_t over t < ctx[s],
 // with K_t, V_t taken from KV head h / (H / H_kv).
 //
-// Work decomposition.  A workgroup of kWaves waves owns one (sequence, group
-// of GT query heads that share a KV head, token range).  The range is the
-// whole context (single pass) or one partition (split).  Wave w takes blocks
-// w, w + kWaves, ... of the range.  Inside a wave, a token row of the K/V tile
-// (head_dim elements) is spread over LPR lanes, 16 bytes per lane, so one
-// load instruction reads RPL = 64 / LPR consecutive rows of a block, fully
-// coalesced.  Each row position keeps its own online-softmax state (running
-// max m, running sum l, fp32 accumulator), so the hot loop needs no cross-row
-// traffic: q.K is a per-lane packed dot plus a DPP sum inside the row.  The
-// per-row states are merged at the end (lane shuffles inside the wave, then
-// LDS across waves) with the same rescaling rule as the split merge.  The GT
-// query heads of a group reuse every K/V element loaded, so a KV element is
-// read from HBM once per group.
+// Pools.  Keys are stored token-major, [NB, H_kv, bs, D]; values dim-major,
+// [NB, H_kv, D, bs] (block size innermost, the arrangement of "Ascend C算子
+// 开发高阶实战…" §3.1/§5.2).  Each 16-byte load then holds 8 (4 for fp32)
+// consecutive elements along the contraction axis of its product: head_dim
+// for q.K, tokens for P.V, which is what a matrix-core operand wants.
+//
+// Work decomposition.  A workgroup of kWaves waves owns one (sequence, GT
+// query heads that share a KV head, token range); the range is the whole
+// context (single pass) or one partition (split).  A wave walks the range in
+// steps of TS tokens (32 for fp16/bf16, 16 for fp32); wave w takes steps
+// w, w + kWaves, ...  In a step, with lane = 16 q + n:
+//   * q.K: one 16x16 tile per 16 tokens, C[m][n'] = sum_d K[tok(m)][d] Q[n'][d]
+//     on v_mfma_f32_16x16x32_{f16,bf16} (fp32: 16x16x4).  Column n' of Q is
+//     query head n' % GT, so the GT heads are replicated to fill the 16
+//     columns and every lane ends up holding logits of one head.  Token rows
+//     are permuted so that lane (q, n) receives tokens EPL q .. EPL q + EPL-1
+//     of the step, exactly the slice it supplies to P.V.
+//   * online softmax per head on those EPL logits per lane: running max (made
+//     common to the four lanes of a column with two cross-row max steps),
+//     running sum, rescale of the accumulator when the max grows.
+//   * P.V: out^T tile C[m][d'] = sum_t P[m][t] V[t][d'], one product per 16
+//     output dims; P never leaves the registers that computed it.  For bf16,
+//     P is split into a bf16 high part and a bf16 residual (two products) so
+//     the weights keep ~16 significant bits; fp16 P keeps 11.
+// Each KV element is loaded once per workgroup; the GT query heads share it.
 //
 // Logits are kept in base-2 units (scale folded with log2 e) so the hardware
-// exp2 is used; the running max and sum are rescaled together with the
-// accumulator whenever the max grows (the page's own loop rescales only the
-// sum; the correct rule rescales both).
+// exp2 is used.  Tokens past the context are masked by select (never by
+// multiplying by 0), and their value columns are zeroed before the product,
+// so NaN garbage in unused rows cannot leak.  The merge of the waves (LDS) and
+// of the split partials uses the same rescaling rule.  Reduction order depends
+// only on logical token positions, so relabelling physical blocks gives
+// bit-identical results.
 //
 // Invalid device data never leads to an out-of-bounds access: a block id
 // outside the pool is not read and turns the affected outputs into NaN; a
 // context length outside its bound does the same.
 #include <math.h>
+
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -63,20 +80,22 @@ struct DecodeParams {
 
 template <typename T, int D, int BS, int GT, bool SPLIT, bool CACHED>
 __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams a) {
-  constexpr int EPL = T::kEPL;
-  constexpr int LPR = D / EPL;   // lanes per token row
-  constexpr int RPL = 64 / LPR;  // rows per wave load
-  constexpr int NJ = BS / RPL;   // loads per block per pool
-  constexpr int JB0 = GT >= 8 ? 2 : 8;
-  constexpr int JB = NJ < JB0 ? NJ : JB0;  // loads consumed per inner step
-  static_assert(NJ % JB == 0, "block rows");
+  constexpr int EPL = T::kEPL;       // elements per 16-byte chunk
+  constexpr int E = T::kBytes;
+  constexpr int KV = D / EPL / 4;    // q.K products per 16-token tile (chunks 4v + q of a row)
+  constexpr int NT = EPL / 4;        // 16-token q.K tiles per step
+  constexpr int TS = 16 * NT;        // tokens per step
+  constexpr int NV = D / 16;         // P.V products per step (16 output dims each)
+  constexpr int NBS = TS > BS ? TS / BS : 1;  // blocks touched by one step
+  constexpr bool SPLIT_P = std::is_same<T, TBF16>::value;
   constexpr float kNegInf = -__builtin_huge_valf();
+  static_assert(GT >= 1 && GT <= 16, "heads per workgroup");
 
   const int lane = threadIdx.x & 63;
-  // wave-uniform: keeps the block loop and the table lookups in scalar registers
+  // wave-uniform: keeps the step loop and the table lookups in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane / LPR;
-  const int c = lane - r * LPR;
+  const int q = lane >> 4;
+  const int n = lane & 15;
   const int groups = a.num_heads / GT;
   const int slot = blockIdx.x / groups;
   const int h0 = (blockIdx.x - slot * groups) * GT;
@@ -85,125 +104,166 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams a) {
   const int s = a.order ? a.order[slot] : slot;
   if (static_cast<uint32_t>(s) >= static_cast<uint32_t>(a.num_seqs)) return;
   const int kvh = h0 / (a.num_heads / a.num_kv_heads);
-  const int n = a.ctx[s];
-  const bool bad_len = n < 0 || n > a.len_limit;
+  const int nctx = a.ctx[s];
+  const bool bad_len = nctx < 0 || nctx > a.len_limit;
 
-  int t_begin = 0, t_end = bad_len ? 0 : n;
+  int t_begin = 0, t_end = bad_len ? 0 : nctx;
   if constexpr (SPLIT) {
     t_begin = blockIdx.y * a.part_size;
-    if (bad_len || t_begin >= n) return;  // nothing to write for this partition
-    t_end = min(t_begin + a.part_size, n);
+    if (bad_len || t_begin >= nctx) return;  // nothing to write for this partition
+    t_end = min(t_begin + a.part_size, nctx);
   }
-  const int b_begin = t_begin / BS;
   const int b_end = (t_end + BS - 1) / BS;
   const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.max_blocks;
 
-  u32x4 qv[GT];
+  // Q operand of q.K: lane (q, n) holds head h0 + n % GT, chunks 4v + q.
+  u32x4 qv[KV];
+  {
+    const char* qrow = a.q + (static_cast<int64_t>(s) * a.num_heads + h0 + n % GT) * D * E;
 #pragma unroll
-  for (int g = 0; g < GT; ++g)
-    qv[g] = load16(a.q + ((static_cast<int64_t>(s) * a.num_heads + h0 + g) * D + c * EPL) * T::kBytes);
-
-  float m[GT], l[GT], acc[GT][EPL];
-#pragma unroll
-  for (int g = 0; g < GT; ++g) {
-    m[g] = kNegInf;
-    l[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+    for (int v = 0; v < KV; ++v) qv[v] = load16(qrow + (4 * v + q) * 16);
   }
+
+  // Online-softmax state of this lane's head (n % GT), and the P.V
+  // accumulator: acc[v][j] is out^T row 4q + j (head (4q + j) % GT), dim 16v + n.
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 acc[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
   int bad = 0;
 
-  for (int b = b_begin + wave; b < b_end; b += kWaves) {
-    const int32_t phys = trow[b];
-    if (static_cast<uint32_t>(phys) >= static_cast<uint32_t>(a.num_blocks)) {
+  const int n_steps = (t_end - t_begin + TS - 1) / TS;
+  const int64_t hkv = a.num_kv_heads;
+  for (int st = wave; st < n_steps; st += kWaves) {
+    const int t0 = t_begin + st * TS;
+    const int b0 = t0 / BS;
+    const int off0 = t0 - b0 * BS;  // nonzero only when a step is shorter than a block
+    int32_t ph[NBS];
+    bool skip = false;
+#pragma unroll
+    for (int i = 0; i < NBS; ++i) {
+      if (b0 + i < b_end) {
+        ph[i] = trow[b0 + i];
+        if (static_cast<uint32_t>(ph[i]) >= static_cast<uint32_t>(a.num_blocks)) skip = true;
+      } else {
+        ph[i] = -1;  // past the context: masked below, read from block ph[0]
+      }
+    }
+    if (skip) {
       bad = 1;
       continue;
     }
-    const int64_t row0 = (static_cast<int64_t>(phys) * a.num_kv_heads + kvh) * BS + r;
-    const char* kp = a.kc + (row0 * D + c * EPL) * T::kBytes;
-    const char* vp = a.vc + (row0 * D + c * EPL) * T::kBytes;
-    const int tok0 = b * BS + r;
 #pragma unroll
-    for (int j0 = 0; j0 < NJ; j0 += JB) {
-      u32x4 kv[JB], vv[JB];
+    for (int i = 1; i < NBS; ++i)
+      if (ph[i] < 0) ph[i] = ph[0];
+
+    // K rows: in tile tau, lane (q, n) supplies row n = token
+    // EPL (n / 4) + 4 tau + n % 4 of the step, chunks 4v + q.
+    u32x4 kr[NT][KV];
 #pragma unroll
-      for (int jj = 0; jj < JB; ++jj) {
-        const int64_t off = static_cast<int64_t>((j0 + jj) * RPL) * D * T::kBytes;
-        if constexpr (CACHED) {
-          kv[jj] = load16(kp + off);
-          vv[jj] = load16(vp + off);
-        } else {
-          kv[jj] = load16_stream(kp + off);
-          vv[jj] = load16_stream(vp + off);
-        }
+    for (int tau = 0; tau < NT; ++tau) {
+      const int x = off0 + EPL * (n >> 2) + 4 * tau + (n & 3);
+      const int bi = NBS == 1 ? 0 : x / BS;
+      const int64_t phys = bi ? ph[NBS - 1] : ph[0];
+      const char* kp = a.kc + (((phys * hkv + kvh) * BS + (x - bi * BS)) * D) * E + q * 16;
+#pragma unroll
+      for (int v = 0; v < KV; ++v) kr[tau][v] = CACHED ? load16(kp + v * 64) : load16_stream(kp + v * 64);
+    }
+    // V columns: lane (q, n) supplies dim 16v + n of tokens EPL q .. EPL q + EPL-1.
+    u32x4 vr[NV];
+    {
+      const int x = off0 + EPL * q;
+      const int bi = NBS == 1 ? 0 : x / BS;
+      const int64_t phys = bi ? ph[NBS - 1] : ph[0];
+      const char* vp = a.vc + (((phys * hkv + kvh) * D + n) * BS + (x - bi * BS)) * E;
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        vr[v] = CACHED ? load16(vp + v * 16 * BS * E) : load16_stream(vp + v * 16 * BS * E);
+    }
+
+    f32x4 c[NT];
+#pragma unroll
+    for (int tau = 0; tau < NT; ++tau) {
+      c[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < KV; ++v) c[tau] = mma(T{}, kr[tau][v], qv[v], c[tau]);
+    }
+    // c[tau][j]: logit of token t0 + EPL q + 4 tau + j for head n % GT
+    const bool tail = t0 + TS > t_end;
+    float z[EPL];
+    float mx = kNegInf;
+#pragma unroll
+    for (int tau = 0; tau < NT; ++tau)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float v = c[tau][j] * a.scale_log2;
+        const bool ok = !tail || t0 + EPL * q + 4 * tau + j < t_end;
+        z[4 * tau + j] = ok ? v : kNegInf;
+        mx = fmaxf(mx, z[4 * tau + j]);
       }
-      bool valid[JB];
-      float vf[JB][EPL];
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float p[EPL];
+    float ps = 0.f;
 #pragma unroll
-      for (int jj = 0; jj < JB; ++jj) {
-        valid[jj] = tok0 + (j0 + jj) * RPL < t_end;
-        // masked rows may hold anything (even NaN): zero them before use
-        const u32x4 zero = {0u, 0u, 0u, 0u};
-        to_float(T{}, valid[jj] ? vv[jj] : zero, vf[jj]);
+    for (int e = 0; e < EPL; ++e) {
+      p[e] = fast_exp2(z[e] - m_use);
+      ps += p[e];
+    }
+    l_run = l_run * alpha + ps;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+      // acc[.][j] belongs to head (4q + j) % GT; its factor sits in a lane of
+      // the same row whose column has that head.
+      float al[4];
+      if constexpr (4 % GT == 0) {
+        al[0] = quad_bcast<0>(alpha);
+        al[1] = quad_bcast<1>(alpha);
+        al[2] = quad_bcast<2>(alpha);
+        al[3] = quad_bcast<3>(alpha);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) al[j] = __shfl(alpha, 16 * q + (4 * q + j) % GT);
       }
 #pragma unroll
-      for (int g = 0; g < GT; ++g) {
-        float z[JB];
-        float mx = kNegInf;
+      for (int v = 0; v < NV; ++v)
 #pragma unroll
-        for (int jj = 0; jj < JB; ++jj) {
-          const float d = row_sum<LPR>(dot16(T{}, qv[g], kv[jj])) * a.scale_log2;
-          z[jj] = valid[jj] ? d : kNegInf;
-          mx = fmaxf(mx, z[jj]);
-        }
-        const float m_new = fmaxf(m[g], mx);
-        const float m_use = m_new == kNegInf ? 0.f : m_new;
-        const float alpha = fast_exp2(m[g] - m_use);
-        l[g] *= alpha;
+        for (int j = 0; j < 4; ++j) acc[v][j] *= al[j];
+    }
+    u32x4 phi, plo;
+    pack_p(T{}, p, phi, plo);
+    if (tail) {
+      const u32x4 keep = keep_mask(T{}, t_end - (t0 + EPL * q));
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+      for (int v = 0; v < NV; ++v) vr[v] &= keep;
+    }
 #pragma unroll
-        for (int jj = 0; jj < JB; ++jj) {
-          const float p = fast_exp2(z[jj] - m_use);
-          l[g] += p;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[g][e] = __builtin_fmaf(p, vf[jj][e], acc[g][e]);
-        }
-        m[g] = m_new;
-      }
+    for (int v = 0; v < NV; ++v) {
+      acc[v] = mma(T{}, phi, vr[v], acc[v]);
+      if constexpr (SPLIT_P) acc[v] = mma(T{}, plo, vr[v], acc[v]);
     }
   }
 
-  // merge the RPL row states of this wave (partners differ only in the row)
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      const float mo = __shfl_xor(m[g], off);
-      const float lo = __shfl_xor(l[g], off);
-      const float M = fmaxf(m[g], mo);
-      const float Mu = M == kNegInf ? 0.f : M;
-      const float w1 = fast_exp2(m[g] - Mu);
-      const float w2 = fast_exp2(mo - Mu);
-      l[g] = l[g] * w1 + lo * w2;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] = acc[g][e] * w1 + __shfl_xor(acc[g][e], off) * w2;
-      m[g] = M;
-    }
-  }
+  // the four lanes of a column summed disjoint tokens with a common max
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
 
   __shared__ float sm_m[kWaves][GT];
   __shared__ float sm_l[kWaves][GT];
   __shared__ float sm_acc[kWaves][GT][D];
-  if (r == 0) {
+  if (q == 0 && n < GT) {
+    sm_m[wave][n] = m_run;
+    sm_l[wave][n] = l_run;
+  }
 #pragma unroll
-    for (int g = 0; g < GT; ++g) {
+  for (int j = 0; j < 4; ++j) {
+    const int g = 4 * q + j;  // first replica of each head
+    if (g < GT) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_acc[wave][g][c * EPL + e] = acc[g][e];
-      if (c == 0) {
-        sm_m[wave][g] = m[g];
-        sm_l[wave][g] = l[g];
-      }
+      for (int v = 0; v < NV; ++v) sm_acc[wave][g][16 * v + n] = acc[v][j];
     }
   }
   const int any_bad = __syncthreads_or(bad);
@@ -299,6 +359,7 @@ hipError_t by_group(const DecodeParams& p, int32_t num_seqs, int gt, bool cached
     case 2: return launch_t<T, D, BS, 2, SPLIT>(p, num_seqs, cached, stream);
     case 4: return launch_t<T, D, BS, 4, SPLIT>(p, num_seqs, cached, stream);
     case 8: return launch_t<T, D, BS, 8, SPLIT>(p, num_seqs, cached, stream);
+    case 16: return launch_t<T, D, BS, 16, SPLIT>(p, num_seqs, cached, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -324,9 +385,10 @@ hipError_t by_dtype(const DecodeParams& p, int32_t num_seqs, pa_dtype dt, int d,
   return hipErrorInvalidValue;
 }
 
-// Largest head-group tile in {8, 4, 2, 1} dividing the group size.
+// Heads per workgroup: the largest of {16, 8, 4, 2, 1} dividing the group size
+// (16 fills the 16 columns of a q.K tile without replication).
 int group_tile(int group) {
-  for (int gt : {8, 4, 2}) if (group % gt == 0) return gt;
+  for (int gt : {16, 8, 4, 2}) if (group % gt == 0) return gt;
   return 1;
 }
 

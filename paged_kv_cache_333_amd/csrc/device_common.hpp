@@ -1,5 +1,5 @@
-// Device helpers shared by the gfx950 kernels: element types, 16-byte row
-// chunks, fp32 conversions, and cross-lane sums inside a row of lanes.
+// Device helpers shared by the gfx950 kernels: element types, 16-byte
+// chunks, conversions, matrix-core products on chunks, and lane moves.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -8,8 +8,6 @@
 namespace pa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Element types.  Every K/V/q row is moved in 16-byte chunks (one
 // global_load_dwordx4 per lane); EPL elements per chunk.
@@ -45,54 +43,6 @@ __device__ __forceinline__ uint32_t word(u32x4 w, int i) {
   return x;
 }
 
-// Unpack a 16-byte chunk into EPL floats (exact conversions).
-__device__ __forceinline__ void to_float(TF32, u32x4 w, float* f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f[i] = __builtin_bit_cast(float, word(w, i));
-}
-__device__ __forceinline__ void to_float(TF16, u32x4 w, float* f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f16x2 h = __builtin_bit_cast(f16x2, word(w, i));
-    f[2 * i] = static_cast<float>(h[0]);
-    f[2 * i + 1] = static_cast<float>(h[1]);
-  }
-}
-__device__ __forceinline__ void to_float(TBF16, u32x4 w, float* f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t x = word(w, i);
-    f[2 * i] = __builtin_bit_cast(float, x << 16);
-    f[2 * i + 1] = __builtin_bit_cast(float, x & 0xffff0000u);
-  }
-}
-
-// Dot product of two 16-byte chunks with fp32 accumulation.  fp16 and bf16
-// use the packed two-element dot instructions (products are exact in fp32).
-__device__ __forceinline__ float dot16(TF32, u32x4 a, u32x4 b) {
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    s = __builtin_fmaf(__builtin_bit_cast(float, word(a, i)), __builtin_bit_cast(float, word(b, i)), s);
-  return s;
-}
-__device__ __forceinline__ float dot16(TF16, u32x4 a, u32x4 b) {
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, word(a, i)), __builtin_bit_cast(f16x2, word(b, i)),
-                               s, false);
-  return s;
-}
-__device__ __forceinline__ float dot16(TBF16, u32x4 a, u32x4 b) {
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word(a, i)),
-                                        __builtin_bit_cast(bf16x2, word(b, i)), s, false);
-  return s;
-}
-
 // fp32 -> storage type, round to nearest even.
 __device__ __forceinline__ uint32_t from_float_bits(TF32, float x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ __forceinline__ uint16_t from_float_bits(TF16, float x) {
@@ -113,30 +63,77 @@ __device__ __forceinline__ void store_elem(T, void* base, int64_t idx, float x) 
     reinterpret_cast<uint16_t*>(base)[idx] = from_float_bits(T{}, x);
 }
 
-// DPP lane moves inside a 16-lane row.
-template <int kCtrl>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xf, 0xf, false));
-}
-constexpr int kQuadXor1 = 0xb1;      // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4e;      // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141;
-constexpr int kRowMirror = 0x140;
+// ---------------------------------------------------------------------------
+// Matrix-core products on 16-byte chunks.  For a 16x16 output tile C, lane
+// l = 16 q + r supplies chunk a of row r of A and chunk b of column r of B;
+// mma() adds, for every (m, n), the dot product of the chunks held by lanes
+// {16 q + m} of A and {16 q + n} of B over all four q (4 x EPL elements).
+// Lane 16 q + r receives C[4 q + j][r] in element j.  fp16/bf16 use one
+// v_mfma_f32_16x16x32; fp32 uses four v_mfma_f32_16x16x4 (one per element).
 
-// Sum over each aligned group of LPR lanes; every lane of the group gets the sum.
-// After the two quad steps all four lanes of a quad hold the quad's sum, so the
-// mirror steps (lane i <-> 7-i, then i <-> 15-i) pair each lane with a lane of
-// the other quad / half-row.
-template <int LPR>
-__device__ __forceinline__ float row_sum(float x) {
-  static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row width");
-  x += dpp<kQuadXor1>(x);
-  x += dpp<kQuadXor2>(x);
-  x += dpp<kRowHalfMirror>(x);
-  if constexpr (LPR >= 16) x += dpp<kRowMirror>(x);
-  if constexpr (LPR == 32) x += __shfl_xor(x, 16);
-  return x;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mma(TF16, u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                0, 0);
+}
+__device__ __forceinline__ f32x4 mma(TBF16, u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(TF32, u32x4 a, u32x4 b, f32x4 c) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, word(a, e)),
+                                             __builtin_bit_cast(float, word(b, e)), c, 0, 0, 0);
+  return c;
+}
+
+// EPL fp32 softmax weights -> one chunk of T, rounded to nearest even.  For
+// bf16, `lo` receives the rounded residual p - hi, so hi + lo carries about
+// 16 significant bits; the other types leave it untouched.
+__device__ __forceinline__ void pack_p(TF32, const float* p, u32x4& hi, u32x4&) {
+  hi = u32x4{__builtin_bit_cast(uint32_t, p[0]), __builtin_bit_cast(uint32_t, p[1]),
+             __builtin_bit_cast(uint32_t, p[2]), __builtin_bit_cast(uint32_t, p[3])};
+}
+__device__ __forceinline__ void pack_p(TF16, const float* p, u32x4& hi, u32x4&) {
+  f16x8 h;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(p[e]);
+  hi = __builtin_bit_cast(u32x4, h);
+}
+__device__ __forceinline__ void pack_p(TBF16, const float* p, u32x4& hi, u32x4& lo) {
+  bf16x8 h, l;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = static_cast<__bf16>(p[e]);
+    l[e] = static_cast<__bf16>(p[e] - static_cast<float>(h[e]));
+  }
+  hi = __builtin_bit_cast(u32x4, h);
+  lo = __builtin_bit_cast(u32x4, l);
+}
+
+// Bit mask keeping the first `keep` elements of a chunk (keep may be < 0 or > EPL).
+__device__ __forceinline__ u32x4 keep_mask(TF32, int keep) {
+  return u32x4{0 < keep ? ~0u : 0u, 1 < keep ? ~0u : 0u, 2 < keep ? ~0u : 0u, 3 < keep ? ~0u : 0u};
+}
+__device__ __forceinline__ u32x4 keep_mask_16(int keep) {
+  u32x4 m;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) m[w] = (2 * w < keep ? 0x0000ffffu : 0u) | (2 * w + 1 < keep ? 0xffff0000u : 0u);
+  return m;
+}
+__device__ __forceinline__ u32x4 keep_mask(TF16, int keep) { return keep_mask_16(keep); }
+__device__ __forceinline__ u32x4 keep_mask(TBF16, int keep) { return keep_mask_16(keep); }
+
+// Value of lane J of this lane's quad (DPP quad_perm [J, J, J, J]).
+template <int J>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               J | (J << 2) | (J << 4) | (J << 6), 0xf, 0xf,
+                                                               false));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -35,8 +35,8 @@ struct SplitLayout {
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,
                                     void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
-                                    int32_t num_blocks, int32_t num_kv_heads, int32_t row_bytes,
-                                    int32_t block_size, hipStream_t stream);
+                                    int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t elem_bytes, int32_t block_size, hipStream_t stream);
 hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
                               int32_t num_pairs, int32_t num_blocks, int64_t block_bytes,
                               hipStream_t stream);

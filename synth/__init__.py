@@ -120,6 +120,12 @@ def workload(key: int) -> Workload:
     raise ValueError(f"unknown workload {key}")
 
 
+def pool_shapes(w: Workload):
+    """Shapes of the key pool [NB, H_kv, bs, D] and the value pool [NB, H_kv, D, bs]."""
+    return ((w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim),
+            (w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size))
+
+
 # ----------------------------------------------------------------------------
 # tensor contents
 

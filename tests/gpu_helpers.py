@@ -71,19 +71,19 @@ class DeviceWorkload:
         self.device = dev
         self.tables = torch.tensor(tabs_c, dtype=torch.int32, device=dev)
         self.context_lens = torch.tensor(lens_c, dtype=torch.int32, device=dev)
-        pool_shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+        k_shape, v_shape = synth.pool_shapes(w)
         if pool_on_host is None:
             pool_on_host = key == 1
         if pool_on_host:
-            self.key_cache = synth.to_torch(synth.normal_host(pool_shape, self.seeds["key_cache"], w.dtype),
+            self.key_cache = synth.to_torch(synth.normal_host(k_shape, self.seeds["key_cache"], w.dtype),
                                             w.dtype).to(dev)
-            self.value_cache = synth.to_torch(synth.normal_host(pool_shape, self.seeds["value_cache"], w.dtype),
+            self.value_cache = synth.to_torch(synth.normal_host(v_shape, self.seeds["value_cache"], w.dtype),
                                               w.dtype).to(dev)
             self.query = synth.to_torch(synth.normal_host((w.num_seqs, w.num_heads, w.head_dim),
                                                           self.seeds["query"], w.dtype), w.dtype).to(dev)
         else:
-            self.key_cache = synth.normal_device(pool_shape, self.seeds["key_cache"], w.dtype)
-            self.value_cache = synth.normal_device(pool_shape, self.seeds["value_cache"], w.dtype)
+            self.key_cache = synth.normal_device(k_shape, self.seeds["key_cache"], w.dtype)
+            self.value_cache = synth.normal_device(v_shape, self.seeds["value_cache"], w.dtype)
             self.query = synth.normal_device((w.num_seqs, w.num_heads, w.head_dim), self.seeds["query"], w.dtype)
         self.out = torch.empty_like(self.query)
 
@@ -99,7 +99,8 @@ class DeviceWorkload:
         return tabs, lens
 
     def _fetch_blocks(self, table, g):
-        """Copy back the listed blocks of KV head g as [len(table), 1, bs, D] storage arrays."""
+        """Copy back the listed blocks of KV head g: keys [len(table), 1, bs, D], values
+        [len(table), 1, D, bs] (storage arrays)."""
         import torch
         idx = torch.tensor(table, dtype=torch.long, device=self.device)
         kc = synth.to_numpy(self.key_cache[:, g].index_select(0, idx), self.w.dtype)[:, None]

@@ -47,7 +47,7 @@ def scatter_case(seed, S, H, Hkv, D, bs, ctx, dtype, extra_blocks=3):
         tables[s, : need[s]] = perm[pos:pos + need[s]]
         pos += need[s]
     kc = normal_host((NB, Hkv, bs, D), seed + 1, dtype)
-    vc = normal_host((NB, Hkv, bs, D), seed + 2, dtype)
+    vc = normal_host((NB, Hkv, D, bs), seed + 2, dtype)
     q = normal_host((S, H, D), seed + 3, dtype)
     Ks, Vs = [], []
     for s in range(S):
@@ -57,7 +57,7 @@ def scatter_case(seed, S, H, Hkv, D, bs, ctx, dtype, extra_blocks=3):
         for t in range(n):
             b = tables[s, t // bs]
             K[:, t] = A.to_f64(kc[b, :, t % bs], dtype)
-            V[:, t] = A.to_f64(vc[b, :, t % bs], dtype)
+            V[:, t] = A.to_f64(vc[b, :, :, t % bs], dtype)
         Ks.append(K)
         Vs.append(V)
     return q, kc, vc, tables, list(ctx), Ks, Vs
@@ -201,7 +201,7 @@ def check_p4_gather_demo():
     case = [c for c in g["cases"] if c["source"] == "impl"][0]
     bs, n, table = case["block_size"], case["tokens"], case["table"]
     kc = normal_host((24, 1, bs, 8), 5, "f32")
-    vc = normal_host((24, 1, bs, 8), 6, "f32")
+    vc = normal_host((24, 1, 8, bs), 6, "f32")
     K, V = A.gather_kv(kc, vc, np.array(table), n, 0, "f32")
     assert K.shape == (n, 8)
     assert A.blocks_for(n, bs) == case["blocks"] == len(table)
@@ -209,7 +209,7 @@ def check_p4_gather_demo():
     assert rows_last == case["last_block_rows"]
     assert f"{(n % bs) / bs * 100:.0f}%" == case["last_block_fill_printed"]
     assert np.array_equal(K[48:50], kc[21, 0, 0:2].astype(np.float64))
-    assert np.array_equal(V[16:32], vc[7, 0].astype(np.float64))
+    assert np.array_equal(V[16:32], vc[7, 0].T.astype(np.float64))
 
 
 # --------------------------------------------------------------------------- allocator
@@ -272,14 +272,16 @@ def check_p4_cow_timeline():
     assert al.block_table("A") == ea["table_a"] and al.block_table("B") == ea["table_b"]
     # data: copy then write; the two blocks differ only at the written offset
     kc = normal_host((nb, 2, bs, 4), 1, "f16")
-    vc = normal_host((nb, 2, bs, 4), 2, "f16")
+    vc = normal_host((nb, 2, 4, bs), 2, "f16")
     kc, vc = C.copy_blocks(kc, vc, [[src, dst]])
     newk = normal_host((1, 2, 4), 3, "f16")
     newv = normal_host((1, 2, 4), 4, "f16")
     kc, vc = C.reshape_and_cache(newk, newv, kc, vc, [slot])
     differ = [o for o in range(bs) if not np.array_equal(kc[5, :, o], kc[42, :, o])]
     assert differ == [ea["differs_only_at_offset"]]
-    assert np.array_equal(kc[42, :, 8], newk[0]) and np.array_equal(vc[42, :, 8], newv[0])
+    differ_v = [o for o in range(bs) if not np.array_equal(vc[5, :, :, o], vc[42, :, :, o])]
+    assert differ_v == [ea["differs_only_at_offset"]]
+    assert np.array_equal(kc[42, :, 8], newk[0]) and np.array_equal(vc[42, :, :, 8], newv[0])
 
 
 def check_p2_lifecycle():

@@ -27,7 +27,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_status_strings():
-    assert pa.lib.pa_abi_version() == 1
+    assert pa.lib.pa_abi_version() == 2
     for code in range(9):
         assert pa.lib.pa_status_string(code)
     assert pa.lib.pa_status_string(99) == b"unknown status"

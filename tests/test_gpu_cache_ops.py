@@ -24,7 +24,7 @@ def test_reshape_and_cache_bit_exact(dtype, D, bs, Hkv):
     NB, T = 13, 37
     rng = np.random.default_rng(D + bs + Hkv)
     kc = synth.normal_host((NB, Hkv, bs, D), 1, dtype)
-    vc = synth.normal_host((NB, Hkv, bs, D), 2, dtype)
+    vc = synth.normal_host((NB, Hkv, D, bs), 2, dtype)
     key = synth.normal_host((T, Hkv, D), 3, dtype)
     val = synth.normal_host((T, Hkv, D), 4, dtype)
     slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int32)
@@ -43,7 +43,7 @@ def test_copy_blocks_bit_exact(dtype, D, bs, Hkv):
     NB = 20
     rng = np.random.default_rng(7 * D + bs)
     kc = synth.normal_host((NB, Hkv, bs, D), 5, dtype)
-    vc = synth.normal_host((NB, Hkv, bs, D), 6, dtype)
+    vc = synth.normal_host((NB, Hkv, D, bs), 6, dtype)
     ids = rng.permutation(NB)
     pairs = np.stack([ids[:6], ids[6:12]], axis=1).astype(np.int32)   # disjoint sources and targets
     ek, ev = C.copy_blocks(kc, vc, pairs)
@@ -101,10 +101,11 @@ def test_parallel_sampling_cow_step_bit_exact():
 def test_out_of_range_indices_write_nothing():
     dtype, D, bs, Hkv, NB = "f16", 128, 16, 2, 4
     kc = synth.normal_host((NB, Hkv, bs, D), 1, dtype)
+    vc = synth.normal_host((NB, Hkv, D, bs), 3, dtype)
     key = synth.normal_host((3, Hkv, D), 2, dtype)
-    dk, dv = _dev(kc, dtype), _dev(kc, dtype)
+    dk, dv = _dev(kc, dtype), _dev(vc, dtype)
     pa.pa_reshape_and_cache(_dev(key, dtype), _dev(key, dtype), dk, dv,
                             torch.tensor([NB * bs, NB * bs + 100, -5], dtype=torch.int32).cuda())
     pa.pa_copy_blocks(dk, dv, torch.tensor([[0, NB], [-1, 1], [NB + 3, 2]], dtype=torch.int32).cuda())
     torch.cuda.synchronize()
-    assert np.array_equal(synth.to_numpy(dk, dtype), kc) and np.array_equal(synth.to_numpy(dv, dtype), kc)
+    assert np.array_equal(synth.to_numpy(dk, dtype), kc) and np.array_equal(synth.to_numpy(dv, dtype), vc)

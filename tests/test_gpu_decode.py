@@ -33,7 +33,7 @@ def make_case(seed, dtype, S, H, Hkv, D, bs, ctx, extra_blocks=5, poison=False):
         tables[s, :need[s]] = perm[pos:pos + need[s]]
         pos += need[s]
     kc = synth.normal_host((NB, Hkv, bs, D), seed + 1, dtype)
-    vc = synth.normal_host((NB, Hkv, bs, D), seed + 2, dtype)
+    vc = synth.normal_host((NB, Hkv, D, bs), seed + 2, dtype)
     q = synth.normal_host((S, H, D), seed + 3, dtype)
     if poison:  # NaN in every row no sequence may read
         nan = {"f32": np.float32(np.nan), "f16": np.float16(np.nan), "bf16": np.uint16(0x7FC0)}[dtype]
@@ -45,7 +45,7 @@ def make_case(seed, dtype, S, H, Hkv, D, bs, ctx, extra_blocks=5, poison=False):
             for o in range(bs):
                 if not used[b, o]:
                     kc[b, :, o, :] = nan
-                    vc[b, :, o, :] = nan
+                    vc[b, :, :, o] = nan
     return dict(q=q, kc=kc, vc=vc, tables=tables, ctx=list(ctx), NB=NB, MB=MB, dtype=dtype, S=S, H=H,
                 Hkv=Hkv, D=D, bs=bs)
 
@@ -250,7 +250,7 @@ def test_identical_keys_give_mean_of_v_and_ctx1_gives_v0():
     for s in range(2):
         n = c["ctx"][s]
         for h in range(4):
-            V = np.stack([c["vc"][c["tables"][s, t // 16], h, t % 16] for t in range(n)]).astype(np.float64)
+            V = np.stack([c["vc"][c["tables"][s, t // 16], h, :, t % 16] for t in range(n)]).astype(np.float64)
             assert np.max(np.abs(got[s, h] - V.mean(axis=0))) <= 1e-5
             if n == 1:
                 assert np.array_equal(got[s, h], V[0])
@@ -297,9 +297,10 @@ def test_bad_launch_order_entries_do_not_fault():
 def test_zero_sequences_is_a_no_op():
     q = torch.empty((0, 4, 64), dtype=torch.float16, device="cuda")
     kc = torch.zeros((2, 4, 16, 64), dtype=torch.float16, device="cuda")
+    vc = torch.zeros((2, 4, 64, 16), dtype=torch.float16, device="cuda")
     t = torch.zeros((0, 1), dtype=torch.int32, device="cuda")
     cl = torch.zeros((0,), dtype=torch.int32, device="cuda")
-    pa.pa_decode(q, q, kc, kc, t, cl, 16, 0.125)
+    pa.pa_decode(q, q, kc, vc, t, cl, 16, 0.125)
     torch.cuda.synchronize()
 
 

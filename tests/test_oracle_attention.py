@@ -44,7 +44,8 @@ def test_single_token_context_returns_v0_exactly():
 def test_empty_context_gives_zeros():
     q = np.ones((1, 2, 8), dtype=np.float32)
     kc = np.ones((2, 2, 16, 8), dtype=np.float32)
-    out = A.paged_decode(q, kc, kc, np.array([[-1]], dtype=np.int32), [0], 0.3, "f32")
+    vc = np.ones((2, 2, 8, 16), dtype=np.float32)
+    out = A.paged_decode(q, kc, vc, np.array([[-1]], dtype=np.int32), [0], 0.3, "f32")
     assert np.array_equal(out, np.zeros((1, 2, 8)))
 
 
@@ -76,9 +77,10 @@ def test_scale_is_taken_at_float32():
     rng = np.random.default_rng(4)
     q = rng.standard_normal((1, 1, 64)).astype(np.float32)
     kc = rng.standard_normal((2, 1, 16, 64)).astype(np.float32)
+    vc = rng.standard_normal((2, 1, 64, 16)).astype(np.float32)
     t = np.array([[1, 0]], dtype=np.int32)
-    a = A.paged_decode(q, kc, kc, t, [20], 1 / 8.000001, "f32")
-    b = A.paged_decode(q, kc, kc, t, [20], float(np.float32(1 / 8.000001)), "f32")
+    a = A.paged_decode(q, kc, vc, t, [20], 1 / 8.000001, "f32")
+    b = A.paged_decode(q, kc, vc, t, [20], float(np.float32(1 / 8.000001)), "f32")
     assert np.array_equal(a, b)
 
 
@@ -94,5 +96,6 @@ def test_bf16_upcast_is_exact():
 def test_out_of_pool_table_entry_is_rejected():
     q = np.ones((1, 1, 8), dtype=np.float32)
     kc = np.ones((2, 1, 16, 8), dtype=np.float32)
+    vc = np.ones((2, 1, 8, 16), dtype=np.float32)
     with pytest.raises(IndexError):
-        A.paged_decode(q, kc, kc, np.array([[5]], dtype=np.int32), [3], 0.3, "f32")
+        A.paged_decode(q, kc, vc, np.array([[5]], dtype=np.int32), [3], 0.3, "f32")
