@@ -263,7 +263,8 @@ class Bench:
             nbytes = pa.pa_decode_split_workspace_bytes(S, H, D, self.max_ctx, args.partition)
             self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.dev)
 
-        # double-buffered index data, one pinned staging buffer and one upload per step:
+        # double-buffered index data, one pinned staging buffer and one upload (pa_upload, a
+        # kernel on the compute stream) per step:
         # [slots S | lens S | order S | pairs 2S | tables S*MB] int32
         self.ids = torch.arange(S, dtype=torch.int64).pin_memory()
         self.bufs = []
@@ -298,7 +299,7 @@ class Bench:
         if self.order == "longest":
             pa.pa_order_longest_first_into(b["len_h"].data_ptr(), S, b["order_h"].data_ptr())
             order = b["order_d"]
-        b["idx_d"].copy_(b["idx_h"], non_blocking=True)
+        pa.pa_upload(b["idx_d"], b["idx_h"])
         b["staged"].record(self.stream)
         if npairs:
             pa.pa_copy_blocks(self.kc, self.vc, b["pairs_d"], num_pairs=npairs)

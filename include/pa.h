@@ -205,6 +205,23 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* pair
                          int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
                          int32_t head_dim, int32_t block_size, pa_dtype dtype, void* stream);
 
+/* Move one step's index data (block tables, context lengths, slot mapping,
+ * copy pairs, launch order) from page-locked host memory to the device with a
+ * kernel on `stream`, instead of a copy-engine transfer.  This is the upload
+ * half of materialising the host bookkeeping on the device (block tables from
+ * the allocator, [ATB] §4.2 get_block_table / get_context_lens; slot_mapping,
+ * [ASC] §3.1).  On the compute stream a copy-engine transfer is bracketed by
+ * cross-engine synchronisations that idle the GPU for tens of microseconds
+ * per step; the kernel needs only the ordinary dispatch gap.
+ *   dst: device memory, nbytes bytes, 4-byte aligned.
+ *   src: page-locked host memory mapped for the device (hipHostMalloc, or a
+ *        torch tensor from pin_memory()), nbytes bytes, 4-byte aligned.  The
+ *        caller must not modify it until the work on `stream` has completed.
+ *   nbytes: a multiple of 4 (0 is a no-op).
+ * Returns PA_ERR_INVALID_ARG, without launching anything, when src is not
+ * such host memory or dst is not device memory.  Bit-exact. */
+pa_status pa_upload(void* dst, const void* src, size_t nbytes, void* stream);
+
 /* Single-pass paged decode attention ([IMPL] §3.1 index-based kernel and
  * §3.4 PagedAttention.forward; [ATB] §3.2 PagedAttentionOperation.apply;
  * [ASC] §三/§四 fused gather + QK^T + softmax + OV):

@@ -6,7 +6,7 @@ stream.  Importing this package fails loudly when libpa.so has not been
 built (python paged_kv_cache_333_amd/build.py): there is no fallback.
 
 Names follow the C ABI in include/pa.h:
-  pa_reshape_and_cache, pa_copy_blocks, pa_decode, pa_decode_split,
+  pa_reshape_and_cache, pa_copy_blocks, pa_upload, pa_decode, pa_decode_split,
   pa_decode_split_workspace_bytes, pa_lse_reduce, and the allocator verbs as
   methods of `Allocator` (pa_seq_create -> Allocator.seq_create, ...).
 """
@@ -85,6 +85,7 @@ _PROTOS = {
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_order_longest_first": (_i32, [_pi32, _i32, _pi32]),
+    "pa_upload": (_i32, [_vp, _vp, _sz, _vp]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                          _f32, _i32, _u32, _vp]),
     "pa_decode_split_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -174,6 +175,17 @@ def pa_copy_blocks(key_cache, value_cache, pairs, stream=None, num_pairs=None):
     P = pairs.shape[0] if num_pairs is None else num_pairs
     _check(lib.pa_copy_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(pairs), P, NB, H_kv, D, bs,
                               _dtype_code(key_cache), _stream(stream)), "pa_copy_blocks")
+
+
+def pa_upload(dst, src, stream=None):
+    """Copy the pinned host tensor `src` into the device tensor `dst` (same byte size) with a
+    kernel on the stream: no copy engine, no cross-engine synchronisation."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("pa_upload: dst and src differ in size")
+    if not src.is_pinned():
+        raise ValueError("pa_upload: src must be a pinned host tensor (pin_memory())")
+    _check(lib.pa_upload(_ptr(dst), _ptr(src), nbytes, _stream(stream)), "pa_upload")
 
 
 def _opt(t):

@@ -235,6 +235,30 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* pair
                 st, "pa_copy_blocks");
 }
 
+pa_status pa_upload(void* dst, const void* src, size_t nbytes, void* stream) {
+  if (nbytes == 0) return PA_OK;
+  if (!dst || !src) return fail(PA_ERR_INVALID_ARG, "null pointer");
+  if ((nbytes & 3u) || (reinterpret_cast<uintptr_t>(dst) & 3u) || (reinterpret_cast<uintptr_t>(src) & 3u))
+    return fail(PA_ERR_INVALID_ARG, "pa_upload moves whole 4-byte words: pointers and nbytes must be 4-aligned");
+  // The kernel dereferences the source from the GPU, so both ends of the range
+  // must lie in page-locked host memory mapped for the device, contiguously.
+  hipPointerAttribute_t first{}, last{}, d{};
+  const char* end = static_cast<const char*>(src) + nbytes - 1;
+  const bool ok_first = hipPointerGetAttributes(&first, src) == hipSuccess;
+  const bool ok_last = ok_first && hipPointerGetAttributes(&last, end) == hipSuccess;
+  const bool ok_dst = hipPointerGetAttributes(&d, dst) == hipSuccess;
+  (void)hipGetLastError();  // a failed query must not surface as a later launch error
+  if (!ok_first || !ok_last || first.type != hipMemoryTypeHost || last.type != hipMemoryTypeHost ||
+      !first.devicePointer ||
+      static_cast<const char*>(last.devicePointer) - static_cast<const char*>(first.devicePointer) !=
+          static_cast<ptrdiff_t>(nbytes - 1))
+    return fail(PA_ERR_INVALID_ARG, "pa_upload: src must be page-locked host memory mapped for the device");
+  if (!ok_dst || d.type != hipMemoryTypeDevice)
+    return fail(PA_ERR_INVALID_ARG, "pa_upload: dst must be device memory");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return finish(pa::launch_upload(dst, first.devicePointer, static_cast<int64_t>(nbytes), st), st, "pa_upload");
+}
+
 pa_status pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
                     const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
                     int32_t num_seqs,

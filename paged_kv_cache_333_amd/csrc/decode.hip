@@ -79,7 +79,7 @@ struct DecodeParams {
 };
 
 template <typename T, int D, int BS, int GT, bool SPLIT, bool CACHED>
-__global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams a) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void decode_kernel(DecodeParams a) {
   constexpr int EPL = T::kEPL;       // elements per 16-byte chunk
   constexpr int E = T::kBytes;
   constexpr int KV = D / EPL / 4;    // q.K products per 16-token tile (chunks 4v + q of a row)
@@ -134,21 +134,40 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams a) {
 
   const int n_steps = (t_end - t_begin + TS - 1) / TS;
   const int64_t hkv = a.num_kv_heads;
+  // Block ids are prefetched with one vector load per wave: lane i holds the
+  // id of block i % NBS of the wave's step k + i / NBS, for the next IDS_PER
+  // steps, so a step's K/V loads never wait for a table lookup.  Indices are
+  // clamped into the table row; an id is used (and validated) only below b_end.
+  constexpr int IDS_PER = 64 / NBS;  // steps covered by one prefetch
+  const int mb_last = a.max_blocks - 1;
+  const int lane_step = lane / NBS, lane_blk = lane - lane_step * NBS;
+  auto fetch_ids = [&](int first_step) {
+    const int st_l = first_step + kWaves * lane_step;
+    const int b = (t_begin + st_l * TS) / BS + lane_blk;
+    return trow[min(b, mb_last)];
+  };
+  int32_t ids = mb_last >= 0 ? fetch_ids(wave) : 0;  // needs only s, not the context length
+  int k_ids = 0;                                    // steps consumed from `ids`
   for (int st = wave; st < n_steps; st += kWaves) {
     const int t0 = t_begin + st * TS;
     const int b0 = t0 / BS;
     const int off0 = t0 - b0 * BS;  // nonzero only when a step is shorter than a block
+    if (k_ids == IDS_PER) {
+      ids = fetch_ids(st);
+      k_ids = 0;
+    }
     int32_t ph[NBS];
     bool skip = false;
 #pragma unroll
     for (int i = 0; i < NBS; ++i) {
+      ph[i] = __builtin_amdgcn_readlane(ids, NBS * k_ids + i);
       if (b0 + i < b_end) {
-        ph[i] = trow[b0 + i];
         if (static_cast<uint32_t>(ph[i]) >= static_cast<uint32_t>(a.num_blocks)) skip = true;
       } else {
         ph[i] = -1;  // past the context: masked below, read from block ph[0]
       }
     }
+    ++k_ids;
     if (skip) {
       bad = 1;
       continue;
@@ -180,6 +199,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams a) {
       for (int v = 0; v < NV; ++v)
         vr[v] = CACHED ? load16(vp + v * 16 * BS * E) : load16_stream(vp + v * 16 * BS * E);
     }
+    // All of the step's loads are issued before any of them is consumed.
+    __builtin_amdgcn_sched_barrier(0);
 
     f32x4 c[NT];
 #pragma unroll

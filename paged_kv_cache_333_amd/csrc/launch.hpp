@@ -40,6 +40,7 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* ke
 hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
                               int32_t num_pairs, int32_t num_blocks, int64_t block_bytes,
                               hipStream_t stream);
+hipError_t launch_upload(void* dst, const void* src_device_view, int64_t nbytes, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeArgs& a, const SplitLayout& ws, hipStream_t stream);
 hipError_t launch_lse_reduce(void* out, const SplitLayout& ws, const int32_t* context_lens,

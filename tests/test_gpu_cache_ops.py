@@ -109,3 +109,32 @@ def test_out_of_range_indices_write_nothing():
     pa.pa_copy_blocks(dk, dv, torch.tensor([[0, NB], [-1, 1], [NB + 3, 2]], dtype=torch.int32).cuda())
     torch.cuda.synchronize()
     assert np.array_equal(synth.to_numpy(dk, dtype), kc) and np.array_equal(synth.to_numpy(dv, dtype), vc)
+
+
+def test_upload_is_bit_exact_and_sees_rewrites_of_the_staging_buffer():
+    """pa_upload copies a pinned host buffer word for word; rewriting the same staging
+    buffer and uploading again (as a double-buffered step loop does) yields the new words."""
+    rng = np.random.default_rng(5)
+    for n in (1, 7, 1000, 70_001):      # ragged sizes, beyond one pass of the grid
+        host = torch.empty(n, dtype=torch.int32).pin_memory()
+        dev = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            vals = rng.integers(-2**31, 2**31 - 1, size=n, dtype=np.int64).astype(np.int32)
+            host.numpy()[:] = vals
+            pa.pa_upload(dev, host)
+            torch.cuda.synchronize()
+            assert np.array_equal(dev.cpu().numpy(), vals)
+
+
+def test_upload_rejects_pageable_source_without_launching():
+    host = torch.arange(64, dtype=torch.int32)          # ordinary (pageable) memory
+    dev = torch.zeros(64, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    st = pa.lib.pa_upload(dev.data_ptr(), host.data_ptr(), 256, stream)
+    assert st == 1  # PA_ERR_INVALID_ARG
+    pinned = torch.arange(64, dtype=torch.int32).pin_memory()
+    st = pa.lib.pa_upload(pinned.data_ptr(), pinned.data_ptr(), 256, stream)   # dst on the host
+    assert st == 1
+    pa.pa_upload(dev, pinned)                           # the runtime state is clean afterwards
+    torch.cuda.synchronize()
+    assert torch.equal(dev.cpu(), pinned)
