@@ -134,10 +134,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
 
   const int n_steps = (t_end - t_begin + TS - 1) / TS;
   const int64_t hkv = a.num_kv_heads;
-  // Block ids are prefetched with one vector load per wave: lane i holds the
-  // id of block i % NBS of the wave's step k + i / NBS, for the next IDS_PER
-  // steps, so a step's K/V loads never wait for a table lookup.  Indices are
-  // clamped into the table row; an id is used (and validated) only below b_end.
+  // Block ids.  The first step's come through the scalar path, which a new
+  // workgroup reaches without queueing behind the streaming loads the other
+  // workgroups on its CU have in flight.  Later steps' ids are prefetched with
+  // one vector load per wave: lane i holds the id of block i % NBS of the
+  // wave's step k + i / NBS, for the next IDS_PER steps, so no step waits for
+  // a table lookup.  Indices are clamped into the table row; an id is used
+  // (and validated) only below b_end.
   constexpr int IDS_PER = 64 / NBS;  // steps covered by one prefetch
   const int mb_last = a.max_blocks - 1;
   const int lane_step = lane / NBS, lane_blk = lane - lane_step * NBS;
@@ -146,8 +149,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     const int b = (t_begin + st_l * TS) / BS + lane_blk;
     return trow[min(b, mb_last)];
   };
-  int32_t ids = mb_last >= 0 ? fetch_ids(wave) : 0;  // needs only s, not the context length
-  int k_ids = 0;                                    // steps consumed from `ids`
+  int32_t ph_first[NBS];
+  int32_t ids = 0;
+  if (mb_last >= 0) {  // needs only s, not the context length
+    const int b = (t_begin + wave * TS) / BS;
+#pragma unroll
+    for (int i = 0; i < NBS; ++i) ph_first[i] = trow[min(b + i, mb_last)];
+    ids = fetch_ids(wave + kWaves);
+  }
+  int k_ids = -1;  // steps consumed from `ids`; -1: the first step uses ph_first
   for (int st = wave; st < n_steps; st += kWaves) {
     const int t0 = t_begin + st * TS;
     const int b0 = t0 / BS;
@@ -160,7 +170,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     bool skip = false;
 #pragma unroll
     for (int i = 0; i < NBS; ++i) {
-      ph[i] = __builtin_amdgcn_readlane(ids, NBS * k_ids + i);
+      ph[i] = k_ids < 0 ? ph_first[i] : __builtin_amdgcn_readlane(ids, NBS * k_ids + i);
       if (b0 + i < b_end) {
         if (static_cast<uint32_t>(ph[i]) >= static_cast<uint32_t>(a.num_blocks)) skip = true;
       } else {
