@@ -14,11 +14,13 @@
 // consecutive elements along the contraction axis of its product: head_dim
 // for q.K, tokens for P.V, which is what a matrix-core operand wants.
 //
-// Work decomposition.  A workgroup of kWaves waves owns one (sequence, GT
-// query heads that share a KV head, token range); the range is the whole
-// context (single pass) or one partition (split).  A wave walks the range in
-// steps of TS tokens (32 for fp16/bf16, 16 for fp32); wave w takes steps
-// w, w + kWaves, ...  In a step, with lane = 16 q + n:
+// Work decomposition.  A workgroup of kWaves waves serves one (sequence, GT
+// query heads that share a KV head).  Single pass: the waves share the whole
+// context, wave w taking steps w, w + kWaves, ... of TS tokens (32 for
+// fp16/bf16, 16 for fp32), and merge through LDS at the end.  Split: each wave
+// owns one partition outright and writes its partial (m, l, o) itself, so a
+// workgroup covers kWaves consecutive partitions with no barrier.  In a step,
+// with lane = 16 q + n:
 //   * q.K: one 16x16 tile per 16 tokens, C[m][n'] = sum_d K[tok(m)][d] Q[n'][d]
 //     on v_mfma_f32_16x16x32_{f16,bf16} (fp32: 16x16x4).  Column n' of Q is
 //     query head n' % GT, so the GT heads are replicated to fill the 16
@@ -107,12 +109,18 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int nctx = a.ctx[s];
   const bool bad_len = nctx < 0 || nctx > a.len_limit;
 
-  int t_begin = 0, t_end = bad_len ? 0 : nctx;
+  // Single pass: the workgroup's waves share the context, wave w taking steps
+  // w, w + kWaves, ...  Split: each wave owns one partition outright (partition
+  // blockIdx.y * kWaves + wave) and writes its partial itself.
+  constexpr int WSTEP = SPLIT ? 1 : kWaves;
+  int t_begin = 0, t_end = bad_len ? 0 : nctx, part = 0;
   if constexpr (SPLIT) {
-    t_begin = blockIdx.y * a.part_size;
-    if (bad_len || t_begin >= nctx) return;  // nothing to write for this partition
+    part = blockIdx.y * kWaves + wave;
+    t_begin = part * a.part_size;
+    if (bad_len || t_begin >= nctx) return;  // nothing to write for this partition (no barrier follows)
     t_end = min(t_begin + a.part_size, nctx);
   }
+  const int st_first = SPLIT ? 0 : wave;
   const int b_end = (t_end + BS - 1) / BS;
   const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.max_blocks;
 
@@ -145,20 +153,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int mb_last = a.max_blocks - 1;
   const int lane_step = lane / NBS, lane_blk = lane - lane_step * NBS;
   auto fetch_ids = [&](int first_step) {
-    const int st_l = first_step + kWaves * lane_step;
+    const int st_l = first_step + WSTEP * lane_step;
     const int b = (t_begin + st_l * TS) / BS + lane_blk;
     return trow[min(b, mb_last)];
   };
   int32_t ph_first[NBS];
   int32_t ids = 0;
   if (mb_last >= 0) {  // needs only s, not the context length
-    const int b = (t_begin + wave * TS) / BS;
+    const int b = (t_begin + st_first * TS) / BS;
 #pragma unroll
     for (int i = 0; i < NBS; ++i) ph_first[i] = trow[min(b + i, mb_last)];
-    ids = fetch_ids(wave + kWaves);
+    ids = fetch_ids(st_first + WSTEP);
   }
   int k_ids = -1;  // steps consumed from `ids`; -1: the first step uses ph_first
-  for (int st = wave; st < n_steps; st += kWaves) {
+  for (int st = st_first; st < n_steps; st += WSTEP) {
     const int t0 = t_begin + st * TS;
     const int b0 = t0 / BS;
     const int off0 = t0 - b0 * BS;  // nonzero only when a step is shorter than a block
@@ -282,6 +290,39 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
 
+  if constexpr (SPLIT) {
+    // This wave's partition: (m_p in natural-log units, l_p, o_p = acc / l_p)
+    // for each of the GT heads.  acc[.][j] belongs to head (4q + j) % GT, whose
+    // l sits in a lane of the same row (see the rescale above).
+    float lg[4];
+    if constexpr (4 % GT == 0) {
+      lg[0] = quad_bcast<0>(l_run);
+      lg[1] = quad_bcast<1>(l_run);
+      lg[2] = quad_bcast<2>(l_run);
+      lg[3] = quad_bcast<3>(l_run);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lg[j] = __shfl(l_run, 16 * q + (4 * q + j) % GT);
+    }
+    const float qnan = __builtin_nanf("");
+    const int64_t sh0 = static_cast<int64_t>(s) * a.num_heads + h0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int g = 4 * q + j;  // first replica of each head
+      if (g < GT) {
+        float* o = a.ws_o + ((sh0 + g) * a.num_parts + part) * D + n;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) o[16 * v] = bad ? qnan : acc[v][j] / lg[j];
+      }
+    }
+    if (q == 0 && n < GT) {
+      const int64_t idx = (sh0 + n) * a.num_parts + part;
+      a.ws_m[idx] = m_run * 0.6931471805599453f;  // back to natural-log units
+      a.ws_l[idx] = bad ? qnan : l_run;
+    }
+    return;
+  }
+
   __shared__ float sm_m[kWaves][GT];
   __shared__ float sm_l[kWaves][GT];
   __shared__ float sm_acc[kWaves][GT][D];
@@ -314,57 +355,76 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       A = __builtin_fmaf(sm_acc[w][g][d], wt, A);
     }
     const int64_t sh = static_cast<int64_t>(s) * a.num_heads + h0 + g;
-    if constexpr (SPLIT) {
-      const int64_t idx = sh * a.num_parts + blockIdx.y;
-      const float qnan = __builtin_nanf("");
-      if (d == 0) {
-        a.ws_m[idx] = M * 0.6931471805599453f;  // back to natural-log units
-        a.ws_l[idx] = any_bad ? qnan : L;
-      }
-      a.ws_o[idx * D + d] = any_bad ? qnan : A / L;
-    } else {
-      const float val = any_bad || bad_len ? __builtin_nanf("") : (L > 0.f ? A / L : 0.f);
-      store_elem(T{}, a.out, sh * D + d, val);
-    }
+    const float val = any_bad || bad_len ? __builtin_nanf("") : (L > 0.f ? A / L : 0.f);
+    store_elem(T{}, a.out, sh * D + d, val);
   }
 }
 
 // Log-sum-exp merge of split partials: M = max_p m_p, w_p = l_p exp(m_p - M),
-// out = sum_p w_p o_p / sum_p w_p.  One workgroup per (sequence, head), one
-// lane per output element.
+// out = sum_p w_p o_p / sum_p w_p.  One workgroup of four waves per
+// (sequence, head): the threads first take the max of m_p together, then wave
+// w accumulates partitions w, w + 4, ... with each lane holding D / 64 output
+// dims and several partitions' loads in flight; the waves' sums share M and
+// are added through LDS.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void lse_reduce_kernel(void* out, const float* __restrict__ ws_m,
-                                                       const float* __restrict__ ws_l,
-                                                       const float* __restrict__ ws_o,
-                                                       const int32_t* __restrict__ ctx,
-                                                       const int32_t* __restrict__ order, int32_t num_seqs,
-                                                       int32_t num_heads, int32_t len_limit,
-                                                       int32_t part_size, int32_t num_parts) {
+__global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float* __restrict__ ws_m,
+                                                         const float* __restrict__ ws_l,
+                                                         const float* __restrict__ ws_o,
+                                                         const int32_t* __restrict__ ctx,
+                                                         const int32_t* __restrict__ order, int32_t num_seqs,
+                                                         int32_t num_heads, int32_t len_limit,
+                                                         int32_t part_size, int32_t num_parts) {
   constexpr float kLog2e = 1.4426950408889634f;
+  constexpr int DPL = D / 64;  // output dims per lane
   const int slot = blockIdx.x / num_heads;
   const int h = blockIdx.x - slot * num_heads;
   const int s = order ? order[slot] : slot;  // same sequence set as the partials pass
   if (static_cast<uint32_t>(s) >= static_cast<uint32_t>(num_seqs)) return;
   const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
-  const int d = threadIdx.x;
   const int n = ctx[s];
   if (n < 0 || n > len_limit) {
-    store_elem(T{}, out, sh * D + d, __builtin_nanf(""));
+    if (threadIdx.x < D) store_elem(T{}, out, sh * D + threadIdx.x, __builtin_nanf(""));
     return;
   }
   const int np = (n + part_size - 1) / part_size;
   const float* mp = ws_m + sh * num_parts;
   const float* lp = ws_l + sh * num_parts;
-  const float* op = ws_o + sh * num_parts * D + d;
+  const float* op = ws_o + sh * num_parts * D;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+
+  __shared__ float sm_max[4];
+  __shared__ float sm_l[4];
+  __shared__ float sm_a[4][D];
   float M = -__builtin_huge_valf();
-  for (int p = 0; p < np; ++p) M = fmaxf(M, mp[p]);
-  float L = 0.f, A = 0.f;
-  for (int p = 0; p < np; ++p) {
+  for (int p = threadIdx.x; p < np; p += 256) M = fmaxf(M, mp[p]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) sm_max[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(sm_max[0], sm_max[1]), fmaxf(sm_max[2], sm_max[3]));
+
+  float L = 0.f, A[DPL];
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) A[k] = 0.f;
+#pragma unroll 4
+  for (int p = wave; p < np; p += 4) {
     const float w = lp[p] * fast_exp2((mp[p] - M) * kLog2e);
     L += w;
-    A = __builtin_fmaf(w, op[static_cast<int64_t>(p) * D], A);
+    const float* o = op + static_cast<int64_t>(p) * D + lane * DPL;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) A[k] = __builtin_fmaf(w, o[k], A[k]);
   }
-  store_elem(T{}, out, sh * D + d, np == 0 ? 0.f : A / L);
+  if (lane == 0) sm_l[wave] = L;
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) sm_a[wave][lane * DPL + k] = A[k];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    const float Ls = (sm_l[0] + sm_l[1]) + (sm_l[2] + sm_l[3]);
+    const float As = (sm_a[0][d] + sm_a[1][d]) + (sm_a[2][d] + sm_a[3][d]);
+    store_elem(T{}, out, sh * D + d, np == 0 ? 0.f : As / Ls);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -375,7 +435,7 @@ namespace {
 template <typename T, int D, int BS, int GT, bool SPLIT>
 hipError_t launch_t(const DecodeParams& p, int32_t num_seqs, bool cached, hipStream_t stream) {
   const uint32_t gx = static_cast<uint32_t>(num_seqs) * (p.num_heads / GT);
-  const uint32_t gy = SPLIT ? static_cast<uint32_t>(p.num_parts) : 1u;
+  const uint32_t gy = SPLIT ? static_cast<uint32_t>((p.num_parts + kWaves - 1) / kWaves) : 1u;
   if (cached)
     hipLaunchKernelGGL((decode_kernel<T, D, BS, GT, SPLIT, true>), dim3(gx, gy), dim3(kWaves * 64), 0, stream, p);
   else
@@ -472,7 +532,7 @@ hipError_t launch_lse_reduce(void* out, const SplitLayout& ws, const int32_t* ct
                              pa_dtype dt, hipStream_t stream) {
   const dim3 grid(static_cast<uint32_t>(num_seqs) * num_heads);
 #define PA_REDUCE(T, D)                                                                          \
-  hipLaunchKernelGGL((lse_reduce_kernel<T, D>), grid, dim3(D), 0, stream, out, ws.m, ws.l, ws.o, \
+  hipLaunchKernelGGL((lse_reduce_kernel<T, D>), grid, dim3(256), 0, stream, out, ws.m, ws.l, ws.o, \
                      ctx, order, num_seqs, num_heads, len_limit, ws.partition_size, ws.num_parts)
   if (head_dim == 64) {
     if (dt == PA_F32) PA_REDUCE(TF32, 64);
