@@ -37,8 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--path", choices=["single", "split"], default=None,
-                    help="decode path (default: split for workload 4, single otherwise)")
+    ap.add_argument("--path", choices=["auto", "single", "split"], default="auto",
+                    help="decode path: pa_decode_auto (default: the library picks), pa_decode or pa_decode_split")
     ap.add_argument("--partition", type=int, default=512)
     ap.add_argument("--order", choices=["longest", "index"], default=None,
                     help="launch order of the sequences (default: index for workload 5, whose forked branches "
@@ -132,6 +132,7 @@ def _counter_per_dispatch(folder: str, counter: str, kernel_substr: str) -> tupl
 
 
 def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
+    # the path pa_decode_auto takes on these workloads (the bench line reports it)
     w_path = path or ("split" if workload == 4 else "single")
     decode = "decode_kernel"
     stats = _csv_rows(os.path.join(outdir, "trace"), "kernel_stats.csv")
@@ -218,7 +219,8 @@ class Bench:
         self.np, self.torch, self.pa, self.synth = np, torch, pa, synth
         self.args = args
         self.w = w = synth.workload(args.workload)
-        self.path = args.path or ("split" if args.workload == 4 else "single")
+        self.path = args.path
+        self.path_ran = set()
         shared = args.workload == 5
         self.order = args.order or ("index" if shared else "longest")
         self.cached = (args.cache or ("cached" if shared else "stream")) == "cached"
@@ -259,7 +261,8 @@ class Bench:
         self.newk = synth.normal_device((R, S, Hkv, D), seeds["new_key"], w.dtype)
         self.newv = synth.normal_device((R, S, Hkv, D), seeds["new_value"], w.dtype)
         self.out = torch.empty_like(self.q)
-        if self.path == "split":
+        self.ws = None
+        if self.path != "single":
             nbytes = pa.pa_decode_split_workspace_bytes(S, H, D, self.max_ctx, args.partition)
             self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.dev)
 
@@ -311,9 +314,15 @@ class Bench:
         if self.path == "single":
             pa.pa_decode(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"], self.max_ctx, w.scale,
                          seq_order=order, cached_kv=self.cached)
-        else:
+            self.path_ran.add("single")
+        elif self.path == "split":
             pa.pa_decode_split(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"], self.max_ctx, w.scale,
                                self.args.partition, self.ws, seq_order=order, cached_kv=self.cached)
+            self.path_ran.add("split")
+        else:
+            self.path_ran.add(pa.pa_decode_auto(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"],
+                                                self.max_ctx, w.scale, self.args.partition, self.ws,
+                                                seq_order=order, cached_kv=self.cached))
         if timing is not None:
             e1.record(self.stream)
             lens = b["len_h"].numpy()
@@ -399,7 +408,7 @@ def main():
     avg_dur = sum(durs) / len(durs)
     avg_bytes = sum(alg_bytes) / len(alg_bytes)
     achieved = avg_bytes / avg_dur / 1e9
-    traffic = measured_traffic(args.workload, bench.path)
+    traffic = measured_traffic(args.workload, "+".join(sorted(bench.path_ran)))
     res = {
         "metric": "paged decode attention: KV GB/s achieved (% of HBM peak) and KV tokens/s",
         "value": kv_tokens / wall,
@@ -416,8 +425,9 @@ def main():
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "context_lens": "per workload definition, +1 token per step",
-                   "mean_kv_tokens_per_step": kv_tokens / len(timing), "decode_path": bench.path,
-                   "partition_size": args.partition if bench.path == "split" else None,
+                   "mean_kv_tokens_per_step": kv_tokens / len(timing),
+                   "decode_path": ("auto: " if bench.path == "auto" else "") + "+".join(sorted(bench.path_ran)),
+                   "partition_size": args.partition if "split" in bench.path_ran else None,
                    "launch_order": bench.order, "kv_cache_policy": "cached" if bench.cached else "stream",
                    "cow_pairs_per_step": sum(t[4] for t in timing) / len(timing)},
         "decode_kernel_us": avg_dur * 1e6,

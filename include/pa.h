@@ -277,6 +277,27 @@ pa_status pa_decode_split(void* out, const void* query, const void* key_cache,
                           float scale, pa_dtype dtype, uint32_t flags, int32_t partition_size,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode with the path chosen for the launch.  The vLLM notes of [ATB] §2.3
+ * keep a second kernel for few, very long requests; here the choice comes
+ * from the launch shape instead of the page's length thresholds:
+ *   split (pa_decode_split with partition_size and workspace) when the single
+ *   pass would start fewer workgroups than the device holds at once
+ *   (num_seqs x KV-head groups below the resident capacity, so compute units
+ *   would idle while a few workgroups walk long contexts) and max_context_len
+ *   spans at least 4 partitions;
+ *   otherwise the single pass (pa_decode).
+ * Same arguments and error behaviour as pa_decode_split.  workspace may be
+ * NULL, or smaller than pa_decode_split_workspace_bytes for this shape: then
+ * the single pass runs.  *path (may be NULL) receives 0 for the single pass
+ * and 1 for split.  Both paths agree within the stated tolerances. */
+pa_status pa_decode_auto(void* out, const void* query, const void* key_cache, const void* value_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
+                         int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                         int32_t max_context_len, float scale, pa_dtype dtype, uint32_t flags,
+                         int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* path,
+                         void* stream);
+
 /* Log-sum-exp merge of split partials (the standard rule; the pages do not
  * spell it out): with M = max_p m_p and w_p = l_p * exp(m_p - M),
  *   out[s,h,:] = sum_p w_p o_p / sum_p w_p   over p < ceil(n / partition_size),

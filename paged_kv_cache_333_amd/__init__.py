@@ -6,7 +6,7 @@ stream.  Importing this package fails loudly when libpa.so has not been
 built (python paged_kv_cache_333_amd/build.py): there is no fallback.
 
 Names follow the C ABI in include/pa.h:
-  pa_reshape_and_cache, pa_copy_blocks, pa_upload, pa_decode, pa_decode_split,
+  pa_reshape_and_cache, pa_copy_blocks, pa_upload, pa_decode, pa_decode_split, pa_decode_auto,
   pa_decode_split_workspace_bytes, pa_lse_reduce, and the allocator verbs as
   methods of `Allocator` (pa_seq_create -> Allocator.seq_create, ...).
 """
@@ -91,6 +91,8 @@ _PROTOS = {
     "pa_decode_split_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode_split": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                _i32, _f32, _i32, _u32, _i32, _vp, _sz, _vp]),
+    "pa_decode_auto": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                              _i32, _f32, _i32, _u32, _i32, _vp, _sz, _pi32, _vp]),
     "pa_lse_reduce": (_i32, [_vp, _vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_status_string": (C.c_char_p, [_i32]),
     "pa_last_error": (C.c_char_p, []),
@@ -223,6 +225,23 @@ def pa_decode_split(out, query, key_cache, value_cache, block_tables, context_le
                                block_tables.shape[1], NB, max_context_len, scale, _dtype_code(query),
                                PA_DECODE_CACHED_KV if cached_kv else 0, partition_size, _ptr(workspace), nbytes,
                                _stream(stream)), "pa_decode_split")
+
+
+def pa_decode_auto(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len: int,
+                   scale: float, partition_size: int = 512, workspace=None, stream=None, seq_order=None,
+                   cached_kv: bool = False) -> str:
+    """pa_decode or pa_decode_split, chosen by the library for this launch; returns
+    "single" or "split"."""
+    S, H, D = query.shape
+    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    path = C.c_int32(-1)
+    _check(lib.pa_decode_auto(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+                              _ptr(context_lens), _opt(seq_order), S, H, H_kv, D, bs, block_tables.shape[1], NB,
+                              max_context_len, scale, _dtype_code(query), PA_DECODE_CACHED_KV if cached_kv else 0,
+                              partition_size, _opt(workspace), nbytes, C.byref(path), _stream(stream)),
+           "pa_decode_auto")
+    return "split" if path.value == 1 else "single"
 
 
 def pa_lse_reduce(out, workspace, context_lens, max_context_len: int, partition_size: int, stream=None):

@@ -308,6 +308,41 @@ pa_status pa_decode_split(void* out, const void* query, const void* key_cache, c
   return finish(pa::launch_decode_split(a, ws, st), st, "pa_decode_split");
 }
 
+pa_status pa_decode_auto(void* out, const void* query, const void* key_cache, const void* value_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
+                         int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                         int32_t max_context_len, float scale, pa_dtype dtype, uint32_t flags,
+                         int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* path,
+                         void* stream) {
+  pa::DecodeArgs a = pack(out, query, key_cache, value_cache, block_tables, context_lens, seq_order, num_seqs,
+                          num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                          max_context_len, scale, dtype, flags);
+  pa_status s = check_decode_args(a);
+  if (s != PA_OK) return s;
+  bool split = false;
+  if (workspace && num_seqs > 0 && partition_size > 0 && partition_size % block_size == 0 &&
+      partition_size <= 4096 && max_context_len >= 4 * static_cast<int64_t>(partition_size) &&
+      workspace_bytes >= pa_decode_split_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
+                                                         partition_size)) {
+    // Split only when the single pass could not fill the device: fewer
+    // workgroups than it holds at once means some compute units would sit idle
+    // while a few workgroups walk very long contexts.
+    int64_t workgroups = 0, resident = 0;
+    if (pa::single_pass_shape(a, &workgroups, &resident) == hipSuccess) split = workgroups < resident;
+    (void)hipGetLastError();
+  }
+  if (path) *path = split ? 1 : 0;
+  if (split)
+    return pa_decode_split(out, query, key_cache, value_cache, block_tables, context_lens, seq_order, num_seqs,
+                           num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                           max_context_len, scale, dtype, flags, partition_size, workspace, workspace_bytes,
+                           stream);
+  return pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, seq_order, num_seqs, num_heads,
+                   num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
+                   dtype, flags, stream);
+}
+
 pa_status pa_lse_reduce(void* out, const void* workspace, size_t workspace_bytes, const int32_t* context_lens,
                         int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
                         int32_t partition_size, pa_dtype dtype, void* stream) {

@@ -432,46 +432,64 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float*
 
 namespace {
 
-template <typename T, int D, int BS, int GT, bool SPLIT>
-hipError_t launch_t(const DecodeParams& p, int32_t num_seqs, bool cached, hipStream_t stream) {
-  const uint32_t gx = static_cast<uint32_t>(num_seqs) * (p.num_heads / GT);
-  const uint32_t gy = SPLIT ? static_cast<uint32_t>((p.num_parts + kWaves - 1) / kWaves) : 1u;
-  if (cached)
-    hipLaunchKernelGGL((decode_kernel<T, D, BS, GT, SPLIT, true>), dim3(gx, gy), dim3(kWaves * 64), 0, stream, p);
-  else
-    hipLaunchKernelGGL((decode_kernel<T, D, BS, GT, SPLIT, false>), dim3(gx, gy), dim3(kWaves * 64), 0, stream, p);
-  return hipGetLastError();
-}
+// The kernel instance for (dtype, head_dim, block_size, heads per workgroup)
+// is chosen at run time; Op::run<T, D, BS, GT, SPLIT>() does the work with it.
+struct LaunchOp {
+  const DecodeParams& p;
+  int32_t num_seqs;
+  bool cached;
+  hipStream_t stream;
+  template <typename T, int D, int BS, int GT, bool SPLIT>
+  hipError_t run() const {
+    const uint32_t gx = static_cast<uint32_t>(num_seqs) * (p.num_heads / GT);
+    const uint32_t gy = SPLIT ? static_cast<uint32_t>((p.num_parts + kWaves - 1) / kWaves) : 1u;
+    if (cached)
+      hipLaunchKernelGGL((decode_kernel<T, D, BS, GT, SPLIT, true>), dim3(gx, gy), dim3(kWaves * 64), 0, stream,
+                         p);
+    else
+      hipLaunchKernelGGL((decode_kernel<T, D, BS, GT, SPLIT, false>), dim3(gx, gy), dim3(kWaves * 64), 0, stream,
+                         p);
+    return hipGetLastError();
+  }
+};
 
-template <typename T, int D, int BS, bool SPLIT>
-hipError_t by_group(const DecodeParams& p, int32_t num_seqs, int gt, bool cached, hipStream_t stream) {
+// Workgroups of the instance that one compute unit holds at once.
+struct OccupancyOp {
+  int* per_cu;
+  template <typename T, int D, int BS, int GT, bool SPLIT>
+  hipError_t run() const {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, decode_kernel<T, D, BS, GT, SPLIT, false>,
+                                                        kWaves * 64, 0);
+  }
+};
+
+template <typename T, int D, int BS, bool SPLIT, typename Op>
+hipError_t by_group(const Op& op, int gt) {
   switch (gt) {
-    case 1: return launch_t<T, D, BS, 1, SPLIT>(p, num_seqs, cached, stream);
-    case 2: return launch_t<T, D, BS, 2, SPLIT>(p, num_seqs, cached, stream);
-    case 4: return launch_t<T, D, BS, 4, SPLIT>(p, num_seqs, cached, stream);
-    case 8: return launch_t<T, D, BS, 8, SPLIT>(p, num_seqs, cached, stream);
-    case 16: return launch_t<T, D, BS, 16, SPLIT>(p, num_seqs, cached, stream);
+    case 1: return op.template run<T, D, BS, 1, SPLIT>();
+    case 2: return op.template run<T, D, BS, 2, SPLIT>();
+    case 4: return op.template run<T, D, BS, 4, SPLIT>();
+    case 8: return op.template run<T, D, BS, 8, SPLIT>();
+    case 16: return op.template run<T, D, BS, 16, SPLIT>();
   }
   return hipErrorInvalidValue;
 }
 
-template <typename T, bool SPLIT>
-hipError_t by_shape(const DecodeParams& p, int32_t num_seqs, int d, int bs, int gt, bool cached,
-                    hipStream_t stream) {
-  if (d == 64 && bs == 16) return by_group<T, 64, 16, SPLIT>(p, num_seqs, gt, cached, stream);
-  if (d == 64 && bs == 32) return by_group<T, 64, 32, SPLIT>(p, num_seqs, gt, cached, stream);
-  if (d == 128 && bs == 16) return by_group<T, 128, 16, SPLIT>(p, num_seqs, gt, cached, stream);
-  if (d == 128 && bs == 32) return by_group<T, 128, 32, SPLIT>(p, num_seqs, gt, cached, stream);
+template <typename T, bool SPLIT, typename Op>
+hipError_t by_shape(const Op& op, int d, int bs, int gt) {
+  if (d == 64 && bs == 16) return by_group<T, 64, 16, SPLIT>(op, gt);
+  if (d == 64 && bs == 32) return by_group<T, 64, 32, SPLIT>(op, gt);
+  if (d == 128 && bs == 16) return by_group<T, 128, 16, SPLIT>(op, gt);
+  if (d == 128 && bs == 32) return by_group<T, 128, 32, SPLIT>(op, gt);
   return hipErrorInvalidValue;
 }
 
-template <bool SPLIT>
-hipError_t by_dtype(const DecodeParams& p, int32_t num_seqs, pa_dtype dt, int d, int bs, int gt, bool cached,
-                    hipStream_t stream) {
+template <bool SPLIT, typename Op>
+hipError_t by_dtype(const Op& op, pa_dtype dt, int d, int bs, int gt) {
   switch (dt) {
-    case PA_F32: return by_shape<TF32, SPLIT>(p, num_seqs, d, bs, gt, cached, stream);
-    case PA_F16: return by_shape<TF16, SPLIT>(p, num_seqs, d, bs, gt, cached, stream);
-    case PA_BF16: return by_shape<TBF16, SPLIT>(p, num_seqs, d, bs, gt, cached, stream);
+    case PA_F32: return by_shape<TF32, SPLIT>(op, d, bs, gt);
+    case PA_F16: return by_shape<TF16, SPLIT>(op, d, bs, gt);
+    case PA_BF16: return by_shape<TBF16, SPLIT>(op, d, bs, gt);
   }
   return hipErrorInvalidValue;
 }
@@ -508,8 +526,8 @@ DecodeParams make_params(const DecodeArgs& x) {
 hipError_t launch_decode(const DecodeArgs& x, hipStream_t stream) {
   DecodeParams p = make_params(x);
   const int gt = group_tile(x.num_heads / x.num_kv_heads);
-  return by_dtype<false>(p, x.num_seqs, x.dtype, x.head_dim, x.block_size, gt, x.flags & PA_DECODE_CACHED_KV,
-                         stream);
+  return by_dtype<false>(LaunchOp{p, x.num_seqs, (x.flags & PA_DECODE_CACHED_KV) != 0, stream}, x.dtype,
+                         x.head_dim, x.block_size, gt);
 }
 
 hipError_t launch_decode_split(const DecodeArgs& x, const SplitLayout& ws, hipStream_t stream) {
@@ -520,11 +538,22 @@ hipError_t launch_decode_split(const DecodeArgs& x, const SplitLayout& ws, hipSt
   p.part_size = ws.partition_size;
   p.num_parts = ws.num_parts;
   const int gt = group_tile(x.num_heads / x.num_kv_heads);
-  hipError_t e = by_dtype<true>(p, x.num_seqs, x.dtype, x.head_dim, x.block_size, gt,
-                                x.flags & PA_DECODE_CACHED_KV, stream);
+  hipError_t e = by_dtype<true>(LaunchOp{p, x.num_seqs, (x.flags & PA_DECODE_CACHED_KV) != 0, stream}, x.dtype,
+                                x.head_dim, x.block_size, gt);
   if (e != hipSuccess) return e;
   return launch_lse_reduce(x.out, ws, x.context_lens, x.seq_order, x.num_seqs, x.num_heads, x.head_dim,
                            p.len_limit, x.dtype, stream);
+}
+
+hipError_t single_pass_shape(const DecodeArgs& x, int64_t* workgroups, int64_t* resident) {
+  const int gt = group_tile(x.num_heads / x.num_kv_heads);
+  *workgroups = static_cast<int64_t>(x.num_seqs) * (x.num_heads / gt);
+  int per_cu = 0, dev = 0, cus = 0;
+  hipError_t e = by_dtype<false>(OccupancyOp{&per_cu}, x.dtype, x.head_dim, x.block_size, gt);
+  if (e == hipSuccess) e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  *resident = static_cast<int64_t>(per_cu) * cus;
+  return e;
 }
 
 hipError_t launch_lse_reduce(void* out, const SplitLayout& ws, const int32_t* ctx, const int32_t* order,

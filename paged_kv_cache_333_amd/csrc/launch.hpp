@@ -43,6 +43,9 @@ hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t*
 hipError_t launch_upload(void* dst, const void* src_device_view, int64_t nbytes, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeArgs& a, const SplitLayout& ws, hipStream_t stream);
+// Workgroups the single-pass launch would start, and how many of them the
+// current device holds at once.
+hipError_t single_pass_shape(const DecodeArgs& a, int64_t* workgroups, int64_t* resident);
 hipError_t launch_lse_reduce(void* out, const SplitLayout& ws, const int32_t* context_lens,
                              const int32_t* seq_order, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                              int32_t len_limit, pa_dtype dtype, hipStream_t stream);

@@ -346,3 +346,32 @@ def test_parallel_sampling_decode_after_cow_step():
     for s, h in picks:
         ref = A.decode_one(q[s], kc1, vc1, dw.ora.tables[s], dw.ora.lens[s], h, w.num_heads, w.scale, w.dtype)
         assert_close(out[s, h], ref, w.dtype, f"seq {s} head {h}")
+
+
+def test_auto_picks_split_for_few_long_sequences_and_single_otherwise():
+    """pa_decode_auto runs the split path when the single pass could not fill the device
+    (the long-context workload: 4 sequences x 32 heads) and the single pass for a full batch
+    (the LLaMA-7B-like workload); each result equals the direct call bit for bit."""
+    for key, want in ((4, "split"), (2, "single")):
+        dw = DeviceWorkload(key)
+        w = dw.w
+        ws = torch.empty(pa.pa_decode_split_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim,
+                                                            dw.max_context_len, 512), dtype=torch.uint8,
+                         device="cuda")
+        got = pa.pa_decode_auto(dw.out, dw.query, dw.key_cache, dw.value_cache, dw.tables, dw.context_lens,
+                                dw.max_context_len, w.scale, 512, ws)
+        assert got == want
+        direct = torch.empty_like(dw.out)
+        if want == "split":
+            pa.pa_decode_split(direct, dw.query, dw.key_cache, dw.value_cache, dw.tables, dw.context_lens,
+                               dw.max_context_len, w.scale, 512, ws)
+        else:
+            pa.pa_decode(direct, dw.query, dw.key_cache, dw.value_cache, dw.tables, dw.context_lens,
+                         dw.max_context_len, w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(direct, dw.out)
+        # without a workspace it always takes the single pass
+        assert pa.pa_decode_auto(direct, dw.query, dw.key_cache, dw.value_cache, dw.tables, dw.context_lens,
+                                 dw.max_context_len, w.scale, 512, None) == "single"
+        del dw, ws, direct
+        torch.cuda.empty_cache()
