@@ -3,9 +3,11 @@
 
 One step = the whole hot path over one batch:
   host allocator bookkeeping for one new token per sequence (slots, copy-on-write
-  pairs, block tables), the table/slot uploads, pa_copy_blocks (when pairs exist),
-  pa_reshape_and_cache of the new K/V, and the decode over every cached token
-  (pa_decode, or pa_decode_split + its LSE merge).
+  pairs, block tables), the upload of the step's index data (pa_upload),
+  pa_copy_blocks (when pairs exist), pa_reshape_and_cache of the new K/V, and the
+  decode over every cached token (pa_decode_auto: single pass, or split partials +
+  LSE merge).  --fused-write runs the write inside the decode launch instead
+  (pa_decode_append).
 
 Default workload: 64 sequences, 32 query / 32 KV heads of dimension 128, fp16,
 block size 16, contexts uniform in [256, 2048] (a LLaMA-7B-like layer), pool of
@@ -40,6 +42,9 @@ def parse():
     ap.add_argument("--path", choices=["auto", "single", "split"], default="auto",
                     help="decode path: pa_decode_auto (default: the library picks), pa_decode or pa_decode_split")
     ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--fused-write", action="store_true",
+                    help="write the new K/V inside the decode launch (pa_decode_append, auto path) instead of "
+                         "pa_reshape_and_cache before it; measured no faster per step, so off by default")
     ap.add_argument("--order", choices=["longest", "index"], default=None,
                     help="launch order of the sequences (default: index for workload 5, whose forked branches "
                          "share blocks and should run side by side; longest-first otherwise)")
@@ -307,7 +312,9 @@ class Bench:
         if npairs:
             pa.pa_copy_blocks(self.kc, self.vc, b["pairs_d"], num_pairs=npairs)
         r = k % self.newk.shape[0]
-        pa.pa_reshape_and_cache(self.newk[r], self.newv[r], self.kc, self.vc, b["slots_d"])
+        fused = self.path == "auto" and self.args.fused_write
+        if not fused:
+            pa.pa_reshape_and_cache(self.newk[r], self.newv[r], self.kc, self.vc, b["slots_d"])
         if timing is not None:
             e0, e1 = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
             e0.record(self.stream)
@@ -319,6 +326,11 @@ class Bench:
             pa.pa_decode_split(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"], self.max_ctx, w.scale,
                                self.args.partition, self.ws, seq_order=order, cached_kv=self.cached)
             self.path_ran.add("split")
+        elif fused:
+            self.path_ran.add(pa.pa_decode_append(self.out, self.q, self.newk[r], self.newv[r], b["slots_d"],
+                                                  self.kc, self.vc, b["tab_d"], b["len_d"], self.max_ctx, w.scale,
+                                                  self.args.partition, self.ws, seq_order=order,
+                                                  cached_kv=self.cached))
         else:
             self.path_ran.add(pa.pa_decode_auto(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"],
                                                 self.max_ctx, w.scale, self.args.partition, self.ws,
@@ -404,7 +416,9 @@ def main():
     kv_tokens = sum(t[2] for t in timing)
     kv_bytes_token = 2 * w.num_kv_heads * w.head_dim * e
     qo_bytes = 2 * w.num_seqs * w.num_heads * w.head_dim * e
-    alg_bytes = [t[2] * kv_bytes_token + qo_bytes + 4 * t[3] + 4 * w.num_seqs for t in timing]
+    # the fused call also reads the step's new K/V rows and writes them into the pools
+    fused_write = 2 * w.num_seqs * kv_bytes_token if (bench.path == "auto" and args.fused_write) else 0
+    alg_bytes = [t[2] * kv_bytes_token + qo_bytes + 4 * t[3] + 4 * w.num_seqs + fused_write for t in timing]
     avg_dur = sum(durs) / len(durs)
     avg_bytes = sum(alg_bytes) / len(alg_bytes)
     achieved = avg_bytes / avg_dur / 1e9
@@ -427,6 +441,8 @@ def main():
                    "context_lens": "per workload definition, +1 token per step",
                    "mean_kv_tokens_per_step": kv_tokens / len(timing),
                    "decode_path": ("auto: " if bench.path == "auto" else "") + "+".join(sorted(bench.path_ran)),
+                   "kv_write": "fused into the decode (pa_decode_append)" if fused_write
+                   else "pa_reshape_and_cache, then decode",
                    "partition_size": args.partition if "split" in bench.path_ran else None,
                    "launch_order": bench.order, "kv_cache_policy": "cached" if bench.cached else "stream",
                    "cow_pairs_per_step": sum(t[4] for t in timing) / len(timing)},

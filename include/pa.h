@@ -298,6 +298,35 @@ pa_status pa_decode_auto(void* out, const void* query, const void* key_cache, co
                          int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* path,
                          void* stream);
 
+/* One decode step with the slot-mapping write fused in: equivalent to
+ * pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping,
+ * num_seqs, ...) followed by pa_decode_auto, in one launch.  The pages write
+ * each step's new K/V into its block ([IMPL] §3.4 _add_kv_cache; [ASC] §3.1
+ * slot_mapping) and attend over the context that includes it (the step
+ * writes, then decodes).
+ *   key, value: device [num_seqs, num_kv_heads, head_dim], one new token per
+ *     sequence (row s belongs to sequence s).
+ *   slot_mapping: device int32 [num_seqs]; slot_mapping[s] must be the slot of
+ *     token context_lens[s] - 1 of sequence s (the slot pa_seq_append_slot
+ *     returned), or negative for no write.  A slot elsewhere is still written,
+ *     but the decode may read that block's old or new contents (a race).
+ *   key_cache, value_cache: written (one key row and one value column per
+ *     sequence and KV head) and read.
+ * The wave that reads the new token's step writes it and makes the writes
+ * visible before loading that step, so the write costs no extra launch.  When
+ * num_heads / num_kv_heads is above 16 (several workgroups per KV head) the
+ * two operations run as two launches.  Other arguments, the path choice,
+ * *path and the errors are those of pa_decode_auto; under PA_DEBUG the slots
+ * are validated as in pa_reshape_and_cache. */
+pa_status pa_decode_append(void* out, const void* query, const void* key, const void* value,
+                           const int32_t* slot_mapping, void* key_cache, void* value_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                           int32_t max_context_len, float scale, pa_dtype dtype, uint32_t flags,
+                           int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* path,
+                           void* stream);
+
 /* Log-sum-exp merge of split partials (the standard rule; the pages do not
  * spell it out): with M = max_p m_p and w_p = l_p * exp(m_p - M),
  *   out[s,h,:] = sum_p w_p o_p / sum_p w_p   over p < ceil(n / partition_size),

@@ -113,6 +113,22 @@ pa_status debug_check_tables(const pa::DecodeArgs& a, hipStream_t st) {
   return PA_OK;
 }
 
+pa_status debug_check_slots(const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                            int32_t block_size, hipStream_t st) {
+  std::vector<int32_t> slots;
+  pa_status s = fetch(slots, slot_mapping, num_tokens, st);
+  if (s != PA_OK) return s;
+  const int64_t nslots = static_cast<int64_t>(num_blocks) * block_size;
+  std::unordered_set<int32_t> seen;
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    if (slots[i] < 0) continue;
+    if (slots[i] >= nslots) return fail(PA_ERR_BAD_TABLE, "slot_mapping[" + std::to_string(i) + "] past the pool");
+    if (!seen.insert(slots[i]).second)
+      return fail(PA_ERR_BAD_TABLE, "slot " + std::to_string(slots[i]) + " written twice");
+  }
+  return PA_OK;
+}
+
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 struct SplitSizes {
@@ -154,6 +170,24 @@ pa_status make_layout(void* workspace, size_t workspace_bytes, int32_t num_seqs,
   return PA_OK;
 }
 
+// The pa_decode_auto rule: split only when the single pass could not fill the
+// device (fewer workgroups than it holds at once, so compute units would sit
+// idle while a few workgroups walk very long contexts), the context spans at
+// least four partitions and the workspace is large enough.
+bool choose_split(const pa::DecodeArgs& a, int32_t partition_size, const void* workspace, size_t workspace_bytes) {
+  if (!workspace || a.num_seqs <= 0 || partition_size <= 0 || partition_size % a.block_size ||
+      partition_size > 4096 || a.max_context_len < 4 * static_cast<int64_t>(partition_size))
+    return false;
+  SplitSizes z;
+  if (!split_sizes(a.num_seqs, a.num_heads, a.head_dim, a.max_context_len, partition_size, &z) ||
+      static_cast<int64_t>(workspace_bytes) < z.total)
+    return false;
+  int64_t workgroups = 0, resident = 0;
+  const bool ok = pa::single_pass_shape(a, &workgroups, &resident) == hipSuccess;
+  (void)hipGetLastError();
+  return ok && workgroups < resident;
+}
+
 pa::DecodeArgs pack(void* out, const void* query, const void* key_cache, const void* value_cache,
                     const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
                     int32_t num_seqs,
@@ -183,20 +217,8 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cac
   if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
     return fail(PA_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (debug_mode()) {
-    std::vector<int32_t> slots;
-    s = fetch(slots, slot_mapping, num_tokens, st);
-    if (s != PA_OK) return s;
-    const int64_t nslots = static_cast<int64_t>(num_blocks) * block_size;
-    std::unordered_set<int32_t> seen;
-    for (int32_t i = 0; i < num_tokens; ++i) {
-      if (slots[i] < 0) continue;
-      if (slots[i] >= nslots)
-        return fail(PA_ERR_BAD_TABLE, "slot_mapping[" + std::to_string(i) + "] past the pool");
-      if (!seen.insert(slots[i]).second)
-        return fail(PA_ERR_BAD_TABLE, "slot " + std::to_string(slots[i]) + " written twice");
-    }
-  }
+  if (debug_mode() && (s = debug_check_slots(slot_mapping, num_tokens, num_blocks, block_size, st)) != PA_OK)
+    return s;
   return finish(pa::launch_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, num_tokens,
                                              num_blocks, num_kv_heads, head_dim, elem_bytes(dtype),
                                              block_size, st),
@@ -320,18 +342,7 @@ pa_status pa_decode_auto(void* out, const void* query, const void* key_cache, co
                           max_context_len, scale, dtype, flags);
   pa_status s = check_decode_args(a);
   if (s != PA_OK) return s;
-  bool split = false;
-  if (workspace && num_seqs > 0 && partition_size > 0 && partition_size % block_size == 0 &&
-      partition_size <= 4096 && max_context_len >= 4 * static_cast<int64_t>(partition_size) &&
-      workspace_bytes >= pa_decode_split_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
-                                                         partition_size)) {
-    // Split only when the single pass could not fill the device: fewer
-    // workgroups than it holds at once means some compute units would sit idle
-    // while a few workgroups walk very long contexts.
-    int64_t workgroups = 0, resident = 0;
-    if (pa::single_pass_shape(a, &workgroups, &resident) == hipSuccess) split = workgroups < resident;
-    (void)hipGetLastError();
-  }
+  const bool split = choose_split(a, partition_size, workspace, workspace_bytes);
   if (path) *path = split ? 1 : 0;
   if (split)
     return pa_decode_split(out, query, key_cache, value_cache, block_tables, context_lens, seq_order, num_seqs,
@@ -341,6 +352,41 @@ pa_status pa_decode_auto(void* out, const void* query, const void* key_cache, co
   return pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, seq_order, num_seqs, num_heads,
                    num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
                    dtype, flags, stream);
+}
+
+pa_status pa_decode_append(void* out, const void* query, const void* key, const void* value,
+                           const int32_t* slot_mapping, void* key_cache, void* value_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                           int32_t max_context_len, float scale, pa_dtype dtype, uint32_t flags,
+                           int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* path,
+                           void* stream) {
+  pa::DecodeArgs a = pack(out, query, key_cache, value_cache, block_tables, context_lens, seq_order, num_seqs,
+                          num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                          max_context_len, scale, dtype, flags);
+  pa_status s = check_decode_args(a);
+  if (s != PA_OK) return s;
+  if (flags & ~uint32_t(PA_DECODE_CACHED_KV)) return fail(PA_ERR_INVALID_ARG, "unknown flag bits");
+  if (num_seqs == 0) {
+    if (path) *path = 0;
+    return PA_OK;
+  }
+  if (!key || !value || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(key) || !aligned16(value)) return fail(PA_ERR_INVALID_ARG, "key and value must be 16-byte aligned");
+  const bool split = choose_split(a, partition_size, workspace, workspace_bytes);
+  if (path) *path = split ? 1 : 0;
+  pa::SplitLayout ws;
+  if (split && (s = make_layout(workspace, workspace_bytes, num_seqs, num_heads, head_dim, max_context_len,
+                                partition_size, &ws)) != PA_OK)
+    return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_mode()) {
+    if ((s = debug_check_slots(slot_mapping, num_seqs, num_blocks, block_size, st)) != PA_OK) return s;
+    if ((s = debug_check_tables(a, st)) != PA_OK) return s;
+  }
+  return finish(pa::launch_decode_append(a, key, value, slot_mapping, split ? &ws : nullptr, st), st,
+                "pa_decode_append");
 }
 
 pa_status pa_lse_reduce(void* out, const void* workspace, size_t workspace_bytes, const int32_t* context_lens,

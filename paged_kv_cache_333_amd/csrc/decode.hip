@@ -1,495 +1,20 @@
-// Paged decode attention for gfx950 on the matrix cores: single pass, split
-// partials, and the log-sum-exp merge of partials.
-//
-// What is computed ("PagedAttention 实现细节" §3.1 index-based kernel: token t
-// of a sequence lives in block table[t / bs] at row t % bs, read in place;
-// "Ascend C算子开发高阶实战…" §三/§四: gather, QK^T, softmax and OV fused in one
-// pass with an online softmax and fp32 accumulation):
-//   out[s,h] = sum_t softmax_t(scale * <q[s,h], K_t>) V_t over t < ctx[s],
-// with K_t, V_t taken from KV head h / (H / H_kv).
-//
-// Pools.  Keys are stored token-major, [NB, H_kv, bs, D]; values dim-major,
-// [NB, H_kv, D, bs] (block size innermost, the arrangement of "Ascend C算子
-// 开发高阶实战…" §3.1/§5.2).  Each 16-byte load then holds 8 (4 for fp32)
-// consecutive elements along the contraction axis of its product: head_dim
-// for q.K, tokens for P.V, which is what a matrix-core operand wants.
-//
-// Work decomposition.  A workgroup of kWaves waves serves one (sequence, GT
-// query heads that share a KV head).  Single pass: the waves share the whole
-// context, wave w taking steps w, w + kWaves, ... of TS tokens (32 for
-// fp16/bf16, 16 for fp32), and merge through LDS at the end.  Split: each wave
-// owns one partition outright and writes its partial (m, l, o) itself, so a
-// workgroup covers kWaves consecutive partitions with no barrier.  In a step,
-// with lane = 16 q + n:
-//   * q.K: one 16x16 tile per 16 tokens, C[m][n'] = sum_d K[tok(m)][d] Q[n'][d]
-//     on v_mfma_f32_16x16x32_{f16,bf16} (fp32: 16x16x4).  Column n' of Q is
-//     query head n' % GT, so the GT heads are replicated to fill the 16
-//     columns and every lane ends up holding logits of one head.  Token rows
-//     are permuted so that lane (q, n) receives tokens EPL q .. EPL q + EPL-1
-//     of the step, exactly the slice it supplies to P.V.
-//   * online softmax per head on those EPL logits per lane: running max (made
-//     common to the four lanes of a column with two cross-row max steps),
-//     running sum, rescale of the accumulator when the max grows.
-//   * P.V: out^T tile C[m][d'] = sum_t P[m][t] V[t][d'], one product per 16
-//     output dims; P never leaves the registers that computed it.  For bf16,
-//     P is split into a bf16 high part and a bf16 residual (two products) so
-//     the weights keep ~16 significant bits; fp16 P keeps 11.
-// Each KV element is loaded once per workgroup; the GT query heads share it.
-//
-// Logits are kept in base-2 units (scale folded with log2 e) so the hardware
-// exp2 is used.  Tokens past the context are masked by select (never by
-// multiplying by 0), and their value columns are zeroed before the product,
-// so NaN garbage in unused rows cannot leak.  The merge of the waves (LDS) and
-// of the split partials uses the same rescaling rule.  Reduction order depends
-// only on logical token positions, so relabelling physical blocks gives
-// bit-identical results.
-//
-// Invalid device data never leads to an out-of-bounds access: a block id
-// outside the pool is not read and turns the affected outputs into NaN; a
-// context length outside its bound does the same.
-#include <math.h>
-
-#include <type_traits>
-
-#include "device_common.hpp"
-#include "launch.hpp"
+// Host-side launchers of the paged decode kernels (decode_kernel.hpp): the
+// single pass, the split pass plus its log-sum-exp merge, the fused
+// slot-mapping write, and the occupancy query behind pa_decode_auto.
+#include "decode_kernel.hpp"
 
 namespace pa {
-
-constexpr int kWaves = 4;
-
-struct DecodeParams {
-  void* out;
-  const char* q;
-  const char* kc;
-  const char* vc;
-  const int32_t* tables;
-  const int32_t* ctx;
-  const int32_t* order;  // optional launch order of the sequences (a permutation), or null
-  float* ws_m;
-  float* ws_l;
-  float* ws_o;
-  int32_t num_seqs;
-  int32_t num_heads;
-  int32_t num_kv_heads;
-  int32_t max_blocks;
-  int32_t num_blocks;
-  int32_t len_limit;   // largest valid context length
-  int32_t part_size;   // split only
-  int32_t num_parts;   // split only
-  float scale_log2;    // scale * log2(e)
-};
-
-template <typename T, int D, int BS, int GT, bool SPLIT, bool CACHED>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void decode_kernel(DecodeParams a) {
-  constexpr int EPL = T::kEPL;       // elements per 16-byte chunk
-  constexpr int E = T::kBytes;
-  constexpr int KV = D / EPL / 4;    // q.K products per 16-token tile (chunks 4v + q of a row)
-  constexpr int NT = EPL / 4;        // 16-token q.K tiles per step
-  constexpr int TS = 16 * NT;        // tokens per step
-  constexpr int NV = D / 16;         // P.V products per step (16 output dims each)
-  constexpr int NBS = TS > BS ? TS / BS : 1;  // blocks touched by one step
-  constexpr bool SPLIT_P = std::is_same<T, TBF16>::value;
-  constexpr float kNegInf = -__builtin_huge_valf();
-  static_assert(GT >= 1 && GT <= 16, "heads per workgroup");
-
-  const int lane = threadIdx.x & 63;
-  // wave-uniform: keeps the step loop and the table lookups in scalar registers
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int q = lane >> 4;
-  const int n = lane & 15;
-  const int groups = a.num_heads / GT;
-  const int slot = blockIdx.x / groups;
-  const int h0 = (blockIdx.x - slot * groups) * GT;
-  // Workgroups start in blockIdx order; with a longest-first order the long
-  // sequences start first and the short ones fill in behind them.
-  const int s = a.order ? a.order[slot] : slot;
-  if (static_cast<uint32_t>(s) >= static_cast<uint32_t>(a.num_seqs)) return;
-  const int kvh = h0 / (a.num_heads / a.num_kv_heads);
-  const int nctx = a.ctx[s];
-  const bool bad_len = nctx < 0 || nctx > a.len_limit;
-
-  // Single pass: the workgroup's waves share the context, wave w taking steps
-  // w, w + kWaves, ...  Split: each wave owns one partition outright (partition
-  // blockIdx.y * kWaves + wave) and writes its partial itself.
-  constexpr int WSTEP = SPLIT ? 1 : kWaves;
-  int t_begin = 0, t_end = bad_len ? 0 : nctx, part = 0;
-  if constexpr (SPLIT) {
-    part = blockIdx.y * kWaves + wave;
-    t_begin = part * a.part_size;
-    if (bad_len || t_begin >= nctx) return;  // nothing to write for this partition (no barrier follows)
-    t_end = min(t_begin + a.part_size, nctx);
-  }
-  const int st_first = SPLIT ? 0 : wave;
-  const int b_end = (t_end + BS - 1) / BS;
-  const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.max_blocks;
-
-  // Q operand of q.K: lane (q, n) holds head h0 + n % GT, chunks 4v + q.
-  u32x4 qv[KV];
-  {
-    const char* qrow = a.q + (static_cast<int64_t>(s) * a.num_heads + h0 + n % GT) * D * E;
-#pragma unroll
-    for (int v = 0; v < KV; ++v) qv[v] = load16(qrow + (4 * v + q) * 16);
-  }
-
-  // Online-softmax state of this lane's head (n % GT), and the P.V
-  // accumulator: acc[v][j] is out^T row 4q + j (head (4q + j) % GT), dim 16v + n.
-  float m_run = kNegInf, l_run = 0.f;
-  f32x4 acc[NV];
-#pragma unroll
-  for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int bad = 0;
-
-  const int n_steps = (t_end - t_begin + TS - 1) / TS;
-  const int64_t hkv = a.num_kv_heads;
-  // Block ids.  The first step's come through the scalar path, which a new
-  // workgroup reaches without queueing behind the streaming loads the other
-  // workgroups on its CU have in flight.  Later steps' ids are prefetched with
-  // one vector load per wave: lane i holds the id of block i % NBS of the
-  // wave's step k + i / NBS, for the next IDS_PER steps, so no step waits for
-  // a table lookup.  Indices are clamped into the table row; an id is used
-  // (and validated) only below b_end.
-  constexpr int IDS_PER = 64 / NBS;  // steps covered by one prefetch
-  const int mb_last = a.max_blocks - 1;
-  const int lane_step = lane / NBS, lane_blk = lane - lane_step * NBS;
-  auto fetch_ids = [&](int first_step) {
-    const int st_l = first_step + WSTEP * lane_step;
-    const int b = (t_begin + st_l * TS) / BS + lane_blk;
-    return trow[min(b, mb_last)];
-  };
-  int32_t ph_first[NBS];
-  int32_t ids = 0;
-  if (mb_last >= 0) {  // needs only s, not the context length
-    const int b = (t_begin + st_first * TS) / BS;
-#pragma unroll
-    for (int i = 0; i < NBS; ++i) ph_first[i] = trow[min(b + i, mb_last)];
-    ids = fetch_ids(st_first + WSTEP);
-  }
-  int k_ids = -1;  // steps consumed from `ids`; -1: the first step uses ph_first
-  for (int st = st_first; st < n_steps; st += WSTEP) {
-    const int t0 = t_begin + st * TS;
-    const int b0 = t0 / BS;
-    const int off0 = t0 - b0 * BS;  // nonzero only when a step is shorter than a block
-    if (k_ids == IDS_PER) {
-      ids = fetch_ids(st);
-      k_ids = 0;
-    }
-    int32_t ph[NBS];
-    bool skip = false;
-#pragma unroll
-    for (int i = 0; i < NBS; ++i) {
-      ph[i] = k_ids < 0 ? ph_first[i] : __builtin_amdgcn_readlane(ids, NBS * k_ids + i);
-      if (b0 + i < b_end) {
-        if (static_cast<uint32_t>(ph[i]) >= static_cast<uint32_t>(a.num_blocks)) skip = true;
-      } else {
-        ph[i] = -1;  // past the context: masked below, read from block ph[0]
-      }
-    }
-    ++k_ids;
-    if (skip) {
-      bad = 1;
-      continue;
-    }
-#pragma unroll
-    for (int i = 1; i < NBS; ++i)
-      if (ph[i] < 0) ph[i] = ph[0];
-
-    // K rows: in tile tau, lane (q, n) supplies row n = token
-    // EPL (n / 4) + 4 tau + n % 4 of the step, chunks 4v + q.
-    u32x4 kr[NT][KV];
-#pragma unroll
-    for (int tau = 0; tau < NT; ++tau) {
-      const int x = off0 + EPL * (n >> 2) + 4 * tau + (n & 3);
-      const int bi = NBS == 1 ? 0 : x / BS;
-      const int64_t phys = bi ? ph[NBS - 1] : ph[0];
-      const char* kp = a.kc + (((phys * hkv + kvh) * BS + (x - bi * BS)) * D) * E + q * 16;
-#pragma unroll
-      for (int v = 0; v < KV; ++v) kr[tau][v] = CACHED ? load16(kp + v * 64) : load16_stream(kp + v * 64);
-    }
-    // V columns: lane (q, n) supplies dim 16v + n of tokens EPL q .. EPL q + EPL-1.
-    u32x4 vr[NV];
-    {
-      const int x = off0 + EPL * q;
-      const int bi = NBS == 1 ? 0 : x / BS;
-      const int64_t phys = bi ? ph[NBS - 1] : ph[0];
-      const char* vp = a.vc + (((phys * hkv + kvh) * D + n) * BS + (x - bi * BS)) * E;
-#pragma unroll
-      for (int v = 0; v < NV; ++v)
-        vr[v] = CACHED ? load16(vp + v * 16 * BS * E) : load16_stream(vp + v * 16 * BS * E);
-    }
-    // All of the step's loads are issued before any of them is consumed.
-    __builtin_amdgcn_sched_barrier(0);
-
-    f32x4 c[NT];
-#pragma unroll
-    for (int tau = 0; tau < NT; ++tau) {
-      c[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int v = 0; v < KV; ++v) c[tau] = mma(T{}, kr[tau][v], qv[v], c[tau]);
-    }
-    // c[tau][j]: logit of token t0 + EPL q + 4 tau + j for head n % GT
-    const bool tail = t0 + TS > t_end;
-    float z[EPL];
-    float mx = kNegInf;
-#pragma unroll
-    for (int tau = 0; tau < NT; ++tau)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float v = c[tau][j] * a.scale_log2;
-        const bool ok = !tail || t0 + EPL * q + 4 * tau + j < t_end;
-        z[4 * tau + j] = ok ? v : kNegInf;
-        mx = fmaxf(mx, z[4 * tau + j]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    float p[EPL];
-    float ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      p[e] = fast_exp2(z[e] - m_use);
-      ps += p[e];
-    }
-    l_run = l_run * alpha + ps;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-      // acc[.][j] belongs to head (4q + j) % GT; its factor sits in a lane of
-      // the same row whose column has that head.
-      float al[4];
-      if constexpr (4 % GT == 0) {
-        al[0] = quad_bcast<0>(alpha);
-        al[1] = quad_bcast<1>(alpha);
-        al[2] = quad_bcast<2>(alpha);
-        al[3] = quad_bcast<3>(alpha);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) al[j] = __shfl(alpha, 16 * q + (4 * q + j) % GT);
-      }
-#pragma unroll
-      for (int v = 0; v < NV; ++v)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[v][j] *= al[j];
-    }
-    u32x4 phi, plo;
-    pack_p(T{}, p, phi, plo);
-    if (tail) {
-      const u32x4 keep = keep_mask(T{}, t_end - (t0 + EPL * q));
-#pragma unroll
-      for (int v = 0; v < NV; ++v) vr[v] &= keep;
-    }
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      acc[v] = mma(T{}, phi, vr[v], acc[v]);
-      if constexpr (SPLIT_P) acc[v] = mma(T{}, plo, vr[v], acc[v]);
-    }
-  }
-
-  // the four lanes of a column summed disjoint tokens with a common max
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-
-  if constexpr (SPLIT) {
-    // This wave's partition: (m_p in natural-log units, l_p, o_p = acc / l_p)
-    // for each of the GT heads.  acc[.][j] belongs to head (4q + j) % GT, whose
-    // l sits in a lane of the same row (see the rescale above).
-    float lg[4];
-    if constexpr (4 % GT == 0) {
-      lg[0] = quad_bcast<0>(l_run);
-      lg[1] = quad_bcast<1>(l_run);
-      lg[2] = quad_bcast<2>(l_run);
-      lg[3] = quad_bcast<3>(l_run);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) lg[j] = __shfl(l_run, 16 * q + (4 * q + j) % GT);
-    }
-    const float qnan = __builtin_nanf("");
-    const int64_t sh0 = static_cast<int64_t>(s) * a.num_heads + h0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int g = 4 * q + j;  // first replica of each head
-      if (g < GT) {
-        float* o = a.ws_o + ((sh0 + g) * a.num_parts + part) * D + n;
-#pragma unroll
-        for (int v = 0; v < NV; ++v) o[16 * v] = bad ? qnan : acc[v][j] / lg[j];
-      }
-    }
-    if (q == 0 && n < GT) {
-      const int64_t idx = (sh0 + n) * a.num_parts + part;
-      a.ws_m[idx] = m_run * 0.6931471805599453f;  // back to natural-log units
-      a.ws_l[idx] = bad ? qnan : l_run;
-    }
-    return;
-  }
-
-  __shared__ float sm_m[kWaves][GT];
-  __shared__ float sm_l[kWaves][GT];
-  __shared__ float sm_acc[kWaves][GT][D];
-  if (q == 0 && n < GT) {
-    sm_m[wave][n] = m_run;
-    sm_l[wave][n] = l_run;
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int g = 4 * q + j;  // first replica of each head
-    if (g < GT) {
-#pragma unroll
-      for (int v = 0; v < NV; ++v) sm_acc[wave][g][16 * v + n] = acc[v][j];
-    }
-  }
-  const int any_bad = __syncthreads_or(bad);
-
-  for (int i = threadIdx.x; i < GT * D; i += kWaves * 64) {
-    const int g = i / D;
-    const int d = i - g * D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][g]);
-    const float Mu = M == kNegInf ? 0.f : M;
-    float L = 0.f, A = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float wt = fast_exp2(sm_m[w][g] - Mu);
-      L = __builtin_fmaf(sm_l[w][g], wt, L);
-      A = __builtin_fmaf(sm_acc[w][g][d], wt, A);
-    }
-    const int64_t sh = static_cast<int64_t>(s) * a.num_heads + h0 + g;
-    const float val = any_bad || bad_len ? __builtin_nanf("") : (L > 0.f ? A / L : 0.f);
-    store_elem(T{}, a.out, sh * D + d, val);
-  }
-}
-
-// Log-sum-exp merge of split partials: M = max_p m_p, w_p = l_p exp(m_p - M),
-// out = sum_p w_p o_p / sum_p w_p.  One workgroup of four waves per
-// (sequence, head): the threads first take the max of m_p together, then wave
-// w accumulates partitions w, w + 4, ... with each lane holding D / 64 output
-// dims and several partitions' loads in flight; the waves' sums share M and
-// are added through LDS.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float* __restrict__ ws_m,
-                                                         const float* __restrict__ ws_l,
-                                                         const float* __restrict__ ws_o,
-                                                         const int32_t* __restrict__ ctx,
-                                                         const int32_t* __restrict__ order, int32_t num_seqs,
-                                                         int32_t num_heads, int32_t len_limit,
-                                                         int32_t part_size, int32_t num_parts) {
-  constexpr float kLog2e = 1.4426950408889634f;
-  constexpr int DPL = D / 64;  // output dims per lane
-  const int slot = blockIdx.x / num_heads;
-  const int h = blockIdx.x - slot * num_heads;
-  const int s = order ? order[slot] : slot;  // same sequence set as the partials pass
-  if (static_cast<uint32_t>(s) >= static_cast<uint32_t>(num_seqs)) return;
-  const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
-  const int n = ctx[s];
-  if (n < 0 || n > len_limit) {
-    if (threadIdx.x < D) store_elem(T{}, out, sh * D + threadIdx.x, __builtin_nanf(""));
-    return;
-  }
-  const int np = (n + part_size - 1) / part_size;
-  const float* mp = ws_m + sh * num_parts;
-  const float* lp = ws_l + sh * num_parts;
-  const float* op = ws_o + sh * num_parts * D;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-
-  __shared__ float sm_max[4];
-  __shared__ float sm_l[4];
-  __shared__ float sm_a[4][D];
-  float M = -__builtin_huge_valf();
-  for (int p = threadIdx.x; p < np; p += 256) M = fmaxf(M, mp[p]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) sm_max[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(sm_max[0], sm_max[1]), fmaxf(sm_max[2], sm_max[3]));
-
-  float L = 0.f, A[DPL];
-#pragma unroll
-  for (int k = 0; k < DPL; ++k) A[k] = 0.f;
-#pragma unroll 4
-  for (int p = wave; p < np; p += 4) {
-    const float w = lp[p] * fast_exp2((mp[p] - M) * kLog2e);
-    L += w;
-    const float* o = op + static_cast<int64_t>(p) * D + lane * DPL;
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) A[k] = __builtin_fmaf(w, o[k], A[k]);
-  }
-  if (lane == 0) sm_l[wave] = L;
-#pragma unroll
-  for (int k = 0; k < DPL; ++k) sm_a[wave][lane * DPL + k] = A[k];
-  __syncthreads();
-  if (threadIdx.x < D) {
-    const int d = threadIdx.x;
-    const float Ls = (sm_l[0] + sm_l[1]) + (sm_l[2] + sm_l[3]);
-    const float As = (sm_a[0][d] + sm_a[1][d]) + (sm_a[2][d] + sm_a[3][d]);
-    store_elem(T{}, out, sh * D + d, np == 0 ? 0.f : As / Ls);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // host-side dispatch
 
 namespace {
 
-// The kernel instance for (dtype, head_dim, block_size, heads per workgroup)
-// is chosen at run time; Op::run<T, D, BS, GT, SPLIT>() does the work with it.
-struct LaunchOp {
-  const DecodeParams& p;
-  int32_t num_seqs;
-  bool cached;
-  hipStream_t stream;
-  template <typename T, int D, int BS, int GT, bool SPLIT>
-  hipError_t run() const {
-    const uint32_t gx = static_cast<uint32_t>(num_seqs) * (p.num_heads / GT);
-    const uint32_t gy = SPLIT ? static_cast<uint32_t>((p.num_parts + kWaves - 1) / kWaves) : 1u;
-    if (cached)
-      hipLaunchKernelGGL((decode_kernel<T, D, BS, GT, SPLIT, true>), dim3(gx, gy), dim3(kWaves * 64), 0, stream,
-                         p);
-    else
-      hipLaunchKernelGGL((decode_kernel<T, D, BS, GT, SPLIT, false>), dim3(gx, gy), dim3(kWaves * 64), 0, stream,
-                         p);
-    return hipGetLastError();
-  }
-};
-
-// Workgroups of the instance that one compute unit holds at once.
-struct OccupancyOp {
-  int* per_cu;
-  template <typename T, int D, int BS, int GT, bool SPLIT>
-  hipError_t run() const {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, decode_kernel<T, D, BS, GT, SPLIT, false>,
-                                                        kWaves * 64, 0);
-  }
-};
-
-template <typename T, int D, int BS, bool SPLIT, typename Op>
-hipError_t by_group(const Op& op, int gt) {
-  switch (gt) {
-    case 1: return op.template run<T, D, BS, 1, SPLIT>();
-    case 2: return op.template run<T, D, BS, 2, SPLIT>();
-    case 4: return op.template run<T, D, BS, 4, SPLIT>();
-    case 8: return op.template run<T, D, BS, 8, SPLIT>();
-    case 16: return op.template run<T, D, BS, 16, SPLIT>();
-  }
-  return hipErrorInvalidValue;
-}
-
-template <typename T, bool SPLIT, typename Op>
-hipError_t by_shape(const Op& op, int d, int bs, int gt) {
-  if (d == 64 && bs == 16) return by_group<T, 64, 16, SPLIT>(op, gt);
-  if (d == 64 && bs == 32) return by_group<T, 64, 32, SPLIT>(op, gt);
-  if (d == 128 && bs == 16) return by_group<T, 128, 16, SPLIT>(op, gt);
-  if (d == 128 && bs == 32) return by_group<T, 128, 32, SPLIT>(op, gt);
-  return hipErrorInvalidValue;
-}
-
-template <bool SPLIT, typename Op>
-hipError_t by_dtype(const Op& op, pa_dtype dt, int d, int bs, int gt) {
+hipError_t by_dtype(const LaunchOp& op, pa_dtype dt, bool split, bool append, int d, int bs, int gt) {
   switch (dt) {
-    case PA_F32: return by_shape<TF32, SPLIT>(op, d, bs, gt);
-    case PA_F16: return by_shape<TF16, SPLIT>(op, d, bs, gt);
-    case PA_BF16: return by_shape<TBF16, SPLIT>(op, d, bs, gt);
+    case PA_F32: return dispatch_f32(op, split, append, d, bs, gt);
+    case PA_F16: return dispatch_f16(op, split, append, d, bs, gt);
+    case PA_BF16: return dispatch_bf16(op, split, append, d, bs, gt);
   }
   return hipErrorInvalidValue;
 }
@@ -526,8 +51,8 @@ DecodeParams make_params(const DecodeArgs& x) {
 hipError_t launch_decode(const DecodeArgs& x, hipStream_t stream) {
   DecodeParams p = make_params(x);
   const int gt = group_tile(x.num_heads / x.num_kv_heads);
-  return by_dtype<false>(LaunchOp{p, x.num_seqs, (x.flags & PA_DECODE_CACHED_KV) != 0, stream}, x.dtype,
-                         x.head_dim, x.block_size, gt);
+  return by_dtype(LaunchOp{p, x.num_seqs, (x.flags & PA_DECODE_CACHED_KV) != 0, stream}, x.dtype, false, false,
+                  x.head_dim, x.block_size, gt);
 }
 
 hipError_t launch_decode_split(const DecodeArgs& x, const SplitLayout& ws, hipStream_t stream) {
@@ -538,10 +63,42 @@ hipError_t launch_decode_split(const DecodeArgs& x, const SplitLayout& ws, hipSt
   p.part_size = ws.partition_size;
   p.num_parts = ws.num_parts;
   const int gt = group_tile(x.num_heads / x.num_kv_heads);
-  hipError_t e = by_dtype<true>(LaunchOp{p, x.num_seqs, (x.flags & PA_DECODE_CACHED_KV) != 0, stream}, x.dtype,
-                                x.head_dim, x.block_size, gt);
+  hipError_t e = by_dtype(LaunchOp{p, x.num_seqs, (x.flags & PA_DECODE_CACHED_KV) != 0, stream}, x.dtype, true,
+                           false, x.head_dim, x.block_size, gt);
   if (e != hipSuccess) return e;
   return launch_lse_reduce(x.out, ws, x.context_lens, x.seq_order, x.num_seqs, x.num_heads, x.head_dim,
+                           p.len_limit, x.dtype, stream);
+}
+
+hipError_t launch_decode_append(const DecodeArgs& x, const void* new_k, const void* new_v, const int32_t* slots,
+                                const SplitLayout* ws, hipStream_t stream) {
+  const int group = x.num_heads / x.num_kv_heads;
+  const int gt = group_tile(group);
+  if (gt != group) {
+    // A KV head spans several workgroups, which cannot order one writer
+    // before the other readers: write first, then decode.
+    hipError_t e = launch_reshape_and_cache(new_k, new_v, const_cast<void*>(x.key_cache),
+                                            const_cast<void*>(x.value_cache), slots, x.num_seqs, x.num_blocks,
+                                            x.num_kv_heads, x.head_dim, x.dtype == PA_F32 ? 4 : 2, x.block_size,
+                                            stream);
+    if (e != hipSuccess) return e;
+    return ws ? launch_decode_split(x, *ws, stream) : launch_decode(x, stream);
+  }
+  DecodeParams p = make_params(x);
+  p.new_k = static_cast<const char*>(new_k);
+  p.new_v = static_cast<const char*>(new_v);
+  p.slots = slots;
+  if (ws) {
+    p.ws_m = ws->m;
+    p.ws_l = ws->l;
+    p.ws_o = ws->o;
+    p.part_size = ws->partition_size;
+    p.num_parts = ws->num_parts;
+  }
+  hipError_t e = by_dtype(LaunchOp{p, x.num_seqs, (x.flags & PA_DECODE_CACHED_KV) != 0, stream}, x.dtype,
+                          ws != nullptr, true, x.head_dim, x.block_size, gt);
+  if (e != hipSuccess || !ws) return e;
+  return launch_lse_reduce(x.out, *ws, x.context_lens, x.seq_order, x.num_seqs, x.num_heads, x.head_dim,
                            p.len_limit, x.dtype, stream);
 }
 
@@ -549,7 +106,9 @@ hipError_t single_pass_shape(const DecodeArgs& x, int64_t* workgroups, int64_t* 
   const int gt = group_tile(x.num_heads / x.num_kv_heads);
   *workgroups = static_cast<int64_t>(x.num_seqs) * (x.num_heads / gt);
   int per_cu = 0, dev = 0, cus = 0;
-  hipError_t e = by_dtype<false>(OccupancyOp{&per_cu}, x.dtype, x.head_dim, x.block_size, gt);
+  hipError_t e = x.dtype == PA_F32   ? occupancy_f32(&per_cu, x.head_dim, x.block_size, gt)
+                 : x.dtype == PA_F16 ? occupancy_f16(&per_cu, x.head_dim, x.block_size, gt)
+                                     : occupancy_bf16(&per_cu, x.head_dim, x.block_size, gt);
   if (e == hipSuccess) e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   *resident = static_cast<int64_t>(per_cu) * cus;

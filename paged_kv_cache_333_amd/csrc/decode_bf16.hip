@@ -1,0 +1,13 @@
+// Instantiates the bf16 decode kernels (every head_dim, block size, heads per
+// workgroup, single/split, fused write or not) in a translation unit of its own.
+#include "decode_kernel.hpp"
+
+namespace pa {
+
+hipError_t dispatch_bf16(const LaunchOp& op, bool split, bool append, int d, int bs, int gt) {
+  return dispatch_t<TBF16>(op, split, append, d, bs, gt);
+}
+
+hipError_t occupancy_bf16(int* per_cu, int d, int bs, int gt) { return occupancy_t<TBF16>(per_cu, d, bs, gt); }
+
+}  // namespace pa

@@ -43,6 +43,10 @@ hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t*
 hipError_t launch_upload(void* dst, const void* src_device_view, int64_t nbytes, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeArgs& a, const SplitLayout& ws, hipStream_t stream);
+// Slot-mapping write of one new token per sequence fused into the decode
+// (single pass when ws is null, else split + merge).
+hipError_t launch_decode_append(const DecodeArgs& a, const void* new_k, const void* new_v, const int32_t* slots,
+                                const SplitLayout* ws, hipStream_t stream);
 // Workgroups the single-pass launch would start, and how many of them the
 // current device holds at once.
 hipError_t single_pass_shape(const DecodeArgs& a, int64_t* workgroups, int64_t* resident);
