@@ -8,6 +8,8 @@ nothing from the HIP side.
   attention   gather through the block table, then standard softmax attention;
               the per-partition (m, l, o) partials and their log-sum-exp merge
   cache_ops   the slot-mapping scatter of new K/V, and whole-block copies
+  quant       the 8-bit KV codes (FP8 E4M3, int8): encode with per-pool
+              scales, decode
   allocator   the block pool: FIFO free list, per-block refcounts, fork,
               append with copy-on-write, free
 
@@ -15,4 +17,4 @@ Every function is pinned by the CPU tests (tests/test_oracle_*.py) to closed
 forms, invariants, an independent library attention, brute force on tiny
 inputs and the worked examples the pages print (tests/golden/).
 """
-from . import allocator, attention, cache_ops  # noqa: F401
+from . import allocator, attention, cache_ops, quant  # noqa: F401

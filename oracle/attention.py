@@ -29,13 +29,19 @@ What is computed, and where the pages define it:
   (m_p = max logit, l_p = sum exp(z - m_p), o_p = normalised partial output)
   per partition, and merges with the log-sum-exp rule.
 
+* 8-bit pools (quant = (fmt, k_scale, v_scale)): the pools hold codes and
+  stand for decode(code) * scale (oracle/quant.py); the attention over those
+  values is the same definition.
+
 Inputs are NumPy arrays in storage type: float32, float16, or bf16 given as
-uint16 bit patterns.  Everything is upcast exactly to float64; the scale is
-taken as the float32 value the kernels receive.
+uint16 bit patterns (8-bit pools: uint8 codes).  Everything is upcast exactly
+to float64; the scales are taken as the float32 values the kernels receive.
 """
 from __future__ import annotations
 
 import numpy as np
+
+from . import quant as Q
 
 
 def to_f64(x, dtype: str) -> np.ndarray:
@@ -59,14 +65,14 @@ def blocks_for(num_tokens: int, block_size: int) -> int:
     return (num_tokens + block_size - 1) // block_size
 
 
-def gather_kv(key_cache, value_cache, table_row, num_tokens: int, kv_head: int, dtype: str):
-    """Collect the first `num_tokens` K and V rows of one sequence and KV head.
+def gather_rows(key_cache, value_cache, table_row, num_tokens: int, kv_head: int):
+    """Collect the first `num_tokens` K and V rows of one sequence and KV head, as stored.
 
     Logical block j of the sequence lives in physical block table_row[j]; its
     rows are tokens j*bs .. j*bs + bs - 1, of which only those below
     `num_tokens` are valid ("PagedAttention 实现细节" §3.1, the gather step).
     key_cache is [NB, H_kv, bs, D] and value_cache [NB, H_kv, D, bs].
-    Returns float64 arrays K, V of shape [num_tokens, head_dim].
+    Returns storage-typed arrays K, V of shape [num_tokens, head_dim].
     """
     num_blocks, _, block_size, head_dim = key_cache.shape
     ks, vs = [], []
@@ -75,12 +81,29 @@ def gather_kv(key_cache, value_cache, table_row, num_tokens: int, kv_head: int, 
         if not 0 <= phys < num_blocks:
             raise IndexError(f"block table entry {phys} outside the pool of {num_blocks}")
         valid = min(block_size, num_tokens - j * block_size)
-        ks.append(to_f64(key_cache[phys, kv_head, :valid, :], dtype))
-        vs.append(to_f64(value_cache[phys, kv_head, :, :valid].T, dtype))
+        ks.append(key_cache[phys, kv_head, :valid, :])
+        vs.append(value_cache[phys, kv_head, :, :valid].T)
     if not ks:
-        empty = np.zeros((0, head_dim), dtype=np.float64)
+        empty = np.zeros((0, head_dim), dtype=key_cache.dtype)
         return empty, empty.copy()
     return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
+
+
+def gather_kv(key_cache, value_cache, table_row, num_tokens: int, kv_head: int, dtype: str):
+    """gather_rows, upcast exactly to float64 [num_tokens, head_dim]."""
+    K, V = gather_rows(key_cache, value_cache, table_row, num_tokens, kv_head)
+    return to_f64(K, dtype), to_f64(V, dtype)
+
+
+def kv_for(key_cache, value_cache, table_row, num_tokens: int, kv_head: int, dtype: str, quant=None):
+    """float64 K, V of one sequence and KV head.  With quant = (fmt, k_scale,
+    v_scale) the pools hold 8-bit codes and stand for decode(code) * scale
+    (oracle/quant.py); otherwise they hold `dtype` values."""
+    if quant is None:
+        return gather_kv(key_cache, value_cache, table_row, num_tokens, kv_head, dtype)
+    fmt, k_scale, v_scale = quant
+    K8, V8 = gather_rows(key_cache, value_cache, table_row, num_tokens, kv_head)
+    return Q.dequantize(K8, k_scale, fmt), Q.dequantize(V8, v_scale, fmt)
 
 
 def logits(q64: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:
@@ -102,12 +125,13 @@ def attend(q64: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.nd
 
 
 def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scale: float,
-                 dtype: str) -> np.ndarray:
+                 dtype: str, quant=None) -> np.ndarray:
     """out[s, h] = attention of query[s, h] over the first context_lens[s] tokens of
     sequence s, gathered through block_tables[s] from the KV head h // G.
 
     query [S, H, D]; key_cache [NB, H_kv, bs, D]; value_cache [NB, H_kv, D, bs];
     block_tables [S, MB]; context_lens [S].  Returns float64 [S, H, D].
+    quant = (fmt, k_scale, v_scale) when the pools hold 8-bit codes.
     """
     S, H, D = query.shape
     H_kv = key_cache.shape[1]
@@ -119,18 +143,18 @@ def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scal
     for s in range(S):
         n = int(context_lens[s])
         for g in range(H_kv):
-            K, V = gather_kv(key_cache, value_cache, block_tables[s], n, g, dtype)
+            K, V = kv_for(key_cache, value_cache, block_tables[s], n, g, dtype, quant)
             for h in range(g * G, (g + 1) * G):
                 out[s, h] = attend(to_f64(query[s, h], dtype), K, V, sig)
     return out
 
 
 def decode_one(query, key_cache, value_cache, table_row, num_tokens: int, head: int,
-               num_heads: int, scale: float, dtype: str) -> np.ndarray:
+               num_heads: int, scale: float, dtype: str, quant=None) -> np.ndarray:
     """One output row out[s, head] (query = query[s], table_row = block_tables[s])."""
     H_kv = key_cache.shape[1]
     g = head // (num_heads // H_kv)
-    K, V = gather_kv(key_cache, value_cache, table_row, num_tokens, g, dtype)
+    K, V = kv_for(key_cache, value_cache, table_row, num_tokens, g, dtype, quant)
     return attend(to_f64(query[head], dtype), K, V, scale_f64(scale))
 
 
@@ -171,7 +195,7 @@ def lse_merge(m: np.ndarray, l: np.ndarray, o: np.ndarray) -> np.ndarray:
 
 
 def split_decode_partials(query, key_cache, value_cache, block_tables, context_lens, scale: float,
-                          dtype: str, partition_size: int, seqs=None, heads=None):
+                          dtype: str, partition_size: int, seqs=None, heads=None, quant=None):
     """Partials (m, l, o) for every (seq, head) in `seqs` x `heads`: a dict keyed by (s, h)."""
     S, H, D = query.shape
     H_kv = key_cache.shape[1]
@@ -186,7 +210,7 @@ def split_decode_partials(query, key_cache, value_cache, block_tables, context_l
         for h in heads:
             g = h // G
             if g not in cache:
-                cache[g] = gather_kv(key_cache, value_cache, block_tables[s], n, g, dtype)
+                cache[g] = kv_for(key_cache, value_cache, block_tables[s], n, g, dtype, quant)
             K, V = cache[g]
             res[(s, h)] = partition_partials(to_f64(query[s, h], dtype), K, V, sig, partition_size)
     return res

@@ -15,11 +15,14 @@ Pools: key_cache [NB, H_kv, bs, D] (token rows), value_cache [NB, H_kv, D, bs]
 (block size innermost, "Ascend C算子开发高阶实战…" §3.1/§5.2), so a token's
 value vector is written down column `offset` of its tile.  Arrays are NumPy
 storage arrays (bf16 as uint16 bits), so the results are bit patterns and
-compare bit-exactly.
+compare bit-exactly.  8-bit pools hold uint8 codes; their write quantises
+first (reshape_and_cache_quant), their block copy is the same byte copy.
 """
 from __future__ import annotations
 
 import numpy as np
+
+from . import quant as Q
 
 
 def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping):
@@ -34,6 +37,15 @@ def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping):
         kc[block, :, offset, :] = key[i]
         vc[block, :, :, offset] = value[i]
     return kc, vc
+
+
+def reshape_and_cache_quant(key, value, key_cache, value_cache, slot_mapping, dtype: str, fmt: str,
+                            k_scale: float, v_scale: float):
+    """The slot-mapping write into 8-bit pools: each new row is quantised
+    (code = Q(x / scale), oracle/quant.py; keys with k_scale, values with
+    v_scale), then written exactly like reshape_and_cache."""
+    return reshape_and_cache(Q.quantize(key, dtype, k_scale, fmt), Q.quantize(value, dtype, v_scale, fmt),
+                             key_cache, value_cache, slot_mapping)
 
 
 def copy_blocks(key_cache, value_cache, pairs):

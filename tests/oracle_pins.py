@@ -298,3 +298,184 @@ def check_p2_lifecycle():
             al.seq_free(st["seq"])
         assert al.ref_count(first) == st["expect_ref0"]
         assert al.num_free_blocks() == st["expect_free"]
+
+
+# ----------------------------------------------------------------------------
+# 8-bit KV codes (oracle/quant.py)
+
+def check_e4m3_special_values():
+    """Fixed points of the OCP FP8 E4M3 ("fn") format: bias 7, three mantissa
+    bits, subnormals below 2^-6, no infinities, NaN only at S.1111.111."""
+    from oracle import quant as Q
+    t = Q.E4M3_TABLE
+    assert t[0x00] == 0.0 and not np.signbit(t[0x00])
+    assert t[0x80] == 0.0 and np.signbit(t[0x80])
+    assert t[0x01] == 2.0 ** -9          # smallest subnormal
+    assert t[0x07] == 7 * 2.0 ** -9      # largest subnormal
+    assert t[0x08] == 2.0 ** -6          # smallest normal
+    assert t[0x38] == 1.0
+    assert t[0x3C] == 1.5
+    assert t[0x7E] == 448.0              # largest finite
+    assert t[0xFE] == -448.0
+    nan = [c for c in range(256) if np.isnan(t[c])]
+    assert nan == [0x7F, 0xFF], nan
+    assert not np.isinf(t).any()
+    pos = t[:0x7F]
+    assert np.all(np.diff(pos) > 0), "codes 0x00..0x7E must increase"
+    assert np.array_equal(t[0x80:0xFF], -pos)
+
+
+def check_e4m3_table_vs_torch():
+    """The code table against torch's float8_e4m3fn (an independent decoder)."""
+    import torch
+    from oracle import quant as Q
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    same = (ref == Q.E4M3_TABLE) | (np.isnan(ref) & np.isnan(Q.E4M3_TABLE))
+    assert same.all(), np.nonzero(~same)
+    fin = ~np.isnan(ref)
+    assert np.array_equal(np.signbit(ref[fin]), np.signbit(Q.E4M3_TABLE[fin]))
+
+
+def _e4m3_probe_values(seed):
+    from oracle import quant as Q
+    rng = np.random.default_rng(seed)
+    pos = Q.E4M3_TABLE[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2            # every tie between neighbours
+    near = np.concatenate([np.nextafter(mids.astype(np.float32), np.float32(0)),
+                           np.nextafter(mids.astype(np.float32), np.float32(1e9))])
+    mags = np.exp2(rng.uniform(-12, 9, size=4000))
+    mags = mags[mags <= 464]
+    y = np.concatenate([pos, mids, near.astype(np.float64), mags, [464.0, 2.0 ** -10, 2.0 ** -11]])
+    y = y.astype(np.float32)
+    sign = np.where(rng.random(y.shape) < 0.5, -1, 1).astype(np.float32)
+    return np.concatenate([y, y * sign])
+
+
+def check_e4m3_encode_vs_torch(seed=31):
+    """Encoding agrees with torch's round-to-nearest-even cast wherever that
+    cast does not overflow (|y| <= 464), ties and subnormals included."""
+    import torch
+    from oracle import quant as Q
+    y = _e4m3_probe_values(seed)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = Q.encode(y, "fp8_e4m3")
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(y[i]), int(got[i]), int(ref[i])) for i in bad[:5]]
+
+
+def check_e4m3_round_trip():
+    from oracle import quant as Q
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = Q.decode(codes, "fp8_e4m3").astype(np.float32)
+    assert np.array_equal(Q.encode(vals, "fp8_e4m3"), codes)
+
+
+def check_e4m3_saturation():
+    """Saturation past +-448 and the NaN code (the chosen readings)."""
+    from oracle import quant as Q
+    y = np.array([448.0, 449.0, 463.9, 464.0, 480.0, 1e30, np.inf, -449.0, -np.inf, np.nan],
+                 dtype=np.float32)
+    want = [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x7F]
+    assert Q.encode(y, "fp8_e4m3").tolist() == want
+
+
+def check_int8_encode(seed=37):
+    """int8 codes: nearest integer by brute force over [-127, 127], ties to
+    the even integer, against torch.round; saturation; NaN -> 0."""
+    import torch
+    from oracle import quant as Q
+    rng = np.random.default_rng(seed)
+    y = np.concatenate([rng.uniform(-140, 140, size=3000), np.arange(-130, 131) + 0.5,
+                        [-0.5, 0.5, 1.5, 2.5, -2.5]]).astype(np.float32)
+    got = Q.encode(y, "int8").view(np.int8).astype(np.int64)
+    ks = np.arange(-127, 128)
+    d = np.abs(y.astype(np.float64)[:, None] - ks[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = (d == best)
+    brute = np.where((cand & (ks % 2 == 0)).any(axis=1), ks[np.argmax(cand & (ks % 2 == 0), axis=1)],
+                     ks[np.argmax(cand, axis=1)])
+    assert np.array_equal(got, brute)
+    ref = torch.clamp(torch.round(torch.from_numpy(y)), -127, 127).to(torch.int64).numpy()
+    assert np.array_equal(got, ref)
+    special = Q.encode(np.array([np.inf, -np.inf, np.nan, 1e9, -1e9], np.float32), "int8").view(np.int8)
+    assert special.tolist() == [127, -127, 0, 127, -127]
+    assert Q.INT8_TABLE[0x80] == -128 and Q.INT8_TABLE[0xFF] == -1 and Q.INT8_TABLE[0x7F] == 127
+
+
+def check_quantize_division(seed=41):
+    """quantize(x, scale) takes the code of the float32 quotient x / scale:
+    compared with torch computing the quotient and casting on its own."""
+    import torch
+    from oracle import quant as Q
+    x = normal_host((4000,), seed, "f16")
+    for scale in (5.0 / 448, 0.3, 1.0 / 7):
+        tq = torch.from_numpy(x.astype(np.float32)) / torch.tensor(scale, dtype=torch.float32)
+        ref8 = tq.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(Q.quantize(x, "f16", scale, "fp8_e4m3"), ref8)
+        refi = torch.clamp(torch.round(tq * 100), -127, 127)  # a wider spread for int8
+        xi = (x.astype(np.float32) * np.float32(100)).astype(np.float16)
+        tqi = torch.from_numpy(xi.astype(np.float32)) / torch.tensor(scale, dtype=torch.float32)
+        refi = torch.clamp(torch.round(tqi), -127, 127).to(torch.int8).view(torch.uint8).numpy()
+        assert np.array_equal(Q.quantize(xi, "f16", scale, "int8"), refi)
+
+
+def _lossless_pools(fmt, seed, NB, Hkv, bs, D):
+    """Random non-NaN codes and the float32 values they stand for at scale 1."""
+    from oracle import quant as Q
+    rng = np.random.default_rng(seed)
+    allowed = np.array([c for c in range(256) if not np.isnan(Q.decode(c, fmt))], dtype=np.uint8)
+    allowed = allowed[np.abs(Q.decode(allowed, fmt)) <= 8]  # keeps the logits moderate
+    kc8 = rng.choice(allowed, size=(NB, Hkv, bs, D))
+    vc8 = rng.choice(allowed, size=(NB, Hkv, D, bs))
+    return kc8, vc8
+
+
+def check_quant_attention_lossless(seed=43):
+    """Pools whose values are exactly code * scale (power-of-two scales, K and
+    V different): attention over the 8-bit pools equals attention over the
+    same values stored in float32."""
+    from oracle import quant as Q
+    S, H, Hkv, D, bs = 3, 8, 2, 32, 16
+    ctx = [1, 29, 64]
+    NB = 16
+    k_scale, v_scale = 0.125, 4.0
+    rng = np.random.default_rng(seed)
+    tables = np.stack([rng.permutation(NB)[:4] for _ in range(S)]).astype(np.int32)
+    q = normal_host((S, H, D), seed + 1, "f32")
+    for fmt in Q.FORMATS:
+        kc8, vc8 = _lossless_pools(fmt, seed + 2, NB, Hkv, bs, D)
+        kf = (Q.decode(kc8, fmt) * k_scale).astype(np.float32)
+        vf = (Q.decode(vc8, fmt) * v_scale).astype(np.float32)
+        want = A.paged_decode(q, kf, vf, tables, ctx, 0.25, "f32")
+        got = A.paged_decode(q, kc8, vc8, tables, ctx, 0.25, "f32", quant=(fmt, k_scale, v_scale))
+        assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, np.max(np.abs(want))), fmt
+
+
+def check_quant_write_round_trip(seed=47):
+    """Rows made of code * scale values, written through the quantising
+    slot-mapping write, read back as exactly those values."""
+    from oracle import quant as Q
+    NB, Hkv, bs, D = 6, 2, 16, 32
+    k_scale, v_scale = 0.0625, 2.0
+    rng = np.random.default_rng(seed)
+    for fmt in Q.FORMATS:
+        kc8, vc8 = _lossless_pools(fmt, seed, NB, Hkv, bs, D)
+        n = 9
+        slots = rng.choice(NB * bs, size=n, replace=False).astype(np.int32)
+        kcode, vcode = _lossless_pools(fmt, seed + 1, n, Hkv, 1, D)
+        kv = (Q.decode(kcode[:, :, 0, :], fmt) * k_scale).astype(np.float32)
+        vv = (Q.decode(vcode[:, :, :, 0], fmt) * v_scale).astype(np.float32)
+        kc2, vc2 = C.reshape_and_cache_quant(kv, vv, kc8, vc8, slots, "f32", fmt, k_scale, v_scale)
+        for i, slot in enumerate(slots.tolist()):
+            b, o = divmod(slot, bs)
+            assert np.array_equal(Q.dequantize(kc2[b, :, o, :], k_scale, fmt), kv[i].astype(np.float64))
+            assert np.array_equal(Q.dequantize(vc2[b, :, :, o], v_scale, fmt), vv[i].astype(np.float64))
+        untouched = np.ones((NB, bs), bool)
+        for slot in slots.tolist():
+            untouched[slot // bs, slot % bs] = False
+        assert np.array_equal(kc2.transpose(0, 2, 1, 3)[untouched], kc8.transpose(0, 2, 1, 3)[untouched])
+
+
+QUANT_PINS = [check_e4m3_special_values, check_e4m3_table_vs_torch, check_e4m3_encode_vs_torch,
+              check_e4m3_round_trip, check_e4m3_saturation, check_int8_encode, check_quantize_division,
+              check_quant_attention_lossless, check_quant_write_round_trip]

@@ -8,6 +8,7 @@ import pytest
 
 from oracle import allocator as AL
 from oracle import attention as A
+from oracle import quant as Q
 from tests import oracle_pins as P
 
 
@@ -159,3 +160,87 @@ ALLOCATOR_PINS = [P.check_p1_block_mapping, P.check_block_counts, P.check_addres
 def test_allocator_mutant_is_caught(monkeypatch, cls):
     monkeypatch.setattr(AL, "BlockAllocator", cls)
     assert _caught(ALLOCATOR_PINS), f"no pin caught {cls.__name__}"
+
+
+# ----------------------------------------------------------------------------
+# 8-bit KV codes
+
+def _e4m3_ties_away(y32, _orig=Q._e4m3_encode):
+    import numpy as np
+    out = _orig(y32)
+    mag = np.abs(y32.astype(np.float64))
+    pos = Q.E4M3_TABLE[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2
+    at = np.isin(mag, mids)
+    return np.where(at & ((out & 1) == 0) & (mag > Q.decode(out & 0x7F, "fp8_e4m3")), out + 1, out).astype(np.uint8)
+
+
+def _e4m3_overflow_nan(y32, _orig=Q._e4m3_encode):
+    import numpy as np
+    out = _orig(y32)
+    return np.where(np.abs(y32) > 448, 0x7F, out).astype(np.uint8)
+
+
+def _e4m3_value_no_subnormals(code):
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0 and m:
+        mag = (1.0 + m / 8.0) * 2.0 ** -7
+        return -mag if code & 0x80 else mag
+    return _ORIG_E4M3_VALUE(code)
+
+
+_ORIG_E4M3_VALUE = Q.e4m3_value
+
+
+def _quantize_multiplies(x, dtype, scale, fmt):
+    import numpy as np
+    return Q.encode(Q.to_f32(x, dtype) * np.float32(scale), fmt)
+
+
+def _dequantize_divides(codes, scale, fmt):
+    import numpy as np
+    return Q.decode(codes, fmt) / float(np.float32(scale))
+
+
+def _kv_swapped_scales(kc, vc, row, n, g, dtype, quant=None, _orig=A.kv_for):
+    if quant is not None:
+        quant = (quant[0], quant[2], quant[1])
+    return _orig(kc, vc, row, n, g, dtype, quant)
+
+
+def _int8_ties_away(y32):
+    import numpy as np
+    y = y32.astype(np.float64)
+    r = np.clip(np.sign(y) * np.floor(np.abs(np.nan_to_num(y)) + 0.5), -127, 127)
+    return r.astype(np.int64).astype(np.uint8)
+
+
+def _int8_asymmetric(y32):
+    import numpy as np
+    y = np.nan_to_num(y32.astype(np.float64))
+    return np.clip(np.rint(y), -128, 127).astype(np.int64).astype(np.uint8)
+
+
+QUANT_MUTANTS = [
+    (Q, "_e4m3_encode", _e4m3_ties_away),
+    (Q, "_e4m3_encode", _e4m3_overflow_nan),
+    (Q, "quantize", _quantize_multiplies),
+    (Q, "dequantize", _dequantize_divides),
+    (A, "kv_for", _kv_swapped_scales),
+    (Q, "_int8_encode", _int8_ties_away),
+    (Q, "_int8_encode", _int8_asymmetric),
+]
+
+
+@pytest.mark.parametrize("mod,name,bad", QUANT_MUTANTS, ids=[f"{n}:{b.__name__}" for _, n, b in QUANT_MUTANTS])
+def test_quant_mutant_is_caught(monkeypatch, mod, name, bad):
+    monkeypatch.setattr(mod, name, bad)
+    assert _caught(P.QUANT_PINS), f"no pin caught the planted mistake in {name}"
+
+
+def test_quant_table_mutant_is_caught(monkeypatch):
+    import numpy as np
+    table = np.array([_e4m3_value_no_subnormals(c) for c in range(256)])
+    monkeypatch.setattr(Q, "E4M3_TABLE", table)
+    monkeypatch.setattr(Q, "_POS_VALUES", table[:0x7F])
+    assert _caught(P.QUANT_PINS)
