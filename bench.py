@@ -7,14 +7,16 @@ One step = the whole hot path over one batch:
   pa_copy_blocks (when pairs exist), pa_reshape_and_cache of the new K/V, and the
   decode over every cached token (pa_decode_auto: single pass, or split partials +
   LSE merge).  --fused-write runs the write inside the decode launch instead
-  (pa_decode_append).
+  (pa_decode_append).  Workloads 6 and 7 keep the pools as 8-bit codes (FP8 E4M3 /
+  int8 with per-pool scales): pa_reshape_and_cache_quant quantises the new K/V and
+  pa_decode_quant decodes.
 
 Default workload: 64 sequences, 32 query / 32 KV heads of dimension 128, fp16,
 block size 16, contexts uniform in [256, 2048] (a LLaMA-7B-like layer), pool of
 8192 blocks in shuffled order.  Inputs are synthetic (seeded normals) and
 resident in HBM before the timed region.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload 1..5] [--path single|split]
+  python bench.py [--steps K] [--warmup W] [--workload 1..7] [--path single|split]
 """
 from __future__ import annotations
 
@@ -38,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--path", choices=["auto", "single", "split"], default="auto",
                     help="decode path: pa_decode_auto (default: the library picks), pa_decode or pa_decode_split")
     ap.add_argument("--partition", type=int, default=512)
@@ -169,7 +171,8 @@ def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
         json.dump(rec, f, indent=1, sort_keys=True)
         f.write("\n")
     out = [f"# rocprofv3: decode kernel, workload {workload} ({w_path} path)", "",
-           f"Decode kernel source digest (decode.hip + device_common.hpp): `{source_digest()}`", "",
+           f"Decode kernel source digest (decode.hip + decode_kernel.hpp + device_common.hpp): "
+           f"`{source_digest()}`", "",
            "Commands (run from any directory with TMPDIR=/tmp; OUTDIR is a scratch folder):", "", "```"]
     out += profile_commands(workload, "OUTDIR", path) + ["```", "", "## Kernel trace (--kernel-trace --stats)", "",
                                                         "| kernel | calls | avg us | min us | max us | % time |",
@@ -193,7 +196,7 @@ def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
 
 def source_digest() -> str:
     h = hashlib.sha256()
-    for name in ("decode.hip", "device_common.hpp"):
+    for name in ("decode.hip", "decode_kernel.hpp", "device_common.hpp"):
         with open(os.path.join(ROOT, "paged_kv_cache_333_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -259,8 +262,16 @@ class Bench:
 
         # device data, resident before timing
         k_shape, v_shape = synth.pool_shapes(w)
-        self.kc = synth.normal_device(k_shape, seeds["key_cache"], w.dtype)
-        self.vc = synth.normal_device(v_shape, seeds["value_cache"], w.dtype)
+        self.quant = bool(w.kv_format)
+        if self.quant and args.fused_write:
+            raise SystemExit("--fused-write has no 8-bit form: 8-bit pools are written by "
+                             "pa_reshape_and_cache_quant")
+        if self.quant:
+            self.kc = synth.normal_codes_device(k_shape, seeds["key_cache"], w.kv_format)
+            self.vc = synth.normal_codes_device(v_shape, seeds["value_cache"], w.kv_format)
+        else:
+            self.kc = synth.normal_device(k_shape, seeds["key_cache"], w.dtype)
+            self.vc = synth.normal_device(v_shape, seeds["value_cache"], w.dtype)
         self.q = synth.normal_device((S, H, D), seeds["query"], w.dtype)
         R = 8  # distinct new-token K/V batches, cycled
         self.newk = synth.normal_device((R, S, Hkv, D), seeds["new_key"], w.dtype)
@@ -290,6 +301,7 @@ class Bench:
             b["staged"].record(self.stream)
             self.bufs.append(b)
         self.elem = synth.ELEM_BYTES[w.dtype]
+        self.kv_elem = 1 if self.quant else self.elem
         torch.cuda.synchronize()
 
     def step(self, k: int, timing: list | None):
@@ -313,12 +325,21 @@ class Bench:
             pa.pa_copy_blocks(self.kc, self.vc, b["pairs_d"], num_pairs=npairs)
         r = k % self.newk.shape[0]
         fused = self.path == "auto" and self.args.fused_write
-        if not fused:
+        if self.quant:
+            pa.pa_reshape_and_cache_quant(self.newk[r], self.newv[r], self.kc, self.vc, b["slots_d"], w.k_scale,
+                                          w.v_scale, kv_format=w.kv_format)
+        elif not fused:
             pa.pa_reshape_and_cache(self.newk[r], self.newv[r], self.kc, self.vc, b["slots_d"])
         if timing is not None:
             e0, e1 = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
             e0.record(self.stream)
-        if self.path == "single":
+        if self.quant:
+            self.path_ran.add(pa.pa_decode_quant(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"],
+                                                 self.max_ctx, w.scale, w.k_scale, w.v_scale,
+                                                 kv_format=w.kv_format, partition_size=self.args.partition,
+                                                 workspace=self.ws, split=self.path == "split", seq_order=order,
+                                                 cached_kv=self.cached))
+        elif self.path == "single":
             pa.pa_decode(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"], self.max_ctx, w.scale,
                          seq_order=order, cached_kv=self.cached)
             self.path_ran.add("single")
@@ -370,15 +391,20 @@ class Bench:
         remap = -np.ones(w.num_blocks, dtype=np.int32)
         remap[used] = np.arange(len(used), dtype=np.int32)
         idx = torch.from_numpy(used.astype(np.int64)).to(self.dev)
-        kc = synth.to_numpy(self.kc.index_select(0, idx), w.dtype)
-        vc = synth.to_numpy(self.vc.index_select(0, idx), w.dtype)
+        if self.quant:
+            kc = self.kc.index_select(0, idx).cpu().numpy()
+            vc = self.vc.index_select(0, idx).cpu().numpy()
+        else:
+            kc = synth.to_numpy(self.kc.index_select(0, idx), w.dtype)
+            vc = synth.to_numpy(self.vc.index_select(0, idx), w.dtype)
         q = synth.to_numpy(self.q, w.dtype)
+        quant = (w.kv_format, w.k_scale, w.v_scale) if self.quant else None
         t2 = np.where(tabs >= 0, remap[np.maximum(tabs, 0)], -1)
         passes, tokens = 0, 0
         with threadpool_limits(1):
             t0 = time.perf_counter()
             while True:
-                A.paged_decode(q, kc, vc, t2, lens, w.scale, w.dtype)
+                A.paged_decode(q, kc, vc, t2, lens, w.scale, w.dtype, quant=quant)
                 passes += 1
                 tokens += int(lens.sum())
                 el = time.perf_counter() - t0
@@ -414,7 +440,7 @@ def main():
     e = bench.elem
     durs = [a.elapsed_time(b) * 1e-3 for a, b, *_ in timing]  # seconds
     kv_tokens = sum(t[2] for t in timing)
-    kv_bytes_token = 2 * w.num_kv_heads * w.head_dim * e
+    kv_bytes_token = 2 * w.num_kv_heads * w.head_dim * bench.kv_elem
     qo_bytes = 2 * w.num_seqs * w.num_heads * w.head_dim * e
     # the fused call also reads the step's new K/V rows and writes them into the pools
     fused_write = 2 * w.num_seqs * kv_bytes_token if (bench.path == "auto" and args.fused_write) else 0
@@ -438,11 +464,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "kv_cache_dtype": w.kv_format or w.dtype,
                    "context_lens": "per workload definition, +1 token per step",
                    "mean_kv_tokens_per_step": kv_tokens / len(timing),
                    "decode_path": ("auto: " if bench.path == "auto" else "") + "+".join(sorted(bench.path_ran)),
                    "kv_write": "fused into the decode (pa_decode_append)" if fused_write
-                   else "pa_reshape_and_cache, then decode",
+                   else ("pa_reshape_and_cache_quant, then pa_decode_quant" if bench.quant
+                         else "pa_reshape_and_cache, then decode"),
                    "partition_size": args.partition if "split" in bench.path_ran else None,
                    "launch_order": bench.order, "kv_cache_policy": "cached" if bench.cached else "stream",
                    "cow_pairs_per_step": sum(t[4] for t in timing) / len(timing)},

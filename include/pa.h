@@ -37,8 +37,9 @@
  * Query head h reads KV head h / (num_heads / num_kv_heads) (contiguous
  * groups; num_heads must be a multiple of num_kv_heads).
  *
- * Supported shapes: dtype f32, f16, bf16; head_dim 64 or 128; block_size 16
- * or 32.  Other values return PA_ERR_UNSUPPORTED.
+ * Supported shapes: dtype f32, f16, bf16 (8-bit pools: see the quantised KV
+ * cache below); head_dim 64 or 128; block_size 16 or 32.  Other values
+ * return PA_ERR_UNSUPPORTED.
  *
  * Streams: device calls enqueue work on `stream` (a hipStream_t; NULL is the
  * null stream) and return without synchronising.  The library allocates no
@@ -59,7 +60,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -73,7 +74,18 @@ typedef enum pa_status {
   PA_ERR_HIP = 8                 /* a HIP runtime call or kernel launch failed */
 } pa_status;
 
-typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+/* Element types.  PA_F32, PA_F16 and PA_BF16 are model types (query, out,
+ * new K/V rows, 16-bit and 32-bit pools).  PA_FP8_E4M3 and PA_INT8 are the
+ * 8-bit KV code types of the quantised cache (see pa_reshape_and_cache_quant):
+ * they are valid only as kv_dtype of the *_quant calls and as the dtype of
+ * pa_copy_blocks on 8-bit pools. */
+typedef enum pa_dtype {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  PA_FP8_E4M3 = 3, /* OCP FP8 E4M3 ("fn"): bias 7, 3 mantissa bits, max 448, NaN 0x7F/0xFF */
+  PA_INT8 = 4      /* two's-complement int8 */
+} pa_dtype;
 
 /* Decode flags (bit mask).  By default K/V rows are read with a streaming
  * (non-temporal) cache hint: each KV element is read once per step, so it
@@ -83,6 +95,9 @@ typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
  * can hit the caches; order such sharers next to each other in seq_order.
  * Results do not depend on the flag. */
 #define PA_DECODE_CACHED_KV 1u
+/* pa_decode_quant only: take the split path (partials + merge) regardless of
+ * the launch shape; the workspace must then be large enough. */
+#define PA_DECODE_SPLIT 2u
 
 /* ======================================================================== *
  * Host block allocator                                                      *
@@ -338,6 +353,55 @@ pa_status pa_lse_reduce(void* out, const void* workspace, size_t workspace_bytes
                         const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                         int32_t head_dim, int32_t max_context_len, int32_t partition_size,
                         pa_dtype dtype, void* stream);
+
+/* ======================================================================== *
+ * Quantised (8-bit) KV cache                                                *
+ * ======================================================================== *
+ * [XDNF] §2.3 and §6.3 store the KV cache in 8-bit integers alongside paging:
+ * quantisation changes the values the pools hold, paging only how the memory
+ * is organised; [IMPL] §3.4 lists int8 among the paged backend's dtypes.  The
+ * pages fix neither the code format nor the scales; here:
+ *   - the pools have the layouts above with 1-byte elements of kv_dtype
+ *     (PA_FP8_E4M3 or PA_INT8): key codes [num_blocks, num_kv_heads,
+ *     block_size, head_dim], value codes [num_blocks, num_kv_heads, head_dim,
+ *     block_size];
+ *   - one fp32 scale per pool: the key pool stands for decode(code) * k_scale,
+ *     the value pool for decode(code) * v_scale;
+ *   - a stored code is Q(x / scale), the quotient in fp32 (correctly rounded),
+ *     Q rounding to nearest with ties to even.  E4M3: finite values beyond
+ *     +-448 and +-inf saturate to +-448, NaN is stored as 0x7F, zeros keep
+ *     their sign.  INT8: saturate to [-127, 127], NaN is stored as 0.
+ * pa_copy_blocks copies 8-bit pools with dtype = kv_dtype. */
+
+/* The slot-mapping write of pa_reshape_and_cache into 8-bit pools: every
+ * element of key[i, h, :] (of type dtype: PA_F32, PA_F16 or PA_BF16) is
+ * quantised with k_scale and stored at key_cache[s / bs, h, s % bs, :]; value
+ * rows likewise with v_scale at value_cache[s / bs, h, :, s % bs].  kv_dtype
+ * selects the code format.  Slots, skipping, races and errors as in
+ * pa_reshape_and_cache; k_scale and v_scale must be finite and > 0
+ * (PA_ERR_INVALID_ARG).  Bit-exact (integer codes). */
+pa_status pa_reshape_and_cache_quant(const void* key, const void* value, void* key_cache, void* value_cache,
+                                     const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pa_dtype dtype,
+                                     pa_dtype kv_dtype, float k_scale, float v_scale, void* stream);
+
+/* Paged decode attention over 8-bit pools: pa_decode's definition with
+ * K_t = decode(key code) * k_scale and V_t = decode(value code) * v_scale.
+ * query and out are PA_F16 or PA_BF16 (dtype); the codes are widened exactly
+ * to dtype on the fly, the scales folded into the logit scale and the output.
+ * Path: the single pass when workspace is NULL; the split path (partials +
+ * merge, as pa_decode_split) when flags has PA_DECODE_SPLIT; otherwise the
+ * pa_decode_auto rule.  *path (may be NULL) receives 0 for the single pass,
+ * 1 for split.  Other arguments, sizes, flags and the handling of invalid
+ * device data as in pa_decode_split; k_scale and v_scale must be finite and
+ * > 0 (PA_ERR_INVALID_ARG). */
+pa_status pa_decode_quant(void* out, const void* query, const void* key_cache, const void* value_cache,
+                          const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
+                          int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                          int32_t max_context_len, float scale, float k_scale, float v_scale, pa_dtype dtype,
+                          pa_dtype kv_dtype, uint32_t flags, int32_t partition_size, void* workspace,
+                          size_t workspace_bytes, int32_t* path, void* stream);
 
 /* ======================================================================== *
  * Errors and version                                                        *

@@ -7,7 +7,7 @@ built (python paged_kv_cache_333_amd/build.py): there is no fallback.
 
 Names follow the C ABI in include/pa.h:
   pa_reshape_and_cache, pa_copy_blocks, pa_upload, pa_decode, pa_decode_split, pa_decode_auto,
-  pa_decode_append,
+  pa_decode_append, pa_reshape_and_cache_quant, pa_decode_quant,
   pa_decode_split_workspace_bytes, pa_lse_reduce, and the allocator verbs as
   methods of `Allocator` (pa_seq_create -> Allocator.seq_create, ...).
 """
@@ -54,9 +54,11 @@ PA_OK = 0
 STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_NO_FREE_BLOCKS", 3: "PA_ERR_UNKNOWN_SEQ",
           4: "PA_ERR_SEQ_EXISTS", 5: "PA_ERR_UNSUPPORTED", 6: "PA_ERR_BAD_TABLE",
           7: "PA_ERR_WORKSPACE_TOO_SMALL", 8: "PA_ERR_HIP"}
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3, 4
 PA_DECODE_CACHED_KV = 1
+PA_DECODE_SPLIT = 2
 DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
+KV_FORMATS = {"fp8_e4m3": PA_FP8_E4M3, "int8": PA_INT8}
 
 _i32, _u32, _i64, _f32, _vp, _sz = C.c_int32, C.c_uint32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
 _pi32, _pi64 = C.POINTER(C.c_int32), C.POINTER(C.c_int64)
@@ -97,6 +99,10 @@ _PROTOS = {
     "pa_decode_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _i32, _f32, _i32, _u32, _i32, _vp, _sz, _pi32, _vp]),
     "pa_lse_reduce": (_i32, [_vp, _vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_reshape_and_cache_quant": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                          _f32, _f32, _vp]),
+    "pa_decode_quant": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _i32, _f32, _f32, _f32, _i32, _i32, _u32, _i32, _vp, _sz, _pi32, _vp]),
     "pa_status_string": (C.c_char_p, [_i32]),
     "pa_last_error": (C.c_char_p, []),
     "pa_abi_version": (_i32, []),
@@ -175,11 +181,37 @@ def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, strea
 
 
 def pa_copy_blocks(key_cache, value_cache, pairs, stream=None, num_pairs=None):
-    """pairs int32 [P, 2] (src, dst) on the device; num_pairs may cover a prefix of it."""
+    """pairs int32 [P, 2] (src, dst) on the device; num_pairs may cover a prefix of it.
+    8-bit pools (one-byte elements) are copied as such."""
     NB, H_kv, bs, D = _pool_dims(key_cache, value_cache)
     P = pairs.shape[0] if num_pairs is None else num_pairs
+    code = PA_FP8_E4M3 if key_cache.element_size() == 1 else _dtype_code(key_cache)
     _check(lib.pa_copy_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(pairs), P, NB, H_kv, D, bs,
-                              _dtype_code(key_cache), _stream(stream)), "pa_copy_blocks")
+                              code, _stream(stream)), "pa_copy_blocks")
+
+
+def _kv_format(key_cache, kv_format):
+    """Code type of 8-bit pools: `kv_format` ("fp8_e4m3" or "int8"), else from the pool dtype
+    (torch.float8_e4m3fn or torch.int8); uint8 pools need kv_format."""
+    torch = _torch()
+    if key_cache.element_size() != 1:
+        raise TypeError(f"8-bit pools expected, got {key_cache.dtype}")
+    if kv_format is None:
+        kv_format = {torch.float8_e4m3fn: "fp8_e4m3", torch.int8: "int8"}.get(key_cache.dtype)
+        if kv_format is None:
+            raise TypeError("uint8 pools need kv_format='fp8_e4m3' or 'int8'")
+    return KV_FORMATS[kv_format]
+
+
+def pa_reshape_and_cache_quant(key, value, key_cache, value_cache, slot_mapping, k_scale: float, v_scale: float,
+                               kv_format=None, stream=None):
+    """The slot-mapping write into 8-bit pools: key, value [T, H_kv, D] (f32/f16/bf16) are
+    stored as codes of x / k_scale and x / v_scale."""
+    NB, H_kv, bs, D = _pool_dims(key_cache, value_cache)
+    _check(lib.pa_reshape_and_cache_quant(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                          _ptr(slot_mapping), slot_mapping.numel(), NB, H_kv, D, bs,
+                                          _dtype_code(key), _kv_format(key_cache, kv_format), k_scale, v_scale,
+                                          _stream(stream)), "pa_reshape_and_cache_quant")
 
 
 def pa_upload(dst, src, stream=None):
@@ -263,6 +295,26 @@ def pa_decode_append(out, query, key, value, slot_mapping, key_cache, value_cach
                                 _opt(seq_order), S, H, H_kv, D, bs, block_tables.shape[1], NB, max_context_len,
                                 scale, _dtype_code(query), PA_DECODE_CACHED_KV if cached_kv else 0, partition_size,
                                 _opt(workspace), nbytes, C.byref(path), _stream(stream)), "pa_decode_append")
+    return "split" if path.value == 1 else "single"
+
+
+def pa_decode_quant(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len: int,
+                    scale: float, k_scale: float, v_scale: float, kv_format=None, partition_size: int = 512,
+                    workspace=None, split: bool = False, stream=None, seq_order=None,
+                    cached_kv: bool = False) -> str:
+    """Decode over 8-bit pools (K = code * k_scale, V = code * v_scale) with f16/bf16 query and
+    output.  Single pass without a workspace; split with split=True; else the pa_decode_auto
+    rule.  Returns "single" or "split"."""
+    S, H, D = query.shape
+    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    flags = (PA_DECODE_CACHED_KV if cached_kv else 0) | (PA_DECODE_SPLIT if split else 0)
+    path = C.c_int32(-1)
+    _check(lib.pa_decode_quant(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+                               _ptr(context_lens), _opt(seq_order), S, H, H_kv, D, bs, block_tables.shape[1], NB,
+                               max_context_len, scale, k_scale, v_scale, _dtype_code(query),
+                               _kv_format(key_cache, kv_format), flags, partition_size, _opt(workspace), nbytes,
+                               C.byref(path), _stream(stream)), "pa_decode_quant")
     return "split" if path.value == 1 else "single"
 
 

@@ -24,7 +24,16 @@ bool debug_mode() {
   return on;
 }
 
-int elem_bytes(pa_dtype dt) { return dt == PA_F32 ? 4 : 2; }
+int elem_bytes(pa_dtype dt) { return dt == PA_F32 ? 4 : dt == PA_F16 || dt == PA_BF16 ? 2 : 1; }
+
+bool is_code_type(pa_dtype dt) { return dt == PA_FP8_E4M3 || dt == PA_INT8; }
+
+pa_status check_scales(float k_scale, float v_scale) {
+  // finite and positive (NaN fails the comparisons)
+  if (!(k_scale > 0.0f && k_scale <= 3.4028235e38f) || !(v_scale > 0.0f && v_scale <= 3.4028235e38f))
+    return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0");
+  return PA_OK;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -194,9 +203,11 @@ pa::DecodeArgs pack(void* out, const void* query, const void* key_cache, const v
                     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                     int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len, float scale,
                     pa_dtype dtype, uint32_t flags) {
-  return pa::DecodeArgs{out, query, key_cache, value_cache, block_tables, context_lens, seq_order, num_seqs,
-                        num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
-                        max_context_len, scale, dtype, flags};
+  pa::DecodeArgs a{out, query, key_cache, value_cache, block_tables, context_lens, seq_order, num_seqs,
+                   num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                   max_context_len, scale, dtype, flags};
+  a.kv_dtype = dtype;
+  return a;
 }
 
 }  // namespace
@@ -225,10 +236,34 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cac
                 st, "pa_reshape_and_cache");
 }
 
+pa_status pa_reshape_and_cache_quant(const void* key, const void* value, void* key_cache, void* value_cache,
+                                     const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pa_dtype dtype,
+                                     pa_dtype kv_dtype, float k_scale, float v_scale, void* stream) {
+  pa_status s = check_shape(dtype, head_dim, block_size);
+  if (s != PA_OK) return s;
+  if (!is_code_type(kv_dtype)) return fail(PA_ERR_UNSUPPORTED, "kv_dtype must be PA_FP8_E4M3 or PA_INT8");
+  if ((s = check_scales(k_scale, v_scale)) != PA_OK) return s;
+  if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID_ARG, "negative size or zero heads");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PA_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_mode() && (s = debug_check_slots(slot_mapping, num_tokens, num_blocks, block_size, st)) != PA_OK)
+    return s;
+  return finish(pa::launch_reshape_and_cache_quant(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                                                   num_blocks, num_kv_heads, head_dim, block_size, dtype, kv_dtype,
+                                                   k_scale, v_scale, st),
+                st, "pa_reshape_and_cache_quant");
+}
+
 pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs, int32_t num_pairs,
                          int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                          pa_dtype dtype, void* stream) {
-  pa_status s = check_shape(dtype, head_dim, block_size);
+  pa_status s = check_shape(is_code_type(dtype) ? PA_F16 : dtype, head_dim, block_size);
   if (s != PA_OK) return s;
   if (num_pairs < 0 || num_blocks < 0 || num_kv_heads <= 0)
     return fail(PA_ERR_INVALID_ARG, "negative size or zero heads");
@@ -387,6 +422,47 @@ pa_status pa_decode_append(void* out, const void* query, const void* key, const 
   }
   return finish(pa::launch_decode_append(a, key, value, slot_mapping, split ? &ws : nullptr, st), st,
                 "pa_decode_append");
+}
+
+pa_status pa_decode_quant(void* out, const void* query, const void* key_cache, const void* value_cache,
+                          const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
+                          int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                          int32_t max_context_len, float scale, float k_scale, float v_scale, pa_dtype dtype,
+                          pa_dtype kv_dtype, uint32_t flags, int32_t partition_size, void* workspace,
+                          size_t workspace_bytes, int32_t* path, void* stream) {
+  pa::DecodeArgs a = pack(out, query, key_cache, value_cache, block_tables, context_lens, seq_order, num_seqs,
+                          num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                          max_context_len, scale, dtype, flags);
+  a.kv_dtype = kv_dtype;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  pa_status s = check_decode_args(a);
+  if (s != PA_OK) return s;
+  if (dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "8-bit pools decode with PA_F16 or PA_BF16 queries");
+  if (!is_code_type(kv_dtype)) return fail(PA_ERR_UNSUPPORTED, "kv_dtype must be PA_FP8_E4M3 or PA_INT8");
+  if ((s = check_scales(k_scale, v_scale)) != PA_OK) return s;
+  if (flags & ~uint32_t(PA_DECODE_CACHED_KV | PA_DECODE_SPLIT))
+    return fail(PA_ERR_INVALID_ARG, "unknown flag bits");
+  a.flags = flags & PA_DECODE_CACHED_KV;
+  bool split = false;
+  if (flags & PA_DECODE_SPLIT) {
+    if (partition_size <= 0 || partition_size % block_size || partition_size > 4096)
+      return fail(PA_ERR_INVALID_ARG, "partition_size must be a multiple of block_size, at most 4096");
+    split = true;
+  } else {
+    split = choose_split(a, partition_size, workspace, workspace_bytes);
+  }
+  if (path) *path = split ? 1 : 0;
+  if (num_seqs == 0) return PA_OK;
+  pa::SplitLayout ws;
+  if (split && (s = make_layout(workspace, workspace_bytes, num_seqs, num_heads, head_dim, max_context_len,
+                                partition_size, &ws)) != PA_OK)
+    return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_mode() && (s = debug_check_tables(a, st)) != PA_OK) return s;
+  return finish(split ? pa::launch_decode_split(a, ws, st) : pa::launch_decode(a, st), st, "pa_decode_quant");
 }
 
 pa_status pa_lse_reduce(void* out, const void* workspace, size_t workspace_bytes, const int32_t* context_lens,

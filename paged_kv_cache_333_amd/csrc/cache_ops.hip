@@ -50,6 +50,52 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
+// The slot-mapping write into 8-bit pools (the quantised cache of the xdnf.cn
+// article, §2.3 and §6.3: KV values stored as 8-bit codes).  Same thread
+// layout as above: one thread per 16-byte chunk of one (token, KV head) input
+// row, EPL elements of the model type T.  Each element becomes the code of
+// x / scale (fp32 quotient, round to nearest even; to_code); the EPL key codes
+// are stored as one EPL-byte piece of the key row, the value codes one byte
+// each down column `offset` of the value tile.
+template <typename T, typename C>
+__global__ __launch_bounds__(256) void reshape_and_cache_quant_kernel(
+    const char* __restrict__ key, const char* __restrict__ value, uint8_t* __restrict__ key_cache,
+    uint8_t* __restrict__ value_cache, const int32_t* __restrict__ slot_mapping, int32_t num_tokens,
+    int64_t num_slots, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float k_scale,
+    float v_scale) {
+  constexpr int EPL = T::kEPL;
+  constexpr int NW = EPL / 4;  // 32-bit words of codes per chunk
+  const int32_t cpr = head_dim / EPL;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t per_token = static_cast<int64_t>(num_kv_heads) * cpr;
+  if (idx >= per_token * num_tokens) return;
+  const int64_t tok = idx / per_token;
+  const int64_t rem = idx - tok * per_token;
+  const int32_t h = static_cast<int32_t>(rem / cpr);
+  const int32_t c = static_cast<int32_t>(rem - static_cast<int64_t>(h) * cpr);
+  const int64_t slot = slot_mapping[tok];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / block_size;
+  const int64_t off = slot - blk * block_size;
+  const int64_t tile = blk * num_kv_heads + h;
+  const u32x4 kx = load16(key + idx * 16);
+  const u32x4 vx = load16(value + idx * 16);
+  uint32_t kw[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) kw[w] = 0;
+  uint8_t* vcol = value_cache + (tile * head_dim + static_cast<int64_t>(c) * EPL) * block_size + off;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    kw[e / 4] |= to_code(C{}, elem_to_float(T{}, kx, e) / k_scale) << (8 * (e % 4));
+    vcol[static_cast<int64_t>(e) * block_size] =
+        static_cast<uint8_t>(to_code(C{}, elem_to_float(T{}, vx, e) / v_scale));
+  }
+  uint32_t* krow = reinterpret_cast<uint32_t*>(key_cache + (tile * block_size + off) * head_dim +
+                                               static_cast<int64_t>(c) * EPL);
+#pragma unroll
+  for (int w = 0; w < NW; ++w) krow[w] = kw[w];
+}
+
 // Whole-block copy ("PagedAttention 实现细节" §3.3: the full contents of the
 // original block go to the new one).  grid.x = pair * groups_per_pair + group,
 // grid.y = pool (K or V); each workgroup copies a stretch of the block's
@@ -98,6 +144,34 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* ke
   else
     PA_RESHAPE(2);
 #undef PA_RESHAPE
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache_quant(const void* key, const void* value, void* key_cache, void* value_cache,
+                                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                          pa_dtype dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
+                                          hipStream_t stream) {
+  const int32_t elem = dtype == PA_F32 ? 4 : 2;
+  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * (head_dim * elem / 16);
+  if (total == 0) return hipSuccess;
+  const dim3 grid(static_cast<uint32_t>((total + 255) / 256));
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
+#define PA_QWRITE(T, C)                                                                                    \
+  hipLaunchKernelGGL((reshape_and_cache_quant_kernel<T, C>), grid, dim3(256), 0, stream,                   \
+                     static_cast<const char*>(key), static_cast<const char*>(value),                      \
+                     static_cast<uint8_t*>(key_cache), static_cast<uint8_t*>(value_cache), slot_mapping,    \
+                     num_tokens, num_slots, num_kv_heads, head_dim, block_size, k_scale, v_scale)
+  if (kv_dtype == PA_FP8_E4M3) {
+    if (dtype == PA_F32) PA_QWRITE(TF32, TE4M3);
+    else if (dtype == PA_F16) PA_QWRITE(TF16, TE4M3);
+    else PA_QWRITE(TBF16, TE4M3);
+  } else {
+    if (dtype == PA_F32) PA_QWRITE(TF32, TI8);
+    else if (dtype == PA_F16) PA_QWRITE(TF16, TI8);
+    else PA_QWRITE(TBF16, TI8);
+  }
+#undef PA_QWRITE
   return hipGetLastError();
 }
 

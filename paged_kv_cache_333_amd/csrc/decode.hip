@@ -10,12 +10,35 @@ namespace pa {
 
 namespace {
 
-hipError_t by_dtype(const LaunchOp& op, pa_dtype dt, bool split, bool append, int d, int bs, int gt) {
-  switch (dt) {
-    case PA_F32: return dispatch_f32(op, split, append, d, bs, gt);
-    case PA_F16: return dispatch_f16(op, split, append, d, bs, gt);
-    case PA_BF16: return dispatch_bf16(op, split, append, d, bs, gt);
+hipError_t by_dtype(const LaunchOp& op, pa_dtype dt, pa_dtype kv, bool split, bool append, int d, int bs, int gt) {
+  if (kv == dt) {
+    switch (dt) {
+      case PA_F32: return dispatch_f32(op, split, append, d, bs, gt);
+      case PA_F16: return dispatch_f16(op, split, append, d, bs, gt);
+      case PA_BF16: return dispatch_bf16(op, split, append, d, bs, gt);
+      default: return hipErrorInvalidValue;
+    }
   }
+  if (kv == PA_FP8_E4M3 && dt == PA_F16) return dispatch_e4m3_f16(op, split, append, d, bs, gt);
+  if (kv == PA_FP8_E4M3 && dt == PA_BF16) return dispatch_e4m3_bf16(op, split, append, d, bs, gt);
+  if (kv == PA_INT8 && dt == PA_F16) return dispatch_i8_f16(op, split, append, d, bs, gt);
+  if (kv == PA_INT8 && dt == PA_BF16) return dispatch_i8_bf16(op, split, append, d, bs, gt);
+  return hipErrorInvalidValue;
+}
+
+hipError_t occupancy_by_dtype(int* per_cu, pa_dtype dt, pa_dtype kv, int d, int bs, int gt) {
+  if (kv == dt) {
+    switch (dt) {
+      case PA_F32: return occupancy_f32(per_cu, d, bs, gt);
+      case PA_F16: return occupancy_f16(per_cu, d, bs, gt);
+      case PA_BF16: return occupancy_bf16(per_cu, d, bs, gt);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (kv == PA_FP8_E4M3 && dt == PA_F16) return occupancy_e4m3_f16(per_cu, d, bs, gt);
+  if (kv == PA_FP8_E4M3 && dt == PA_BF16) return occupancy_e4m3_bf16(per_cu, d, bs, gt);
+  if (kv == PA_INT8 && dt == PA_F16) return occupancy_i8_f16(per_cu, d, bs, gt);
+  if (kv == PA_INT8 && dt == PA_BF16) return occupancy_i8_bf16(per_cu, d, bs, gt);
   return hipErrorInvalidValue;
 }
 
@@ -42,7 +65,10 @@ DecodeParams make_params(const DecodeArgs& x) {
   p.num_blocks = x.num_blocks;
   const int64_t cap = static_cast<int64_t>(x.max_blocks_per_seq) * x.block_size;
   p.len_limit = static_cast<int32_t>(cap < x.max_context_len ? cap : x.max_context_len);
-  p.scale_log2 = x.scale * 1.4426950408889634f;
+  // 8-bit pools: the key scale folds into the logit scale, the value scale
+  // into the output (both 1 for model-type pools)
+  p.scale_log2 = x.scale * x.k_scale * 1.4426950408889634f;
+  p.v_scale = x.v_scale;
   return p;
 }
 
@@ -51,8 +77,8 @@ DecodeParams make_params(const DecodeArgs& x) {
 hipError_t launch_decode(const DecodeArgs& x, hipStream_t stream) {
   DecodeParams p = make_params(x);
   const int gt = group_tile(x.num_heads / x.num_kv_heads);
-  return by_dtype(LaunchOp{p, x.num_seqs, (x.flags & PA_DECODE_CACHED_KV) != 0, stream}, x.dtype, false, false,
-                  x.head_dim, x.block_size, gt);
+  return by_dtype(LaunchOp{p, x.num_seqs, (x.flags & PA_DECODE_CACHED_KV) != 0, stream}, x.dtype, x.kv_dtype,
+                  false, false, x.head_dim, x.block_size, gt);
 }
 
 hipError_t launch_decode_split(const DecodeArgs& x, const SplitLayout& ws, hipStream_t stream) {
@@ -63,8 +89,8 @@ hipError_t launch_decode_split(const DecodeArgs& x, const SplitLayout& ws, hipSt
   p.part_size = ws.partition_size;
   p.num_parts = ws.num_parts;
   const int gt = group_tile(x.num_heads / x.num_kv_heads);
-  hipError_t e = by_dtype(LaunchOp{p, x.num_seqs, (x.flags & PA_DECODE_CACHED_KV) != 0, stream}, x.dtype, true,
-                           false, x.head_dim, x.block_size, gt);
+  hipError_t e = by_dtype(LaunchOp{p, x.num_seqs, (x.flags & PA_DECODE_CACHED_KV) != 0, stream}, x.dtype,
+                           x.kv_dtype, true, false, x.head_dim, x.block_size, gt);
   if (e != hipSuccess) return e;
   return launch_lse_reduce(x.out, ws, x.context_lens, x.seq_order, x.num_seqs, x.num_heads, x.head_dim,
                            p.len_limit, x.dtype, stream);
@@ -96,7 +122,7 @@ hipError_t launch_decode_append(const DecodeArgs& x, const void* new_k, const vo
     p.num_parts = ws->num_parts;
   }
   hipError_t e = by_dtype(LaunchOp{p, x.num_seqs, (x.flags & PA_DECODE_CACHED_KV) != 0, stream}, x.dtype,
-                          ws != nullptr, true, x.head_dim, x.block_size, gt);
+                          x.kv_dtype, ws != nullptr, true, x.head_dim, x.block_size, gt);
   if (e != hipSuccess || !ws) return e;
   return launch_lse_reduce(x.out, *ws, x.context_lens, x.seq_order, x.num_seqs, x.num_heads, x.head_dim,
                            p.len_limit, x.dtype, stream);
@@ -106,9 +132,7 @@ hipError_t single_pass_shape(const DecodeArgs& x, int64_t* workgroups, int64_t* 
   const int gt = group_tile(x.num_heads / x.num_kv_heads);
   *workgroups = static_cast<int64_t>(x.num_seqs) * (x.num_heads / gt);
   int per_cu = 0, dev = 0, cus = 0;
-  hipError_t e = x.dtype == PA_F32   ? occupancy_f32(&per_cu, x.head_dim, x.block_size, gt)
-                 : x.dtype == PA_F16 ? occupancy_f16(&per_cu, x.head_dim, x.block_size, gt)
-                                     : occupancy_bf16(&per_cu, x.head_dim, x.block_size, gt);
+  hipError_t e = occupancy_by_dtype(&per_cu, x.dtype, x.kv_dtype, x.head_dim, x.block_size, gt);
   if (e == hipSuccess) e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   *resident = static_cast<int64_t>(per_cu) * cus;

@@ -80,7 +80,8 @@ struct DecodeParams {
   int32_t len_limit;   // largest valid context length
   int32_t part_size;   // split only
   int32_t num_parts;   // split only
-  float scale_log2;    // scale * log2(e)
+  float scale_log2;    // scale * k_scale * log2(e)
+  float v_scale;       // multiplies the output (8-bit value pools; 1 otherwise)
   // fused slot-mapping write (pa_decode_append): new K/V rows [num_seqs, H_kv, D]
   // and the slot of each sequence's new token
   const char* new_k;
@@ -161,18 +162,31 @@ struct AppendRow {
   }
 };
 
-template <typename T, int D, int BS, int GT, bool SPLIT, bool CACHED, bool APPEND>
+// T is the query/output type and the type the matrix cores compute in; S is
+// the pools' storage type: T itself, or an 8-bit code type (TE4M3, TI8) whose
+// chunks are widened exactly to T in registers after the load.
+template <typename T, typename S, int D, int BS, int GT, bool SPLIT, bool CACHED, bool APPEND>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void decode_kernel(DecodeParams a) {
-  constexpr int EPL = T::kEPL;       // elements per 16-byte chunk
+  constexpr bool Q8 = S::kBytes == 1;  // 8-bit codes
+  constexpr int EPL = T::kEPL;       // compute elements per 16-byte chunk
   constexpr int E = T::kBytes;
-  constexpr int KV = D / EPL / 4;    // q.K products per 16-token tile (chunks 4v + q of a row)
-  constexpr int NT = EPL / 4;        // 16-token q.K tiles per step
+  constexpr int SE = S::kEPL;        // stored elements per 16-byte load
+  constexpr int SB = S::kBytes;
+  constexpr int KV = D / EPL / 4;    // q.K products per 16-token tile
+  constexpr int KL = D / SE / 4;     // key loads per 16-token tile and lane (chunks 4l + q of a row)
+  constexpr int NT = SE / 4;         // 16-token q.K tiles per step
+  constexpr int TPL = SE;            // tokens per lane in P.V (= 4 NT)
   constexpr int TS = 16 * NT;        // tokens per step
-  constexpr int NV = D / 16;         // P.V products per step (16 output dims each)
+  constexpr int NV = D / 16;         // value loads per step, 16 output dims each
+  constexpr int PV = TPL / EPL;      // P.V products per 16 output dims (2 for 8-bit codes)
   constexpr int NBS = TS > BS ? TS / BS : 1;  // blocks touched by one step
   constexpr bool SPLIT_P = std::is_same<T, TBF16>::value;
   constexpr float kNegInf = -__builtin_huge_valf();
   static_assert(GT >= 1 && GT <= 16, "heads per workgroup");
+  static_assert(Q8 ? T::kBytes == 2 : std::is_same<T, S>::value, "8-bit pools decode in fp16/bf16");
+  static_assert(!(Q8 && APPEND), "the fused write stores model-type rows");
+  static_assert(NBS <= 4 && KL * SE * 4 == D && KV * EPL * 4 == D, "step shape");
+  static_assert(TPL % BS == 0 || BS % TPL == 0, "a lane's tokens never straddle a block boundary");
 
   const int lane = threadIdx.x & 63;
   // wave-uniform: keeps the step loop and the table lookups in scalar registers
@@ -215,12 +229,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int b_end = (t_end + BS - 1) / BS;
   const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.max_blocks;
 
-  // Q operand of q.K: lane (q, n) holds head h0 + n % GT, chunks 4v + q.
+  // Q operand of q.K: lane (q, n) holds head h0 + n % GT, the dims its key
+  // chunks hold: chunk 4v + q; with 8-bit keys, key load l = v / 2 holds dims
+  // 16 (4l + q) .. + 15 and widens into chunks 2 (4l + q) and 2 (4l + q) + 1.
   u32x4 qv[KV];
   {
     const char* qrow = a.q + (static_cast<int64_t>(s) * a.num_heads + h0 + n % GT) * D * E;
 #pragma unroll
-    for (int v = 0; v < KV; ++v) qv[v] = load16(qrow + (4 * v + q) * 16);
+    for (int v = 0; v < KV; ++v) {
+      const int c = Q8 ? 2 * (4 * (v >> 1) + q) + (v & 1) : 4 * v + q;
+      qv[v] = load16(qrow + c * 16);
+    }
   }
 
   // Online-softmax state of this lane's head (n % GT), and the P.V
@@ -295,29 +314,45 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
 #pragma unroll
     for (int i = 1; i < NBS; ++i)
       if (ph[i] < 0) ph[i] = ph[0];
+    // Physical block of step block bi (lane-dependent), by selects on the bits
+    // of bi (a compare chain would be turned into an indexed load from a
+    // stack copy of ph).
+    auto pick = [&](int bi) -> int64_t {
+      if constexpr (NBS == 1) {
+        return ph[0];
+      } else if constexpr (NBS == 2) {
+        return bi ? ph[1] : ph[0];
+      } else {
+        const int32_t lo = bi & 1 ? ph[1] : ph[0];
+        const int32_t hi = bi & 1 ? ph[3] : ph[2];
+        return bi & 2 ? hi : lo;
+      }
+    };
 
     // K rows: in tile tau, lane (q, n) supplies row n = token
-    // EPL (n / 4) + 4 tau + n % 4 of the step, chunks 4v + q.
-    u32x4 kr[NT][KV];
+    // TPL (n / 4) + 4 tau + n % 4 of the step, chunks 4l + q.  The 4 tau +
+    // n % 4 part stays below TPL, and TPL and BS divide one another (off0 is
+    // nonzero only when NBS == 1), so the row's block does not depend on tau.
+    const int bik = NBS == 1 ? 0 : (off0 + TPL * (n >> 2)) / BS;
+    const int64_t kblk = pick(bik);
+    u32x4 kr[NT][KL];
 #pragma unroll
     for (int tau = 0; tau < NT; ++tau) {
-      const int x = off0 + EPL * (n >> 2) + 4 * tau + (n & 3);
-      const int bi = NBS == 1 ? 0 : x / BS;
-      const int64_t phys = bi ? ph[NBS - 1] : ph[0];
-      const char* kp = a.kc + (((phys * hkv + kvh) * BS + (x - bi * BS)) * D) * E + q * 16;
+      const int x = off0 + TPL * (n >> 2) + 4 * tau + (n & 3);
+      const char* kp = a.kc + (((kblk * hkv + kvh) * BS + (x - bik * BS)) * D) * SB + q * 16;
 #pragma unroll
-      for (int v = 0; v < KV; ++v) kr[tau][v] = CACHED ? load16(kp + v * 64) : load16_stream(kp + v * 64);
+      for (int l = 0; l < KL; ++l) kr[tau][l] = CACHED ? load16(kp + l * 64) : load16_stream(kp + l * 64);
     }
-    // V columns: lane (q, n) supplies dim 16v + n of tokens EPL q .. EPL q + EPL-1.
+    // V columns: lane (q, n) supplies dim 16v + n of tokens TPL q .. TPL q + TPL-1.
     u32x4 vr[NV];
     {
-      const int x = off0 + EPL * q;
+      const int x = off0 + TPL * q;
       const int bi = NBS == 1 ? 0 : x / BS;
-      const int64_t phys = bi ? ph[NBS - 1] : ph[0];
-      const char* vp = a.vc + (((phys * hkv + kvh) * D + n) * BS + (x - bi * BS)) * E;
+      const int64_t phys = pick(bi);  // bi < NBS: TPL q < TS
+      const char* vp = a.vc + (((phys * hkv + kvh) * D + n) * BS + (x - bi * BS)) * SB;
 #pragma unroll
       for (int v = 0; v < NV; ++v)
-        vr[v] = CACHED ? load16(vp + v * 16 * BS * E) : load16_stream(vp + v * 16 * BS * E);
+        vr[v] = CACHED ? load16(vp + v * 16 * BS * SB) : load16_stream(vp + v * 16 * BS * SB);
     }
     // All of the step's loads are issued before any of them is consumed.
     __builtin_amdgcn_sched_barrier(0);
@@ -329,19 +364,29 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
 #pragma unroll
     for (int tau = 0; tau < NT; ++tau) {
       c[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (Q8) {
 #pragma unroll
-      for (int v = 0; v < KV; ++v) c[tau] = mma(T{}, kr[tau][v], qv[v], c[tau]);
+        for (int l = 0; l < KL; ++l) {
+          u32x4 lo, hi;
+          widen(S{}, T{}, kr[tau][l], lo, hi);
+          c[tau] = mma(T{}, lo, qv[2 * l], c[tau]);
+          c[tau] = mma(T{}, hi, qv[2 * l + 1], c[tau]);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < KV; ++v) c[tau] = mma(T{}, kr[tau][v], qv[v], c[tau]);
+      }
     }
-    // c[tau][j]: logit of token t0 + EPL q + 4 tau + j for head n % GT
+    // c[tau][j]: logit of token t0 + TPL q + 4 tau + j for head n % GT
     const bool tail = t0 + TS > t_end;
-    float z[EPL];
+    float z[TPL];
     float mx = kNegInf;
 #pragma unroll
     for (int tau = 0; tau < NT; ++tau)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float v = c[tau][j] * a.scale_log2;
-        const bool ok = !tail || t0 + EPL * q + 4 * tau + j < t_end;
+        const bool ok = !tail || t0 + TPL * q + 4 * tau + j < t_end;
         z[4 * tau + j] = ok ? v : kNegInf;
         mx = fmaxf(mx, z[4 * tau + j]);
       }
@@ -351,10 +396,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     const float m_use = m_new == kNegInf ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
     m_run = m_new;
-    float p[EPL];
+    float p[TPL];
     float ps = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
+    for (int e = 0; e < TPL; ++e) {
       p[e] = fast_exp2(z[e] - m_use);
       ps += p[e];
     }
@@ -377,17 +422,27 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[v][j] *= al[j];
     }
-    u32x4 phi, plo;
-    pack_p(T{}, p, phi, plo);
+    // P in chunks of the compute type: chunk u holds tokens TPL q + EPL u ..
+    u32x4 phi[PV], plo[PV];
+#pragma unroll
+    for (int u = 0; u < PV; ++u) pack_p(T{}, p + EPL * u, phi[u], plo[u]);
     if (tail) {
-      const u32x4 keep = keep_mask(T{}, t_end - (t0 + EPL * q));
+      const u32x4 keep = keep_mask(S{}, t_end - (t0 + TPL * q));
 #pragma unroll
       for (int v = 0; v < NV; ++v) vr[v] &= keep;
     }
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      acc[v] = mma(T{}, phi, vr[v], acc[v]);
-      if constexpr (SPLIT_P) acc[v] = mma(T{}, plo, vr[v], acc[v]);
+      u32x4 vc[PV];
+      if constexpr (Q8)
+        widen(S{}, T{}, vr[v], vc[0], vc[PV - 1]);
+      else
+        vc[0] = vr[v];
+#pragma unroll
+      for (int u = 0; u < PV; ++u) {
+        acc[v] = mma(T{}, phi[u], vc[u], acc[v]);
+        if constexpr (SPLIT_P) acc[v] = mma(T{}, plo[u], vc[u], acc[v]);
+      }
     }
   }
 
@@ -421,7 +476,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       if (g < GT) {
         float* o = a.ws_o + ((sh0 + g) * a.num_parts + part) * D + n;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) o[16 * v] = bad ? qnan : acc[v][j] / lg[j];
+        for (int v = 0; v < NV; ++v) o[16 * v] = bad ? qnan : acc[v][j] / lg[j] * a.v_scale;
       }
     }
     if (q == 0 && n < GT) {
@@ -464,7 +519,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       A = __builtin_fmaf(sm_acc[w][g][d], wt, A);
     }
     const int64_t sh = static_cast<int64_t>(s) * a.num_heads + h0 + g;
-    const float val = any_bad || bad_len ? __builtin_nanf("") : (L > 0.f ? A / L : 0.f);
+    const float val = any_bad || bad_len ? __builtin_nanf("") : (L > 0.f ? A / L * a.v_scale : 0.f);
     store_elem(T{}, a.out, sh * D + d, val);
   }
 }
@@ -544,16 +599,16 @@ struct LaunchOp {
   int32_t num_seqs;
   bool cached;
   hipStream_t stream;
-  template <typename T, int D, int BS, int GT, bool SPLIT, bool APPEND>
+  template <typename T, typename S, int D, int BS, int GT, bool SPLIT, bool APPEND>
   hipError_t run() const {
     const uint32_t gx = static_cast<uint32_t>(num_seqs) * (p.num_heads / GT);
     const uint32_t gy = SPLIT ? static_cast<uint32_t>((p.num_parts + kWaves - 1) / kWaves) : 1u;
     if (cached)
-      hipLaunchKernelGGL((decode_kernel<T, D, BS, GT, SPLIT, true, APPEND>), dim3(gx, gy), dim3(kWaves * 64), 0,
-                         stream, p);
+      hipLaunchKernelGGL((decode_kernel<T, S, D, BS, GT, SPLIT, true, APPEND>), dim3(gx, gy), dim3(kWaves * 64),
+                         0, stream, p);
     else
-      hipLaunchKernelGGL((decode_kernel<T, D, BS, GT, SPLIT, false, APPEND>), dim3(gx, gy), dim3(kWaves * 64), 0,
-                         stream, p);
+      hipLaunchKernelGGL((decode_kernel<T, S, D, BS, GT, SPLIT, false, APPEND>), dim3(gx, gy),
+                         dim3(kWaves * 64), 0, stream, p);
     return hipGetLastError();
   }
 };
@@ -561,51 +616,66 @@ struct LaunchOp {
 // Workgroups of the instance that one compute unit holds at once.
 struct OccupancyOp {
   int* per_cu;
-  template <typename T, int D, int BS, int GT, bool SPLIT, bool APPEND>
+  template <typename T, typename S, int D, int BS, int GT, bool SPLIT, bool APPEND>
   hipError_t run() const {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, decode_kernel<T, D, BS, GT, SPLIT, false, APPEND>,
-                                                        kWaves * 64, 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        per_cu, decode_kernel<T, S, D, BS, GT, SPLIT, false, APPEND>, kWaves * 64, 0);
   }
 };
 
-template <typename T, int D, int BS, bool SPLIT, bool APPEND, typename Op>
+template <typename T, typename S, int D, int BS, bool SPLIT, bool APPEND, typename Op>
 hipError_t by_group(const Op& op, int gt) {
   switch (gt) {
-    case 1: return op.template run<T, D, BS, 1, SPLIT, APPEND>();
-    case 2: return op.template run<T, D, BS, 2, SPLIT, APPEND>();
-    case 4: return op.template run<T, D, BS, 4, SPLIT, APPEND>();
-    case 8: return op.template run<T, D, BS, 8, SPLIT, APPEND>();
-    case 16: return op.template run<T, D, BS, 16, SPLIT, APPEND>();
+    case 1: return op.template run<T, S, D, BS, 1, SPLIT, APPEND>();
+    case 2: return op.template run<T, S, D, BS, 2, SPLIT, APPEND>();
+    case 4: return op.template run<T, S, D, BS, 4, SPLIT, APPEND>();
+    case 8: return op.template run<T, S, D, BS, 8, SPLIT, APPEND>();
+    case 16: return op.template run<T, S, D, BS, 16, SPLIT, APPEND>();
   }
   return hipErrorInvalidValue;
 }
 
-template <typename T, bool SPLIT, bool APPEND, typename Op>
+template <typename T, typename S, bool SPLIT, bool APPEND, typename Op>
 hipError_t by_shape(const Op& op, int d, int bs, int gt) {
-  if (d == 64 && bs == 16) return by_group<T, 64, 16, SPLIT, APPEND>(op, gt);
-  if (d == 64 && bs == 32) return by_group<T, 64, 32, SPLIT, APPEND>(op, gt);
-  if (d == 128 && bs == 16) return by_group<T, 128, 16, SPLIT, APPEND>(op, gt);
-  if (d == 128 && bs == 32) return by_group<T, 128, 32, SPLIT, APPEND>(op, gt);
+  if (d == 64 && bs == 16) return by_group<T, S, 64, 16, SPLIT, APPEND>(op, gt);
+  if (d == 64 && bs == 32) return by_group<T, S, 64, 32, SPLIT, APPEND>(op, gt);
+  if (d == 128 && bs == 16) return by_group<T, S, 128, 16, SPLIT, APPEND>(op, gt);
+  if (d == 128 && bs == 32) return by_group<T, S, 128, 32, SPLIT, APPEND>(op, gt);
   return hipErrorInvalidValue;
 }
 
-// One translation unit per element type instantiates its kernels (they build
-// in parallel): decode_f32.hip, decode_f16.hip, decode_bf16.hip.
+// One translation unit per (query type, storage type) instantiates its
+// kernels (they build in parallel): decode_f32.hip, decode_f16.hip,
+// decode_bf16.hip, and decode_{e4m3,i8}_{f16,bf16}.hip for 8-bit pools.
 hipError_t dispatch_f32(const LaunchOp& op, bool split, bool append, int d, int bs, int gt);
 hipError_t dispatch_f16(const LaunchOp& op, bool split, bool append, int d, int bs, int gt);
 hipError_t dispatch_bf16(const LaunchOp& op, bool split, bool append, int d, int bs, int gt);
+hipError_t dispatch_e4m3_f16(const LaunchOp& op, bool split, bool append, int d, int bs, int gt);
+hipError_t dispatch_e4m3_bf16(const LaunchOp& op, bool split, bool append, int d, int bs, int gt);
+hipError_t dispatch_i8_f16(const LaunchOp& op, bool split, bool append, int d, int bs, int gt);
+hipError_t dispatch_i8_bf16(const LaunchOp& op, bool split, bool append, int d, int bs, int gt);
 hipError_t occupancy_f32(int* per_cu, int d, int bs, int gt);
 hipError_t occupancy_f16(int* per_cu, int d, int bs, int gt);
 hipError_t occupancy_bf16(int* per_cu, int d, int bs, int gt);
+hipError_t occupancy_e4m3_f16(int* per_cu, int d, int bs, int gt);
+hipError_t occupancy_e4m3_bf16(int* per_cu, int d, int bs, int gt);
+hipError_t occupancy_i8_f16(int* per_cu, int d, int bs, int gt);
+hipError_t occupancy_i8_bf16(int* per_cu, int d, int bs, int gt);
 
-template <typename T>
+template <typename T, typename S = T>
 hipError_t dispatch_t(const LaunchOp& op, bool split, bool append, int d, int bs, int gt) {
-  if (split) return append ? by_shape<T, true, true>(op, d, bs, gt) : by_shape<T, true, false>(op, d, bs, gt);
-  return append ? by_shape<T, false, true>(op, d, bs, gt) : by_shape<T, false, false>(op, d, bs, gt);
+  if constexpr (S::kBytes == 1) {  // no fused write into 8-bit pools
+    if (append) return hipErrorInvalidValue;
+    return split ? by_shape<T, S, true, false>(op, d, bs, gt) : by_shape<T, S, false, false>(op, d, bs, gt);
+  } else {
+    if (split)
+      return append ? by_shape<T, S, true, true>(op, d, bs, gt) : by_shape<T, S, true, false>(op, d, bs, gt);
+    return append ? by_shape<T, S, false, true>(op, d, bs, gt) : by_shape<T, S, false, false>(op, d, bs, gt);
+  }
 }
-template <typename T>
+template <typename T, typename S = T>
 hipError_t occupancy_t(int* per_cu, int d, int bs, int gt) {
-  return by_shape<T, false, false>(OccupancyOp{per_cu}, d, bs, gt);
+  return by_shape<T, S, false, false>(OccupancyOp{per_cu}, d, bs, gt);
 }
 
 

@@ -23,6 +23,17 @@ struct TBF16 {
   static constexpr int kBytes = 2;
   static constexpr int kEPL = 8;
 };
+// 8-bit KV codes (the quantised cache): OCP FP8 E4M3 and two's-complement
+// int8, 16 codes per chunk.  They are storage types only: decode widens them
+// exactly to fp16/bf16 in registers.
+struct TE4M3 {
+  static constexpr int kBytes = 1;
+  static constexpr int kEPL = 16;
+};
+struct TI8 {
+  static constexpr int kBytes = 1;
+  static constexpr int kEPL = 16;
+};
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -127,6 +138,113 @@ __device__ __forceinline__ u32x4 keep_mask_16(int keep) {
 }
 __device__ __forceinline__ u32x4 keep_mask(TF16, int keep) { return keep_mask_16(keep); }
 __device__ __forceinline__ u32x4 keep_mask(TBF16, int keep) { return keep_mask_16(keep); }
+
+// Bit mask keeping the first `keep` codes of a chunk of 8-bit codes.
+__device__ __forceinline__ u32x4 keep_mask_8(int keep) {
+  u32x4 m;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int k = keep - 4 * w;
+    m[w] = k >= 4 ? ~0u : k <= 0 ? 0u : (1u << (8 * k)) - 1u;
+  }
+  return m;
+}
+__device__ __forceinline__ u32x4 keep_mask(TE4M3, int keep) { return keep_mask_8(keep); }
+__device__ __forceinline__ u32x4 keep_mask(TI8, int keep) { return keep_mask_8(keep); }
+
+// ---------------------------------------------------------------------------
+// 8-bit codes -> fp16/bf16, exactly.  widen() turns one chunk of 16 codes into
+// two chunks of the compute type: lo holds codes 0..7, hi codes 8..15, in
+// order.  Every E4M3 value (subnormals and NaN included) and every int8 value
+// is exact in both fp16 and bf16.
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Codes 2*HI and 2*HI + 1 of word w.  The gfx950 conversion scales by the
+// power of two of its scale operand; 1.0 leaves the value as it is.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pair(TF16, uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pair(TBF16, uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// int8: for fp16, byte b is biased to u = b + 128 and placed in the mantissa
+// of 1024 (f16 bits 0x6400 | u), then 1152 is subtracted: u - 128 = b, exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t i8_pair(TF16, uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  // bytes (u0, 0x64, u1, 0x64) for HI = false, (u2, 0x64, u3, 0x64) for HI = true
+  const uint32_t t = __builtin_amdgcn_perm(0x64646464u, u, HI ? 0x04030402u : 0x04010400u);
+  const f16x2 v = __builtin_bit_cast(f16x2, t) - f16x2{static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+template <bool HI>
+__device__ __forceinline__ uint32_t i8_pair(TBF16, uint32_t w) {
+  const float a = static_cast<float>(static_cast<int32_t>(w << (HI ? 8 : 24)) >> 24);  // byte 2 HI, signed
+  const float b = static_cast<float>(static_cast<int32_t>(w << (HI ? 0 : 16)) >> 24);  // byte 2 HI + 1
+  const bf16x2 v{static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <typename T>
+__device__ __forceinline__ void widen(TE4M3, T, u32x4 raw, u32x4& lo, u32x4& hi) {
+  lo = u32x4{e4m3_pair<false>(T{}, raw[0]), e4m3_pair<true>(T{}, raw[0]), e4m3_pair<false>(T{}, raw[1]),
+             e4m3_pair<true>(T{}, raw[1])};
+  hi = u32x4{e4m3_pair<false>(T{}, raw[2]), e4m3_pair<true>(T{}, raw[2]), e4m3_pair<false>(T{}, raw[3]),
+             e4m3_pair<true>(T{}, raw[3])};
+}
+template <typename T>
+__device__ __forceinline__ void widen(TI8, T, u32x4 raw, u32x4& lo, u32x4& hi) {
+  lo = u32x4{i8_pair<false>(T{}, raw[0]), i8_pair<true>(T{}, raw[0]), i8_pair<false>(T{}, raw[1]),
+             i8_pair<true>(T{}, raw[1])};
+  hi = u32x4{i8_pair<false>(T{}, raw[2]), i8_pair<true>(T{}, raw[2]), i8_pair<false>(T{}, raw[3]),
+             i8_pair<true>(T{}, raw[3])};
+}
+
+// ---------------------------------------------------------------------------
+// fp32 -> 8-bit code, round to nearest even (the quantising write).
+
+// E4M3: NaN -> 0x7F; |y| >= 448 (inf included) saturates to 448 (0x7E); the
+// sign bit is kept, zeros included.  Below 2^-6 the codes are multiples of
+// 2^-9 (subnormals; 8 * 2^-9 is the smallest normal, code 0x08, so the two
+// ranges join).  Above, the fp32 mantissa is rounded to 3 bits on its bit
+// pattern and the exponent rebiased from 127 to 7.
+__device__ __forceinline__ uint32_t to_code(TE4M3, float y) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t ua = u & 0x7fffffffu;
+  if (ua > 0x7f800000u) return 0x7fu;
+  const float a = __builtin_bit_cast(float, ua);
+  if (a >= 448.0f) return sign | 0x7eu;
+  uint32_t mag;
+  if (a < 0x1p-6f) {
+    mag = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
+  } else {
+    const uint32_t r = ua + 0x7ffffu + ((ua >> 20) & 1u);
+    mag = (r >> 20) - ((127u - 7u) << 3);
+  }
+  return sign | mag;
+}
+// int8: saturate to [-127, 127]; NaN -> 0.
+__device__ __forceinline__ uint32_t to_code(TI8, float y) {
+  if (y != y) return 0u;
+  const float r = fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f);
+  return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xffu;
+}
+
+// Storage element i of a chunk of a model type, as fp32 (exact).
+__device__ __forceinline__ float elem_to_float(TF32, u32x4 c, int i) { return __builtin_bit_cast(float, word(c, i)); }
+__device__ __forceinline__ float elem_to_float(TF16, u32x4 c, int i) {
+  const uint32_t w = word(c, i >> 1);
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(i & 1 ? w >> 16 : w)));
+}
+__device__ __forceinline__ float elem_to_float(TBF16, u32x4 c, int i) {
+  const uint32_t w = word(c, i >> 1);
+  return __builtin_bit_cast(float, i & 1 ? w & 0xffff0000u : w << 16);
+}
 
 // Value of lane J of this lane's quad (DPP quad_perm [J, J, J, J]).
 template <int J>

@@ -20,8 +20,12 @@ struct DecodeArgs {
   int32_t num_seqs, num_heads, num_kv_heads, head_dim, block_size;
   int32_t max_blocks_per_seq, num_blocks, max_context_len;
   float scale;
-  pa_dtype dtype;
+  pa_dtype dtype;  // query / output type
   uint32_t flags;  // PA_DECODE_* bits
+  // pools: kv_dtype == dtype, or an 8-bit code type with per-pool scales
+  pa_dtype kv_dtype = PA_F32;
+  float k_scale = 1.0f;
+  float v_scale = 1.0f;
 };
 
 // The three fp32 arrays of the split workspace (see pa_decode_split_workspace_bytes).
@@ -37,6 +41,12 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* ke
                                     void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
                                     int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                                     int32_t elem_bytes, int32_t block_size, hipStream_t stream);
+// The quantising slot-mapping write: rows of `dtype` -> codes of `kv_dtype`.
+hipError_t launch_reshape_and_cache_quant(const void* key, const void* value, void* key_cache, void* value_cache,
+                                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                          pa_dtype dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
+                                          hipStream_t stream);
 hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
                               int32_t num_pairs, int32_t num_blocks, int64_t block_bytes,
                               hipStream_t stream);

@@ -16,13 +16,21 @@ dimension 128, blocks of 16 or 32 tokens, contexts up to 2048 and beyond):
                    pool 22645, split into 512-token partitions
   5 cow-fp16       fp16, 32 groups x 5 branches, 32/32 heads, D 128, bs 16, a 2048-token shared
                    prefix plus a per-branch suffix U{0..256}
+  6 llama7b-fp8kv  workload 2's shapes (own draw of lengths and free order) with 8-bit FP8 E4M3
+                   pools, fp16 query/output, k_scale 0.0165, v_scale 0.0145
+  7 gqa-bf16-int8kv  workload 3's shapes (own draw) with int8 pools, bf16 query/output,
+                   k_scale 0.031, v_scale 0.029
 
 Draw order for workload k (numpy PCG64, seed 1000+k): context lengths, then the
 pool's initial free order (a permutation), then (workload 5) the suffix
 lengths.  Tensor contents (pools, q, new K/V) come from `normal_host` (numpy,
 small cases) or `normal_device` (torch's device generator, full-size pools),
 each with its own derived seed.  Normals are drawn in float32 and rounded to
-nearest-even into fp16/bf16.
+nearest-even into fp16/bf16.  8-bit pools hold codes drawn the same way at a
+code scale of CODE_SIGMA (N(0, CODE_SIGMA^2) in code units) and rounded onto
+the code grid: torch's float8_e4m3fn cast after clamping to +-448, or the
+nearest integer clamped to +-127; `normal_codes_host` / `normal_codes_device`.
+With scale ~ 1 / CODE_SIGMA the values they stand for are about N(0, 1).
 """
 from __future__ import annotations
 
@@ -33,6 +41,8 @@ import numpy as np
 
 DTYPES = ("f32", "f16", "bf16")
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+KV_FORMATS = ("fp8_e4m3", "int8")
+CODE_SIGMA = {"fp8_e4m3": 64.0, "int8": 32.0}
 
 
 @dataclass
@@ -55,6 +65,10 @@ class Workload:
     prefix_len: int = 0
     parent_len: int = 0
     suffix_lens: list = field(default_factory=list)
+    # 8-bit pools (workloads 6, 7): code format and per-pool scales
+    kv_format: str = ""
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def scale(self) -> float:
@@ -117,7 +131,33 @@ def workload(key: int) -> Workload:
         w.suffix_lens = [int(x) for x in rng.integers(0, 256, size=w.num_seqs, endpoint=True)]
         w.context_lens = [w.prefix_len + s for s in w.suffix_lens]
         return w
+    if key == 6:
+        w = workload_shapes_like(2, key, rng)
+        w.name, w.kv_format = "llama7b-fp8kv", "fp8_e4m3"
+        w.k_scale, w.v_scale = float(np.float32(0.0165)), float(np.float32(0.0145))
+        return w
+    if key == 7:
+        w = workload_shapes_like(3, key, rng)
+        w.name, w.kv_format = "gqa-bf16-int8kv", "int8"
+        w.k_scale, w.v_scale = float(np.float32(0.031)), float(np.float32(0.029))
+        return w
     raise ValueError(f"unknown workload {key}")
+
+
+def workload_shapes_like(base: int, key: int, rng: np.random.Generator) -> Workload:
+    """Workload `base`'s shapes and length distribution, drawn again from `rng`."""
+    if base == 2:
+        w = Workload(key, "", "f16", 64, 32, 32, 128, 16)
+        w.context_lens = [int(x) for x in rng.integers(256, 2048, size=64, endpoint=True)]
+        w.num_blocks = 8192
+    else:
+        w = Workload(key, "", "bf16", 256, 32, 8, 128, 32)
+        u = rng.uniform(math.log(128), math.log(4096), size=256)
+        w.context_lens = [int(min(4096, max(128, round(math.exp(x))))) for x in u]
+        need = sum(_ceil_div(c, 32) for c in w.context_lens)
+        w.num_blocks = _ceil_div(11 * need, 10)
+    w.free_order = rng.permutation(w.num_blocks).astype(np.int32)
+    return w
 
 
 def pool_shapes(w: Workload):
@@ -184,6 +224,32 @@ def to_numpy(t, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
+
+
+def normal_codes_host(shape, seed: int, fmt: str) -> np.ndarray:
+    """8-bit codes (uint8) of N(0, CODE_SIGMA^2) float32 draws from numpy PCG64(seed)."""
+    import torch
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(CODE_SIGMA[fmt])
+    return _codes(torch.from_numpy(x), fmt).numpy()
+
+
+def normal_codes_device(shape, seed: int, fmt: str, device="cuda"):
+    """8-bit codes (torch.uint8 on `device`) of N(0, CODE_SIGMA^2) draws from torch's generator."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32) * CODE_SIGMA[fmt]
+    return _codes(x, fmt)
+
+
+def _codes(x, fmt: str):
+    import torch
+    if fmt == "fp8_e4m3":
+        return x.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    if fmt == "int8":
+        return x.round().clamp(-127.0, 127.0).to(torch.int8).view(torch.uint8)
+    raise ValueError(fmt)
 
 
 def tensor_seeds(key: int) -> dict:

@@ -74,7 +74,18 @@ class DeviceWorkload:
         k_shape, v_shape = synth.pool_shapes(w)
         if pool_on_host is None:
             pool_on_host = key == 1
-        if pool_on_host:
+        self.quant = (w.kv_format, w.k_scale, w.v_scale) if w.kv_format else None
+        if self.quant:  # 8-bit pools: uint8 codes
+            if pool_on_host:
+                self.key_cache = torch.from_numpy(synth.normal_codes_host(k_shape, self.seeds["key_cache"],
+                                                                          w.kv_format)).to(dev)
+                self.value_cache = torch.from_numpy(synth.normal_codes_host(v_shape, self.seeds["value_cache"],
+                                                                            w.kv_format)).to(dev)
+            else:
+                self.key_cache = synth.normal_codes_device(k_shape, self.seeds["key_cache"], w.kv_format)
+                self.value_cache = synth.normal_codes_device(v_shape, self.seeds["value_cache"], w.kv_format)
+            self.query = synth.normal_device((w.num_seqs, w.num_heads, w.head_dim), self.seeds["query"], w.dtype)
+        elif pool_on_host:
             self.key_cache = synth.to_torch(synth.normal_host(k_shape, self.seeds["key_cache"], w.dtype),
                                             w.dtype).to(dev)
             self.value_cache = synth.to_torch(synth.normal_host(v_shape, self.seeds["value_cache"], w.dtype),
@@ -103,6 +114,10 @@ class DeviceWorkload:
         [len(table), 1, D, bs] (storage arrays)."""
         import torch
         idx = torch.tensor(table, dtype=torch.long, device=self.device)
+        if self.quant:
+            kc = self.key_cache[:, g].index_select(0, idx).cpu().numpy()[:, None]
+            vc = self.value_cache[:, g].index_select(0, idx).cpu().numpy()[:, None]
+            return kc, vc
         kc = synth.to_numpy(self.key_cache[:, g].index_select(0, idx), self.w.dtype)[:, None]
         vc = synth.to_numpy(self.value_cache[:, g].index_select(0, idx), self.w.dtype)[:, None]
         return kc, vc
@@ -117,7 +132,7 @@ class DeviceWorkload:
         kc, vc = self._fetch_blocks(table, g)
         q = synth.to_numpy(self.query[s, h:h + 1], w.dtype)
         ident = np.arange(len(table), dtype=np.int32)
-        return A.decode_one(q, kc, vc, ident, n, 0, 1, w.scale, w.dtype)
+        return A.decode_one(q, kc, vc, ident, n, 0, 1, w.scale, w.dtype, quant=self.quant)
 
     def oracle_partials(self, s: int, h: int, partition_size: int):
         import torch
@@ -126,7 +141,7 @@ class DeviceWorkload:
         table = self.ora.tables[s]
         g = h // (w.num_heads // w.num_kv_heads)
         kc, vc = self._fetch_blocks(table, g)
-        K, V = A.gather_kv(kc, vc, np.arange(len(table)), n, 0, w.dtype)
+        K, V = A.kv_for(kc, vc, np.arange(len(table)), n, 0, w.dtype, self.quant)
         q = A.to_f64(synth.to_numpy(self.query[s, h], w.dtype), w.dtype)
         return A.partition_partials(q, K, V, A.scale_f64(w.scale), partition_size)
 

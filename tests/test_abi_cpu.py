@@ -19,7 +19,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 29
+    assert len(names) == 31
     for n in names:
         assert hasattr(pa.lib, n), n
         assert C.cast(getattr(pa.lib, n), C.c_void_p).value
@@ -27,7 +27,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_status_strings():
-    assert pa.lib.pa_abi_version() == 2
+    assert pa.lib.pa_abi_version() == 3
     for code in range(9):
         assert pa.lib.pa_status_string(code)
     assert pa.lib.pa_status_string(99) == b"unknown status"
@@ -102,3 +102,58 @@ def test_longest_first_order():
         got = pa.pa_order_longest_first(lens.tolist())
         assert got == [int(i) for i in np.argsort(-lens, kind="stable")]
     assert pa.lib.pa_order_longest_first(None, 3, None) == 1
+
+
+def _decode_quant(**kw):
+    a = dict(out=16, query=16, kc=16, vc=16, tab=16, ctx=16, S=0, H=32, Hkv=32, D=128, bs=16, MB=4, NB=8,
+             maxlen=64, scale=0.1, ks=0.02, vs=0.03, dt=F, kv=pa.PA_FP8_E4M3, flags=0, ps=512, ws=None, wsb=0)
+    a.update(kw)
+    path = C.c_int32(-7)
+    st = pa.lib.pa_decode_quant(a["out"], a["query"], a["kc"], a["vc"], a["tab"], a["ctx"], None, a["S"],
+                                a["H"], a["Hkv"], a["D"], a["bs"], a["MB"], a["NB"], a["maxlen"], a["scale"],
+                                a["ks"], a["vs"], a["dt"], a["kv"], a["flags"], a["ps"], a["ws"], a["wsb"],
+                                C.byref(path), None)
+    return st, path.value
+
+
+def test_decode_quant_validation_rejects_before_launch():
+    # num_seqs = 0: every check runs, nothing is launched
+    assert _decode_quant() == (0, 0)
+    assert _decode_quant(kv=pa.PA_INT8) == (0, 0)
+    assert _decode_quant(dt=pa.PA_BF16)[0] == 0
+    assert _decode_quant(dt=pa.PA_F32)[0] == 5        # 8-bit pools decode in f16/bf16
+    assert _decode_quant(kv=pa.PA_F16)[0] == 5        # kv_dtype must be a code type
+    assert _decode_quant(kv=9)[0] == 5
+    assert _decode_quant(ks=0.0)[0] == 1
+    assert _decode_quant(vs=-1.0)[0] == 1
+    assert _decode_quant(ks=float("nan"))[0] == 1
+    assert _decode_quant(vs=float("inf"))[0] == 1
+    assert _decode_quant(flags=4)[0] == 1             # unknown flag bit
+    assert _decode_quant(flags=pa.PA_DECODE_SPLIT, ps=24)[0] == 1  # not a multiple of block_size
+    assert _decode_quant(flags=pa.PA_DECODE_SPLIT, ps=512) == (0, 1)
+    assert _decode_quant(D=96)[0] == 5
+
+
+def test_reshape_quant_validation_rejects_before_launch():
+    def call(**kw):
+        a = dict(k=16, v=16, kc=16, vc=16, slots=16, T=0, NB=8, Hkv=2, D=64, bs=16, dt=F, kv=pa.PA_FP8_E4M3,
+                 ks=0.5, vs=0.5)
+        a.update(kw)
+        return pa.lib.pa_reshape_and_cache_quant(a["k"], a["v"], a["kc"], a["vc"], a["slots"], a["T"], a["NB"],
+                                                 a["Hkv"], a["D"], a["bs"], a["dt"], a["kv"], a["ks"], a["vs"],
+                                                 None)
+    assert call() == 0
+    assert call(dt=pa.PA_F32, kv=pa.PA_INT8) == 0
+    assert call(kv=pa.PA_BF16) == 5
+    assert call(dt=pa.PA_FP8_E4M3) == 5
+    assert call(ks=0.0) == 1
+    assert call(vs=float("nan")) == 1
+    assert call(T=-1) == 1
+    assert call(T=3, k=0) == 1
+    assert call(T=3, kc=8) == 1                     # not 16-byte aligned
+
+
+def test_copy_blocks_accepts_8bit_pools():
+    for kv in (pa.PA_FP8_E4M3, pa.PA_INT8):
+        assert pa.lib.pa_copy_blocks(16, 16, 16, 0, 8, 2, 64, 16, kv, None) == 0
+        assert pa.lib.pa_copy_blocks(16, 16, 16, 0, 8, 2, 96, 16, kv, None) == 5
