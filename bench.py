@@ -139,8 +139,9 @@ def _counter_per_dispatch(folder: str, counter: str, kernel_substr: str) -> tupl
 
 
 def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
-    # the path pa_decode_auto takes on these workloads (the bench line reports it)
-    w_path = path or ("split" if workload == 4 else "single")
+    # the path that ran (pa_decode_auto takes split on the long-context workload only); the bench
+    # line looks its traffic up under the same name
+    w_path = ("split" if workload == 4 else "single") if path in (None, "auto") else path
     decode = "decode_kernel"
     stats = _csv_rows(os.path.join(outdir, "trace"), "kernel_stats.csv")
     stats.sort(key=lambda r: -float(r["totaldurationns"]))
@@ -173,8 +174,10 @@ def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
     out = [f"# rocprofv3: decode kernel, workload {workload} ({w_path} path)", "",
            f"Decode kernel source digest (decode.hip + decode_kernel.hpp + device_common.hpp): "
            f"`{source_digest()}`", "",
-           "Commands (run from any directory with TMPDIR=/tmp; OUTDIR is a scratch folder):", "", "```"]
-    out += profile_commands(workload, "OUTDIR", path) + ["```", "", "## Kernel trace (--kernel-trace --stats)", "",
+           "Commands (run from /tmp with TMPDIR=/tmp; REPO is the repository root, OUTDIR a scratch folder):", "",
+           "```"]
+    out += [c.replace(ROOT, "$REPO") for c in profile_commands(workload, "OUTDIR", path)]
+    out += ["```", "", "## Kernel trace (--kernel-trace --stats)", "",
                                                         "| kernel | calls | avg us | min us | max us | % time |",
                                                         "|---|---|---|---|---|---|"]
     for r in stats[:8]:
