@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -71,7 +71,8 @@ typedef enum pa_status {
   PA_ERR_UNSUPPORTED = 5,        /* dtype / head_dim / block_size not built */
   PA_ERR_BAD_TABLE = 6,          /* PA_DEBUG validation: index outside its range, or a write race */
   PA_ERR_WORKSPACE_TOO_SMALL = 7,
-  PA_ERR_HIP = 8                 /* a HIP runtime call or kernel launch failed */
+  PA_ERR_HIP = 8,                /* a HIP runtime call or kernel launch failed */
+  PA_ERR_UNKNOWN_PREFIX = 9      /* no prefix-cache entry with this id */
 } pa_status;
 
 /* Element types.  PA_F32, PA_F16 and PA_BF16 are model types (query, out,
@@ -191,6 +192,51 @@ pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out)
  * scheduling); this changes no result.  Host arrays; PA_ERR_INVALID_ARG on a
  * null pointer or negative n. */
 pa_status pa_order_longest_first(const int32_t* context_lens, int32_t n, int32_t* order);
+
+/* ------------------------------------------------------------------------ *
+ * Prefix caching ([IMPL] §3.2 CachedPrefix / PrefixCacheManager): requests
+ * that share a prompt prefix (a system prompt) share the blocks holding its
+ * KV.  An entry maps the prefix's tokens to ceil(n / bs) blocks, counts the
+ * requests using it (users) and holds one reference on each block.  The key
+ * is the token sequence itself, compared in full (the page hashes it to 12
+ * hex digits; exact keys keep different prompts from sharing blocks).
+ * ------------------------------------------------------------------------ */
+
+/* Look up tokens[0..num_tokens).  Known: one more user, *hit = 1.  New: the
+ * entry takes ceil(num_tokens / bs) blocks from the head of the free queue,
+ * has one user and *hit = 0; the caller computes the prefix's KV and writes
+ * it into those blocks (pa_prefix_info lists them).  *prefix_id receives the
+ * entry's id (ids count up from 1 and are not reused).  PA_ERR_NO_FREE_BLOCKS
+ * leaves the state unchanged. */
+pa_status pa_prefix_get_or_create(pa_allocator* a, const int32_t* tokens, int32_t num_tokens,
+                                  int64_t* prefix_id, int32_t* hit);
+
+/* One user fewer; at zero the entry releases its block references (table
+ * order; blocks still used by sequences stay allocated) and is removed.
+ * PA_ERR_UNKNOWN_PREFIX for an unknown id. */
+pa_status pa_prefix_release(pa_allocator* a, int64_t prefix_id);
+
+/* An entry's blocks (host out[0..capacity), *num_blocks receives the count),
+ * its token count and its number of users.  Any output pointer but
+ * num_blocks may be NULL. */
+pa_status pa_prefix_info(const pa_allocator* a, int64_t prefix_id, int32_t* blocks, int32_t capacity,
+                         int32_t* num_blocks, int32_t* num_tokens, int32_t* users);
+
+/* New sequence on a cached prefix of n_p tokens in P blocks: its table starts
+ * with the entry's blocks (one more reference each, never written through
+ * this sequence) followed by ceil(own_tokens / bs) fresh blocks for its own
+ * tokens, which start at position P * bs ([IMPL] §3.2's demo counts them in
+ * blocks of their own).  Its length counts positions: P * bs + own_tokens.
+ * When n_p < P * bs, positions [n_p, P * bs) hold no token: a hole that the
+ * decode must skip (pa_build_masks gives it, pa_decode_masked skips it).
+ * Appends continue after the own tokens.  A fork keeps the hole and may not
+ * end inside it (PA_ERR_INVALID_ARG). */
+pa_status pa_seq_create_with_prefix(pa_allocator* a, int64_t seq_id, int64_t prefix_id, int32_t own_tokens);
+
+/* Per sequence the positions [mask_lo, mask_hi) that hold no token, for
+ * pa_decode_masked (both 0 when there is none).  mask_lo, mask_hi: host [n]. */
+pa_status pa_build_masks(const pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t* mask_lo,
+                         int32_t* mask_hi);
 
 /* ======================================================================== *
  * Device operations                                                         *

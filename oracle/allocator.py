@@ -28,6 +28,26 @@ Policy, and where the pages fix it:
   ("PagedAttention 源码解析…" §三 raises, xdnf.cn §4.2 asserts, "PagedAttention
   实现细节" §3.3 fails the copy-on-write).
 * A batch of appends is processed in the order given, and all-or-nothing.
+
+Prefix caching ("PagedAttention 实现细节" §3.2, CachedPrefix and
+PrefixCacheManager):
+* An entry maps a prompt prefix (its tokens) to the blocks that hold its KV,
+  with a count of the requests using it and its token count.  get_or_create
+  on a known prefix adds one user and returns the same blocks; on a new one it
+  takes ceil(n / bs) blocks from the pool (the caller then computes and writes
+  their KV) with one user.  release drops one user; at zero the entry lets go
+  of its blocks.  Reading taken: the key is the token sequence itself (the
+  page hashes its text to 12 hex digits; comparing the tokens in full keeps two
+  different prompts from ever sharing blocks).  Entry ids count up from 1.
+* The entry holds one reference on each of its blocks; a sequence built on it
+  holds another (so blocks outlive a released entry while sequences use them).
+* A sequence built on a prefix of n_p tokens (seq_create_with_prefix) has the
+  prefix's P = ceil(n_p / bs) blocks first and its own tokens from position
+  P * bs on, in fresh blocks: the page's demo counts the request's own tokens
+  in blocks of their own (9-token prompt, 1 block; 30 own tokens, 2 blocks).
+  Positions n_p .. P*bs - 1 are then a hole in the sequence: they hold no
+  token and decode must skip them (`masks`).  A sequence's length counts
+  positions, hole included; fork keeps the hole and may not end inside it.
 """
 from __future__ import annotations
 
@@ -43,6 +63,7 @@ class AllocatorError(Exception):
 
 NO_FREE_BLOCKS = "NO_FREE_BLOCKS"
 UNKNOWN_SEQ = "UNKNOWN_SEQ"
+UNKNOWN_PREFIX = "UNKNOWN_PREFIX"
 SEQ_EXISTS = "SEQ_EXISTS"
 INVALID_ARG = "INVALID_ARG"
 
@@ -61,6 +82,10 @@ class BlockAllocator:
         self.tables: dict[int, list[int]] = {}
         self.lens: dict[int, int] = {}
         self.stats = {"blocks_allocated": 0, "blocks_freed": 0, "cow_copies": 0}
+        self.holes: dict[int, tuple[int, int]] = {}      # seq -> (lo, hi) positions with no token
+        self.prefixes: dict[tuple, int] = {}             # prefix tokens -> entry id
+        self.entries: dict[int, dict] = {}               # entry id -> blocks, users, length, key
+        self.next_prefix_id = 1
 
     # -- helpers -------------------------------------------------------------
     def _blocks_for(self, n: int) -> int:
@@ -106,11 +131,16 @@ class BlockAllocator:
         n = self.lens[parent] if num_tokens < 0 else num_tokens
         if n > self.lens[parent]:
             raise AllocatorError(INVALID_ARG, "fork length beyond the parent")
+        hole = self.holes.get(parent)
+        if hole and hole[0] < n < hole[1]:
+            raise AllocatorError(INVALID_ARG, "fork length inside the prefix hole")
         shared = self.tables[parent][: self._blocks_for(n)]
         for b in shared:
             self.refs[b] += 1
         self.tables[child] = list(shared)
         self.lens[child] = n
+        if hole and n >= hole[1]:
+            self.holes[child] = hole
 
     def seq_append_slot(self, seq_id: int):
         """Reserve the slot of the next token; returns (slot, cow_src, cow_dst), -1s when no copy."""
@@ -153,6 +183,7 @@ class BlockAllocator:
             self._release(b)
         del self.tables[seq_id]
         del self.lens[seq_id]
+        self.holes.pop(seq_id, None)
 
     def can_allocate(self, num_blocks: int) -> bool:
         return num_blocks <= len(self.free)
@@ -185,3 +216,71 @@ class BlockAllocator:
             tables.append(t + [-1] * (max_blocks - len(t)))
             lens.append(self.lens[s])
         return tables, lens
+
+    # -- prefix caching ------------------------------------------------------
+    def prefix_get_or_create(self, tokens):
+        """Entry for this prompt prefix: (entry id, hit).  A hit adds a user; a miss takes
+        ceil(n / bs) blocks (one reference each, held by the entry) with one user."""
+        key = tuple(int(t) for t in tokens)
+        if key in self.prefixes:
+            pid = self.prefixes[key]
+            self.entries[pid]["users"] += 1
+            return pid, True
+        nb = self._blocks_for(len(key))
+        if nb > len(self.free):
+            raise AllocatorError(NO_FREE_BLOCKS)
+        pid = self.next_prefix_id
+        self.next_prefix_id += 1
+        self.entries[pid] = {"blocks": [self._take() for _ in range(nb)], "users": 1, "length": len(key),
+                             "key": key}
+        self.prefixes[key] = pid
+        return pid, False
+
+    def _entry(self, pid):
+        if pid not in self.entries:
+            raise AllocatorError(UNKNOWN_PREFIX, f"prefix {pid}")
+        return self.entries[pid]
+
+    def prefix_release(self, pid):
+        """Drop one user; at zero the entry releases its blocks (table order) and is removed."""
+        e = self._entry(pid)
+        e["users"] -= 1
+        if e["users"] <= 0:
+            for b in e["blocks"]:
+                self._release(b)
+            del self.prefixes[e["key"]]
+            del self.entries[pid]
+
+    def prefix_info(self, pid):
+        """(blocks, token count, users) of an entry."""
+        e = self._entry(pid)
+        return list(e["blocks"]), e["length"], e["users"]
+
+    def seq_create_with_prefix(self, seq_id, pid, own_tokens: int):
+        """Sequence = the entry's blocks (one more reference each), then ceil(own / bs) fresh
+        blocks for its own tokens at positions P*bs ..; positions n_p .. P*bs - 1 are a hole."""
+        if seq_id in self.tables:
+            raise AllocatorError(SEQ_EXISTS, str(seq_id))
+        if own_tokens < 0:
+            raise AllocatorError(INVALID_ARG, "own_tokens < 0")
+        e = self._entry(pid)
+        nb = self._blocks_for(own_tokens)
+        if nb > len(self.free):
+            raise AllocatorError(NO_FREE_BLOCKS)
+        for b in e["blocks"]:
+            self.refs[b] += 1
+        P = len(e["blocks"])
+        self.tables[seq_id] = list(e["blocks"]) + [self._take() for _ in range(nb)]
+        self.lens[seq_id] = P * self.block_size + own_tokens
+        if e["length"] < P * self.block_size:
+            self.holes[seq_id] = (e["length"], P * self.block_size)
+
+    def masks(self, seq_ids):
+        """Per sequence the positions [lo, hi) that hold no token (lo = hi = 0: none)."""
+        lo, hi = [], []
+        for s in seq_ids:
+            self._need(s)
+            a, b = self.holes.get(s, (0, 0))
+            lo.append(a)
+            hi.append(b)
+        return lo, hi

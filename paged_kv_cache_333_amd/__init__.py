@@ -53,7 +53,7 @@ if len(_RUNTIMES) > 1:
 PA_OK = 0
 STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_NO_FREE_BLOCKS", 3: "PA_ERR_UNKNOWN_SEQ",
           4: "PA_ERR_SEQ_EXISTS", 5: "PA_ERR_UNSUPPORTED", 6: "PA_ERR_BAD_TABLE",
-          7: "PA_ERR_WORKSPACE_TOO_SMALL", 8: "PA_ERR_HIP"}
+          7: "PA_ERR_WORKSPACE_TOO_SMALL", 8: "PA_ERR_HIP", 9: "PA_ERR_UNKNOWN_PREFIX"}
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3, 4
 PA_DECODE_CACHED_KV = 1
 PA_DECODE_SPLIT = 2
@@ -85,6 +85,11 @@ _PROTOS = {
     "pa_free_list": (_i32, [_vp, _pi32, _i32, _pi32]),
     "pa_build_block_tables": (_i32, [_vp, _pi64, _i32, _i32, _pi32, _pi32]),
     "pa_allocator_get_stats": (_i32, [_vp, C.POINTER(pa_allocator_stats)]),
+    "pa_prefix_get_or_create": (_i32, [_vp, _pi32, _i32, _pi64, _pi32]),
+    "pa_prefix_release": (_i32, [_vp, _i64]),
+    "pa_prefix_info": (_i32, [_vp, _i64, _pi32, _i32, _pi32, _pi32, _pi32]),
+    "pa_seq_create_with_prefix": (_i32, [_vp, _i64, _i64, _i32]),
+    "pa_build_masks": (_i32, [_vp, _pi64, _i32, _pi32, _pi32]),
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_order_longest_first": (_i32, [_pi32, _i32, _pi32]),
@@ -373,10 +378,12 @@ class Allocator:
         _check(lib.pa_allocator_create(num_blocks, block_size, order, C.byref(h)), "pa_allocator_create")
         self._h = h
 
+    _destroy = lib.pa_allocator_destroy  # kept on the class: module globals may be gone at exit
+
     def __del__(self):
         h = getattr(self, "_h", None)
         if h is not None and h.value:
-            lib.pa_allocator_destroy(h)
+            self._destroy(h)
             self._h = None
 
     def clone(self) -> "Allocator":
@@ -459,6 +466,38 @@ class Allocator:
         _check(lib.pa_build_block_tables(self._h, C.cast(seq_ids_ptr, _pi64), n, max_blocks,
                                          C.cast(tables_ptr, _pi32), C.cast(lens_ptr, _pi32)),
                "pa_build_block_tables")
+
+    # -- prefix caching --------------------------------------------------------
+    def prefix_get_or_create(self, tokens):
+        """(entry id, hit) for this prompt prefix; a miss takes ceil(n / bs) blocks."""
+        n = len(tokens)
+        arr = (C.c_int32 * max(n, 1))(*[int(t) for t in tokens])
+        pid, hit = C.c_int64(), C.c_int32()
+        _check(lib.pa_prefix_get_or_create(self._h, arr, n, C.byref(pid), C.byref(hit)), "pa_prefix_get_or_create")
+        return pid.value, bool(hit.value)
+
+    def prefix_release(self, prefix_id: int):
+        _check(lib.pa_prefix_release(self._h, prefix_id), "pa_prefix_release")
+
+    def prefix_info(self, prefix_id: int):
+        """(blocks, token count, users) of an entry."""
+        nb, nt, users = C.c_int32(), C.c_int32(), C.c_int32()
+        _check(lib.pa_prefix_info(self._h, prefix_id, None, 0, C.byref(nb), None, None), "pa_prefix_info")
+        buf = (C.c_int32 * max(nb.value, 1))()
+        _check(lib.pa_prefix_info(self._h, prefix_id, buf, nb.value, C.byref(nb), C.byref(nt), C.byref(users)),
+               "pa_prefix_info")
+        return list(buf[:nb.value]), nt.value, users.value
+
+    def seq_create_with_prefix(self, seq_id: int, prefix_id: int, own_tokens: int):
+        _check(lib.pa_seq_create_with_prefix(self._h, seq_id, prefix_id, own_tokens), "pa_seq_create_with_prefix")
+
+    def masks(self, seq_ids):
+        """Per sequence the positions [lo, hi) with no token: (lo list, hi list)."""
+        n = len(seq_ids)
+        ids = (C.c_int64 * max(n, 1))(*seq_ids)
+        lo, hi = (C.c_int32 * max(n, 1))(), (C.c_int32 * max(n, 1))()
+        _check(lib.pa_build_masks(self._h, ids, n, lo, hi), "pa_build_masks")
+        return list(lo[:n]), list(hi[:n])
 
     def stats(self) -> dict:
         st = pa_allocator_stats()

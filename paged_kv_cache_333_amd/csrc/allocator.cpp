@@ -12,6 +12,12 @@
 //    if its count is above one (the copy is done on the device by the caller);
 //  * every call is all-or-nothing.
 //
+// Prefix caching ("PagedAttention 实现细节" §3.2): entries map a prompt
+// prefix's tokens (compared in full) to the blocks holding its KV, count their
+// users, and hold one reference per block.  A sequence built on an entry
+// shares its blocks and puts its own tokens from the next block boundary on,
+// leaving a hole [n_p, P * bs) that decode masks.
+//
 // The free queue is a ring buffer of num_blocks entries; a block is never in
 // it twice, so it never overflows.
 #include <algorithm>
@@ -28,6 +34,28 @@ namespace {
 struct Seq {
   std::vector<int32_t> table;
   int32_t len = 0;
+  int32_t hole_lo = 0, hole_hi = 0;  // positions [lo, hi) hold no token (lo == hi: none)
+};
+
+struct PrefixEntry {
+  std::vector<int32_t> key;     // the prefix's tokens
+  std::vector<int32_t> blocks;
+  int32_t users = 0;
+};
+
+// FNV-1a over the token values, for bucketing; keys are compared in full.
+struct TokensHash {
+  size_t operator()(const std::vector<int32_t>& v) const {
+    uint64_t h = 1469598103934665603ull;
+    for (int32_t t : v) {
+      uint32_t u = static_cast<uint32_t>(t);
+      for (int i = 0; i < 4; ++i) {
+        h ^= (u >> (8 * i)) & 0xffu;
+        h *= 1099511628211ull;
+      }
+    }
+    return static_cast<size_t>(h);
+  }
 };
 
 }  // namespace
@@ -40,6 +68,9 @@ struct pa_allocator {
   int32_t count = 0;          // number of free blocks
   std::vector<int32_t> refs;
   std::unordered_map<int64_t, Seq> seqs;
+  std::unordered_map<int64_t, PrefixEntry> prefixes;                 // by entry id
+  std::unordered_map<std::vector<int32_t>, int64_t, TokensHash> prefix_ids;  // by tokens
+  int64_t next_prefix_id = 1;
   pa_allocator_stats stats{0, 0, 0};
   mutable std::mutex mu;
 
@@ -183,6 +214,9 @@ pa_status pa_allocator_clone(const pa_allocator* a, pa_allocator** out) {
   c->count = a->count;
   c->refs = a->refs;
   c->seqs = a->seqs;
+  c->prefixes = a->prefixes;
+  c->prefix_ids = a->prefix_ids;
+  c->next_prefix_id = a->next_prefix_id;
   c->stats = a->stats;
   *out = c;
   return PA_OK;
@@ -212,10 +246,15 @@ pa_status pa_seq_fork(pa_allocator* a, int64_t parent, int64_t child, int32_t nu
   const Seq& p = it->second;
   int32_t n = num_tokens < 0 ? p.len : num_tokens;
   if (n > p.len) return fail(PA_ERR_INVALID_ARG, "fork length beyond the parent's length");
+  if (p.hole_lo < n && n < p.hole_hi) return fail(PA_ERR_INVALID_ARG, "fork length inside the prefix hole");
   Seq c;
   int32_t nb = a->blocks_for(n);
   c.table.assign(p.table.begin(), p.table.begin() + nb);
   c.len = n;
+  if (p.hole_lo < p.hole_hi && n >= p.hole_hi) {
+    c.hole_lo = p.hole_lo;
+    c.hole_hi = p.hole_hi;
+  }
   for (int32_t b : c.table) ++a->refs[b];
   a->seqs.emplace(child, std::move(c));
   return PA_OK;
@@ -362,6 +401,113 @@ pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out)
   if (!a || !out) return fail(PA_ERR_INVALID_ARG, "null argument");
   std::lock_guard<std::mutex> g(a->mu);
   *out = a->stats;
+  return PA_OK;
+}
+
+pa_status pa_prefix_get_or_create(pa_allocator* a, const int32_t* tokens, int32_t num_tokens,
+                                  int64_t* prefix_id, int32_t* hit) {
+  if (!a || !prefix_id || !hit || num_tokens < 0 || (num_tokens > 0 && !tokens))
+    return fail(PA_ERR_INVALID_ARG, "null argument or negative count");
+  std::lock_guard<std::mutex> g(a->mu);
+  std::vector<int32_t> key(tokens, tokens + num_tokens);
+  auto it = a->prefix_ids.find(key);
+  if (it != a->prefix_ids.end()) {
+    ++a->prefixes[it->second].users;
+    *prefix_id = it->second;
+    *hit = 1;
+    return PA_OK;
+  }
+  const int32_t nb = a->blocks_for(num_tokens);
+  if (nb > a->count) return fail(PA_ERR_NO_FREE_BLOCKS, "not enough free blocks for the prefix");
+  PrefixEntry e;
+  e.key = key;
+  e.users = 1;
+  e.blocks.reserve(nb);
+  for (int32_t i = 0; i < nb; ++i) e.blocks.push_back(a->pop_head());
+  const int64_t id = a->next_prefix_id++;
+  a->prefixes.emplace(id, std::move(e));
+  a->prefix_ids.emplace(std::move(key), id);
+  *prefix_id = id;
+  *hit = 0;
+  return PA_OK;
+}
+
+pa_status pa_prefix_release(pa_allocator* a, int64_t prefix_id) {
+  if (!a) return fail(PA_ERR_INVALID_ARG, "null allocator");
+  std::lock_guard<std::mutex> g(a->mu);
+  auto it = a->prefixes.find(prefix_id);
+  if (it == a->prefixes.end()) return fail(PA_ERR_UNKNOWN_PREFIX, "unknown prefix id");
+  PrefixEntry& e = it->second;
+  if (--e.users <= 0) {
+    for (int32_t b : e.blocks) a->release(b);
+    a->prefix_ids.erase(e.key);
+    a->prefixes.erase(it);
+  }
+  return PA_OK;
+}
+
+pa_status pa_prefix_info(const pa_allocator* a, int64_t prefix_id, int32_t* blocks, int32_t capacity,
+                         int32_t* num_blocks, int32_t* num_tokens, int32_t* users) {
+  if (!a || !num_blocks || capacity < 0 || (capacity > 0 && !blocks))
+    return fail(PA_ERR_INVALID_ARG, "null argument or negative capacity");
+  std::lock_guard<std::mutex> g(a->mu);
+  auto it = a->prefixes.find(prefix_id);
+  if (it == a->prefixes.end()) return fail(PA_ERR_UNKNOWN_PREFIX, "unknown prefix id");
+  const PrefixEntry& e = it->second;
+  const int32_t nb = static_cast<int32_t>(e.blocks.size());
+  if (blocks) {
+    if (nb > capacity) return fail(PA_ERR_INVALID_ARG, "capacity too small");
+    if (nb) std::memcpy(blocks, e.blocks.data(), nb * sizeof(int32_t));
+  }
+  *num_blocks = nb;
+  if (num_tokens) *num_tokens = static_cast<int32_t>(e.key.size());
+  if (users) *users = e.users;
+  return PA_OK;
+}
+
+pa_status pa_seq_create_with_prefix(pa_allocator* a, int64_t seq_id, int64_t prefix_id, int32_t own_tokens) {
+  if (!a) return fail(PA_ERR_INVALID_ARG, "null allocator");
+  std::lock_guard<std::mutex> g(a->mu);
+  if (a->seqs.count(seq_id)) return fail(PA_ERR_SEQ_EXISTS, "sequence id already in use");
+  if (own_tokens < 0) return fail(PA_ERR_INVALID_ARG, "own_tokens < 0");
+  auto it = a->prefixes.find(prefix_id);
+  if (it == a->prefixes.end()) return fail(PA_ERR_UNKNOWN_PREFIX, "unknown prefix id");
+  const PrefixEntry& e = it->second;
+  const int64_t start = static_cast<int64_t>(e.blocks.size()) * a->block_size;
+  if (start + own_tokens > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "sequence length overflow");
+  const int32_t nb = a->blocks_for(own_tokens);
+  if (nb > a->count) return fail(PA_ERR_NO_FREE_BLOCKS, "not enough free blocks for the sequence");
+  Seq s;
+  s.table.reserve(e.blocks.size() + nb + 1);
+  for (int32_t b : e.blocks) {
+    ++a->refs[b];
+    s.table.push_back(b);
+  }
+  for (int32_t i = 0; i < nb; ++i) s.table.push_back(a->pop_head());
+  s.len = static_cast<int32_t>(start) + own_tokens;
+  if (static_cast<int64_t>(e.key.size()) < start) {
+    s.hole_lo = static_cast<int32_t>(e.key.size());
+    s.hole_hi = static_cast<int32_t>(start);
+  }
+  a->seqs.emplace(seq_id, std::move(s));
+  return PA_OK;
+}
+
+pa_status pa_build_masks(const pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t* mask_lo,
+                         int32_t* mask_hi) {
+  if (!a || n < 0 || (n > 0 && (!seq_ids || !mask_lo || !mask_hi)))
+    return fail(PA_ERR_INVALID_ARG, "null argument or negative count");
+  std::lock_guard<std::mutex> g(a->mu);
+  std::vector<const Seq*> ptrs(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence");
+    ptrs[i] = &it->second;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    mask_lo[i] = ptrs[i]->hole_lo;
+    mask_hi[i] = ptrs[i]->hole_hi;
+  }
   return PA_OK;
 }
 

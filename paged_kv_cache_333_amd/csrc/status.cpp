@@ -25,6 +25,7 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_BAD_TABLE: return "index outside its range";
     case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case PA_ERR_HIP: return "HIP error";
+    case PA_ERR_UNKNOWN_PREFIX: return "unknown prefix";
   }
   return "unknown status";
 }

@@ -479,3 +479,56 @@ def check_quant_write_round_trip(seed=47):
 QUANT_PINS = [check_e4m3_special_values, check_e4m3_table_vs_torch, check_e4m3_encode_vs_torch,
               check_e4m3_round_trip, check_e4m3_saturation, check_int8_encode, check_quantize_division,
               check_quant_attention_lossless, check_quant_write_round_trip]
+
+
+# ----------------------------------------------------------------------------
+# prefix caching ("PagedAttention 实现细节" §3.2)
+
+def check_p4_prefix_demo():
+    """The page's demo, run through the allocator: blocks in use without and with the
+    prefix cache, the saving, the one prompt evaluation, the hole, and the teardown."""
+    g = golden("p4_prefix_demo.json")
+    R, bs = g["num_requests"], g["block_size"]
+    NB = 4 * R * (g["prefix_blocks"] + g["user_blocks"])
+    system = list(range(1000, 1000 + g["system_tokens"]))
+
+    plain = AL.BlockAllocator(NB, bs)
+    for r in range(R):
+        plain.seq_create(r, g["system_tokens"] + g["user_tokens"])
+    without = NB - plain.num_free_blocks()
+    assert without == g["blocks_without_cache"]
+
+    al = AL.BlockAllocator(NB, bs)
+    misses, pids = 0, set()
+    for r in range(R):
+        pid, hit = al.prefix_get_or_create(system)
+        misses += 0 if hit else 1
+        pids.add(pid)
+        al.seq_create_with_prefix(r, pid, g["user_tokens"])
+    with_cache = NB - al.num_free_blocks()
+    assert with_cache == g["blocks_with_cache"]
+    assert misses == g["prompt_evaluations_with_cache"] and len(pids) == 1
+    saved = without - with_cache
+    assert saved == g["blocks_saved"]
+    assert f"{saved / without * 100:.1f}" == g["saving_percent"]
+    assert f"{saved * g['kib_per_block'] / 1024:.1f}" == g["saved_mib"]
+    (pid,) = pids
+    blocks, length, users = al.prefix_info(pid)
+    assert len(blocks) == g["prefix_blocks"] and length == g["system_tokens"] and users == R
+    assert al.ref_count(blocks[0]) == 1 + R          # the entry's reference and one per request
+    for r in range(R):
+        t = al.block_table(r)
+        assert t[0] == blocks[0] and len(t) == g["prefix_blocks"] + g["user_blocks"]
+    # the request's own tokens start at the next block: positions 9..15 are a hole
+    assert al.seq_len(0) == g["prefix_blocks"] * bs + g["user_tokens"]
+    assert al.masks([0]) == ([g["system_tokens"]], [g["prefix_blocks"] * bs])
+    slot, src, dst = al.seq_append_slot(0)          # the next token goes after the own tokens
+    assert (src, dst) == (-1, -1)
+    assert slot == al.block_table(0)[(bs + g["user_tokens"]) // bs] * bs + (bs + g["user_tokens"]) % bs
+    # teardown: every request leaves; the entry goes with its last user
+    for r in range(R):
+        al.seq_free(r)
+        al.prefix_release(pid)
+    assert al.num_free_blocks() == NB and all(c == 0 for c in al.refs)
+    _, hit = al.prefix_get_or_create(system)
+    assert not hit

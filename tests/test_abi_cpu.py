@@ -19,7 +19,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 31
+    assert len(names) == 36
     for n in names:
         assert hasattr(pa.lib, n), n
         assert C.cast(getattr(pa.lib, n), C.c_void_p).value
@@ -27,8 +27,8 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_status_strings():
-    assert pa.lib.pa_abi_version() == 3
-    for code in range(9):
+    assert pa.lib.pa_abi_version() == 4
+    for code in range(10):
         assert pa.lib.pa_status_string(code)
     assert pa.lib.pa_status_string(99) == b"unknown status"
 

@@ -9,7 +9,8 @@ from oracle import allocator as AL
 from tests import oracle_pins as P
 
 CODE = {"PA_ERR_NO_FREE_BLOCKS": AL.NO_FREE_BLOCKS, "PA_ERR_UNKNOWN_SEQ": AL.UNKNOWN_SEQ,
-        "PA_ERR_SEQ_EXISTS": AL.SEQ_EXISTS, "PA_ERR_INVALID_ARG": AL.INVALID_ARG}
+        "PA_ERR_SEQ_EXISTS": AL.SEQ_EXISTS, "PA_ERR_INVALID_ARG": AL.INVALID_ARG,
+        "PA_ERR_UNKNOWN_PREFIX": AL.UNKNOWN_PREFIX}
 
 
 def same_state(cpp, ora):
@@ -18,6 +19,10 @@ def same_state(cpp, ora):
     for s in ora.tables:
         assert cpp.block_table(s) == ora.tables[s]
         assert cpp.seq_len(s) == ora.lens[s]
+    ids = list(ora.tables)
+    assert cpp.masks(ids) == ora.masks(ids)
+    for pid in ora.entries:
+        assert cpp.prefix_info(pid) == ora.prefix_info(pid)
     assert cpp.stats() == ora.stats
 
 
@@ -56,10 +61,20 @@ class _Shim:
     def free_list(self): return self._a.free_list()
     def ref_count(self, b): return self._a.ref_count(b)
     def num_free_blocks(self): return self._a.num_free_blocks()
+    def seq_len(self, s): return self._a.seq_len(self._id(s))
+    def prefix_get_or_create(self, t): return self._a.prefix_get_or_create(t)
+    def prefix_release(self, p): self._a.prefix_release(p)
+    def prefix_info(self, p): return self._a.prefix_info(p)
+    def seq_create_with_prefix(self, s, p, n): self._a.seq_create_with_prefix(self._id(s), p, n)
+    def masks(self, ids): return self._a.masks([self._id(s) for s in ids])
+
+    @property
+    def refs(self):
+        return [self._a.ref_count(b) for b in range(self.num_blocks)]
 
 
 @pytest.mark.parametrize("check", [P.check_p1_block_mapping, P.check_block_counts, P.check_addressing,
-                                   P.check_p4_cow_timeline, P.check_p2_lifecycle])
+                                   P.check_p4_cow_timeline, P.check_p2_lifecycle, P.check_p4_prefix_demo])
 def test_page_examples_on_cpp(monkeypatch, check):
     monkeypatch.setattr(AL, "BlockAllocator", _Shim)
     check()
@@ -145,3 +160,56 @@ def test_create_rejects_bad_free_order():
         pa.Allocator(3, 16, [0, 0, 1])
     with pytest.raises(pa.PAError):
         pa.Allocator(3, 16, [0, 1, 3])
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_prefix_ops_bit_exact(seed):
+    rng = np.random.default_rng(100 + seed)
+    NB = int(rng.integers(16, 150))
+    bs = int(rng.choice([4, 8, 16]))
+    order = rng.permutation(NB)
+    cpp = pa.Allocator(NB, bs, order)
+    ora = AL.BlockAllocator(NB, bs, order)
+    prompts = [[int(x) for x in rng.integers(0, 40, size=int(n))] for n in (0, 2, bs, bs + 3, 2 * bs + 1)]
+    live, users, nxt = [], [], 0
+    for step in range(1200):
+        op = int(rng.integers(0, 9))
+        if op == 0:
+            t = prompts[int(rng.integers(len(prompts)))]
+            r = both(lambda: cpp.prefix_get_or_create(t), lambda: ora.prefix_get_or_create(t))
+            if r is None:
+                users.append(ora.prefixes[tuple(t)])
+        elif op == 1:
+            pid = users[int(rng.integers(len(users)))] if users and rng.random() < 0.9 else 777
+            n = int(rng.integers(-1, 3 * bs))
+            if both(lambda: cpp.seq_create_with_prefix(nxt, pid, n),
+                    lambda: ora.seq_create_with_prefix(nxt, pid, n)) is None:
+                live.append(nxt)
+            nxt += 1
+        elif op == 2 and users:
+            pid = users.pop(int(rng.integers(len(users))))
+            both(lambda: cpp.prefix_release(pid), lambda: ora.prefix_release(pid))
+        elif op == 3 and live:
+            p = live[int(rng.integers(len(live)))]
+            n = int(rng.integers(-1, ora.lens[p] + 2))
+            if both(lambda: cpp.seq_fork(p, nxt, n), lambda: ora.seq_fork(p, nxt, n)) is None:
+                live.append(nxt)
+            nxt += 1
+        elif op in (4, 5) and live:
+            ids = [live[i] for i in rng.integers(0, len(live), size=int(rng.integers(1, 6)))]
+            both(lambda: cpp.seq_append_slots(ids), lambda: ora.seq_append_slots(ids))
+        elif op == 6 and live:
+            s = live.pop(int(rng.integers(len(live))))
+            both(lambda: cpp.seq_free(s), lambda: ora.seq_free(s))
+        elif op == 7:
+            n = int(rng.integers(0, 3 * bs))
+            if both(lambda: cpp.seq_create(nxt, n), lambda: ora.seq_create(nxt, n)) is None:
+                live.append(nxt)
+            nxt += 1
+        else:
+            both(lambda: cpp.prefix_release(9999), lambda: ora.prefix_release(9999))
+        if step % 20 == 0:
+            same_state(cpp, ora)
+    same_state(cpp, ora)
+    c2, o2 = cpp.clone(), ora.clone()
+    same_state(c2, o2)

@@ -110,3 +110,60 @@ def test_random_operations_keep_pool_invariants():
         assert sorted(al.free_list()) == [b for b in range(64) if counts[b] == 0]
         for s, t in al.tables.items():
             assert len(t) == -(-al.lens[s] // 8)
+
+
+def test_p4_prefix_demo():
+    P.check_p4_prefix_demo()
+
+
+def test_prefix_random_operations_keep_pool_invariants():
+    """Random prefix, sequence and append operations: every block's count equals the
+    references held by sequences and prefix entries; sequences built on a prefix start
+    with its blocks and never get a copy-on-write pair for them."""
+    rng = np.random.default_rng(4)
+    NB, bs = 96, 8
+    al = AL.BlockAllocator(NB, bs, initial_free_order=rng.permutation(NB))
+    prompts = [list(rng.integers(0, 50, size=int(n))) for n in (0, 3, 8, 11, 16, 21)]
+    live, users, nxt = [], [], 0
+    for _ in range(3000):
+        op = int(rng.integers(0, 7))
+        try:
+            if op == 0:
+                pid, _ = al.prefix_get_or_create(prompts[int(rng.integers(len(prompts)))])
+                users.append(pid)
+            elif op == 1 and users:
+                pid = users[int(rng.integers(len(users)))]
+                al.seq_create_with_prefix(nxt, pid, int(rng.integers(0, 20)))
+                live.append(nxt)
+                nxt += 1
+            elif op == 2 and users:
+                al.prefix_release(users.pop(int(rng.integers(len(users)))))
+            elif op == 3 and live:
+                p = live[int(rng.integers(len(live)))]
+                al.seq_fork(p, nxt, int(rng.integers(-1, al.seq_len(p) + 1)))
+                live.append(nxt)
+                nxt += 1
+            elif op == 4 and live:
+                _, pairs = al.seq_append_slots([live[i] for i in rng.integers(0, len(live), size=3)])
+                entry_blocks = {b for e in al.entries.values() for b in e["blocks"]}
+                assert not [p for p in pairs if p[0] in entry_blocks and al.holes]
+            elif op == 5 and live:
+                al.seq_free(live.pop(int(rng.integers(len(live)))))
+            else:
+                al.seq_create(nxt, int(rng.integers(0, 30)))
+                live.append(nxt)
+                nxt += 1
+        except AL.AllocatorError as e:
+            assert e.code in (AL.NO_FREE_BLOCKS, AL.INVALID_ARG)
+        counts = np.zeros(NB, dtype=int)
+        for t in al.tables.values():
+            for b in t:
+                counts[b] += 1
+        for e in al.entries.values():
+            for b in e["blocks"]:
+                counts[b] += 1
+        assert list(counts) == al.refs
+        assert sorted(al.free_list()) == [b for b in range(NB) if counts[b] == 0]
+        for s, (lo, hi) in al.holes.items():
+            assert lo < hi <= al.lens[s] and hi % bs == 0
+        assert sum(e["users"] for e in al.entries.values()) == len(users)

@@ -244,3 +244,39 @@ def test_quant_table_mutant_is_caught(monkeypatch):
     monkeypatch.setattr(Q, "E4M3_TABLE", table)
     monkeypatch.setattr(Q, "_POS_VALUES", table[:0x7F])
     assert _caught(P.QUANT_PINS)
+
+
+# ----------------------------------------------------------------------------
+# prefix caching
+
+class _PrefixAlwaysMiss(AL.BlockAllocator):
+    def prefix_get_or_create(self, tokens):
+        self.prefixes.pop(tuple(int(t) for t in tokens), None)   # forgets every entry
+        return super().prefix_get_or_create(tokens)
+
+
+class _PrefixNoHole(AL.BlockAllocator):
+    def seq_create_with_prefix(self, seq_id, pid, own_tokens):
+        # own tokens continue right after the prefix, in the prefix's last block
+        e = self._entry(pid)
+        n = e["length"] + own_tokens
+        for b in e["blocks"]:
+            self.refs[b] += 1
+        extra = self._blocks_for(n) - len(e["blocks"])
+        self.tables[seq_id] = list(e["blocks"]) + [self._take() for _ in range(max(extra, 0))]
+        self.lens[seq_id] = n
+
+
+class _PrefixReleaseKeepsBlocks(AL.BlockAllocator):
+    def prefix_release(self, pid):
+        e = self._entry(pid)
+        e["users"] -= 1
+        if e["users"] <= 0:
+            del self.prefixes[e["key"]]
+            del self.entries[pid]
+
+
+@pytest.mark.parametrize("cls", [_PrefixAlwaysMiss, _PrefixNoHole, _PrefixReleaseKeepsBlocks])
+def test_prefix_mutant_is_caught(monkeypatch, cls):
+    monkeypatch.setattr(AL, "BlockAllocator", cls)
+    assert _caught([P.check_p4_prefix_demo]), f"no pin caught {cls.__name__}"
