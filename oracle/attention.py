@@ -29,6 +29,14 @@ What is computed, and where the pages define it:
   (m_p = max logit, l_p = sum exp(z - m_p), o_p = normalised partial output)
   per partition, and merges with the log-sum-exp rule.
 
+* Masked positions (masks = (lo, hi) per sequence): positions lo <= t < hi
+  hold no token and are left out of the softmax.  This serves a sequence
+  built on a cached prefix, whose own tokens start at the next block boundary
+  ("PagedAttention 实现细节" §3.2; the allocator's hole), and a sliding window
+  of the last W tokens ([0, n - W) masked; the window itself is the
+  "滑动窗口" of "PagedAttention 源码解析：KV Cache 怎么管理" §六, which lists it
+  as partly supported on Ascend).  A sequence with every token masked gives a
+  zero row, like an empty context.
 * 8-bit pools (quant = (fmt, k_scale, v_scale)): the pools hold codes and
   stand for decode(code) * scale (oracle/quant.py); the attention over those
   values is the same definition.
@@ -95,6 +103,12 @@ def gather_kv(key_cache, value_cache, table_row, num_tokens: int, kv_head: int, 
     return to_f64(K, dtype), to_f64(V, dtype)
 
 
+def keep_positions(num_tokens: int, lo: int, hi: int) -> np.ndarray:
+    """Positions t < num_tokens outside [lo, hi)."""
+    t = np.arange(num_tokens)
+    return t[(t < lo) | (t >= hi)]
+
+
 def kv_for(key_cache, value_cache, table_row, num_tokens: int, kv_head: int, dtype: str, quant=None):
     """float64 K, V of one sequence and KV head.  With quant = (fmt, k_scale,
     v_scale) the pools hold 8-bit codes and stand for decode(code) * scale
@@ -125,13 +139,14 @@ def attend(q64: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.nd
 
 
 def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scale: float,
-                 dtype: str, quant=None) -> np.ndarray:
+                 dtype: str, quant=None, masks=None) -> np.ndarray:
     """out[s, h] = attention of query[s, h] over the first context_lens[s] tokens of
     sequence s, gathered through block_tables[s] from the KV head h // G.
 
     query [S, H, D]; key_cache [NB, H_kv, bs, D]; value_cache [NB, H_kv, D, bs];
     block_tables [S, MB]; context_lens [S].  Returns float64 [S, H, D].
-    quant = (fmt, k_scale, v_scale) when the pools hold 8-bit codes.
+    quant = (fmt, k_scale, v_scale) when the pools hold 8-bit codes; masks = (lo, hi)
+    per-sequence lists of masked positions.
     """
     S, H, D = query.shape
     H_kv = key_cache.shape[1]
@@ -144,17 +159,23 @@ def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scal
         n = int(context_lens[s])
         for g in range(H_kv):
             K, V = kv_for(key_cache, value_cache, block_tables[s], n, g, dtype, quant)
+            if masks is not None:
+                keep = keep_positions(n, int(masks[0][s]), int(masks[1][s]))
+                K, V = K[keep], V[keep]
             for h in range(g * G, (g + 1) * G):
                 out[s, h] = attend(to_f64(query[s, h], dtype), K, V, sig)
     return out
 
 
 def decode_one(query, key_cache, value_cache, table_row, num_tokens: int, head: int,
-               num_heads: int, scale: float, dtype: str, quant=None) -> np.ndarray:
+               num_heads: int, scale: float, dtype: str, quant=None, mask=None) -> np.ndarray:
     """One output row out[s, head] (query = query[s], table_row = block_tables[s])."""
     H_kv = key_cache.shape[1]
     g = head // (num_heads // H_kv)
     K, V = kv_for(key_cache, value_cache, table_row, num_tokens, g, dtype, quant)
+    if mask is not None:
+        keep = keep_positions(num_tokens, int(mask[0]), int(mask[1]))
+        K, V = K[keep], V[keep]
     return attend(to_f64(query[head], dtype), K, V, scale_f64(scale))
 
 
@@ -163,10 +184,12 @@ def decode_one(query, key_cache, value_cache, table_row, num_tokens: int, head: 
 
 
 def partition_partials(q64: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
-                       partition_size: int):
+                       partition_size: int, mask=None):
     """Per partition p = tokens [p*PS, min((p+1)*PS, n)):
     m_p = max z, l_p = sum exp(z - m_p), o_p = sum exp(z - m_p) V / l_p.
-    Returns float64 arrays m [P], l [P], o [P, D] with P = ceil(n / PS).
+    Returns float64 arrays m [P], l [P], o [P, D] with P = ceil(n / PS).  With
+    mask = (lo, hi) the positions lo <= t < hi are left out; a partition with no
+    token left has m_p = -inf, l_p = 0, o_p = 0 (the merge gives it no weight).
     """
     n = K.shape[0]
     P = (n + partition_size - 1) // partition_size
@@ -176,6 +199,18 @@ def partition_partials(q64: np.ndarray, K: np.ndarray, V: np.ndarray, scale: flo
     o = np.zeros((P, D))
     for p in range(P):
         lo, hi = p * partition_size, min((p + 1) * partition_size, n)
+        if mask is not None:
+            t = np.arange(lo, hi)
+            t = t[(t < mask[0]) | (t >= mask[1])]
+            if t.size == 0:
+                m[p], l[p] = -np.inf, 0.0
+                continue
+            z = logits(q64, K[t], scale)
+            m[p] = np.max(z)
+            e = np.exp(z - m[p])
+            l[p] = np.sum(e)
+            o[p] = (e @ V[t]) / l[p]
+            continue
         z = logits(q64, K[lo:hi], scale)
         m[p] = np.max(z)
         e = np.exp(z - m[p])
@@ -186,16 +221,16 @@ def partition_partials(q64: np.ndarray, K: np.ndarray, V: np.ndarray, scale: flo
 
 def lse_merge(m: np.ndarray, l: np.ndarray, o: np.ndarray) -> np.ndarray:
     """Merge partition partials: M = max m_p, w_p = l_p exp(m_p - M),
-    out = sum_p w_p o_p / sum_p w_p.  No partitions -> zeros."""
-    if m.shape[0] == 0:
+    out = sum_p w_p o_p / sum_p w_p.  No partitions, or none with a token -> zeros."""
+    if m.shape[0] == 0 or not np.any(l > 0):
         return np.zeros(o.shape[1], dtype=np.float64)
     M = np.max(m)
-    w = l * np.exp(m - M)
+    w = np.where(l > 0, l * np.exp(m - M), 0.0)
     return (w @ o) / np.sum(w)
 
 
 def split_decode_partials(query, key_cache, value_cache, block_tables, context_lens, scale: float,
-                          dtype: str, partition_size: int, seqs=None, heads=None, quant=None):
+                          dtype: str, partition_size: int, seqs=None, heads=None, quant=None, masks=None):
     """Partials (m, l, o) for every (seq, head) in `seqs` x `heads`: a dict keyed by (s, h)."""
     S, H, D = query.shape
     H_kv = key_cache.shape[1]
@@ -212,5 +247,6 @@ def split_decode_partials(query, key_cache, value_cache, block_tables, context_l
             if g not in cache:
                 cache[g] = kv_for(key_cache, value_cache, block_tables[s], n, g, dtype, quant)
             K, V = cache[g]
-            res[(s, h)] = partition_partials(to_f64(query[s, h], dtype), K, V, sig, partition_size)
+            mask = None if masks is None else (int(masks[0][s]), int(masks[1][s]))
+            res[(s, h)] = partition_partials(to_f64(query[s, h], dtype), K, V, sig, partition_size, mask)
     return res

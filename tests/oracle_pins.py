@@ -532,3 +532,54 @@ def check_p4_prefix_demo():
     assert al.num_free_blocks() == NB and all(c == 0 for c in al.refs)
     _, hit = al.prefix_get_or_create(system)
     assert not hit
+
+
+# ----------------------------------------------------------------------------
+# masked positions (prefix hole, sliding window)
+
+def check_masked_against_sdpa(seed=61, S=4, H=8, Hkv=2, D=32, bs=16):
+    """Masked decode equals torch's SDPA on the contiguous cache with the masked rows
+    removed (independent of the oracle's gather), for a prefix hole, a sliding window, an
+    empty mask and a mask covering everything (zero row)."""
+    import torch
+    import torch.nn.functional as F
+
+    ctx = (46, 90, 33, 20)
+    q, kc, vc, tables, ctx, Ks, Vs = scatter_case(seed, S, H, Hkv, D, bs, ctx, "f32")
+    lo = [9, 0, 5, 0]            # hole [9, 16); window of the last 24; [5, 5) empty; all masked
+    hi = [16, 90 - 24, 5, 20]
+    scale = 1.0 / math.sqrt(D)
+    out = A.paged_decode(q, kc, vc, tables, ctx, scale, "f32", masks=(lo, hi))
+    for s in range(S):
+        keep = [t for t in range(ctx[s]) if not lo[s] <= t < hi[s]]
+        if not keep:
+            assert np.array_equal(out[s], np.zeros((H, D)))
+            continue
+        qt = torch.from_numpy(A.to_f64(q[s], "f32")).view(1, H, 1, D)
+        kt = torch.from_numpy(Ks[s][:, keep]).view(1, Hkv, len(keep), D)
+        vt = torch.from_numpy(Vs[s][:, keep]).view(1, Hkv, len(keep), D)
+        ref = F.scaled_dot_product_attention(qt, kt, vt, scale=float(np.float32(scale)),
+                                             enable_gqa=True).view(H, D).numpy()
+        assert np.max(np.abs(out[s] - ref)) <= 1e-12, f"seq {s}"
+
+
+def check_masked_split_merge(seed=67, n=700, D=16):
+    """Masked partials merge to the masked direct result for any partition size; a partition
+    wholly inside the mask is (-inf, 0, 0); everything masked merges to zeros."""
+    rng = np.random.default_rng(seed)
+    q, K, V = rng.standard_normal(D), rng.standard_normal((n, D)), rng.standard_normal((n, D))
+    scale = 0.3
+    for lo, hi in ((100, 480), (0, 650), (9, 16), (0, 0)):
+        keep = [t for t in range(n) if not lo <= t < hi]
+        direct = A.attend(q, K[keep], V[keep], scale)
+        for ps in (16, 100, 512):
+            m, l, o = A.partition_partials(q, K, V, scale, ps, (lo, hi))
+            assert np.max(np.abs(A.lse_merge(m, l, o) - direct)) <= 1e-12, (lo, hi, ps)
+            for p in range(len(m)):
+                if all(lo <= t < hi for t in range(p * ps, min((p + 1) * ps, n))):
+                    assert m[p] == -np.inf and l[p] == 0 and not o[p].any()
+    m, l, o = A.partition_partials(q, K, V, scale, 64, (0, n))
+    assert np.array_equal(A.lse_merge(m, l, o), np.zeros(D))
+
+
+MASK_PINS = [check_masked_against_sdpa, check_masked_split_merge]

@@ -99,3 +99,8 @@ def test_out_of_pool_table_entry_is_rejected():
     vc = np.ones((2, 1, 8, 16), dtype=np.float32)
     with pytest.raises(IndexError):
         A.paged_decode(q, kc, vc, np.array([[5]], dtype=np.int32), [3], 0.3, "f32")
+
+
+@pytest.mark.parametrize("pin", P.MASK_PINS, ids=[p.__name__ for p in P.MASK_PINS])
+def test_mask_pin(pin):
+    pin()

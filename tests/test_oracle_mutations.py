@@ -280,3 +280,33 @@ class _PrefixReleaseKeepsBlocks(AL.BlockAllocator):
 def test_prefix_mutant_is_caught(monkeypatch, cls):
     monkeypatch.setattr(AL, "BlockAllocator", cls)
     assert _caught([P.check_p4_prefix_demo]), f"no pin caught {cls.__name__}"
+
+
+# ----------------------------------------------------------------------------
+# masked positions
+
+def _keep_off_by_one(num_tokens, lo, hi):
+    import numpy as np
+    t = np.arange(num_tokens)
+    return t[(t < lo) | (t > hi)]
+
+
+def _keep_ignores_mask(num_tokens, lo, hi):
+    import numpy as np
+    return np.arange(num_tokens)
+
+
+def _merge_unguarded(m, l, o):
+    import numpy as np
+    if m.shape[0] == 0:
+        return np.zeros(o.shape[1])
+    M = np.max(m)
+    w = l * np.exp(m - M)
+    return (w @ o) / np.sum(w)
+
+
+@pytest.mark.parametrize("name,bad", [("keep_positions", _keep_off_by_one), ("keep_positions", _keep_ignores_mask),
+                                      ("lse_merge", _merge_unguarded)])
+def test_mask_mutant_is_caught(monkeypatch, name, bad):
+    monkeypatch.setattr(A, name, bad)
+    assert _caught(P.MASK_PINS), f"no pin caught {bad.__name__}"
