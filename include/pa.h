@@ -400,6 +400,30 @@ pa_status pa_lse_reduce(void* out, const void* workspace, size_t workspace_bytes
                         int32_t head_dim, int32_t max_context_len, int32_t partition_size,
                         pa_dtype dtype, void* stream);
 
+/* Decode with masked positions: pa_decode's definition over the tokens
+ * t < n = context_lens[s] that lie outside [mask_lo[s], mask_hi[s]).  This is
+ * the decode of a sequence built on a cached prefix ([IMPL] §3.2; the hole
+ * [n_p, P * bs) from pa_build_masks) and of a sliding window over the last W
+ * tokens ([SRC-1] §六 lists the window among the features: mask [0, n - W)).
+ *   mask_lo, mask_hi: device int32 [num_seqs], or both NULL (no mask); an
+ *     interval with mask_hi <= mask_lo masks nothing.
+ * Blocks whose positions below n are all masked are never read: their table
+ * entries may hold anything (a window's dropped blocks), and steps wholly
+ * inside the interval cost nothing when it covers the start of the context.
+ * A sequence with every token masked gets a zero row.  Pools are `dtype`
+ * (kv_dtype == dtype, the scales ignored) or 8-bit codes (kv_dtype
+ * PA_FP8_E4M3 / PA_INT8 with k_scale, v_scale, as pa_decode_quant).  Path,
+ * flags (PA_DECODE_CACHED_KV, PA_DECODE_SPLIT), workspace, *path and errors
+ * as in pa_decode_quant; under PA_DEBUG only blocks with an unmasked token
+ * are validated. */
+pa_status pa_decode_masked(void* out, const void* query, const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, const int32_t* mask_lo,
+                           const int32_t* mask_hi, const int32_t* seq_order, int32_t num_seqs, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                           int32_t num_blocks, int32_t max_context_len, float scale, float k_scale, float v_scale,
+                           pa_dtype dtype, pa_dtype kv_dtype, uint32_t flags, int32_t partition_size,
+                           void* workspace, size_t workspace_bytes, int32_t* path, void* stream);
+
 /* ======================================================================== *
  * Quantised (8-bit) KV cache                                                *
  * ======================================================================== *

@@ -109,15 +109,36 @@ def keep_positions(num_tokens: int, lo: int, hi: int) -> np.ndarray:
     return t[(t < lo) | (t >= hi)]
 
 
-def kv_for(key_cache, value_cache, table_row, num_tokens: int, kv_head: int, dtype: str, quant=None):
-    """float64 K, V of one sequence and KV head.  With quant = (fmt, k_scale,
-    v_scale) the pools hold 8-bit codes and stand for decode(code) * scale
-    (oracle/quant.py); otherwise they hold `dtype` values."""
+def gather_positions(key_cache, value_cache, table_row, positions: np.ndarray, kv_head: int):
+    """K and V rows (as stored) of the given token positions of one sequence and KV head:
+    position t is row t % bs of block table_row[t // bs].  Blocks holding none of the
+    positions are not looked at.  Returns arrays [len(positions), head_dim]."""
+    num_blocks, _, block_size, head_dim = key_cache.shape
+    positions = np.asarray(positions, dtype=np.int64)
+    phys = np.asarray(table_row, dtype=np.int64)[positions // block_size]
+    if np.any((phys < 0) | (phys >= num_blocks)):
+        raise IndexError("block table entry outside the pool")
+    off = positions % block_size
+    return key_cache[phys, kv_head, off, :], value_cache[phys, kv_head, :, off]
+
+
+def kv_for(key_cache, value_cache, table_row, num_tokens: int, kv_head: int, dtype: str, quant=None,
+           mask=None):
+    """float64 K, V of one sequence and KV head, one row per position that holds a token:
+    all t < num_tokens, or with mask = (lo, hi) those outside [lo, hi) (keep_positions).
+    With quant = (fmt, k_scale, v_scale) the pools hold 8-bit codes and stand for
+    decode(code) * scale (oracle/quant.py); otherwise they hold `dtype` values."""
+    if mask is None:
+        if quant is None:
+            return gather_kv(key_cache, value_cache, table_row, num_tokens, kv_head, dtype)
+        K, V = gather_rows(key_cache, value_cache, table_row, num_tokens, kv_head)
+    else:
+        K, V = gather_positions(key_cache, value_cache, table_row,
+                                keep_positions(num_tokens, int(mask[0]), int(mask[1])), kv_head)
     if quant is None:
-        return gather_kv(key_cache, value_cache, table_row, num_tokens, kv_head, dtype)
+        return to_f64(K, dtype), to_f64(V, dtype)
     fmt, k_scale, v_scale = quant
-    K8, V8 = gather_rows(key_cache, value_cache, table_row, num_tokens, kv_head)
-    return Q.dequantize(K8, k_scale, fmt), Q.dequantize(V8, v_scale, fmt)
+    return Q.dequantize(K, k_scale, fmt), Q.dequantize(V, v_scale, fmt)
 
 
 def logits(q64: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:
@@ -158,10 +179,8 @@ def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scal
     for s in range(S):
         n = int(context_lens[s])
         for g in range(H_kv):
-            K, V = kv_for(key_cache, value_cache, block_tables[s], n, g, dtype, quant)
-            if masks is not None:
-                keep = keep_positions(n, int(masks[0][s]), int(masks[1][s]))
-                K, V = K[keep], V[keep]
+            mask = None if masks is None else (masks[0][s], masks[1][s])
+            K, V = kv_for(key_cache, value_cache, block_tables[s], n, g, dtype, quant, mask)
             for h in range(g * G, (g + 1) * G):
                 out[s, h] = attend(to_f64(query[s, h], dtype), K, V, sig)
     return out
@@ -172,10 +191,7 @@ def decode_one(query, key_cache, value_cache, table_row, num_tokens: int, head: 
     """One output row out[s, head] (query = query[s], table_row = block_tables[s])."""
     H_kv = key_cache.shape[1]
     g = head // (num_heads // H_kv)
-    K, V = kv_for(key_cache, value_cache, table_row, num_tokens, g, dtype, quant)
-    if mask is not None:
-        keep = keep_positions(num_tokens, int(mask[0]), int(mask[1]))
-        K, V = K[keep], V[keep]
+    K, V = kv_for(key_cache, value_cache, table_row, num_tokens, g, dtype, quant, mask)
     return attend(to_f64(query[head], dtype), K, V, scale_f64(scale))
 
 
@@ -184,38 +200,31 @@ def decode_one(query, key_cache, value_cache, table_row, num_tokens: int, head: 
 
 
 def partition_partials(q64: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
-                       partition_size: int, mask=None):
-    """Per partition p = tokens [p*PS, min((p+1)*PS, n)):
-    m_p = max z, l_p = sum exp(z - m_p), o_p = sum exp(z - m_p) V / l_p.
-    Returns float64 arrays m [P], l [P], o [P, D] with P = ceil(n / PS).  With
-    mask = (lo, hi) the positions lo <= t < hi are left out; a partition with no
-    token left has m_p = -inf, l_p = 0, o_p = 0 (the merge gives it no weight).
+                       partition_size: int, positions=None, num_tokens=None):
+    """Per partition p = positions [p*PS, min((p+1)*PS, n)):
+    m_p = max z, l_p = sum exp(z - m_p), o_p = sum exp(z - m_p) V / l_p over its tokens.
+    Row i of K, V is the token at positions[i] (default: row i is position i, n = rows);
+    num_tokens = n sets the partition count P = ceil(n / PS).  A partition holding no
+    token (all its positions masked) has m_p = -inf, l_p = 0, o_p = 0: the merge gives it
+    no weight.  Returns float64 arrays m [P], l [P], o [P, D].
     """
-    n = K.shape[0]
+    pos = np.arange(K.shape[0]) if positions is None else np.asarray(positions)
+    n = K.shape[0] if num_tokens is None else num_tokens
     P = (n + partition_size - 1) // partition_size
     D = V.shape[1]
     m = np.zeros(P)
     l = np.zeros(P)
     o = np.zeros((P, D))
     for p in range(P):
-        lo, hi = p * partition_size, min((p + 1) * partition_size, n)
-        if mask is not None:
-            t = np.arange(lo, hi)
-            t = t[(t < mask[0]) | (t >= mask[1])]
-            if t.size == 0:
-                m[p], l[p] = -np.inf, 0.0
-                continue
-            z = logits(q64, K[t], scale)
-            m[p] = np.max(z)
-            e = np.exp(z - m[p])
-            l[p] = np.sum(e)
-            o[p] = (e @ V[t]) / l[p]
+        rows = np.nonzero((pos >= p * partition_size) & (pos < (p + 1) * partition_size))[0]
+        if rows.size == 0:
+            m[p], l[p] = -np.inf, 0.0
             continue
-        z = logits(q64, K[lo:hi], scale)
+        z = logits(q64, K[rows], scale)
         m[p] = np.max(z)
         e = np.exp(z - m[p])
         l[p] = np.sum(e)
-        o[p] = (e @ V[lo:hi]) / l[p]
+        o[p] = (e @ V[rows]) / l[p]
     return m, l, o
 
 
@@ -241,12 +250,13 @@ def split_decode_partials(query, key_cache, value_cache, block_tables, context_l
     res = {}
     for s in seqs:
         n = int(context_lens[s])
+        mask = None if masks is None else (int(masks[0][s]), int(masks[1][s]))
+        pos = np.arange(n) if mask is None else keep_positions(n, *mask)
         cache = {}
         for h in heads:
             g = h // G
             if g not in cache:
-                cache[g] = kv_for(key_cache, value_cache, block_tables[s], n, g, dtype, quant)
+                cache[g] = kv_for(key_cache, value_cache, block_tables[s], n, g, dtype, quant, mask)
             K, V = cache[g]
-            mask = None if masks is None else (int(masks[0][s]), int(masks[1][s]))
-            res[(s, h)] = partition_partials(to_f64(query[s, h], dtype), K, V, sig, partition_size, mask)
+            res[(s, h)] = partition_partials(to_f64(query[s, h], dtype), K, V, sig, partition_size, pos, n)
     return res

@@ -7,7 +7,7 @@ built (python paged_kv_cache_333_amd/build.py): there is no fallback.
 
 Names follow the C ABI in include/pa.h:
   pa_reshape_and_cache, pa_copy_blocks, pa_upload, pa_decode, pa_decode_split, pa_decode_auto,
-  pa_decode_append, pa_reshape_and_cache_quant, pa_decode_quant,
+  pa_decode_append, pa_reshape_and_cache_quant, pa_decode_quant, pa_decode_masked,
   pa_decode_split_workspace_bytes, pa_lse_reduce, and the allocator verbs as
   methods of `Allocator` (pa_seq_create -> Allocator.seq_create, ...).
 """
@@ -106,6 +106,8 @@ _PROTOS = {
     "pa_lse_reduce": (_i32, [_vp, _vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_reshape_and_cache_quant": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                           _f32, _f32, _vp]),
+    "pa_decode_masked": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                _i32, _i32, _f32, _f32, _f32, _i32, _i32, _u32, _i32, _vp, _sz, _pi32, _vp]),
     "pa_decode_quant": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                _i32, _f32, _f32, _f32, _i32, _i32, _u32, _i32, _vp, _sz, _pi32, _vp]),
     "pa_status_string": (C.c_char_p, [_i32]),
@@ -320,6 +322,28 @@ def pa_decode_quant(out, query, key_cache, value_cache, block_tables, context_le
                                max_context_len, scale, k_scale, v_scale, _dtype_code(query),
                                _kv_format(key_cache, kv_format), flags, partition_size, _opt(workspace), nbytes,
                                C.byref(path), _stream(stream)), "pa_decode_quant")
+    return "split" if path.value == 1 else "single"
+
+
+def pa_decode_masked(out, query, key_cache, value_cache, block_tables, context_lens, mask_lo, mask_hi,
+                     max_context_len: int, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                     kv_format=None, partition_size: int = 512, workspace=None, split: bool = False, stream=None,
+                     seq_order=None, cached_kv: bool = False) -> str:
+    """Decode leaving out positions mask_lo[s] <= t < mask_hi[s] (device int32 [S] each, or both
+    None): a prefix hole or the tokens before a sliding window.  Pools of the query's dtype, or
+    8-bit pools (K = code * k_scale, V = code * v_scale).  Single pass without a workspace; split
+    with split=True; else the pa_decode_auto rule.  Returns "single" or "split"."""
+    S, H, D = query.shape
+    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache)
+    kv = _kv_format(key_cache, kv_format) if key_cache.element_size() == 1 else _dtype_code(key_cache)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    flags = (PA_DECODE_CACHED_KV if cached_kv else 0) | (PA_DECODE_SPLIT if split else 0)
+    path = C.c_int32(-1)
+    _check(lib.pa_decode_masked(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+                                _ptr(context_lens), _opt(mask_lo), _opt(mask_hi), _opt(seq_order), S, H, H_kv, D,
+                                bs, block_tables.shape[1], NB, max_context_len, scale, k_scale, v_scale,
+                                _dtype_code(query), kv, flags, partition_size, _opt(workspace), nbytes,
+                                C.byref(path), _stream(stream)), "pa_decode_masked")
     return "split" if path.value == 1 else "single"
 
 

@@ -2,6 +2,7 @@
 // PA_DEBUG checks of device-side indices, and dispatch to the kernels.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -96,6 +97,11 @@ pa_status debug_check_tables(const pa::DecodeArgs& a, hipStream_t st) {
   pa_status s = fetch(ctx, a.context_lens, a.num_seqs, st);
   if (s == PA_OK) s = fetch(tab, a.block_tables, static_cast<size_t>(a.num_seqs) * a.max_blocks_per_seq, st);
   if (s != PA_OK) return s;
+  std::vector<int32_t> mlo, mhi;  // masked positions: blocks wholly inside are never read
+  if (a.mask_lo) {
+    if ((s = fetch(mlo, a.mask_lo, a.num_seqs, st)) != PA_OK) return s;
+    if ((s = fetch(mhi, a.mask_hi, a.num_seqs, st)) != PA_OK) return s;
+  }
   const int64_t lim = len_limit(a);
   for (int32_t i = 0; i < a.num_seqs; ++i) {
     if (ctx[i] < 0 || ctx[i] > lim)
@@ -103,6 +109,11 @@ pa_status debug_check_tables(const pa::DecodeArgs& a, hipStream_t st) {
                                         " outside [0, " + std::to_string(lim) + "]");
     const int32_t nb = (ctx[i] + a.block_size - 1) / a.block_size;
     for (int32_t j = 0; j < nb; ++j) {
+      if (a.mask_lo && mlo[i] < mhi[i]) {
+        const int64_t first = static_cast<int64_t>(j) * a.block_size;
+        const int64_t stop = std::min<int64_t>(first + a.block_size, ctx[i]);
+        if (first >= mlo[i] && stop <= mhi[i]) continue;
+      }
       const int32_t b = tab[static_cast<size_t>(i) * a.max_blocks_per_seq + j];
       if (b < 0 || b >= a.num_blocks)
         return fail(PA_ERR_BAD_TABLE, "block_tables[" + std::to_string(i) + "][" + std::to_string(j) +
@@ -422,6 +433,54 @@ pa_status pa_decode_append(void* out, const void* query, const void* key, const 
   }
   return finish(pa::launch_decode_append(a, key, value, slot_mapping, split ? &ws : nullptr, st), st,
                 "pa_decode_append");
+}
+
+pa_status pa_decode_masked(void* out, const void* query, const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, const int32_t* mask_lo,
+                           const int32_t* mask_hi, const int32_t* seq_order, int32_t num_seqs, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                           int32_t num_blocks, int32_t max_context_len, float scale, float k_scale, float v_scale,
+                           pa_dtype dtype, pa_dtype kv_dtype, uint32_t flags, int32_t partition_size,
+                           void* workspace, size_t workspace_bytes, int32_t* path, void* stream) {
+  pa::DecodeArgs a = pack(out, query, key_cache, value_cache, block_tables, context_lens, seq_order, num_seqs,
+                          num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                          max_context_len, scale, dtype, flags);
+  a.kv_dtype = kv_dtype;
+  pa_status s = check_decode_args(a);
+  if (s != PA_OK) return s;
+  if (is_code_type(kv_dtype)) {
+    if (dtype != PA_F16 && dtype != PA_BF16)
+      return fail(PA_ERR_UNSUPPORTED, "8-bit pools decode with PA_F16 or PA_BF16 queries");
+    if ((s = check_scales(k_scale, v_scale)) != PA_OK) return s;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+  } else if (kv_dtype != dtype) {
+    return fail(PA_ERR_UNSUPPORTED, "kv_dtype must equal dtype, or be PA_FP8_E4M3 / PA_INT8");
+  }
+  if ((mask_lo == nullptr) != (mask_hi == nullptr))
+    return fail(PA_ERR_INVALID_ARG, "mask_lo and mask_hi must both be given or both be NULL");
+  a.mask_lo = mask_lo;
+  a.mask_hi = mask_hi;
+  if (flags & ~uint32_t(PA_DECODE_CACHED_KV | PA_DECODE_SPLIT))
+    return fail(PA_ERR_INVALID_ARG, "unknown flag bits");
+  a.flags = flags & PA_DECODE_CACHED_KV;
+  bool split = false;
+  if (flags & PA_DECODE_SPLIT) {
+    if (partition_size <= 0 || partition_size % block_size || partition_size > 4096)
+      return fail(PA_ERR_INVALID_ARG, "partition_size must be a multiple of block_size, at most 4096");
+    split = true;
+  } else {
+    split = choose_split(a, partition_size, workspace, workspace_bytes);
+  }
+  if (path) *path = split ? 1 : 0;
+  if (num_seqs == 0) return PA_OK;
+  pa::SplitLayout ws;
+  if (split && (s = make_layout(workspace, workspace_bytes, num_seqs, num_heads, head_dim, max_context_len,
+                                partition_size, &ws)) != PA_OK)
+    return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_mode() && (s = debug_check_tables(a, st)) != PA_OK) return s;
+  return finish(split ? pa::launch_decode_split(a, ws, st) : pa::launch_decode(a, st), st, "pa_decode_masked");
 }
 
 pa_status pa_decode_quant(void* out, const void* query, const void* key_cache, const void* value_cache,

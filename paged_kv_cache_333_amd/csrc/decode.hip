@@ -58,6 +58,8 @@ DecodeParams make_params(const DecodeArgs& x) {
   p.tables = x.block_tables;
   p.ctx = x.context_lens;
   p.order = x.seq_order;
+  p.mask_lo = x.mask_lo;
+  p.mask_hi = x.mask_hi;
   p.num_seqs = x.num_seqs;
   p.num_heads = x.num_heads;
   p.num_kv_heads = x.num_kv_heads;

@@ -45,6 +45,14 @@
 // only on logical token positions, so relabelling physical blocks gives
 // bit-identical results.
 //
+// Masked positions.  With mask arrays, positions mask_lo[s] <= t < mask_hi[s]
+// are left out: their logits are -inf and their value rows are zeroed, a step
+// wholly inside the interval is not visited (nor its block ids checked), and
+// when the interval covers the start of the range the walk starts at the first
+// step that reaches past it (a sliding window skips everything before it).
+// A block wholly inside the interval is never read, so its table entry may be
+// anything (a window's dropped blocks).  No token left: a zero row.
+//
 // Invalid device data never leads to an out-of-bounds access: a block id
 // outside the pool is not read and turns the affected outputs into NaN; a
 // context length outside its bound does the same.
@@ -69,6 +77,10 @@ struct DecodeParams {
   const int32_t* tables;
   const int32_t* ctx;
   const int32_t* order;  // optional launch order of the sequences (a permutation), or null
+  // optional per-sequence masked positions [mask_lo, mask_hi) (a prefix hole, or the
+  // tokens before a sliding window), or null; not used by the fused write
+  const int32_t* mask_lo;
+  const int32_t* mask_hi;
   float* ws_m;
   float* ws_l;
   float* ws_o;
@@ -203,6 +215,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int kvh = h0 / (a.num_heads / a.num_kv_heads);
   const int nctx = a.ctx[s];
   const bool bad_len = nctx < 0 || nctx > a.len_limit;
+  int mlo = 0, mhi = 0;  // masked positions; empty unless mask_lo < mask_hi
+  if (!APPEND && a.mask_lo) {
+    mlo = a.mask_lo[s];
+    mhi = a.mask_hi[s];
+    if (mhi <= mlo) mlo = mhi = 0;
+  }
 
   // Single pass: the workgroup's waves share the context, wave w taking steps
   // w, w + kWaves, ...  Split: each wave owns one partition outright (partition
@@ -225,7 +243,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       return;
     }
   }
-  const int st_first = SPLIT ? 0 : wave;
+  // steps wholly inside a mask that covers the start of the range are skipped
+  const int st_skip = mlo <= t_begin && mhi > t_begin ? (min(mhi, t_end) - t_begin) / TS : 0;
+  const int st_first = st_skip + (SPLIT ? 0 : wave);
   const int b_end = (t_end + BS - 1) / BS;
   const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.max_blocks;
 
@@ -284,18 +304,25 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       ids = fetch_ids(st);
       k_ids = 0;
     }
+    // the step meets the masked interval / lies wholly inside it (wave-uniform)
+    const int t_stop = min(t0 + TS, t_end);
+    const bool meets = t0 < mhi && t_stop > mlo;
+    const bool inside = t0 >= mlo && t_stop <= mhi;
     int32_t ph[NBS];
     bool skip = false;
 #pragma unroll
     for (int i = 0; i < NBS; ++i) {
       ph[i] = k_ids < 0 ? ph_first[i] : __builtin_amdgcn_readlane(ids, NBS * k_ids + i);
-      if (b0 + i < b_end) {
+      const int blk = b0 + i;
+      const bool dead = blk >= b_end || (meets && blk * BS >= mlo && min((blk + 1) * BS, t_end) <= mhi);
+      if (!dead) {
         if (static_cast<uint32_t>(ph[i]) >= static_cast<uint32_t>(a.num_blocks)) skip = true;
       } else {
-        ph[i] = -1;  // past the context: masked below, read from block ph[0]
+        ph[i] = -1;  // no token of this block is used: masked below, read from a live block
       }
     }
     ++k_ids;
+    if (inside) continue;
     if (skip) {
       bad = 1;
       continue;
@@ -311,9 +338,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       }
     }
+    {
+      int32_t live = ph[0];
 #pragma unroll
-    for (int i = 1; i < NBS; ++i)
-      if (ph[i] < 0) ph[i] = ph[0];
+      for (int i = 1; i < NBS; ++i) live = live < 0 ? ph[i] : live;
+#pragma unroll
+      for (int i = 0; i < NBS; ++i) ph[i] = ph[i] < 0 ? live : ph[i];
+    }
     // Physical block of step block bi (lane-dependent), by selects on the bits
     // of bi (a compare chain would be turned into an indexed load from a
     // stack copy of ph).
@@ -377,8 +408,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
         for (int v = 0; v < KV; ++v) c[tau] = mma(T{}, kr[tau][v], qv[v], c[tau]);
       }
     }
-    // c[tau][j]: logit of token t0 + TPL q + 4 tau + j for head n % GT
-    const bool tail = t0 + TS > t_end;
+    // c[tau][j]: logit of token t0 + TPL q + 4 tau + j for head n % GT.  In a
+    // ragged step (the context ends, or the masked interval starts or ends,
+    // inside it) bit e of `use` says whether the lane's token TPL q + e counts.
+    const bool ragged = t0 + TS > t_end || meets;
+    uint32_t use = ~0u;
+    if (ragged) {
+      const int base = t0 + TPL * q;
+      use = low_bits(t_end - base) & ~(low_bits(mhi - base) & ~low_bits(mlo - base));
+    }
     float z[TPL];
     float mx = kNegInf;
 #pragma unroll
@@ -386,7 +424,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float v = c[tau][j] * a.scale_log2;
-        const bool ok = !tail || t0 + TPL * q + 4 * tau + j < t_end;
+        const bool ok = !ragged || ((use >> (4 * tau + j)) & 1u);
         z[4 * tau + j] = ok ? v : kNegInf;
         mx = fmaxf(mx, z[4 * tau + j]);
       }
@@ -426,8 +464,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     u32x4 phi[PV], plo[PV];
 #pragma unroll
     for (int u = 0; u < PV; ++u) pack_p(T{}, p + EPL * u, phi[u], plo[u]);
-    if (tail) {
-      const u32x4 keep = keep_mask(S{}, t_end - (t0 + TPL * q));
+    if (ragged) {
+      const u32x4 keep = bits_mask(S{}, use);
 #pragma unroll
       for (int v = 0; v < NV; ++v) vr[v] &= keep;
     }
@@ -476,7 +514,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       if (g < GT) {
         float* o = a.ws_o + ((sh0 + g) * a.num_parts + part) * D + n;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) o[16 * v] = bad ? qnan : acc[v][j] / lg[j] * a.v_scale;
+        for (int v = 0; v < NV; ++v)
+          o[16 * v] = bad ? qnan : (lg[j] == 0.f ? 0.f : acc[v][j] / lg[j] * a.v_scale);  // 0: all masked
       }
     }
     if (q == 0 && n < GT) {
@@ -573,7 +612,8 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float*
   for (int k = 0; k < DPL; ++k) A[k] = 0.f;
 #pragma unroll 4
   for (int p = wave; p < np; p += 4) {
-    const float w = lp[p] * fast_exp2((mp[p] - M) * kLog2e);
+    // a partition with no token (l = 0, m = -inf: all masked) has no weight
+    const float w = lp[p] == 0.f ? 0.f : lp[p] * fast_exp2((mp[p] - M) * kLog2e);
     L += w;
     const float* o = op + static_cast<int64_t>(p) * D + lane * DPL;
 #pragma unroll
@@ -587,7 +627,7 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float*
     const int d = threadIdx.x;
     const float Ls = (sm_l[0] + sm_l[1]) + (sm_l[2] + sm_l[3]);
     const float As = (sm_a[0][d] + sm_a[1][d]) + (sm_a[2][d] + sm_a[3][d]);
-    store_elem(T{}, out, sh * D + d, np == 0 ? 0.f : As / Ls);
+    store_elem(T{}, out, sh * D + d, Ls == 0.f ? 0.f : As / Ls);
   }
 }
 

@@ -126,31 +126,35 @@ __device__ __forceinline__ void pack_p(TBF16, const float* p, u32x4& hi, u32x4& 
   lo = __builtin_bit_cast(u32x4, l);
 }
 
-// Bit mask keeping the first `keep` elements of a chunk (keep may be < 0 or > EPL).
-__device__ __forceinline__ u32x4 keep_mask(TF32, int keep) {
-  return u32x4{0 < keep ? ~0u : 0u, 1 < keep ? ~0u : 0u, 2 < keep ? ~0u : 0u, 3 < keep ? ~0u : 0u};
+// Low k bits set (k clamped to [0, 32]).
+__device__ __forceinline__ uint32_t low_bits(int k) { return k <= 0 ? 0u : k >= 32 ? ~0u : (1u << k) - 1u; }
+
+// Element mask of a chunk from a bit set: element e is kept iff bit e is set.
+__device__ __forceinline__ u32x4 bits_mask(TF32, uint32_t bits) {
+  return u32x4{bits & 1u ? ~0u : 0u, bits & 2u ? ~0u : 0u, bits & 4u ? ~0u : 0u, bits & 8u ? ~0u : 0u};
 }
-__device__ __forceinline__ u32x4 keep_mask_16(int keep) {
+__device__ __forceinline__ u32x4 bits_mask_16(uint32_t bits) {
   u32x4 m;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) m[w] = (2 * w < keep ? 0x0000ffffu : 0u) | (2 * w + 1 < keep ? 0xffff0000u : 0u);
+  for (int w = 0; w < 4; ++w)
+    m[w] = ((bits >> (2 * w)) & 1u ? 0x0000ffffu : 0u) | ((bits >> (2 * w + 1)) & 1u ? 0xffff0000u : 0u);
   return m;
 }
-__device__ __forceinline__ u32x4 keep_mask(TF16, int keep) { return keep_mask_16(keep); }
-__device__ __forceinline__ u32x4 keep_mask(TBF16, int keep) { return keep_mask_16(keep); }
-
-// Bit mask keeping the first `keep` codes of a chunk of 8-bit codes.
-__device__ __forceinline__ u32x4 keep_mask_8(int keep) {
+__device__ __forceinline__ u32x4 bits_mask(TF16, uint32_t bits) { return bits_mask_16(bits); }
+__device__ __forceinline__ u32x4 bits_mask(TBF16, uint32_t bits) { return bits_mask_16(bits); }
+__device__ __forceinline__ u32x4 bits_mask_8(uint32_t bits) {
   u32x4 m;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const int k = keep - 4 * w;
-    m[w] = k >= 4 ? ~0u : k <= 0 ? 0u : (1u << (8 * k)) - 1u;
+    uint32_t x = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x |= (bits >> (4 * w + i)) & 1u ? 0xffu << (8 * i) : 0u;
+    m[w] = x;
   }
   return m;
 }
-__device__ __forceinline__ u32x4 keep_mask(TE4M3, int keep) { return keep_mask_8(keep); }
-__device__ __forceinline__ u32x4 keep_mask(TI8, int keep) { return keep_mask_8(keep); }
+__device__ __forceinline__ u32x4 bits_mask(TE4M3, uint32_t bits) { return bits_mask_8(bits); }
+__device__ __forceinline__ u32x4 bits_mask(TI8, uint32_t bits) { return bits_mask_8(bits); }
 
 // ---------------------------------------------------------------------------
 // 8-bit codes -> fp16/bf16, exactly.  widen() turns one chunk of 16 codes into

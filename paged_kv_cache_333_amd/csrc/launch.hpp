@@ -26,6 +26,9 @@ struct DecodeArgs {
   pa_dtype kv_dtype = PA_F32;
   float k_scale = 1.0f;
   float v_scale = 1.0f;
+  // optional per-sequence masked positions [mask_lo, mask_hi)
+  const int32_t* mask_lo = nullptr;
+  const int32_t* mask_hi = nullptr;
 };
 
 // The three fp32 arrays of the split workspace (see pa_decode_split_workspace_bytes).

@@ -19,7 +19,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 36
+    assert len(names) == 37
     for n in names:
         assert hasattr(pa.lib, n), n
         assert C.cast(getattr(pa.lib, n), C.c_void_p).value
@@ -157,3 +157,23 @@ def test_copy_blocks_accepts_8bit_pools():
     for kv in (pa.PA_FP8_E4M3, pa.PA_INT8):
         assert pa.lib.pa_copy_blocks(16, 16, 16, 0, 8, 2, 64, 16, kv, None) == 0
         assert pa.lib.pa_copy_blocks(16, 16, 16, 0, 8, 2, 96, 16, kv, None) == 5
+
+
+def test_decode_masked_validation_rejects_before_launch():
+    def call(**kw):
+        a = dict(lo=16, hi=16, S=0, dt=F, kv=F, ks=1.0, vs=1.0, flags=0, ps=512)
+        a.update(kw)
+        path = C.c_int32(-7)
+        st = pa.lib.pa_decode_masked(16, 16, 16, 16, 16, 16, a["lo"], a["hi"], None, a["S"], 32, 32, 128, 16, 4, 8,
+                                     64, 0.1, a["ks"], a["vs"], a["dt"], a["kv"], a["flags"], a["ps"], None, 0,
+                                     C.byref(path), None)
+        return st, path.value
+    assert call() == (0, 0)
+    assert call(lo=None, hi=None) == (0, 0)
+    assert call(lo=None)[0] == 1                      # both or neither
+    assert call(kv=pa.PA_BF16)[0] == 5                # pools must match the query unless 8-bit
+    assert call(kv=pa.PA_FP8_E4M3, ks=0.5, vs=0.5) == (0, 0)
+    assert call(kv=pa.PA_INT8, dt=pa.PA_F32)[0] == 5
+    assert call(kv=pa.PA_INT8, ks=0.0)[0] == 1
+    assert call(flags=8)[0] == 1
+    assert call(flags=pa.PA_DECODE_SPLIT) == (0, 1)

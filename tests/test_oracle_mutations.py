@@ -202,10 +202,10 @@ def _dequantize_divides(codes, scale, fmt):
     return Q.decode(codes, fmt) / float(np.float32(scale))
 
 
-def _kv_swapped_scales(kc, vc, row, n, g, dtype, quant=None, _orig=A.kv_for):
+def _kv_swapped_scales(kc, vc, row, n, g, dtype, quant=None, mask=None, _orig=A.kv_for):
     if quant is not None:
         quant = (quant[0], quant[2], quant[1])
-    return _orig(kc, vc, row, n, g, dtype, quant)
+    return _orig(kc, vc, row, n, g, dtype, quant, mask)
 
 
 def _int8_ties_away(y32):
