@@ -37,6 +37,12 @@ What is computed, and where the pages define it:
   "滑动窗口" of "PagedAttention 源码解析：KV Cache 怎么管理" §六, which lists it
   as partly supported on Ascend).  A sequence with every token masked gives a
   zero row, like an empty context.
+* Several query tokens per sequence (paged_decode_multi): the query rows of
+  sequence s are query_start[s] .. query_start[s+1] - 1, its last L tokens,
+  whose K/V are already in the cache; query token i of the span sits at
+  position n - L + i and attends to positions 0 .. n - L + i (causal).  This
+  is the verification pass of speculative decoding, which the xdnf.cn article
+  (§6.3) combines with paging; one query token per sequence is plain decode.
 * 8-bit pools (quant = (fmt, k_scale, v_scale)): the pools hold codes and
   stand for decode(code) * scale (oracle/quant.py); the attention over those
   values is the same definition.
@@ -260,3 +266,32 @@ def split_decode_partials(query, key_cache, value_cache, block_tables, context_l
             K, V = cache[g]
             res[(s, h)] = partition_partials(to_f64(query[s, h], dtype), K, V, sig, partition_size, pos, n)
     return res
+
+
+# ----------------------------------------------------------------------------
+# several query tokens per sequence
+
+
+def paged_decode_multi(query, key_cache, value_cache, block_tables, context_lens, query_start, scale: float,
+                       dtype: str, quant=None) -> np.ndarray:
+    """out[r, h] for every query row r = query_start[s] + i (i < L = query_start[s+1] -
+    query_start[s]): attention of query[r, h] over positions 0 .. n - L + i of sequence s
+    (n = context_lens[s]).  query [T, H, D]; returns float64 [T, H, D]."""
+    T, H, D = query.shape
+    H_kv = key_cache.shape[1]
+    G = H // H_kv
+    sig = scale_f64(scale)
+    out = np.zeros((T, H, D), dtype=np.float64)
+    for s in range(len(context_lens)):
+        n = int(context_lens[s])
+        r0, r1 = int(query_start[s]), int(query_start[s + 1])
+        L = r1 - r0
+        if L > n:
+            raise ValueError("a sequence has more query tokens than cached tokens")
+        for g in range(H_kv):
+            K, V = kv_for(key_cache, value_cache, block_tables[s], n, g, dtype, quant)
+            for i in range(L):
+                lim = n - L + i + 1
+                for h in range(g * G, (g + 1) * G):
+                    out[r0 + i, h] = attend(to_f64(query[r0 + i, h], dtype), K[:lim], V[:lim], sig)
+    return out

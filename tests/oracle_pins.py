@@ -583,3 +583,51 @@ def check_masked_split_merge(seed=67, n=700, D=16):
 
 
 MASK_PINS = [check_masked_against_sdpa, check_masked_split_merge]
+
+
+# ----------------------------------------------------------------------------
+# several query tokens per sequence
+
+def check_multi_against_sdpa(seed=71, H=8, Hkv=2, D=32, bs=16):
+    """Each sequence's span of query tokens against torch's float64 SDPA with an explicit
+    boolean mask (key t allowed for query i iff t <= n - L + i), on the contiguous cache."""
+    import torch
+    import torch.nn.functional as F
+
+    ctx = (40, 7, 100, 16)
+    spans = (4, 1, 7, 16)            # the last span covers the whole context
+    q, kc, vc, tables, ctx, Ks, Vs = scatter_case(seed, len(ctx), H, Hkv, D, bs, ctx, "f32")
+    qstart = np.concatenate([[0], np.cumsum(spans)]).astype(np.int32)
+    qm = normal_host((int(qstart[-1]), H, D), seed + 9, "f32")
+    scale = 0.2
+    out = A.paged_decode_multi(qm, kc, vc, tables, ctx, qstart, scale, "f32")
+    for s, (n, L) in enumerate(zip(ctx, spans)):
+        rows = slice(int(qstart[s]), int(qstart[s + 1]))
+        qt = torch.from_numpy(qm[rows].astype(np.float64)).permute(1, 0, 2).unsqueeze(0)   # [1, H, L, D]
+        kt = torch.from_numpy(Ks[s]).unsqueeze(0)
+        vt = torch.from_numpy(Vs[s]).unsqueeze(0)
+        allowed = torch.tensor([[t <= n - L + i for t in range(n)] for i in range(L)])
+        ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=allowed, scale=float(np.float32(scale)),
+                                             enable_gqa=True)
+        ref = ref.squeeze(0).permute(1, 0, 2).numpy()
+        assert np.max(np.abs(out[rows] - ref)) <= 1e-12, f"seq {s}"
+
+
+def check_multi_reduces_to_decode(seed=73):
+    """One query token per sequence is plain decode; the last token of any span sees the
+    whole context, so it equals plain decode of that token."""
+    H, Hkv, D, bs = 4, 4, 16, 16
+    ctx = (1, 30, 64)
+    q, kc, vc, tables, ctx, _, _ = scatter_case(seed, 3, H, Hkv, D, bs, ctx, "f32")
+    ones = np.arange(4, dtype=np.int32)
+    assert np.array_equal(A.paged_decode_multi(q, kc, vc, tables, ctx, ones, 0.25, "f32"),
+                          A.paged_decode(q, kc, vc, tables, ctx, 0.25, "f32"))
+    spans = (1, 5, 9)
+    qstart = np.concatenate([[0], np.cumsum(spans)]).astype(np.int32)
+    qm = normal_host((int(qstart[-1]), H, D), seed + 1, "f32")
+    out = A.paged_decode_multi(qm, kc, vc, tables, ctx, qstart, 0.25, "f32")
+    last = qm[qstart[1:] - 1]
+    assert np.array_equal(out[qstart[1:] - 1], A.paged_decode(last, kc, vc, tables, ctx, 0.25, "f32"))
+
+
+MULTI_PINS = [check_multi_against_sdpa, check_multi_reduces_to_decode]

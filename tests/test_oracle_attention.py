@@ -104,3 +104,8 @@ def test_out_of_pool_table_entry_is_rejected():
 @pytest.mark.parametrize("pin", P.MASK_PINS, ids=[p.__name__ for p in P.MASK_PINS])
 def test_mask_pin(pin):
     pin()
+
+
+@pytest.mark.parametrize("pin", P.MULTI_PINS, ids=[p.__name__ for p in P.MULTI_PINS])
+def test_multi_pin(pin):
+    pin()

@@ -310,3 +310,35 @@ def _merge_unguarded(m, l, o):
 def test_mask_mutant_is_caught(monkeypatch, name, bad):
     monkeypatch.setattr(A, name, bad)
     assert _caught(P.MASK_PINS), f"no pin caught {bad.__name__}"
+
+
+# ----------------------------------------------------------------------------
+# several query tokens per sequence
+
+def _multi_not_causal(query, kc, vc, tables, ctx, qstart, scale, dtype, quant=None):
+    import numpy as np
+    T, H, D = query.shape
+    out = np.zeros((T, H, D))
+    for s in range(len(ctx)):
+        for r in range(int(qstart[s]), int(qstart[s + 1])):
+            out[r] = A.paged_decode(query[r:r + 1], kc, vc, tables[s:s + 1], [ctx[s]], scale, dtype, quant)[0]
+    return out
+
+
+def _multi_off_by_one(query, kc, vc, tables, ctx, qstart, scale, dtype, quant=None):
+    import numpy as np
+    T, H, D = query.shape
+    out = np.zeros((T, H, D))
+    for s in range(len(ctx)):
+        n, L = int(ctx[s]), int(qstart[s + 1] - qstart[s])
+        for i in range(L):
+            lim = max(1, n - L + i)      # forgets that the token sees itself
+            r = int(qstart[s]) + i
+            out[r] = A.paged_decode(query[r:r + 1], kc, vc, tables[s:s + 1], [lim], scale, dtype, quant)[0]
+    return out
+
+
+@pytest.mark.parametrize("bad", [_multi_not_causal, _multi_off_by_one])
+def test_multi_mutant_is_caught(monkeypatch, bad):
+    monkeypatch.setattr(A, "paged_decode_multi", bad)
+    assert _caught(P.MULTI_PINS), f"no pin caught {bad.__name__}"
