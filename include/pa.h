@@ -424,6 +424,39 @@ pa_status pa_decode_masked(void* out, const void* query, const void* key_cache, 
                            pa_dtype dtype, pa_dtype kv_dtype, uint32_t flags, int32_t partition_size,
                            void* workspace, size_t workspace_bytes, int32_t* path, void* stream);
 
+/* Workspace of pa_decode_multi's split path: the three arrays of
+ * pa_decode_split_workspace_bytes with one row per query row (num_query_tokens
+ * in place of num_seqs), then one int32 per query row at the next 256-byte
+ * boundary (each row's causal context length, written by the partials pass for
+ * the merge).  Returns 0 on an invalid argument. */
+size_t pa_decode_multi_workspace_bytes(int32_t num_query_tokens, int32_t num_heads, int32_t head_dim,
+                                       int32_t max_context_len, int32_t partition_size);
+
+/* Decode with several query tokens per sequence, causal among themselves: the
+ * verification pass of speculative decoding, which [XDNF] §6.3 combines with
+ * paging.  The query rows of sequence s are query_start[s] ..
+ * query_start[s+1] - 1: the last L of its n = context_lens[s] tokens, whose
+ * K/V are already in the pools.  Row query_start[s] + i (i < L) sits at
+ * position n - L + i and attends to positions 0 .. n - L + i:
+ *   out[r, h, :] = sum_{t <= n-L+i} softmax_t(scale <query[r,h], K_t>) V_t.
+ *   query, out: device [num_query_tokens, num_heads, head_dim], dtype.
+ *   query_start: device int32 [num_seqs + 1], from 0 to num_query_tokens,
+ *     non-decreasing; every span at most max_query_len and at most n (a longer
+ *     span, or L > n, gives NaN rows or no output; rejected under PA_DEBUG).
+ * One launch covers every span: the q.K tile's 16 columns hold (query token,
+ * head) pairs of one KV head, so each workgroup reads its KV once for up to 16
+ * such pairs.  Pools, scales, kv_dtype, flags, partition_size, path choice
+ * (PA_DECODE_SPLIT / auto / single without a workspace) and errors as in
+ * pa_decode_masked, with pa_decode_multi_workspace_bytes for the workspace. */
+pa_status pa_decode_multi(void* out, const void* query, const void* key_cache, const void* value_cache,
+                          const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+                          const int32_t* seq_order, int32_t num_seqs, int32_t num_query_tokens,
+                          int32_t max_query_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                          int32_t max_context_len, float scale, float k_scale, float v_scale, pa_dtype dtype,
+                          pa_dtype kv_dtype, uint32_t flags, int32_t partition_size, void* workspace,
+                          size_t workspace_bytes, int32_t* path, void* stream);
+
 /* ======================================================================== *
  * Quantised (8-bit) KV cache                                                *
  * ======================================================================== *

@@ -483,6 +483,99 @@ pa_status pa_decode_masked(void* out, const void* query, const void* key_cache, 
   return finish(split ? pa::launch_decode_split(a, ws, st) : pa::launch_decode(a, st), st, "pa_decode_masked");
 }
 
+size_t pa_decode_multi_workspace_bytes(int32_t num_query_tokens, int32_t num_heads, int32_t head_dim,
+                                       int32_t max_context_len, int32_t partition_size) {
+  SplitSizes z;
+  if (!split_sizes(num_query_tokens, num_heads, head_dim, max_context_len, partition_size, &z)) return 0;
+  return static_cast<size_t>(align256(z.total) + static_cast<int64_t>(num_query_tokens) * 4);
+}
+
+pa_status pa_decode_multi(void* out, const void* query, const void* key_cache, const void* value_cache,
+                          const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+                          const int32_t* seq_order, int32_t num_seqs, int32_t num_query_tokens,
+                          int32_t max_query_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                          int32_t max_context_len, float scale, float k_scale, float v_scale, pa_dtype dtype,
+                          pa_dtype kv_dtype, uint32_t flags, int32_t partition_size, void* workspace,
+                          size_t workspace_bytes, int32_t* path, void* stream) {
+  pa::DecodeArgs a = pack(out, query, key_cache, value_cache, block_tables, context_lens, seq_order, num_seqs,
+                          num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                          max_context_len, scale, dtype, flags);
+  a.kv_dtype = kv_dtype;
+  pa_status s = check_decode_args(a);
+  if (s != PA_OK) return s;
+  if (is_code_type(kv_dtype)) {
+    if (dtype != PA_F16 && dtype != PA_BF16)
+      return fail(PA_ERR_UNSUPPORTED, "8-bit pools decode with PA_F16 or PA_BF16 queries");
+    if ((s = check_scales(k_scale, v_scale)) != PA_OK) return s;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+  } else if (kv_dtype != dtype) {
+    return fail(PA_ERR_UNSUPPORTED, "kv_dtype must equal dtype, or be PA_FP8_E4M3 / PA_INT8");
+  }
+  if (num_query_tokens < 0 || max_query_len < 1 || max_query_len > 4096)
+    return fail(PA_ERR_INVALID_ARG, "num_query_tokens >= 0 and 1 <= max_query_len <= 4096");
+  if (static_cast<int64_t>(num_query_tokens) * num_heads > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "num_query_tokens * num_heads too large");
+  if (flags & ~uint32_t(PA_DECODE_CACHED_KV | PA_DECODE_SPLIT))
+    return fail(PA_ERR_INVALID_ARG, "unknown flag bits");
+  a.flags = flags & PA_DECODE_CACHED_KV;
+  if (num_seqs > 0 && !query_start) return fail(PA_ERR_INVALID_ARG, "null query_start");
+  // path: as pa_decode_quant, with the workgroup count of the multi-token launch
+  SplitSizes z;
+  const bool sizes_ok = split_sizes(num_query_tokens, num_heads, head_dim, max_context_len,
+                                    partition_size > 0 ? partition_size : 1, &z);
+  const int64_t need = sizes_ok ? align256(z.total) + static_cast<int64_t>(num_query_tokens) * 4 : -1;
+  bool split = false;
+  if (flags & PA_DECODE_SPLIT) {
+    if (partition_size <= 0 || partition_size % block_size || partition_size > 4096)
+      return fail(PA_ERR_INVALID_ARG, "partition_size must be a multiple of block_size, at most 4096");
+    split = true;
+  } else if (workspace && num_seqs > 0 && partition_size > 0 && partition_size % block_size == 0 &&
+             partition_size <= 4096 && a.max_context_len >= 4 * static_cast<int64_t>(partition_size) && sizes_ok &&
+             static_cast<int64_t>(workspace_bytes) >= need) {
+    int64_t workgroups = 0, resident = 0;
+    const bool ok = pa::multi_pass_shape(a, max_query_len, &workgroups, &resident) == hipSuccess;
+    (void)hipGetLastError();
+    split = ok && workgroups < resident;
+  }
+  if (path) *path = split ? 1 : 0;
+  if (num_seqs == 0 || num_query_tokens == 0) return PA_OK;
+  if (!aligned16(out) || !aligned16(query)) return fail(PA_ERR_INVALID_ARG, "query and out must be 16-byte aligned");
+  pa::SplitLayout ws;
+  int32_t* ws_len = nullptr;
+  if (split) {
+    if (!sizes_ok) return fail(PA_ERR_INVALID_ARG, "split sizes (at most 65535 partitions)");
+    if (static_cast<int64_t>(workspace_bytes) < need)
+      return fail(PA_ERR_WORKSPACE_TOO_SMALL,
+                  "need " + std::to_string(need) + " bytes, got " + std::to_string(workspace_bytes));
+    if ((s = make_layout(workspace, workspace_bytes, num_query_tokens, num_heads, head_dim, max_context_len,
+                         partition_size, &ws)) != PA_OK)
+      return s;
+    ws.rows = num_query_tokens;
+    ws_len = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align256(z.total));
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_mode()) {
+    if ((s = debug_check_tables(a, st)) != PA_OK) return s;
+    std::vector<int32_t> qsv, ctx;
+    if ((s = fetch(qsv, query_start, static_cast<size_t>(num_seqs) + 1, st)) != PA_OK) return s;
+    if ((s = fetch(ctx, context_lens, num_seqs, st)) != PA_OK) return s;
+    if (qsv[0] != 0 || qsv[num_seqs] != num_query_tokens)
+      return fail(PA_ERR_BAD_TABLE, "query_start must run from 0 to num_query_tokens");
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      const int32_t span = qsv[i + 1] - qsv[i];
+      if (span < 0 || span > max_query_len || span > ctx[i])
+        return fail(PA_ERR_BAD_TABLE, "query span of sequence " + std::to_string(i) +
+                                          " negative, above max_query_len or above its context length");
+    }
+  }
+  return finish(pa::launch_decode_multi(a, query_start, num_query_tokens, max_query_len, split ? &ws : nullptr,
+                                        ws_len, st),
+                st,
+                "pa_decode_multi");
+}
+
 pa_status pa_decode_quant(void* out, const void* query, const void* key_cache, const void* value_cache,
                           const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -49,8 +49,16 @@ int group_tile(int group) {
   return 1;
 }
 
+int log2_of(int x) {
+  int l = 0;
+  while ((1 << (l + 1)) <= x) ++l;
+  return l;
+}
+
 DecodeParams make_params(const DecodeArgs& x) {
   DecodeParams p{};
+  p.col_heads_log2 = log2_of(group_tile(x.num_heads / x.num_kv_heads));
+  p.q_chunks = 1;
   p.out = x.out;
   p.q = static_cast<const char*>(x.query);
   p.kc = static_cast<const char*>(x.key_cache);
@@ -128,6 +136,64 @@ hipError_t launch_decode_append(const DecodeArgs& x, const void* new_k, const vo
   if (e != hipSuccess || !ws) return e;
   return launch_lse_reduce(x.out, *ws, x.context_lens, x.seq_order, x.num_seqs, x.num_heads, x.head_dim,
                            p.len_limit, x.dtype, stream);
+}
+
+// Columns of a tile for several query tokens per sequence: 2^lg heads x the
+// rest tokens, NC <= 16; the choice minimises the workgroups per (sequence, KV
+// head) (each reads that KV head once), then prefers fewer padding columns.
+void multi_tile(int group, int max_q, int* nc, int* lg_heads, int* chunks) {
+  int best = -1;
+  for (int gh = 1; gh <= 16 && gh <= group; gh *= 2) {
+    if (group % gh) continue;
+    int nq = 1;
+    while (nq * 2 * gh <= 16 && nq < max_q) nq *= 2;
+    const int wgs = (group / gh) * ((max_q + nq - 1) / nq);
+    const int cols = gh * nq;
+    const int cost = wgs * 64 + cols;  // workgroups first, then tile width
+    if (best < 0 || cost < best) {
+      best = cost;
+      *nc = cols;
+      *lg_heads = log2_of(gh);
+      *chunks = (max_q + nq - 1) / nq;
+    }
+  }
+}
+
+hipError_t launch_decode_multi(const DecodeArgs& x, const int32_t* query_start, int32_t num_query_tokens,
+                               int32_t max_query_len, const SplitLayout* ws, int32_t* ws_len, hipStream_t stream) {
+  DecodeParams p = make_params(x);
+  p.num_q_rows = num_query_tokens;
+  int nc = 1, lg = 0, chunks = 1;
+  multi_tile(x.num_heads / x.num_kv_heads, max_query_len, &nc, &lg, &chunks);
+  p.q_start = query_start;
+  p.col_heads_log2 = lg;
+  p.q_chunks = chunks;
+  if (ws) {
+    p.ws_m = ws->m;
+    p.ws_l = ws->l;
+    p.ws_o = ws->o;
+    p.part_size = ws->partition_size;
+    p.num_parts = ws->num_parts;
+    p.ws_len = ws_len;
+  }
+  hipError_t e = by_dtype(LaunchOp{p, x.num_seqs, (x.flags & PA_DECODE_CACHED_KV) != 0, stream}, x.dtype,
+                          x.kv_dtype, ws != nullptr, false, x.head_dim, x.block_size, nc);
+  if (e != hipSuccess || !ws) return e;
+  // one merge row per (query row, head); each row's context length was written by the partials pass
+  return launch_lse_reduce(x.out, *ws, ws_len, nullptr, ws->rows, x.num_heads, x.head_dim, p.len_limit, x.dtype,
+                           stream);
+}
+
+hipError_t multi_pass_shape(const DecodeArgs& x, int32_t max_query_len, int64_t* workgroups, int64_t* resident) {
+  int nc = 1, lg = 0, chunks = 1;
+  multi_tile(x.num_heads / x.num_kv_heads, max_query_len, &nc, &lg, &chunks);
+  *workgroups = static_cast<int64_t>(x.num_seqs) * (x.num_heads >> lg) * chunks;
+  int per_cu = 0, dev = 0, cus = 0;
+  hipError_t e = occupancy_by_dtype(&per_cu, x.dtype, x.kv_dtype, x.head_dim, x.block_size, nc);
+  if (e == hipSuccess) e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  *resident = static_cast<int64_t>(per_cu) * cus;
+  return e;
 }
 
 hipError_t single_pass_shape(const DecodeArgs& x, int64_t* workgroups, int64_t* resident) {

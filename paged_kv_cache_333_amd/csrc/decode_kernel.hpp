@@ -15,8 +15,9 @@
 // consecutive elements along the contraction axis of its product: head_dim
 // for q.K, tokens for P.V, which is what a matrix-core operand wants.
 //
-// Work decomposition.  A workgroup of kWaves waves serves one (sequence, GT
-// query heads that share a KV head).  Single pass: the waves share the whole
+// Work decomposition.  A workgroup of kWaves waves serves one (sequence, NC
+// columns that share a KV head: query heads, or with several query tokens per
+// sequence, (query token, head) pairs).  Single pass: the waves share the whole
 // context, wave w taking steps w, w + kWaves, ... of TS tokens (32 for
 // fp16/bf16, 16 for fp32), and merge through LDS at the end.  Split: each wave
 // owns one partition outright and writes its partial (m, l, o) itself, so a
@@ -24,8 +25,8 @@
 // with lane = 16 q + n:
 //   * q.K: one 16x16 tile per 16 tokens, C[m][n'] = sum_d K[tok(m)][d] Q[n'][d]
 //     on v_mfma_f32_16x16x32_{f16,bf16} (fp32: 16x16x4).  Column n' of Q is
-//     query head n' % GT, so the GT heads are replicated to fill the 16
-//     columns and every lane ends up holding logits of one head.  Token rows
+//     column n' % NC, so the NC columns are replicated to fill the 16 and
+//     every lane ends up holding logits of one column.  Token rows
 //     are permuted so that lane (q, n) receives tokens EPL q .. EPL q + EPL-1
 //     of the step, exactly the slice it supplies to P.V.
 //   * online softmax per head on those EPL logits per lane: running max (made
@@ -35,7 +36,13 @@
 //     output dims; P never leaves the registers that computed it.  For bf16,
 //     P is split into a bf16 high part and a bf16 residual (two products) so
 //     the weights keep ~16 significant bits; fp16 P keeps 11.
-// Each KV element is loaded once per workgroup; the GT query heads share it.
+// Each KV element is loaded once per workgroup; the NC columns share it.
+//
+// Several query tokens per sequence (speculative verification): query token i
+// of a span of L sits at position n - L + i and sees positions up to it.  The
+// columns of a tile are heads x consecutive query tokens; each lane applies its
+// column's causal limit in the last steps, and value rows are zeroed only past
+// the tile's furthest limit.
 //
 // Logits are kept in base-2 units (scale folded with log2 e) so the hardware
 // exp2 is used.  Tokens past the context are masked by select (never by
@@ -81,6 +88,16 @@ struct DecodeParams {
   // tokens before a sliding window), or null; not used by the fused write
   const int32_t* mask_lo;
   const int32_t* mask_hi;
+  // query tokens: rows q_start[s] .. q_start[s+1]-1 of q/out belong to sequence s
+  // (several causal query tokens, pa_decode_multi); null: row s, one token.  The
+  // NC columns of a q.K tile carry 2^col_heads_log2 heads x NC / 2^col_heads_log2
+  // query tokens; q_chunks workgroups cover one (sequence, head group) along the
+  // tokens.  ws_len (split with q_start): per query row, its causal context length.
+  const int32_t* q_start;
+  int32_t num_q_rows;  // rows of q/out when q_start is set
+  int32_t col_heads_log2;
+  int32_t q_chunks;
+  int32_t* ws_len;
   float* ws_m;
   float* ws_l;
   float* ws_o;
@@ -177,8 +194,11 @@ struct AppendRow {
 // T is the query/output type and the type the matrix cores compute in; S is
 // the pools' storage type: T itself, or an 8-bit code type (TE4M3, TI8) whose
 // chunks are widened exactly to T in registers after the load.
+// GT is NC, the number of distinct columns of a q.K tile: query heads that
+// share a KV head times query tokens of the same sequence (one token: heads).
 template <typename T, typename S, int D, int BS, int GT, bool SPLIT, bool CACHED, bool APPEND>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void decode_kernel(DecodeParams a) {
+  constexpr int NC = GT;
   constexpr bool Q8 = S::kBytes == 1;  // 8-bit codes
   constexpr int EPL = T::kEPL;       // compute elements per 16-byte chunk
   constexpr int E = T::kBytes;
@@ -194,7 +214,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   constexpr int NBS = TS > BS ? TS / BS : 1;  // blocks touched by one step
   constexpr bool SPLIT_P = std::is_same<T, TBF16>::value;
   constexpr float kNegInf = -__builtin_huge_valf();
-  static_assert(GT >= 1 && GT <= 16, "heads per workgroup");
+  static_assert(NC >= 1 && NC <= 16 && (NC & (NC - 1)) == 0, "columns per tile");
   static_assert(Q8 ? T::kBytes == 2 : std::is_same<T, S>::value, "8-bit pools decode in fp16/bf16");
   static_assert(!(Q8 && APPEND), "the fused write stores model-type rows");
   static_assert(NBS <= 4 && KL * SE * 4 == D && KV * EPL * 4 == D, "step shape");
@@ -205,16 +225,42 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4;
   const int n = lane & 15;
-  const int groups = a.num_heads / GT;
-  const int slot = blockIdx.x / groups;
-  const int h0 = (blockIdx.x - slot * groups) * GT;
+  // Columns: column c = n % NC is head h0 + (c & (col_heads - 1)) for query
+  // token tok0 + (c >> log2 col_heads) of the sequence.
+  const int lg_h = a.col_heads_log2;
+  const int col_heads = 1 << lg_h;
+  const int col_toks = NC >> lg_h;
+  const int groups = a.num_heads >> lg_h;
+  const int per_slot = groups * a.q_chunks;
+  const int slot = blockIdx.x / per_slot;
+  const int grp = (blockIdx.x - slot * per_slot) / a.q_chunks;
+  const int chunk = blockIdx.x - slot * per_slot - grp * a.q_chunks;
+  const int h0 = grp << lg_h;
   // Workgroups start in blockIdx order; with a longest-first order the long
   // sequences start first and the short ones fill in behind them.
   const int s = a.order ? a.order[slot] : slot;
   if (static_cast<uint32_t>(s) >= static_cast<uint32_t>(a.num_seqs)) return;
+  int qs = s, L = 1;  // the sequence's query rows qs .. qs + L - 1
+  if (a.q_start) {
+    qs = a.q_start[s];
+    L = a.q_start[s + 1] - qs;
+    if (qs < 0 || L < 0 || qs > a.num_q_rows - L) return;  // a span outside the rows: no output
+  }
+  const int tok0 = chunk * col_toks;
+  if (tok0 >= L) return;  // no query token for this workgroup
   const int kvh = h0 / (a.num_heads / a.num_kv_heads);
   const int nctx = a.ctx[s];
-  const bool bad_len = nctx < 0 || nctx > a.len_limit;
+  // (an empty context is valid for plain decode: a zero row; a span of query
+  // tokens must lie inside the context)
+  const bool bad_len = nctx < 0 || nctx > a.len_limit || (a.q_start && L > nctx);
+  // Causal limits: query token i sits at position nctx - L + i and sees the
+  // positions before nctx - L + i + 1.  This lane's column, and the tile's
+  // nearest and furthest limits (all nctx for one token per sequence).
+  const int my_tok = tok0 + ((n % NC) >> lg_h);
+  const int lim_base = nctx - L + 1;
+  const int lane_lim = lim_base + min(my_tok, L - 1);
+  const int tile_lim_lo = lim_base + tok0;
+  const int tile_lim_hi = lim_base + min(tok0 + col_toks, L) - 1;
   int mlo = 0, mhi = 0;  // masked positions; empty unless mask_lo < mask_hi
   if (!APPEND && a.mask_lo) {
     mlo = a.mask_lo[s];
@@ -226,17 +272,21 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   // w, w + kWaves, ...  Split: each wave owns one partition outright (partition
   // blockIdx.y * kWaves + wave) and writes its partial itself.
   constexpr int WSTEP = SPLIT ? 1 : kWaves;
-  int t_begin = 0, t_end = bad_len ? 0 : nctx, part = 0;
+  const int t_all = bad_len ? 0 : tile_lim_hi;  // the tile's range is [0, t_all)
+  int t_begin = 0, t_end = t_all, part = 0;
   if constexpr (SPLIT) {
     part = blockIdx.y * kWaves + wave;
     t_begin = part * a.part_size;
     t_end = min(t_begin + a.part_size, t_end);
+    // the merge needs each query row's context length (any head group writes the same)
+    if (a.ws_len && part == 0 && grp == 0 && q == 0 && n < NC && (n & (col_heads - 1)) == 0 && my_tok < L)
+      a.ws_len[qs + my_tok] = bad_len ? -1 : lim_base + my_tok;
   }
   AppendRow<T, D> fresh;  // the fused slot-mapping write (pa_decode_append)
   if constexpr (APPEND)
     fresh.template prepare<BS, TS, SPLIT>(a, s, kvh, nctx, bad_len, t_begin, t_end, wave, lane);
   if constexpr (SPLIT) {
-    if (bad_len || t_begin >= nctx) {  // nothing to read in this partition (no barrier follows)
+    if (bad_len || t_begin >= t_all) {  // nothing to read in this partition (no barrier follows)
       if constexpr (APPEND) {
         if (fresh.pending) fresh.template commit<BS>(a, lane);
       }
@@ -249,12 +299,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int b_end = (t_end + BS - 1) / BS;
   const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.max_blocks;
 
-  // Q operand of q.K: lane (q, n) holds head h0 + n % GT, the dims its key
-  // chunks hold: chunk 4v + q; with 8-bit keys, key load l = v / 2 holds dims
-  // 16 (4l + q) .. + 15 and widens into chunks 2 (4l + q) and 2 (4l + q) + 1.
+  // Q operand of q.K: lane (q, n) holds column n % NC (a padding column past
+  // the last query token repeats it), the dims its key chunks hold: chunk
+  // 4v + q; with 8-bit keys, key load l = v / 2 holds dims 16 (4l + q) .. + 15
+  // and widens into chunks 2 (4l + q) and 2 (4l + q) + 1.
   u32x4 qv[KV];
   {
-    const char* qrow = a.q + (static_cast<int64_t>(s) * a.num_heads + h0 + n % GT) * D * E;
+    const int64_t row = static_cast<int64_t>(qs + min(my_tok, L - 1)) * a.num_heads + h0 + (n & (col_heads - 1));
+    const char* qrow = a.q + row * D * E;
 #pragma unroll
     for (int v = 0; v < KV; ++v) {
       const int c = Q8 ? 2 * (4 * (v >> 1) + q) + (v & 1) : 4 * v + q;
@@ -262,8 +314,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     }
   }
 
-  // Online-softmax state of this lane's head (n % GT), and the P.V
-  // accumulator: acc[v][j] is out^T row 4q + j (head (4q + j) % GT), dim 16v + n.
+  // Online-softmax state of this lane's column (n % NC), and the P.V
+  // accumulator: acc[v][j] is out^T row 4q + j (column (4q + j) % NC), dim 16v + n.
   float m_run = kNegInf, l_run = 0.f;
   f32x4 acc[NV];
 #pragma unroll
@@ -408,14 +460,18 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
         for (int v = 0; v < KV; ++v) c[tau] = mma(T{}, kr[tau][v], qv[v], c[tau]);
       }
     }
-    // c[tau][j]: logit of token t0 + TPL q + 4 tau + j for head n % GT.  In a
-    // ragged step (the context ends, or the masked interval starts or ends,
-    // inside it) bit e of `use` says whether the lane's token TPL q + e counts.
-    const bool ragged = t0 + TS > t_end || meets;
-    uint32_t use = ~0u;
+    // c[tau][j]: logit of token t0 + TPL q + 4 tau + j for column n % NC.  In
+    // a ragged step (the context or a query token's causal limit ends, or the
+    // masked interval starts or ends, inside it) bit e of `use` says whether
+    // the lane's token TPL q + e counts for its column, and bit e of `vuse`
+    // whether it counts for any column (the value rows to keep).
+    const bool ragged = t0 + TS > min(t_end, tile_lim_lo) || meets;
+    uint32_t use = ~0u, vuse = ~0u;
     if (ragged) {
       const int base = t0 + TPL * q;
-      use = low_bits(t_end - base) & ~(low_bits(mhi - base) & ~low_bits(mlo - base));
+      const uint32_t hole = low_bits(mhi - base) & ~low_bits(mlo - base);
+      use = low_bits(min(t_end, lane_lim) - base) & ~hole;
+      vuse = low_bits(t_end - base) & ~hole;
     }
     float z[TPL];
     float mx = kNegInf;
@@ -443,17 +499,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     }
     l_run = l_run * alpha + ps;
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-      // acc[.][j] belongs to head (4q + j) % GT; its factor sits in a lane of
-      // the same row whose column has that head.
+      // acc[.][j] belongs to column (4q + j) % NC; its factor sits in a lane
+      // of the same row whose column is that one.
       float al[4];
-      if constexpr (4 % GT == 0) {
+      if constexpr (4 % NC == 0) {
         al[0] = quad_bcast<0>(alpha);
         al[1] = quad_bcast<1>(alpha);
         al[2] = quad_bcast<2>(alpha);
         al[3] = quad_bcast<3>(alpha);
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) al[j] = __shfl(alpha, 16 * q + (4 * q + j) % GT);
+        for (int j = 0; j < 4; ++j) al[j] = __shfl(alpha, 16 * q + (4 * q + j) % NC);
       }
 #pragma unroll
       for (int v = 0; v < NV; ++v)
@@ -465,7 +521,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
 #pragma unroll
     for (int u = 0; u < PV; ++u) pack_p(T{}, p + EPL * u, phi[u], plo[u]);
     if (ragged) {
-      const u32x4 keep = bits_mask(S{}, use);
+      const u32x4 keep = bits_mask(S{}, vuse);
 #pragma unroll
       for (int v = 0; v < NV; ++v) vr[v] &= keep;
     }
@@ -494,71 +550,79 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
 
   if constexpr (SPLIT) {
     // This wave's partition: (m_p in natural-log units, l_p, o_p = acc / l_p)
-    // for each of the GT heads.  acc[.][j] belongs to head (4q + j) % GT, whose
-    // l sits in a lane of the same row (see the rescale above).
+    // for each of the NC columns.  acc[.][j] belongs to column (4q + j) % NC,
+    // whose l sits in a lane of the same row (see the rescale above).
     float lg[4];
-    if constexpr (4 % GT == 0) {
+    if constexpr (4 % NC == 0) {
       lg[0] = quad_bcast<0>(l_run);
       lg[1] = quad_bcast<1>(l_run);
       lg[2] = quad_bcast<2>(l_run);
       lg[3] = quad_bcast<3>(l_run);
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) lg[j] = __shfl(l_run, 16 * q + (4 * q + j) % GT);
+      for (int j = 0; j < 4; ++j) lg[j] = __shfl(l_run, 16 * q + (4 * q + j) % NC);
     }
     const float qnan = __builtin_nanf("");
-    const int64_t sh0 = static_cast<int64_t>(s) * a.num_heads + h0;
+    // output row of column c (query row x heads + head), or -1 for a padding column
+    auto out_row = [&](int c) -> int64_t {
+      const int tok = tok0 + (c >> lg_h);
+      return tok < L ? static_cast<int64_t>(qs + tok) * a.num_heads + h0 + (c & (col_heads - 1)) : -1;
+    };
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int g = 4 * q + j;  // first replica of each head
-      if (g < GT) {
-        float* o = a.ws_o + ((sh0 + g) * a.num_parts + part) * D + n;
+      const int g = 4 * q + j;  // first replica of each column
+      const int64_t r = g < NC ? out_row(g) : -1;
+      if (r >= 0) {
+        float* o = a.ws_o + (r * a.num_parts + part) * D + n;
 #pragma unroll
         for (int v = 0; v < NV; ++v)
           o[16 * v] = bad ? qnan : (lg[j] == 0.f ? 0.f : acc[v][j] / lg[j] * a.v_scale);  // 0: all masked
       }
     }
-    if (q == 0 && n < GT) {
-      const int64_t idx = (sh0 + n) * a.num_parts + part;
+    const int64_t rn = q == 0 && n < NC ? out_row(n) : -1;
+    if (rn >= 0) {
+      const int64_t idx = rn * a.num_parts + part;
       a.ws_m[idx] = m_run * 0.6931471805599453f;  // back to natural-log units
       a.ws_l[idx] = bad ? qnan : l_run;
     }
     return;
   }
 
-  __shared__ float sm_m[kWaves][GT];
-  __shared__ float sm_l[kWaves][GT];
-  __shared__ float sm_acc[kWaves][GT][D];
-  if (q == 0 && n < GT) {
+  __shared__ float sm_m[kWaves][NC];
+  __shared__ float sm_l[kWaves][NC];
+  __shared__ float sm_acc[kWaves][NC][D];
+  if (q == 0 && n < NC) {
     sm_m[wave][n] = m_run;
     sm_l[wave][n] = l_run;
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int g = 4 * q + j;  // first replica of each head
-    if (g < GT) {
+    const int g = 4 * q + j;  // first replica of each column
+    if (g < NC) {
 #pragma unroll
       for (int v = 0; v < NV; ++v) sm_acc[wave][g][16 * v + n] = acc[v][j];
     }
   }
   const int any_bad = __syncthreads_or(bad);
 
-  for (int i = threadIdx.x; i < GT * D; i += kWaves * 64) {
+  for (int i = threadIdx.x; i < NC * D; i += kWaves * 64) {
     const int g = i / D;
     const int d = i - g * D;
+    const int tok = tok0 + (g >> lg_h);
+    if (tok >= L) continue;  // a padding column
     float M = kNegInf;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][g]);
     const float Mu = M == kNegInf ? 0.f : M;
-    float L = 0.f, A = 0.f;
+    float Lsum = 0.f, A = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float wt = fast_exp2(sm_m[w][g] - Mu);
-      L = __builtin_fmaf(sm_l[w][g], wt, L);
+      Lsum = __builtin_fmaf(sm_l[w][g], wt, Lsum);
       A = __builtin_fmaf(sm_acc[w][g][d], wt, A);
     }
-    const int64_t sh = static_cast<int64_t>(s) * a.num_heads + h0 + g;
-    const float val = any_bad || bad_len ? __builtin_nanf("") : (L > 0.f ? A / L * a.v_scale : 0.f);
+    const int64_t sh = static_cast<int64_t>(qs + tok) * a.num_heads + h0 + (g & (col_heads - 1));
+    const float val = any_bad || bad_len ? __builtin_nanf("") : (Lsum > 0.f ? A / Lsum * a.v_scale : 0.f);
     store_elem(T{}, a.out, sh * D + d, val);
   }
 }
@@ -641,7 +705,7 @@ struct LaunchOp {
   hipStream_t stream;
   template <typename T, typename S, int D, int BS, int GT, bool SPLIT, bool APPEND>
   hipError_t run() const {
-    const uint32_t gx = static_cast<uint32_t>(num_seqs) * (p.num_heads / GT);
+    const uint32_t gx = static_cast<uint32_t>(num_seqs) * (p.num_heads >> p.col_heads_log2) * p.q_chunks;
     const uint32_t gy = SPLIT ? static_cast<uint32_t>((p.num_parts + kWaves - 1) / kWaves) : 1u;
     if (cached)
       hipLaunchKernelGGL((decode_kernel<T, S, D, BS, GT, SPLIT, true, APPEND>), dim3(gx, gy), dim3(kWaves * 64),

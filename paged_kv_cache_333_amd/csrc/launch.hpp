@@ -38,6 +38,7 @@ struct SplitLayout {
   float* o;
   int32_t partition_size;
   int32_t num_parts;
+  int32_t rows = 0;  // rows of the partials (sequences; query rows for several query tokens)
 };
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,
@@ -63,6 +64,12 @@ hipError_t launch_decode_append(const DecodeArgs& a, const void* new_k, const vo
 // Workgroups the single-pass launch would start, and how many of them the
 // current device holds at once.
 hipError_t single_pass_shape(const DecodeArgs& a, int64_t* workgroups, int64_t* resident);
+// Several causal query tokens per sequence: rows query_start[s] .. query_start[s+1]-1
+// of query/out (single pass when ws is null, else split + merge; ws_len: one int per
+// query row in the workspace, the merge's context lengths).
+hipError_t launch_decode_multi(const DecodeArgs& a, const int32_t* query_start, int32_t num_query_tokens,
+                               int32_t max_query_len, const SplitLayout* ws, int32_t* ws_len, hipStream_t stream);
+hipError_t multi_pass_shape(const DecodeArgs& a, int32_t max_query_len, int64_t* workgroups, int64_t* resident);
 hipError_t launch_lse_reduce(void* out, const SplitLayout& ws, const int32_t* context_lens,
                              const int32_t* seq_order, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                              int32_t len_limit, pa_dtype dtype, hipStream_t stream);

@@ -19,7 +19,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 37
+    assert len(names) == 39
     for n in names:
         assert hasattr(pa.lib, n), n
         assert C.cast(getattr(pa.lib, n), C.c_void_p).value
@@ -177,3 +177,25 @@ def test_decode_masked_validation_rejects_before_launch():
     assert call(kv=pa.PA_INT8, ks=0.0)[0] == 1
     assert call(flags=8)[0] == 1
     assert call(flags=pa.PA_DECODE_SPLIT) == (0, 1)
+
+
+def test_decode_multi_validation_rejects_before_launch():
+    def call(**kw):
+        a = dict(S=0, T=0, Lmax=4, dt=F, kv=F, flags=0, ps=512, qst=16)
+        a.update(kw)
+        path = C.c_int32(-7)
+        st = pa.lib.pa_decode_multi(16, 16, 16, 16, 16, 16, a["qst"], None, a["S"], a["T"], a["Lmax"], 32, 8, 128,
+                                    16, 4, 8, 64, 0.1, 1.0, 1.0, a["dt"], a["kv"], a["flags"], a["ps"], None, 0,
+                                    C.byref(path), None)
+        return st, path.value
+    assert call() == (0, 0)
+    assert call(Lmax=0)[0] == 1
+    assert call(T=-1)[0] == 1
+    assert call(kv=pa.PA_BF16)[0] == 5
+    assert call(flags=4)[0] == 1
+    assert call(flags=pa.PA_DECODE_SPLIT, ps=24)[0] == 1
+    assert call(flags=pa.PA_DECODE_SPLIT) == (0, 1)
+    # workspace: the split arrays per query row, then one int32 per row at a 256-byte boundary
+    n = pa.lib.pa_decode_multi_workspace_bytes(10, 32, 128, 1000, 512)
+    lay = pa.split_layout(10, 32, 128, 1000, 512)
+    assert n == (lay["total"] + 255) // 256 * 256 + 40
