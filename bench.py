@@ -9,7 +9,8 @@ One step = the whole hot path over one batch:
   LSE merge).  --fused-write runs the write inside the decode launch instead
   (pa_decode_append).  Workloads 6 and 7 keep the pools as 8-bit codes (FP8 E4M3 /
   int8 with per-pool scales): pa_reshape_and_cache_quant quantises the new K/V and
-  pa_decode_quant decodes.
+  pa_decode_quant decodes.  Workload 8 appends 4 tokens per sequence and verifies them
+  in one pa_decode_multi launch (4 causal query tokens per sequence).
 
 Default workload: 64 sequences, 32 query / 32 KV heads of dimension 128, fp16,
 block size 16, contexts uniform in [256, 2048] (a LLaMA-7B-like layer), pool of
@@ -40,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8])
     ap.add_argument("--path", choices=["auto", "single", "split"], default="auto",
                     help="decode path: pa_decode_auto (default: the library picks), pa_decode or pa_decode_split")
     ap.add_argument("--partition", type=int, default=512)
@@ -259,7 +260,7 @@ class Bench:
             for s, n in enumerate(w.context_lens):
                 self.alloc.seq_create(s, n)
             self.base = self.alloc.clone() if args.workload == 1 else None
-            growth = 1 if args.workload == 1 else total_steps
+            growth = 1 if args.workload == 1 else total_steps * w.query_len
         self.max_blocks = -(-(max(w.context_lens) + growth) // bs) + 1
         self.max_ctx = self.max_blocks * bs
 
@@ -275,32 +276,39 @@ class Bench:
         else:
             self.kc = synth.normal_device(k_shape, seeds["key_cache"], w.dtype)
             self.vc = synth.normal_device(v_shape, seeds["value_cache"], w.dtype)
-        self.q = synth.normal_device((S, H, D), seeds["query"], w.dtype)
+        L = self.L = w.query_len  # query tokens (new tokens) per sequence and step
+        NS = L * S
+        if L > 1 and (self.quant or args.fused_write):
+            raise SystemExit("the multi-token workload has model-type pools and a separate write")
+        self.q = synth.normal_device((NS, H, D), seeds["query"], w.dtype)
         R = 8  # distinct new-token K/V batches, cycled
-        self.newk = synth.normal_device((R, S, Hkv, D), seeds["new_key"], w.dtype)
-        self.newv = synth.normal_device((R, S, Hkv, D), seeds["new_value"], w.dtype)
+        self.newk = synth.normal_device((R, NS, Hkv, D), seeds["new_key"], w.dtype)
+        self.newv = synth.normal_device((R, NS, Hkv, D), seeds["new_value"], w.dtype)
         self.out = torch.empty_like(self.q)
+        # query rows of sequence s: s L .. s L + L - 1 (constant, resident)
+        self.qstart = torch.arange(0, NS + 1, L, dtype=torch.int32, device=self.dev)
         self.ws = None
         if self.path != "single":
-            nbytes = pa.pa_decode_split_workspace_bytes(S, H, D, self.max_ctx, args.partition)
+            nbytes = (pa.pa_decode_multi_workspace_bytes(NS, H, D, self.max_ctx, args.partition) if L > 1 else
+                      pa.pa_decode_split_workspace_bytes(S, H, D, self.max_ctx, args.partition))
             self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.dev)
 
         # double-buffered index data, one pinned staging buffer and one upload (pa_upload, a
         # kernel on the compute stream) per step:
-        # [slots S | lens S | order S | pairs 2S | tables S*MB] int32
-        self.ids = torch.arange(S, dtype=torch.int64).pin_memory()
+        # [slots LS | lens S | order S | pairs 2LS | tables S*MB] int32 (L new tokens per sequence)
+        self.ids = torch.arange(S, dtype=torch.int64).repeat(L).pin_memory()
         self.bufs = []
-        total = 5 * S + S * self.max_blocks
+        total = 3 * NS + 2 * S + S * self.max_blocks
         for _ in range(2):
             hb = torch.empty(total, dtype=torch.int32).pin_memory()
             db = torch.empty(total, dtype=torch.int32, device=self.dev)
             b = {"idx_h": hb, "idx_d": db, "staged": torch.cuda.Event()}
             for side, t in (("h", hb), ("d", db)):
-                b["slots_" + side] = t[0:S]
-                b["len_" + side] = t[S:2 * S]
-                b["order_" + side] = t[2 * S:3 * S]
-                b["pairs_" + side] = t[3 * S:5 * S].view(S, 2)
-                b["tab_" + side] = t[5 * S:].view(S, self.max_blocks)
+                b["slots_" + side] = t[0:NS]
+                b["len_" + side] = t[NS:NS + S]
+                b["order_" + side] = t[NS + S:NS + 2 * S]
+                b["pairs_" + side] = t[NS + 2 * S:3 * NS + 2 * S].view(NS, 2)
+                b["tab_" + side] = t[3 * NS + 2 * S:].view(S, self.max_blocks)
             b["staged"].record(self.stream)
             self.bufs.append(b)
         self.elem = synth.ELEM_BYTES[w.dtype]
@@ -315,7 +323,8 @@ class Bench:
         if self.base is not None:
             alloc = self.alloc = self.base.clone()
         S = w.num_seqs
-        npairs = alloc.seq_append_slots_into(self.ids.data_ptr(), S, b["slots_h"].data_ptr(), b["pairs_h"].data_ptr())
+        npairs = alloc.seq_append_slots_into(self.ids.data_ptr(), self.L * S, b["slots_h"].data_ptr(),
+                                             b["pairs_h"].data_ptr())
         alloc.build_block_tables_into(self.ids.data_ptr(), S, self.max_blocks, b["tab_h"].data_ptr(),
                                       b["len_h"].data_ptr())
         order = None
@@ -336,7 +345,13 @@ class Bench:
         if timing is not None:
             e0, e1 = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
             e0.record(self.stream)
-        if self.quant:
+        if self.L > 1:
+            self.path_ran.add(pa.pa_decode_multi(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"],
+                                                 self.qstart, self.L, self.max_ctx, w.scale,
+                                                 partition_size=self.args.partition, workspace=self.ws,
+                                                 split=self.path == "split", seq_order=order,
+                                                 cached_kv=self.cached))
+        elif self.quant:
             self.path_ran.add(pa.pa_decode_quant(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"],
                                                  self.max_ctx, w.scale, w.k_scale, w.v_scale,
                                                  kv_format=w.kv_format, partition_size=self.args.partition,
@@ -402,12 +417,16 @@ class Bench:
             vc = synth.to_numpy(self.vc.index_select(0, idx), w.dtype)
         q = synth.to_numpy(self.q, w.dtype)
         quant = (w.kv_format, w.k_scale, w.v_scale) if self.quant else None
+        qstart = self.qstart.cpu().numpy()
         t2 = np.where(tabs >= 0, remap[np.maximum(tabs, 0)], -1)
         passes, tokens = 0, 0
         with threadpool_limits(1):
             t0 = time.perf_counter()
             while True:
-                A.paged_decode(q, kc, vc, t2, lens, w.scale, w.dtype, quant=quant)
+                if self.L > 1:
+                    A.paged_decode_multi(q, kc, vc, t2, lens, qstart, w.scale, w.dtype)
+                else:
+                    A.paged_decode(q, kc, vc, t2, lens, w.scale, w.dtype, quant=quant)
                 passes += 1
                 tokens += int(lens.sum())
                 el = time.perf_counter() - t0
@@ -444,7 +463,7 @@ def main():
     durs = [a.elapsed_time(b) * 1e-3 for a, b, *_ in timing]  # seconds
     kv_tokens = sum(t[2] for t in timing)
     kv_bytes_token = 2 * w.num_kv_heads * w.head_dim * bench.kv_elem
-    qo_bytes = 2 * w.num_seqs * w.num_heads * w.head_dim * e
+    qo_bytes = 2 * w.num_seqs * w.query_len * w.num_heads * w.head_dim * e
     # the fused call also reads the step's new K/V rows and writes them into the pools
     fused_write = 2 * w.num_seqs * kv_bytes_token if (bench.path == "auto" and args.fused_write) else 0
     alg_bytes = [t[2] * kv_bytes_token + qo_bytes + 4 * t[3] + 4 * w.num_seqs + fused_write for t in timing]
@@ -468,6 +487,7 @@ def main():
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "kv_cache_dtype": w.kv_format or w.dtype,
+                   "query_tokens_per_seq": w.query_len,
                    "context_lens": "per workload definition, +1 token per step",
                    "mean_kv_tokens_per_step": kv_tokens / len(timing),
                    "decode_path": ("auto: " if bench.path == "auto" else "") + "+".join(sorted(bench.path_ran)),

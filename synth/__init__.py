@@ -20,6 +20,8 @@ dimension 128, blocks of 16 or 32 tokens, contexts up to 2048 and beyond):
                    pools, fp16 query/output, k_scale 0.0165, v_scale 0.0145
   7 gqa-bf16-int8kv  workload 3's shapes (own draw) with int8 pools, bf16 query/output,
                    k_scale 0.031, v_scale 0.029
+  8 llama7b-fp16-verify4  workload 2's shapes (own draw) with 4 query tokens per sequence
+                   (a speculative verification pass of 4 draft tokens)
 
 Draw order for workload k (numpy PCG64, seed 1000+k): context lengths, then the
 pool's initial free order (a permutation), then (workload 5) the suffix
@@ -69,6 +71,8 @@ class Workload:
     kv_format: str = ""
     k_scale: float = 1.0
     v_scale: float = 1.0
+    # query tokens per sequence per step (workload 8: 4, a verification pass)
+    query_len: int = 1
 
     @property
     def scale(self) -> float:
@@ -140,6 +144,10 @@ def workload(key: int) -> Workload:
         w = workload_shapes_like(3, key, rng)
         w.name, w.kv_format = "gqa-bf16-int8kv", "int8"
         w.k_scale, w.v_scale = float(np.float32(0.031)), float(np.float32(0.029))
+        return w
+    if key == 8:
+        w = workload_shapes_like(2, key, rng)
+        w.name, w.query_len = "llama7b-fp16-verify4", 4
         return w
     raise ValueError(f"unknown workload {key}")
 
