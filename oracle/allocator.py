@@ -48,6 +48,26 @@ PrefixCacheManager):
   Positions n_p .. P*bs - 1 are then a hole in the sequence: they hold no
   token and decode must skip them (`masks`).  A sequence's length counts
   positions, hole included; fork keeps the hole and may not end inside it.
+
+Swap ("PagedAttention 实现细节" §3.4: the cache engine keeps a GPU pool and a
+CPU pool "for swap"):
+* A second, host-side pool of block ids with its own first-in-first-out free
+  queue and counts.  swap_out(group) moves the sequences of a group to it: every
+  distinct device block of their tables (table order, first appearance) gets a
+  host block, a (device, host) pair is emitted for the copy, each reference the
+  group held moves from the device block to the host block (the device block
+  returns to the free queue when nothing else holds it).  swap_in is the
+  mirror image with (host, device) pairs.  A group is moved whole, so blocks
+  shared inside it stay shared.  A swapped sequence can only be swapped in or
+  freed.  All-or-nothing.
+
+Sliding window (the feature "PagedAttention 源码解析：KV Cache 怎么管理" §六
+lists): set_window(seq, W) keeps only the last W positions live.  Every block
+whose positions all lie before len - W is released and its table entry
+becomes -1 (decode never reads it); appends keep releasing as the window moves.
+masks() gives [0, len - W).  Not combined with a prefix hole.  A fork of a
+windowed sequence keeps the window and must still hold the blocks its own
+window needs.
 """
 from __future__ import annotations
 
@@ -86,6 +106,10 @@ class BlockAllocator:
         self.prefixes: dict[tuple, int] = {}             # prefix tokens -> entry id
         self.entries: dict[int, dict] = {}               # entry id -> blocks, users, length, key
         self.next_prefix_id = 1
+        self.host_free: deque = deque()                  # host pool (swap)
+        self.host_refs: list[int] = []
+        self.swapped: set = set()
+        self.windows: dict[int, int] = {}
 
     # -- helpers -------------------------------------------------------------
     def _blocks_for(self, n: int) -> int:
@@ -128,6 +152,8 @@ class BlockAllocator:
         self._need(parent)
         if child in self.tables:
             raise AllocatorError(SEQ_EXISTS, str(child))
+        if parent in self.swapped:
+            raise AllocatorError(INVALID_ARG, "parent is swapped out")
         n = self.lens[parent] if num_tokens < 0 else num_tokens
         if n > self.lens[parent]:
             raise AllocatorError(INVALID_ARG, "fork length beyond the parent")
@@ -135,16 +161,27 @@ class BlockAllocator:
         if hole and hole[0] < n < hole[1]:
             raise AllocatorError(INVALID_ARG, "fork length inside the prefix hole")
         shared = self.tables[parent][: self._blocks_for(n)]
+        W = self.windows.get(parent)
+        if W is not None:
+            first_live = max(0, n - W) // self.block_size
+            if any(b < 0 for b in shared[first_live:]):
+                raise AllocatorError(INVALID_ARG, "the child's window needs blocks the parent dropped")
         for b in shared:
-            self.refs[b] += 1
+            if b >= 0:
+                self.refs[b] += 1
         self.tables[child] = list(shared)
         self.lens[child] = n
         if hole and n >= hole[1]:
             self.holes[child] = hole
+        if W is not None:
+            self.windows[child] = W
+            self._drop_behind_window(child)
 
     def seq_append_slot(self, seq_id: int):
         """Reserve the slot of the next token; returns (slot, cow_src, cow_dst), -1s when no copy."""
         self._need(seq_id)
+        if seq_id in self.swapped:
+            raise AllocatorError(INVALID_ARG, "sequence is swapped out")
         table = self.tables[seq_id]
         L = self.lens[seq_id]
         src = dst = -1
@@ -160,11 +197,15 @@ class BlockAllocator:
                 self.stats["cow_copies"] += 1
         slot = table[L // self.block_size] * self.block_size + L % self.block_size
         self.lens[seq_id] = L + 1
+        if seq_id in self.windows:
+            self._drop_behind_window(seq_id)
         return slot, src, dst
 
     def seq_append_slots(self, seq_ids):
         """Append one token to each sequence, in order.  Returns (slots, pairs).  All-or-nothing."""
         saved = copy.deepcopy((self.free, self.refs, self.tables, self.lens, self.stats))
+        for s in seq_ids:
+            self._need(s)
         try:
             slots, pairs = [], []
             for s in seq_ids:
@@ -179,11 +220,19 @@ class BlockAllocator:
 
     def seq_free(self, seq_id: int):
         self._need(seq_id)
-        for b in self.tables[seq_id]:
-            self._release(b)
+        if seq_id in self.swapped:
+            for h in self.tables[seq_id]:
+                if h >= 0:
+                    self._release_host(h)
+            self.swapped.discard(seq_id)
+        else:
+            for b in self.tables[seq_id]:
+                if b >= 0:
+                    self._release(b)
         del self.tables[seq_id]
         del self.lens[seq_id]
         self.holes.pop(seq_id, None)
+        self.windows.pop(seq_id, None)
 
     def can_allocate(self, num_blocks: int) -> bool:
         return num_blocks <= len(self.free)
@@ -210,6 +259,8 @@ class BlockAllocator:
         tables, lens = [], []
         for s in seq_ids:
             self._need(s)
+            if s in self.swapped:
+                raise AllocatorError(INVALID_ARG, "sequence is swapped out")
             t = self.tables[s]
             if len(t) > max_blocks:
                 raise AllocatorError(INVALID_ARG, "block table longer than max_blocks")
@@ -281,6 +332,98 @@ class BlockAllocator:
         for s in seq_ids:
             self._need(s)
             a, b = self.holes.get(s, (0, 0))
+            if s in self.windows:
+                a, b = 0, max(0, self.lens[s] - self.windows[s])
             lo.append(a)
             hi.append(b)
         return lo, hi
+
+    # -- sliding window --------------------------------------------------------
+    def _drop_behind_window(self, seq_id):
+        start = self.lens[seq_id] - self.windows[seq_id]
+        t = self.tables[seq_id]
+        for j in range(len(t)):
+            if (j + 1) * self.block_size > start:
+                break
+            if t[j] >= 0:
+                self._release(t[j])
+                t[j] = -1
+
+    def seq_set_window(self, seq_id, window: int):
+        """Keep only the last `window` positions live; release the blocks wholly before them."""
+        self._need(seq_id)
+        if window < 1:
+            raise AllocatorError(INVALID_ARG, "window < 1")
+        if seq_id in self.swapped or seq_id in self.holes:
+            raise AllocatorError(INVALID_ARG, "window on a swapped sequence or one with a prefix hole")
+        self.windows[seq_id] = window
+        self._drop_behind_window(seq_id)
+
+    # -- swap to the host pool -------------------------------------------------
+    def set_host_pool(self, num_host_blocks: int):
+        """(Re)create the host pool of num_host_blocks blocks, ids 0.. in order; only while empty."""
+        if num_host_blocks < 0:
+            raise AllocatorError(INVALID_ARG, "num_host_blocks < 0")
+        if self.swapped:
+            raise AllocatorError(INVALID_ARG, "sequences are swapped out")
+        self.host_free = deque(range(num_host_blocks))
+        self.host_refs = [0] * num_host_blocks
+
+    def _release_host(self, h):
+        self.host_refs[h] -= 1
+        if self.host_refs[h] == 0:
+            self.host_free.append(h)
+
+    def _group(self, seq_ids, swapped: bool):
+        ids = list(dict.fromkeys(seq_ids))
+        for s in ids:
+            self._need(s)
+            if (s in self.swapped) != swapped:
+                raise AllocatorError(INVALID_ARG, "sequence already swapped out" if not swapped else
+                                     "sequence is not swapped out")
+        distinct = list(dict.fromkeys(b for s in ids for b in self.tables[s] if b >= 0))
+        return ids, distinct
+
+    def seq_swap_out(self, seq_ids):
+        """Move a group to the host pool; returns the (device, host) copy pairs."""
+        ids, distinct = self._group(seq_ids, False)
+        if len(distinct) > len(self.host_free):
+            raise AllocatorError(NO_FREE_BLOCKS, "host pool")
+        where = {}
+        for b in distinct:
+            h = self.host_free.popleft()
+            self.host_refs[h] = 0
+            where[b] = h
+        for s in ids:
+            t = self.tables[s]
+            for j, b in enumerate(t):
+                if b >= 0:
+                    t[j] = where[b]
+                    self.host_refs[where[b]] += 1
+                    self._release(b)
+            self.swapped.add(s)
+        return [(b, where[b]) for b in distinct]
+
+    def seq_swap_in(self, seq_ids):
+        """Move a swapped group back to the device pool; returns the (host, device) copy pairs."""
+        ids, distinct = self._group(seq_ids, True)
+        if len(distinct) > len(self.free):
+            raise AllocatorError(NO_FREE_BLOCKS)
+        where = {}
+        for h in distinct:
+            d = self.free.popleft()
+            self.refs[d] = 0
+            self.stats["blocks_allocated"] += 1
+            where[h] = d
+        for s in ids:
+            t = self.tables[s]
+            for j, h in enumerate(t):
+                if h >= 0:
+                    t[j] = where[h]
+                    self.refs[where[h]] += 1
+                    self._release_host(h)
+            self.swapped.discard(s)
+        return [(h, where[h]) for h in distinct]
+
+    def host_free_list(self) -> list:
+        return list(self.host_free)

@@ -631,3 +631,103 @@ def check_multi_reduces_to_decode(seed=73):
 
 
 MULTI_PINS = [check_multi_against_sdpa, check_multi_reduces_to_decode]
+
+
+# ----------------------------------------------------------------------------
+# swap to the host pool, sliding-window release
+
+def _logical(al, pools, s):
+    """Token data of sequence s read through its table from the pool it lives in
+    (pools = {"dev": array [NB, bs], "host": array [NH, bs]})."""
+    pool = pools["host"] if s in al.swapped else pools["dev"]
+    bs = al.block_size
+    return [pool[al.tables[s][t // bs], t % bs] for t in range(al.lens[s])]
+
+
+def check_swap_round_trip(seed=81):
+    """Swapping a group out and back in keeps every sequence's token data (the copy pairs,
+    applied as whole-block copies between the pools, move exactly what the tables need),
+    keeps sharing inside the group, returns the group's device blocks while it is out and
+    takes the host blocks back afterwards."""
+    rng = np.random.default_rng(seed)
+    NB, NH, bs = 40, 24, 4
+    al = AL.BlockAllocator(NB, bs, rng.permutation(NB))
+    al.set_host_pool(NH)
+    al.seq_create(1, 10)
+    al.seq_fork(1, 2, 9)                 # shares 3 blocks with 1
+    al.seq_append_slot(2)                # copy-on-write of the shared last block
+    al.seq_create(3, 7)
+    al.seq_fork(3, 4)                    # 4 shares with 3, which stays on the device
+    pools = {"dev": rng.integers(0, 10**6, size=(NB, bs)), "host": np.full((NH, bs), -1)}
+    before = {s: _logical(al, pools, s) for s in (1, 2, 3, 4)}
+    free0 = al.num_free_blocks()
+    distinct = len({b for s in (1, 2, 4) for b in al.tables[s]})
+    private = len({b for s in (1, 2, 4) for b in al.tables[s]} - set(al.tables[3]))
+    pairs = al.seq_swap_out([1, 2, 4])
+    assert len(pairs) == distinct and len({d for d, _ in pairs}) == distinct
+    for d, h in pairs:
+        pools["host"][h] = pools["dev"][d]
+    assert al.num_free_blocks() == free0 + private
+    assert len(al.host_free_list()) == NH - distinct
+    assert all(al.ref_count(b) == 1 for b in al.tables[3])       # 4's references left with it
+    assert al.tables[1][:2] == al.tables[2][:2]                     # still shared, now on the host
+    assert al.host_refs[al.tables[1][0]] == 2
+    for s in (1, 2, 3, 4):
+        assert _logical(al, pools, s) == before[s]
+    # the freed device blocks may be reused meanwhile
+    al.seq_create(5, 4 * al.num_free_blocks() - 8)
+    pools["dev"][al.tables[5]] = -7
+    al.seq_free(5)
+    pairs = al.seq_swap_in([2, 1, 4])
+    for h, d in pairs:
+        pools["dev"][d] = pools["host"][h]
+    assert len(al.host_free_list()) == NH
+    for s in (1, 2, 3, 4):
+        assert _logical(al, pools, s) == before[s]
+    assert al.tables[1][:2] == al.tables[2][:2] and al.ref_count(al.tables[1][0]) == 2
+    assert al.ref_count(al.tables[4][0]) == 1 and al.tables[4][0] != al.tables[3][0]
+
+
+def check_window_release():
+    """A window of W keeps the blocks holding positions >= len - W: closed-form tables,
+    free counts and masks as the sequence grows."""
+    bs, W = 16, 40
+    al = AL.BlockAllocator(64, bs)
+    al.seq_create(1, 100)                # blocks 0..6, positions 0..99
+    t0 = list(al.tables[1])
+    al.seq_set_window(1, W)              # start 60: blocks 0..2 (positions 0..47) released
+    assert al.tables[1] == [-1, -1, -1] + t0[3:]
+    assert al.num_free_blocks() == 64 - 7 + 3
+    assert al.masks([1]) == ([0], [60])
+    for _ in range(20):                  # len 120, start 80: block 3 (48..63) and 4 (64..79) released
+        al.seq_append_slot(1)
+    assert al.tables[1][:5] == [-1] * 5 and all(b >= 0 for b in al.tables[1][5:])
+    assert len(al.tables[1]) == 8 and al.masks([1]) == ([0], [80])
+    assert al.num_free_blocks() == 64 - 3
+
+
+def _check_window_fork():
+    bs, W = 16, 40
+    al = AL.BlockAllocator(64, bs)
+    al.seq_create(1, 120)
+    al.seq_set_window(1, W)              # start 80: blocks 0..4 dropped
+    try:
+        al.seq_fork(1, 2, 110)           # start 70 needs block 4
+    except AL.AllocatorError as e:
+        assert e.code == AL.INVALID_ARG
+    else:
+        raise AssertionError("fork into dropped blocks must fail")
+    al.seq_fork(1, 3, 120)
+    assert al.tables[3] == al.tables[1] and al.masks([3]) == ([0], [80])
+    assert all(al.ref_count(b) == 2 for b in al.tables[1] if b >= 0)
+    al.seq_free(1)
+    al.seq_free(3)
+    assert al.num_free_blocks() == 64
+
+
+def check_window():
+    check_window_release()
+    _check_window_fork()
+
+
+SWAP_WINDOW_PINS = [check_swap_round_trip, check_window]

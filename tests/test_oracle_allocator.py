@@ -167,3 +167,8 @@ def test_prefix_random_operations_keep_pool_invariants():
         for s, (lo, hi) in al.holes.items():
             assert lo < hi <= al.lens[s] and hi % bs == 0
         assert sum(e["users"] for e in al.entries.values()) == len(users)
+
+
+@pytest.mark.parametrize("pin", P.SWAP_WINDOW_PINS, ids=[p.__name__ for p in P.SWAP_WINDOW_PINS])
+def test_swap_window_pin(pin):
+    pin()

@@ -342,3 +342,55 @@ def _multi_off_by_one(query, kc, vc, tables, ctx, qstart, scale, dtype, quant=No
 def test_multi_mutant_is_caught(monkeypatch, bad):
     monkeypatch.setattr(A, "paged_decode_multi", bad)
     assert _caught(P.MULTI_PINS), f"no pin caught {bad.__name__}"
+
+
+# ----------------------------------------------------------------------------
+# swap and sliding window
+
+class _SwapOutKeepsDeviceRefs(AL.BlockAllocator):
+    def _release(self, b):
+        if self.swapped is not None and getattr(self, "_in_swap", False):
+            return
+        super()._release(b)
+
+    def seq_swap_out(self, seq_ids):
+        self._in_swap = True
+        try:
+            return super().seq_swap_out(seq_ids)
+        finally:
+            self._in_swap = False
+
+
+class _SwapInUnshares(AL.BlockAllocator):
+    def seq_swap_in(self, seq_ids):
+        pairs = super().seq_swap_in(seq_ids)
+        # gives every reference its own device copy (loses sharing inside the group)
+        seen = set()
+        for s in seq_ids:
+            t = self.tables[s]
+            for j, b in enumerate(t):
+                if b in seen and b >= 0:
+                    self.refs[b] -= 1
+                    n = self._take()
+                    t[j] = n
+                    pairs.append((-1, n))
+                seen.add(b)
+        return pairs
+
+
+class _WindowOffByOneBlock(AL.BlockAllocator):
+    def _drop_behind_window(self, seq_id):
+        start = self.lens[seq_id] - self.windows[seq_id] + self.block_size
+        t = self.tables[seq_id]
+        for j in range(len(t)):
+            if (j + 1) * self.block_size > start:
+                break
+            if t[j] >= 0:
+                self._release(t[j])
+                t[j] = -1
+
+
+@pytest.mark.parametrize("cls", [_SwapOutKeepsDeviceRefs, _SwapInUnshares, _WindowOffByOneBlock])
+def test_swap_window_mutant_is_caught(monkeypatch, cls):
+    monkeypatch.setattr(AL, "BlockAllocator", cls)
+    assert _caught(P.SWAP_WINDOW_PINS), f"no pin caught {cls.__name__}"
