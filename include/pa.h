@@ -238,6 +238,51 @@ pa_status pa_seq_create_with_prefix(pa_allocator* a, int64_t seq_id, int64_t pre
 pa_status pa_build_masks(const pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t* mask_lo,
                          int32_t* mask_hi);
 
+/* ------------------------------------------------------------------------ *
+ * Swap to a host pool ([IMPL] §3.4: the cache engine keeps a GPU pool and a
+ * CPU pool for swap) and sliding-window release.
+ * ------------------------------------------------------------------------ */
+
+/* (Re)create the host pool: num_host_blocks block ids 0.. with their own FIFO
+ * free queue and counts (the memory is the caller's: pinned host pools of the
+ * device pools' shapes, see pa_swap_blocks).  PA_ERR_INVALID_ARG while any
+ * sequence is swapped out. */
+pa_status pa_allocator_set_host_pool(pa_allocator* a, int32_t num_host_blocks);
+
+/* Move a group of sequences to the host pool.  Every distinct device block of
+ * their tables (table order, first appearance; -1 entries skipped) takes the
+ * head of the host queue; pairs[2i], pairs[2i+1] = (device id, host id) for
+ * the copy (pa_swap_blocks from the device pools into the host pools); each
+ * reference the group held moves to the host block, and a device block goes
+ * back to the free queue when nothing else holds it.  Blocks shared inside
+ * the group stay shared; blocks shared with sequences outside it are copied
+ * and keep their other references.  pairs: host int32 [capacity, 2].
+ * Duplicated ids count once.  A swapped sequence can only be swapped in or
+ * freed (other verbs: PA_ERR_INVALID_ARG).  All-or-nothing
+ * (PA_ERR_NO_FREE_BLOCKS when the host pool is short). */
+pa_status pa_seq_swap_out(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t* pairs, int32_t capacity,
+                          int32_t* num_pairs);
+
+/* The mirror image: every distinct host block of a swapped group takes the
+ * head of the device queue; pairs = (host id, device id); host blocks go back
+ * to the host queue when free. */
+pa_status pa_seq_swap_in(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t* pairs, int32_t capacity,
+                         int32_t* num_pairs);
+
+/* Host queue, head first, and a host block's count (-1 outside the pool). */
+pa_status pa_host_free_list(const pa_allocator* a, int32_t* out, int32_t capacity, int32_t* n);
+int32_t pa_host_ref_count(const pa_allocator* a, int32_t block);
+
+/* Sliding window ([SRC-1] §六 lists it): only the last `window` positions of
+ * the sequence stay live.  Every block whose positions all lie before
+ * len - window is released and its table entry becomes -1, now and after
+ * every append; pa_build_masks then gives [0, len - window) for
+ * pa_decode_masked, which never reads those blocks.  A fork keeps the window
+ * and fails (PA_ERR_INVALID_ARG) when its own window needs a released block.
+ * PA_ERR_INVALID_ARG for window < 1, a swapped sequence or one with a prefix
+ * hole. */
+pa_status pa_seq_set_window(pa_allocator* a, int64_t seq_id, int32_t window);
+
 /* ======================================================================== *
  * Device operations                                                         *
  * ======================================================================== */

@@ -203,9 +203,12 @@ class BlockAllocator:
 
     def seq_append_slots(self, seq_ids):
         """Append one token to each sequence, in order.  Returns (slots, pairs).  All-or-nothing."""
-        saved = copy.deepcopy((self.free, self.refs, self.tables, self.lens, self.stats))
         for s in seq_ids:
             self._need(s)
+        for s in seq_ids:
+            if s in self.swapped:
+                raise AllocatorError(INVALID_ARG, "a sequence in the batch is swapped out")
+        saved = copy.deepcopy((self.free, self.refs, self.tables, self.lens, self.stats))
         try:
             slots, pairs = [], []
             for s in seq_ids:

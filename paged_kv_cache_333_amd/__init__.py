@@ -91,6 +91,12 @@ _PROTOS = {
     "pa_prefix_info": (_i32, [_vp, _i64, _pi32, _i32, _pi32, _pi32, _pi32]),
     "pa_seq_create_with_prefix": (_i32, [_vp, _i64, _i64, _i32]),
     "pa_build_masks": (_i32, [_vp, _pi64, _i32, _pi32, _pi32]),
+    "pa_allocator_set_host_pool": (_i32, [_vp, _i32]),
+    "pa_seq_swap_out": (_i32, [_vp, _pi64, _i32, _pi32, _i32, _pi32]),
+    "pa_seq_swap_in": (_i32, [_vp, _pi64, _i32, _pi32, _i32, _pi32]),
+    "pa_host_free_list": (_i32, [_vp, _pi32, _i32, _pi32]),
+    "pa_host_ref_count": (_i32, [_vp, _i32]),
+    "pa_seq_set_window": (_i32, [_vp, _i64, _i32]),
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_order_longest_first": (_i32, [_pi32, _i32, _pi32]),
@@ -556,6 +562,45 @@ class Allocator:
         lo, hi = (C.c_int32 * max(n, 1))(), (C.c_int32 * max(n, 1))()
         _check(lib.pa_build_masks(self._h, ids, n, lo, hi), "pa_build_masks")
         return list(lo[:n]), list(hi[:n])
+
+    # -- swap and sliding window ------------------------------------------------
+    def set_host_pool(self, num_host_blocks: int):
+        _check(lib.pa_allocator_set_host_pool(self._h, num_host_blocks), "pa_allocator_set_host_pool")
+
+    def _swap(self, fn, seq_ids, where):
+        n = len(seq_ids)
+        ids = (C.c_int64 * max(n, 1))(*seq_ids)
+        cap = 0
+        for s in set(seq_ids):
+            try:
+                cap += len(self.block_table(s))
+            except PAError:
+                pass
+        buf = (C.c_int32 * max(2 * cap, 2))()
+        k = C.c_int32()
+        _check(fn(self._h, ids, n, buf, cap, C.byref(k)), where)
+        return [(buf[2 * i], buf[2 * i + 1]) for i in range(k.value)]
+
+    def seq_swap_out(self, seq_ids):
+        """Move a group to the host pool; returns the (device, host) copy pairs."""
+        return self._swap(lib.pa_seq_swap_out, seq_ids, "pa_seq_swap_out")
+
+    def seq_swap_in(self, seq_ids):
+        """Move a swapped group back; returns the (host, device) copy pairs."""
+        return self._swap(lib.pa_seq_swap_in, seq_ids, "pa_seq_swap_in")
+
+    def host_free_list(self) -> list:
+        n = C.c_int32()
+        cap = 1 << 20
+        buf = (C.c_int32 * cap)()
+        _check(lib.pa_host_free_list(self._h, buf, cap, C.byref(n)), "pa_host_free_list")
+        return list(buf[:n.value])
+
+    def host_ref_count(self, block: int) -> int:
+        return lib.pa_host_ref_count(self._h, block)
+
+    def seq_set_window(self, seq_id: int, window: int):
+        _check(lib.pa_seq_set_window(self._h, seq_id, window), "pa_seq_set_window")
 
     def stats(self) -> dict:
         st = pa_allocator_stats()

@@ -18,6 +18,11 @@
 // shares its blocks and puts its own tokens from the next block boundary on,
 // leaving a hole [n_p, P * bs) that decode masks.
 //
+// Swap ("PagedAttention 实现细节" §3.4: a GPU pool and a CPU pool for swap): a
+// host pool with its own FIFO queue and counts; a group of sequences moves
+// whole, one copy pair per distinct block.  Sliding window: blocks wholly
+// before the last W positions are released and their entries become -1.
+//
 // The free queue is a ring buffer of num_blocks entries; a block is never in
 // it twice, so it never overflows.
 #include <algorithm>
@@ -25,6 +30,7 @@
 #include <numeric>
 #include <mutex>
 #include <unordered_map>
+#include <unordered_set>
 #include <vector>
 
 #include "status.hpp"
@@ -35,6 +41,9 @@ struct Seq {
   std::vector<int32_t> table;
   int32_t len = 0;
   int32_t hole_lo = 0, hole_hi = 0;  // positions [lo, hi) hold no token (lo == hi: none)
+  int32_t window = 0;                // > 0: only the last `window` positions are live
+  int32_t first_live = 0;            // table entries below it are -1 (released behind the window)
+  bool swapped = false;              // the table holds host-pool ids
 };
 
 struct PrefixEntry {
@@ -71,6 +80,11 @@ struct pa_allocator {
   std::unordered_map<int64_t, PrefixEntry> prefixes;                 // by entry id
   std::unordered_map<std::vector<int32_t>, int64_t, TokensHash> prefix_ids;  // by tokens
   int64_t next_prefix_id = 1;
+  // host pool (swap): FIFO queue and counts, like the device pool
+  int32_t num_host = 0;
+  std::vector<int32_t> host_ring, host_refs;
+  int32_t host_head = 0, host_count = 0;
+  int32_t num_swapped = 0;
   pa_allocator_stats stats{0, 0, 0};
   mutable std::mutex mu;
 
@@ -93,6 +107,19 @@ struct pa_allocator {
   }
   void release(int32_t b) {
     if (--refs[b] == 0) push_tail(b);
+  }
+  int32_t host_pop() {
+    int32_t h = host_ring[host_head];
+    host_head = host_head + 1 == num_host ? 0 : host_head + 1;
+    --host_count;
+    host_refs[h] = 0;
+    return h;
+  }
+  void host_release(int32_t h) {
+    if (--host_refs[h] == 0) {
+      host_ring[(static_cast<int64_t>(host_head) + host_count) % num_host] = h;
+      ++host_count;
+    }
   }
 };
 
@@ -148,6 +175,23 @@ pa_status append_one(pa_allocator* a, Seq& s, int32_t* slot, int32_t* src, int32
   }
   *slot = s.table[lb] * bs + L % bs;
   s.len = L + 1;
+  if (s.window > 0) {
+    // release the blocks that fell wholly behind the window
+    const int64_t start = static_cast<int64_t>(s.len) - s.window;
+    while (s.first_live < static_cast<int32_t>(s.table.size()) &&
+           static_cast<int64_t>(s.first_live + 1) * bs <= start) {
+      const int32_t b = s.table[s.first_live];
+      if (b >= 0) {
+        if (j) {
+          j->seqs.push_back({&s, L, s.first_live, b, false});
+          j->refs.push_back({b, a->refs[b]});
+        }
+        a->release(b);
+        s.table[s.first_live] = -1;
+      }
+      ++s.first_live;
+    }
+  }
   return PA_OK;
 }
 
@@ -158,10 +202,48 @@ void rollback(pa_allocator* a, Journal& j) {
     if (it->appended) s.table.pop_back();
     else if (it->old_block >= 0) s.table[it->index] = it->old_block;
     s.len = it->old_len;
+    if (s.window > 0 && it->index < s.first_live && !it->appended && it->old_block >= 0 &&
+        s.table[it->index] >= 0)
+      s.first_live = it->index;  // a released entry is back: the live range starts there again
   }
   a->head = j.head;
   a->count = j.count;
   a->stats = j.stats;
+}
+
+// Release the blocks wholly behind the sequence's window (a fresh window or a
+// fork; appends do the same inside append_one, under the journal).
+void drop_behind_window(pa_allocator* a, Seq& s) {
+  const int64_t start = static_cast<int64_t>(s.len) - s.window;
+  while (s.first_live < static_cast<int32_t>(s.table.size()) &&
+         static_cast<int64_t>(s.first_live + 1) * a->block_size <= start) {
+    const int32_t b = s.table[s.first_live];
+    if (b >= 0) {
+      a->release(b);
+      s.table[s.first_live] = -1;
+    }
+    ++s.first_live;
+  }
+}
+
+// The sequences of a swap group (duplicates ignored, first appearance kept),
+// checked, and their distinct non-negative table entries in order.
+pa_status swap_group(pa_allocator* a, const int64_t* seq_ids, int32_t n, bool swapped, std::vector<Seq*>* group,
+                     std::vector<int32_t>* distinct) {
+  std::unordered_set<int64_t> seen_ids;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!seen_ids.insert(seq_ids[i]).second) continue;
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence in the group");
+    if (it->second.swapped != swapped)
+      return fail(PA_ERR_INVALID_ARG, swapped ? "sequence is not swapped out" : "sequence already swapped out");
+    group->push_back(&it->second);
+  }
+  std::unordered_set<int32_t> seen;
+  for (Seq* s : *group)
+    for (int32_t b : s->table)
+      if (b >= 0 && seen.insert(b).second) distinct->push_back(b);
+  return PA_OK;
 }
 
 }  // namespace
@@ -217,6 +299,12 @@ pa_status pa_allocator_clone(const pa_allocator* a, pa_allocator** out) {
   c->prefixes = a->prefixes;
   c->prefix_ids = a->prefix_ids;
   c->next_prefix_id = a->next_prefix_id;
+  c->num_host = a->num_host;
+  c->host_ring = a->host_ring;
+  c->host_refs = a->host_refs;
+  c->host_head = a->host_head;
+  c->host_count = a->host_count;
+  c->num_swapped = a->num_swapped;
   c->stats = a->stats;
   *out = c;
   return PA_OK;
@@ -244,19 +332,28 @@ pa_status pa_seq_fork(pa_allocator* a, int64_t parent, int64_t child, int32_t nu
   if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown parent sequence");
   if (a->seqs.count(child)) return fail(PA_ERR_SEQ_EXISTS, "child id already in use");
   const Seq& p = it->second;
+  if (p.swapped) return fail(PA_ERR_INVALID_ARG, "parent is swapped out");
   int32_t n = num_tokens < 0 ? p.len : num_tokens;
   if (n > p.len) return fail(PA_ERR_INVALID_ARG, "fork length beyond the parent's length");
   if (p.hole_lo < n && n < p.hole_hi) return fail(PA_ERR_INVALID_ARG, "fork length inside the prefix hole");
-  Seq c;
   int32_t nb = a->blocks_for(n);
+  if (p.window > 0) {
+    const int32_t first_live = std::max(0, n - p.window) / a->block_size;
+    for (int32_t j = first_live; j < nb; ++j)
+      if (p.table[j] < 0) return fail(PA_ERR_INVALID_ARG, "the child's window needs blocks the parent dropped");
+  }
+  Seq c;
   c.table.assign(p.table.begin(), p.table.begin() + nb);
   c.len = n;
   if (p.hole_lo < p.hole_hi && n >= p.hole_hi) {
     c.hole_lo = p.hole_lo;
     c.hole_hi = p.hole_hi;
   }
-  for (int32_t b : c.table) ++a->refs[b];
-  a->seqs.emplace(child, std::move(c));
+  for (int32_t b : c.table)
+    if (b >= 0) ++a->refs[b];
+  c.window = p.window;
+  auto ins = a->seqs.emplace(child, std::move(c));
+  if (p.window > 0) drop_behind_window(a, ins.first->second);
   return PA_OK;
 }
 
@@ -266,6 +363,7 @@ pa_status pa_seq_append_slot(pa_allocator* a, int64_t seq_id, int32_t* slot, int
   std::lock_guard<std::mutex> g(a->mu);
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence");
+  if (it->second.swapped) return fail(PA_ERR_INVALID_ARG, "sequence is swapped out");
   return append_one(a, it->second, slot, cow_src, cow_dst, nullptr);
 }
 
@@ -280,6 +378,8 @@ pa_status pa_seq_append_slots(pa_allocator* a, const int64_t* seq_ids, int32_t n
     if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence in batch");
     ptrs[i] = &it->second;
   }
+  for (int32_t i = 0; i < n; ++i)
+    if (ptrs[i]->swapped) return fail(PA_ERR_INVALID_ARG, "a sequence in the batch is swapped out");
   // Each append needs at most one block: with n free blocks nothing can fail
   // for lack of blocks and the journal is skipped.
   Journal journal;
@@ -313,7 +413,13 @@ pa_status pa_seq_free(pa_allocator* a, int64_t seq_id) {
   std::lock_guard<std::mutex> g(a->mu);
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence");
-  for (int32_t b : it->second.table) a->release(b);
+  const Seq& sq = it->second;
+  for (int32_t b : sq.table) {
+    if (b < 0) continue;  // released behind a window
+    if (sq.swapped) a->host_release(b);
+    else a->release(b);
+  }
+  if (sq.swapped) --a->num_swapped;
   a->seqs.erase(it);
   return PA_OK;
 }
@@ -382,6 +488,7 @@ pa_status pa_build_block_tables(const pa_allocator* a, const int64_t* seq_ids, i
   for (int32_t i = 0; i < n; ++i) {
     auto it = a->seqs.find(seq_ids[i]);
     if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence");
+    if (it->second.swapped) return fail(PA_ERR_INVALID_ARG, "sequence is swapped out");
     if (static_cast<int64_t>(it->second.table.size()) > max_blocks)
       return fail(PA_ERR_INVALID_ARG, "a block table is longer than max_blocks");
     ptrs[i] = &it->second;
@@ -505,10 +612,130 @@ pa_status pa_build_masks(const pa_allocator* a, const int64_t* seq_ids, int32_t 
     ptrs[i] = &it->second;
   }
   for (int32_t i = 0; i < n; ++i) {
-    mask_lo[i] = ptrs[i]->hole_lo;
-    mask_hi[i] = ptrs[i]->hole_hi;
+    if (ptrs[i]->window > 0) {
+      mask_lo[i] = 0;
+      mask_hi[i] = std::max(0, ptrs[i]->len - ptrs[i]->window);
+    } else {
+      mask_lo[i] = ptrs[i]->hole_lo;
+      mask_hi[i] = ptrs[i]->hole_hi;
+    }
   }
   return PA_OK;
+}
+
+pa_status pa_seq_set_window(pa_allocator* a, int64_t seq_id, int32_t window) {
+  if (!a) return fail(PA_ERR_INVALID_ARG, "null allocator");
+  std::lock_guard<std::mutex> g(a->mu);
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence");
+  if (window < 1) return fail(PA_ERR_INVALID_ARG, "window < 1");
+  Seq& s = it->second;
+  if (s.swapped || s.hole_lo < s.hole_hi)
+    return fail(PA_ERR_INVALID_ARG, "window on a swapped sequence or one with a prefix hole");
+  s.window = window;
+  drop_behind_window(a, s);
+  return PA_OK;
+}
+
+pa_status pa_allocator_set_host_pool(pa_allocator* a, int32_t num_host_blocks) {
+  if (!a) return fail(PA_ERR_INVALID_ARG, "null allocator");
+  std::lock_guard<std::mutex> g(a->mu);
+  if (num_host_blocks < 0) return fail(PA_ERR_INVALID_ARG, "num_host_blocks < 0");
+  if (a->num_swapped > 0) return fail(PA_ERR_INVALID_ARG, "sequences are swapped out");
+  a->num_host = num_host_blocks;
+  a->host_ring.resize(num_host_blocks);
+  for (int32_t i = 0; i < num_host_blocks; ++i) a->host_ring[i] = i;
+  a->host_refs.assign(num_host_blocks, 0);
+  a->host_head = 0;
+  a->host_count = num_host_blocks;
+  return PA_OK;
+}
+
+pa_status pa_seq_swap_out(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t* pairs, int32_t capacity,
+                          int32_t* num_pairs) {
+  if (!a || !num_pairs || n < 0 || capacity < 0 || (n > 0 && !seq_ids) || (capacity > 0 && !pairs))
+    return fail(PA_ERR_INVALID_ARG, "null argument or negative count");
+  std::lock_guard<std::mutex> g(a->mu);
+  std::vector<Seq*> group;
+  std::vector<int32_t> distinct;
+  pa_status st = swap_group(a, seq_ids, n, false, &group, &distinct);
+  if (st != PA_OK) return st;
+  const int32_t k = static_cast<int32_t>(distinct.size());
+  if (k > a->host_count) return fail(PA_ERR_NO_FREE_BLOCKS, "not enough free host blocks");
+  if (k > capacity) return fail(PA_ERR_INVALID_ARG, "pairs capacity too small");
+  std::unordered_map<int32_t, int32_t> where;
+  for (int32_t i = 0; i < k; ++i) {
+    const int32_t h = a->host_pop();
+    where[distinct[i]] = h;
+    pairs[2 * i] = distinct[i];
+    pairs[2 * i + 1] = h;
+  }
+  for (Seq* s : group) {
+    for (int32_t& b : s->table) {
+      if (b < 0) continue;
+      const int32_t h = where[b];
+      ++a->host_refs[h];
+      a->release(b);
+      b = h;
+    }
+    s->swapped = true;
+    ++a->num_swapped;
+  }
+  *num_pairs = k;
+  return PA_OK;
+}
+
+pa_status pa_seq_swap_in(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t* pairs, int32_t capacity,
+                         int32_t* num_pairs) {
+  if (!a || !num_pairs || n < 0 || capacity < 0 || (n > 0 && !seq_ids) || (capacity > 0 && !pairs))
+    return fail(PA_ERR_INVALID_ARG, "null argument or negative count");
+  std::lock_guard<std::mutex> g(a->mu);
+  std::vector<Seq*> group;
+  std::vector<int32_t> distinct;
+  pa_status st = swap_group(a, seq_ids, n, true, &group, &distinct);
+  if (st != PA_OK) return st;
+  const int32_t k = static_cast<int32_t>(distinct.size());
+  if (k > a->count) return fail(PA_ERR_NO_FREE_BLOCKS, "not enough free device blocks");
+  if (k > capacity) return fail(PA_ERR_INVALID_ARG, "pairs capacity too small");
+  std::unordered_map<int32_t, int32_t> where;
+  for (int32_t i = 0; i < k; ++i) {
+    const int32_t d = a->pop_head();
+    a->refs[d] = 0;
+    where[distinct[i]] = d;
+    pairs[2 * i] = distinct[i];
+    pairs[2 * i + 1] = d;
+  }
+  for (Seq* s : group) {
+    for (int32_t& h : s->table) {
+      if (h < 0) continue;
+      const int32_t d = where[h];
+      ++a->refs[d];
+      a->host_release(h);
+      h = d;
+    }
+    s->swapped = false;
+    --a->num_swapped;
+  }
+  *num_pairs = k;
+  return PA_OK;
+}
+
+pa_status pa_host_free_list(const pa_allocator* a, int32_t* out, int32_t capacity, int32_t* n) {
+  if (!a || !n || capacity < 0 || (capacity > 0 && !out))
+    return fail(PA_ERR_INVALID_ARG, "null argument or negative capacity");
+  std::lock_guard<std::mutex> g(a->mu);
+  if (a->host_count > capacity) return fail(PA_ERR_INVALID_ARG, "capacity too small");
+  for (int32_t i = 0; i < a->host_count; ++i)
+    out[i] = a->host_ring[(static_cast<int64_t>(a->host_head) + i) % a->num_host];
+  *n = a->host_count;
+  return PA_OK;
+}
+
+int32_t pa_host_ref_count(const pa_allocator* a, int32_t block) {
+  if (!a) return -1;
+  std::lock_guard<std::mutex> g(a->mu);
+  if (block < 0 || block >= a->num_host) return -1;
+  return a->host_refs[block];
 }
 
 pa_status pa_order_longest_first(const int32_t* context_lens, int32_t n, int32_t* order) {

@@ -213,3 +213,70 @@ def test_random_prefix_ops_bit_exact(seed):
     same_state(cpp, ora)
     c2, o2 = cpp.clone(), ora.clone()
     same_state(c2, o2)
+
+
+def same_host_state(cpp, ora):
+    assert cpp.host_free_list() == ora.host_free_list()
+    assert [cpp.host_ref_count(h) for h in range(len(ora.host_refs))] == ora.host_refs
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_random_swap_and_window_ops_bit_exact(seed):
+    rng = np.random.default_rng(200 + seed)
+    NB = int(rng.integers(12, 120))
+    NH = int(rng.integers(4, 80))
+    bs = int(rng.choice([4, 8, 16]))
+    order = rng.permutation(NB)
+    cpp = pa.Allocator(NB, bs, order)
+    ora = AL.BlockAllocator(NB, bs, order)
+    cpp.set_host_pool(NH)
+    ora.set_host_pool(NH)
+    live, nxt = [], 0
+    for step in range(1500):
+        op = int(rng.integers(0, 10))
+        if op == 0 or not live:
+            n = int(rng.integers(0, 6 * bs))
+            if both(lambda: cpp.seq_create(nxt, n), lambda: ora.seq_create(nxt, n)) is None:
+                live.append(nxt)
+            nxt += 1
+        elif op == 1:
+            p = live[int(rng.integers(len(live)))]
+            n = int(rng.integers(-1, ora.lens[p] + 2))
+            if both(lambda: cpp.seq_fork(p, nxt, n), lambda: ora.seq_fork(p, nxt, n)) is None:
+                live.append(nxt)
+            nxt += 1
+        elif op in (2, 3):
+            ids = [live[i] for i in rng.integers(0, len(live), size=int(rng.integers(1, 5)))]
+            both(lambda: cpp.seq_append_slots(ids), lambda: ora.seq_append_slots(ids))
+        elif op == 4:
+            s = live[int(rng.integers(len(live)))]
+            w = int(rng.integers(0, 4 * bs))
+            both(lambda: cpp.seq_set_window(s, w), lambda: ora.seq_set_window(s, w))
+        elif op == 5:
+            grp = [live[i] for i in rng.integers(0, len(live), size=int(rng.integers(1, 4)))]
+            both(lambda: cpp.seq_swap_out(grp), lambda: ora.seq_swap_out(grp))
+        elif op == 6:
+            grp = [live[i] for i in rng.integers(0, len(live), size=int(rng.integers(1, 4)))]
+            both(lambda: cpp.seq_swap_in(grp), lambda: ora.seq_swap_in(grp))
+        elif op == 7:
+            s = live.pop(int(rng.integers(len(live))))
+            both(lambda: cpp.seq_free(s), lambda: ora.seq_free(s))
+        elif op == 8:
+            s = live[int(rng.integers(len(live)))]
+            both(lambda: cpp.seq_append_slot(s), lambda: ora.seq_append_slot(s))
+        else:
+            ids = [s for s in live if s not in ora.swapped]
+            if ids:
+                mb = max(len(ora.tables[s]) for s in ids) + 1
+                assert cpp.build_block_tables(ids, mb) == ora.build_block_tables(ids, mb)
+            if ora.swapped:
+                s = sorted(ora.swapped)[0]
+                both(lambda: cpp.build_block_tables([s], 999), lambda: ora.build_block_tables([s], 999))
+        if step % 20 == 0:
+            same_state(cpp, ora)
+            same_host_state(cpp, ora)
+    same_state(cpp, ora)
+    same_host_state(cpp, ora)
+    c2, o2 = cpp.clone(), ora.clone()
+    same_state(c2, o2)
+    same_host_state(c2, o2)
