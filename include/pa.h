@@ -311,6 +311,23 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* pair
                          int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
                          int32_t head_dim, int32_t block_size, pa_dtype dtype, void* stream);
 
+/* Swap copies ([IMPL] §3.4, the GPU and CPU pools of the cache engine):
+ * block pairs[2p] of the source pools -> block pairs[2p+1] of the destination
+ * pools, for p < num_pairs, K and V, whole blocks (the pairs pa_seq_swap_out
+ * and pa_seq_swap_in return).  Each side is either device memory or
+ * page-locked host memory (hipHostMalloc, or torch's pin_memory()) of the
+ * pools' shapes with num_src_blocks / num_dst_blocks blocks; K and V of one
+ * side live in the same kind of memory.  pairs: device memory or page-locked
+ * host memory, int32 [num_pairs, 2], read on the device when the copy runs.
+ * Host memory is read with system-scope loads; host-side results are visible
+ * once the stream has finished.  Pairs with an id outside its pool are
+ * skipped.  dtype: the pools' element type (8-bit code types included).
+ * PA_ERR_INVALID_ARG when a pointer is neither kind.  Bit-exact. */
+pa_status pa_swap_blocks(void* dst_key_cache, void* dst_value_cache, const void* src_key_cache,
+                         const void* src_value_cache, const int32_t* pairs, int32_t num_pairs,
+                         int32_t num_src_blocks, int32_t num_dst_blocks, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, pa_dtype dtype, void* stream);
+
 /* Move one step's index data (block tables, context lengths, slot mapping,
  * copy pairs, launch order) from page-locked host memory to the device with a
  * kernel on `stream`, instead of a copy-engine transfer.  This is the upload

@@ -8,7 +8,7 @@ built (python paged_kv_cache_333_amd/build.py): there is no fallback.
 Names follow the C ABI in include/pa.h:
   pa_reshape_and_cache, pa_copy_blocks, pa_upload, pa_decode, pa_decode_split, pa_decode_auto,
   pa_decode_append, pa_reshape_and_cache_quant, pa_decode_quant, pa_decode_masked, pa_decode_multi,
-  pa_decode_multi_workspace_bytes,
+  pa_decode_multi_workspace_bytes, pa_swap_blocks,
   pa_decode_split_workspace_bytes, pa_lse_reduce, and the allocator verbs as
   methods of `Allocator` (pa_seq_create -> Allocator.seq_create, ...).
 """
@@ -101,6 +101,7 @@ _PROTOS = {
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_order_longest_first": (_i32, [_pi32, _i32, _pi32]),
     "pa_upload": (_i32, [_vp, _vp, _sz, _vp]),
+    "pa_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                          _f32, _i32, _u32, _vp]),
     "pa_decode_split_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -229,6 +230,22 @@ def pa_reshape_and_cache_quant(key, value, key_cache, value_cache, slot_mapping,
                                           _ptr(slot_mapping), slot_mapping.numel(), NB, H_kv, D, bs,
                                           _dtype_code(key), _kv_format(key_cache, kv_format), k_scale, v_scale,
                                           _stream(stream)), "pa_reshape_and_cache_quant")
+
+
+def pa_swap_blocks(dst_key_cache, dst_value_cache, src_key_cache, src_value_cache, pairs, stream=None,
+                   num_pairs=None):
+    """Whole-block copies pairs[p] = (src id, dst id) between two pools of the same block shape,
+    each on the device or in pinned host memory (swap out: device -> host; swap in: host ->
+    device).  pairs: int32 [P, 2] on the device or pinned."""
+    NB_d, H_kv, bs, D = _pool_dims(dst_key_cache, dst_value_cache)
+    NB_s = _pool_dims(src_key_cache, src_value_cache)[0]
+    if tuple(src_key_cache.shape[1:]) != (H_kv, bs, D) or src_key_cache.dtype != dst_key_cache.dtype:
+        raise ValueError("source and destination pools differ in block shape or dtype")
+    P = pairs.shape[0] if num_pairs is None else num_pairs
+    code = PA_FP8_E4M3 if dst_key_cache.element_size() == 1 else _dtype_code(dst_key_cache)
+    _check(lib.pa_swap_blocks(_ptr(dst_key_cache), _ptr(dst_value_cache), _ptr(src_key_cache),
+                              _ptr(src_value_cache), _ptr(pairs), P, NB_s, NB_d, H_kv, D, bs, code,
+                              _stream(stream)), "pa_swap_blocks")
 
 
 def pa_upload(dst, src, stream=None):

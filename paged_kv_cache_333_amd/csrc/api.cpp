@@ -303,6 +303,55 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* pair
                 st, "pa_copy_blocks");
 }
 
+namespace {
+// Device view of a buffer for a kernel: device memory as it is, page-locked
+// host memory through its mapping.  kind: 0 device, 1 host; -1 if neither.
+int device_view(const void* p, const void** view) {
+  hipPointerAttribute_t at{};
+  const bool ok = hipPointerGetAttributes(&at, p) == hipSuccess;
+  (void)hipGetLastError();
+  if (!ok) return -1;
+  if (at.type == hipMemoryTypeDevice) {
+    *view = p;
+    return 0;
+  }
+  if (at.type == hipMemoryTypeHost && at.devicePointer) {
+    *view = at.devicePointer;
+    return 1;
+  }
+  return -1;
+}
+}  // namespace
+
+pa_status pa_swap_blocks(void* dst_key_cache, void* dst_value_cache, const void* src_key_cache,
+                         const void* src_value_cache, const int32_t* pairs, int32_t num_pairs,
+                         int32_t num_src_blocks, int32_t num_dst_blocks, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, pa_dtype dtype, void* stream) {
+  pa_status s = check_shape(is_code_type(dtype) ? PA_F16 : dtype, head_dim, block_size);
+  if (s != PA_OK) return s;
+  if (num_pairs < 0 || num_src_blocks < 0 || num_dst_blocks < 0 || num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID_ARG, "negative size or zero heads");
+  if (num_pairs == 0) return PA_OK;
+  if (!dst_key_cache || !dst_value_cache || !src_key_cache || !src_value_cache || !pairs)
+    return fail(PA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(dst_key_cache) || !aligned16(dst_value_cache) || !aligned16(src_key_cache) ||
+      !aligned16(src_value_cache))
+    return fail(PA_ERR_INVALID_ARG, "pools must be 16-byte aligned");
+  const void *dk = nullptr, *dv = nullptr, *sk = nullptr, *sv = nullptr, *pv = nullptr;
+  const int kdk = device_view(dst_key_cache, &dk), kdv = device_view(dst_value_cache, &dv);
+  const int ksk = device_view(src_key_cache, &sk), ksv = device_view(src_value_cache, &sv);
+  const int kp = device_view(pairs, &pv);
+  if (kdk < 0 || kdv < 0 || ksk < 0 || ksv < 0 || kp < 0)
+    return fail(PA_ERR_INVALID_ARG, "pools and pairs must be device memory or page-locked host memory");
+  if (kdk != kdv || ksk != ksv) return fail(PA_ERR_INVALID_ARG, "K and V pools of one side must live together");
+  const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return finish(pa::launch_swap_blocks(const_cast<void*>(dk), const_cast<void*>(dv), sk, sv,
+                                       static_cast<const int32_t*>(pv), num_pairs, num_src_blocks, num_dst_blocks,
+                                       block_bytes, ksk == 1, st),
+                st, "pa_swap_blocks");
+}
+
 pa_status pa_upload(void* dst, const void* src, size_t nbytes, void* stream) {
   if (nbytes == 0) return PA_OK;
   if (!dst || !src) return fail(PA_ERR_INVALID_ARG, "null pointer");

@@ -126,6 +126,62 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ key
   for (; i < chunks_per_block; i += stride) store16(d + i * 16, load16(s + i * 16));
 }
 
+// Swap copies ("PagedAttention 实现细节" §3.4: blocks move between the GPU
+// pool and the CPU pool): block pairs[2p] of the source pools -> block
+// pairs[2p+1] of the destination pools, K and V, whole blocks.  One side is
+// page-locked host memory mapped for the device (either side may be).  Reads
+// of host memory, and of the pairs, are system-scope loads, so the copy sees
+// what the host (or an earlier swap) wrote whatever the mapping's caching;
+// writes to host memory are visible to the host once the stream has finished.
+// grid.x = pair * groups_per_pair + group, grid.y = pool (K or V).
+template <bool SRC_HOST>
+__global__ __launch_bounds__(256) void swap_blocks_kernel(char* __restrict__ dst_key, char* __restrict__ dst_value,
+                                                          const char* src_key, const char* src_value,
+                                                          const int32_t* pairs, int32_t num_src_blocks,
+                                                          int32_t num_dst_blocks, int64_t chunks_per_block,
+                                                          int32_t groups_per_pair) {
+  const int32_t p = blockIdx.x / groups_per_pair;
+  const int32_t grp = blockIdx.x - p * groups_per_pair;
+  const int32_t src = __hip_atomic_load(pairs + 2 * p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  const int32_t dst = __hip_atomic_load(pairs + 2 * p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (src < 0 || src >= num_src_blocks || dst < 0 || dst >= num_dst_blocks) return;
+  const char* s = (blockIdx.y == 0 ? src_key : src_value) + static_cast<int64_t>(src) * chunks_per_block * 16;
+  char* d = (blockIdx.y == 0 ? dst_key : dst_value) + static_cast<int64_t>(dst) * chunks_per_block * 16;
+  const int64_t stride = static_cast<int64_t>(groups_per_pair) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(grp) * blockDim.x + threadIdx.x; i < chunks_per_block; i += stride) {
+    u32x4 v;
+    if constexpr (SRC_HOST) {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(s + i * 16);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = __hip_atomic_load(w + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    } else {
+      v = load16(s + i * 16);
+    }
+    store16(d + i * 16, v);
+  }
+}
+
+hipError_t launch_swap_blocks(void* dst_key, void* dst_value, const void* src_key, const void* src_value,
+                              const int32_t* pairs, int32_t num_pairs, int32_t num_src_blocks,
+                              int32_t num_dst_blocks, int64_t block_bytes, bool src_host, hipStream_t stream) {
+  if (num_pairs == 0) return hipSuccess;
+  const int64_t chunks = block_bytes / 16;
+  int64_t gx = (chunks + 1023) / 1024;
+  if (gx < 1) gx = 1;
+  const dim3 grid(static_cast<uint32_t>(gx * num_pairs), 2);
+#define PA_SWAP(H)                                                                                           \
+  hipLaunchKernelGGL(swap_blocks_kernel<H>, grid, dim3(256), 0, stream, static_cast<char*>(dst_key),         \
+                     static_cast<char*>(dst_value), static_cast<const char*>(src_key),                      \
+                     static_cast<const char*>(src_value), pairs, num_src_blocks, num_dst_blocks, chunks,      \
+                     static_cast<int32_t>(gx))
+  if (src_host)
+    PA_SWAP(true);
+  else
+    PA_SWAP(false);
+#undef PA_SWAP
+  return hipGetLastError();
+}
+
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,
                                     void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
                                     int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,

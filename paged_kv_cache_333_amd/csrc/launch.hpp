@@ -55,6 +55,10 @@ hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t*
                               int32_t num_pairs, int32_t num_blocks, int64_t block_bytes,
                               hipStream_t stream);
 hipError_t launch_upload(void* dst, const void* src_device_view, int64_t nbytes, hipStream_t stream);
+// Whole-block copies between two pools (device views of host pools allowed).
+hipError_t launch_swap_blocks(void* dst_key, void* dst_value, const void* src_key, const void* src_value,
+                              const int32_t* pairs, int32_t num_pairs, int32_t num_src_blocks,
+                              int32_t num_dst_blocks, int64_t block_bytes, bool src_host, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeArgs& a, const SplitLayout& ws, hipStream_t stream);
 // Slot-mapping write of one new token per sequence fused into the decode
