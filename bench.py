@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain copy of known size instead (pa_copy_blocks, 1 GiB read + 1 GiB written "
                          "per launch), to scale HBM counters and give a measured copy bandwidth")
+    ap.add_argument("--measure-swap", action="store_true",
+                    help="time pa_swap_blocks between the device pool and a pinned host pool instead "
+                         "(1024 blocks of 256 KiB each way)")
     ap.add_argument("--profile-commands", metavar="OUTDIR",
                     help="print the rocprofv3 commands that profile this workload into OUTDIR (no GPU needed)")
     ap.add_argument("--summarize-profile", metavar="OUTDIR",
@@ -88,6 +91,38 @@ def calibrate_copy(launches: int = 10):
     print(json.dumps({"calibration": "pa_copy_blocks", "launches": launches + 1,
                       "bytes_read_per_launch": per_launch, "bytes_written_per_launch": per_launch,
                       "kernel_us": us, "copy_gbps_read_plus_write": 2 * per_launch / us / 1e3}), flush=True)
+
+
+def measure_swap(launches: int = 10):
+    """Swap bandwidth over the host link: pa_swap_blocks moving 1024 LLaMA-7B-like blocks
+    (128 KiB per block and pool, 256 MiB in all) from the device pool to a pinned host pool
+    and back, timed with HIP events on the stream."""
+    import torch
+
+    import paged_kv_cache_333_amd as pa
+    NB, NH, Hkv, bs, D = 4096, 1024, 32, 16, 128
+    kc = torch.zeros((NB, Hkv, bs, D), dtype=torch.float16, device="cuda")
+    vc = torch.zeros((NB, Hkv, D, bs), dtype=torch.float16, device="cuda")
+    hk = torch.zeros((NH, Hkv, bs, D), dtype=torch.float16).pin_memory()
+    hv = torch.zeros((NH, Hkv, D, bs), dtype=torch.float16).pin_memory()
+    dev_ids = torch.randperm(NB, generator=torch.Generator().manual_seed(7))[:NH].to(torch.int32)
+    out_pairs = torch.stack([dev_ids, torch.arange(NH, dtype=torch.int32)], dim=1).contiguous().cuda()
+    in_pairs = torch.stack([torch.arange(NH, dtype=torch.int32), dev_ids], dim=1).contiguous().cuda()
+    nbytes = NH * Hkv * bs * D * 2 * 2
+    res = {"measurement": "pa_swap_blocks", "blocks": NH, "bytes_per_launch": nbytes}
+    for name, args in (("swap_out", (hk, hv, kc, vc, out_pairs)), ("swap_in", (kc, vc, hk, hv, in_pairs))):
+        pa.pa_swap_blocks(*args)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+        for a, b in ev:
+            a.record()
+            pa.pa_swap_blocks(*args)
+            b.record()
+        torch.cuda.synchronize()
+        us = sum(a.elapsed_time(b) for a, b in ev) / launches * 1e3
+        res[name + "_us"] = us
+        res[name + "_gbps"] = nbytes / us / 1e3
+    print(json.dumps(res), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -455,6 +490,9 @@ def main():
         sys.exit(1)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.measure_swap:
+        measure_swap()
         return
     bench = Bench(args)
     wall, timing = bench.run()

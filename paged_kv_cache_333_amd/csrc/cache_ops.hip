@@ -148,16 +148,29 @@ __global__ __launch_bounds__(256) void swap_blocks_kernel(char* __restrict__ dst
   const char* s = (blockIdx.y == 0 ? src_key : src_value) + static_cast<int64_t>(src) * chunks_per_block * 16;
   char* d = (blockIdx.y == 0 ? dst_key : dst_value) + static_cast<int64_t>(dst) * chunks_per_block * 16;
   const int64_t stride = static_cast<int64_t>(groups_per_pair) * blockDim.x;
-  for (int64_t i = static_cast<int64_t>(grp) * blockDim.x + threadIdx.x; i < chunks_per_block; i += stride) {
-    u32x4 v;
-    if constexpr (SRC_HOST) {
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(s + i * 16);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) v[k] = __hip_atomic_load(w + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    } else {
-      v = load16(s + i * 16);
+  int64_t i = static_cast<int64_t>(grp) * blockDim.x + threadIdx.x;
+  if constexpr (SRC_HOST) {
+    // 16-byte loads at system scope (the sc0 sc1 bits of a system-scope load),
+    // four in flight per lane: each is one host-link read.  The waitcnt takes
+    // the four registers as operands, so nothing uses them before the data is in.
+    for (; i < chunks_per_block; i += 4 * stride) {
+      u32x4 v0{}, v1{}, v2{}, v3{};
+      const bool ok1 = i + stride < chunks_per_block, ok2 = i + 2 * stride < chunks_per_block,
+                 ok3 = i + 3 * stride < chunks_per_block;
+      asm volatile("global_load_dwordx4 %0, %1, off sc0 sc1" : "=v"(v0) : "v"(s + i * 16) : "memory");
+      if (ok1) asm volatile("global_load_dwordx4 %0, %1, off sc0 sc1" : "=v"(v1) : "v"(s + (i + stride) * 16) : "memory");
+      if (ok2)
+        asm volatile("global_load_dwordx4 %0, %1, off sc0 sc1" : "=v"(v2) : "v"(s + (i + 2 * stride) * 16) : "memory");
+      if (ok3)
+        asm volatile("global_load_dwordx4 %0, %1, off sc0 sc1" : "=v"(v3) : "v"(s + (i + 3 * stride) * 16) : "memory");
+      asm volatile("s_waitcnt vmcnt(0)" : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3) : : "memory");
+      store16(d + i * 16, v0);
+      if (ok1) store16(d + (i + stride) * 16, v1);
+      if (ok2) store16(d + (i + 2 * stride) * 16, v2);
+      if (ok3) store16(d + (i + 3 * stride) * 16, v3);
     }
-    store16(d + i * 16, v);
+  } else {
+    for (; i < chunks_per_block; i += stride) store16(d + i * 16, load16(s + i * 16));
   }
 }
 
