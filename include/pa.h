@@ -239,8 +239,8 @@ pa_status pa_build_masks(const pa_allocator* a, const int64_t* seq_ids, int32_t 
                          int32_t* mask_hi);
 
 /* ------------------------------------------------------------------------ *
- * Swap to a host pool ([IMPL] §3.4: the cache engine keeps a GPU pool and a
- * CPU pool for swap) and sliding-window release.
+ * Swap to a host pool ([IMPL] §3.4: the cache engine has a device-side pool
+ * and a host-side one used for swapping) and sliding-window release.
  * ------------------------------------------------------------------------ */
 
 /* (Re)create the host pool: num_host_blocks block ids 0.. with their own FIFO

@@ -49,8 +49,8 @@ PrefixCacheManager):
   token and decode must skip them (`masks`).  A sequence's length counts
   positions, hole included; fork keeps the hole and may not end inside it.
 
-Swap ("PagedAttention 实现细节" §3.4: the cache engine keeps a GPU pool and a
-CPU pool "for swap"):
+Swap ("PagedAttention 实现细节" §3.4: its cache engine holds a device-side pool
+and a host-side pool used for swapping):
 * A second, host-side pool of block ids with its own first-in-first-out free
   queue and counts.  swap_out(group) moves the sequences of a group to it: every
   distinct device block of their tables (table order, first appearance) gets a

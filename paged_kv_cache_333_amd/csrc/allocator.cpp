@@ -18,7 +18,7 @@
 // shares its blocks and puts its own tokens from the next block boundary on,
 // leaving a hole [n_p, P * bs) that decode masks.
 //
-// Swap ("PagedAttention 实现细节" §3.4: a GPU pool and a CPU pool for swap): a
+// Swap ("PagedAttention 实现细节" §3.4: the cache engine has a host-side pool used for swapping): a
 // host pool with its own FIFO queue and counts; a group of sequences moves
 // whole, one copy pair per distinct block.  Sliding window: blocks wholly
 // before the last W positions are released and their entries become -1.
