@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--fused-write", action="store_true",
                     help="write the new K/V inside the decode launch (pa_decode_append, auto path) instead of "
                          "pa_reshape_and_cache before it; measured no faster per step, so off by default")
+    ap.add_argument("--separate-upload", action="store_true",
+                    help="upload the index data and write the new K/V in two launches (pa_upload, then "
+                         "pa_reshape_and_cache) instead of one (pa_upload_and_cache)")
     ap.add_argument("--order", choices=["longest", "index"], default=None,
                     help="launch order of the sequences (default: index for workload 5, whose forked branches "
                          "share blocks and should run side by side; longest-first otherwise)")
@@ -366,13 +369,22 @@ class Bench:
         if self.order == "longest":
             pa.pa_order_longest_first_into(b["len_h"].data_ptr(), S, b["order_h"].data_ptr())
             order = b["order_d"]
-        pa.pa_upload(b["idx_d"], b["idx_h"])
+        r = k % self.newk.shape[0]
+        fused = self.path == "auto" and self.args.fused_write
+        # One launch for the upload and the K/V write when no copy-on-write pair must come
+        # between them (the write may land in a block the copy fills).
+        one_launch = not npairs and not fused and not self.args.separate_upload
+        if one_launch:
+            pa.pa_upload_and_cache(b["idx_d"], b["idx_h"], self.newk[r], self.newv[r], self.kc, self.vc,
+                                   b["slots_h"], w.k_scale, w.v_scale, kv_format=w.kv_format or None)
+        else:
+            pa.pa_upload(b["idx_d"], b["idx_h"])
         b["staged"].record(self.stream)
         if npairs:
             pa.pa_copy_blocks(self.kc, self.vc, b["pairs_d"], num_pairs=npairs)
-        r = k % self.newk.shape[0]
-        fused = self.path == "auto" and self.args.fused_write
-        if self.quant:
+        if one_launch:
+            pass
+        elif self.quant:
             pa.pa_reshape_and_cache_quant(self.newk[r], self.newv[r], self.kc, self.vc, b["slots_d"], w.k_scale,
                                           w.v_scale, kv_format=w.kv_format)
         elif not fused:
@@ -530,8 +542,9 @@ def main():
                    "mean_kv_tokens_per_step": kv_tokens / len(timing),
                    "decode_path": ("auto: " if bench.path == "auto" else "") + "+".join(sorted(bench.path_ran)),
                    "kv_write": "fused into the decode (pa_decode_append)" if fused_write
-                   else ("pa_reshape_and_cache_quant, then pa_decode_quant" if bench.quant
-                         else "pa_reshape_and_cache, then decode"),
+                   else ("upload and write in one launch (pa_upload_and_cache) when the step has no "
+                         "copy-on-write pair, else pa_upload, pa_copy_blocks, write"
+                         if not args.separate_upload else "pa_upload, then the write (two launches)"),
                    "partition_size": args.partition if "split" in bench.path_ran else None,
                    "launch_order": bench.order, "kv_cache_policy": "cached" if bench.cached else "stream",
                    "cow_pairs_per_step": sum(t[4] for t in timing) / len(timing)},

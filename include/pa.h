@@ -345,6 +345,23 @@ pa_status pa_swap_blocks(void* dst_key_cache, void* dst_value_cache, const void*
  * such host memory or dst is not device memory.  Bit-exact. */
 pa_status pa_upload(void* dst, const void* src, size_t nbytes, void* stream);
 
+/* pa_upload and the slot-mapping write of the step's new K/V rows in one
+ * launch (two launches would cost a dependent-dispatch gap between them):
+ * copies nbytes from src (page-locked host memory) to dst (device) as
+ * pa_upload, and writes key/value [num_tokens, num_kv_heads, head_dim] of
+ * `dtype` at the slots slot_mapping[0..num_tokens), which it reads straight
+ * from page-locked host memory (typically inside src).  kv_dtype == dtype:
+ * the write of pa_reshape_and_cache; PA_FP8_E4M3 / PA_INT8: the quantising
+ * write of pa_reshape_and_cache_quant with k_scale, v_scale.  The two parts
+ * are independent: nothing in dst may be needed by the write, and a write
+ * into a block that a copy-on-write pair of the same step copies must wait
+ * for that copy (use pa_upload, pa_copy_blocks, then the write).  Errors as
+ * in pa_upload and the write it stands for.  Bit-exact. */
+pa_status pa_upload_and_cache(void* dst, const void* src, size_t nbytes, const void* key, const void* value,
+                              void* key_cache, void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                              int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              float k_scale, float v_scale, pa_dtype dtype, pa_dtype kv_dtype, void* stream);
+
 /* Single-pass paged decode attention ([IMPL] §3.1 index-based kernel and
  * §3.4 PagedAttention.forward; [ATB] §3.2 PagedAttentionOperation.apply;
  * [ASC] §三/§四 fused gather + QK^T + softmax + OV):

@@ -8,7 +8,7 @@ built (python paged_kv_cache_333_amd/build.py): there is no fallback.
 Names follow the C ABI in include/pa.h:
   pa_reshape_and_cache, pa_copy_blocks, pa_upload, pa_decode, pa_decode_split, pa_decode_auto,
   pa_decode_append, pa_reshape_and_cache_quant, pa_decode_quant, pa_decode_masked, pa_decode_multi,
-  pa_decode_multi_workspace_bytes, pa_swap_blocks,
+  pa_decode_multi_workspace_bytes, pa_swap_blocks, pa_upload_and_cache,
   pa_decode_split_workspace_bytes, pa_lse_reduce, and the allocator verbs as
   methods of `Allocator` (pa_seq_create -> Allocator.seq_create, ...).
 """
@@ -101,6 +101,8 @@ _PROTOS = {
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_order_longest_first": (_i32, [_pi32, _i32, _pi32]),
     "pa_upload": (_i32, [_vp, _vp, _sz, _vp]),
+    "pa_upload_and_cache": (_i32, [_vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
+                                   _f32, _i32, _i32, _vp]),
     "pa_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                          _f32, _i32, _u32, _vp]),
@@ -230,6 +232,22 @@ def pa_reshape_and_cache_quant(key, value, key_cache, value_cache, slot_mapping,
                                           _ptr(slot_mapping), slot_mapping.numel(), NB, H_kv, D, bs,
                                           _dtype_code(key), _kv_format(key_cache, kv_format), k_scale, v_scale,
                                           _stream(stream)), "pa_reshape_and_cache_quant")
+
+
+def pa_upload_and_cache(dst, src, key, value, key_cache, value_cache, slot_mapping_host, k_scale: float = 1.0,
+                        v_scale: float = 1.0, kv_format=None, stream=None):
+    """pa_upload(dst, src) and the slot-mapping write of key, value [T, H_kv, D] in one launch;
+    slot_mapping_host: int32 [T] in pinned host memory (e.g. a view into src).  8-bit pools
+    take the quantising write with k_scale, v_scale."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("pa_upload_and_cache: dst and src differ in size")
+    NB, H_kv, bs, D = _pool_dims(key_cache, value_cache)
+    kv = _kv_format(key_cache, kv_format) if key_cache.element_size() == 1 else _dtype_code(key_cache)
+    _check(lib.pa_upload_and_cache(_ptr(dst), _ptr(src), nbytes, _ptr(key), _ptr(value), _ptr(key_cache),
+                                   _ptr(value_cache), _ptr(slot_mapping_host), slot_mapping_host.numel(), NB, H_kv,
+                                   D, bs, k_scale, v_scale, _dtype_code(key), kv, _stream(stream)),
+           "pa_upload_and_cache")
 
 
 def pa_swap_blocks(dst_key_cache, dst_value_cache, src_key_cache, src_value_cache, pairs, stream=None,

@@ -376,6 +376,50 @@ pa_status pa_upload(void* dst, const void* src, size_t nbytes, void* stream) {
   return finish(pa::launch_upload(dst, first.devicePointer, static_cast<int64_t>(nbytes), st), st, "pa_upload");
 }
 
+pa_status pa_upload_and_cache(void* dst, const void* src, size_t nbytes, const void* key, const void* value,
+                              void* key_cache, void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                              int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              float k_scale, float v_scale, pa_dtype dtype, pa_dtype kv_dtype, void* stream) {
+  pa_status s = check_shape(dtype, head_dim, block_size);
+  if (s != PA_OK) return s;
+  const bool quant = is_code_type(kv_dtype);
+  if (!quant && kv_dtype != dtype)
+    return fail(PA_ERR_UNSUPPORTED, "kv_dtype must equal dtype, or be PA_FP8_E4M3 / PA_INT8");
+  if (quant && (s = check_scales(k_scale, v_scale)) != PA_OK) return s;
+  if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID_ARG, "negative size or zero heads");
+  if ((nbytes & 3u) || (reinterpret_cast<uintptr_t>(dst) & 3u) || (reinterpret_cast<uintptr_t>(src) & 3u))
+    return fail(PA_ERR_INVALID_ARG, "the upload moves whole 4-byte words: pointers and nbytes must be 4-aligned");
+  if (nbytes == 0 && num_tokens == 0) return PA_OK;
+  const void* src_view = nullptr;
+  const void* slots_view = nullptr;
+  const void* dst_view = nullptr;
+  if (nbytes > 0) {
+    if (!dst || !src) return fail(PA_ERR_INVALID_ARG, "null pointer");
+    const void* last_view = nullptr;
+    if (device_view(src, &src_view) != 1 ||
+        device_view(static_cast<const char*>(src) + nbytes - 1, &last_view) != 1 ||
+        static_cast<const char*>(last_view) - static_cast<const char*>(src_view) !=
+            static_cast<ptrdiff_t>(nbytes - 1))
+      return fail(PA_ERR_INVALID_ARG, "src must be page-locked host memory mapped for the device");
+    if (device_view(dst, &dst_view) != 0) return fail(PA_ERR_INVALID_ARG, "dst must be device memory");
+  }
+  if (num_tokens > 0) {
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+      return fail(PA_ERR_INVALID_ARG, "null pointer");
+    if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+      return fail(PA_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+    if (device_view(slot_mapping, &slots_view) != 1)
+      return fail(PA_ERR_INVALID_ARG, "slot_mapping must be page-locked host memory");
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return finish(pa::launch_upload_and_cache(dst, src_view, static_cast<int64_t>(nbytes), key, value, key_cache,
+                                            value_cache, static_cast<const int32_t*>(slots_view), num_tokens,
+                                            num_blocks, num_kv_heads, head_dim, block_size, dtype, kv_dtype,
+                                            k_scale, v_scale, st),
+                st, "pa_upload_and_cache");
+}
+
 pa_status pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
                     const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
                     int32_t num_seqs,

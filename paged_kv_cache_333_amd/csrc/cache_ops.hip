@@ -8,92 +8,165 @@
 
 namespace pa {
 
+// Arguments of the slot-mapping write (both forms below).
+struct WriteArgs {
+  const char* key;
+  const char* value;
+  char* key_cache;
+  char* value_cache;
+  const int32_t* slots;
+  int32_t num_tokens;
+  int64_t num_slots;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  float k_scale, v_scale;  // 8-bit pools only
+};
+
+// Slot of token `tok`: from device memory, or (HOST_SLOTS) from the
+// workgroup's LDS copy of its tokens' slots (staged from host memory once per
+// workgroup, see upload_and_cache_kernel; tok_first is its first token).
+struct HostSlots {
+  const int32_t* lds;
+  int64_t tok_first;
+};
+template <bool HOST_SLOTS>
+__device__ __forceinline__ int64_t slot_of(const int32_t* slots, const HostSlots& hs, int64_t tok) {
+  if constexpr (HOST_SLOTS)
+    return hs.lds[tok - hs.tok_first];
+  else
+    return slots[tok];
+}
+
 // Slot-mapping write ("Ascend C算子开发高阶实战…" §3.1: slot_mapping maps a
 // token to block slot / bs, offset slot % bs; "PagedAttention 实现细节" §3.4:
-// the new K/V of each step goes into its block).  One thread per 16-byte chunk
-// of one (token, KV head) row.  The key chunk is stored whole (keys are token
-// rows, [NB, H_kv, bs, D]); the value chunk's EPL elements go down column
-// `offset` of the value tile ([NB, H_kv, D, bs]), one element per dim.  Slots
-// outside [0, num_blocks * block_size) write nothing.
-template <int E>
-__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
-    const char* __restrict__ key, const char* __restrict__ value, char* __restrict__ key_cache,
-    char* __restrict__ value_cache, const int32_t* __restrict__ slot_mapping, int32_t num_tokens,
-    int64_t num_slots, int32_t num_kv_heads, int32_t head_dim, int32_t block_size) {
+// the new K/V of each step goes into its block).  Thread `idx` handles one
+// 16-byte chunk of one (token, KV head) row.  The key chunk is stored whole
+// (keys are token rows, [NB, H_kv, bs, D]); the value chunk's EPL elements go
+// down column `offset` of the value tile ([NB, H_kv, D, bs]), one element per
+// dim.  Slots outside [0, num_blocks * block_size) write nothing.
+template <int E, bool HOST_SLOTS>
+__device__ __forceinline__ void write_chunk(const WriteArgs& a, int64_t idx, const HostSlots& hs) {
   constexpr int EPL = 16 / E;
-  const int32_t cpr = head_dim / EPL;  // chunks per row
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t per_token = static_cast<int64_t>(num_kv_heads) * cpr;
-  if (idx >= per_token * num_tokens) return;
+  const int32_t cpr = a.head_dim / EPL;  // chunks per row
+  const int64_t per_token = static_cast<int64_t>(a.num_kv_heads) * cpr;
+  if (idx >= per_token * a.num_tokens) return;
   const int64_t tok = idx / per_token;
   const int64_t rem = idx - tok * per_token;  // = h * cpr + c
   const int32_t h = static_cast<int32_t>(rem / cpr);
   const int32_t c = static_cast<int32_t>(rem - static_cast<int64_t>(h) * cpr);
-  const int64_t slot = slot_mapping[tok];
-  if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot / block_size;
-  const int64_t off = slot - blk * block_size;
-  const int64_t tile = blk * num_kv_heads + h;  // (block, KV head) tile
+  const int64_t slot = slot_of<HOST_SLOTS>(a.slots, hs, tok);
+  if (slot < 0 || slot >= a.num_slots) return;
+  const int64_t blk = slot / a.block_size;
+  const int64_t off = slot - blk * a.block_size;
+  const int64_t tile = blk * a.num_kv_heads + h;  // (block, KV head) tile
   const int64_t src = idx * 16;
-  store16(key_cache + ((tile * block_size + off) * head_dim + static_cast<int64_t>(c) * EPL) * E,
-          load16(key + src));
-  const u32x4 v = load16(value + src);
-  char* vcol = value_cache + ((tile * head_dim + static_cast<int64_t>(c) * EPL) * block_size + off) * E;
+  store16(a.key_cache + ((tile * a.block_size + off) * a.head_dim + static_cast<int64_t>(c) * EPL) * E,
+          load16(a.key + src));
+  const u32x4 v = load16(a.value + src);
+  char* vcol = a.value_cache + ((tile * a.head_dim + static_cast<int64_t>(c) * EPL) * a.block_size + off) * E;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     const uint32_t w = word(v, e * E / 4);
     if constexpr (E == 4)
-      *reinterpret_cast<uint32_t*>(vcol + static_cast<int64_t>(e) * block_size * E) = w;
+      *reinterpret_cast<uint32_t*>(vcol + static_cast<int64_t>(e) * a.block_size * E) = w;
     else
-      *reinterpret_cast<uint16_t*>(vcol + static_cast<int64_t>(e) * block_size * E) =
+      *reinterpret_cast<uint16_t*>(vcol + static_cast<int64_t>(e) * a.block_size * E) =
           static_cast<uint16_t>(e & 1 ? w >> 16 : w);
   }
 }
 
 // The slot-mapping write into 8-bit pools (the quantised cache of the xdnf.cn
 // article, §2.3 and §6.3: KV values stored as 8-bit codes).  Same thread
-// layout as above: one thread per 16-byte chunk of one (token, KV head) input
-// row, EPL elements of the model type T.  Each element becomes the code of
-// x / scale (fp32 quotient, round to nearest even; to_code); the EPL key codes
-// are stored as one EPL-byte piece of the key row, the value codes one byte
-// each down column `offset` of the value tile.
-template <typename T, typename C>
-__global__ __launch_bounds__(256) void reshape_and_cache_quant_kernel(
-    const char* __restrict__ key, const char* __restrict__ value, uint8_t* __restrict__ key_cache,
-    uint8_t* __restrict__ value_cache, const int32_t* __restrict__ slot_mapping, int32_t num_tokens,
-    int64_t num_slots, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float k_scale,
-    float v_scale) {
+// layout: one thread per 16-byte chunk of one (token, KV head) input row, EPL
+// elements of the model type T.  Each element becomes the code of x / scale
+// (fp32 quotient, round to nearest even; to_code); the EPL key codes are
+// stored as one EPL-byte piece of the key row, the value codes one byte each
+// down column `offset` of the value tile.
+template <typename T, typename C, bool HOST_SLOTS>
+__device__ __forceinline__ void write_chunk_quant(const WriteArgs& a, int64_t idx, const HostSlots& hs) {
   constexpr int EPL = T::kEPL;
   constexpr int NW = EPL / 4;  // 32-bit words of codes per chunk
-  const int32_t cpr = head_dim / EPL;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t per_token = static_cast<int64_t>(num_kv_heads) * cpr;
-  if (idx >= per_token * num_tokens) return;
+  const int32_t cpr = a.head_dim / EPL;
+  const int64_t per_token = static_cast<int64_t>(a.num_kv_heads) * cpr;
+  if (idx >= per_token * a.num_tokens) return;
   const int64_t tok = idx / per_token;
   const int64_t rem = idx - tok * per_token;
   const int32_t h = static_cast<int32_t>(rem / cpr);
   const int32_t c = static_cast<int32_t>(rem - static_cast<int64_t>(h) * cpr);
-  const int64_t slot = slot_mapping[tok];
-  if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot / block_size;
-  const int64_t off = slot - blk * block_size;
-  const int64_t tile = blk * num_kv_heads + h;
-  const u32x4 kx = load16(key + idx * 16);
-  const u32x4 vx = load16(value + idx * 16);
+  const int64_t slot = slot_of<HOST_SLOTS>(a.slots, hs, tok);
+  if (slot < 0 || slot >= a.num_slots) return;
+  const int64_t blk = slot / a.block_size;
+  const int64_t off = slot - blk * a.block_size;
+  const int64_t tile = blk * a.num_kv_heads + h;
+  const u32x4 kx = load16(a.key + idx * 16);
+  const u32x4 vx = load16(a.value + idx * 16);
   uint32_t kw[NW];
 #pragma unroll
   for (int w = 0; w < NW; ++w) kw[w] = 0;
-  uint8_t* vcol = value_cache + (tile * head_dim + static_cast<int64_t>(c) * EPL) * block_size + off;
+  uint8_t* vcol = reinterpret_cast<uint8_t*>(a.value_cache) +
+                  (tile * a.head_dim + static_cast<int64_t>(c) * EPL) * a.block_size + off;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    kw[e / 4] |= to_code(C{}, elem_to_float(T{}, kx, e) / k_scale) << (8 * (e % 4));
-    vcol[static_cast<int64_t>(e) * block_size] =
-        static_cast<uint8_t>(to_code(C{}, elem_to_float(T{}, vx, e) / v_scale));
+    kw[e / 4] |= to_code(C{}, elem_to_float(T{}, kx, e) / a.k_scale) << (8 * (e % 4));
+    vcol[static_cast<int64_t>(e) * a.block_size] =
+        static_cast<uint8_t>(to_code(C{}, elem_to_float(T{}, vx, e) / a.v_scale));
   }
-  uint32_t* krow = reinterpret_cast<uint32_t*>(key_cache + (tile * block_size + off) * head_dim +
+  uint32_t* krow = reinterpret_cast<uint32_t*>(a.key_cache + (tile * a.block_size + off) * a.head_dim +
                                                static_cast<int64_t>(c) * EPL);
 #pragma unroll
   for (int w = 0; w < NW; ++w) krow[w] = kw[w];
+}
+
+// W::template run<HOST_SLOTS>(a, idx) is one of the two writes above.
+template <int E>
+struct PlainWrite {
+  static constexpr int kEPL = 16 / E;
+  template <bool H>
+  __device__ static void run(const WriteArgs& a, int64_t idx, const HostSlots& hs) { write_chunk<E, H>(a, idx, hs); }
+};
+template <typename T, typename C>
+struct QuantWrite {
+  static constexpr int kEPL = T::kEPL;
+  template <bool H>
+  __device__ static void run(const WriteArgs& a, int64_t idx, const HostSlots& hs) {
+    write_chunk_quant<T, C, H>(a, idx, hs);
+  }
+};
+
+template <typename W>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(WriteArgs a) {
+  W::template run<false>(a, static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x, HostSlots{nullptr, 0});
+}
+
+// One launch for the two small transfers of a decode step: the first
+// `up_blocks` workgroups copy the step's index block from page-locked host
+// memory to the device (as pa_upload), the others do the slot-mapping write,
+// with the slots read from the host copy.  Two launches would cost a
+// dependent-dispatch gap between them.  A host read is a round trip over the
+// host link, so a writing workgroup fetches the slots of its few tokens once
+// (one lane each, system-scope loads) into LDS and its threads read them there.
+template <typename W>
+__global__ __launch_bounds__(256) void upload_and_cache_kernel(WriteArgs a, uint32_t* __restrict__ dst,
+                                                               const uint32_t* src, int64_t words,
+                                                               int32_t up_blocks) {
+  if (static_cast<int32_t>(blockIdx.x) < up_blocks) {
+    const int64_t stride = static_cast<int64_t>(up_blocks) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < words; i += stride)
+      dst[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    return;
+  }
+  __shared__ int32_t slots_lds[256];
+  const int64_t base = static_cast<int64_t>(blockIdx.x - up_blocks) * blockDim.x;
+  const int64_t per_token = static_cast<int64_t>(a.num_kv_heads) * (a.head_dim / W::kEPL);
+  const int64_t tok_first = base / per_token;
+  // tokens of this workgroup's 256 chunks: at most 256 (a row has at least one chunk)
+  const int64_t tok_stop = min((base + blockDim.x - 1) / per_token + 1, static_cast<int64_t>(a.num_tokens));
+  if (tok_first + threadIdx.x < tok_stop)
+    slots_lds[threadIdx.x] = __hip_atomic_load(a.slots + tok_first + threadIdx.x, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_SYSTEM);
+  __syncthreads();
+  W::template run<true>(a, base + threadIdx.x, HostSlots{slots_lds, tok_first});
 }
 
 // Whole-block copy ("PagedAttention 实现细节" §3.3: the full contents of the
@@ -195,25 +268,84 @@ hipError_t launch_swap_blocks(void* dst_key, void* dst_value, const void* src_ke
   return hipGetLastError();
 }
 
+namespace {
+
+WriteArgs write_args(const void* key, const void* value, void* key_cache, void* value_cache,
+                     const int32_t* slots, int32_t num_tokens, int32_t num_blocks, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, float k_scale, float v_scale) {
+  return WriteArgs{static_cast<const char*>(key), static_cast<const char*>(value), static_cast<char*>(key_cache),
+                   static_cast<char*>(value_cache), slots, num_tokens,
+                   static_cast<int64_t>(num_blocks) * block_size, num_kv_heads, head_dim, block_size, k_scale,
+                   v_scale};
+}
+
+// Launch `Op` (reshape alone, or upload + reshape) with the write for
+// (dtype, kv_dtype); `chunks` write threads.
+template <typename Op>
+hipError_t by_write(const Op& op, pa_dtype dtype, pa_dtype kv_dtype) {
+  if (kv_dtype == PA_FP8_E4M3) {
+    if (dtype == PA_F32) return op.template run<QuantWrite<TF32, TE4M3>>();
+    if (dtype == PA_F16) return op.template run<QuantWrite<TF16, TE4M3>>();
+    return op.template run<QuantWrite<TBF16, TE4M3>>();
+  }
+  if (kv_dtype == PA_INT8) {
+    if (dtype == PA_F32) return op.template run<QuantWrite<TF32, TI8>>();
+    if (dtype == PA_F16) return op.template run<QuantWrite<TF16, TI8>>();
+    return op.template run<QuantWrite<TBF16, TI8>>();
+  }
+  if (dtype == PA_F32) return op.template run<PlainWrite<4>>();
+  return op.template run<PlainWrite<2>>();
+}
+
+struct ReshapeOp {
+  WriteArgs a;
+  int64_t chunks;
+  hipStream_t stream;
+  template <typename W>
+  hipError_t run() const {
+    hipLaunchKernelGGL(reshape_and_cache_kernel<W>, dim3(static_cast<uint32_t>((chunks + 255) / 256)), dim3(256), 0,
+                       stream, a);
+    return hipGetLastError();
+  }
+};
+
+struct UploadAndWriteOp {
+  WriteArgs a;
+  int64_t chunks;
+  uint32_t* dst;
+  const uint32_t* src;
+  int64_t words;
+  hipStream_t stream;
+  template <typename W>
+  hipError_t run() const {
+    int64_t up = (words + 255) / 256;
+    if (up > 64) up = 64;  // the index block is a few KB to a few hundred KB
+    if (up < 1) up = 1;
+    const int64_t wr = (chunks + 255) / 256;
+    hipLaunchKernelGGL(upload_and_cache_kernel<W>, dim3(static_cast<uint32_t>(up + wr)), dim3(256), 0, stream, a,
+                       dst, src, words, static_cast<int32_t>(up));
+    return hipGetLastError();
+  }
+};
+
+int64_t write_chunks(int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype) {
+  const int32_t e = dtype == PA_F32 ? 4 : 2;
+  return static_cast<int64_t>(num_tokens) * num_kv_heads * (head_dim * e / 16);
+}
+
+}  // namespace
+
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,
                                     void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
                                     int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                                     int32_t elem_bytes, int32_t block_size, hipStream_t stream) {
-  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * (head_dim * elem_bytes / 16);
-  if (total == 0) return hipSuccess;
-  const int64_t grid = (total + 255) / 256;
-  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
-#define PA_RESHAPE(E)                                                                                      \
-  hipLaunchKernelGGL(reshape_and_cache_kernel<E>, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream, \
-                     static_cast<const char*>(key), static_cast<const char*>(value),                      \
-                     static_cast<char*>(key_cache), static_cast<char*>(value_cache), slot_mapping,          \
-                     num_tokens, num_slots, num_kv_heads, head_dim, block_size)
-  if (elem_bytes == 4)
-    PA_RESHAPE(4);
-  else
-    PA_RESHAPE(2);
-#undef PA_RESHAPE
-  return hipGetLastError();
+  const pa_dtype dt = elem_bytes == 4 ? PA_F32 : PA_F16;
+  const int64_t chunks = write_chunks(num_tokens, num_kv_heads, head_dim, dt);
+  if (chunks == 0) return hipSuccess;
+  return by_write(ReshapeOp{write_args(key, value, key_cache, value_cache, slot_mapping, num_tokens, num_blocks,
+                                       num_kv_heads, head_dim, block_size, 1.f, 1.f),
+                            chunks, stream},
+                  dt, dt);
 }
 
 hipError_t launch_reshape_and_cache_quant(const void* key, const void* value, void* key_cache, void* value_cache,
@@ -221,27 +353,29 @@ hipError_t launch_reshape_and_cache_quant(const void* key, const void* value, vo
                                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                           pa_dtype dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
                                           hipStream_t stream) {
-  const int32_t elem = dtype == PA_F32 ? 4 : 2;
-  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * (head_dim * elem / 16);
-  if (total == 0) return hipSuccess;
-  const dim3 grid(static_cast<uint32_t>((total + 255) / 256));
-  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
-#define PA_QWRITE(T, C)                                                                                    \
-  hipLaunchKernelGGL((reshape_and_cache_quant_kernel<T, C>), grid, dim3(256), 0, stream,                   \
-                     static_cast<const char*>(key), static_cast<const char*>(value),                      \
-                     static_cast<uint8_t*>(key_cache), static_cast<uint8_t*>(value_cache), slot_mapping,    \
-                     num_tokens, num_slots, num_kv_heads, head_dim, block_size, k_scale, v_scale)
-  if (kv_dtype == PA_FP8_E4M3) {
-    if (dtype == PA_F32) PA_QWRITE(TF32, TE4M3);
-    else if (dtype == PA_F16) PA_QWRITE(TF16, TE4M3);
-    else PA_QWRITE(TBF16, TE4M3);
-  } else {
-    if (dtype == PA_F32) PA_QWRITE(TF32, TI8);
-    else if (dtype == PA_F16) PA_QWRITE(TF16, TI8);
-    else PA_QWRITE(TBF16, TI8);
-  }
-#undef PA_QWRITE
-  return hipGetLastError();
+  const int64_t chunks = write_chunks(num_tokens, num_kv_heads, head_dim, dtype);
+  if (chunks == 0) return hipSuccess;
+  return by_write(ReshapeOp{write_args(key, value, key_cache, value_cache, slot_mapping, num_tokens, num_blocks,
+                                       num_kv_heads, head_dim, block_size, k_scale, v_scale),
+                            chunks, stream},
+                  dtype, kv_dtype);
+}
+
+hipError_t launch_upload_and_cache(void* dst, const void* src_device_view, int64_t nbytes, const void* key,
+                                   const void* value, void* key_cache, void* value_cache,
+                                   const int32_t* slot_mapping_device_view, int32_t num_tokens,
+                                   int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   pa_dtype dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
+                                   hipStream_t stream) {
+  const int64_t chunks = write_chunks(num_tokens, num_kv_heads, head_dim, dtype);
+  const int64_t words = nbytes / 4;
+  if (chunks == 0 && words == 0) return hipSuccess;
+  return by_write(UploadAndWriteOp{write_args(key, value, key_cache, value_cache, slot_mapping_device_view,
+                                              num_tokens, num_blocks, num_kv_heads, head_dim, block_size, k_scale,
+                                              v_scale),
+                                   chunks, static_cast<uint32_t*>(dst), static_cast<const uint32_t*>(src_device_view),
+                                   words, stream},
+                  dtype, kv_dtype);
 }
 
 hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,

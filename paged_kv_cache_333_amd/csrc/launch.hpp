@@ -55,6 +55,14 @@ hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t*
                               int32_t num_pairs, int32_t num_blocks, int64_t block_bytes,
                               hipStream_t stream);
 hipError_t launch_upload(void* dst, const void* src_device_view, int64_t nbytes, hipStream_t stream);
+// pa_upload and the slot-mapping write (plain or quantising) in one launch; the
+// slots are read from page-locked host memory (its device view).
+hipError_t launch_upload_and_cache(void* dst, const void* src_device_view, int64_t nbytes, const void* key,
+                                   const void* value, void* key_cache, void* value_cache,
+                                   const int32_t* slot_mapping_device_view, int32_t num_tokens,
+                                   int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   pa_dtype dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
+                                   hipStream_t stream);
 // Whole-block copies between two pools (device views of host pools allowed).
 hipError_t launch_swap_blocks(void* dst_key, void* dst_value, const void* src_key, const void* src_value,
                               const int32_t* pairs, int32_t num_pairs, int32_t num_src_blocks,

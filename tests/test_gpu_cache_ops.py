@@ -138,3 +138,43 @@ def test_upload_rejects_pageable_source_without_launching():
     pa.pa_upload(dev, pinned)                           # the runtime state is clean afterwards
     torch.cuda.synchronize()
     assert torch.equal(dev.cpu(), pinned)
+
+
+@pytest.mark.parametrize("dtype,D,bs,Hkv,fmt", [s + (None,) for s in SHAPES] +
+                         [("f16", 128, 16, 8, "fp8_e4m3"), ("bf16", 64, 32, 2, "int8"), ("f32", 128, 16, 4, "fp8_e4m3")])
+def test_upload_and_cache_equals_upload_then_write(dtype, D, bs, Hkv, fmt):
+    """One launch: the index block arrives bit for bit and the write (slots read from the
+    pinned block itself) equals the oracle's write, plain or quantising."""
+    from oracle import quant as Q  # noqa: F401  (the quantising write's definition)
+    NB, T = 13, 37
+    rng = np.random.default_rng(11 * D + bs + Hkv)
+    if fmt:
+        kc = synth.normal_codes_host((NB, Hkv, bs, D), 1, fmt)
+        vc = synth.normal_codes_host((NB, Hkv, D, bs), 2, fmt)
+        dk, dv = torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda()
+    else:
+        kc = synth.normal_host((NB, Hkv, bs, D), 1, dtype)
+        vc = synth.normal_host((NB, Hkv, D, bs), 2, dtype)
+        dk, dv = _dev(kc, dtype), _dev(vc, dtype)
+    key = synth.normal_host((T, Hkv, D), 3, dtype)
+    val = synth.normal_host((T, Hkv, D), 4, dtype)
+    slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int32)
+    slots[[0, 5]] = -1
+    slots[9] = NB * bs + 3               # past the pool: skipped
+    # the staging block: [slots | other index data]
+    other = rng.integers(-5, 10**6, size=3000).astype(np.int32)
+    host = torch.from_numpy(np.concatenate([slots, other])).pin_memory()
+    dst = torch.full((host.numel(),), -1, dtype=torch.int32, device="cuda")
+    ks, vs = (0.02, 0.03) if fmt else (1.0, 1.0)
+    pa.pa_upload_and_cache(dst, host, _dev(key, dtype), _dev(val, dtype), dk, dv, host[:T], ks, vs,
+                           kv_format=fmt)
+    torch.cuda.synchronize()
+    assert torch.equal(dst.cpu(), host)
+    ref_slots = slots.copy()
+    ref_slots[9] = -1                    # the kernel skips a slot past the pool (invalid for the oracle)
+    if fmt:
+        ek, ev = C.reshape_and_cache_quant(key, val, kc, vc, ref_slots, dtype, fmt, ks, vs)
+        assert np.array_equal(dk.cpu().numpy(), ek) and np.array_equal(dv.cpu().numpy(), ev)
+    else:
+        ek, ev = C.reshape_and_cache(key, val, kc, vc, ref_slots)
+        assert np.array_equal(synth.to_numpy(dk, dtype), ek) and np.array_equal(synth.to_numpy(dv, dtype), ev)
