@@ -212,7 +212,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   constexpr int NV = D / 16;         // value loads per step, 16 output dims each
   constexpr int PV = TPL / EPL;      // P.V products per 16 output dims (2 for 8-bit codes)
   constexpr int NBS = TS > BS ? TS / BS : 1;  // blocks touched by one step
-  constexpr bool SPLIT_P = std::is_same<T, TBF16>::value;
+  // P.V runs in TP: the query type, except over 8-bit pools, whose codes are
+  // exact in fp16 (and P is in [0, 1]): fp16 there, one product per chunk
+  // instead of bf16's high part + residual, and the cheaper fp16 widening.
+  using TP = typename std::conditional<Q8, TF16, T>::type;
+  constexpr bool SPLIT_P = std::is_same<TP, TBF16>::value;
   constexpr float kNegInf = -__builtin_huge_valf();
   static_assert(NC >= 1 && NC <= 16 && (NC & (NC - 1)) == 0, "columns per tile");
   static_assert(Q8 ? T::kBytes == 2 : std::is_same<T, S>::value, "8-bit pools decode in fp16/bf16");
@@ -519,7 +523,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     // P in chunks of the compute type: chunk u holds tokens TPL q + EPL u ..
     u32x4 phi[PV], plo[PV];
 #pragma unroll
-    for (int u = 0; u < PV; ++u) pack_p(T{}, p + EPL * u, phi[u], plo[u]);
+    for (int u = 0; u < PV; ++u) pack_p(TP{}, p + EPL * u, phi[u], plo[u]);
     if (ragged) {
       const u32x4 keep = bits_mask(S{}, vuse);
 #pragma unroll
@@ -529,13 +533,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     for (int v = 0; v < NV; ++v) {
       u32x4 vc[PV];
       if constexpr (Q8)
-        widen(S{}, T{}, vr[v], vc[0], vc[PV - 1]);
+        widen(S{}, TP{}, vr[v], vc[0], vc[PV - 1]);
       else
         vc[0] = vr[v];
 #pragma unroll
       for (int u = 0; u < PV; ++u) {
-        acc[v] = mma(T{}, phi[u], vc[u], acc[v]);
-        if constexpr (SPLIT_P) acc[v] = mma(T{}, plo[u], vc[u], acc[v]);
+        acc[v] = mma(TP{}, phi[u], vc[u], acc[v]);
+        if constexpr (SPLIT_P) acc[v] = mma(TP{}, plo[u], vc[u], acc[v]);
       }
     }
   }
