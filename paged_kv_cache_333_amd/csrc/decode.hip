@@ -210,7 +210,7 @@ hipError_t single_pass_shape(const DecodeArgs& x, int64_t* workgroups, int64_t* 
 hipError_t launch_lse_reduce(void* out, const SplitLayout& ws, const int32_t* ctx, const int32_t* order,
                              int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t len_limit,
                              pa_dtype dt, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>(num_seqs) * num_heads);
+  const dim3 grid(static_cast<uint32_t>(num_seqs) * num_heads, static_cast<uint32_t>(head_dim / 32));
 #define PA_REDUCE(T, D)                                                                          \
   hipLaunchKernelGGL((lse_reduce_kernel<T, D>), grid, dim3(256), 0, stream, out, ws.m, ws.l, ws.o, \
                      ctx, order, num_seqs, num_heads, len_limit, ws.partition_size, ws.num_parts)

@@ -632,11 +632,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
 }
 
 // Log-sum-exp merge of split partials: M = max_p m_p, w_p = l_p exp(m_p - M),
-// out = sum_p w_p o_p / sum_p w_p.  One workgroup of four waves per
-// (sequence, head): the threads first take the max of m_p together, then wave
-// w accumulates partitions w, w + 4, ... with each lane holding D / 64 output
-// dims and several partitions' loads in flight; the waves' sums share M and
-// are added through LDS.
+// out = sum_p w_p o_p / sum_p w_p.  A workgroup owns 32 output dims (slice
+// blockIdx.y) of one (row, head): thread t takes dims 4 (t % 8) .. +3 of the
+// slice and partitions t / 8, t / 8 + 32, ...  A round issues all of a thread's
+// loads of 8 partitions (8 x 16 bytes of o, and their m and l) before the first
+// is used, so a whole 256-partition context is in flight at once.  Each thread
+// keeps its own running max and rescales its sums when it grows; the 32
+// partition rows are then brought to the common max and summed across lanes
+// and, for the four waves, through LDS.  The summation order depends only on
+// the partition count, not on timing.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float* __restrict__ ws_m,
                                                          const float* __restrict__ ws_l,
@@ -645,57 +649,99 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float*
                                                          const int32_t* __restrict__ order, int32_t num_seqs,
                                                          int32_t num_heads, int32_t len_limit,
                                                          int32_t part_size, int32_t num_parts) {
+  static_assert(D % 32 == 0, "dims in slices of 32");
   constexpr float kLog2e = 1.4426950408889634f;
-  constexpr int DPL = D / 64;  // output dims per lane
+  constexpr float kNegInf = -__builtin_huge_valf();
+  constexpr int kRows = 32;   // partition rows of a workgroup
+  constexpr int kRound = 8;   // partitions per thread per round
   const int slot = blockIdx.x / num_heads;
   const int h = blockIdx.x - slot * num_heads;
   const int s = order ? order[slot] : slot;  // same sequence set as the partials pass
   if (static_cast<uint32_t>(s) >= static_cast<uint32_t>(num_seqs)) return;
   const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
+  const int d_lo = 32 * static_cast<int>(blockIdx.y);
   const int n = ctx[s];
   if (n < 0 || n > len_limit) {
-    if (threadIdx.x < D) store_elem(T{}, out, sh * D + threadIdx.x, __builtin_nanf(""));
+    if (threadIdx.x < 32) store_elem(T{}, out, sh * D + d_lo + threadIdx.x, __builtin_nanf(""));
     return;
   }
   const int np = (n + part_size - 1) / part_size;
   const float* mp = ws_m + sh * num_parts;
   const float* lp = ws_l + sh * num_parts;
-  const float* op = ws_o + sh * num_parts * D;
+  const float* op = ws_o + sh * num_parts * D + d_lo + 4 * (threadIdx.x & 7);
+  const int row = threadIdx.x >> 3;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
+  float m = kNegInf, L = 0.f, A[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int base = 0; base < np; base += kRows * kRound) {
+    float mv[kRound], lv[kRound];
+    float4 ov[kRound];
+#pragma unroll
+    for (int u = 0; u < kRound; ++u) {
+      const int p = base + row + kRows * u;
+      if (p < np) {
+        mv[u] = mp[p];
+        lv[u] = lp[p];
+        ov[u] = *reinterpret_cast<const float4*>(op + static_cast<int64_t>(p) * D);
+      } else {
+        mv[u] = kNegInf;
+        lv[u] = 0.f;
+        ov[u] = float4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    float mc = m;
+#pragma unroll
+    for (int u = 0; u < kRound; ++u) mc = fmaxf(mc, mv[u]);
+    // sums so far are re-based to the new max (nothing to re-base while L is 0)
+    const float r = L == 0.f ? 0.f : fast_exp2((m - mc) * kLog2e);
+    L *= r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) A[k] *= r;
+#pragma unroll
+    for (int u = 0; u < kRound; ++u) {
+      // a partition with no token (l = 0, m = -inf: all masked) has no weight
+      const float w = lv[u] == 0.f ? 0.f : lv[u] * fast_exp2((mv[u] - mc) * kLog2e);
+      L += w;
+      A[0] = __builtin_fmaf(w, ov[u].x, A[0]);
+      A[1] = __builtin_fmaf(w, ov[u].y, A[1]);
+      A[2] = __builtin_fmaf(w, ov[u].z, A[2]);
+      A[3] = __builtin_fmaf(w, ov[u].w, A[3]);
+    }
+    m = mc;
+  }
+
+  // common max of the 32 rows: lanes 8 apart hold other rows of the wave
   __shared__ float sm_max[4];
   __shared__ float sm_l[4];
-  __shared__ float sm_a[4][D];
-  float M = -__builtin_huge_valf();
-  for (int p = threadIdx.x; p < np; p += 256) M = fmaxf(M, mp[p]);
+  __shared__ float sm_a[4][32];
+  float M = m;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  for (int off = 8; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
   if (lane == 0) sm_max[wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(sm_max[0], sm_max[1]), fmaxf(sm_max[2], sm_max[3]));
-
-  float L = 0.f, A[DPL];
+  const float f = L == 0.f ? 0.f : fast_exp2((m - M) * kLog2e);
+  L *= f;
 #pragma unroll
-  for (int k = 0; k < DPL; ++k) A[k] = 0.f;
-#pragma unroll 4
-  for (int p = wave; p < np; p += 4) {
-    // a partition with no token (l = 0, m = -inf: all masked) has no weight
-    const float w = lp[p] == 0.f ? 0.f : lp[p] * fast_exp2((mp[p] - M) * kLog2e);
-    L += w;
-    const float* o = op + static_cast<int64_t>(p) * D + lane * DPL;
+  for (int k = 0; k < 4; ++k) A[k] *= f;
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) A[k] = __builtin_fmaf(w, o[k], A[k]);
+  for (int off = 8; off < 64; off <<= 1) {
+    L += __shfl_xor(L, off);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) A[k] += __shfl_xor(A[k], off);
   }
   if (lane == 0) sm_l[wave] = L;
+  if (lane < 8) {
 #pragma unroll
-  for (int k = 0; k < DPL; ++k) sm_a[wave][lane * DPL + k] = A[k];
+    for (int k = 0; k < 4; ++k) sm_a[wave][4 * lane + k] = A[k];
+  }
   __syncthreads();
-  if (threadIdx.x < D) {
+  if (threadIdx.x < 32) {
     const int d = threadIdx.x;
     const float Ls = (sm_l[0] + sm_l[1]) + (sm_l[2] + sm_l[3]);
     const float As = (sm_a[0][d] + sm_a[1][d]) + (sm_a[2][d] + sm_a[3][d]);
-    store_elem(T{}, out, sh * D + d, Ls == 0.f ? 0.f : As / Ls);
+    store_elem(T{}, out, sh * D + d_lo + d, Ls == 0.f ? 0.f : As / Ls);
   }
 }
 
