@@ -109,6 +109,59 @@ def test_decode_long_and_odd_partitions(dt):
         assert_close(run_decode(c, dv, split=ps), ref, dt, f"split {ps}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_split_merge_over_more_than_256_partitions(D):
+    """16-token partitions: 313, 256, 257 and 1 partitions per sequence, so the merge
+    takes a second round of loads with its running max carried over."""
+    ctx = (5000, 4096, 4112, 1)
+    c = make_case(41 + D, "f16", 4, 8, 2, D, 16, ctx)
+    dv = to_dev(c)
+    ref = oracle(c)
+    assert_close(run_decode(c, dv, split=16), ref, "f16", "split 16")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_lse_reduce_many_partitions_and_empty_ones(D):
+    """The merge alone on 600-partition rows: the largest m in the first, the middle or the
+    last round of loads; partitions with no token (l = 0, m = -inf) anywhere; a row with
+    no token at all gives zeros."""
+    S, H, ps = 5, 2, 16
+    max_ctx = ps * 600
+    ctx = [max_ctx, max_ctx, max_ctx - 5, ps * 300 + 1, max_ctx]
+    lay = pa.split_layout(S, H, D, max_ctx, ps)
+    P = lay["parts"]
+    rng = np.random.default_rng(D)
+    m = rng.normal(size=(S, H, P)) * 3
+    m[0, :, 10] += 30          # max in the first round
+    m[1, :, 300] += 30         # in the middle
+    m[2, :, 599] += 30         # in the last
+    m[3] = np.linspace(-20, 20, P)   # rising: every round rescales
+    l_ = rng.uniform(1, 60, size=(S, H, P))
+    empty = rng.uniform(size=(S, H, P)) < 0.2
+    empty[4] = True            # a row with no token in any partition
+    l_[empty] = 0.0
+    m[empty] = -np.inf
+    o = rng.normal(size=(S, H, P, D))
+    o[empty] = 0.0
+    buf = np.zeros(lay["total"] // 4, dtype=np.float32)
+    buf[: S * H * P] = m.ravel()
+    buf[lay["off_l"] // 4: lay["off_l"] // 4 + S * H * P] = l_.ravel()
+    buf[lay["off_o"] // 4:] = o.ravel()
+    ws = torch.from_numpy(buf).cuda()
+    out = torch.full((S, H, D), 7.0, dtype=torch.float32, device="cuda")
+    pa.pa_lse_reduce(out, ws, torch.tensor(ctx, dtype=torch.int32).cuda(), max_ctx, ps)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    for s in range(S):
+        np_ = -(-ctx[s] // ps)
+        for h in range(H):
+            ref = A.lse_merge(m[s, h, :np_].astype(np.float32).astype(np.float64),
+                              l_[s, h, :np_].astype(np.float32).astype(np.float64),
+                              o[s, h, :np_].astype(np.float32).astype(np.float64))
+            assert_close(got[s, h], ref, "f32", f"seq {s} head {h}")
+    assert np.array_equal(got[4], np.zeros((H, D)))
+
+
 def test_tiny_fp32_workload_before_and_after_the_write():
     """Workload 1: contexts {1,16,17,45}; then one new token per sequence is written and the
     decode runs over {2,17,18,46} including it."""
