@@ -126,6 +126,26 @@ def test_upload_is_bit_exact_and_sees_rewrites_of_the_staging_buffer():
             assert np.array_equal(dev.cpu().numpy(), vals)
 
 
+def test_upload_every_relative_alignment_and_ragged_length():
+    """Source and destination at every pair of word offsets 0..3 (modulo 16 bytes), lengths
+    around the 4-word boundaries: the words arrive bit for bit and the words outside the
+    range stay untouched."""
+    rng = np.random.default_rng(9)
+    host = torch.empty(80_000, dtype=torch.int32).pin_memory()
+    dev = torch.empty(80_000, dtype=torch.int32, device="cuda")
+    for n in (1, 2, 3, 4, 5, 7, 8, 9, 37, 1001, 70_001):
+        for os_ in range(4):
+            for od in range(4):
+                vals = rng.integers(-2**31, 2**31 - 1, size=host.numel(), dtype=np.int64).astype(np.int32)
+                host.numpy()[:] = vals
+                dev.fill_(-7)
+                pa.pa_upload(dev[od:od + n], host[os_:os_ + n])
+                torch.cuda.synchronize()
+                got = dev.cpu().numpy()
+                assert np.array_equal(got[od:od + n], vals[os_:os_ + n]), (n, os_, od)
+                assert np.all(got[:od] == -7) and np.all(got[od + n:] == -7), (n, os_, od)
+
+
 def test_upload_rejects_pageable_source_without_launching():
     host = torch.arange(64, dtype=torch.int32)          # ordinary (pageable) memory
     dev = torch.zeros(64, dtype=torch.int32, device="cuda")
@@ -170,6 +190,14 @@ def test_upload_and_cache_equals_upload_then_write(dtype, D, bs, Hkv, fmt):
                            kv_format=fmt)
     torch.cuda.synchronize()
     assert torch.equal(dst.cpu(), host)
+    # the index block at another alignment than its destination
+    dst2 = torch.full((host.numel() + 1,), -1, dtype=torch.int32, device="cuda")
+    k2, v2 = dk.clone(), dv.clone()
+    pa.pa_upload_and_cache(dst2[1:], host, _dev(key, dtype), _dev(val, dtype), k2, v2, host[:T], ks, vs,
+                           kv_format=fmt)
+    torch.cuda.synchronize()
+    assert torch.equal(dst2[1:].cpu(), host) and int(dst2[0]) == -1
+    assert torch.equal(k2, dk) and torch.equal(v2, dv)   # the same write again
     ref_slots = slots.copy()
     ref_slots[9] = -1                    # the kernel skips a slot past the pool (invalid for the oracle)
     if fmt:
