@@ -42,8 +42,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8])
-    ap.add_argument("--path", choices=["auto", "single", "split"], default="auto",
-                    help="decode path: pa_decode_auto (default: the library picks), pa_decode or pa_decode_split")
+    ap.add_argument("--path", choices=["auto", "single", "split", "shared"], default=None,
+                    help="decode path: pa_decode_auto (the library picks), pa_decode, pa_decode_split, or "
+                         "pa_decode_shared (groups of sequences sharing leading blocks, from "
+                         "pa_shared_prefix_groups each step); default: shared for the parallel-sampling "
+                         "workload (5), auto otherwise")
     ap.add_argument("--partition", type=int, default=512)
     ap.add_argument("--fused-write", action="store_true",
                     help="write the new K/V inside the decode launch (pa_decode_append, auto path) instead of "
@@ -135,6 +138,13 @@ def measure_swap(launches: int = 10):
 PROFILE_STEPS = {"trace": (20, 5), "counters": (3, 2)}  # (steps, warmup)
 
 
+def default_path(workload: int, path: str | None) -> str:
+    """The decode path a bench run takes: the one asked for, else pa_decode_shared for the
+    parallel-sampling workload (its branches share their prefix blocks) and pa_decode_auto
+    for the others."""
+    return path or ("shared" if workload == 5 else "auto")
+
+
 def profile_commands(workload: int, outdir: str, path: str | None) -> list[str]:
     bench = f"python3 {os.path.join(ROOT, 'bench.py')}"
     sel = f" --workload {workload}" + (f" --path {path}" if path else "") + " --no-cpu-baseline"
@@ -180,21 +190,27 @@ def _counter_per_dispatch(folder: str, counter: str, kernel_substr: str) -> tupl
 def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
     # the path that ran (pa_decode_auto takes split on the long-context workload only); the bench
     # line looks its traffic up under the same name
-    w_path = ("split" if workload == 4 else "single") if path in (None, "auto") else path
+    path = default_path(workload, path)
+    w_path = ("split" if workload == 4 else "single") if path == "auto" else path
     decode = "decode_kernel"
     stats = _csv_rows(os.path.join(outdir, "trace"), "kernel_stats.csv")
     stats.sort(key=lambda r: -float(r["totaldurationns"]))
     dec = [r for r in stats if decode in r["name"]]
     if not dec:
         raise SystemExit("decode kernel missing from the kernel trace")
-    dec_avg_ns = float(dec[0]["averagens"])
+    # the shared-prefix path launches the decode kernel twice per call (the groups' prefixes,
+    # then the sequences' own tokens): its figures are per call, both launches together
+    per_call = 2 if w_path == "shared" else 1
+    if per_call == 2 and len(dec) < 2:
+        raise SystemExit("the shared-prefix path's two decode launches are not both in the trace")
+    dec_avg_ns = sum(float(r["averagens"]) for r in dec[:per_call])
     copy_bytes = 8192 // 2 * 32 * 16 * 128 * 2 * 2   # calibrate_copy: read (= written) per launch
     scale, meas = {}, {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
         ck, cn = _counter_per_dispatch(os.path.join(outdir, f"copy_{ctr.lower()}"), ctr, "copy_blocks_kernel")
         scale[ctr] = copy_bytes / (ck * 1024.0)
         meas[ctr] = _counter_per_dispatch(os.path.join(outdir, ctr.lower()), ctr, decode)
-        meas[ctr] = (meas[ctr][0], meas[ctr][1], ck, cn)
+        meas[ctr] = (meas[ctr][0] * per_call, meas[ctr][1] // per_call, ck, cn)
     traffic = sum(meas[c][0] * 1024.0 * scale[c] for c in meas)
     key = f"workload{workload}-{w_path}"
     try:
@@ -224,7 +240,8 @@ def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
         out.append(f"| `{name}` | {r['calls']} | {float(r['averagens']) / 1e3:.2f} | "
                    f"{float(r['minns']) / 1e3:.2f} | {float(r['maxns']) / 1e3:.2f} | {float(r['percentage']):.1f} |")
     out += ["", "## HBM counters (--pmc, one counter per run, KiB per dispatch)", "",
-            "| counter | decode kernel | dispatches | copy kernel (1 GiB each way) | dispatches | scale |",
+            "| counter | decode kernel" + (" (both launches of a call)" if per_call == 2 else "") +
+            " | " + ("calls" if per_call == 2 else "dispatches") + " | copy kernel (1 GiB each way) | dispatches | scale |",
             "|---|---|---|---|---|---|"]
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         v, n, ck, cn = meas[c]
@@ -269,11 +286,13 @@ class Bench:
         self.np, self.torch, self.pa, self.synth = np, torch, pa, synth
         self.args = args
         self.w = w = synth.workload(args.workload)
-        self.path = args.path
+        self.path = args.path = default_path(args.workload, args.path)
         self.path_ran = set()
         shared = args.workload == 5
+        # the branches of a fork stay next to each other (the shared-prefix groups need it);
+        # plain decode over shared blocks reads them through the caches
         self.order = args.order or ("index" if shared else "longest")
-        self.cached = (args.cache or ("cached" if shared else "stream")) == "cached"
+        self.cached = (args.cache or ("cached" if shared and self.path != "shared" else "stream")) == "cached"
         self.dev = torch.device("cuda:0")
         self.stream = torch.cuda.current_stream()
         seeds = synth.tensor_seeds(args.workload)
@@ -326,17 +345,24 @@ class Bench:
         # query rows of sequence s: s L .. s L + L - 1 (constant, resident)
         self.qstart = torch.arange(0, NS + 1, L, dtype=torch.int32, device=self.dev)
         self.ws = None
-        if self.path != "single":
+        if self.path == "shared":
+            if L > 1 or self.quant:
+                raise SystemExit("--path shared runs on workloads with model-type pools and one query token")
+            nbytes = pa.pa_decode_shared_workspace_bytes(S, H, D, self.max_ctx)
+            self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.dev)
+        elif self.path != "single":
             nbytes = (pa.pa_decode_multi_workspace_bytes(NS, H, D, self.max_ctx, args.partition) if L > 1 else
                       pa.pa_decode_split_workspace_bytes(S, H, D, self.max_ctx, args.partition))
             self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.dev)
 
         # double-buffered index data, one pinned staging buffer and one upload (pa_upload, a
         # kernel on the compute stream) per step:
-        # [slots LS | lens S | order S | pairs 2LS | tables S*MB] int32 (L new tokens per sequence)
+        # [slots LS | lens S | order S | pairs 2LS | tables S*MB | group_start S+1 | prefix_len S]
+        # int32 (L new tokens per sequence; the last two for the shared-prefix path)
         self.ids = torch.arange(S, dtype=torch.int64).repeat(L).pin_memory()
         self.bufs = []
-        total = 3 * NS + 2 * S + S * self.max_blocks
+        tab_end = 3 * NS + 2 * S + S * self.max_blocks
+        total = tab_end + 2 * S + 1
         for _ in range(2):
             hb = torch.empty(total, dtype=torch.int32).pin_memory()
             db = torch.empty(total, dtype=torch.int32, device=self.dev)
@@ -346,7 +372,9 @@ class Bench:
                 b["len_" + side] = t[NS:NS + S]
                 b["order_" + side] = t[NS + S:NS + 2 * S]
                 b["pairs_" + side] = t[NS + 2 * S:3 * NS + 2 * S].view(NS, 2)
-                b["tab_" + side] = t[3 * NS + 2 * S:].view(S, self.max_blocks)
+                b["tab_" + side] = t[3 * NS + 2 * S:tab_end].view(S, self.max_blocks)
+                b["gs_" + side] = t[tab_end:tab_end + S + 1]
+                b["pl_" + side] = t[tab_end + S + 1:]
             b["staged"].record(self.stream)
             self.bufs.append(b)
         self.elem = synth.ELEM_BYTES[w.dtype]
@@ -365,8 +393,13 @@ class Bench:
                                              b["pairs_h"].data_ptr())
         alloc.build_block_tables_into(self.ids.data_ptr(), S, self.max_blocks, b["tab_h"].data_ptr(),
                                       b["len_h"].data_ptr())
+        groups = None
+        if self.path == "shared":
+            groups = pa.pa_shared_prefix_groups_into(b["tab_h"].data_ptr(), b["len_h"].data_ptr(), S,
+                                                     self.max_blocks, w.block_size, b["gs_h"].data_ptr(),
+                                                     b["pl_h"].data_ptr())
         order = None
-        if self.order == "longest":
+        if self.order == "longest" and self.path != "shared":
             pa.pa_order_longest_first_into(b["len_h"].data_ptr(), S, b["order_h"].data_ptr())
             order = b["order_d"]
         r = k % self.newk.shape[0]
@@ -408,6 +441,10 @@ class Bench:
             pa.pa_decode(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"], self.max_ctx, w.scale,
                          seq_order=order, cached_kv=self.cached)
             self.path_ran.add("single")
+        elif self.path == "shared":
+            pa.pa_decode_shared(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"], b["gs_d"], b["pl_d"],
+                                groups[0], groups[1], self.max_ctx, w.scale, self.ws, cached_kv=self.cached)
+            self.path_ran.add("shared")
         elif self.path == "split":
             pa.pa_decode_split(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"], self.max_ctx, w.scale,
                                self.args.partition, self.ws, seq_order=order, cached_kv=self.cached)

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 4
+#define PA_ABI_VERSION 5
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -192,6 +192,20 @@ pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out)
  * scheduling); this changes no result.  Host arrays; PA_ERR_INVALID_ARG on a
  * null pointer or negative n. */
 pa_status pa_order_longest_first(const int32_t* context_lens, int32_t n, int32_t* order);
+
+/* Groups for pa_decode_shared, from host block tables (host int32
+ * [n, max_blocks]) and context lengths (host [n]).  Consecutive sequences whose
+ * first table entry is the same block form a candidate group (the branches of
+ * a fork sit next to each other in a batch built in fork order); its prefix P
+ * is the number of leading table entries every member shares with the first
+ * member, times block_size, capped at the members' shortest context.  A
+ * candidate with P below one block becomes groups of one (P = 0).  Writes
+ * group_start (host [n + 1], from 0 to n), prefix_len (host [n]),
+ * *num_groups and *max_group_size (1 when no group has two members; 0 for
+ * n = 0).  PA_ERR_INVALID_ARG on a null pointer or a negative size. */
+pa_status pa_shared_prefix_groups(const int32_t* tables, const int32_t* context_lens, int32_t n, int32_t max_blocks,
+                                  int32_t block_size, int32_t* group_start, int32_t* prefix_len,
+                                  int32_t* num_groups, int32_t* max_group_size);
 
 /* ------------------------------------------------------------------------ *
  * Prefix caching ([IMPL] §3.2 CachedPrefix / PrefixCacheManager): requests
@@ -535,6 +549,42 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache, c
                           int32_t max_context_len, float scale, float k_scale, float v_scale, pa_dtype dtype,
                           pa_dtype kv_dtype, uint32_t flags, int32_t partition_size, void* workspace,
                           size_t workspace_bytes, int32_t* path, void* stream);
+
+/* Workspace of pa_decode_shared: the three arrays of
+ * pa_decode_split_workspace_bytes for num_seqs rows, with partitions of an
+ * eighth of max_context_len rounded up to 64 tokens (at most eight), then one
+ * int32 per sequence at the next 256-byte boundary (the prefix length the
+ * first pass used).  Returns 0 on an invalid argument. */
+size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                        int32_t max_context_len);
+
+/* Decode for batches whose sequences share their leading blocks: the branches
+ * of parallel sampling or beam search, forked from one parent ([XDNF] §3.4
+ * fork; [IMPL] §3.3: forked sequences point at the same physical blocks until
+ * one of them writes).  The result is pa_decode's definition for every
+ * sequence; only the reading differs.
+ *   group_start: device int32 [num_groups + 1], from 0 to num_seqs, increasing:
+ *     sequences group_start[g] .. group_start[g+1] - 1 form group g (at most
+ *     max_group_size of them; a sequence sharing nothing is a group of one).
+ *   prefix_len: device int32 [num_seqs], the same P for every member of a
+ *     group, 0 <= P <= each member's context length, and the first ceil(P/bs)
+ *     table entries of every member equal to its group's first member's.
+ * Two launches: the first reads each group's first P tokens once, with the
+ * members' queries as the columns of the q.K tile, into per-member partials;
+ * the second decodes each sequence's own tokens P .. n-1 (the prefix's blocks
+ * are not read) and merges the two by the log-sum-exp rule.  A member whose
+ * prefix_len differs from its group's gets NaN rows; sequences outside every
+ * group, or groups that do not share the blocks they claim, give undefined
+ * values (all of this is rejected under PA_DEBUG).  Pools, scales, kv_dtype
+ * and errors as in pa_decode_masked; flags: PA_DECODE_CACHED_KV only;
+ * workspace: at least pa_decode_shared_workspace_bytes, 256-byte aligned. */
+pa_status pa_decode_shared(void* out, const void* query, const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_start,
+                           const int32_t* prefix_len, int32_t num_seqs, int32_t num_groups, int32_t max_group_size,
+                           int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len, float scale,
+                           float k_scale, float v_scale, pa_dtype dtype, pa_dtype kv_dtype, uint32_t flags,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ======================================================================== *
  * Quantised (8-bit) KV cache                                                *

@@ -121,6 +121,10 @@ _PROTOS = {
     "pa_decode_multi_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode_multi": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                _i32, _i32, _i32, _f32, _f32, _f32, _i32, _i32, _u32, _i32, _vp, _sz, _pi32, _vp]),
+    "pa_decode_shared_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "pa_decode_shared": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                _i32, _i32, _i32, _f32, _f32, _f32, _i32, _i32, _u32, _vp, _sz, _vp]),
+    "pa_shared_prefix_groups": (_i32, [_pi32, _pi32, _i32, _i32, _i32, _pi32, _pi32, _pi32, _pi32]),
     "pa_decode_quant": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                _i32, _f32, _f32, _f32, _i32, _i32, _u32, _i32, _vp, _sz, _pi32, _vp]),
     "pa_status_string": (C.c_char_p, [_i32]),
@@ -429,6 +433,59 @@ def pa_lse_reduce(out, workspace, context_lens, max_context_len: int, partition_
     _check(lib.pa_lse_reduce(_ptr(out), _ptr(workspace), nbytes, _ptr(context_lens), S, H, D,
                              max_context_len, partition_size, _dtype_code(out), _stream(stream)),
            "pa_lse_reduce")
+
+
+def pa_decode_shared_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int) -> int:
+    return lib.pa_decode_shared_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len)
+
+
+def pa_decode_shared(out, query, key_cache, value_cache, block_tables, context_lens, group_start, prefix_len,
+                     num_groups: int, max_group_size: int, max_context_len: int, scale: float, workspace,
+                     k_scale: float = 1.0, v_scale: float = 1.0, kv_format=None, stream=None,
+                     cached_kv: bool = False):
+    """Decode of sequences that share their leading blocks in groups (device int32
+    group_start [num_groups + 1] and prefix_len [S], e.g. from pa_shared_prefix_groups):
+    each group's shared prefix is read once for all its members, then each sequence's own
+    tokens, merged.  Same result as pa_decode; workspace of pa_decode_shared_workspace_bytes."""
+    S, H, D = query.shape
+    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache)
+    kv = _kv_format(key_cache, kv_format) if key_cache.element_size() == 1 else _dtype_code(key_cache)
+    nbytes = workspace.numel() * workspace.element_size()
+    flags = PA_DECODE_CACHED_KV if cached_kv else 0
+    _check(lib.pa_decode_shared(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+                                _ptr(context_lens), _ptr(group_start), _ptr(prefix_len), S, num_groups,
+                                max_group_size, H, H_kv, D, bs, block_tables.shape[1], NB, max_context_len, scale,
+                                k_scale, v_scale, _dtype_code(query), kv, flags, _ptr(workspace), nbytes,
+                                _stream(stream)), "pa_decode_shared")
+
+
+def pa_shared_prefix_groups(tables, context_lens, block_size: int):
+    """Host helper: (group_start list [G + 1], prefix_len list [S], num_groups, max_group_size)
+    from host block tables (S rows of max_blocks ids) and context lengths [S]: sequences that
+    share their leading blocks with their neighbours form a group."""
+    n = len(context_lens)
+    rows = [list(r) for r in tables]
+    mb = len(rows[0]) if rows else 0
+    if any(len(r) != mb for r in rows) or len(rows) != n:
+        raise ValueError("tables must have one row of max_blocks ids per sequence")
+    tab = (C.c_int32 * max(n * mb, 1))(*[int(x) for r in rows for x in r])
+    lens = (C.c_int32 * max(n, 1))(*[int(x) for x in context_lens])
+    gs = (C.c_int32 * (n + 1))()
+    pl = (C.c_int32 * max(n, 1))()
+    ng, mg = C.c_int32(0), C.c_int32(0)
+    _check(lib.pa_shared_prefix_groups(tab, lens, n, mb, block_size, gs, pl, C.byref(ng), C.byref(mg)),
+           "pa_shared_prefix_groups")
+    return list(gs[:ng.value + 1]), list(pl[:n]), ng.value, mg.value
+
+
+def pa_shared_prefix_groups_into(tables_ptr: int, lens_ptr: int, n: int, max_blocks: int, block_size: int,
+                                 group_start_ptr: int, prefix_len_ptr: int):
+    """Raw form for pinned host buffers (int32 pointers); returns (num_groups, max_group_size)."""
+    ng, mg = C.c_int32(0), C.c_int32(0)
+    _check(lib.pa_shared_prefix_groups(C.cast(tables_ptr, _pi32), C.cast(lens_ptr, _pi32), n, max_blocks,
+                                       block_size, C.cast(group_start_ptr, _pi32), C.cast(prefix_len_ptr, _pi32),
+                                       C.byref(ng), C.byref(mg)), "pa_shared_prefix_groups")
+    return ng.value, mg.value
 
 
 def pa_order_longest_first(context_lens) -> list:

@@ -746,4 +746,50 @@ pa_status pa_order_longest_first(const int32_t* context_lens, int32_t n, int32_t
   return PA_OK;
 }
 
+pa_status pa_shared_prefix_groups(const int32_t* tables, const int32_t* context_lens, int32_t n, int32_t max_blocks,
+                                  int32_t block_size, int32_t* group_start, int32_t* prefix_len,
+                                  int32_t* num_groups, int32_t* max_group_size) {
+  if (n < 0 || max_blocks < 0 || block_size <= 0 || !group_start || !num_groups || !max_group_size ||
+      (n > 0 && (!tables || !context_lens || !prefix_len)))
+    return fail(PA_ERR_INVALID_ARG, "null argument or negative size");
+  auto used = [&](int32_t i) -> int32_t {  // table entries holding the sequence's tokens
+    const int64_t nb = (static_cast<int64_t>(std::max(context_lens[i], 0)) + block_size - 1) / block_size;
+    return static_cast<int32_t>(std::min<int64_t>(nb, max_blocks));
+  };
+  auto row = [&](int32_t i) { return tables + static_cast<int64_t>(i) * max_blocks; };
+  int32_t groups = 0, widest = n > 0 ? 1 : 0;
+  int32_t i = 0;
+  while (i < n) {
+    // consecutive sequences whose first block is the leader's
+    int32_t stop = i + 1;
+    if (used(i) > 0)
+      while (stop < n && used(stop) > 0 && row(stop)[0] == row(i)[0]) ++stop;
+    // tokens every member holds in the same blocks
+    int64_t common = used(i), shortest = std::max(context_lens[i], 0);
+    for (int32_t m = i + 1; m < stop; ++m) {
+      int32_t j = 0;
+      const int32_t lim = std::min(used(m), used(i));
+      while (j < lim && row(m)[j] == row(i)[j]) ++j;
+      common = std::min<int64_t>(common, j);
+      shortest = std::min<int64_t>(shortest, std::max(context_lens[m], 0));
+    }
+    const int64_t p = std::min<int64_t>(common * block_size, shortest);
+    if (stop - i > 1 && p >= block_size) {
+      group_start[groups++] = i;
+      for (int32_t m = i; m < stop; ++m) prefix_len[m] = static_cast<int32_t>(p);
+      widest = std::max(widest, stop - i);
+    } else {  // nothing worth sharing: groups of one
+      for (int32_t m = i; m < stop; ++m) {
+        group_start[groups++] = m;
+        prefix_len[m] = 0;
+      }
+    }
+    i = stop;
+  }
+  group_start[groups] = n;
+  *num_groups = groups;
+  *max_group_size = widest;
+  return PA_OK;
+}
+
 }  // extern "C"

@@ -669,6 +669,100 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache, c
                 "pa_decode_multi");
 }
 
+namespace {
+
+// Partition of a shared prefix in pass 1: an eighth of the longest context,
+// rounded up to 64 tokens (a multiple of every step and block size): at most
+// eight partitions, two workgroups of four waves for the longest prefix.
+int32_t shared_partition(int32_t max_context_len) {
+  const int64_t eighth = (static_cast<int64_t>(max_context_len) + 7) / 8;
+  const int64_t p = (eighth + 63) / 64 * 64;
+  return static_cast<int32_t>(p < 64 ? 64 : p);
+}
+
+}  // namespace
+
+size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                        int32_t max_context_len) {
+  SplitSizes z;
+  if (!split_sizes(num_seqs, num_heads, head_dim, max_context_len, shared_partition(max_context_len), &z)) return 0;
+  return static_cast<size_t>(align256(z.total) + static_cast<int64_t>(num_seqs) * 4);
+}
+
+pa_status pa_decode_shared(void* out, const void* query, const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_start,
+                           const int32_t* prefix_len, int32_t num_seqs, int32_t num_groups, int32_t max_group_size,
+                           int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len, float scale,
+                           float k_scale, float v_scale, pa_dtype dtype, pa_dtype kv_dtype, uint32_t flags,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  pa::DecodeArgs a = pack(out, query, key_cache, value_cache, block_tables, context_lens, nullptr, num_seqs,
+                          num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                          max_context_len, scale, dtype, flags);
+  a.kv_dtype = kv_dtype;
+  pa_status s = check_decode_args(a);
+  if (s != PA_OK) return s;
+  if (is_code_type(kv_dtype)) {
+    if (dtype != PA_F16 && dtype != PA_BF16)
+      return fail(PA_ERR_UNSUPPORTED, "8-bit pools decode with PA_F16 or PA_BF16 queries");
+    if ((s = check_scales(k_scale, v_scale)) != PA_OK) return s;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+  } else if (kv_dtype != dtype) {
+    return fail(PA_ERR_UNSUPPORTED, "kv_dtype must equal dtype, or be PA_FP8_E4M3 / PA_INT8");
+  }
+  if (flags & ~uint32_t(PA_DECODE_CACHED_KV)) return fail(PA_ERR_INVALID_ARG, "unknown flag bits");
+  if (max_group_size < 1 || max_group_size > 4096)
+    return fail(PA_ERR_INVALID_ARG, "1 <= max_group_size <= 4096");
+  if (num_seqs == 0) return PA_OK;
+  if (num_groups < 1 || num_groups > num_seqs)
+    return fail(PA_ERR_INVALID_ARG, "the groups must partition the sequences: 1 <= num_groups <= num_seqs");
+  if (!group_start || !prefix_len) return fail(PA_ERR_INVALID_ARG, "null group_start or prefix_len");
+  SplitSizes z;
+  const int32_t part = shared_partition(max_context_len);
+  if (!split_sizes(num_seqs, num_heads, head_dim, max_context_len, part, &z))
+    return fail(PA_ERR_INVALID_ARG, "workspace sizes");
+  const int64_t need = align256(z.total) + static_cast<int64_t>(num_seqs) * 4;
+  if (static_cast<int64_t>(workspace_bytes) < need)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL,
+                "need " + std::to_string(need) + " bytes, got " + std::to_string(workspace_bytes));
+  pa::SplitLayout ws;
+  if ((s = make_layout(workspace, workspace_bytes, num_seqs, num_heads, head_dim, max_context_len, part, &ws)) !=
+      PA_OK)
+    return s;
+  ws.rows = num_seqs;
+  int32_t* ws_len = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align256(z.total));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_mode()) {
+    if ((s = debug_check_tables(a, st)) != PA_OK) return s;
+    std::vector<int32_t> gs, pl, ctx, tab;
+    if ((s = fetch(gs, group_start, static_cast<size_t>(num_groups) + 1, st)) != PA_OK) return s;
+    if ((s = fetch(pl, prefix_len, num_seqs, st)) != PA_OK) return s;
+    if ((s = fetch(ctx, context_lens, num_seqs, st)) != PA_OK) return s;
+    if ((s = fetch(tab, block_tables, static_cast<size_t>(num_seqs) * max_blocks_per_seq, st)) != PA_OK) return s;
+    if (gs[0] != 0 || gs[num_groups] != num_seqs)
+      return fail(PA_ERR_BAD_TABLE, "group_start must run from 0 to num_seqs");
+    for (int32_t g = 0; g < num_groups; ++g) {
+      const int32_t lead = gs[g], stop = gs[g + 1];
+      if (stop <= lead || stop - lead > max_group_size)
+        return fail(PA_ERR_BAD_TABLE, "group " + std::to_string(g) + " empty or above max_group_size");
+      const int32_t nb = (pl[lead] + block_size - 1) / block_size;
+      for (int32_t i = lead; i < stop; ++i) {
+        if (pl[i] != pl[lead] || pl[i] < 0 || pl[i] > ctx[i])
+          return fail(PA_ERR_BAD_TABLE, "prefix_len of sequence " + std::to_string(i) +
+                                            " differs from its group's or lies outside [0, its context]");
+        for (int32_t j = 0; j < nb; ++j)
+          if (tab[static_cast<size_t>(i) * max_blocks_per_seq + j] !=
+              tab[static_cast<size_t>(lead) * max_blocks_per_seq + j])
+            return fail(PA_ERR_BAD_TABLE, "sequence " + std::to_string(i) + " does not share block " +
+                                              std::to_string(j) + " of its group's prefix");
+      }
+    }
+  }
+  return finish(pa::launch_decode_shared(a, group_start, num_groups, max_group_size, prefix_len, ws, ws_len, st),
+                st, "pa_decode_shared");
+}
+
 pa_status pa_decode_quant(void* out, const void* query, const void* key_cache, const void* value_cache,
                           const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,

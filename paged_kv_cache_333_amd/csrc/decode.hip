@@ -184,6 +184,51 @@ hipError_t launch_decode_multi(const DecodeArgs& x, const int32_t* query_start, 
                            stream);
 }
 
+hipError_t launch_decode_shared(const DecodeArgs& x, const int32_t* group_start, int32_t num_groups,
+                                int32_t max_group, const int32_t* prefix_len, const SplitLayout& ws, int32_t* ws_len,
+                                hipStream_t stream) {
+  if (ws.num_parts > kMaxPrior) return hipErrorInvalidValue;  // the merge takes at most kMaxPrior partitions
+  const bool cached = (x.flags & PA_DECODE_CACHED_KV) != 0;
+  // Pass 1: each group's shared prefix, read once for all its members (their
+  // queries are the columns of the tile), into per-member partials.
+  DecodeArgs g = x;
+  g.num_seqs = num_groups;
+  g.context_lens = prefix_len;  // read at each group's first member
+  g.seq_order = nullptr;
+  g.mask_lo = g.mask_hi = nullptr;
+  DecodeParams p1 = make_params(g);
+  p1.shared = 1;
+  p1.q_start = group_start;
+  p1.num_q_rows = x.num_seqs;
+  int nc = 1, lg = 0, chunks = 1;
+  multi_tile(x.num_heads / x.num_kv_heads, max_group, &nc, &lg, &chunks);
+  p1.col_heads_log2 = lg;
+  p1.q_chunks = chunks;
+  p1.ws_m = ws.m;
+  p1.ws_l = ws.l;
+  p1.ws_o = ws.o;
+  p1.part_size = ws.partition_size;
+  p1.num_parts = ws.num_parts;
+  p1.ws_len = ws_len;
+  hipError_t e = by_dtype(LaunchOp{p1, num_groups, cached, stream}, x.dtype, x.kv_dtype, true, false, x.head_dim,
+                          x.block_size, nc);
+  if (e != hipSuccess) return e;
+  // Pass 2: every sequence over its own tokens (the prefix masked, its blocks
+  // not read), merged with its prefix partials.
+  DecodeArgs o = x;
+  o.mask_lo = nullptr;
+  o.mask_hi = prefix_len;
+  DecodeParams p2 = make_params(o);
+  p2.prior_m = ws.m;
+  p2.prior_l = ws.l;
+  p2.prior_o = ws.o;
+  p2.prior_len = ws_len;
+  p2.prior_parts = ws.num_parts;
+  p2.prior_part_size = ws.partition_size;
+  return by_dtype(LaunchOp{p2, x.num_seqs, cached, stream}, x.dtype, x.kv_dtype, false, false, x.head_dim,
+                  x.block_size, group_tile(x.num_heads / x.num_kv_heads));
+}
+
 hipError_t multi_pass_shape(const DecodeArgs& x, int32_t max_query_len, int64_t* workgroups, int64_t* resident) {
   int nc = 1, lg = 0, chunks = 1;
   multi_tile(x.num_heads / x.num_kv_heads, max_query_len, &nc, &lg, &chunks);

@@ -75,6 +75,7 @@
 namespace pa {
 
 constexpr int kWaves = 4;
+constexpr int kMaxPrior = 8;  // partitions of a prior partial (the shared-prefix pass)
 
 struct DecodeParams {
   void* out;
@@ -95,6 +96,22 @@ struct DecodeParams {
   // tokens.  ws_len (split with q_start): per query row, its causal context length.
   const int32_t* q_start;
   int32_t num_q_rows;  // rows of q/out when q_start is set
+  // Shared-prefix pass (with q_start, split): "sequence" s is a group of
+  // sequences q_start[s] .. q_start[s+1]-1 whose first ctx[q_start[s]] tokens
+  // are the same blocks; the q_start[s] row of the tables addresses them, every
+  // member's query sees all of them (no causal limit), and the partials land
+  // in the members' rows.
+  int32_t shared;
+  // A prior partial per (sequence, head), merged into a single-pass result:
+  // the shared-prefix pass's partitions of the masked positions [0, mask_hi)
+  // (prior_len: the prefix length that pass used, per sequence; it must equal
+  // mask_hi, else the row is NaN).  Null: none.
+  const float* prior_m;
+  const float* prior_l;
+  const float* prior_o;
+  const int32_t* prior_len;
+  int32_t prior_parts;
+  int32_t prior_part_size;
   int32_t col_heads_log2;
   int32_t q_chunks;
   int32_t* ws_len;
@@ -253,23 +270,47 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int tok0 = chunk * col_toks;
   if (tok0 >= L) return;  // no query token for this workgroup
   const int kvh = h0 / (a.num_heads / a.num_kv_heads);
-  const int nctx = a.ctx[s];
+  const bool shared = a.shared != 0;  // a group's shared prefix (see DecodeParams)
+  const int nctx = a.ctx[shared ? qs : s];
   // (an empty context is valid for plain decode: a zero row; a span of query
   // tokens must lie inside the context)
-  const bool bad_len = nctx < 0 || nctx > a.len_limit || (a.q_start && L > nctx);
+  const bool bad_len = nctx < 0 || nctx > a.len_limit || (a.q_start && !shared && L > nctx);
   // Causal limits: query token i sits at position nctx - L + i and sees the
   // positions before nctx - L + i + 1.  This lane's column, and the tile's
-  // nearest and furthest limits (all nctx for one token per sequence).
+  // nearest and furthest limits (all nctx for one token per sequence, and for
+  // the members of a shared prefix).
   const int my_tok = tok0 + ((n % NC) >> lg_h);
-  const int lim_base = nctx - L + 1;
-  const int lane_lim = lim_base + min(my_tok, L - 1);
-  const int tile_lim_lo = lim_base + tok0;
-  const int tile_lim_hi = lim_base + min(tok0 + col_toks, L) - 1;
-  int mlo = 0, mhi = 0;  // masked positions; empty unless mask_lo < mask_hi
-  if (!APPEND && a.mask_lo) {
-    mlo = a.mask_lo[s];
+  const int lim_base = shared ? nctx : nctx - L + 1;
+  const int lane_lim = shared ? nctx : lim_base + min(my_tok, L - 1);
+  const int tile_lim_lo = shared ? nctx : lim_base + tok0;
+  const int tile_lim_hi = shared ? nctx : lim_base + min(tok0 + col_toks, L) - 1;
+  int mlo = 0, mhi = 0;  // masked positions; empty unless mask_lo < mask_hi (mask_lo null: 0)
+  if (!APPEND && a.mask_hi) {
+    mlo = a.mask_lo ? a.mask_lo[s] : 0;
     mhi = a.mask_hi[s];
     if (mhi <= mlo) mlo = mhi = 0;
+  }
+  // a prior partial covers [0, mhi); it must be the one the shared pass made
+  const bool use_prior = !SPLIT && a.prior_m && mlo == 0 && mhi > 0;
+  const bool prior_bad = use_prior && (mhi > nctx || a.prior_len[s] != mhi);
+  // Its partitions that hold tokens (only for a valid prefix: mhi <= nctx <=
+  // len_limit lies within them), and this thread's share of their m and l,
+  // loaded now so that the loads overlap the main loop: thread t < NC *
+  // kMaxPrior takes column t / kMaxPrior, partition t % kMaxPrior.
+  const int prior_np = use_prior && !prior_bad && !bad_len
+                           ? min(min((mhi + a.prior_part_size - 1) / a.prior_part_size, a.prior_parts), kMaxPrior)
+                           : 0;
+  float pre_m = kNegInf, pre_l = 0.f;
+  if (prior_np > 0) {
+    const int pg = static_cast<int>(threadIdx.x) / kMaxPrior;
+    const int pp = static_cast<int>(threadIdx.x) - pg * kMaxPrior;
+    const int ptok = tok0 + (pg >> lg_h);
+    if (pg < NC && pp < prior_np && ptok < L) {
+      const int64_t idx =
+          (static_cast<int64_t>(qs + ptok) * a.num_heads + h0 + (pg & (col_heads - 1))) * a.prior_parts + pp;
+      pre_m = a.prior_m[idx] * 1.4426950408889634f;  // base-2 units, like m_run
+      pre_l = a.prior_l[idx];
+    }
   }
 
   // Single pass: the workgroup's waves share the context, wave w taking steps
@@ -284,7 +325,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     t_end = min(t_begin + a.part_size, t_end);
     // the merge needs each query row's context length (any head group writes the same)
     if (a.ws_len && part == 0 && grp == 0 && q == 0 && n < NC && (n & (col_heads - 1)) == 0 && my_tok < L)
-      a.ws_len[qs + my_tok] = bad_len ? -1 : lim_base + my_tok;
+      a.ws_len[qs + my_tok] = bad_len ? -1 : (shared ? nctx : lim_base + my_tok);
   }
   AppendRow<T, D> fresh;  // the fused slot-mapping write (pa_decode_append)
   if constexpr (APPEND)
@@ -301,7 +342,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int st_skip = mlo <= t_begin && mhi > t_begin ? (min(mhi, t_end) - t_begin) / TS : 0;
   const int st_first = st_skip + (SPLIT ? 0 : wave);
   const int b_end = (t_end + BS - 1) / BS;
-  const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.max_blocks;
+  const int32_t* trow = a.tables + static_cast<int64_t>(shared ? qs : s) * a.max_blocks;
 
   // Q operand of q.K: lane (q, n) holds column n % NC (a padding column past
   // the last query token repeats it), the dims its key chunks hold: chunk
@@ -607,6 +648,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       for (int v = 0; v < NV; ++v) sm_acc[wave][g][16 * v + n] = acc[v][j];
     }
   }
+  __shared__ float sm_pm[NC][kMaxPrior];  // prior partitions: m (base 2) and l; -inf and 0 past prior_np
+  __shared__ float sm_pl[NC][kMaxPrior];
+  if (prior_np > 0 && threadIdx.x < NC * kMaxPrior) {
+    sm_pm[threadIdx.x / kMaxPrior][threadIdx.x % kMaxPrior] = pre_m;
+    sm_pl[threadIdx.x / kMaxPrior][threadIdx.x % kMaxPrior] = pre_l;
+  }
   const int any_bad = __syncthreads_or(bad);
 
   for (int i = threadIdx.x; i < NC * D; i += kWaves * 64) {
@@ -614,9 +661,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     const int d = i - g * D;
     const int tok = tok0 + (g >> lg_h);
     if (tok >= L) continue;  // a padding column
+    const int64_t sh = static_cast<int64_t>(qs + tok) * a.num_heads + h0 + (g & (col_heads - 1));
+    float po[kMaxPrior];  // the prior partitions' o for this element, all loads in flight at once
+    if (prior_np > 0) {
+#pragma unroll
+      for (int p = 0; p < kMaxPrior; ++p)
+        po[p] = p < prior_np ? a.prior_o[(sh * a.prior_parts + p) * D + d] : 0.f;
+    }
     float M = kNegInf;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][g]);
+    if (prior_np > 0) {
+#pragma unroll
+      for (int p = 0; p < kMaxPrior; ++p) M = fmaxf(M, sm_pm[g][p]);
+    }
     const float Mu = M == kNegInf ? 0.f : M;
     float Lsum = 0.f, A = 0.f;
 #pragma unroll
@@ -625,8 +683,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       Lsum = __builtin_fmaf(sm_l[w][g], wt, Lsum);
       A = __builtin_fmaf(sm_acc[w][g][d], wt, A);
     }
-    const int64_t sh = static_cast<int64_t>(qs + tok) * a.num_heads + h0 + (g & (col_heads - 1));
-    const float val = any_bad || bad_len ? __builtin_nanf("") : (Lsum > 0.f ? A / Lsum * a.v_scale : 0.f);
+    if (prior_np > 0) {
+#pragma unroll
+      for (int p = 0; p < kMaxPrior; ++p) {
+        // o_p is acc_p / l_p with v_scale applied; A is in unscaled acc units.  A
+        // partition with no token (l = 0) has no weight.
+        const float lp = sm_pl[g][p];
+        const float wt = lp == 0.f ? 0.f : lp * fast_exp2(sm_pm[g][p] - Mu);
+        Lsum += wt;
+        A = __builtin_fmaf(po[p] / a.v_scale, wt, A);
+      }
+    }
+    const float val = any_bad || bad_len || prior_bad ? __builtin_nanf("")
+                                                      : (Lsum > 0.f ? A / Lsum * a.v_scale : 0.f);
     store_elem(T{}, a.out, sh * D + d, val);
   }
 }

@@ -82,6 +82,14 @@ hipError_t single_pass_shape(const DecodeArgs& a, int64_t* workgroups, int64_t* 
 hipError_t launch_decode_multi(const DecodeArgs& a, const int32_t* query_start, int32_t num_query_tokens,
                                int32_t max_query_len, const SplitLayout* ws, int32_t* ws_len, hipStream_t stream);
 hipError_t multi_pass_shape(const DecodeArgs& a, int32_t max_query_len, int64_t* workgroups, int64_t* resident);
+// Groups of sequences sharing their first prefix_len tokens' blocks: sequences
+// group_start[g] .. group_start[g+1]-1, prefix_len per sequence (equal within a
+// group).  Pass 1 reads each group's prefix once into per-member partials
+// (ws, one int per sequence in ws_len); pass 2 decodes each sequence's own
+// tokens and merges.
+hipError_t launch_decode_shared(const DecodeArgs& a, const int32_t* group_start, int32_t num_groups,
+                                int32_t max_group, const int32_t* prefix_len, const SplitLayout& ws, int32_t* ws_len,
+                                hipStream_t stream);
 hipError_t launch_lse_reduce(void* out, const SplitLayout& ws, const int32_t* context_lens,
                              const int32_t* seq_order, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                              int32_t len_limit, pa_dtype dtype, hipStream_t stream);

@@ -19,7 +19,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 47
+    assert len(names) == 50
     for n in names:
         assert hasattr(pa.lib, n), n
         assert C.cast(getattr(pa.lib, n), C.c_void_p).value
@@ -27,7 +27,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_status_strings():
-    assert pa.lib.pa_abi_version() == 4
+    assert pa.lib.pa_abi_version() == 5
     for code in range(10):
         assert pa.lib.pa_status_string(code)
     assert pa.lib.pa_status_string(99) == b"unknown status"
@@ -199,3 +199,33 @@ def test_decode_multi_validation_rejects_before_launch():
     n = pa.lib.pa_decode_multi_workspace_bytes(10, 32, 128, 1000, 512)
     lay = pa.split_layout(10, 32, 128, 1000, 512)
     assert n == (lay["total"] + 255) // 256 * 256 + 40
+
+
+def _shared(**kw):
+    a = dict(out=16, query=16, kc=16, vc=16, tab=16, ctx=16, gs=16, pl=16, S=4, G=2, MG=4, H=32, Hkv=32, D=128,
+             bs=16, MB=4, NB=8, maxlen=64, scale=0.1, ks=1.0, vs=1.0, dt=F, kv=F, flags=0, ws=256, wsb=1 << 20)
+    a.update(kw)
+    return pa.lib.pa_decode_shared(a["out"], a["query"], a["kc"], a["vc"], a["tab"], a["ctx"], a["gs"], a["pl"],
+                                   a["S"], a["G"], a["MG"], a["H"], a["Hkv"], a["D"], a["bs"], a["MB"], a["NB"],
+                                   a["maxlen"], a["scale"], a["ks"], a["vs"], a["dt"], a["kv"], a["flags"], a["ws"],
+                                   a["wsb"], None)
+
+
+def test_shared_prefix_decode_validation_rejects_before_launch():
+    assert _shared(S=0, G=0) == 0            # nothing to do, nothing launched
+    assert _shared(MG=0) == 1
+    assert _shared(G=0) == 1                 # the groups must cover the sequences
+    assert _shared(G=5) == 1
+    assert _shared(gs=0) == 1
+    assert _shared(pl=0) == 1
+    assert _shared(flags=2) == 1             # no split flag
+    assert _shared(wsb=64) == 7              # workspace too small
+    assert _shared(ws=16) == 1               # not 256-byte aligned
+    assert _shared(D=96) == 5
+    assert _shared(kv=pa.PA_FP8_E4M3, ks=0.0) == 1
+    # m and l (4 x 32 rows of one 64-token partition, each padded to 256 bytes), o, then
+    # one int per sequence
+    assert pa.pa_decode_shared_workspace_bytes(4, 32, 128, 64) == 512 + 512 + 4 * 32 * 128 * 4 + 4 * 4
+    # 4096 tokens: eight partitions of 512
+    assert pa.pa_decode_shared_workspace_bytes(4, 32, 128, 4096) == 4096 + 4096 + 4 * 32 * 8 * 128 * 4 + 4 * 4
+    assert pa.pa_decode_shared_workspace_bytes(-1, 32, 128, 64) == 0

@@ -280,3 +280,96 @@ def test_random_swap_and_window_ops_bit_exact(seed):
     c2, o2 = cpp.clone(), ora.clone()
     same_state(c2, o2)
     same_host_state(c2, o2)
+
+
+def _groups_reference(tables, lens, bs):
+    """Shared-prefix groups written out from their definition in include/pa.h."""
+    n = len(lens)
+    used = [min(-(-max(c, 0) // bs), len(tables[i])) for i, c in enumerate(lens)]
+    gs, pl, widest = [], [0] * n, 1 if n else 0
+    i = 0
+    while i < n:
+        stop = i + 1
+        while used[i] and stop < n and used[stop] and tables[stop][0] == tables[i][0]:
+            stop += 1
+        shared = []
+        for m in range(i, stop):
+            k = 0
+            while k < min(used[m], used[i]) and tables[m][k] == tables[i][k]:
+                k += 1
+            shared.append(k)
+        p = min(min(shared) * bs, min(max(lens[m], 0) for m in range(i, stop)))
+        if stop - i > 1 and p >= bs:
+            gs.append(i)
+            for m in range(i, stop):
+                pl[m] = p
+            widest = max(widest, stop - i)
+        else:
+            gs.extend(range(i, stop))
+        i = stop
+    return gs + [n], pl, len(gs), widest
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_shared_prefix_groups_match_definition(seed):
+    """Random families of forked sequences (shared leading blocks, then own blocks), loners
+    and empty sequences: the C++ grouping equals the definition, and every member's first
+    P tokens sit in the same (block, offset) as its group's first member's."""
+    rng = np.random.default_rng(seed)
+    bs = int(rng.choice([16, 32]))
+    tables, lens = [], []
+    nxt = 0
+    while len(lens) < 40:
+        kind = rng.integers(0, 4)
+        if kind == 0:                                   # an empty sequence
+            tables.append([]), lens.append(0)
+            continue
+        members = int(rng.integers(1, 7))
+        shared_blocks = int(rng.integers(0, 6))
+        base = list(range(nxt, nxt + shared_blocks))
+        nxt += shared_blocks
+        for _ in range(members):
+            own = int(rng.integers(0, 4))
+            t = base + list(range(nxt, nxt + own))
+            nxt += own
+            if not t:
+                t = [nxt]
+                nxt += 1
+            n = int(rng.integers((len(t) - 1) * bs + 1, len(t) * bs + 1))
+            tables.append(t), lens.append(n)
+    mb = max(len(t) for t in tables) + 1
+    rows = [t + [-1] * (mb - len(t)) for t in tables]
+    got = pa.pa_shared_prefix_groups(rows, lens, bs)
+    assert got == _groups_reference(rows, lens, bs)
+    gs, pl, ng, mg = got
+    assert gs[0] == 0 and gs[-1] == len(lens) and all(a < b for a, b in zip(gs, gs[1:]))
+    for g in range(ng):
+        lead = gs[g]
+        for m in range(gs[g], gs[g + 1]):
+            assert pl[m] == pl[lead] <= lens[m]
+            for t in range(pl[m]):
+                assert rows[m][t // bs] == rows[lead][t // bs]
+
+
+def test_shared_prefix_groups_of_a_forked_batch():
+    """Parallel sampling through the allocator: three parents of 100, 64 and 40 tokens forked
+    into 3, 2 and 1 branches; each branch appends its own tokens (copy-on-write of the last
+    block).  The families become the groups; a single branch is a group of one."""
+    bs = 16
+    al = pa.Allocator(200, bs)
+    sid = 0
+    ids = []
+    for parent, (n, k) in enumerate([(100, 3), (64, 2), (40, 1)]):
+        al.seq_create(1000 + parent, n)
+        for _ in range(k):
+            al.seq_fork(1000 + parent, sid, n)
+            ids.append(sid)
+            sid += 1
+        al.seq_free(1000 + parent)
+    for _ in range(5):
+        al.seq_append_slots(ids)
+    tabs, lens = al.build_block_tables(ids, 16)
+    gs, pl, ng, mg = pa.pa_shared_prefix_groups(tabs, lens, bs)
+    # 100 tokens: 6 full blocks shared, the 7th copied on the first append; 64 tokens: 4 full blocks
+    assert (gs, ng, mg) == ([0, 3, 5, 6], 3, 3)
+    assert pl == [96, 96, 96, 64, 64, 0]
