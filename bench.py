@@ -246,10 +246,12 @@ def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         v, n, ck, cn = meas[c]
         out.append(f"| {c} | {v:.1f} | {n} | {ck:.1f} | {cn} | {scale[c]:.4f} |")
-    out += ["", f"Scaled HBM traffic per decode launch: **{traffic / 1e6:.2f} MB** "
+    unit = "call (both launches)" if per_call == 2 else "launch"
+    out += ["", f"Scaled HBM traffic per decode {unit}: **{traffic / 1e6:.2f} MB** "
                 f"(fetch {meas['FETCH_SIZE'][0] * 1024 * scale['FETCH_SIZE'] / 1e6:.2f} MB + write "
                 f"{meas['WRITE_SIZE'][0] * 1024 * scale['WRITE_SIZE'] / 1e6:.2f} MB); "
-                f"average decode duration in the trace {dec_avg_ns / 1e3:.2f} us."]
+                f"average decode duration in the trace {dec_avg_ns / 1e3:.2f} us"
+                + (" (the two launches' averages added)." if per_call == 2 else ".")]
     print("\n".join(out))
 
 
