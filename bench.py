@@ -368,7 +368,11 @@ class Bench:
         for _ in range(2):
             hb = torch.empty(total, dtype=torch.int32).pin_memory()
             db = torch.empty(total, dtype=torch.int32, device=self.dev)
-            b = {"idx_h": hb, "idx_d": db, "staged": torch.cuda.Event()}
+            # "done": recorded after the step's decode; the step that reuses this buffer waits for it
+            # on the host (the decode that read the buffer, and so its upload, has finished).  One
+            # event per step serves both this and, in timed steps, the end of the decode's timing:
+            # every event recorded on the stream adds a few microseconds between kernels.
+            b = {"idx_h": hb, "idx_d": db, "done": torch.cuda.Event()}
             for side, t in (("h", hb), ("d", db)):
                 b["slots_" + side] = t[0:NS]
                 b["len_" + side] = t[NS:NS + S]
@@ -377,7 +381,7 @@ class Bench:
                 b["tab_" + side] = t[3 * NS + 2 * S:tab_end].view(S, self.max_blocks)
                 b["gs_" + side] = t[tab_end:tab_end + S + 1]
                 b["pl_" + side] = t[tab_end + S + 1:]
-            b["staged"].record(self.stream)
+            b["done"].record(self.stream)
             self.bufs.append(b)
         self.elem = synth.ELEM_BYTES[w.dtype]
         self.kv_elem = 1 if self.quant else self.elem
@@ -386,7 +390,7 @@ class Bench:
     def step(self, k: int, timing: list | None):
         pa, w = self.pa, self.w
         b = self.bufs[k % 2]
-        b["staged"].synchronize()  # the uploads that last read this staging buffer are done
+        b["done"].synchronize()  # the step that last used this buffer is done, its upload included
         alloc = self.alloc
         if self.base is not None:
             alloc = self.alloc = self.base.clone()
@@ -414,7 +418,6 @@ class Bench:
                                    b["slots_h"], w.k_scale, w.v_scale, kv_format=w.kv_format or None)
         else:
             pa.pa_upload(b["idx_d"], b["idx_h"])
-        b["staged"].record(self.stream)
         if npairs:
             pa.pa_copy_blocks(self.kc, self.vc, b["pairs_d"], num_pairs=npairs)
         if one_launch:
@@ -460,8 +463,12 @@ class Bench:
             self.path_ran.add(pa.pa_decode_auto(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"],
                                                 self.max_ctx, w.scale, self.args.partition, self.ws,
                                                 seq_order=order, cached_kv=self.cached))
-        if timing is not None:
+        if timing is None:
+            b["done"] = self.torch.cuda.Event()  # a fresh one: a timing event may sit here
+            b["done"].record(self.stream)
+        else:
             e1.record(self.stream)
+            b["done"] = e1
             lens = b["len_h"].numpy()
             timing.append((e0, e1, int(lens.sum()), int(((lens + w.block_size - 1) // w.block_size).sum()), npairs))
 
