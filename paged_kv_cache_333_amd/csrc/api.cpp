@@ -6,6 +6,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <unordered_set>
 #include <vector>
@@ -156,6 +157,51 @@ struct SplitSizes {
   int32_t parts;
 };
 
+// Launch shape of the single pass (max_query_len 0) or of the several-token
+// pass: workgroups per sequence and workgroups the device holds at once.  The
+// occupancy query behind it costs host time on every decode call, so the
+// answer is kept per (device, dtypes, head_dim, block_size, heads, group,
+// max_query_len).
+hipError_t launch_shape(const pa::DecodeArgs& a, int32_t max_query_len, int64_t* workgroups, int64_t* resident) {
+  struct Entry {
+    int64_t key[8];
+    int64_t per_seq, resident;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> memo;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const int64_t key[8] = {dev, a.dtype, a.kv_dtype, a.head_dim, a.block_size, a.num_heads, a.num_kv_heads,
+                          max_query_len};
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Entry& en : memo)
+      if (std::equal(key, key + 8, en.key)) {
+        *workgroups = en.per_seq * a.num_seqs;
+        *resident = en.resident;
+        return hipSuccess;
+      }
+  }
+  pa::DecodeArgs one = a;
+  one.num_seqs = 1;
+  int64_t per_seq = 0, res = 0;
+  e = max_query_len > 0 ? pa::multi_pass_shape(one, max_query_len, &per_seq, &res)
+                        : pa::single_pass_shape(one, &per_seq, &res);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    Entry en{};
+    std::copy(key, key + 8, en.key);
+    en.per_seq = per_seq;
+    en.resident = res;
+    if (memo.size() < 256) memo.push_back(en);
+  }
+  *workgroups = per_seq * a.num_seqs;
+  *resident = res;
+  return hipSuccess;
+}
+
 bool split_sizes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
                  int32_t partition_size, SplitSizes* out) {
   if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0 || partition_size <= 0)
@@ -203,7 +249,7 @@ bool choose_split(const pa::DecodeArgs& a, int32_t partition_size, const void* w
       static_cast<int64_t>(workspace_bytes) < z.total)
     return false;
   int64_t workgroups = 0, resident = 0;
-  const bool ok = pa::single_pass_shape(a, &workgroups, &resident) == hipSuccess;
+  const bool ok = launch_shape(a, 0, &workgroups, &resident) == hipSuccess;
   (void)hipGetLastError();
   return ok && workgroups < resident;
 }
@@ -628,7 +674,7 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache, c
              partition_size <= 4096 && a.max_context_len >= 4 * static_cast<int64_t>(partition_size) && sizes_ok &&
              static_cast<int64_t>(workspace_bytes) >= need) {
     int64_t workgroups = 0, resident = 0;
-    const bool ok = pa::multi_pass_shape(a, max_query_len, &workgroups, &resident) == hipSuccess;
+    const bool ok = launch_shape(a, max_query_len, &workgroups, &resident) == hipSuccess;
     (void)hipGetLastError();
     split = ok && workgroups < resident;
   }
