@@ -573,7 +573,8 @@ size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int
  * members' queries as the columns of the q.K tile, into per-member partials;
  * the second decodes each sequence's own tokens P .. n-1 (the prefix's blocks
  * are not read) and merges the two by the log-sum-exp rule.  A member whose
- * prefix_len differs from its group's gets NaN rows; sequences outside every
+ * prefix_len differs from its group's, and every member of a group larger
+ * than max_group_size, get NaN rows; sequences outside every
  * group, or groups that do not share the blocks they claim, give undefined
  * values (all of this is rejected under PA_DEBUG).  Pools, scales, kv_dtype
  * and errors as in pa_decode_masked; flags: PA_DECODE_CACHED_KV only;

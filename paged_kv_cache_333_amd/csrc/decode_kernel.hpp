@@ -274,7 +274,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int nctx = a.ctx[shared ? qs : s];
   // (an empty context is valid for plain decode: a zero row; a span of query
   // tokens must lie inside the context)
-  const bool bad_len = nctx < 0 || nctx > a.len_limit || (a.q_start && !shared && L > nctx);
+  // (a group with more members than the launch's tiles cover is invalid as a
+  // whole: its members get no partials, and the merge sees a -1 length)
+  const bool bad_len = nctx < 0 || nctx > a.len_limit || (a.q_start && !shared && L > nctx) ||
+                       (shared && L > a.q_chunks * col_toks);
   // Causal limits: query token i sits at position nctx - L + i and sees the
   // positions before nctx - L + i + 1.  This lane's column, and the tile's
   // nearest and furthest limits (all nctx for one token per sequence, and for
@@ -326,6 +329,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     // the merge needs each query row's context length (any head group writes the same)
     if (a.ws_len && part == 0 && grp == 0 && q == 0 && n < NC && (n & (col_heads - 1)) == 0 && my_tok < L)
       a.ws_len[qs + my_tok] = bad_len ? -1 : (shared ? nctx : lim_base + my_tok);
+    if (shared && a.ws_len && part == 0 && grp == 0 && chunk == 0) {
+      // members past the last tile of the launch: no workgroup computes them
+      for (int i = a.q_chunks * col_toks + lane; i < L; i += 64) a.ws_len[qs + i] = -1;
+    }
   }
   AppendRow<T, D> fresh;  // the fused slot-mapping write (pa_decode_append)
   if constexpr (APPEND)

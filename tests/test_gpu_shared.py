@@ -176,3 +176,20 @@ def test_parallel_sampling_workload_full_size_sampled():
     for s, h in sample_pairs(w, 12, seed=5):
         assert_close(got[s, h], dw.oracle_row(s, h), w.dtype, f"seq {s} head {h}")
     assert np.max(np.abs(got - out_to_f64(plain, w.dtype))) < 2e-3
+
+
+def test_group_larger_than_max_group_size_gets_nan_rows():
+    """max_group_size below a group's size: that group's rows are NaN (none stale), the
+    other groups still match the oracle."""
+    c = make_case(6, "f16", None, 4, 4, 64, 16)
+    gs, pl, ng, mg = pa.pa_shared_prefix_groups(c["tables"].tolist(), c["ctx"], 16)
+    assert mg == 17
+    dv = dev(c)
+    run_shared(c, dv, (gs, pl, ng, mg))              # a valid call first: the workspace holds its lengths
+    got = run_shared(c, dv, (gs, pl, ng, 5))
+    big = [g for g in range(ng) if gs[g + 1] - gs[g] == 17][0]
+    rows = list(range(gs[big], gs[big + 1]))
+    assert np.all(np.isnan(got[rows]))
+    ref = oracle(c)
+    ok = [s for s in range(c["S"]) if s not in rows]
+    assert_close(got[ok], ref[ok], "f16", "the other groups")
