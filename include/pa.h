@@ -49,6 +49,12 @@
  * is loaded, device calls first copy the index arrays back to the host
  * (synchronising `stream`) and validate them, returning PA_ERR_BAD_TABLE on
  * any violation, and synchronise after the launch to report kernel errors.
+ *
+ * Two more switches are read on every call: PA_SPLIT=never / always overrides
+ * the automatic path choice of pa_decode_auto, pa_decode_quant,
+ * pa_decode_masked and pa_decode_multi (always: whenever the workspace and
+ * partition size allow a split); PA_LOG=1 makes pa_build_block_tables print
+ * each table to stderr ("pa: seq <id>: [blocks] len <n>").
  */
 #ifndef PA_H_
 #define PA_H_

@@ -26,8 +26,11 @@
 // The free queue is a ring buffer of num_blocks entries; a block is never in
 // it twice, so it never overflows.
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <numeric>
+#include <string>
 #include <mutex>
 #include <unordered_map>
 #include <unordered_set>
@@ -36,6 +39,13 @@
 #include "status.hpp"
 
 namespace {
+
+// PA_LOG=1 (or any value but 0): pa_build_block_tables dumps the tables it
+// builds.  Read on every call.
+bool log_tables() {
+  const char* v = std::getenv("PA_LOG");
+  return v && v[0] != '\0' && std::strcmp(v, "0") != 0;
+}
 
 struct Seq {
   std::vector<int32_t> table;
@@ -500,6 +510,15 @@ pa_status pa_build_block_tables(const pa_allocator* a, const int64_t* seq_ids, i
     if (k) std::memcpy(row, t.data(), k * sizeof(int32_t));
     for (int32_t j = k; j < max_blocks; ++j) row[j] = -1;
     context_lens[i] = ptrs[i]->len;
+  }
+  if (log_tables()) {  // PA_LOG=1: one line per sequence on stderr, as "seq 0: [3, 7, 11] len 40"
+    for (int32_t i = 0; i < n; ++i) {
+      std::string line = "pa: seq " + std::to_string(seq_ids[i]) + ": [";
+      const auto& t = ptrs[i]->table;
+      for (size_t j = 0; j < t.size(); ++j) line += (j ? ", " : "") + std::to_string(t[j]);
+      line += "] len " + std::to_string(ptrs[i]->len) + "\n";
+      std::fputs(line.c_str(), stderr);
+    }
   }
   return PA_OK;
 }

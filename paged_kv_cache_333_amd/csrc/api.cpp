@@ -240,14 +240,28 @@ pa_status make_layout(void* workspace, size_t workspace_bytes, int32_t num_seqs,
 // device (fewer workgroups than it holds at once, so compute units would sit
 // idle while a few workgroups walk very long contexts), the context spans at
 // least four partitions and the workspace is large enough.
+// PA_SPLIT=never / always overrides the automatic path choice (always: when
+// the workspace and partition size allow a split); unset or anything else:
+// the rule.  Read on every call, so a process can change it between calls.
+int split_override() {
+  const char* v = std::getenv("PA_SPLIT");
+  if (!v) return 0;
+  if (std::strcmp(v, "never") == 0) return -1;
+  if (std::strcmp(v, "always") == 0) return 1;
+  return 0;
+}
+
 bool choose_split(const pa::DecodeArgs& a, int32_t partition_size, const void* workspace, size_t workspace_bytes) {
-  if (!workspace || a.num_seqs <= 0 || partition_size <= 0 || partition_size % a.block_size ||
-      partition_size > 4096 || a.max_context_len < 4 * static_cast<int64_t>(partition_size))
+  const int force = split_override();
+  if (force < 0 || !workspace || a.num_seqs <= 0 || partition_size <= 0 || partition_size % a.block_size ||
+      partition_size > 4096)
     return false;
   SplitSizes z;
   if (!split_sizes(a.num_seqs, a.num_heads, a.head_dim, a.max_context_len, partition_size, &z) ||
       static_cast<int64_t>(workspace_bytes) < z.total)
     return false;
+  if (force > 0) return true;
+  if (a.max_context_len < 4 * static_cast<int64_t>(partition_size)) return false;
   int64_t workgroups = 0, resident = 0;
   const bool ok = launch_shape(a, 0, &workgroups, &resident) == hipSuccess;
   (void)hipGetLastError();
@@ -670,13 +684,17 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache, c
     if (partition_size <= 0 || partition_size % block_size || partition_size > 4096)
       return fail(PA_ERR_INVALID_ARG, "partition_size must be a multiple of block_size, at most 4096");
     split = true;
-  } else if (workspace && num_seqs > 0 && partition_size > 0 && partition_size % block_size == 0 &&
-             partition_size <= 4096 && a.max_context_len >= 4 * static_cast<int64_t>(partition_size) && sizes_ok &&
+  } else if (split_override() >= 0 && workspace && num_seqs > 0 && partition_size > 0 &&
+             partition_size % block_size == 0 && partition_size <= 4096 && sizes_ok &&
              static_cast<int64_t>(workspace_bytes) >= need) {
-    int64_t workgroups = 0, resident = 0;
-    const bool ok = launch_shape(a, max_query_len, &workgroups, &resident) == hipSuccess;
-    (void)hipGetLastError();
-    split = ok && workgroups < resident;
+    if (split_override() > 0) {
+      split = true;
+    } else if (a.max_context_len >= 4 * static_cast<int64_t>(partition_size)) {
+      int64_t workgroups = 0, resident = 0;
+      const bool ok = launch_shape(a, max_query_len, &workgroups, &resident) == hipSuccess;
+      (void)hipGetLastError();
+      split = ok && workgroups < resident;
+    }
   }
   if (path) *path = split ? 1 : 0;
   if (num_seqs == 0 || num_query_tokens == 0) return PA_OK;

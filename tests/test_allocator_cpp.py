@@ -373,3 +373,16 @@ def test_shared_prefix_groups_of_a_forked_batch():
     # 100 tokens: 6 full blocks shared, the 7th copied on the first append; 64 tokens: 4 full blocks
     assert (gs, ng, mg) == ([0, 3, 5, 6], 3, 3)
     assert pl == [96, 96, 96, 64, 64, 0]
+
+
+def test_pa_log_dumps_tables(monkeypatch, capfd):
+    """PA_LOG=1: pa_build_block_tables writes one line per sequence to stderr; unset, nothing."""
+    al = pa.Allocator(8, 16, list(range(8)))
+    al.seq_create(5, 40)
+    al.seq_create(6, 0)
+    al.build_block_tables([5, 6], 4)
+    assert "pa: seq" not in capfd.readouterr().err
+    monkeypatch.setenv("PA_LOG", "1")
+    al.build_block_tables([5, 6], 4)
+    err = capfd.readouterr().err
+    assert "pa: seq 5: [0, 1, 2] len 40" in err and "pa: seq 6: [] len 0" in err

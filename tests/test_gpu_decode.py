@@ -428,3 +428,25 @@ def test_auto_picks_split_for_few_long_sequences_and_single_otherwise():
                                  dw.max_context_len, w.scale, 512, None) == "single"
         del dw, ws, direct
         torch.cuda.empty_cache()
+
+
+def test_pa_split_environment_override(monkeypatch):
+    """PA_SPLIT=always / never overrides the auto rule (always only with a workspace); both
+    paths agree with the oracle."""
+    ctx = (1000, 513, 37, 2049)
+    c = make_case(71, "f16", 4, 8, 2, 128, 16, ctx)
+    dv = to_dev(c)
+    ref = oracle(c)
+    max_ctx = c["MB"] * c["bs"]
+    ws = torch.empty(pa.pa_decode_split_workspace_bytes(4, 8, 128, max_ctx, 64), dtype=torch.uint8, device="cuda")
+    for env, want in (("always", "split"), ("never", "single")):
+        monkeypatch.setenv("PA_SPLIT", env)
+        out = torch.empty_like(dv["q"])
+        got = pa.pa_decode_auto(out, dv["q"], dv["kc"], dv["vc"], dv["tables"], dv["ctx"], max_ctx, scale_for(128),
+                                64, ws)
+        torch.cuda.synchronize()
+        assert got == want
+        assert_close(out_to_f64(out, "f16"), ref, "f16", env)
+        assert pa.pa_decode_auto(out, dv["q"], dv["kc"], dv["vc"], dv["tables"], dv["ctx"], max_ctx,
+                                 scale_for(128), 64, None) == "single"
+    monkeypatch.delenv("PA_SPLIT")
