@@ -375,8 +375,15 @@ pa_status pa_upload(void* dst, const void* src, size_t nbytes, void* stream);
  * write of pa_reshape_and_cache_quant with k_scale, v_scale.  The two parts
  * are independent: nothing in dst may be needed by the write, and a write
  * into a block that a copy-on-write pair of the same step copies must wait
- * for that copy (use pa_upload, pa_copy_blocks, then the write).  Errors as
- * in pa_upload and the write it stands for.  Bit-exact. */
+ * for that copy (use pa_upload, pa_copy_blocks, then the write).  The call
+ * also reads slot_mapping on the host, so it must hold its final values when
+ * the call is made.  When no two tokens' slots fall in one block (a decode
+ * step appending one token per sequence) and block_size is 32, the write
+ * stores each written value tile whole (every cache line of the tile, the
+ * other columns unchanged) rather than one element per dim row; the result
+ * is the same.  PA_TILE_WRITE=always / never overrides the block-size rule
+ * (never the one-token-per-block condition).  Errors as in pa_upload and the
+ * write it stands for.  Bit-exact. */
 pa_status pa_upload_and_cache(void* dst, const void* src, size_t nbytes, const void* key, const void* value,
                               void* key_cache, void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
                               int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,

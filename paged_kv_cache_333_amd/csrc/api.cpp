@@ -39,6 +39,48 @@ pa_status check_scales(float k_scale, float v_scale) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Form of pa_upload_and_cache's write when every token has a block of its
+// own.  The whole-tile form rewrites each written value tile in full lines
+// instead of one element per dim row.  Measured on full decode steps: with
+// 32-token blocks it shortens the step (GQA bf16 216 -> 200 us, the decode
+// after it running at its clean-cache speed); with 16-token blocks the step
+// is the same either way, the time the shorter write saves reappearing in
+// the decode that follows, so the element-wise form stays there.
+// PA_TILE_WRITE=always / never overrides the rule (read on every call); the
+// whole-tile form is never used when two tokens share a block.
+bool tile_write_wanted(int32_t block_size) {
+  const char* v = std::getenv("PA_TILE_WRITE");
+  if (v && std::strcmp(v, "always") == 0) return true;
+  if (v && std::strcmp(v, "never") == 0) return false;
+  return block_size >= 32;
+}
+
+// True when no two tokens' slots inside the pool fall in one block.  Read on
+// the host from the page-locked slot mapping (final at the call).  O(n) with
+// a per-thread stamp per block.
+bool one_token_per_block(const int32_t* slots, int32_t n, int32_t num_blocks, int32_t block_size) {
+  if (n <= 1) return true;
+  thread_local std::vector<uint32_t> stamp;
+  thread_local uint32_t epoch = 0;
+  if (stamp.size() < static_cast<size_t>(num_blocks)) {
+    stamp.assign(static_cast<size_t>(num_blocks), 0u);
+    epoch = 0;
+  }
+  if (++epoch == 0) {  // wrapped: clear and start again
+    std::fill(stamp.begin(), stamp.end(), 0u);
+    epoch = 1;
+  }
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t slot = slots[i];
+    if (slot < 0 || slot >= num_slots) continue;
+    uint32_t& st = stamp[static_cast<size_t>(slot / block_size)];
+    if (st == epoch) return false;
+    st = epoch;
+  }
+  return true;
+}
+
 pa_status hip_fail(hipError_t e, const char* what) {
   return fail(PA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
@@ -473,10 +515,15 @@ pa_status pa_upload_and_cache(void* dst, const void* src, size_t nbytes, const v
       return fail(PA_ERR_INVALID_ARG, "slot_mapping must be page-locked host memory");
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // whole-tile write when every token has a block of its own (a decode step appending one token per sequence)
+  const int32_t* tiles = num_tokens > 0 && tile_write_wanted(block_size) &&
+                                 one_token_per_block(slot_mapping, num_tokens, num_blocks, block_size)
+                             ? slot_mapping
+                             : nullptr;
   return finish(pa::launch_upload_and_cache(dst, src_view, static_cast<int64_t>(nbytes), key, value, key_cache,
                                             value_cache, static_cast<const int32_t*>(slots_view), num_tokens,
                                             num_blocks, num_kv_heads, head_dim, block_size, dtype, kv_dtype,
-                                            k_scale, v_scale, st),
+                                            k_scale, v_scale, tiles, st),
                 st, "pa_upload_and_cache");
 }
 

@@ -76,6 +76,90 @@ __device__ __forceinline__ void write_chunk(const WriteArgs& a, int64_t idx, con
   }
 }
 
+// Element `e` of a 16-byte chunk of E-byte elements replaced by the low 8*E
+// bits of x (selects over the four words, no indexed register access).
+template <int E>
+__device__ __forceinline__ u32x4 with_element(u32x4 v, int e, uint32_t x) {
+  const int w = e * E / 4;
+  const int sh = (e * E % 4) * 8;
+  uint32_t mask;
+  if constexpr (E == 4)
+    mask = 0xffffffffu;
+  else
+    mask = ((1u << (8 * E)) - 1u) << sh;
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t vi = word(v, i);
+    r[i] = i == w ? (vi & ~mask) | ((x << sh) & mask) : vi;
+  }
+  return r;
+}
+
+// Whole-tile form of the write, used when no two tokens of a call fall in
+// one block (a decode step that appends one token per sequence: the block a
+// sequence writes has that sequence as its only owner).  A token's value
+// column crosses every cache line of its dim-major value tile, so the
+// element-wise stores above leave each line of the tile partly written, and
+// writing such lines back to HBM slows the kernels that follow far beyond
+// their byte count (a decode right after such a write runs measurably slower
+// than after a write of whole lines).  Here one workgroup owns the tiles of
+// KV heads h0..h1-1 of one token: it stores the key rows in 16-byte chunks,
+// reads the value tiles chunk by chunk, puts the new element into the chunk
+// of each dim row that holds column `offset`, and stores every chunk back, so
+// every line of the tiles is written whole and only the new column changes.
+// Bit-exact, like the element-wise form.
+template <int E>
+__device__ __forceinline__ void write_tile(const WriteArgs& a, int64_t tok, int32_t h0, int32_t h1, int64_t slot) {
+  constexpr int EPL = 16 / E;
+  const int64_t blk = slot / a.block_size;
+  const int32_t off = static_cast<int32_t>(slot - blk * a.block_size);
+  const int32_t cpr = a.head_dim / EPL;
+  for (int32_t j = threadIdx.x; j < (h1 - h0) * cpr; j += blockDim.x) {
+    const int32_t h = h0 + j / cpr;
+    const int32_t c = j - (h - h0) * cpr;
+    const int64_t tile = blk * a.num_kv_heads + h;
+    store16(a.key_cache + ((tile * a.block_size + off) * a.head_dim + static_cast<int64_t>(c) * EPL) * E,
+            load16(a.key + ((tok * a.num_kv_heads + h) * a.head_dim + static_cast<int64_t>(c) * EPL) * E));
+  }
+  // the value tiles of heads h0..h1-1 are contiguous: [h, d, chunk of the row]
+  const int32_t rc = a.block_size / EPL;  // chunks per dim row of the value tile
+  const int32_t oc = off / EPL;           // the chunk of a row holding column `off`
+  const int32_t oe = off - oc * EPL;      // and its element there
+  char* vt = a.value_cache + (blk * a.num_kv_heads + h0) * a.head_dim * a.block_size * E;
+  const char* vin = a.value + (tok * a.num_kv_heads + h0) * a.head_dim * E;  // rows of heads h0.. of the token
+  const int32_t n = (h1 - h0) * a.head_dim * rc;
+  for (int32_t i = threadIdx.x; i < n; i += blockDim.x) {
+    u32x4 v = load16(vt + static_cast<int64_t>(i) * 16);
+    const int32_t r = i / rc;  // (head - h0) * head_dim + d
+    if (i - r * rc == oc) {
+      uint32_t x;
+      if constexpr (E == 4)
+        x = *reinterpret_cast<const uint32_t*>(vin + static_cast<int64_t>(r) * 4);
+      else
+        x = *reinterpret_cast<const uint16_t*>(vin + static_cast<int64_t>(r) * 2);
+      v = with_element<E>(v, oe, x);
+    }
+    store16(vt + static_cast<int64_t>(i) * 16, v);
+  }
+}
+
+// The codes of the EPL key elements of input chunk `kx` (x / k_scale, see
+// write_chunk_quant), stored as EPL bytes at `dst`.
+template <typename T, typename C>
+__device__ __forceinline__ void store_key_codes(const WriteArgs& a, u32x4 kx, char* dst) {
+  constexpr int EPL = T::kEPL;
+  constexpr int NW = EPL / 4;  // 32-bit words of codes per chunk
+  uint32_t kw[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) kw[w] = 0;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) kw[e / 4] |= to_code(C{}, elem_to_float(T{}, kx, e) / a.k_scale) << (8 * (e % 4));
+  uint32_t* krow = reinterpret_cast<uint32_t*>(dst);
+#pragma unroll
+  for (int w = 0; w < NW; ++w) krow[w] = kw[w];
+}
+
 // The slot-mapping write into 8-bit pools (the quantised cache of the xdnf.cn
 // article, §2.3 and §6.3: KV values stored as 8-bit codes).  Same thread
 // layout: one thread per 16-byte chunk of one (token, KV head) input row, EPL
@@ -86,7 +170,6 @@ __device__ __forceinline__ void write_chunk(const WriteArgs& a, int64_t idx, con
 template <typename T, typename C, bool HOST_SLOTS>
 __device__ __forceinline__ void write_chunk_quant(const WriteArgs& a, int64_t idx, const HostSlots& hs) {
   constexpr int EPL = T::kEPL;
-  constexpr int NW = EPL / 4;  // 32-bit words of codes per chunk
   const int32_t cpr = a.head_dim / EPL;
   const int64_t per_token = static_cast<int64_t>(a.num_kv_heads) * cpr;
   if (idx >= per_token * a.num_tokens) return;
@@ -99,31 +182,68 @@ __device__ __forceinline__ void write_chunk_quant(const WriteArgs& a, int64_t id
   const int64_t blk = slot / a.block_size;
   const int64_t off = slot - blk * a.block_size;
   const int64_t tile = blk * a.num_kv_heads + h;
-  const u32x4 kx = load16(a.key + idx * 16);
+  store_key_codes<T, C>(a, load16(a.key + idx * 16),
+                        a.key_cache + (tile * a.block_size + off) * a.head_dim + static_cast<int64_t>(c) * EPL);
   const u32x4 vx = load16(a.value + idx * 16);
-  uint32_t kw[NW];
-#pragma unroll
-  for (int w = 0; w < NW; ++w) kw[w] = 0;
   uint8_t* vcol = reinterpret_cast<uint8_t*>(a.value_cache) +
                   (tile * a.head_dim + static_cast<int64_t>(c) * EPL) * a.block_size + off;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    kw[e / 4] |= to_code(C{}, elem_to_float(T{}, kx, e) / a.k_scale) << (8 * (e % 4));
+  for (int e = 0; e < EPL; ++e)
     vcol[static_cast<int64_t>(e) * a.block_size] =
         static_cast<uint8_t>(to_code(C{}, elem_to_float(T{}, vx, e) / a.v_scale));
-  }
-  uint32_t* krow = reinterpret_cast<uint32_t*>(a.key_cache + (tile * a.block_size + off) * a.head_dim +
-                                               static_cast<int64_t>(c) * EPL);
-#pragma unroll
-  for (int w = 0; w < NW; ++w) krow[w] = kw[w];
 }
 
-// W::template run<HOST_SLOTS>(a, idx) is one of the two writes above.
+// Whole-tile form of the quantising write (see write_tile): the key codes of
+// the token's rows, then the value tiles [D, bs] of one-byte codes read and
+// stored back in 16-byte chunks with the new column's codes put in.
+template <typename T, typename C>
+__device__ __forceinline__ void write_tile_quant(const WriteArgs& a, int64_t tok, int32_t h0, int32_t h1,
+                                                 int64_t slot) {
+  constexpr int EPL = T::kEPL;
+  constexpr int EB = T::kBytes;
+  const int64_t blk = slot / a.block_size;
+  const int32_t off = static_cast<int32_t>(slot - blk * a.block_size);
+  const int32_t cpr = a.head_dim / EPL;
+  for (int32_t j = threadIdx.x; j < (h1 - h0) * cpr; j += blockDim.x) {
+    const int32_t h = h0 + j / cpr;
+    const int32_t c = j - (h - h0) * cpr;
+    const int64_t tile = blk * a.num_kv_heads + h;
+    store_key_codes<T, C>(a, load16(a.key + ((tok * a.num_kv_heads + h) * a.head_dim +
+                                             static_cast<int64_t>(c) * EPL) * EB),
+                          a.key_cache + (tile * a.block_size + off) * a.head_dim + static_cast<int64_t>(c) * EPL);
+  }
+  const int32_t rc = a.block_size / 16;  // 16-byte chunks per dim row of codes
+  const int32_t oc = off / 16;
+  const int32_t oe = off - oc * 16;
+  char* vt = a.value_cache + (blk * a.num_kv_heads + h0) * a.head_dim * a.block_size;
+  const char* vin = a.value + (tok * a.num_kv_heads + h0) * a.head_dim * EB;
+  const int32_t n = (h1 - h0) * a.head_dim * rc;
+  for (int32_t i = threadIdx.x; i < n; i += blockDim.x) {
+    u32x4 v = load16(vt + static_cast<int64_t>(i) * 16);
+    const int32_t r = i / rc;
+    if (i - r * rc == oc) {
+      uint32_t x;
+      if constexpr (EB == 4)
+        x = *reinterpret_cast<const uint32_t*>(vin + static_cast<int64_t>(r) * 4);
+      else
+        x = *reinterpret_cast<const uint16_t*>(vin + static_cast<int64_t>(r) * 2);
+      const u32x4 xin = {x, 0u, 0u, 0u};  // the element as element 0 of a chunk
+      v = with_element<1>(v, oe, to_code(C{}, elem_to_float(T{}, xin, 0) / a.v_scale));
+    }
+    store16(vt + static_cast<int64_t>(i) * 16, v);
+  }
+}
+
+// W::template run<HOST_SLOTS>(a, idx, hs) is one of the two element-wise writes above,
+// W::run_tile(a, tok, h0, h1, slot) the matching whole-tile write.
 template <int E>
 struct PlainWrite {
   static constexpr int kEPL = 16 / E;
   template <bool H>
   __device__ static void run(const WriteArgs& a, int64_t idx, const HostSlots& hs) { write_chunk<E, H>(a, idx, hs); }
+  __device__ static void run_tile(const WriteArgs& a, int64_t tok, int32_t h0, int32_t h1, int64_t slot) {
+    write_tile<E>(a, tok, h0, h1, slot);
+  }
 };
 template <typename T, typename C>
 struct QuantWrite {
@@ -131,6 +251,9 @@ struct QuantWrite {
   template <bool H>
   __device__ static void run(const WriteArgs& a, int64_t idx, const HostSlots& hs) {
     write_chunk_quant<T, C, H>(a, idx, hs);
+  }
+  __device__ static void run_tile(const WriteArgs& a, int64_t tok, int32_t h0, int32_t h1, int64_t slot) {
+    write_tile_quant<T, C>(a, tok, h0, h1, slot);
   }
 };
 
@@ -146,14 +269,20 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(WriteArgs a) {
 // dependent-dispatch gap between them.  A host read is a round trip over the
 // host link, so a writing workgroup fetches the slots of its few tokens once
 // (one lane each, system-scope loads) into LDS and its threads read them there.
+// The upload part: workgroups 0..up_blocks-1 copy `words` words from host memory.
+__device__ __forceinline__ void upload_words(uint32_t* __restrict__ dst, const uint32_t* src, int64_t words,
+                                             int32_t up_blocks) {
+  const int64_t stride = static_cast<int64_t>(up_blocks) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < words; i += stride)
+    dst[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 template <typename W>
 __global__ __launch_bounds__(256) void upload_and_cache_kernel(WriteArgs a, uint32_t* __restrict__ dst,
                                                                const uint32_t* src, int64_t words,
                                                                int32_t up_blocks) {
   if (static_cast<int32_t>(blockIdx.x) < up_blocks) {
-    const int64_t stride = static_cast<int64_t>(up_blocks) * blockDim.x;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < words; i += stride)
-      dst[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    upload_words(dst, src, words, up_blocks);
     return;
   }
   __shared__ int32_t slots_lds[256];
@@ -167,6 +296,42 @@ __global__ __launch_bounds__(256) void upload_and_cache_kernel(WriteArgs a, uint
                                                __HIP_MEMORY_SCOPE_SYSTEM);
   __syncthreads();
   W::template run<true>(a, base + threadIdx.x, HostSlots{slots_lds, tok_first});
+}
+
+// The same launch with the whole-tile write (write_tile), for calls in which
+// no two tokens share a block.  Slots come from the kernel arguments when the
+// call has at most kArgSlots tokens: workgroup up_blocks + tok * num_kv_heads
+// + h then writes token tok's tile of KV head h.  Larger calls read each slot
+// from host memory once, and workgroup up_blocks + tok writes all the token's
+// tiles (host reads of one line by many workgroups queue behind each other).
+constexpr int32_t kArgSlots = 256;
+struct ArgSlots {
+  int32_t v[kArgSlots];
+};
+
+template <typename W, bool ARG_SLOTS>
+__global__ __launch_bounds__(256) void upload_and_cache_tiles_kernel(WriteArgs a, uint32_t* __restrict__ dst,
+                                                                     const uint32_t* src, int64_t words,
+                                                                     int32_t up_blocks, ArgSlots arg) {
+  if (static_cast<int32_t>(blockIdx.x) < up_blocks) {
+    upload_words(dst, src, words, up_blocks);
+    return;
+  }
+  const int64_t t = static_cast<int64_t>(blockIdx.x) - up_blocks;
+  if constexpr (ARG_SLOTS) {
+    const int32_t tok = static_cast<int32_t>(t / a.num_kv_heads);
+    const int32_t h = static_cast<int32_t>(t - static_cast<int64_t>(tok) * a.num_kv_heads);
+    const int64_t slot = arg.v[tok];
+    if (slot < 0 || slot >= a.num_slots) return;
+    W::run_tile(a, tok, h, h + 1, slot);
+  } else {
+    __shared__ int32_t slot_lds;
+    if (threadIdx.x == 0) slot_lds = __hip_atomic_load(a.slots + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __syncthreads();
+    const int64_t slot = slot_lds;
+    if (slot < 0 || slot >= a.num_slots) return;
+    W::run_tile(a, t, 0, a.num_kv_heads, slot);
+  }
 }
 
 // Whole-block copy ("PagedAttention 实现细节" §3.3: the full contents of the
@@ -316,14 +481,26 @@ struct UploadAndWriteOp {
   const uint32_t* src;
   int64_t words;
   hipStream_t stream;
+  const int32_t* host_slots;  // non-null: whole-tile write (no two tokens in one block), slots readable here
   template <typename W>
   hipError_t run() const {
     int64_t up = (words + 255) / 256;
     if (up > 64) up = 64;  // the index block is a few KB to a few hundred KB
     if (up < 1) up = 1;
-    const int64_t wr = (chunks + 255) / 256;
-    hipLaunchKernelGGL(upload_and_cache_kernel<W>, dim3(static_cast<uint32_t>(up + wr)), dim3(256), 0, stream, a,
-                       dst, src, words, static_cast<int32_t>(up));
+    if (host_slots && a.num_tokens <= kArgSlots) {
+      ArgSlots arg;
+      for (int32_t i = 0; i < kArgSlots; ++i) arg.v[i] = i < a.num_tokens ? host_slots[i] : -1;
+      const int64_t wr = static_cast<int64_t>(a.num_tokens) * a.num_kv_heads;
+      hipLaunchKernelGGL((upload_and_cache_tiles_kernel<W, true>), dim3(static_cast<uint32_t>(up + wr)), dim3(256),
+                         0, stream, a, dst, src, words, static_cast<int32_t>(up), arg);
+    } else if (host_slots) {
+      hipLaunchKernelGGL((upload_and_cache_tiles_kernel<W, false>), dim3(static_cast<uint32_t>(up + a.num_tokens)),
+                         dim3(256), 0, stream, a, dst, src, words, static_cast<int32_t>(up), ArgSlots{});
+    } else {
+      const int64_t wr = (chunks + 255) / 256;
+      hipLaunchKernelGGL(upload_and_cache_kernel<W>, dim3(static_cast<uint32_t>(up + wr)), dim3(256), 0, stream,
+                         a, dst, src, words, static_cast<int32_t>(up));
+    }
     return hipGetLastError();
   }
 };
@@ -366,15 +543,16 @@ hipError_t launch_upload_and_cache(void* dst, const void* src_device_view, int64
                                    const int32_t* slot_mapping_device_view, int32_t num_tokens,
                                    int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                    pa_dtype dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
-                                   hipStream_t stream) {
+                                   const int32_t* tile_host_slots, hipStream_t stream) {
   const int64_t chunks = write_chunks(num_tokens, num_kv_heads, head_dim, dtype);
   const int64_t words = nbytes / 4;
   if (chunks == 0 && words == 0) return hipSuccess;
+  const int32_t* tiles = num_tokens > 0 ? tile_host_slots : nullptr;
   return by_write(UploadAndWriteOp{write_args(key, value, key_cache, value_cache, slot_mapping_device_view,
                                               num_tokens, num_blocks, num_kv_heads, head_dim, block_size, k_scale,
                                               v_scale),
                                    chunks, static_cast<uint32_t*>(dst), static_cast<const uint32_t*>(src_device_view),
-                                   words, stream},
+                                   words, stream, tiles},
                   dtype, kv_dtype);
 }
 

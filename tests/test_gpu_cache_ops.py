@@ -162,9 +162,15 @@ def test_upload_rejects_pageable_source_without_launching():
 
 @pytest.mark.parametrize("dtype,D,bs,Hkv,fmt", [s + (None,) for s in SHAPES] +
                          [("f16", 128, 16, 8, "fp8_e4m3"), ("bf16", 64, 32, 2, "int8"), ("f32", 128, 16, 4, "fp8_e4m3")])
-def test_upload_and_cache_equals_upload_then_write(dtype, D, bs, Hkv, fmt):
+@pytest.mark.parametrize("form", ["rule", "always"])
+def test_upload_and_cache_equals_upload_then_write(dtype, D, bs, Hkv, fmt, form, monkeypatch):
     """One launch: the index block arrives bit for bit and the write (slots read from the
-    pinned block itself) equals the oracle's write, plain or quantising."""
+    pinned block itself) equals the oracle's write, plain or quantising.  Tokens share blocks
+    here, so even PA_TILE_WRITE=always keeps the element-wise write."""
+    if form == "always":
+        monkeypatch.setenv("PA_TILE_WRITE", "always")
+    else:
+        monkeypatch.delenv("PA_TILE_WRITE", raising=False)
     from oracle import quant as Q  # noqa: F401  (the quantising write's definition)
     NB, T = 13, 37
     rng = np.random.default_rng(11 * D + bs + Hkv)
@@ -206,3 +212,66 @@ def test_upload_and_cache_equals_upload_then_write(dtype, D, bs, Hkv, fmt):
     else:
         ek, ev = C.reshape_and_cache(key, val, kc, vc, ref_slots)
         assert np.array_equal(synth.to_numpy(dk, dtype), ek) and np.array_equal(synth.to_numpy(dv, dtype), ev)
+
+
+_NAN_BITS = {"f32": (np.uint32, 0x7FC0_0123), "f16": (np.uint16, 0x7E05), "bf16": (np.uint16, 0x7FC3)}
+
+
+@pytest.mark.parametrize("dtype,D,bs,Hkv,fmt,T", [s + (None, 17) for s in SHAPES] +
+                         [("f16", 128, 16, 8, "fp8_e4m3", 17), ("bf16", 64, 32, 2, "int8", 17),
+                          ("f32", 128, 32, 4, "fp8_e4m3", 17), ("bf16", 128, 16, 8, "int8", 17),
+                          ("f16", 128, 16, 32, None, 256), ("f16", 128, 32, 32, None, 300),
+                          ("bf16", 128, 32, 8, "int8", 300), ("f32", 64, 16, 3, None, 257)])
+@pytest.mark.parametrize("form", ["always", "rule", "never"])
+def test_upload_and_cache_one_token_per_block(dtype, D, bs, Hkv, fmt, T, form, monkeypatch):
+    """Every token in a block of its own, as in a decode step that appends one token per
+    sequence: the write that stores whole value tiles (slots passed with the launch up to 256
+    tokens, read from host memory per token above), forced (PA_TILE_WRITE=always), by the
+    block-size rule, or off (never).  Bit-exact against the oracle's write;
+    NaN payloads elsewhere in the written tiles come back bit for bit; the first and last
+    column of a block, a skipped slot and a slot past the pool."""
+    NB = T + 6
+    rng = np.random.default_rng(7 * D + bs + Hkv + (3 if fmt else 0))
+    if fmt:
+        kc = synth.normal_codes_host((NB, Hkv, bs, D), 5, fmt)
+        vc = synth.normal_codes_host((NB, Hkv, D, bs), 6, fmt)
+    else:
+        kc = synth.normal_host((NB, Hkv, bs, D), 5, dtype)
+        vc = synth.normal_host((NB, Hkv, D, bs), 6, dtype)
+        ut, bits = _NAN_BITS[dtype]
+        for pool in (kc, vc):                # NaN payloads that a float round trip would not keep
+            pool.reshape(-1).view(ut)[::7] = bits
+    key = synth.normal_host((T, Hkv, D), 7, dtype)
+    val = synth.normal_host((T, Hkv, D), 8, dtype)
+    blocks = rng.choice(NB, size=T, replace=False)
+    offs = rng.integers(0, bs, size=T)
+    offs[0], offs[1] = 0, bs - 1
+    slots = (blocks * bs + offs).astype(np.int32)
+    slots[3] = -1                        # skipped
+    slots[8] = NB * bs + 5               # past the pool: skipped
+    other = rng.integers(-5, 10**6, size=500).astype(np.int32)
+    host = torch.from_numpy(np.concatenate([slots, other])).pin_memory()
+    dst = torch.full((host.numel(),), -1, dtype=torch.int32, device="cuda")
+    if fmt:
+        dk, dv = torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda()
+    else:
+        dk, dv = _dev(kc, dtype), _dev(vc, dtype)
+    ks, vs = (0.02, 0.03) if fmt else (1.0, 1.0)
+    if form == "rule":
+        monkeypatch.delenv("PA_TILE_WRITE", raising=False)
+    else:
+        monkeypatch.setenv("PA_TILE_WRITE", form)
+    pa.pa_upload_and_cache(dst, host, _dev(key, dtype), _dev(val, dtype), dk, dv, host[:T], ks, vs,
+                           kv_format=fmt)
+    torch.cuda.synchronize()
+    assert torch.equal(dst.cpu(), host)
+    ref_slots = slots.copy()
+    ref_slots[8] = -1
+    if fmt:
+        ek, ev = C.reshape_and_cache_quant(key, val, kc, vc, ref_slots, dtype, fmt, ks, vs)
+        assert np.array_equal(dk.cpu().numpy(), ek) and np.array_equal(dv.cpu().numpy(), ev)
+    else:
+        ek, ev = C.reshape_and_cache(key, val, kc, vc, ref_slots)
+        ut = _NAN_BITS[dtype][0]
+        assert np.array_equal(synth.to_numpy(dk, dtype).view(ut), ek.view(ut))
+        assert np.array_equal(synth.to_numpy(dv, dtype).view(ut), ev.view(ut))
