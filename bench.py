@@ -189,7 +189,8 @@ def _counter_per_dispatch(folder: str, counter: str, kernel_substr: str) -> tupl
 
 def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
     # the path that ran (pa_decode_auto takes split on the long-context workload only); the bench
-    # line looks its traffic up under the same name
+    # line looks its traffic up under the same name.  The commands are listed as they were run.
+    asked = path
     path = default_path(workload, path)
     w_path = ("split" if workload == 4 else "single") if path == "auto" else path
     decode = "decode_kernel"
@@ -231,7 +232,7 @@ def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
            f"`{source_digest()}`", "",
            "Commands (run from /tmp with TMPDIR=/tmp; REPO is the repository root, OUTDIR a scratch folder):", "",
            "```"]
-    out += [c.replace(ROOT, "$REPO") for c in profile_commands(workload, "OUTDIR", path)]
+    out += [c.replace(ROOT, "$REPO") for c in profile_commands(workload, "OUTDIR", asked)]
     out += ["```", "", "## Kernel trace (--kernel-trace --stats)", "",
                                                         "| kernel | calls | avg us | min us | max us | % time |",
                                                         "|---|---|---|---|---|---|"]
