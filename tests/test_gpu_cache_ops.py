@@ -275,3 +275,81 @@ def test_upload_and_cache_one_token_per_block(dtype, D, bs, Hkv, fmt, T, form, m
         ut = _NAN_BITS[dtype][0]
         assert np.array_equal(synth.to_numpy(dk, dtype).view(ut), ek.view(ut))
         assert np.array_equal(synth.to_numpy(dv, dtype).view(ut), ev.view(ut))
+
+
+@pytest.mark.parametrize("key", [2, 3, 6, 7])
+def test_upload_and_cache_full_size_step(key):
+    """One decode step at full size as the benchmark runs it: the allocator's append, then the
+    index block and the new K/V in one pa_upload_and_cache launch (the whole-tile write for the
+    32-token-block workloads 3 and 7, element-wise for 2 and 6), then the decode over the
+    uploaded tables, longest first.  Every written block equals the oracle's write into its
+    pre-step contents, every other block is unchanged, and sampled outputs over ctx + 1 match
+    the oracle run on the pre-step blocks plus the oracle's write."""
+    from oracle import attention as A
+    from tests.gpu_helpers import DeviceWorkload, assert_close, out_to_f64, sample_pairs
+    dw = DeviceWorkload(key)
+    w = dw.w
+    S, bs, MB = w.num_seqs, w.block_size, dw.max_blocks
+    slots, pairs = dw.alloc.seq_append_slots(dw.seq_ids)
+    assert (slots, pairs) == dw.ora.seq_append_slots(dw.seq_ids) and not pairs
+    tabs, lens = dw.alloc.build_block_tables(dw.seq_ids, MB)
+    assert (tabs, lens) == dw.ora.build_block_tables(dw.seq_ids, MB)
+    host = torch.from_numpy(np.concatenate([np.array(slots, np.int32), np.array(lens, np.int32),
+                                            np.array(tabs, np.int32).reshape(-1)])).pin_memory()
+    dst = torch.empty(host.numel(), dtype=torch.int32, device="cuda")
+    nk = synth.normal_host((S, w.num_kv_heads, w.head_dim), dw.seeds["new_key"], w.dtype)
+    nv = synth.normal_host((S, w.num_kv_heads, w.head_dim), dw.seeds["new_value"], w.dtype)
+    fmt = w.kv_format or None
+    kc0, vc0 = dw.key_cache.clone(), dw.value_cache.clone()
+    pa.pa_upload_and_cache(dst, host, _dev(nk, w.dtype), _dev(nv, w.dtype), dw.key_cache, dw.value_cache,
+                           host[:S], w.k_scale, w.v_scale, kv_format=fmt)
+    d_lens, d_tabs = dst[S:2 * S], dst[2 * S:].view(S, MB)
+    order = torch.tensor(pa.pa_order_longest_first(lens), dtype=torch.int32, device="cuda")
+    max_ctx = MB * bs
+    if fmt:
+        path = pa.pa_decode_quant(dw.out, dw.query, dw.key_cache, dw.value_cache, d_tabs, d_lens, max_ctx,
+                                  w.scale, w.k_scale, w.v_scale, kv_format=fmt, seq_order=order)
+    else:
+        ws = torch.empty(pa.pa_decode_split_workspace_bytes(S, w.num_heads, w.head_dim, max_ctx, 512),
+                         dtype=torch.uint8, device="cuda")
+        path = pa.pa_decode_auto(dw.out, dw.query, dw.key_cache, dw.value_cache, d_tabs, d_lens, max_ctx,
+                                 w.scale, 512, ws, seq_order=order)
+    torch.cuda.synchronize()
+    assert path == "single"
+    assert torch.equal(dst.cpu(), host)
+
+    def fetch(pool, idx, g=None):
+        t = pool.index_select(0, torch.tensor(idx, dtype=torch.long, device="cuda"))
+        if g is not None:
+            t = t[:, g:g + 1]
+        return t.cpu().numpy() if fmt else synth.to_numpy(t, w.dtype)
+
+    def write(kc, vc, key_rows, val_rows, at):
+        if fmt:
+            return C.reshape_and_cache_quant(key_rows, val_rows, kc, vc, at, w.dtype, fmt, w.k_scale, w.v_scale)
+        return C.reshape_and_cache(key_rows, val_rows, kc, vc, at)
+
+    blocks = [s // bs for s in slots]
+    assert len(set(blocks)) == S                       # one token per block: the step's condition
+    local = np.array([i * bs + s % bs for i, s in enumerate(slots)], dtype=np.int32)
+    ek, ev = write(fetch(kc0, blocks), fetch(vc0, blocks), nk, nv, local)
+    assert np.array_equal(fetch(dw.key_cache, blocks), ek)
+    assert np.array_equal(fetch(dw.value_cache, blocks), ev)
+    rest = torch.ones(w.num_blocks, dtype=torch.bool, device="cuda")
+    rest[torch.tensor(blocks, dtype=torch.long, device="cuda")] = False
+    assert torch.equal(dw.key_cache[rest], kc0[rest]) and torch.equal(dw.value_cache[rest], vc0[rest])
+
+    out = out_to_f64(dw.out, w.dtype)
+    G = w.num_heads // w.num_kv_heads
+    quant = (w.kv_format, w.k_scale, w.v_scale) if fmt else None
+    for s, h in sample_pairs(w, 16, key):
+        n = lens[s]
+        table = tabs[s][:-(-n // bs)]
+        g = h // G
+        kb, vb = fetch(kc0, table, g), fetch(vc0, table, g)
+        at = np.array([table.index(slots[s] // bs) * bs + slots[s] % bs], dtype=np.int32)
+        kb, vb = write(kb, vb, nk[s:s + 1, g:g + 1], nv[s:s + 1, g:g + 1], at)
+        q = synth.to_numpy(dw.query[s, h:h + 1], w.dtype)
+        ref = A.decode_one(q, kb, vb, np.arange(len(table), dtype=np.int32), n, 0, 1, w.scale, w.dtype,
+                           quant=quant)
+        assert_close(out[s, h], ref, w.dtype, f"seq {s} head {h}")
