@@ -782,13 +782,54 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache, c
 
 namespace {
 
-// Partition of a shared prefix in pass 1: an eighth of the longest context,
-// rounded up to 64 tokens (a multiple of every step and block size): at most
-// eight partitions, two workgroups of four waves for the longest prefix.
-int32_t shared_partition(int32_t max_context_len) {
-  const int64_t eighth = (static_cast<int64_t>(max_context_len) + 7) / 8;
-  const int64_t p = (eighth + 63) / 64 * 64;
+// Partition of the longest context into `parts` pieces, rounded up to 64
+// tokens (a multiple of every step and block size).
+int32_t partition_of(int32_t max_context_len, int32_t parts) {
+  const int64_t piece = (static_cast<int64_t>(max_context_len) + parts - 1) / parts;
+  const int64_t p = (piece + 63) / 64 * 64;
   return static_cast<int32_t>(p < 64 ? 64 : p);
+}
+
+// The smallest partition pass 1 of pa_decode_shared uses (kMaxPrior = 8
+// pieces): the workspace is sized for it.
+int32_t shared_partition_min(int32_t max_context_len) { return partition_of(max_context_len, 8); }
+
+// Partition of the shared prefixes in pass 1.  Each unit of the pass (a
+// group and head tile) cuts the longest context into P pieces, one wave
+// each, and the launch packs the waves four to a workgroup across units, so
+// no P leaves a wave idle.  P in 1..8 minimises the estimated time: the
+// rounds of resident workgroups the launch needs, times the tokens of one
+// wave plus 64 for its fixed costs.  On the parallel-sampling workload
+// (1024 units, 768 workgroups resident) that is P = 3, one round; the
+// earlier fixed P = 8 needed 2048 workgroups, and its third round ran two
+// thirds empty.  PA_SHARED_PARTS=1..8 overrides the rule (read on every call).
+int32_t shared_partition(const pa::DecodeArgs& a, int32_t num_groups, int32_t max_group_size) {
+  const char* v = std::getenv("PA_SHARED_PARTS");
+  if (v) {
+    const int forced = std::atoi(v);
+    if (forced >= 1 && forced <= 8) return partition_of(a.max_context_len, forced);
+  }
+  pa::DecodeArgs g = a;
+  g.num_seqs = num_groups;
+  int64_t units = 0, resident = 0;
+  if (launch_shape(g, max_group_size, &units, &resident) != hipSuccess || units <= 0 || resident <= 0) {
+    (void)hipGetLastError();
+    return shared_partition_min(a.max_context_len);
+  }
+  int32_t best = 8;
+  int64_t best_cost = -1;
+  for (int32_t parts = 1; parts <= 8; ++parts) {
+    const int64_t piece = partition_of(a.max_context_len, parts);
+    const int64_t used = (static_cast<int64_t>(a.max_context_len) + piece - 1) / piece;  // pieces with tokens
+    const int64_t workgroups = (units * used + 3) / 4;
+    const int64_t rounds = (workgroups + resident - 1) / resident;
+    const int64_t cost = rounds * (piece + 64);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = parts;
+    }
+  }
+  return partition_of(a.max_context_len, best);
 }
 
 }  // namespace
@@ -796,7 +837,8 @@ int32_t shared_partition(int32_t max_context_len) {
 size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                         int32_t max_context_len) {
   SplitSizes z;
-  if (!split_sizes(num_seqs, num_heads, head_dim, max_context_len, shared_partition(max_context_len), &z)) return 0;
+  if (!split_sizes(num_seqs, num_heads, head_dim, max_context_len, shared_partition_min(max_context_len), &z))
+    return 0;
   return static_cast<size_t>(align256(z.total) + static_cast<int64_t>(num_seqs) * 4);
 }
 
@@ -830,13 +872,17 @@ pa_status pa_decode_shared(void* out, const void* query, const void* key_cache, 
     return fail(PA_ERR_INVALID_ARG, "the groups must partition the sequences: 1 <= num_groups <= num_seqs");
   if (!group_start || !prefix_len) return fail(PA_ERR_INVALID_ARG, "null group_start or prefix_len");
   SplitSizes z;
-  const int32_t part = shared_partition(max_context_len);
-  if (!split_sizes(num_seqs, num_heads, head_dim, max_context_len, part, &z))
+  // the workspace is checked against the size pa_decode_shared_workspace_bytes
+  // returns (the smallest partition), whatever partition this call uses
+  if (!split_sizes(num_seqs, num_heads, head_dim, max_context_len, shared_partition_min(max_context_len), &z))
     return fail(PA_ERR_INVALID_ARG, "workspace sizes");
   const int64_t need = align256(z.total) + static_cast<int64_t>(num_seqs) * 4;
   if (static_cast<int64_t>(workspace_bytes) < need)
     return fail(PA_ERR_WORKSPACE_TOO_SMALL,
                 "need " + std::to_string(need) + " bytes, got " + std::to_string(workspace_bytes));
+  const int32_t part = shared_partition(a, num_groups, max_group_size);
+  if (!split_sizes(num_seqs, num_heads, head_dim, max_context_len, part, &z))
+    return fail(PA_ERR_INVALID_ARG, "workspace sizes");
   pa::SplitLayout ws;
   if ((s = make_layout(workspace, workspace_bytes, num_seqs, num_heads, head_dim, max_context_len, part, &ws)) !=
       PA_OK)

@@ -209,6 +209,7 @@ hipError_t launch_decode_shared(const DecodeArgs& x, const int32_t* group_start,
   p1.ws_o = ws.o;
   p1.part_size = ws.partition_size;
   p1.num_parts = ws.num_parts;
+  p1.flat = 1;  // the partition count need not be a multiple of the waves per workgroup
   p1.ws_len = ws_len;
   hipError_t e = by_dtype(LaunchOp{p1, num_groups, cached, stream}, x.dtype, x.kv_dtype, true, false, x.head_dim,
                           x.block_size, nc);

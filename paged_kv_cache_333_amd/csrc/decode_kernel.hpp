@@ -126,6 +126,12 @@ struct DecodeParams {
   int32_t len_limit;   // largest valid context length
   int32_t part_size;   // split only
   int32_t num_parts;   // split only
+  // Split only, nonzero: a flat launch.  Wave item blockIdx.x * kWaves + wave
+  // is partition item % num_parts of unit item / num_parts (a unit is what
+  // blockIdx.x is otherwise: a (sequence, head group, query chunk)), so a
+  // partition count that kWaves does not divide leaves no wave idle.  Never
+  // with the fused write.
+  int32_t flat;
   float scale_log2;    // scale * k_scale * log2(e)
   float v_scale;       // multiplies the output (8-bit value pools; 1 otherwise)
   // fused slot-mapping write (pa_decode_append): new K/V rows [num_seqs, H_kv, D]
@@ -253,9 +259,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int col_toks = NC >> lg_h;
   const int groups = a.num_heads >> lg_h;
   const int per_slot = groups * a.q_chunks;
-  const int slot = blockIdx.x / per_slot;
-  const int grp = (blockIdx.x - slot * per_slot) / a.q_chunks;
-  const int chunk = blockIdx.x - slot * per_slot - grp * a.q_chunks;
+  int unit = static_cast<int>(blockIdx.x);
+  int flat_part = 0;
+  if constexpr (SPLIT && !APPEND) {
+    if (a.flat) {  // see DecodeParams::flat
+      const int item = static_cast<int>(blockIdx.x) * kWaves + wave;
+      unit = item / a.num_parts;
+      flat_part = item - unit * a.num_parts;
+    }
+  }
+  const int slot = unit / per_slot;
+  if (slot >= a.num_seqs) return;  // a flat launch's last workgroup: waves past the last unit
+  const int grp = (unit - slot * per_slot) / a.q_chunks;
+  const int chunk = unit - slot * per_slot - grp * a.q_chunks;
   const int h0 = grp << lg_h;
   // Workgroups start in blockIdx order; with a longest-first order the long
   // sequences start first and the short ones fill in behind them.
@@ -323,7 +339,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int t_all = bad_len ? 0 : tile_lim_hi;  // the tile's range is [0, t_all)
   int t_begin = 0, t_end = t_all, part = 0;
   if constexpr (SPLIT) {
-    part = blockIdx.y * kWaves + wave;
+    part = !APPEND && a.flat ? flat_part : static_cast<int>(blockIdx.y) * kWaves + wave;
     t_begin = part * a.part_size;
     t_end = min(t_begin + a.part_size, t_end);
     // the merge needs each query row's context length (any head group writes the same)
@@ -831,8 +847,10 @@ struct LaunchOp {
   hipStream_t stream;
   template <typename T, typename S, int D, int BS, int GT, bool SPLIT, bool APPEND>
   hipError_t run() const {
-    const uint32_t gx = static_cast<uint32_t>(num_seqs) * (p.num_heads >> p.col_heads_log2) * p.q_chunks;
-    const uint32_t gy = SPLIT ? static_cast<uint32_t>((p.num_parts + kWaves - 1) / kWaves) : 1u;
+    const int64_t units = static_cast<int64_t>(num_seqs) * (p.num_heads >> p.col_heads_log2) * p.q_chunks;
+    const bool flat = SPLIT && !APPEND && p.flat;
+    const uint32_t gx = static_cast<uint32_t>(flat ? (units * p.num_parts + kWaves - 1) / kWaves : units);
+    const uint32_t gy = SPLIT && !flat ? static_cast<uint32_t>((p.num_parts + kWaves - 1) / kWaves) : 1u;
     if (cached)
       hipLaunchKernelGGL((decode_kernel<T, S, D, BS, GT, SPLIT, true, APPEND>), dim3(gx, gy), dim3(kWaves * 64),
                          0, stream, p);
