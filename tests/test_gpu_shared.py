@@ -193,3 +193,21 @@ def test_group_larger_than_max_group_size_gets_nan_rows():
     ref = oracle(c)
     ok = [s for s in range(c["S"]) if s not in rows]
     assert_close(got[ok], ref[ok], "f16", "the other groups")
+
+
+@pytest.mark.parametrize("parts", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("dt,fmt", [("f16", None), ("bf16", "int8")], ids=lambda v: str(v))
+def test_every_forced_partition_count(parts, dt, fmt, monkeypatch):
+    """The prefix pass's flat launch packs the partition waves of several units into one
+    workgroup: every count 1..8 (PA_SHARED_PARTS) gives the oracle's result, including counts
+    that four waves per workgroup do not divide and the last workgroup's waves past the last
+    unit; and the automatic choice agrees with every forced one within the tolerance."""
+    c = make_case(4242 + parts, dt, fmt, 8, 2, 128, 16)
+    groups = pa.pa_shared_prefix_groups(c["tables"].tolist(), c["ctx"], 16)
+    dv = dev(c)
+    ref = oracle(c)
+    monkeypatch.setenv("PA_SHARED_PARTS", str(parts))
+    got = run_shared(c, dv, groups)
+    assert_close(got, ref, dt, f"{parts} partitions")
+    monkeypatch.delenv("PA_SHARED_PARTS")
+    assert_close(run_shared(c, dv, groups), ref, dt, "automatic partition count")
