@@ -563,11 +563,13 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache, c
                           pa_dtype kv_dtype, uint32_t flags, int32_t partition_size, void* workspace,
                           size_t workspace_bytes, int32_t* path, void* stream);
 
-/* Workspace of pa_decode_shared: the three arrays of
- * pa_decode_split_workspace_bytes for num_seqs rows, with partitions of an
- * eighth of max_context_len rounded up to 64 tokens (at most eight), then one
- * int32 per sequence at the next 256-byte boundary (the prefix length the
- * first pass used).  Returns 0 on an invalid argument. */
+/* Workspace of pa_decode_shared: room for the three arrays of
+ * pa_decode_split_workspace_bytes for num_seqs rows with partitions of an
+ * eighth of max_context_len rounded up to 64 tokens (eight partitions, the
+ * most a call uses), then one int32 per sequence at the next 256-byte
+ * boundary (the prefix length the first pass used).  A call lays the three
+ * arrays out from the start for the partition count it picks (see
+ * pa_decode_shared), at most eight.  Returns 0 on an invalid argument. */
 size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                         int32_t max_context_len);
 
@@ -585,7 +587,11 @@ size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int
  * Two launches: the first reads each group's first P tokens once, with the
  * members' queries as the columns of the q.K tile, into per-member partials;
  * the second decodes each sequence's own tokens P .. n-1 (the prefix's blocks
- * are not read) and merges the two by the log-sum-exp rule.  A member whose
+ * are not read) and merges the two by the log-sum-exp rule.  The first
+ * launch cuts each group's prefix into P partitions of max_context_len / P
+ * (rounded up to 64 tokens), one wave each, P in 1..8 chosen so that the
+ * launch fills whole rounds of the workgroups the device holds at once;
+ * PA_SHARED_PARTS=1..8 (read on every call) forces P.  A member whose
  * prefix_len differs from its group's, and every member of a group larger
  * than max_group_size, get NaN rows; sequences outside every
  * group, or groups that do not share the blocks they claim, give undefined

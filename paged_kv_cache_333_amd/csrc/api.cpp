@@ -876,7 +876,8 @@ pa_status pa_decode_shared(void* out, const void* query, const void* key_cache, 
   // returns (the smallest partition), whatever partition this call uses
   if (!split_sizes(num_seqs, num_heads, head_dim, max_context_len, shared_partition_min(max_context_len), &z))
     return fail(PA_ERR_INVALID_ARG, "workspace sizes");
-  const int64_t need = align256(z.total) + static_cast<int64_t>(num_seqs) * 4;
+  const int64_t len_off = align256(z.total);  // the prefix lengths sit here whatever the partition
+  const int64_t need = len_off + static_cast<int64_t>(num_seqs) * 4;
   if (static_cast<int64_t>(workspace_bytes) < need)
     return fail(PA_ERR_WORKSPACE_TOO_SMALL,
                 "need " + std::to_string(need) + " bytes, got " + std::to_string(workspace_bytes));
@@ -888,7 +889,7 @@ pa_status pa_decode_shared(void* out, const void* query, const void* key_cache, 
       PA_OK)
     return s;
   ws.rows = num_seqs;
-  int32_t* ws_len = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align256(z.total));
+  int32_t* ws_len = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + len_off);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (debug_mode()) {
     if ((s = debug_check_tables(a, st)) != PA_OK) return s;

@@ -96,6 +96,7 @@ def run_shared(c, dv, groups, cached=False):
     max_ctx = c["MB"] * c["bs"]
     ws = torch.empty(pa.pa_decode_shared_workspace_bytes(c["S"], c["H"], c["D"], max_ctx), dtype=torch.uint8,
                      device="cuda")
+    c["ws"] = ws
     out = torch.full_like(dv["q"], 7.0)
     pa.pa_decode_shared(out, dv["q"], dv["kc"], dv["vc"], dv["tab"], dv["ctx"],
                         torch.tensor(gs, dtype=torch.int32, device="cuda"),
@@ -201,7 +202,8 @@ def test_every_forced_partition_count(parts, dt, fmt, monkeypatch):
     """The prefix pass's flat launch packs the partition waves of several units into one
     workgroup: every count 1..8 (PA_SHARED_PARTS) gives the oracle's result, including counts
     that four waves per workgroup do not divide and the last workgroup's waves past the last
-    unit; and the automatic choice agrees with every forced one within the tolerance."""
+    unit; the prefix lengths sit at the documented end of the workspace for every count; and
+    the automatic choice agrees with the oracle too."""
     c = make_case(4242 + parts, dt, fmt, 8, 2, 128, 16)
     groups = pa.pa_shared_prefix_groups(c["tables"].tolist(), c["ctx"], 16)
     dv = dev(c)
@@ -209,5 +211,10 @@ def test_every_forced_partition_count(parts, dt, fmt, monkeypatch):
     monkeypatch.setenv("PA_SHARED_PARTS", str(parts))
     got = run_shared(c, dv, groups)
     assert_close(got, ref, dt, f"{parts} partitions")
+    # the prefix length each sequence's partials cover: one int32 per sequence at the end of
+    # the workspace, wherever this call's partition count put the partials
+    S = c["S"]
+    assert c["ws"].numel() % 4 == 0
+    assert c["ws"][-4 * S:].view(torch.int32).cpu().tolist() == list(groups[1])
     monkeypatch.delenv("PA_SHARED_PARTS")
     assert_close(run_shared(c, dv, groups), ref, dt, "automatic partition count")
