@@ -408,7 +408,7 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* pair
 namespace {
 // Device view of a buffer for a kernel: device memory as it is, page-locked
 // host memory through its mapping.  kind: 0 device, 1 host; -1 if neither.
-int device_view(const void* p, const void** view) {
+static int device_view(const void* p, const void** view) {
   hipPointerAttribute_t at{};
   const bool ok = hipPointerGetAttributes(&at, p) == hipSuccess;
   (void)hipGetLastError();
@@ -784,7 +784,7 @@ namespace {
 
 // Partition of the longest context into `parts` pieces, rounded up to 64
 // tokens (a multiple of every step and block size).
-int32_t partition_of(int32_t max_context_len, int32_t parts) {
+static int32_t partition_of(int32_t max_context_len, int32_t parts) {
   const int64_t piece = (static_cast<int64_t>(max_context_len) + parts - 1) / parts;
   const int64_t p = (piece + 63) / 64 * 64;
   return static_cast<int32_t>(p < 64 ? 64 : p);
@@ -792,7 +792,7 @@ int32_t partition_of(int32_t max_context_len, int32_t parts) {
 
 // The smallest partition pass 1 of pa_decode_shared uses (kMaxPrior = 8
 // pieces): the workspace is sized for it.
-int32_t shared_partition_min(int32_t max_context_len) { return partition_of(max_context_len, 8); }
+static int32_t shared_partition_min(int32_t max_context_len) { return partition_of(max_context_len, 8); }
 
 // Partition of the shared prefixes in pass 1.  Each unit of the pass (a
 // group and head tile) cuts the longest context into P pieces, one wave
@@ -803,7 +803,7 @@ int32_t shared_partition_min(int32_t max_context_len) { return partition_of(max_
 // (1024 units, 768 workgroups resident) that is P = 3, one round; the
 // earlier fixed P = 8 needed 2048 workgroups, and its third round ran two
 // thirds empty.  PA_SHARED_PARTS=1..8 overrides the rule (read on every call).
-int32_t shared_partition(const pa::DecodeArgs& a, int32_t num_groups, int32_t max_group_size) {
+static int32_t shared_partition(const pa::DecodeArgs& a, int32_t num_groups, int32_t max_group_size) {
   const char* v = std::getenv("PA_SHARED_PARTS");
   if (v) {
     const int forced = std::atoi(v);

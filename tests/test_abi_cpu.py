@@ -26,6 +26,21 @@ def test_every_declared_function_is_exported():
     assert sorted(pa.EXPORTED) == names
 
 
+def test_no_undeclared_c_function_is_exported():
+    """Helpers stay internal: every exported function with an unmangled (C) name is one the
+    header declares."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm is not installed")
+    out = subprocess.run([nm, "-D", "--defined-only", pa.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    funcs = {ln.split()[-1] for ln in out.splitlines() if len(ln.split()) == 3 and ln.split()[1] in "TW"}
+    c_names = {f for f in funcs if not f.startswith("_Z")}
+    assert c_names - set(header_functions()) == set()
+
+
 def test_version_and_status_strings():
     assert pa.lib.pa_abi_version() == 5
     for code in range(10):
