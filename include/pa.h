@@ -380,8 +380,10 @@ pa_status pa_upload(void* dst, const void* src, size_t nbytes, void* stream);
  * the call is made.  When no two tokens' slots fall in one block (a decode
  * step appending one token per sequence) and block_size is 32, the write
  * stores each written value tile whole (every cache line of the tile, the
- * other columns unchanged) rather than one element per dim row; the result
- * is the same.  PA_TILE_WRITE=always / never overrides the block-size rule
+ * other columns unchanged) rather than one element per dim row; with
+ * 16-token blocks and model-type pools it stores the elements with
+ * non-temporal stores.  The result is the same.  PA_TILE_WRITE=always /
+ * never overrides the block-size rule
  * (never the one-token-per-block condition).  Errors as in pa_upload and the
  * write it stands for.  Bit-exact. */
 pa_status pa_upload_and_cache(void* dst, const void* src, size_t nbytes, const void* key, const void* value,

@@ -45,7 +45,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // 32-token blocks it shortens the step (GQA bf16 216 -> 200 us, the decode
 // after it running at its clean-cache speed); with 16-token blocks the step
 // is the same either way, the time the shorter write saves reappearing in
-// the decode that follows, so the element-wise form stays there.
+// the decode that follows, so the element-wise form stays there, with
+// non-temporal stores (see put in cache_ops.hip).
 // PA_TILE_WRITE=always / never overrides the rule (read on every call); the
 // whole-tile form is never used when two tokens share a block.
 bool tile_write_wanted(int32_t block_size) {
@@ -515,15 +516,16 @@ pa_status pa_upload_and_cache(void* dst, const void* src, size_t nbytes, const v
       return fail(PA_ERR_INVALID_ARG, "slot_mapping must be page-locked host memory");
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // whole-tile write when every token has a block of its own (a decode step appending one token per sequence)
-  const int32_t* tiles = num_tokens > 0 && tile_write_wanted(block_size) &&
-                                 one_token_per_block(slot_mapping, num_tokens, num_blocks, block_size)
-                             ? slot_mapping
-                             : nullptr;
+  // when every token has a block of its own (a decode step appending one token per sequence): the
+  // whole-tile write, or the element-wise one with non-temporal stores (model-type pools only: the
+  // quantising write's one-byte non-temporal stores made the FP8 step slower, 125 -> 130 us); else
+  // plain element-wise stores
+  const bool own_blocks = num_tokens > 0 && one_token_per_block(slot_mapping, num_tokens, num_blocks, block_size);
+  const int32_t form = !own_blocks ? 0 : tile_write_wanted(block_size) ? 2 : quant ? 0 : 1;
   return finish(pa::launch_upload_and_cache(dst, src_view, static_cast<int64_t>(nbytes), key, value, key_cache,
                                             value_cache, static_cast<const int32_t*>(slots_view), num_tokens,
                                             num_blocks, num_kv_heads, head_dim, block_size, dtype, kv_dtype,
-                                            k_scale, v_scale, tiles, st),
+                                            k_scale, v_scale, form, slot_mapping, st),
                 st, "pa_upload_and_cache");
 }
 

@@ -62,9 +62,10 @@ hipError_t launch_upload_and_cache(void* dst, const void* src_device_view, int64
                                    const int32_t* slot_mapping_device_view, int32_t num_tokens,
                                    int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                    pa_dtype dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
-                                   const int32_t* tile_host_slots, hipStream_t stream);
-// tile_host_slots: NULL, or the host-readable slot mapping of a call in which no two
-// tokens share a block (the write then stores whole value tiles).
+                                   int32_t write_form, const int32_t* host_slots, hipStream_t stream);
+// write_form: 0 element-wise; 1 element-wise with non-temporal stores; 2 whole
+// value tiles (host_slots: the host-readable slot mapping).  Forms 1 and 2
+// need a call in which no two tokens share a block.
 // Whole-block copies between two pools (device views of host pools allowed).
 hipError_t launch_swap_blocks(void* dst_key, void* dst_value, const void* src_key, const void* src_value,
                               const int32_t* pairs, int32_t num_pairs, int32_t num_src_blocks,
