@@ -119,8 +119,8 @@ __device__ __forceinline__ u32x4 with_element(u32x4 v, int e, uint32_t x) {
 // sequence writes has that sequence as its only owner).  A token's value
 // column crosses every cache line of its dim-major value tile, so the
 // element-wise stores above leave each line of the tile partly written, and
-// writing such lines back to HBM slows the kernels that follow far beyond
-// their byte count (a decode right after such a write runs measurably slower
+// the kernel that next reads those lines pays far beyond their byte count
+// (with 32-token blocks, a decode right after such a write ran 16 us slower
 // than after a write of whole lines).  Here one workgroup owns the tiles of
 // KV heads h0..h1-1 of one token: it stores the key rows in 16-byte chunks,
 // reads the value tiles chunk by chunk, puts the new element into the chunk
