@@ -59,6 +59,10 @@ def parse():
                          "share blocks and should run side by side; longest-first otherwise)")
     ap.add_argument("--cache", choices=["stream", "cached"], default=None,
                     help="K/V cache policy (default: cached for workload 5, streaming otherwise)")
+    ap.add_argument("--time-every", type=int, default=4,
+                    help="record the decode's start and end events on every k-th timed step (the first one "
+                         "included); each event recorded on the stream leaves the GPU idle for a few "
+                         "microseconds, so the other steps carry only the one event the staging needs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -371,8 +375,8 @@ class Bench:
             db = torch.empty(total, dtype=torch.int32, device=self.dev)
             # "done": recorded after the step's decode; the step that reuses this buffer waits for it
             # on the host (the decode that read the buffer, and so its upload, has finished).  One
-            # event per step serves both this and, in timed steps, the end of the decode's timing:
-            # every event recorded on the stream adds a few microseconds between kernels.
+            # event per step serves both this and, in the steps that time the decode, the end of
+            # its timing: every event recorded on the stream adds a few microseconds between kernels.
             b = {"idx_h": hb, "idx_d": db, "done": torch.cuda.Event()}
             for side, t in (("h", hb), ("d", db)):
                 b["slots_" + side] = t[0:NS]
@@ -388,7 +392,7 @@ class Bench:
         self.kv_elem = 1 if self.quant else self.elem
         torch.cuda.synchronize()
 
-    def step(self, k: int, timing: list | None):
+    def step(self, k: int, timing: list | None, instrument: bool = False):
         pa, w = self.pa, self.w
         b = self.bufs[k % 2]
         b["done"].synchronize()  # the step that last used this buffer is done, its upload included
@@ -428,7 +432,7 @@ class Bench:
                                           w.v_scale, kv_format=w.kv_format)
         elif not fused:
             pa.pa_reshape_and_cache(self.newk[r], self.newv[r], self.kc, self.vc, b["slots_d"])
-        if timing is not None:
+        if instrument:
             e0, e1 = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
             e0.record(self.stream)
         if self.L > 1:
@@ -464,14 +468,16 @@ class Bench:
             self.path_ran.add(pa.pa_decode_auto(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"],
                                                 self.max_ctx, w.scale, self.args.partition, self.ws,
                                                 seq_order=order, cached_kv=self.cached))
-        if timing is None:
-            b["done"] = self.torch.cuda.Event()  # a fresh one: a timing event may sit here
-            b["done"].record(self.stream)
-        else:
+        if instrument:
             e1.record(self.stream)
             b["done"] = e1
+        else:
+            b["done"] = self.torch.cuda.Event()  # a fresh one: a timing event may sit here
+            b["done"].record(self.stream)
+        if timing is not None:
             lens = b["len_h"].numpy()
-            timing.append((e0, e1, int(lens.sum()), int(((lens + w.block_size - 1) // w.block_size).sum()), npairs))
+            timing.append((e0 if instrument else None, e1 if instrument else None, int(lens.sum()),
+                           int(((lens + w.block_size - 1) // w.block_size).sum()), npairs))
 
     def run(self):
         torch = self.torch
@@ -481,8 +487,9 @@ class Bench:
         torch.cuda.synchronize()
         timing = []
         t0 = time.perf_counter()
+        every = max(1, a.time_every)
         for k in range(a.warmup, a.warmup + a.steps):
-            self.step(k, timing)
+            self.step(k, timing, instrument=(k - a.warmup) % every == 0)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         return wall, timing
@@ -557,13 +564,14 @@ def main():
     wall, timing = bench.run()
     w = bench.w
     e = bench.elem
-    durs = [a.elapsed_time(b) * 1e-3 for a, b, *_ in timing]  # seconds
+    timed = [t for t in timing if t[0] is not None]  # the steps with decode events
+    durs = [a.elapsed_time(b) * 1e-3 for a, b, *_ in timed]  # seconds
     kv_tokens = sum(t[2] for t in timing)
     kv_bytes_token = 2 * w.num_kv_heads * w.head_dim * bench.kv_elem
     qo_bytes = 2 * w.num_seqs * w.query_len * w.num_heads * w.head_dim * e
     # the fused call also reads the step's new K/V rows and writes them into the pools
     fused_write = 2 * w.num_seqs * kv_bytes_token if (bench.path == "auto" and args.fused_write) else 0
-    alg_bytes = [t[2] * kv_bytes_token + qo_bytes + 4 * t[3] + 4 * w.num_seqs + fused_write for t in timing]
+    alg_bytes = [t[2] * kv_bytes_token + qo_bytes + 4 * t[3] + 4 * w.num_seqs + fused_write for t in timed]
     avg_dur = sum(durs) / len(durs)
     avg_bytes = sum(alg_bytes) / len(alg_bytes)
     achieved = avg_bytes / avg_dur / 1e9
@@ -596,6 +604,7 @@ def main():
                    "launch_order": bench.order, "kv_cache_policy": "cached" if bench.cached else "stream",
                    "cow_pairs_per_step": sum(t[4] for t in timing) / len(timing)},
         "decode_kernel_us": avg_dur * 1e6,
+        "decode_timed_steps": len(timed),
         "kv_gbps_step": kv_tokens * kv_bytes_token / wall / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS,
