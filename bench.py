@@ -36,6 +36,13 @@ DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_333_amd", "csrc", "decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 
+STAGING_BUFFERS = 8  # rotating pinned staging buffers of the step's index data
+EVENT_EVERY = 4      # a stream event after the decode of every 4th step (see Bench.__init__)
+# the window [k - STAGING_BUFFERS, k - 2] holds STAGING_BUFFERS - 1 consecutive steps, so it holds
+# an event step whenever EVENT_EVERY <= STAGING_BUFFERS - 1
+assert EVENT_EVERY <= STAGING_BUFFERS - 1
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -362,22 +369,25 @@ class Bench:
                       pa.pa_decode_split_workspace_bytes(S, H, D, self.max_ctx, args.partition))
             self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.dev)
 
-        # double-buffered index data, one pinned staging buffer and one upload (pa_upload, a
-        # kernel on the compute stream) per step:
+        # index data in STAGING_BUFFERS rotating pinned staging buffers, one upload (a kernel on the
+        # compute stream) per step:
         # [slots LS | lens S | order S | pairs 2LS | tables S*MB | group_start S+1 | prefix_len S]
         # int32 (L new tokens per sequence; the last two for the shared-prefix path)
         self.ids = torch.arange(S, dtype=torch.int64).repeat(L).pin_memory()
         self.bufs = []
         tab_end = 3 * NS + 2 * S + S * self.max_blocks
         total = tab_end + 2 * S + 1
-        for _ in range(2):
+        # A step reusing a buffer must know that the step which last used it has finished.  Every
+        # event recorded on the stream leaves the GPU idle for a few microseconds, so events are
+        # recorded after the decode of every EVENT_EVERY-th step (and of the steps that time the
+        # decode, whose end event serves), and step k waits on the host for the latest event
+        # recorded at a step in [k - STAGING_BUFFERS, k - 2]: one exists, every step before it
+        # has finished, and the GPU still has step k - 1 queued while the host prepares step k.
+        self.events = {}
+        for _ in range(STAGING_BUFFERS):
             hb = torch.empty(total, dtype=torch.int32).pin_memory()
             db = torch.empty(total, dtype=torch.int32, device=self.dev)
-            # "done": recorded after the step's decode; the step that reuses this buffer waits for it
-            # on the host (the decode that read the buffer, and so its upload, has finished).  One
-            # event per step serves both this and, in the steps that time the decode, the end of
-            # its timing: every event recorded on the stream adds a few microseconds between kernels.
-            b = {"idx_h": hb, "idx_d": db, "done": torch.cuda.Event()}
+            b = {"idx_h": hb, "idx_d": db}
             for side, t in (("h", hb), ("d", db)):
                 b["slots_" + side] = t[0:NS]
                 b["len_" + side] = t[NS:NS + S]
@@ -386,7 +396,6 @@ class Bench:
                 b["tab_" + side] = t[3 * NS + 2 * S:tab_end].view(S, self.max_blocks)
                 b["gs_" + side] = t[tab_end:tab_end + S + 1]
                 b["pl_" + side] = t[tab_end + S + 1:]
-            b["done"].record(self.stream)
             self.bufs.append(b)
         self.elem = synth.ELEM_BYTES[w.dtype]
         self.kv_elem = 1 if self.quant else self.elem
@@ -394,8 +403,10 @@ class Bench:
 
     def step(self, k: int, timing: list | None, instrument: bool = False):
         pa, w = self.pa, self.w
-        b = self.bufs[k % 2]
-        b["done"].synchronize()  # the step that last used this buffer is done, its upload included
+        b = self.bufs[k % STAGING_BUFFERS]
+        if k >= STAGING_BUFFERS:  # the step that last used this buffer is done, its upload included
+            last = max(j for j in self.events if k - STAGING_BUFFERS <= j <= k - 2)
+            self.events[last].synchronize()
         alloc = self.alloc
         if self.base is not None:
             alloc = self.alloc = self.base.clone()
@@ -470,10 +481,12 @@ class Bench:
                                                 seq_order=order, cached_kv=self.cached))
         if instrument:
             e1.record(self.stream)
-            b["done"] = e1
-        else:
-            b["done"] = self.torch.cuda.Event()  # a fresh one: a timing event may sit here
-            b["done"].record(self.stream)
+            self.events[k] = e1
+        elif k % EVENT_EVERY == 0:
+            self.events[k] = self.torch.cuda.Event()
+            self.events[k].record(self.stream)
+        for j in [j for j in self.events if j < k - STAGING_BUFFERS]:
+            del self.events[j]
         if timing is not None:
             lens = b["len_h"].numpy()
             timing.append((e0 if instrument else None, e1 if instrument else None, int(lens.sum()),
@@ -502,7 +515,7 @@ class Bench:
 
         from oracle import attention as A
         torch, synth, w = self.torch, self.synth, self.w
-        b = self.bufs[(self.args.warmup + self.args.steps - 1) % 2]
+        b = self.bufs[(self.args.warmup + self.args.steps - 1) % STAGING_BUFFERS]
         lens = b["len_h"].numpy().copy()
         tabs = b["tab_h"].numpy().copy()
         # copy just the used blocks back, renumbered 0..n-1 (a plain re-indexing of the inputs)
