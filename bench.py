@@ -67,9 +67,8 @@ def parse():
     ap.add_argument("--cache", choices=["stream", "cached"], default=None,
                     help="K/V cache policy (default: cached for workload 5, streaming otherwise)")
     ap.add_argument("--time-every", type=int, default=4,
-                    help="record the decode's start and end events on every k-th timed step (the first one "
-                         "included); each event recorded on the stream leaves the GPU idle for a few "
-                         "microseconds, so the other steps carry only the one event the staging needs")
+                    help="time the decode on every k-th timed step (the first one included), by start and "
+                         "end events that ride on the decode's own kernels (pa_set_launch_events)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -378,11 +377,11 @@ class Bench:
         tab_end = 3 * NS + 2 * S + S * self.max_blocks
         total = tab_end + 2 * S + 1
         # A step reusing a buffer must know that the step which last used it has finished.  Every
-        # event recorded on the stream leaves the GPU idle for a few microseconds, so events are
-        # recorded after the decode of every EVENT_EVERY-th step (and of the steps that time the
-        # decode, whose end event serves), and step k waits on the host for the latest event
-        # recorded at a step in [k - STAGING_BUFFERS, k - 2]: one exists, every step before it
-        # has finished, and the GPU still has step k - 1 queued while the host prepares step k.
+        # event recorded on the stream as a marker leaves the GPU idle for a few microseconds, so
+        # one is recorded after the decode of every EVENT_EVERY-th step only, and step k waits on
+        # the host for the latest one recorded at a step in [k - STAGING_BUFFERS, k - 2]: one
+        # exists, every step before it has finished, and the GPU still has step k - 1 queued
+        # while the host prepares step k.
         self.events = {}
         for _ in range(STAGING_BUFFERS):
             hb = torch.empty(total, dtype=torch.int32).pin_memory()
@@ -397,6 +396,14 @@ class Bench:
                 b["gs_" + side] = t[tab_end:tab_end + S + 1]
                 b["pl_" + side] = t[tab_end + S + 1:]
             self.bufs.append(b)
+        # event pairs for the steps that time the decode, recorded once here so that they exist
+        # (pa_set_launch_events hands them to the decode's kernels)
+        self.timing_events = []
+        for _ in range(-(-args.steps // max(1, args.time_every))):
+            pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for ev in pair:
+                ev.record(self.stream)
+            self.timing_events.append(pair)
         self.elem = synth.ELEM_BYTES[w.dtype]
         self.kv_elem = 1 if self.quant else self.elem
         torch.cuda.synchronize()
@@ -444,8 +451,9 @@ class Bench:
         elif not fused:
             pa.pa_reshape_and_cache(self.newk[r], self.newv[r], self.kc, self.vc, b["slots_d"])
         if instrument:
-            e0, e1 = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
-            e0.record(self.stream)
+            # the decode's own kernels record these (no marker packet before or after the decode)
+            e0, e1 = self.timing_events.pop()
+            pa.pa_set_launch_events(e0, e1)
         if self.L > 1:
             self.path_ran.add(pa.pa_decode_multi(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"],
                                                  self.qstart, self.L, self.max_ctx, w.scale,
@@ -479,10 +487,7 @@ class Bench:
             self.path_ran.add(pa.pa_decode_auto(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"],
                                                 self.max_ctx, w.scale, self.args.partition, self.ws,
                                                 seq_order=order, cached_kv=self.cached))
-        if instrument:
-            e1.record(self.stream)
-            self.events[k] = e1
-        elif k % EVENT_EVERY == 0:
+        if k % EVENT_EVERY == 0:
             self.events[k] = self.torch.cuda.Event()
             self.events[k].record(self.stream)
         for j in [j for j in self.events if j < k - STAGING_BUFFERS]:

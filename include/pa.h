@@ -391,6 +391,20 @@ pa_status pa_upload_and_cache(void* dst, const void* src, size_t nbytes, const v
                               int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                               float k_scale, float v_scale, pa_dtype dtype, pa_dtype kv_dtype, void* stream);
 
+/* Measurement hook.  The next call of this library made on the calling
+ * thread attaches start_event to the start of its first kernel and
+ * stop_event to the end of its last (hipExtLaunchKernel: the events ride on
+ * the kernels' own dispatches, so no marker packet sits between kernels;
+ * each such packet leaves the GPU idle for microseconds).  The decode calls
+ * (pa_decode, pa_decode_split, pa_decode_auto, pa_decode_append,
+ * pa_decode_quant, pa_decode_masked, pa_decode_multi, pa_decode_shared,
+ * pa_lse_reduce) time their kernels; a call that reaches its launch clears
+ * the setting whatever it is, and a call rejected before launching leaves it
+ * set.  The events are hipEvent_t the caller created with timing enabled;
+ * either may be NULL.  Read them with hipEventElapsedTime once the stream has
+ * passed the call.  Always PA_OK. */
+pa_status pa_set_launch_events(void* start_event, void* stop_event);
+
 /* Single-pass paged decode attention ([IMPL] §3.1 index-based kernel and
  * §3.4 PagedAttention.forward; [ATB] §3.2 PagedAttentionOperation.apply;
  * [ASC] §三/§四 fused gather + QK^T + softmax + OV):

@@ -101,6 +101,7 @@ _PROTOS = {
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_order_longest_first": (_i32, [_pi32, _i32, _pi32]),
     "pa_upload": (_i32, [_vp, _vp, _sz, _vp]),
+    "pa_set_launch_events": (_i32, [_vp, _vp]),
     "pa_upload_and_cache": (_i32, [_vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
                                    _f32, _i32, _i32, _vp]),
     "pa_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
@@ -268,6 +269,21 @@ def pa_swap_blocks(dst_key_cache, dst_value_cache, src_key_cache, src_value_cach
     _check(lib.pa_swap_blocks(_ptr(dst_key_cache), _ptr(dst_value_cache), _ptr(src_key_cache),
                               _ptr(src_value_cache), _ptr(pairs), P, NB_s, NB_d, H_kv, D, bs, code,
                               _stream(stream)), "pa_swap_blocks")
+
+
+def pa_set_launch_events(start_event, stop_event):
+    """Time the next decode call on this thread by events riding on its kernels' own dispatches
+    (no marker packet between kernels): start_event records the start of its first kernel,
+    stop_event the end of its last.  Events are torch.cuda.Event(enable_timing=True) objects that
+    have been recorded once (so that they exist), or None."""
+    def raw(ev):
+        if ev is None:
+            return None
+        h = ev.cuda_event
+        if not h:
+            raise ValueError("pa_set_launch_events: record the event once first, so that it exists")
+        return h
+    _check(lib.pa_set_launch_events(raw(start_event), raw(stop_event)), "pa_set_launch_events")
 
 
 def pa_upload(dst, src, stream=None):

@@ -14,6 +14,13 @@
 #include "launch.hpp"
 #include "status.hpp"
 
+namespace pa {
+LaunchEvents& launch_events() {
+  thread_local LaunchEvents ev{nullptr, nullptr};
+  return ev;
+}
+}  // namespace pa
+
 namespace {
 
 using pa::fail;
@@ -96,6 +103,7 @@ pa_status check_shape(pa_dtype dt, int32_t head_dim, int32_t block_size) {
 // After a launch: report launch errors; in debug mode also wait and report
 // execution errors.
 pa_status finish(hipError_t launch, hipStream_t st, const char* what) {
+  pa::launch_events() = pa::LaunchEvents{nullptr, nullptr};  // they applied to this call only
   if (launch != hipSuccess) return hip_fail(launch, what);
   if (debug_mode()) {
     hipError_t e = hipStreamSynchronize(st);
@@ -327,6 +335,11 @@ pa::DecodeArgs pack(void* out, const void* query, const void* key_cache, const v
 }  // namespace
 
 extern "C" {
+
+pa_status pa_set_launch_events(void* start_event, void* stop_event) {
+  pa::launch_events() = pa::LaunchEvents{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+  return PA_OK;
+}
 
 pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
                                const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,

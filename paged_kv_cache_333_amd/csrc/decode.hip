@@ -258,7 +258,7 @@ hipError_t launch_lse_reduce(void* out, const SplitLayout& ws, const int32_t* ct
                              pa_dtype dt, hipStream_t stream) {
   const dim3 grid(static_cast<uint32_t>(num_seqs) * num_heads, static_cast<uint32_t>(head_dim / 32));
 #define PA_REDUCE(T, D)                                                                          \
-  hipLaunchKernelGGL((lse_reduce_kernel<T, D>), grid, dim3(256), 0, stream, out, ws.m, ws.l, ws.o, \
+  launch_kernel(lse_reduce_kernel<T, D>, grid, dim3(256), stream, out, ws.m, ws.l, ws.o, \
                      ctx, order, num_seqs, num_heads, len_limit, ws.partition_size, ws.num_parts)
   if (head_dim == 64) {
     if (dt == PA_F32) PA_REDUCE(TF32, 64);

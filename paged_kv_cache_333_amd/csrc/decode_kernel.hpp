@@ -852,11 +852,10 @@ struct LaunchOp {
     const uint32_t gx = static_cast<uint32_t>(flat ? (units * p.num_parts + kWaves - 1) / kWaves : units);
     const uint32_t gy = SPLIT && !flat ? static_cast<uint32_t>((p.num_parts + kWaves - 1) / kWaves) : 1u;
     if (cached)
-      hipLaunchKernelGGL((decode_kernel<T, S, D, BS, GT, SPLIT, true, APPEND>), dim3(gx, gy), dim3(kWaves * 64),
-                         0, stream, p);
+      launch_kernel(decode_kernel<T, S, D, BS, GT, SPLIT, true, APPEND>, dim3(gx, gy), dim3(kWaves * 64), stream, p);
     else
-      hipLaunchKernelGGL((decode_kernel<T, S, D, BS, GT, SPLIT, false, APPEND>), dim3(gx, gy),
-                         dim3(kWaves * 64), 0, stream, p);
+      launch_kernel(decode_kernel<T, S, D, BS, GT, SPLIT, false, APPEND>, dim3(gx, gy), dim3(kWaves * 64), stream,
+                    p);
     return hipGetLastError();
   }
 };

@@ -2,12 +2,36 @@
 // launchers.  Arguments reaching these functions have been validated.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "pa.h"
 
 namespace pa {
+
+// Measurement hook (pa_set_launch_events): events to attach to the kernels of
+// the next library call made on this thread.  launch_kernel takes them: the
+// first kernel of the call records `start` when it starts, and every kernel
+// records `stop` when it ends, so the last one's end remains.  The events ride
+// on the kernels' own dispatches (hipExtLaunchKernel): no marker packet sits
+// between kernels.  The call's finish clears them.
+struct LaunchEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+LaunchEvents& launch_events();  // this thread's
+
+template <typename F, typename... Args>
+void launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+  LaunchEvents& ev = launch_events();
+  if (ev.start || ev.stop) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0, args...);
+    ev.start = nullptr;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+  }
+}
 
 struct DecodeArgs {
   void* out;

@@ -450,3 +450,43 @@ def test_pa_split_environment_override(monkeypatch):
         assert pa.pa_decode_auto(out, dv["q"], dv["kc"], dv["vc"], dv["tables"], dv["ctx"], max_ctx,
                                  scale_for(128), 64, None) == "single"
     monkeypatch.delenv("PA_SPLIT")
+
+
+def test_launch_events_time_one_decode_call_and_change_nothing():
+    """pa_set_launch_events: events riding on the decode's own kernels time exactly the next call
+    (the single pass; the split partials and their merge as one window), the output is
+    bit-identical to an untimed call, and the call after it is not timed."""
+    dw = DeviceWorkload(2)
+    w = dw.w
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()                                   # the events exist from here on
+    plain = torch.empty_like(dw.out)
+    pa.pa_decode(plain, dw.query, dw.key_cache, dw.value_cache, dw.tables, dw.context_lens,
+                 dw.max_context_len, w.scale)
+    pa.pa_set_launch_events(e0, e1)
+    pa.pa_decode(dw.out, dw.query, dw.key_cache, dw.value_cache, dw.tables, dw.context_lens,
+                 dw.max_context_len, w.scale)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1)
+    assert 0.01 < t < 50.0, t
+    assert torch.equal(dw.out, plain)
+    again = torch.empty_like(dw.out)
+    pa.pa_decode(again, dw.query, dw.key_cache, dw.value_cache, dw.tables, dw.context_lens,
+                 dw.max_context_len, w.scale)
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) == t              # not re-recorded: the setting applied to one call
+    ws = torch.empty(pa.pa_decode_split_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim,
+                                                        dw.max_context_len, 512), dtype=torch.uint8, device="cuda")
+    split = torch.empty_like(dw.out)
+    pa.pa_set_launch_events(e0, e1)
+    pa.pa_decode_split(split, dw.query, dw.key_cache, dw.value_cache, dw.tables, dw.context_lens,
+                       dw.max_context_len, w.scale, 512, ws)
+    torch.cuda.synchronize()
+    t_split = e0.elapsed_time(e1)
+    assert t_split != t and 0.01 < t_split < 50.0
+    untimed = torch.empty_like(dw.out)
+    pa.pa_decode_split(untimed, dw.query, dw.key_cache, dw.value_cache, dw.tables, dw.context_lens,
+                       dw.max_context_len, w.scale, 512, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(split, untimed)
