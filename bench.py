@@ -38,6 +38,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 STAGING_BUFFERS = 8  # rotating pinned staging buffers of the step's index data
 EVENT_EVERY = 4      # a stream event after the decode of every 4th step (see Bench.__init__)
+TIMING_PAIRS = 4     # event sets reused round robin by the steps that time the decode
 # the window [k - STAGING_BUFFERS, k - 2] holds STAGING_BUFFERS - 1 consecutive steps, so it holds
 # an event step whenever EVENT_EVERY <= STAGING_BUFFERS - 1
 assert EVENT_EVERY <= STAGING_BUFFERS - 1
@@ -396,14 +397,18 @@ class Bench:
                 b["gs_" + side] = t[tab_end:tab_end + S + 1]
                 b["pl_" + side] = t[tab_end + S + 1:]
             self.bufs.append(b)
-        # event pairs for the steps that time the decode, recorded once here so that they exist
-        # (pa_set_launch_events hands them to the decode's kernels)
-        self.timing_events = []
-        for _ in range(-(-args.steps // max(1, args.time_every))):
-            pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for ev in pair:
+        # a few event sets for the steps that time the decode, recorded once here so that they
+        # exist (pa_set_launch_events hands them to the kernels) and reused round robin: an
+        # event's first use in a launch costs the host far more than later ones.  A set's result
+        # is read before its next use, many steps later, when that step has long finished.
+        self.timing_pool = []
+        for _ in range(TIMING_PAIRS):
+            trio = tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+            for ev in trio:
                 ev.record(self.stream)
-            self.timing_events.append(pair)
+            self.timing_pool.append(trio)
+        self.pool_next = 0
+        self.pool_owner = [None] * TIMING_PAIRS  # the timing entry each pair's pending result goes to
         self.elem = synth.ELEM_BYTES[w.dtype]
         self.kv_elem = 1 if self.quant else self.elem
         torch.cuda.synchronize()
@@ -432,28 +437,44 @@ class Bench:
             pa.pa_order_longest_first_into(b["len_h"].data_ptr(), S, b["order_h"].data_ptr())
             order = b["order_d"]
         r = k % self.newk.shape[0]
+        if instrument:
+            # The decode's time, by events that ride on the kernels' own dispatches (no marker packet
+            # sits in the step): the end of its last kernel (e_end) minus the later of two starts,
+            # the end of the last kernel before it (each call below records e_prev at its end; the
+            # last one stays) and the processing of the decode's own first dispatch (e_start).  Both
+            # precede the decode's first wave, e_prev by stream order.  When the decode was queued
+            # behind the previous kernel, e_start comes early and e_prev is the closer bound; when
+            # the host enqueued it late (a host-bound step), e_start is.
+            slot = self.pool_next % TIMING_PAIRS
+            self.pool_next += 1
+            self._resolve(slot)
+            e_prev, e_start, e_end = self.timing_pool[slot]
+        mark = (lambda: pa.pa_set_launch_events(None, e_prev)) if instrument else (lambda: None)
         fused = self.path == "auto" and self.args.fused_write
         # One launch for the upload and the K/V write when no copy-on-write pair must come
         # between them (the write may land in a block the copy fills).
         one_launch = not npairs and not fused and not self.args.separate_upload
         if one_launch:
+            mark()
             pa.pa_upload_and_cache(b["idx_d"], b["idx_h"], self.newk[r], self.newv[r], self.kc, self.vc,
                                    b["slots_h"], w.k_scale, w.v_scale, kv_format=w.kv_format or None)
         else:
+            mark()
             pa.pa_upload(b["idx_d"], b["idx_h"])
         if npairs:
+            mark()
             pa.pa_copy_blocks(self.kc, self.vc, b["pairs_d"], num_pairs=npairs)
         if one_launch:
             pass
         elif self.quant:
+            mark()
             pa.pa_reshape_and_cache_quant(self.newk[r], self.newv[r], self.kc, self.vc, b["slots_d"], w.k_scale,
                                           w.v_scale, kv_format=w.kv_format)
         elif not fused:
+            mark()
             pa.pa_reshape_and_cache(self.newk[r], self.newv[r], self.kc, self.vc, b["slots_d"])
         if instrument:
-            # the decode's own kernels record these (no marker packet before or after the decode)
-            e0, e1 = self.timing_events.pop()
-            pa.pa_set_launch_events(e0, e1)
+            pa.pa_set_launch_events(e_start, e_end)
         if self.L > 1:
             self.path_ran.add(pa.pa_decode_multi(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"],
                                                  self.qstart, self.L, self.max_ctx, w.scale,
@@ -492,24 +513,39 @@ class Bench:
             self.events[k].record(self.stream)
         for j in [j for j in self.events if j < k - STAGING_BUFFERS]:
             del self.events[j]
+        entry = None
         if timing is not None:
             lens = b["len_h"].numpy()
-            timing.append((e0 if instrument else None, e1 if instrument else None, int(lens.sum()),
-                           int(((lens + w.block_size - 1) // w.block_size).sum()), npairs))
+            entry = [None, int(lens.sum()), int(((lens + w.block_size - 1) // w.block_size).sum()), npairs]
+            timing.append(entry)
+        if instrument:
+            self.pool_owner[slot] = entry  # None for a warm-up step: its result is dropped
+
+    def _resolve(self, slot: int):
+        """Store the decode time (ms) of the step that last used event pair `slot`."""
+        entry = self.pool_owner[slot]
+        if entry is not None:
+            prev_end, start, end = self.timing_pool[slot]
+            end.synchronize()
+            # two windows that each hold the whole decode; the smaller is the closer bound
+            entry[0] = min(prev_end.elapsed_time(end), start.elapsed_time(end))
+        self.pool_owner[slot] = None
 
     def run(self):
         torch = self.torch
         a = self.args
-        for k in range(a.warmup):
-            self.step(k, None)
+        every = max(1, a.time_every)
+        for k in range(a.warmup):  # the warm-up steps take every event pair into use
+            self.step(k, None, instrument=True)
         torch.cuda.synchronize()
         timing = []
         t0 = time.perf_counter()
-        every = max(1, a.time_every)
         for k in range(a.warmup, a.warmup + a.steps):
             self.step(k, timing, instrument=(k - a.warmup) % every == 0)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        for slot in range(TIMING_PAIRS):
+            self._resolve(slot)
         return wall, timing
 
     def cpu_baseline(self, min_seconds: float):
@@ -582,14 +618,14 @@ def main():
     wall, timing = bench.run()
     w = bench.w
     e = bench.elem
-    timed = [t for t in timing if t[0] is not None]  # the steps with decode events
-    durs = [a.elapsed_time(b) * 1e-3 for a, b, *_ in timed]  # seconds
-    kv_tokens = sum(t[2] for t in timing)
+    timed = [t for t in timing if t[0] is not None]  # the steps whose decode was timed
+    durs = [t[0] * 1e-3 for t in timed]  # seconds
+    kv_tokens = sum(t[1] for t in timing)
     kv_bytes_token = 2 * w.num_kv_heads * w.head_dim * bench.kv_elem
     qo_bytes = 2 * w.num_seqs * w.query_len * w.num_heads * w.head_dim * e
     # the fused call also reads the step's new K/V rows and writes them into the pools
     fused_write = 2 * w.num_seqs * kv_bytes_token if (bench.path == "auto" and args.fused_write) else 0
-    alg_bytes = [t[2] * kv_bytes_token + qo_bytes + 4 * t[3] + 4 * w.num_seqs + fused_write for t in timed]
+    alg_bytes = [t[1] * kv_bytes_token + qo_bytes + 4 * t[2] + 4 * w.num_seqs + fused_write for t in timed]
     avg_dur = sum(durs) / len(durs)
     avg_bytes = sum(alg_bytes) / len(alg_bytes)
     achieved = avg_bytes / avg_dur / 1e9
@@ -620,7 +656,7 @@ def main():
                          if not args.separate_upload else "pa_upload, then the write (two launches)"),
                    "partition_size": args.partition if "split" in bench.path_ran else None,
                    "launch_order": bench.order, "kv_cache_policy": "cached" if bench.cached else "stream",
-                   "cow_pairs_per_step": sum(t[4] for t in timing) / len(timing)},
+                   "cow_pairs_per_step": sum(t[3] for t in timing) / len(timing)},
         "decode_kernel_us": avg_dur * 1e6,
         "decode_timed_steps": len(timed),
         "kv_gbps_step": kv_tokens * kv_bytes_token / wall / 1e9,

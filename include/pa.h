@@ -395,14 +395,16 @@ pa_status pa_upload_and_cache(void* dst, const void* src, size_t nbytes, const v
  * thread attaches start_event to the start of its first kernel and
  * stop_event to the end of its last (hipExtLaunchKernel: the events ride on
  * the kernels' own dispatches, so no marker packet sits between kernels;
- * each such packet leaves the GPU idle for microseconds).  The decode calls
- * (pa_decode, pa_decode_split, pa_decode_auto, pa_decode_append,
- * pa_decode_quant, pa_decode_masked, pa_decode_multi, pa_decode_shared,
- * pa_lse_reduce) time their kernels; a call that reaches its launch clears
- * the setting whatever it is, and a call rejected before launching leaves it
- * set.  The events are hipEvent_t the caller created with timing enabled;
- * either may be NULL.  Read them with hipEventElapsedTime once the stream has
- * passed the call.  Always PA_OK. */
+ * each such packet leaves the GPU idle for microseconds).  Every device call
+ * of the library times its kernels this way.  A call that reaches its launch
+ * clears the setting, and a call rejected before launching leaves it set.
+ * The start event is taken when the first kernel's dispatch is processed,
+ * which can be before the previous kernel on the stream has finished; the
+ * end of the previous call's last kernel (its stop_event) marks the start of
+ * a call exactly, since no packet sits between the two.  The events are
+ * hipEvent_t the caller created with timing enabled; either may be NULL.
+ * Read them with hipEventElapsedTime once the stream has passed the call.
+ * Always PA_OK. */
 pa_status pa_set_launch_events(void* start_event, void* stop_event);
 
 /* Single-pass paged decode attention ([IMPL] §3.1 index-based kernel and

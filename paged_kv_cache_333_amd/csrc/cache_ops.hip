@@ -452,7 +452,7 @@ hipError_t launch_swap_blocks(void* dst_key, void* dst_value, const void* src_ke
   if (gx < 1) gx = 1;
   const dim3 grid(static_cast<uint32_t>(gx * num_pairs), 2);
 #define PA_SWAP(H)                                                                                           \
-  hipLaunchKernelGGL(swap_blocks_kernel<H>, grid, dim3(256), 0, stream, static_cast<char*>(dst_key),         \
+  launch_kernel(swap_blocks_kernel<H>, grid, dim3(256), stream, static_cast<char*>(dst_key),         \
                      static_cast<char*>(dst_value), static_cast<const char*>(src_key),                      \
                      static_cast<const char*>(src_value), pairs, num_src_blocks, num_dst_blocks, chunks,      \
                      static_cast<int32_t>(gx))
@@ -499,7 +499,7 @@ struct ReshapeOp {
   hipStream_t stream;
   template <typename W>
   hipError_t run() const {
-    hipLaunchKernelGGL(reshape_and_cache_kernel<W>, dim3(static_cast<uint32_t>((chunks + 255) / 256)), dim3(256), 0,
+    launch_kernel(reshape_and_cache_kernel<W>, dim3(static_cast<uint32_t>((chunks + 255) / 256)), dim3(256),
                        stream, a);
     return hipGetLastError();
   }
@@ -524,24 +524,24 @@ struct UploadAndWriteOp {
       ArgSlots arg;
       for (int32_t i = 0; i < kArgSlots; ++i) arg.v[i] = i < a.num_tokens ? host_slots[i] : -1;
       const int64_t wr = static_cast<int64_t>(a.num_tokens) * a.num_kv_heads;
-      hipLaunchKernelGGL((upload_and_cache_tiles_kernel<W, true>), dim3(static_cast<uint32_t>(up + wr)), dim3(256),
-                         0, stream, a, dst, src, words, static_cast<int32_t>(up), arg);
+      launch_kernel(upload_and_cache_tiles_kernel<W, true>, dim3(static_cast<uint32_t>(up + wr)), dim3(256), stream,
+                    a, dst, src, words, static_cast<int32_t>(up), arg);
     } else if (tile) {
-      hipLaunchKernelGGL((upload_and_cache_tiles_kernel<W, false>), dim3(static_cast<uint32_t>(up + a.num_tokens)),
-                         dim3(256), 0, stream, a, dst, src, words, static_cast<int32_t>(up), ArgSlots{});
+      launch_kernel(upload_and_cache_tiles_kernel<W, false>, dim3(static_cast<uint32_t>(up + a.num_tokens)),
+                         dim3(256), stream, a, dst, src, words, static_cast<int32_t>(up), ArgSlots{});
     } else {
       const int64_t wr = (chunks + 255) / 256;
       if (nt && host_slots && a.num_tokens <= kArgSlots) {
         ArgSlots arg;
         for (int32_t i = 0; i < kArgSlots; ++i) arg.v[i] = i < a.num_tokens ? host_slots[i] : -1;
-        hipLaunchKernelGGL((upload_and_cache_kernel<W, true, true>), dim3(static_cast<uint32_t>(up + wr)), dim3(256),
-                           0, stream, a, dst, src, words, static_cast<int32_t>(up), arg);
+        launch_kernel(upload_and_cache_kernel<W, true, true>, dim3(static_cast<uint32_t>(up + wr)), dim3(256),
+                      stream, a, dst, src, words, static_cast<int32_t>(up), arg);
       } else if (nt) {
-        hipLaunchKernelGGL((upload_and_cache_kernel<W, true, false>), dim3(static_cast<uint32_t>(up + wr)),
-                           dim3(256), 0, stream, a, dst, src, words, static_cast<int32_t>(up), ArgSlots{});
+        launch_kernel(upload_and_cache_kernel<W, true, false>, dim3(static_cast<uint32_t>(up + wr)),
+                           dim3(256), stream, a, dst, src, words, static_cast<int32_t>(up), ArgSlots{});
       } else {
-        hipLaunchKernelGGL((upload_and_cache_kernel<W, false, false>), dim3(static_cast<uint32_t>(up + wr)),
-                           dim3(256), 0, stream, a, dst, src, words, static_cast<int32_t>(up), ArgSlots{});
+        launch_kernel(upload_and_cache_kernel<W, false, false>, dim3(static_cast<uint32_t>(up + wr)),
+                           dim3(256), stream, a, dst, src, words, static_cast<int32_t>(up), ArgSlots{});
       }
     }
     return hipGetLastError();
@@ -609,7 +609,7 @@ hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t*
   // about 4 chunks per thread per workgroup pass; at least one workgroup
   int64_t gx = (chunks + 1023) / 1024;
   if (gx < 1) gx = 1;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<uint32_t>(gx * num_pairs), 2), dim3(256), 0,
+  launch_kernel(copy_blocks_kernel, dim3(static_cast<uint32_t>(gx * num_pairs), 2), dim3(256),
                      stream, static_cast<char*>(key_cache), static_cast<char*>(value_cache), pairs,
                      num_blocks, chunks, static_cast<int32_t>(gx));
   return hipGetLastError();

@@ -25,7 +25,7 @@ hipError_t launch_upload(void* dst, const void* src_device_view, int64_t nbytes,
   if (words == 0) return hipSuccess;
   int64_t grid = (words + 255) / 256;
   if (grid > 256) grid = 256;  // one pass of up to 64 K words in flight; the rest loops
-  hipLaunchKernelGGL(upload_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream,
+  launch_kernel(upload_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), stream,
                      static_cast<uint32_t*>(dst), static_cast<const uint32_t*>(src_device_view), words);
   return hipGetLastError();
 }
