@@ -244,3 +244,9 @@ def test_shared_prefix_decode_validation_rejects_before_launch():
     # 4096 tokens: eight partitions of 512
     assert pa.pa_decode_shared_workspace_bytes(4, 32, 128, 4096) == 4096 + 4096 + 4 * 32 * 8 * 128 * 4 + 4 * 4
     assert pa.pa_decode_shared_workspace_bytes(-1, 32, 128, 64) == 0
+
+
+def test_set_launch_events_accepts_null_and_needs_no_device():
+    """The measurement hook only stores the events for the next call on this thread."""
+    assert pa.lib.pa_set_launch_events(None, None) == 0
+    pa.pa_set_launch_events(None, None)
