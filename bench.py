@@ -38,7 +38,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 STAGING_BUFFERS = 8  # rotating pinned staging buffers of the step's index data
 EVENT_EVERY = 4      # a stream event after the decode of every 4th step (see Bench.__init__)
-TIMING_PAIRS = 4     # event sets reused round robin by the steps that time the decode
+TIMING_SETS = 4     # event sets reused round robin by the steps that time the decode
 # the window [k - STAGING_BUFFERS, k - 2] holds STAGING_BUFFERS - 1 consecutive steps, so it holds
 # an event step whenever EVENT_EVERY <= STAGING_BUFFERS - 1
 assert EVENT_EVERY <= STAGING_BUFFERS - 1
@@ -402,13 +402,13 @@ class Bench:
         # event's first use in a launch costs the host far more than later ones.  A set's result
         # is read before its next use, many steps later, when that step has long finished.
         self.timing_pool = []
-        for _ in range(TIMING_PAIRS):
+        for _ in range(TIMING_SETS):
             trio = tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
             for ev in trio:
                 ev.record(self.stream)
             self.timing_pool.append(trio)
         self.pool_next = 0
-        self.pool_owner = [None] * TIMING_PAIRS  # the timing entry each pair's pending result goes to
+        self.pool_owner = [None] * TIMING_SETS  # the timing entry each set's pending result goes to
         self.elem = synth.ELEM_BYTES[w.dtype]
         self.kv_elem = 1 if self.quant else self.elem
         torch.cuda.synchronize()
@@ -445,7 +445,7 @@ class Bench:
             # precede the decode's first wave, e_prev by stream order.  When the decode was queued
             # behind the previous kernel, e_start comes early and e_prev is the closer bound; when
             # the host enqueued it late (a host-bound step), e_start is.
-            slot = self.pool_next % TIMING_PAIRS
+            slot = self.pool_next % TIMING_SETS
             self.pool_next += 1
             self._resolve(slot)
             e_prev, e_start, e_end = self.timing_pool[slot]
@@ -522,7 +522,7 @@ class Bench:
             self.pool_owner[slot] = entry  # None for a warm-up step: its result is dropped
 
     def _resolve(self, slot: int):
-        """Store the decode time (ms) of the step that last used event pair `slot`."""
+        """Store the decode time (ms) of the step that last used event set `slot`."""
         entry = self.pool_owner[slot]
         if entry is not None:
             prev_end, start, end = self.timing_pool[slot]
@@ -535,7 +535,7 @@ class Bench:
         torch = self.torch
         a = self.args
         every = max(1, a.time_every)
-        for k in range(a.warmup):  # the warm-up steps take every event pair into use
+        for k in range(a.warmup):  # the warm-up steps take every event set into use
             self.step(k, None, instrument=True)
         torch.cuda.synchronize()
         timing = []
@@ -544,7 +544,7 @@ class Bench:
             self.step(k, timing, instrument=(k - a.warmup) % every == 0)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        for slot in range(TIMING_PAIRS):
+        for slot in range(TIMING_SETS):
             self._resolve(slot)
         return wall, timing
 
