@@ -397,7 +397,8 @@ pa_status pa_upload_and_cache(void* dst, const void* src, size_t nbytes, const v
  * the kernels' own dispatches, so no marker packet sits between kernels;
  * each such packet leaves the GPU idle for microseconds).  Every device call
  * of the library times its kernels this way.  A call that reaches its launch
- * clears the setting, and a call rejected before launching leaves it set.
+ * clears the setting; a call that launches nothing (rejected, or with nothing
+ * to do, such as zero sequences) leaves it set.
  * The start event is taken when the first kernel's dispatch is processed,
  * which can be before the previous kernel on the stream has finished; the
  * end of the previous call's last kernel (its stop_event) marks the start of
