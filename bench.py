@@ -68,8 +68,8 @@ def parse():
     ap.add_argument("--cache", choices=["stream", "cached"], default=None,
                     help="K/V cache policy (default: cached for workload 5, streaming otherwise)")
     ap.add_argument("--time-every", type=int, default=4,
-                    help="time the decode on every k-th timed step (the first one included), by start and "
-                         "end events that ride on the decode's own kernels (pa_set_launch_events)")
+                    help="time the decode on every k-th timed step (the first one included), by events "
+                         "attached to the kernels (pa_set_launch_events)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -438,13 +438,14 @@ class Bench:
             order = b["order_d"]
         r = k % self.newk.shape[0]
         if instrument:
-            # The decode's time, by events that ride on the kernels' own dispatches (no marker packet
-            # sits in the step): the end of its last kernel (e_end) minus the later of two starts,
-            # the end of the last kernel before it (each call below records e_prev at its end; the
-            # last one stays) and the processing of the decode's own first dispatch (e_start).  Both
-            # precede the decode's first wave, e_prev by stream order.  When the decode was queued
-            # behind the previous kernel, e_start comes early and e_prev is the closer bound; when
-            # the host enqueued it late (a host-bound step), e_start is.
+            # The decode's time, by events attached to the kernels (pa_set_launch_events), which
+            # bound them more tightly than marker events recorded around the call: the end of the
+            # decode's last kernel (e_end) minus the later of two starts, the end of the last kernel
+            # before it (each call below records e_prev at its end; the last one stays) and the
+            # processing of the decode's own first dispatch (e_start).  Both precede the decode's
+            # first wave, e_prev by stream order.  When the decode was queued behind the previous
+            # kernel, e_start comes early and e_prev is the closer bound; when the host enqueued it
+            # late (a host-bound step), e_start is.
             slot = self.pool_next % TIMING_SETS
             self.pool_next += 1
             self._resolve(slot)

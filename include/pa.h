@@ -393,16 +393,13 @@ pa_status pa_upload_and_cache(void* dst, const void* src, size_t nbytes, const v
 
 /* Measurement hook.  The next call of this library made on the calling
  * thread attaches start_event to the start of its first kernel and
- * stop_event to the end of its last (hipExtLaunchKernel: the events ride on
- * the kernels' own dispatches, so no marker packet sits between kernels;
- * each such packet leaves the GPU idle for microseconds).  Every device call
- * of the library times its kernels this way.  A call that reaches its launch
- * clears the setting; a call that launches nothing (rejected, or with nothing
- * to do, such as zero sequences) leaves it set.
- * The start event is taken when the first kernel's dispatch is processed,
- * which can be before the previous kernel on the stream has finished; the
- * end of the previous call's last kernel (its stop_event) marks the start of
- * a call exactly, since no packet sits between the two.  The events are
+ * stop_event to the end of its last (hipExtLaunchKernel).  Such events bound
+ * the call's kernels more tightly than events recorded on the stream before
+ * and after the call, whose own processing falls inside the window; like
+ * them, they still leave a few microseconds of idle GPU around the call.
+ * Every device call of the library honours the setting.  A call that reaches
+ * its launch clears it; a call that launches nothing (rejected, or with
+ * nothing to do, such as zero sequences) leaves it set.  The events are
  * hipEvent_t the caller created with timing enabled; either may be NULL.
  * Read them with hipEventElapsedTime once the stream has passed the call.
  * Always PA_OK. */

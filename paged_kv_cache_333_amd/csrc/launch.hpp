@@ -13,9 +13,8 @@ namespace pa {
 // Measurement hook (pa_set_launch_events): events to attach to the kernels of
 // the next library call made on this thread.  launch_kernel takes them: the
 // first kernel of the call records `start` when it starts, and every kernel
-// records `stop` when it ends, so the last one's end remains.  The events ride
-// on the kernels' own dispatches (hipExtLaunchKernel): no marker packet sits
-// between kernels.  The call's finish clears them.
+// records `stop` when it ends, so the last one's end remains
+// (hipExtLaunchKernel).  The call's finish clears them.
 struct LaunchEvents {
   hipEvent_t start;
   hipEvent_t stop;
