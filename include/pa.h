@@ -391,26 +391,6 @@ pa_status pa_upload_and_cache(void* dst, const void* src, size_t nbytes, const v
                               int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                               float k_scale, float v_scale, pa_dtype dtype, pa_dtype kv_dtype, void* stream);
 
-/* pa_upload_and_cache for a step that changes only a few words of index data
- * kept on the device (a decode step of a steady batch: every length grows by
- * one, and a table entry changes where a sequence opened or redirected a
- * block): sets dst[offsets[i]] = values[i] (int32 words, offsets in words)
- * for i < num_words, and writes key/value at slot_mapping as
- * pa_upload_and_cache does, with the same choice of write form.  offsets,
- * values and slot_mapping are host arrays (any host memory), read at the
- * call: they travel in the kernel arguments, so the launch reads no host
- * memory and the caller may reuse them at once.  At most 320 words and 256
- * tokens (PA_ERR_INVALID_ARG beyond: use pa_upload_and_cache).  dst: device
- * memory, 4-byte aligned, holding every offset (not checked); an offset
- * listed twice is invalid (the words are written in parallel); a negative
- * offset is PA_ERR_INVALID_ARG.  Other errors as in pa_upload_and_cache.
- * Bit-exact. */
-pa_status pa_scatter_and_cache(void* dst, const int32_t* offsets, const int32_t* values, int32_t num_words,
-                               const void* key, const void* value, void* key_cache, void* value_cache,
-                               const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
-                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float k_scale,
-                               float v_scale, pa_dtype dtype, pa_dtype kv_dtype, void* stream);
-
 /* Measurement hook.  The next call of this library made on the calling
  * thread attaches start_event to the start of its first kernel and
  * stop_event to the end of its last (hipExtLaunchKernel).  Such events bound

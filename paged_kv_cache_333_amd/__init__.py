@@ -102,8 +102,6 @@ _PROTOS = {
     "pa_order_longest_first": (_i32, [_pi32, _i32, _pi32]),
     "pa_upload": (_i32, [_vp, _vp, _sz, _vp]),
     "pa_set_launch_events": (_i32, [_vp, _vp]),
-    "pa_scatter_and_cache": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
-                                    _f32, _f32, _i32, _i32, _vp]),
     "pa_upload_and_cache": (_i32, [_vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
                                    _f32, _i32, _i32, _vp]),
     "pa_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
@@ -255,25 +253,6 @@ def pa_upload_and_cache(dst, src, key, value, key_cache, value_cache, slot_mappi
                                    _ptr(value_cache), _ptr(slot_mapping_host), slot_mapping_host.numel(), NB, H_kv,
                                    D, bs, k_scale, v_scale, _dtype_code(key), kv, _stream(stream)),
            "pa_upload_and_cache")
-
-
-def pa_scatter_and_cache(dst, offsets, values, key, value, key_cache, value_cache, slot_mapping,
-                         k_scale: float = 1.0, v_scale: float = 1.0, kv_format=None, stream=None):
-    """dst[offsets[i]] = values[i] (int32 words of a device tensor) and the slot-mapping write of
-    key, value [T, H_kv, D], in one launch whose arguments carry the words and the slots;
-    offsets, values, slot_mapping: int32 host tensors (CPU), at most 320 words and 256 tokens."""
-    for t in (offsets, values, slot_mapping):
-        if t.device.type != "cpu" or t.dtype != _torch().int32 or not t.is_contiguous():
-            raise ValueError("pa_scatter_and_cache: offsets, values and slot_mapping are contiguous int32 CPU tensors")
-    if offsets.numel() != values.numel():
-        raise ValueError("pa_scatter_and_cache: offsets and values differ in length")
-    NB, H_kv, bs, D = _pool_dims(key_cache, value_cache)
-    kv = _kv_format(key_cache, kv_format) if key_cache.element_size() == 1 else _dtype_code(key_cache)
-    _check(lib.pa_scatter_and_cache(_ptr(dst), _ptr(offsets), _ptr(values), offsets.numel(), _ptr(key),
-                                    _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping),
-                                    slot_mapping.numel(), NB, H_kv, D, bs, k_scale, v_scale, _dtype_code(key), kv,
-                                    _stream(stream)),
-           "pa_scatter_and_cache")
 
 
 def pa_swap_blocks(dst_key_cache, dst_value_cache, src_key_cache, src_value_cache, pairs, stream=None,

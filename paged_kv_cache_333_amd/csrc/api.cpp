@@ -89,17 +89,6 @@ bool one_token_per_block(const int32_t* slots, int32_t n, int32_t num_blocks, in
   return true;
 }
 
-// The form of a step's write from its host-readable slots: when every token
-// has a block of its own (a decode step appending one token per sequence),
-// the whole-tile write, or the element-wise one with non-temporal stores
-// (model-type pools only: the quantising write's one-byte non-temporal
-// stores made the FP8 step slower, 125 -> 130 us); else plain element-wise
-// stores.  0 / 1 / 2 as in launch_upload_and_cache.
-int32_t write_form(const int32_t* slots, int32_t n, int32_t num_blocks, int32_t block_size, bool quant) {
-  const bool own_blocks = n > 0 && one_token_per_block(slots, n, num_blocks, block_size);
-  return !own_blocks ? 0 : tile_write_wanted(block_size) ? 2 : quant ? 0 : 1;
-}
-
 pa_status hip_fail(hipError_t e, const char* what) {
   return fail(PA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
@@ -540,51 +529,17 @@ pa_status pa_upload_and_cache(void* dst, const void* src, size_t nbytes, const v
       return fail(PA_ERR_INVALID_ARG, "slot_mapping must be page-locked host memory");
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int32_t form = write_form(slot_mapping, num_tokens, num_blocks, block_size, quant);
+  // when every token has a block of its own (a decode step appending one token per sequence): the
+  // whole-tile write, or the element-wise one with non-temporal stores (model-type pools only: the
+  // quantising write's one-byte non-temporal stores made the FP8 step slower, 125 -> 130 us); else
+  // plain element-wise stores
+  const bool own_blocks = num_tokens > 0 && one_token_per_block(slot_mapping, num_tokens, num_blocks, block_size);
+  const int32_t form = !own_blocks ? 0 : tile_write_wanted(block_size) ? 2 : quant ? 0 : 1;
   return finish(pa::launch_upload_and_cache(dst, src_view, static_cast<int64_t>(nbytes), key, value, key_cache,
                                             value_cache, static_cast<const int32_t*>(slots_view), num_tokens,
                                             num_blocks, num_kv_heads, head_dim, block_size, dtype, kv_dtype,
                                             k_scale, v_scale, form, slot_mapping, st),
                 st, "pa_upload_and_cache");
-}
-
-pa_status pa_scatter_and_cache(void* dst, const int32_t* offsets, const int32_t* values, int32_t num_words,
-                               const void* key, const void* value, void* key_cache, void* value_cache,
-                               const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
-                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float k_scale,
-                               float v_scale, pa_dtype dtype, pa_dtype kv_dtype, void* stream) {
-  pa_status s = check_shape(dtype, head_dim, block_size);
-  if (s != PA_OK) return s;
-  const bool quant = is_code_type(kv_dtype);
-  if (!quant && kv_dtype != dtype)
-    return fail(PA_ERR_UNSUPPORTED, "kv_dtype must equal dtype, or be PA_FP8_E4M3 / PA_INT8");
-  if (quant && (s = check_scales(k_scale, v_scale)) != PA_OK) return s;
-  if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0 || num_words < 0)
-    return fail(PA_ERR_INVALID_ARG, "negative size or zero heads");
-  if (num_words > 320 || num_tokens > 256)
-    return fail(PA_ERR_INVALID_ARG, "at most 320 words and 256 tokens travel in the kernel arguments; "
-                                    "use pa_upload_and_cache");
-  if (num_words == 0 && num_tokens == 0) return PA_OK;
-  if (num_words > 0) {
-    const void* view = nullptr;
-    if (!dst || !offsets || !values) return fail(PA_ERR_INVALID_ARG, "null pointer");
-    if (reinterpret_cast<uintptr_t>(dst) & 3u) return fail(PA_ERR_INVALID_ARG, "dst must be 4-byte aligned");
-    if (device_view(dst, &view) != 0) return fail(PA_ERR_INVALID_ARG, "dst must be device memory");
-    for (int32_t i = 0; i < num_words; ++i)
-      if (offsets[i] < 0) return fail(PA_ERR_INVALID_ARG, "negative offset");
-  }
-  if (num_tokens > 0) {
-    if (!key || !value || !key_cache || !value_cache || !slot_mapping)
-      return fail(PA_ERR_INVALID_ARG, "null pointer");
-    if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
-      return fail(PA_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
-  }
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int32_t form = write_form(slot_mapping, num_tokens, num_blocks, block_size, quant);
-  return finish(pa::launch_scatter_and_cache(dst, offsets, values, num_words, key, value, key_cache, value_cache,
-                                             slot_mapping, num_tokens, num_blocks, num_kv_heads, head_dim,
-                                             block_size, dtype, kv_dtype, k_scale, v_scale, form, st),
-                st, "pa_scatter_and_cache");
 }
 
 pa_status pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,

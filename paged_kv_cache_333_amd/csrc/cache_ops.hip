@@ -3,8 +3,6 @@
 // 16-byte chunk of a row and consecutive lanes take consecutive chunks; key
 // rows are stored as whole chunks, value rows element by element down a
 // column of the dim-major value tile.
-#include <type_traits>
-
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -310,36 +308,12 @@ struct ArgSlots {
   int32_t v[kArgSlots];
 };
 
-// The first part of a write launch, run by its first up_blocks workgroups:
-// the step's index data copied from page-locked host memory (CopyPrelude),
-// or a scatter of a few words passed in the kernel arguments (ScatterPrelude:
-// dst[off[i]] = val[i], one workgroup), for a step that changes only some
-// entries of index data kept on the device.
-struct CopyPrelude {
-  uint32_t* dst;
-  const uint32_t* src;
-  int64_t words;
-  __device__ __forceinline__ void run(int32_t up_blocks) const { upload_words(dst, src, words, up_blocks); }
-};
-constexpr int32_t kArgScatter = 320;
-struct ArgScatter {
-  int32_t n;
-  int32_t off[kArgScatter];
-  int32_t val[kArgScatter];
-};
-struct ScatterPrelude {
-  int32_t* dst;
-  ArgScatter sc;
-  __device__ __forceinline__ void run(int32_t) const {
-    for (int32_t i = threadIdx.x; i < sc.n; i += blockDim.x) dst[sc.off[i]] = sc.val[i];
-  }
-};
-
-template <typename W, bool NT, bool ARG, typename P>
-__global__ __launch_bounds__(256) void upload_and_cache_kernel(WriteArgs a, P pre, int32_t up_blocks,
-                                                               ArgSlots arg) {
+template <typename W, bool NT, bool ARG>
+__global__ __launch_bounds__(256) void upload_and_cache_kernel(WriteArgs a, uint32_t* __restrict__ dst,
+                                                               const uint32_t* src, int64_t words,
+                                                               int32_t up_blocks, ArgSlots arg) {
   if (static_cast<int32_t>(blockIdx.x) < up_blocks) {
-    pre.run(up_blocks);
+    upload_words(dst, src, words, up_blocks);
     return;
   }
   __shared__ int32_t slots_lds[256];
@@ -366,11 +340,12 @@ __global__ __launch_bounds__(256) void upload_and_cache_kernel(WriteArgs a, P pr
 // from host memory once, and workgroup up_blocks + tok writes all the token's
 // tiles (host reads of one line by many workgroups queue behind each other).
 
-template <typename W, bool ARG_SLOTS, typename P>
-__global__ __launch_bounds__(256) void upload_and_cache_tiles_kernel(WriteArgs a, P pre, int32_t up_blocks,
-                                                                     ArgSlots arg) {
+template <typename W, bool ARG_SLOTS>
+__global__ __launch_bounds__(256) void upload_and_cache_tiles_kernel(WriteArgs a, uint32_t* __restrict__ dst,
+                                                                     const uint32_t* src, int64_t words,
+                                                                     int32_t up_blocks, ArgSlots arg) {
   if (static_cast<int32_t>(blockIdx.x) < up_blocks) {
-    pre.run(up_blocks);
+    upload_words(dst, src, words, up_blocks);
     return;
   }
   const int64_t t = static_cast<int64_t>(blockIdx.x) - up_blocks;
@@ -530,39 +505,44 @@ struct ReshapeOp {
   }
 };
 
-template <typename P>
 struct UploadAndWriteOp {
   WriteArgs a;
   int64_t chunks;
-  P pre;
-  int64_t up;                 // workgroups of the prelude
+  uint32_t* dst;
+  const uint32_t* src;
+  int64_t words;
   hipStream_t stream;
-  const int32_t* host_slots;  // the slot mapping readable here, or null
+  const int32_t* host_slots;  // the slot mapping readable here (no two tokens in one block), or null
   bool nt;                    // element-wise write with non-temporal stores (no two tokens in one block)
   bool tile;                  // whole-tile write (no two tokens in one block; host_slots set)
   template <typename W>
   hipError_t run() const {
-    const bool args = host_slots && a.num_tokens <= kArgSlots;
-    ArgSlots arg;
-    for (int32_t i = 0; i < kArgSlots; ++i) arg.v[i] = args && i < a.num_tokens ? host_slots[i] : -1;
-    const int32_t ub = static_cast<int32_t>(up);
-    if (tile && args) {
+    int64_t up = (words + 255) / 256;
+    if (up > 64) up = 64;  // the index block is a few KB to a few hundred KB
+    if (up < 1) up = 1;
+    if (tile && a.num_tokens <= kArgSlots) {
+      ArgSlots arg;
+      for (int32_t i = 0; i < kArgSlots; ++i) arg.v[i] = i < a.num_tokens ? host_slots[i] : -1;
       const int64_t wr = static_cast<int64_t>(a.num_tokens) * a.num_kv_heads;
-      launch_kernel(upload_and_cache_tiles_kernel<W, true, P>, dim3(static_cast<uint32_t>(up + wr)), dim3(256),
-                    stream, a, pre, ub, arg);
+      launch_kernel(upload_and_cache_tiles_kernel<W, true>, dim3(static_cast<uint32_t>(up + wr)), dim3(256), stream,
+                    a, dst, src, words, static_cast<int32_t>(up), arg);
     } else if (tile) {
-      launch_kernel(upload_and_cache_tiles_kernel<W, false, P>, dim3(static_cast<uint32_t>(up + a.num_tokens)),
-                    dim3(256), stream, a, pre, ub, arg);
+      launch_kernel(upload_and_cache_tiles_kernel<W, false>, dim3(static_cast<uint32_t>(up + a.num_tokens)),
+                         dim3(256), stream, a, dst, src, words, static_cast<int32_t>(up), ArgSlots{});
     } else {
-      const uint32_t grid = static_cast<uint32_t>(up + (chunks + 255) / 256);
-      if (nt && args)
-        launch_kernel(upload_and_cache_kernel<W, true, true, P>, dim3(grid), dim3(256), stream, a, pre, ub, arg);
-      else if (nt)
-        launch_kernel(upload_and_cache_kernel<W, true, false, P>, dim3(grid), dim3(256), stream, a, pre, ub, arg);
-      else if (args && std::is_same<P, ScatterPrelude>::value)  // no other source of slots
-        launch_kernel(upload_and_cache_kernel<W, false, true, P>, dim3(grid), dim3(256), stream, a, pre, ub, arg);
-      else
-        launch_kernel(upload_and_cache_kernel<W, false, false, P>, dim3(grid), dim3(256), stream, a, pre, ub, arg);
+      const int64_t wr = (chunks + 255) / 256;
+      if (nt && host_slots && a.num_tokens <= kArgSlots) {
+        ArgSlots arg;
+        for (int32_t i = 0; i < kArgSlots; ++i) arg.v[i] = i < a.num_tokens ? host_slots[i] : -1;
+        launch_kernel(upload_and_cache_kernel<W, true, true>, dim3(static_cast<uint32_t>(up + wr)), dim3(256),
+                      stream, a, dst, src, words, static_cast<int32_t>(up), arg);
+      } else if (nt) {
+        launch_kernel(upload_and_cache_kernel<W, true, false>, dim3(static_cast<uint32_t>(up + wr)),
+                           dim3(256), stream, a, dst, src, words, static_cast<int32_t>(up), ArgSlots{});
+      } else {
+        launch_kernel(upload_and_cache_kernel<W, false, false>, dim3(static_cast<uint32_t>(up + wr)),
+                           dim3(256), stream, a, dst, src, words, static_cast<int32_t>(up), ArgSlots{});
+      }
     }
     return hipGetLastError();
   }
@@ -610,41 +590,14 @@ hipError_t launch_upload_and_cache(void* dst, const void* src_device_view, int64
   const int64_t chunks = write_chunks(num_tokens, num_kv_heads, head_dim, dtype);
   const int64_t words = nbytes / 4;
   if (chunks == 0 && words == 0) return hipSuccess;
-  int64_t up = (words + 255) / 256;
-  if (up > 64) up = 64;  // the index block is a few KB to a few hundred KB
-  if (up < 1) up = 1;
-  const bool tile = num_tokens > 0 && write_form == 2;
+  const int32_t* tiles = num_tokens > 0 && write_form == 2 ? host_slots : nullptr;
   const bool nt = write_form == 1;
-  return by_write(UploadAndWriteOp<CopyPrelude>{write_args(key, value, key_cache, value_cache,
-                                                           slot_mapping_device_view, num_tokens, num_blocks,
-                                                           num_kv_heads, head_dim, block_size, k_scale, v_scale),
-                                                chunks,
-                                                CopyPrelude{static_cast<uint32_t*>(dst),
-                                                            static_cast<const uint32_t*>(src_device_view), words},
-                                                up, stream, tile || nt ? host_slots : nullptr, nt, tile},
-                  dtype, kv_dtype);
-}
-
-hipError_t launch_scatter_and_cache(void* dst, const int32_t* offsets, const int32_t* values, int32_t num_words,
-                                    const void* key, const void* value, void* key_cache, void* value_cache,
-                                    const int32_t* host_slots, int32_t num_tokens, int32_t num_blocks,
-                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pa_dtype dtype,
-                                    pa_dtype kv_dtype, float k_scale, float v_scale, int32_t write_form,
-                                    hipStream_t stream) {
-  if (num_words > kArgScatter || num_tokens > kArgSlots) return hipErrorInvalidValue;
-  const int64_t chunks = write_chunks(num_tokens, num_kv_heads, head_dim, dtype);
-  if (chunks == 0 && num_words == 0) return hipSuccess;
-  ScatterPrelude pre{static_cast<int32_t*>(dst), ArgScatter{}};
-  pre.sc.n = num_words;
-  for (int32_t i = 0; i < num_words; ++i) {
-    pre.sc.off[i] = offsets[i];
-    pre.sc.val[i] = values[i];
-  }
-  const bool tile = num_tokens > 0 && write_form == 2;
-  return by_write(UploadAndWriteOp<ScatterPrelude>{write_args(key, value, key_cache, value_cache, nullptr,
-                                                              num_tokens, num_blocks, num_kv_heads, head_dim,
-                                                              block_size, k_scale, v_scale),
-                                                   chunks, pre, 1, stream, host_slots, write_form == 1, tile},
+  const int32_t* arg_slots = nt ? host_slots : nullptr;
+  return by_write(UploadAndWriteOp{write_args(key, value, key_cache, value_cache, slot_mapping_device_view,
+                                              num_tokens, num_blocks, num_kv_heads, head_dim, block_size, k_scale,
+                                              v_scale),
+                                   chunks, static_cast<uint32_t*>(dst), static_cast<const uint32_t*>(src_device_view),
+                                   words, stream, tiles ? tiles : arg_slots, nt, tiles != nullptr},
                   dtype, kv_dtype);
 }
 

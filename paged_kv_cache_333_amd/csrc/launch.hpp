@@ -86,15 +86,6 @@ hipError_t launch_upload_and_cache(void* dst, const void* src_device_view, int64
                                    int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                    pa_dtype dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
                                    int32_t write_form, const int32_t* host_slots, hipStream_t stream);
-// The write of launch_upload_and_cache, with the index upload replaced by a
-// scatter of num_words (<= 320) words dst[offsets[i]] = values[i] passed in
-// the kernel arguments, and the slots (host_slots, <= 256 tokens) too.
-hipError_t launch_scatter_and_cache(void* dst, const int32_t* offsets, const int32_t* values, int32_t num_words,
-                                    const void* key, const void* value, void* key_cache, void* value_cache,
-                                    const int32_t* host_slots, int32_t num_tokens, int32_t num_blocks,
-                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pa_dtype dtype,
-                                    pa_dtype kv_dtype, float k_scale, float v_scale, int32_t write_form,
-                                    hipStream_t stream);
 // write_form: 0 element-wise; 1 element-wise with non-temporal stores; 2 whole
 // value tiles (host_slots: the host-readable slot mapping).  Forms 1 and 2
 // need a call in which no two tokens share a block.

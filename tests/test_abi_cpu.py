@@ -19,7 +19,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 52
+    assert len(names) == 51
     for n in names:
         assert hasattr(pa.lib, n), n
         assert C.cast(getattr(pa.lib, n), C.c_void_p).value
@@ -250,16 +250,3 @@ def test_set_launch_events_accepts_null_and_needs_no_device():
     """The measurement hook only stores the events for the next call on this thread."""
     assert pa.lib.pa_set_launch_events(None, None) == 0
     pa.pa_set_launch_events(None, None)
-
-
-def test_scatter_and_cache_limits_are_checked_before_any_device_work():
-    """pa_scatter_and_cache carries its words and slots in the kernel arguments: more than 320
-    words or 256 tokens is PA_ERR_INVALID_ARG, and an empty call is a no-op."""
-    f = pa.lib.pa_scatter_and_cache
-    off = (C.c_int32 * 400)()
-    val = (C.c_int32 * 400)()
-    # dst, offsets, values, n, key, value, kc, vc, slots, T, NB, Hkv, D, bs, ks, vs, dtype, kv, stream
-    assert f(None, off, val, 321, None, None, None, None, None, 0, 16, 4, 128, 16, 1.0, 1.0, 1, 1, None) == 1
-    assert f(None, off, val, 0, None, None, None, None, off, 257, 16, 4, 128, 16, 1.0, 1.0, 1, 1, None) == 1
-    assert f(None, off, val, 0, None, None, None, None, None, 0, 16, 4, 128, 16, 1.0, 1.0, 1, 1, None) == 0
-    assert f(None, off, val, -1, None, None, None, None, None, 0, 16, 4, 128, 16, 1.0, 1.0, 1, 1, None) == 1

@@ -353,79 +353,3 @@ def test_upload_and_cache_full_size_step(key):
         ref = A.decode_one(q, kb, vb, np.arange(len(table), dtype=np.int32), n, 0, 1, w.scale, w.dtype,
                            quant=quant)
         assert_close(out[s, h], ref, w.dtype, f"seq {s} head {h}")
-
-
-@pytest.mark.parametrize("dtype,D,bs,Hkv,fmt", [("f16", 128, 16, 32, None), ("bf16", 128, 32, 8, None),
-                                                ("f32", 64, 16, 4, None), ("f16", 128, 16, 8, "fp8_e4m3"),
-                                                ("bf16", 128, 32, 8, "int8")])
-@pytest.mark.parametrize("own_blocks", [True, False])
-def test_scatter_and_cache_bit_exact(dtype, D, bs, Hkv, fmt, own_blocks):
-    """pa_scatter_and_cache: the scattered words land and nothing else of dst changes; the write
-    equals the oracle's, in blocks of their own (whole-tile or non-temporal form) or shared
-    (plain form); the arrays are ordinary (pageable) host memory."""
-    NB, T = 300, 37
-    rng = np.random.default_rng(D + bs + Hkv + (7 if fmt else 0) + own_blocks)
-    if fmt:
-        kc = synth.normal_codes_host((NB, Hkv, bs, D), 9, fmt)
-        vc = synth.normal_codes_host((NB, Hkv, D, bs), 10, fmt)
-        dk, dv = torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda()
-    else:
-        kc = synth.normal_host((NB, Hkv, bs, D), 9, dtype)
-        vc = synth.normal_host((NB, Hkv, D, bs), 10, dtype)
-        dk, dv = _dev(kc, dtype), _dev(vc, dtype)
-    key = synth.normal_host((T, Hkv, D), 11, dtype)
-    val = synth.normal_host((T, Hkv, D), 12, dtype)
-    if own_blocks:
-        slots = (rng.choice(NB, size=T, replace=False) * bs + rng.integers(0, bs, size=T)).astype(np.int32)
-    else:
-        slots = rng.choice(NB // 8 * bs, size=T, replace=False).astype(np.int32)  # the first 37 blocks: shared
-    slots[4] = -1
-    dst_host = rng.integers(-10**6, 10**6, size=5000).astype(np.int32)
-    dst = torch.from_numpy(dst_host).cuda()
-    n = 320
-    offs = rng.choice(dst_host.size, size=n, replace=False).astype(np.int32)
-    vals = rng.integers(-10**6, 10**6, size=n).astype(np.int32)
-    ks, vs = (0.02, 0.03) if fmt else (1.0, 1.0)
-    pa.pa_scatter_and_cache(dst, torch.from_numpy(offs), torch.from_numpy(vals), _dev(key, dtype), _dev(val, dtype),
-                            dk, dv, torch.from_numpy(slots), ks, vs, kv_format=fmt)
-    torch.cuda.synchronize()
-    expect = dst_host.copy()
-    expect[offs] = vals
-    assert np.array_equal(dst.cpu().numpy(), expect)
-    if fmt:
-        ek, ev = C.reshape_and_cache_quant(key, val, kc, vc, slots, dtype, fmt, ks, vs)
-        assert np.array_equal(dk.cpu().numpy(), ek) and np.array_equal(dv.cpu().numpy(), ev)
-    else:
-        ek, ev = C.reshape_and_cache(key, val, kc, vc, slots)
-        assert np.array_equal(synth.to_numpy(dk, dtype), ek) and np.array_equal(synth.to_numpy(dv, dtype), ev)
-
-
-@pytest.mark.parametrize("key", [2, 3])
-def test_scatter_keeps_device_tables_equal_to_the_allocator(key):
-    """Steady decode steps with the index data kept on the device: after a full upload, each
-    step scatters only the words that changed (every length, and the table entries of sequences
-    that opened a block).  After several steps, crossing block boundaries, the device tables and
-    lengths equal the C++ allocator's (and the oracle allocator's) bit for bit."""
-    from tests.gpu_helpers import DeviceWorkload
-    dw = DeviceWorkload(key, extra_blocks_per_seq=4)
-    w = dw.w
-    S, MB = w.num_seqs, dw.max_blocks
-    tabs, lens = dw.alloc.build_block_tables(dw.seq_ids, MB)
-    host = np.concatenate([np.array(lens, np.int32), np.array(tabs, np.int32).reshape(-1)])
-    dev_block = torch.from_numpy(host.copy()).cuda()
-    nk = _dev(synth.normal_host((S, w.num_kv_heads, w.head_dim), 3, w.dtype), w.dtype)
-    nv = _dev(synth.normal_host((S, w.num_kv_heads, w.head_dim), 4, w.dtype), w.dtype)
-    for step in range(w.block_size + 3):                  # every sequence crosses a block boundary
-        slots, pairs = dw.alloc.seq_append_slots(dw.seq_ids)
-        assert (slots, pairs) == dw.ora.seq_append_slots(dw.seq_ids) and not pairs
-        tabs, lens = dw.alloc.build_block_tables(dw.seq_ids, MB)
-        new = np.concatenate([np.array(lens, np.int32), np.array(tabs, np.int32).reshape(-1)])
-        changed = np.nonzero(new != host)[0].astype(np.int32)
-        assert S <= changed.size <= 320
-        pa.pa_scatter_and_cache(dev_block, torch.from_numpy(changed), torch.from_numpy(new[changed]), nk, nv,
-                                dw.key_cache, dw.value_cache, torch.tensor(slots, dtype=torch.int32))
-        host = new
-    torch.cuda.synchronize()
-    assert np.array_equal(dev_block.cpu().numpy(), host)
-    otabs, olens = dw.ora.build_block_tables(dw.seq_ids, MB)
-    assert np.array_equal(host, np.concatenate([np.array(olens, np.int32), np.array(otabs, np.int32).reshape(-1)]))
