@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "launch.hpp"
+#include "slot_blocks.hpp"
 #include "status.hpp"
 
 namespace pa {
@@ -61,53 +62,6 @@ bool tile_write_wanted(int32_t block_size) {
   if (v && std::strcmp(v, "always") == 0) return true;
   if (v && std::strcmp(v, "never") == 0) return false;
   return block_size >= 32;
-}
-
-// True when no two tokens' slots inside the pool fall in one block.  Read on
-// the host from the page-locked slot mapping (final at the call).  O(n) with
-// a per-thread stamp per block for pools of up to kStampBlocks blocks; larger
-// pools sort the call's block ids instead (no allocation that scales with the
-// pool, and nothing that can throw across the C ABI).
-constexpr int32_t kStampBlocks = 1 << 24;
-bool one_token_per_block(const int32_t* slots, int32_t n, int32_t num_blocks, int32_t block_size) {
-  if (n <= 1) return true;
-  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
-  thread_local std::vector<uint32_t> stamp;
-  thread_local uint32_t epoch = 0;
-  bool stamps = num_blocks <= kStampBlocks;
-  if (stamps && stamp.size() < static_cast<size_t>(num_blocks)) {
-    try {
-      stamp.assign(static_cast<size_t>(num_blocks), 0u);
-      epoch = 0;
-    } catch (...) {
-      stamp.clear();
-      stamps = false;
-    }
-  }
-  if (!stamps) {
-    thread_local std::vector<int32_t> ids;
-    try {
-      ids.clear();
-      for (int32_t i = 0; i < n; ++i)
-        if (slots[i] >= 0 && slots[i] < num_slots) ids.push_back(slots[i] / block_size);
-    } catch (...) {
-      return false;  // the element-wise write is correct for any slots
-    }
-    std::sort(ids.begin(), ids.end());
-    return std::adjacent_find(ids.begin(), ids.end()) == ids.end();
-  }
-  if (++epoch == 0) {  // wrapped: clear and start again
-    std::fill(stamp.begin(), stamp.end(), 0u);
-    epoch = 1;
-  }
-  for (int32_t i = 0; i < n; ++i) {
-    const int64_t slot = slots[i];
-    if (slot < 0 || slot >= num_slots) continue;
-    uint32_t& st = stamp[static_cast<size_t>(slot / block_size)];
-    if (st == epoch) return false;
-    st = epoch;
-  }
-  return true;
 }
 
 pa_status hip_fail(hipError_t e, const char* what) {
@@ -554,7 +508,7 @@ pa_status pa_upload_and_cache(void* dst, const void* src, size_t nbytes, const v
   // whole-tile write, or the element-wise one with non-temporal stores (model-type pools only: the
   // quantising write's one-byte non-temporal stores made the FP8 step slower, 125 -> 130 us); else
   // plain element-wise stores
-  const bool own_blocks = num_tokens > 0 && one_token_per_block(slot_mapping, num_tokens, num_blocks, block_size);
+  const bool own_blocks = num_tokens > 0 && pa::one_token_per_block(slot_mapping, num_tokens, num_blocks, block_size);
   const int32_t form = !own_blocks ? 0 : tile_write_wanted(block_size) ? 2 : quant ? 0 : 1;
   return finish(pa::launch_upload_and_cache(dst, src_view, static_cast<int64_t>(nbytes), key, value, key_cache,
                                             value_cache, static_cast<const int32_t*>(slots_view), num_tokens,
