@@ -332,6 +332,16 @@ class Bench:
                 self.alloc.seq_create(s, n)
             self.base = self.alloc.clone() if args.workload == 1 else None
             growth = 1 if args.workload == 1 else total_steps * w.query_len
+            # the pool is a shape of the workload, sized for its initial contexts: say up front
+            # when the run's growth would not fit instead of failing in the middle of it
+            end_blocks = sum(-(-(n + growth) // bs) for n in w.context_lens)
+            if end_blocks > w.num_blocks:
+                per_step = max(1, w.query_len)
+                fit = max(k for k in range(total_steps + 1)
+                          if sum(-(-(n + k * per_step) // bs) for n in w.context_lens) <= w.num_blocks)
+                raise SystemExit(f"workload {args.workload}'s pool of {w.num_blocks} blocks holds "
+                                 f"{fit} steps of growth; --warmup {args.warmup} --steps {args.steps} "
+                                 f"needs {end_blocks} blocks")
         self.max_blocks = -(-(max(w.context_lens) + growth) // bs) + 1
         self.max_ctx = self.max_blocks * bs
 
