@@ -32,6 +32,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+
+
+def steps_that_fit(context_lens, block_size, num_blocks, tokens_per_step, max_steps):
+    """The most steps (up to max_steps) in which every sequence can grow by tokens_per_step
+    tokens without its blocks outgrowing a pool of num_blocks (no block is shared)."""
+    def blocks(k):
+        return sum(-(-(n + k * tokens_per_step) // block_size) for n in context_lens)
+    return max(k for k in range(max_steps + 1) if k == 0 or blocks(k) <= num_blocks)
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_333_amd", "csrc", "decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
@@ -334,14 +342,11 @@ class Bench:
             growth = 1 if args.workload == 1 else total_steps * w.query_len
             # the pool is a shape of the workload, sized for its initial contexts: say up front
             # when the run's growth would not fit instead of failing in the middle of it
-            end_blocks = sum(-(-(n + growth) // bs) for n in w.context_lens)
-            if end_blocks > w.num_blocks:
-                per_step = max(1, w.query_len)
-                fit = max(k for k in range(total_steps + 1)
-                          if sum(-(-(n + k * per_step) // bs) for n in w.context_lens) <= w.num_blocks)
+            fit = steps_that_fit(w.context_lens, bs, w.num_blocks, w.query_len, total_steps)
+            if fit < total_steps:
                 raise SystemExit(f"workload {args.workload}'s pool of {w.num_blocks} blocks holds "
                                  f"{fit} steps of growth; --warmup {args.warmup} --steps {args.steps} "
-                                 f"needs {end_blocks} blocks")
+                                 f"asks for {total_steps}")
         self.max_blocks = -(-(max(w.context_lens) + growth) // bs) + 1
         self.max_ctx = self.max_blocks * bs
 
