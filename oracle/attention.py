@@ -109,6 +109,17 @@ def gather_kv(key_cache, value_cache, table_row, num_tokens: int, kv_head: int, 
     return to_f64(K, dtype), to_f64(V, dtype)
 
 
+def kv_head_of(head: int, num_heads: int, num_kv_heads: int) -> int:
+    """The KV head query head `head` reads: contiguous groups of G = H / H_kv query heads
+    share one KV head, so head h reads KV head h // G (the plain reading of grouped-query
+    attention, which the pages name only as future work)."""
+    if num_kv_heads <= 0 or num_heads % num_kv_heads:
+        raise ValueError("num_heads must be a positive multiple of num_kv_heads")
+    if not 0 <= head < num_heads:
+        raise IndexError(f"query head {head} outside 0..{num_heads - 1}")
+    return head // (num_heads // num_kv_heads)
+
+
 def keep_positions(num_tokens: int, lo: int, hi: int) -> np.ndarray:
     """Positions t < num_tokens outside [lo, hi)."""
     t = np.arange(num_tokens)
@@ -168,7 +179,7 @@ def attend(q64: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.nd
 def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scale: float,
                  dtype: str, quant=None, masks=None) -> np.ndarray:
     """out[s, h] = attention of query[s, h] over the first context_lens[s] tokens of
-    sequence s, gathered through block_tables[s] from the KV head h // G.
+    sequence s, gathered through block_tables[s] from KV head kv_head_of(h, H, H_kv).
 
     query [S, H, D]; key_cache [NB, H_kv, bs, D]; value_cache [NB, H_kv, D, bs];
     block_tables [S, MB]; context_lens [S].  Returns float64 [S, H, D].
@@ -177,26 +188,32 @@ def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scal
     """
     S, H, D = query.shape
     H_kv = key_cache.shape[1]
-    if H % H_kv:
-        raise ValueError("num_heads must be a multiple of num_kv_heads")
-    G = H // H_kv
     sig = scale_f64(scale)
     out = np.zeros((S, H, D), dtype=np.float64)
     for s in range(S):
         n = int(context_lens[s])
-        for g in range(H_kv):
-            mask = None if masks is None else (masks[0][s], masks[1][s])
-            K, V = kv_for(key_cache, value_cache, block_tables[s], n, g, dtype, quant, mask)
-            for h in range(g * G, (g + 1) * G):
-                out[s, h] = attend(to_f64(query[s, h], dtype), K, V, sig)
+        mask = None if masks is None else (masks[0][s], masks[1][s])
+        kv = {}
+        for h in range(H):
+            g = kv_head_of(h, H, H_kv)
+            if g not in kv:
+                kv[g] = kv_for(key_cache, value_cache, block_tables[s], n, g, dtype, quant, mask)
+            K, V = kv[g]
+            out[s, h] = attend(to_f64(query[s, h], dtype), K, V, sig)
     return out
 
 
 def decode_one(query, key_cache, value_cache, table_row, num_tokens: int, head: int,
                num_heads: int, scale: float, dtype: str, quant=None, mask=None) -> np.ndarray:
-    """One output row out[s, head] (query = query[s], table_row = block_tables[s])."""
+    """One output row: out[s, head] of paged_decode, for query = query[s] ([num_heads, D])
+    and table_row = block_tables[s].  The pools may hold every KV head, or only the one
+    this head reads (key_cache.shape[1] == 1, as when a caller fetched just that head's
+    blocks): then query head `head` of `num_heads` still names its row of `query`, and the
+    single stored KV head stands for kv_head_of(head, num_heads, H_kv) of the full pool."""
+    if query.shape[0] != num_heads:
+        raise ValueError("query must hold the sequence's num_heads rows")
     H_kv = key_cache.shape[1]
-    g = head // (num_heads // H_kv)
+    g = 0 if H_kv == 1 else kv_head_of(head, num_heads, H_kv)
     K, V = kv_for(key_cache, value_cache, table_row, num_tokens, g, dtype, quant, mask)
     return attend(to_f64(query[head], dtype), K, V, scale_f64(scale))
 
@@ -244,30 +261,6 @@ def lse_merge(m: np.ndarray, l: np.ndarray, o: np.ndarray) -> np.ndarray:
     return (w @ o) / np.sum(w)
 
 
-def split_decode_partials(query, key_cache, value_cache, block_tables, context_lens, scale: float,
-                          dtype: str, partition_size: int, seqs=None, heads=None, quant=None, masks=None):
-    """Partials (m, l, o) for every (seq, head) in `seqs` x `heads`: a dict keyed by (s, h)."""
-    S, H, D = query.shape
-    H_kv = key_cache.shape[1]
-    G = H // H_kv
-    sig = scale_f64(scale)
-    seqs = range(S) if seqs is None else seqs
-    heads = range(H) if heads is None else heads
-    res = {}
-    for s in seqs:
-        n = int(context_lens[s])
-        mask = None if masks is None else (int(masks[0][s]), int(masks[1][s]))
-        pos = np.arange(n) if mask is None else keep_positions(n, *mask)
-        cache = {}
-        for h in heads:
-            g = h // G
-            if g not in cache:
-                cache[g] = kv_for(key_cache, value_cache, block_tables[s], n, g, dtype, quant, mask)
-            K, V = cache[g]
-            res[(s, h)] = partition_partials(to_f64(query[s, h], dtype), K, V, sig, partition_size, pos, n)
-    return res
-
-
 # ----------------------------------------------------------------------------
 # several query tokens per sequence
 
@@ -279,7 +272,6 @@ def paged_decode_multi(query, key_cache, value_cache, block_tables, context_lens
     (n = context_lens[s]).  query [T, H, D]; returns float64 [T, H, D]."""
     T, H, D = query.shape
     H_kv = key_cache.shape[1]
-    G = H // H_kv
     sig = scale_f64(scale)
     out = np.zeros((T, H, D), dtype=np.float64)
     for s in range(len(context_lens)):
@@ -288,10 +280,13 @@ def paged_decode_multi(query, key_cache, value_cache, block_tables, context_lens
         L = r1 - r0
         if L > n:
             raise ValueError("a sequence has more query tokens than cached tokens")
-        for g in range(H_kv):
-            K, V = kv_for(key_cache, value_cache, block_tables[s], n, g, dtype, quant)
+        kv = {}
+        for h in range(H):
+            g = kv_head_of(h, H, H_kv)
+            if g not in kv:
+                kv[g] = kv_for(key_cache, value_cache, block_tables[s], n, g, dtype, quant)
+            K, V = kv[g]
             for i in range(L):
                 lim = n - L + i + 1
-                for h in range(g * G, (g + 1) * G):
-                    out[r0 + i, h] = attend(to_f64(query[r0 + i, h], dtype), K[:lim], V[:lim], sig)
+                out[r0 + i, h] = attend(to_f64(query[r0 + i, h], dtype), K[:lim], V[:lim], sig)
     return out

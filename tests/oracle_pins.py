@@ -195,6 +195,79 @@ def check_split_merge(seed=23, n=1300, D=32):
     assert np.max(np.abs(A.lse_merge(mm, ll, oo) - np.array([0.25, 0.75]))) <= 1e-15
 
 
+def check_kv_head_mapping():
+    """Contiguous groups: with 32 query heads on 8 KV heads, heads 4k..4k+3 read KV head k;
+    MHA maps each head to itself and one KV head serves every query head."""
+    assert [A.kv_head_of(h, 32, 8) for h in range(32)] == [h // 4 for h in range(32)]
+    assert [A.kv_head_of(h, 6, 2) for h in range(6)] == [0, 0, 0, 1, 1, 1]
+    assert [A.kv_head_of(h, 4, 4) for h in range(4)] == [0, 1, 2, 3]
+    assert [A.kv_head_of(h, 8, 1) for h in range(8)] == [0] * 8
+    for bad in ((0, 6, 4), (6, 6, 2), (-1, 4, 4)):
+        try:
+            A.kv_head_of(*bad)
+        except (ValueError, IndexError):
+            continue
+        raise AssertionError(f"kv_head_of accepted {bad}")
+
+
+def check_decode_one_rows(seed=29):
+    """decode_one gives row (s, h) of paged_decode bit for bit, for every query head of GQA
+    and MHA shapes on permuted tables: with the full pools and the sequence's whole query,
+    and with the pools cut to the one KV head that head reads (as a caller that fetched only
+    those blocks passes them).  Each row also equals torch's float64 SDPA on the contiguous
+    cache, so a wrong head or group index cannot agree with paged_decode by accident."""
+    import torch
+    import torch.nn.functional as F
+
+    for S, H, Hkv, D, bs, ctx, dtype in ((3, 8, 2, 32, 16, (1, 37, 80), "f32"),
+                                          (2, 32, 8, 64, 32, (45, 130), "bf16"),
+                                          (2, 6, 3, 32, 16, (17, 64), "f16"),
+                                          (2, 4, 4, 32, 16, (20, 33), "f16")):
+        q, kc, vc, tables, ctx, Ks, Vs = scatter_case(seed + H, S, H, Hkv, D, bs, ctx, dtype)
+        scale = 1.0 / math.sqrt(D)
+        full = A.paged_decode(q, kc, vc, tables, ctx, scale, dtype)
+        G = H // Hkv
+        for s in range(S):
+            qt = torch.from_numpy(A.to_f64(q[s], dtype)).view(1, H, 1, D)
+            kt = torch.from_numpy(Ks[s]).view(1, Hkv, ctx[s], D)
+            vt = torch.from_numpy(Vs[s]).view(1, Hkv, ctx[s], D)
+            sdpa = F.scaled_dot_product_attention(qt, kt, vt, scale=float(np.float32(scale)),
+                                                  enable_gqa=(H != Hkv)).view(H, D).numpy()
+            for h in range(H):
+                row = A.decode_one(q[s], kc, vc, tables[s], ctx[s], h, H, scale, dtype)
+                assert np.array_equal(row, full[s, h]), f"{(S, H, Hkv)} seq {s} head {h}: differs from paged_decode"
+                assert np.max(np.abs(row - sdpa[h])) <= 1e-12, f"{(S, H, Hkv)} seq {s} head {h}: differs from SDPA"
+                g = h // G
+                cut = A.decode_one(q[s], kc[:, g:g + 1], vc[:, g:g + 1], tables[s], ctx[s], h, H, scale, dtype)
+                assert np.array_equal(cut, row), f"seq {s} head {h}: the one-KV-head form differs"
+
+
+def check_decode_one_masked_and_8bit(seed=31):
+    """decode_one with a mask, and over 8-bit pools, gives paged_decode's row (both pinned
+    on their own: the masked form against SDPA, the 8-bit form against float pools)."""
+    from oracle import quant as Q
+    S, H, Hkv, D, bs = 3, 8, 2, 32, 16
+    q, kc, vc, tables, ctx, _, _ = scatter_case(seed, S, H, Hkv, D, bs, (46, 90, 33), "f16")
+    lo, hi = [9, 0, 5], [16, 66, 5]
+    ref = A.paged_decode(q, kc, vc, tables, ctx, 0.2, "f16", masks=(lo, hi))
+    for s in range(S):
+        for h in range(H):
+            row = A.decode_one(q[s], kc, vc, tables[s], ctx[s], h, H, 0.2, "f16", mask=(lo[s], hi[s]))
+            assert np.array_equal(row, ref[s, h]), f"masked seq {s} head {h}"
+    NB = kc.shape[0]
+    for fmt in Q.FORMATS:
+        k8, v8 = _lossless_pools(fmt, seed + 5, NB, Hkv, bs, D)
+        quant = (fmt, 0.125, 0.5)
+        ref = A.paged_decode(q, k8, v8, tables, ctx, 0.2, "f16", quant=quant)
+        for s in range(S):
+            for h in range(H):
+                row = A.decode_one(q[s], k8, v8, tables[s], ctx[s], h, H, 0.2, "f16", quant=quant)
+                assert np.array_equal(row, ref[s, h]), f"{fmt} seq {s} head {h}"
+
+
+ROW_PINS = [check_kv_head_mapping, check_decode_one_rows, check_decode_one_masked_and_8bit]
+
+
 def check_p4_gather_demo():
     """Table [3, 7, 12, 21] with 50 valid tokens: 4 blocks, the last holds 2 rows (12% full)."""
     g = golden("block_counts.json")
@@ -686,6 +759,33 @@ def check_swap_round_trip(seed=81):
         assert _logical(al, pools, s) == before[s]
     assert al.tables[1][:2] == al.tables[2][:2] and al.ref_count(al.tables[1][0]) == 2
     assert al.ref_count(al.tables[4][0]) == 1 and al.tables[4][0] != al.tables[3][0]
+
+
+def check_swap_blocks(seed=83):
+    """The pool-to-pool copy: swapping a group out to a host pool and back into other device
+    blocks returns each sequence's logical contents unchanged; blocks no pair names keep their
+    bytes; between two halves of one pool it is the in-pool block copy."""
+    rng = np.random.default_rng(seed)
+    NB, NH, Hkv, bs, D = 12, 6, 2, 16, 8
+    kc = normal_host((NB, Hkv, bs, D), seed, "f16")
+    vc = normal_host((NB, Hkv, D, bs), seed + 1, "f16")
+    hk = np.zeros((NH, Hkv, bs, D), np.float16)
+    hv = np.zeros((NH, Hkv, D, bs), np.float16)
+    out_pairs = [(3, 0), (7, 4), (11, 2)]
+    hk2, hv2 = C.swap_blocks(hk, hv, kc, vc, out_pairs)
+    for d, h in out_pairs:
+        assert np.array_equal(hk2[h], kc[d]) and np.array_equal(hv2[h], vc[d])
+    for h in (1, 3, 5):
+        assert not hk2[h].any() and not hv2[h].any()
+    in_pairs = [(0, 9), (4, 1), (2, 5)]
+    kc2, vc2 = C.swap_blocks(np.zeros_like(kc), np.zeros_like(vc), hk2, hv2, in_pairs)
+    moved = {3: 9, 7: 1, 11: 5}
+    for d0, d1 in moved.items():
+        assert np.array_equal(kc2[d1], kc[d0]) and np.array_equal(vc2[d1], vc[d0])
+    pairs = [(int(a), int(b)) for a, b in zip(rng.permutation(6), rng.permutation(6) + 6)]
+    ek, ev = C.copy_blocks(kc, vc, pairs)
+    gk, gv = C.swap_blocks(kc, vc, kc.copy(), vc.copy(), pairs)
+    assert np.array_equal(gk, ek) and np.array_equal(gv, ev)
 
 
 def check_window_release():

@@ -109,3 +109,8 @@ def test_mask_pin(pin):
 @pytest.mark.parametrize("pin", P.MULTI_PINS, ids=[p.__name__ for p in P.MULTI_PINS])
 def test_multi_pin(pin):
     pin()
+
+
+@pytest.mark.parametrize("pin", P.ROW_PINS, ids=[p.__name__ for p in P.ROW_PINS])
+def test_row_pin(pin):
+    pin()

@@ -105,6 +105,40 @@ def test_split_mutant_is_caught(monkeypatch, name, bad):
     assert _caught([P.check_split_merge])
 
 
+def _kv_head_modulo(head, num_heads, num_kv_heads):
+    # interleaved groups instead of contiguous ones
+    return head % num_kv_heads
+
+
+def _kv_head_off_by_one(head, num_heads, num_kv_heads):
+    return min(num_kv_heads - 1, (head + 1) // (num_heads // num_kv_heads))
+
+
+def _decode_one_group_mod(query, kc, vc, row, n, head, num_heads, scale, dtype, quant=None, mask=None):
+    # the row of the right query head, but its KV head taken as head % H_kv
+    g = head % kc.shape[1]
+    K, V = A.kv_for(kc, vc, row, n, g, dtype, quant, mask)
+    return A.attend(A.to_f64(query[head], dtype), K, V, A.scale_f64(scale))
+
+
+def _decode_one_head_zero(query, kc, vc, row, n, head, num_heads, scale, dtype, quant=None, mask=None,
+                          _orig=A.decode_one):
+    # always the sequence's first query head
+    return _orig(query, kc, vc, row, n, 0, num_heads, scale, dtype, quant, mask)
+
+
+@pytest.mark.parametrize("name,bad", [("kv_head_of", _kv_head_modulo), ("kv_head_of", _kv_head_off_by_one),
+                                      ("decode_one", _decode_one_group_mod),
+                                      ("decode_one", _decode_one_head_zero)],
+                         ids=["kv_head_of:modulo", "kv_head_of:off_by_one", "decode_one:group_mod",
+                              "decode_one:head_zero"])
+def test_row_mutant_is_caught(monkeypatch, name, bad):
+    """A wrong head-to-group mapping, in the shared mapping or in decode_one alone, and a
+    decode_one that answers for the wrong query head, each fail a pin."""
+    monkeypatch.setattr(A, name, bad)
+    assert _caught(ATTENTION_PINS + P.ROW_PINS), f"no pin caught the planted mistake in {name}"
+
+
 class _LifoAllocator(AL.BlockAllocator):
     def _take(self):
         if not self.free:
