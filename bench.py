@@ -52,7 +52,7 @@ TIMING_SETS = 4     # event sets reused round robin by the steps that time the d
 assert EVENT_EVERY <= STAGING_BUFFERS - 1
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -78,6 +78,14 @@ def parse():
     ap.add_argument("--time-every", type=int, default=4,
                     help="time the decode on every k-th timed step (the first one included), by events "
                          "attached to the kernels (pa_set_launch_events)")
+    ap.add_argument("--decode-reps", type=int, default=50,
+                    help="after the timed steps, time this many decodes of the last step's inputs each way: "
+                         "after an untimed scratch copy that flushes the caches, and back to back (median, p10, "
+                         "p90; the flushed median sets the roofline figure)")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="HBM traffic of the untimed cache flush before each flushed decode, in MiB (half read, "
+                         "half written by one pa_copy_blocks launch over a scratch pool; at least 512 MiB written "
+                         "is twice the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -91,7 +99,20 @@ def parse():
     ap.add_argument("--summarize-profile", metavar="OUTDIR",
                     help="read the rocprofv3 CSVs those commands wrote, print a markdown summary and record the "
                          "decode kernel's HBM bytes per launch in profiles/decode_traffic.json (no GPU needed)")
-    return ap.parse_args()
+    args = ap.parse_args(argv)
+    if args.decode_reps < 1:
+        ap.error("--decode-reps must be at least 1")
+    if args.flush_mib < 2:
+        ap.error("--flush-mib must be at least 2")
+    return args
+
+
+def percentiles(values):
+    """Median, 10th and 90th percentile (linear interpolation) and the sample count."""
+    import numpy as np
+    v = np.asarray(values, dtype=np.float64)
+    return {"median": float(np.median(v)), "p10": float(np.percentile(v, 10)),
+            "p90": float(np.percentile(v, 90)), "n": int(v.size)}
 
 
 def calibrate_copy(launches: int = 10):
@@ -154,7 +175,8 @@ def measure_swap(launches: int = 10):
 # rocprofv3: kernel trace + HBM counters of the decode kernel, scaled by the same
 # counters read on a plain copy of known size (pa_copy_blocks moving 1 GiB).
 
-PROFILE_STEPS = {"trace": (20, 5), "counters": (3, 2)}  # (steps, warmup)
+PROFILE_STEPS = {"trace": (20, 5, 50), "counters": (3, 2, 5)}  # (steps, warmup, decode reps)
+REP_WARM = 5  # untimed repetitions before each timed set in Bench.kernel_timing
 
 
 def default_path(workload: int, path: str | None) -> str:
@@ -167,13 +189,13 @@ def default_path(workload: int, path: str | None) -> str:
 def profile_commands(workload: int, outdir: str, path: str | None) -> list[str]:
     bench = f"python3 {os.path.join(ROOT, 'bench.py')}"
     sel = f" --workload {workload}" + (f" --path {path}" if path else "") + " --no-cpu-baseline"
-    ts, tw = PROFILE_STEPS["trace"]
-    cs, cw = PROFILE_STEPS["counters"]
+    ts, tw, tr = PROFILE_STEPS["trace"]
+    cs, cw, cr = PROFILE_STEPS["counters"]
     cmds = [f"rocprofv3 --kernel-trace --stats -f csv -d {outdir}/trace -o run -- "
-            f"{bench}{sel} --steps {ts} --warmup {tw}"]
+            f"{bench}{sel} --steps {ts} --warmup {tw} --decode-reps {tr}"]
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
         cmds.append(f"rocprofv3 --pmc {ctr} -f csv -d {outdir}/{ctr.lower()} -o run -- "
-                    f"{bench}{sel} --steps {cs} --warmup {cw}")
+                    f"{bench}{sel} --steps {cs} --warmup {cw} --decode-reps {cr}")
         cmds.append(f"rocprofv3 --pmc {ctr} -f csv -d {outdir}/copy_{ctr.lower()} -o run -- "
                     f"{bench} --calibrate-copy")
     return cmds
@@ -224,6 +246,19 @@ def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
     if per_call == 2 and len(dec) < 2:
         raise SystemExit("the shared-prefix path's two decode launches are not both in the trace")
     dec_avg_ns = sum(float(r["averagens"]) for r in dec[:per_call])
+    # per-dispatch durations of the decode kernel, in dispatch order: the step loop's decodes,
+    # then the flushed repetitions, then the back-to-back ones (each set after REP_WARM untimed)
+    trace = [r for r in _csv_rows(os.path.join(outdir, "trace"), "kernel_trace.csv") if decode in r["kernel_name"]]
+    trace.sort(key=lambda r: int(r["dispatch_id"]))
+    durs = [(int(r["end_timestamp"]) - int(r["start_timestamp"])) / 1e3 for r in trace]
+    calls = [sum(durs[i:i + per_call]) for i in range(0, len(durs) - per_call + 1, per_call)]
+    ts, tw, tr = PROFILE_STEPS["trace"]
+    if len(calls) != ts + tw + 2 * (tr + REP_WARM):
+        raise SystemExit(f"{len(calls)} decode calls in the trace, expected {ts + tw + 2 * (tr + REP_WARM)}")
+    a = ts + tw
+    phases = {"pipelined (timed steps)": calls[tw:a],
+              "flushed": calls[a + REP_WARM:a + REP_WARM + tr],
+              "back to back": calls[a + 2 * REP_WARM + tr:]}
     copy_bytes = 8192 // 2 * 32 * 16 * 128 * 2 * 2   # calibrate_copy: read (= written) per launch
     scale, meas = {}, {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -241,7 +276,8 @@ def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
     rec[key] = {"bytes_per_launch": traffic, "source_digest": source_digest(),
                 "fetch_kib_per_dispatch": meas["FETCH_SIZE"][0], "write_kib_per_dispatch": meas["WRITE_SIZE"][0],
                 "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"],
-                "rocprof_decode_avg_us": dec_avg_ns / 1e3}
+                "rocprof_decode_avg_us": dec_avg_ns / 1e3,
+                "rocprof_decode_flushed_median_us": percentiles(phases["flushed"])["median"]}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w", encoding="utf-8") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
@@ -259,6 +295,12 @@ def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
         name = r["name"] if len(r["name"]) < 90 else r["name"][:87] + "..."
         out.append(f"| `{name}` | {r['calls']} | {float(r['averagens']) / 1e3:.2f} | "
                    f"{float(r['minns']) / 1e3:.2f} | {float(r['maxns']) / 1e3:.2f} | {float(r['percentage']):.1f} |")
+    out += ["", "Decode " + ("call (both launches)" if per_call == 2 else "kernel") +
+            " duration per dispatch in the trace, by phase of the run:", "",
+            "| phase | dispatches | median us | p10 us | p90 us |", "|---|---|---|---|---|"]
+    for name, v in phases.items():
+        st = percentiles(v)
+        out.append(f"| {name} | {st['n']} | {st['median']:.2f} | {st['p10']:.2f} | {st['p90']:.2f} |")
     out += ["", "## HBM counters (--pmc, one counter per run, KiB per dispatch)", "",
             "| counter | decode kernel" + (" (both launches of a call)" if per_call == 2 else "") +
             " | " + ("calls" if per_call == 2 else "dispatches") + " | copy kernel (1 GiB each way) | dispatches | scale |",
@@ -491,6 +533,25 @@ class Bench:
             pa.pa_reshape_and_cache(self.newk[r], self.newv[r], self.kc, self.vc, b["slots_d"])
         if instrument:
             pa.pa_set_launch_events(e_start, e_end)
+        self.last = (b, groups, order, r)
+        self.decode(b, groups, order, r)
+        if k % EVENT_EVERY == 0:
+            self.events[k] = self.torch.cuda.Event()
+            self.events[k].record(self.stream)
+        for j in [j for j in self.events if j < k - STAGING_BUFFERS]:
+            del self.events[j]
+        entry = None
+        if timing is not None:
+            lens = b["len_h"].numpy()
+            entry = [None, int(lens.sum()), int(((lens + w.block_size - 1) // w.block_size).sum()), npairs]
+            timing.append(entry)
+        if instrument:
+            self.pool_owner[slot] = entry  # None for a warm-up step: its result is dropped
+
+    def decode(self, b, groups, order, r):
+        """The step's decode call over the index data in staging buffer b."""
+        pa, w = self.pa, self.w
+        fused = self.path == "auto" and self.args.fused_write
         if self.L > 1:
             self.path_ran.add(pa.pa_decode_multi(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"],
                                                  self.qstart, self.L, self.max_ctx, w.scale,
@@ -524,18 +585,43 @@ class Bench:
             self.path_ran.add(pa.pa_decode_auto(self.out, self.q, self.kc, self.vc, b["tab_d"], b["len_d"],
                                                 self.max_ctx, w.scale, self.args.partition, self.ws,
                                                 seq_order=order, cached_kv=self.cached))
-        if k % EVENT_EVERY == 0:
-            self.events[k] = self.torch.cuda.Event()
-            self.events[k].record(self.stream)
-        for j in [j for j in self.events if j < k - STAGING_BUFFERS]:
-            del self.events[j]
-        entry = None
-        if timing is not None:
-            lens = b["len_h"].numpy()
-            entry = [None, int(lens.sum()), int(((lens + w.block_size - 1) // w.block_size).sum()), npairs]
-            timing.append(entry)
-        if instrument:
-            self.pool_owner[slot] = entry  # None for a warm-up step: its result is dropped
+
+    def kernel_timing(self, reps: int, flush_mib: int, warm: int = 5):
+        """Decode time of the last step's inputs, repeated: `reps` decodes each preceded by an
+        untimed cache flush (one pa_copy_blocks launch over a scratch pool, flush_mib MiB of
+        HBM traffic, half read and half written), then `reps` back to back.  Each decode is
+        timed by events attached to its own kernels, as in the step loop (the tighter of the
+        end of the kernel before it and the decode's first dispatch, to its last kernel's end).
+        The pools hold no more writes than the last step made (its new tokens are rewritten
+        only by a step), so every repetition computes the same output.  Returns
+        {"flushed": [ms...], "unflushed": [ms...]}."""
+        torch, pa = self.torch, self.pa
+        if self.args.fused_write:
+            raise SystemExit("--fused-write writes inside the decode: the repetitions would not be the same call")
+        blk = 32 * 16 * 128  # elements of one scratch block: 128 KiB in fp16
+        half = max(1, flush_mib * 1024 * 1024 // 2 // (blk * 2 * 2))   # read = written = flush_mib / 2
+        sk = torch.zeros((2 * half, 32, 16, 128), dtype=torch.float16, device=self.dev)
+        sv = torch.zeros((2 * half, 32, 128, 16), dtype=torch.float16, device=self.dev)
+        pairs = torch.stack([torch.arange(half), torch.arange(half, 2 * half)], dim=1).to(torch.int32).to(self.dev)
+        res = {}
+        for mode in ("flushed", "unflushed"):
+            trios = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(reps + warm)]
+            for trio in trios:
+                for ev in trio:
+                    ev.record(self.stream)
+            torch.cuda.synchronize()
+            for e_prev, e_start, e_end in trios:
+                if mode == "flushed":
+                    pa.pa_set_launch_events(None, e_prev)
+                    pa.pa_copy_blocks(sk, sv, pairs)
+                else:
+                    e_prev.record(self.stream)
+                pa.pa_set_launch_events(e_start, e_end)
+                self.decode(*self.last)
+            torch.cuda.synchronize()
+            res[mode] = [min(p.elapsed_time(e), s.elapsed_time(e)) for p, s, e in trios[warm:]]
+        del sk, sv
+        return res
 
     def _resolve(self, slot: int):
         """Store the decode time (ms) of the step that last used event set `slot`."""
@@ -603,9 +689,11 @@ class Bench:
                 el = time.perf_counter() - t0
                 if el >= min_seconds:
                     break
-        return {"value": tokens / el, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+        return {"value": tokens / el, "unit": "KV tokens/s", "cores": 1, "host_cores": len(os.sched_getaffinity(0)),
+                "kind": "oracle",
                 "sample": f"float64 NumPy oracle, whole decode step ({w.num_seqs} seqs x {w.num_heads} heads, "
-                          f"{int(lens.sum())} KV tokens) repeated {passes}x in {el:.1f} s, 1 BLAS thread"}
+                          f"{int(lens.sum())} KV tokens) repeated {passes}x in {el:.1f} s on one thread (1 BLAS "
+                          f"thread) of the {len(os.sched_getaffinity(0))} host cores this process may use"}
 
 
 def main():
@@ -632,19 +720,25 @@ def main():
         return
     bench = Bench(args)
     wall, timing = bench.run()
+    reps = bench.kernel_timing(args.decode_reps, args.flush_mib)
     w = bench.w
     e = bench.elem
     timed = [t for t in timing if t[0] is not None]  # the steps whose decode was timed
-    durs = [t[0] * 1e-3 for t in timed]  # seconds
     kv_tokens = sum(t[1] for t in timing)
     kv_bytes_token = 2 * w.num_kv_heads * w.head_dim * bench.kv_elem
     qo_bytes = 2 * w.num_seqs * w.query_len * w.num_heads * w.head_dim * e
-    # the fused call also reads the step's new K/V rows and writes them into the pools
-    fused_write = 2 * w.num_seqs * kv_bytes_token if (bench.path == "auto" and args.fused_write) else 0
-    alg_bytes = [t[1] * kv_bytes_token + qo_bytes + 4 * t[2] + 4 * w.num_seqs + fused_write for t in timed]
-    avg_dur = sum(durs) / len(durs)
-    avg_bytes = sum(alg_bytes) / len(alg_bytes)
-    achieved = avg_bytes / avg_dur / 1e9
+
+    def alg_bytes(t):
+        """Algorithmic bytes of one decode: every valid KV element once, q and out, the table
+        entries read and the context lengths."""
+        return t[1] * kv_bytes_token + qo_bytes + 4 * t[2] + 4 * w.num_seqs
+
+    # the repetitions run the last step's decode: its bytes over the flushed median
+    last_bytes = alg_bytes(timing[-1])
+    stats = {"flushed": percentiles(reps["flushed"]), "unflushed": percentiles(reps["unflushed"]),
+             "pipelined": percentiles([t[0] for t in timed])}
+    med_s = stats["flushed"]["median"] * 1e-3
+    achieved = last_bytes / med_s / 1e9
     traffic = measured_traffic(args.workload, "+".join(sorted(bench.path_ran)))
     res = {
         "metric": "paged decode attention: KV GB/s achieved (% of HBM peak) and KV tokens/s",
@@ -666,15 +760,21 @@ def main():
                    "context_lens": "per workload definition, +1 token per step",
                    "mean_kv_tokens_per_step": kv_tokens / len(timing),
                    "decode_path": ("auto: " if bench.path == "auto" else "") + "+".join(sorted(bench.path_ran)),
-                   "kv_write": "fused into the decode (pa_decode_append)" if fused_write
+                   "kv_write": "fused into the decode (pa_decode_append)" if args.fused_write
                    else ("upload and write in one launch (pa_upload_and_cache) when the step has no "
                          "copy-on-write pair, else pa_upload, pa_copy_blocks, write"
                          if not args.separate_upload else "pa_upload, then the write (two launches)"),
                    "partition_size": args.partition if "split" in bench.path_ran else None,
                    "launch_order": bench.order, "kv_cache_policy": "cached" if bench.cached else "stream",
                    "cow_pairs_per_step": sum(t[3] for t in timing) / len(timing)},
-        "decode_kernel_us": avg_dur * 1e6,
-        "decode_timed_steps": len(timed),
+        "decode_kernel_us": stats["flushed"]["median"] * 1e3,
+        "decode_us": {k: {q: (v * 1e3 if q != "n" else v) for q, v in st.items()} for k, st in stats.items()},
+        "decode_timing": (f"median, p10, p90 of HIP events attached to the decode's kernels: 'flushed' = "
+                          f"{args.decode_reps} decodes of the last step's inputs, each after an untimed "
+                          f"{args.flush_mib} MiB scratch copy (half read, half written); 'unflushed' = the same "
+                          f"decodes back to back; 'pipelined' = the decodes timed inside the step loop (every "
+                          f"{max(1, args.time_every)}th step)"),
+        "decode_alg_bytes": last_bytes,
         "kv_gbps_step": kv_tokens * kv_bytes_token / wall / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS,

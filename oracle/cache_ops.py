@@ -10,6 +10,10 @@
   every row, is copied to the destination block ("PagedAttention 实现细节"
   §3.3: copy the full contents of the original block to the new one).  Pairs
   are applied in list order.
+* Block swap between the device pool and a host pool: the same whole-block copy,
+  from block src of one pool pair to block dst of another (the CPU-side cache of
+  "PagedAttention 实现细节" §3.4's cache engine, swapping blocks out to host
+  memory and back).
 
 Pools: key_cache [NB, H_kv, bs, D] (token rows), value_cache [NB, H_kv, D, bs]
 (block size innermost, "Ascend C算子开发高阶实战…" §3.1/§5.2), so a token's
@@ -56,3 +60,14 @@ def copy_blocks(key_cache, value_cache, pairs):
         kc[dst] = kc[src]
         vc[dst] = vc[src]
     return kc, vc
+
+
+def swap_blocks(dst_key, dst_value, src_key, src_value, pairs):
+    """Return copies of the destination pools after copying block src of the source pools to
+    block dst of the destination pools, for each (src, dst) pair in list order."""
+    kd = np.array(dst_key, copy=True)
+    vd = np.array(dst_value, copy=True)
+    for src, dst in np.asarray(pairs).reshape(-1, 2).tolist():
+        kd[dst] = src_key[src]
+        vd[dst] = src_value[src]
+    return kd, vd

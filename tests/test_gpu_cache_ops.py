@@ -283,10 +283,11 @@ def test_upload_and_cache_full_size_step(key):
     index block and the new K/V in one pa_upload_and_cache launch (the whole-tile write for the
     32-token-block workloads 3 and 7, element-wise for 2 and 6), then the decode over the
     uploaded tables, longest first.  Every written block equals the oracle's write into its
-    pre-step contents, every other block is unchanged, and sampled outputs over ctx + 1 match
-    the oracle run on the pre-step blocks plus the oracle's write."""
+    pre-step contents, every other block is unchanged, and every output row over ctx + 1
+    matches the oracle run on the pre-step blocks plus the oracle's write."""
     from oracle import attention as A
-    from tests.gpu_helpers import DeviceWorkload, assert_close, out_to_f64, sample_pairs
+    from tests.gpu_helpers import DeviceWorkload, assert_close, fetch_blocks, out_to_f64, renumber, renumber_slots, \
+        used_blocks
     dw = DeviceWorkload(key)
     w = dw.w
     S, bs, MB = w.num_seqs, w.block_size, dw.max_blocks
@@ -340,16 +341,11 @@ def test_upload_and_cache_full_size_step(key):
     assert torch.equal(dw.key_cache[rest], kc0[rest]) and torch.equal(dw.value_cache[rest], vc0[rest])
 
     out = out_to_f64(dw.out, w.dtype)
-    G = w.num_heads // w.num_kv_heads
     quant = (w.kv_format, w.k_scale, w.v_scale) if fmt else None
-    for s, h in sample_pairs(w, 16, key):
-        n = lens[s]
-        table = tabs[s][:-(-n // bs)]
-        g = h // G
-        kb, vb = fetch(kc0, table, g), fetch(vc0, table, g)
-        at = np.array([table.index(slots[s] // bs) * bs + slots[s] % bs], dtype=np.int32)
-        kb, vb = write(kb, vb, nk[s:s + 1, g:g + 1], nv[s:s + 1, g:g + 1], at)
-        q = synth.to_numpy(dw.query[s, h:h + 1], w.dtype)
-        ref = A.decode_one(q, kb, vb, np.arange(len(table), dtype=np.int32), n, 0, 1, w.scale, w.dtype,
-                           quant=quant)
-        assert_close(out[s, h], ref, w.dtype, f"seq {s} head {h}")
+    used = used_blocks(tabs, lens, bs)
+    kb = fetch_blocks(kc0, used, w.dtype, bool(fmt))
+    vb = fetch_blocks(vc0, used, w.dtype, bool(fmt))
+    kb, vb = write(kb, vb, nk, nv, renumber_slots(used, slots, bs))
+    q = synth.to_numpy(dw.query, w.dtype)
+    ref = A.paged_decode(q, kb, vb, renumber(used, tabs), lens, w.scale, w.dtype, quant=quant)
+    assert_close(out, ref, w.dtype, f"workload {key} after pa_upload_and_cache, every row")

@@ -13,7 +13,8 @@ import torch
 import paged_kv_cache_333_amd as pa
 import synth
 from oracle import attention as A
-from tests.gpu_helpers import DeviceWorkload, assert_close, out_to_f64, sample_pairs, scale_for
+from tests.gpu_helpers import (DeviceWorkload, assert_close, out_to_f64, renumber, renumber_slots, scale_for,
+                               used_blocks, fetch_blocks)
 
 pytestmark = pytest.mark.gpu
 
@@ -167,7 +168,7 @@ def test_tiny_fp32_workload_before_and_after_the_write():
     decode runs over {2,17,18,46} including it."""
     dw = DeviceWorkload(1)
     w = dw.w
-    ref = np.stack([np.stack([dw.oracle_row(s, h) for h in range(w.num_heads)]) for s in range(w.num_seqs)])
+    ref = dw.oracle_all()
     pa.pa_decode(dw.out, dw.query, dw.key_cache, dw.value_cache, dw.tables, dw.context_lens,
                  dw.max_context_len, w.scale)
     torch.cuda.synchronize()
@@ -183,14 +184,14 @@ def test_tiny_fp32_workload_before_and_after_the_write():
     pa.pa_decode(dw.out, dw.query, dw.key_cache, dw.value_cache, dw.tables, dw.context_lens,
                  dw.max_context_len, w.scale)
     torch.cuda.synchronize()
-    ref2 = np.stack([np.stack([dw.oracle_row(s, h) for h in range(w.num_heads)]) for s in range(w.num_seqs)])
-    assert_close(out_to_f64(dw.out, w.dtype), ref2, w.dtype, "after write")
+    assert_close(out_to_f64(dw.out, w.dtype), dw.oracle_all(), w.dtype, "after write")
 
 
 @pytest.mark.parametrize("key", [2, 3])
-def test_full_size_workload_sampled(key):
+def test_full_size_workload_every_row(key):
     """Full-size workloads 2 and 3 in the configuration the benchmark times (single pass,
-    longest-first launch order), and through the split path."""
+    longest-first launch order), and through the split path: every output row against the
+    oracle."""
     dw = DeviceWorkload(key)
     w = dw.w
     order = torch.tensor(pa.pa_order_longest_first(w.context_lens), dtype=torch.int32, device="cuda")
@@ -210,15 +211,15 @@ def test_full_size_workload_sampled(key):
     torch.cuda.synchronize()
     assert torch.equal(plain, dw.out), "launch order changed a result"
     split = out_to_f64(split, w.dtype)
-    for s, h in sample_pairs(w, 24, key):
-        ref = dw.oracle_row(s, h)
-        assert_close(out[s, h], ref, w.dtype, f"seq {s} head {h}")
-        assert_close(split[s, h], ref, w.dtype, f"split seq {s} head {h}")
+    ref = dw.oracle_all()
+    assert_close(out, ref, w.dtype, f"workload {key} single pass, every row")
+    assert_close(split, ref, w.dtype, f"workload {key} split 512, every row")
 
 
-def test_long_context_split_workload_sampled():
+def test_long_context_split_workload_every_row():
     """Workload 4: contexts up to 131072 through 512-token partitions and the LSE merge;
-    the partials in the workspace are checked too."""
+    every output row and every (sequence, head)'s partials in the workspace against the
+    oracle."""
     dw = DeviceWorkload(4)
     w = dw.w
     ps = w.partition_size
@@ -234,16 +235,14 @@ def test_long_context_split_workload_sampled():
     m = wsf[: lay["off_l"] // 4][: w.num_seqs * w.num_heads * P].view(w.num_seqs, w.num_heads, P)
     l_ = wsf[lay["off_l"] // 4: lay["off_l"] // 4 + w.num_seqs * w.num_heads * P].view(w.num_seqs, w.num_heads, P)
     o = wsf[lay["off_o"] // 4:].view(w.num_seqs, w.num_heads, P, w.head_dim)
-    for s, h in sample_pairs(w, 6, 4):
-        assert_close(out[s, h], dw.oracle_row(s, h), w.dtype, f"seq {s} head {h}")
-        rm, rl, ro = dw.oracle_partials(s, h, ps)
+    assert_close(out, dw.oracle_all(), w.dtype, "workload 4 split 512, every row")
+    gm_all, gl_all, go_all = m.double().cpu().numpy(), l_.double().cpu().numpy(), o.double().cpu().numpy()
+    for (s, h), (rm, rl, ro) in dw.oracle_partials_all(ps).items():
         np_ = rm.shape[0]
-        gm = m[s, h, :np_].double().cpu().numpy()
-        gl = l_[s, h, :np_].double().cpu().numpy()
-        go = o[s, h, :np_].double().cpu().numpy()
-        assert np.max(np.abs(gm - rm)) <= 1e-4 * max(1.0, np.max(np.abs(rm)))
-        assert np.max(np.abs(gl - rl) / rl) <= 1e-4
-        assert np.max(np.abs(go - ro)) <= 2e-3
+        gm, gl, go = gm_all[s, h, :np_], gl_all[s, h, :np_], go_all[s, h, :np_]
+        assert np.max(np.abs(gm - rm)) <= 1e-4 * max(1.0, np.max(np.abs(rm))), f"m seq {s} head {h}"
+        assert np.max(np.abs(gl - rl) / rl) <= 1e-4, f"l seq {s} head {h}"
+        assert np.max(np.abs(go - ro)) <= 2e-3, f"o seq {s} head {h}"
 
 
 def test_lse_reduce_alone_on_oracle_partials():
@@ -367,16 +366,20 @@ def test_max_context_single_sequence_long():
 
 
 def test_parallel_sampling_decode_after_cow_step():
-    """Workload 5: one full step (copy-on-write copies, new-token writes, decode over ctx+1).
-    The oracle applies its own copy/write to host copies of the original pools and decodes
-    from those, so no oracle input comes from the device kernels."""
+    """Workload 5: one full step (copy-on-write copies, new-token writes, plain decode over
+    ctx+1), every output row against the oracle.  The oracle applies its own copy/write to
+    host copies of the pre-step blocks and decodes from those, so no oracle input comes from
+    the device kernels."""
     from oracle import cache_ops as OC
     dw = DeviceWorkload(5)
     w = dw.w
-    kc0, vc0 = synth.to_numpy(dw.key_cache, w.dtype), synth.to_numpy(dw.value_cache, w.dtype)
     slots, pairs = dw.alloc.seq_append_slots(dw.seq_ids)
     assert dw.ora.seq_append_slots(dw.seq_ids) == (slots, pairs)
-    dw.refresh_tables()
+    assert len(pairs) > 0
+    tabs, lens = dw.refresh_tables()
+    used = used_blocks(tabs, lens, w.block_size, [b for p in pairs for b in p])
+    kc0 = fetch_blocks(dw.key_cache, used, w.dtype, False)
+    vc0 = fetch_blocks(dw.value_cache, used, w.dtype, False)
     key = synth.normal_device((w.num_seqs, w.num_kv_heads, w.head_dim), dw.seeds["new_key"], w.dtype)
     val = synth.normal_device((w.num_seqs, w.num_kv_heads, w.head_dim), dw.seeds["new_value"], w.dtype)
     kh, vh = synth.to_numpy(key, w.dtype), synth.to_numpy(val, w.dtype)
@@ -386,19 +389,11 @@ def test_parallel_sampling_decode_after_cow_step():
                  dw.max_context_len, w.scale, cached_kv=True)
     torch.cuda.synchronize()
     out = out_to_f64(dw.out, w.dtype)
-    kc1, vc1 = OC.copy_blocks(kc0, vc0, np.array(pairs))
-    kc1, vc1 = OC.reshape_and_cache(kh, vh, kc1, vc1, np.array(slots))
+    kc1, vc1 = OC.copy_blocks(kc0, vc0, renumber(used, np.array(pairs).reshape(-1)).reshape(-1, 2))
+    kc1, vc1 = OC.reshape_and_cache(kh, vh, kc1, vc1, renumber_slots(used, slots, w.block_size))
     q = synth.to_numpy(dw.query, w.dtype)
-    copied = {dst for _, dst in pairs}
-    picks = sample_pairs(w, 12, 5)
-    # make sure a branch that copied its last block is among the checked rows
-    for s in dw.seq_ids:
-        if dw.ora.tables[s][-1] in copied:
-            picks.append((s, 7))
-            break
-    for s, h in picks:
-        ref = A.decode_one(q[s], kc1, vc1, dw.ora.tables[s], dw.ora.lens[s], h, w.num_heads, w.scale, w.dtype)
-        assert_close(out[s, h], ref, w.dtype, f"seq {s} head {h}")
+    ref = A.paged_decode(q, kc1, vc1, renumber(used, tabs), lens, w.scale, w.dtype)
+    assert_close(out, ref, w.dtype, "workload 5 after copy-on-write, plain decode, every row")
 
 
 def test_auto_picks_split_for_few_long_sequences_and_single_otherwise():

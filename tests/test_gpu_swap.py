@@ -1,15 +1,18 @@
 """GPU parity of swap (pa_swap_blocks between a device pool and a pinned host pool, driven by
 the allocator's swap_out / swap_in pairs) and of the sliding window built by the allocator:
-whole-block copies are bit-exact against the oracle's copy; a group swapped out, its device
-blocks reused and overwritten, and swapped back in decodes bit-identically; a windowed
-sequence whose early blocks were released decodes like the oracle over its window."""
+whole-block copies are bit-exact against the oracle's pool-to-pool copy; a group swapped out,
+its device blocks reused and overwritten, and swapped back in decodes like the oracle on the
+post-swap-in tables (and bit-identically to before); a windowed sequence whose early blocks
+were released decodes like the oracle over its window."""
 import numpy as np
 import pytest
 import torch
 
 import paged_kv_cache_333_amd as pa
 import synth
+from oracle import allocator as AL
 from oracle import attention as A
+from oracle import cache_ops as OC
 from tests.gpu_helpers import assert_close, out_to_f64, scale_for
 
 pytestmark = pytest.mark.gpu
@@ -38,62 +41,90 @@ def test_swap_blocks_bit_exact_both_ways(dt):
     hk, hv = (t.pin_memory() for t in pools(NH, 3))
     out_pairs = np.array([[3, 0], [17, 5], [0, 15], [23, 7]], dtype=np.int32)
     # swap out: device -> host, pairs on the device
+    hk0, hv0 = u8(hk).numpy().copy(), u8(hv).numpy().copy()
     pa.pa_swap_blocks(hk, hv, dk, dv, torch.from_numpy(out_pairs).cuda())
     torch.cuda.synchronize()
-    ref_k, ref_v = hk.clone(), hv.clone()
-    for s, d in out_pairs:
-        ref_k[d], ref_v[d] = dk[s].cpu(), dv[s].cpu()
-    assert torch.equal(u8(hk), u8(ref_k)) and torch.equal(u8(hv), u8(ref_v))
+    ref_k, ref_v = OC.swap_blocks(hk0, hv0, u8(dk.cpu()).numpy(), u8(dv.cpu()).numpy(), out_pairs)
+    assert np.array_equal(u8(hk).numpy(), ref_k) and np.array_equal(u8(hv).numpy(), ref_v)
     # swap in: host -> device, pairs in pinned host memory, after host-side writes
     hk[9] = hk[0]
     hv[9] = hv[0]
     in_pairs = np.array([[9, 1], [5, 2], [7, 20]], dtype=np.int32)
-    before_k, before_v = dk.cpu(), dv.cpu()
+    before_k, before_v = u8(dk.cpu()).numpy().copy(), u8(dv.cpu()).numpy().copy()
     pa.pa_swap_blocks(dk, dv, hk, hv, torch.from_numpy(in_pairs).pin_memory())
     torch.cuda.synchronize()
-    ek, ev = before_k.clone(), before_v.clone()
-    for s, d in in_pairs:
-        ek[d], ev[d] = hk[s], hv[s]
-    assert torch.equal(u8(dk.cpu()), u8(ek)) and torch.equal(u8(dv.cpu()), u8(ev))
+    ek, ev = OC.swap_blocks(before_k, before_v, u8(hk).numpy(), u8(hv).numpy(), in_pairs)
+    assert np.array_equal(u8(dk.cpu()).numpy(), ek) and np.array_equal(u8(dv.cpu()).numpy(), ev)
 
 
-def test_swap_out_reuse_swap_in_decodes_identically():
-    """A group of three sequences (two sharing blocks through a fork) is swapped out, its
-    device blocks are reused by another sequence and overwritten with NaN, then the group
-    is swapped back into other blocks: the decode is bit-identical to the one before."""
+def test_swap_out_reuse_swap_in_matches_oracle():
+    """A group of three sequences (two sharing blocks through a fork; the child's append copies
+    the shared last block and writes its token) is swapped out, its device blocks are reused by
+    another sequence and overwritten with NaN, then swapped back into other blocks.  The oracle
+    runs the same allocator operations and applies every copy, write, overwrite and swap to
+    host copies of the pools: the decode after swap-in equals the oracle's decode on the
+    post-swap-in tables, and is bit-identical to the decode before the swap."""
     NB, NH, H, Hkv, bs, D, dt = 64, 40, 8, 2, 16, 128, "bf16"
-    al = pa.Allocator(NB, bs, np.random.default_rng(4).permutation(NB))
-    al.set_host_pool(NH)
-    al.seq_create(1, 70)
-    al.seq_fork(1, 2, 60)
-    al.seq_append_slot(2)
-    al.seq_create(3, 33)
+    order = np.random.default_rng(4).permutation(NB)
+    al = pa.Allocator(NB, bs, order)
+    ora = AL.BlockAllocator(NB, bs, order)
+    for a in (al, ora):
+        a.set_host_pool(NH)
+        a.seq_create(1, 70)
+        a.seq_fork(1, 2, 60)
+    slot, src, dst = al.seq_append_slot(2)
+    assert (slot, src, dst) == ora.seq_append_slot(2) and src >= 0   # the shared last block is copied
+    for a in (al, ora):
+        a.seq_create(3, 33)
     ids = [1, 2, 3]
-    kc = synth.to_torch(synth.normal_host((NB, Hkv, bs, D), 5, dt), dt).cuda()
-    vc = synth.to_torch(synth.normal_host((NB, Hkv, D, bs), 6, dt), dt).cuda()
-    q = synth.to_torch(synth.normal_host((3, H, D), 7, dt), dt).cuda()
-    hk = torch.empty((NH, Hkv, bs, D), dtype=kc.dtype).pin_memory()
-    hv = torch.empty((NH, Hkv, D, bs), dtype=kc.dtype).pin_memory()
+    kc_h = synth.normal_host((NB, Hkv, bs, D), 5, dt)
+    vc_h = synth.normal_host((NB, Hkv, D, bs), 6, dt)
+    q_h = synth.normal_host((3, H, D), 7, dt)
+    nk = synth.normal_host((1, Hkv, D), 8, dt)
+    nv = synth.normal_host((1, Hkv, D), 9, dt)
+    kc, vc = synth.to_torch(kc_h, dt).cuda(), synth.to_torch(vc_h, dt).cuda()
+    q = synth.to_torch(q_h, dt).cuda()
+    pa.pa_copy_blocks(kc, vc, torch.tensor([[src, dst]], dtype=torch.int32).cuda())
+    pa.pa_reshape_and_cache(synth.to_torch(nk, dt).cuda(), synth.to_torch(nv, dt).cuda(), kc, vc,
+                            torch.tensor([slot], dtype=torch.int32).cuda())
+    okc, ovc = OC.copy_blocks(kc_h, vc_h, [(src, dst)])
+    okc, ovc = OC.reshape_and_cache(nk, nv, okc, ovc, [slot])
+    hk = torch.zeros((NH, Hkv, bs, D), dtype=kc.dtype).pin_memory()
+    hv = torch.zeros((NH, Hkv, D, bs), dtype=kc.dtype).pin_memory()
+    ohk, ohv = synth.to_numpy(hk, dt), synth.to_numpy(hv, dt)
 
     def decode():
         tabs, lens = al.build_block_tables(ids, 8)
+        assert (tabs, lens) == ora.build_block_tables(ids, 8)
         out = torch.empty_like(q)
         pa.pa_decode(out, q, kc, vc, torch.tensor(tabs, dtype=torch.int32).cuda(),
                      torch.tensor(lens, dtype=torch.int32).cuda(), 8 * bs, scale_for(D))
         torch.cuda.synchronize()
-        return out_to_f64(out, dt)
+        ref = A.paged_decode(q_h, okc, ovc, np.array(tabs), lens, scale_for(D), dt)
+        got = out_to_f64(out, dt)
+        assert_close(got, ref, dt, "swap round trip")
+        return got
 
     before = decode()
     pairs = al.seq_swap_out(ids)
+    assert pairs == ora.seq_swap_out(ids)
     pa.pa_swap_blocks(hk, hv, kc, vc, torch.tensor(pairs, dtype=torch.int32).cuda())
-    torch.cuda.synchronize()
-    al.seq_create(9, bs * al.num_free_blocks())       # takes every free device block
-    t9 = torch.tensor(al.block_table(9), dtype=torch.long).cuda()
-    kc[t9] = float("nan")
-    vc[t9] = float("nan")
-    al.seq_free(9)
+    ohk, ohv = OC.swap_blocks(ohk, ohv, okc, ovc, pairs)
+    for a in (al, ora):
+        a.seq_create(9, bs * a.num_free_blocks())       # takes every free device block
+    assert al.block_table(9) == ora.block_table(9)
+    t9 = al.block_table(9)
+    kc[torch.tensor(t9, dtype=torch.long).cuda()] = float("nan")
+    vc[torch.tensor(t9, dtype=torch.long).cuda()] = float("nan")
+    nan = np.uint16(0x7FC0)
+    okc[t9] = nan
+    ovc[t9] = nan
+    for a in (al, ora):
+        a.seq_free(9)
     pairs = al.seq_swap_in(ids)
+    assert pairs == ora.seq_swap_in(ids)
     pa.pa_swap_blocks(kc, vc, hk, hv, torch.tensor(pairs, dtype=torch.int32).cuda())
+    okc, ovc = OC.swap_blocks(okc, ovc, ohk, ohv, pairs)
     torch.cuda.synchronize()
     assert np.array_equal(decode(), before)
 

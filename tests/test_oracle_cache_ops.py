@@ -1,5 +1,6 @@
 """CPU pins of the pool-writing oracles: slot-mapping scatter and whole-block copy."""
 import numpy as np
+import pytest
 
 from oracle import cache_ops as C
 from tests import oracle_pins as P
@@ -46,3 +47,24 @@ def test_copy_blocks_hand_example():
 
 def test_cow_timeline_from_impl_page():
     P.check_p4_cow_timeline()
+
+
+def test_swap_blocks_pin():
+    P.check_swap_blocks()
+
+
+def test_swap_blocks_mutants_are_caught(monkeypatch):
+    """A swap that copies only the keys, or applies the pairs reversed, fails the pin."""
+    from oracle import cache_ops as C
+
+    def keys_only(dk, dv, sk, sv, pairs, _orig=C.swap_blocks):
+        kd, _ = _orig(dk, dv, sk, sv, pairs)
+        return kd, np.array(dv, copy=True)
+
+    def reversed_pairs(dk, dv, sk, sv, pairs, _orig=C.swap_blocks):
+        return _orig(dk, dv, sk, sv, [(b, a) for a, b in np.asarray(pairs).reshape(-1, 2).tolist()])
+
+    for bad in (keys_only, reversed_pairs):
+        monkeypatch.setattr(C, "swap_blocks", bad)
+        with pytest.raises((AssertionError, IndexError)):
+            P.check_swap_blocks()
