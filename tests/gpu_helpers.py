@@ -24,11 +24,15 @@ MANT = {"f32": 23, "f16": 10, "bf16": 7}
 
 
 def tolerance(ref: np.ndarray, dtype: str) -> np.ndarray:
-    """max-abs-error bound: the stated tolerance for fp32 accumulation, plus half an ulp of
-    the output type at |ref| for the final rounding of the result to the query dtype."""
+    """max-abs-error bound: 1e-5 for fp32 and 2e-3 for fp16 outputs, as stated; for bf16
+    outputs 2e-3 plus half an ulp of bf16 at |ref|, because rounding the result to bf16 alone
+    moves it by up to 3.9e-3 once |ref| >= 1 (8 significant bits), beyond the stated bound
+    whatever the accumulation does."""
+    if dtype != "bf16":
+        return np.full(np.shape(ref), TOL[dtype])
     mag = np.maximum(np.abs(ref), 2.0 ** -14)
     half_ulp = 0.5 * np.exp2(np.floor(np.log2(mag)) - MANT[dtype])
-    return TOL[dtype] + (half_ulp if dtype != "f32" else 0.0)
+    return TOL[dtype] + half_ulp
 
 
 def log_parity(what: str, dtype: str, err: np.ndarray, tol: np.ndarray):

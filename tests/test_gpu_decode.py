@@ -2,7 +2,7 @@
 against the float64 oracle, plus GPU-side invariants and edge cases.
 
 Tolerance: max abs error 1e-5 for fp32 inputs and 2e-3 for fp16/bf16 inputs (fp32
-accumulation), plus half an ulp of the output type for the final rounding to it
+accumulation); for bf16 outputs plus half a bf16 ulp for the final rounding to it
 (tests/gpu_helpers.py: tolerance)."""
 import zlib
 

@@ -2,10 +2,10 @@
 the quantising slot-mapping write and the block copy (bit-exact codes against the
 oracle), decode over 8-bit pools in every kernel family, single pass and split
 (against the float64 oracle over the values the codes stand for), and the
-full-size 8-bit workloads on sampled outputs.
+full-size 8-bit workloads on every output row.
 
-Tolerance: as for fp16/bf16 decode (tests/gpu_helpers.py: tolerance): 2e-3 plus
-half an ulp of the output type.  The codes are widened exactly, so the only
+Tolerance: as for fp16/bf16 decode (tests/gpu_helpers.py: tolerance): 2e-3, plus
+half a bf16 ulp for bf16 outputs.  The codes are widened exactly, so the only
 differences from the oracle are fp32 accumulation and the rounding of P."""
 import zlib
 
