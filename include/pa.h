@@ -460,6 +460,32 @@ pa_status pa_decode_split(void* out, const void* query, const void* key_cache,
                           float scale, pa_dtype dtype, uint32_t flags, int32_t partition_size,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the library's static split workspace (pa_decode_split_static):
+ * 32 MiB per device, enough for the partials of 4 sequences x 32 heads of
+ * dimension 128 over 131072-token contexts in 512-token partitions. */
+#define PA_STATIC_SCRATCH_BYTES (32u * 1024u * 1024u)
+
+/* pa_decode_split without a workspace argument, for callers that cannot
+ * allocate device memory (work recorded under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the partials go to a
+ * file-scope device array of PA_STATIC_SCRATCH_BYTES owned by the library,
+ * one per device, held from the first call on that device until the process
+ * ends.  The call makes no allocation (no hipMalloc / hipFree, none by a
+ * library routine).  Arguments, results and error behaviour are those of
+ * pa_decode_split; a shape whose partials need more than
+ * PA_STATIC_SCRATCH_BYTES (pa_decode_split_workspace_bytes) returns
+ * PA_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.  Every call on a
+ * device shares that device's array and nothing in it needs clearing (each
+ * partial is written before it is read), so calls on one device that may
+ * overlap in time (different streams, different host threads) race on it:
+ * serialise them, e.g. on one stream. */
+pa_status pa_decode_split_static(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
+                                 int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                 int32_t max_context_len, float scale, pa_dtype dtype, uint32_t flags,
+                                 int32_t partition_size, void* stream);
+
 /* Decode with the path chosen for the launch.  The vLLM notes of [ATB] §2.3
  * keep a second kernel for few, very long requests; here the choice comes
  * from the launch shape instead of the page's length thresholds:

@@ -566,6 +566,41 @@ pa_status pa_decode_split(void* out, const void* query, const void* key_cache, c
   return finish(pa::launch_decode_split(a, ws, st), st, "pa_decode_split");
 }
 
+pa_status pa_decode_split_static(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
+                                 int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                 int32_t max_context_len, float scale, pa_dtype dtype, uint32_t flags,
+                                 int32_t partition_size, void* stream) {
+  pa::DecodeArgs a = pack(out, query, key_cache, value_cache, block_tables, context_lens, seq_order, num_seqs,
+                          num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                          max_context_len, scale, dtype, flags);
+  pa_status s = check_decode_args(a);
+  if (s != PA_OK) return s;
+  if (flags & ~uint32_t(PA_DECODE_CACHED_KV)) return fail(PA_ERR_INVALID_ARG, "unknown flag bits");
+  if (partition_size <= 0 || partition_size % block_size || partition_size > 4096)
+    return fail(PA_ERR_INVALID_ARG, "partition_size must be a multiple of block_size, at most 4096");
+  if (num_seqs == 0) return PA_OK;
+  SplitSizes z;
+  if (!split_sizes(num_seqs, num_heads, head_dim, max_context_len, partition_size, &z))
+    return fail(PA_ERR_INVALID_ARG, "split sizes (at most 65535 partitions)");
+  if (z.total > static_cast<int64_t>(PA_STATIC_SCRATCH_BYTES))
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL,
+                "the partials need " + std::to_string(z.total) + " bytes, the static workspace holds " +
+                    std::to_string(static_cast<int64_t>(PA_STATIC_SCRATCH_BYTES)) +
+                    "; pass a workspace to pa_decode_split instead");
+  void* scratch = nullptr;
+  hipError_t e = pa::static_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "pa_decode_split_static: static workspace lookup");
+  pa::SplitLayout ws;
+  s = make_layout(scratch, PA_STATIC_SCRATCH_BYTES, num_seqs, num_heads, head_dim, max_context_len, partition_size,
+                  &ws);
+  if (s != PA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_mode() && (s = debug_check_tables(a, st)) != PA_OK) return s;
+  return finish(pa::launch_decode_split(a, ws, st), st, "pa_decode_split_static");
+}
+
 pa_status pa_decode_auto(void* out, const void* query, const void* key_cache, const void* value_cache,
                          const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
                          int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,

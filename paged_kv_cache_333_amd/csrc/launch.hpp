@@ -116,6 +116,10 @@ hipError_t multi_pass_shape(const DecodeArgs& a, int32_t max_query_len, int64_t*
 hipError_t launch_decode_shared(const DecodeArgs& a, const int32_t* group_start, int32_t num_groups,
                                 int32_t max_group, const int32_t* prefix_len, const SplitLayout& ws, int32_t* ws_len,
                                 hipStream_t stream);
+// Device address of the library's static split workspace on the current device
+// (PA_STATIC_SCRATCH_BYTES bytes, 256-byte aligned), looked up on the first
+// call per device.
+hipError_t static_scratch(void** ptr);
 hipError_t launch_lse_reduce(void* out, const SplitLayout& ws, const int32_t* context_lens,
                              const int32_t* seq_order, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                              int32_t len_limit, pa_dtype dtype, hipStream_t stream);
