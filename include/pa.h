@@ -27,6 +27,21 @@
  *                   decode kernel's matrix-core products 16-byte operand loads
  *                   along their contraction axes (head_dim for q.K, tokens for
  *                   P.V).
+ *                   This value layout departs from [IMPL] §3.1/§3.4, where both
+ *                   pools hold token rows [num_blocks, num_kv_heads, block_size,
+ *                   head_dim]; it follows the Ascend kernel's value arrangement
+ *                   instead.  Its cost falls on the write: one new token's value
+ *                   is a column, head_dim elements each block_size elements
+ *                   apart, so it touches every 128-byte line of its tile, and
+ *                   the decode that follows pays 8-16 us for rereading those
+ *                   lines at the LLaMA-7B-like shapes (64 sequences x 32 heads).
+ *                   pa_upload_and_cache narrows that with a whole-tile write for
+ *                   32-token blocks and non-temporal stores for 16-token blocks.
+ *
+ * Beyond the pages' problem interface (query, pools, block_tables,
+ * context_lens, scale), the decode calls take two more arguments: seq_order
+ * (an optional launch order of the sequences, longest first to balance the
+ * last wave) and flags (PA_DECODE_CACHED_KV, the K/V cache policy).
  *   block_tables    [num_seqs, max_blocks_per_seq] int32; entry j of row s is
  *                   the physical block of logical block j (tokens j*bs ..
  *                   j*bs+bs-1) of sequence s; unused entries are -1 by
@@ -43,7 +58,9 @@
  *
  * Streams: device calls enqueue work on `stream` (a hipStream_t; NULL is the
  * null stream) and return without synchronising.  The library allocates no
- * device memory; the split path's workspace is passed in by the caller.
+ * device memory; the split path's workspace is passed in by the caller, except
+ * for pa_decode_split_static, whose partials live in a fixed array the library
+ * holds on each device it runs on.
  *
  * Debug mode: with the environment variable PA_DEBUG=1 set when the library
  * is loaded, device calls first copy the index arrays back to the host

@@ -11,17 +11,20 @@ namespace pa {
 
 // True when no two tokens' slots inside the pool fall in one block.  Read on
 // the host from the page-locked slot mapping (final at the call).  O(n) with
-// a per-thread stamp per block for pools of up to stamp_blocks blocks; larger
-// pools sort the call's block ids instead (no allocation that scales with the
-// pool, and nothing that can throw across the C ABI).
-constexpr int32_t kStampBlocks = 1 << 24;
+// a per-thread stamp per block when the pool is small next to the call (at
+// most kStampPerToken blocks per token and stamp_blocks blocks in all, so the
+// kept stamp array is at most 4 MB and scales with the calls, not with the
+// pool); otherwise the call's block ids are sorted (a few hundred ids per
+// decode step).  Nothing here can throw across the C ABI.
+constexpr int32_t kStampBlocks = 1 << 20;
+constexpr int64_t kStampPerToken = 16;
 inline bool one_token_per_block(const int32_t* slots, int32_t n, int32_t num_blocks, int32_t block_size,
                                 int32_t stamp_blocks = kStampBlocks) {
   if (n <= 1) return true;
   const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
   thread_local std::vector<uint32_t> stamp;
   thread_local uint32_t epoch = 0;
-  bool stamps = num_blocks <= stamp_blocks;
+  bool stamps = num_blocks <= stamp_blocks && num_blocks <= kStampPerToken * n;
   if (stamps && stamp.size() < static_cast<size_t>(num_blocks)) {
     try {
       stamp.assign(static_cast<size_t>(num_blocks), 0u);

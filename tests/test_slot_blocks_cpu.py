@@ -1,7 +1,7 @@
 """The host check that picks pa_upload_and_cache's write form: a call's new tokens each
 in a block of their own (slots outside [0, num_blocks * block_size) are skipped, as the
 write skips them).  Both of its paths, the per-block stamp array and the sort used for
-pools above the stamp bound, are compiled into a small CPU harness with g++ and compared
+pools above the stamp bound or with more than 16 blocks per token of the call, are compiled into a small CPU harness with g++ and compared
 with a set-based count on seeded random calls that share one thread, as successive
 library calls do (stamp reuse, pools that grow and shrink between calls)."""
 import pathlib
