@@ -385,7 +385,7 @@ class Bench:
             # the pool is a shape of the workload, sized for its initial contexts: say up front
             # when the run's growth would not fit instead of failing in the middle of it
             fit = steps_that_fit(w.context_lens, bs, w.num_blocks, w.query_len, total_steps)
-            if fit < total_steps:
+            if self.base is None and fit < total_steps:  # workload 1 restarts from its base state
                 raise SystemExit(f"workload {args.workload}'s pool of {w.num_blocks} blocks holds "
                                  f"{fit} steps of growth; --warmup {args.warmup} --steps {args.steps} "
                                  f"asks for {total_steps}")
