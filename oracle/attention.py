@@ -45,7 +45,10 @@ What is computed, and where the pages define it:
   (§6.3) combines with paging; one query token per sequence is plain decode.
 * 8-bit pools (quant = (fmt, k_scale, v_scale)): the pools hold codes and
   stand for decode(code) * scale (oracle/quant.py); the attention over those
-  values is the same definition.
+  values is the same definition.  With quant = ("int8_token", k_scales,
+  v_scales) the pools hold int8 codes and each (token, KV head) row has its
+  own scale: k_scales / v_scales [NB, H_kv, bs] float32, the scale of the row
+  at block b, KV head g, offset o being k_scales[b, g, o].
 
 Inputs are NumPy arrays in storage type: float32, float16, or bf16 given as
 uint16 bit patterns (8-bit pools: uint8 codes).  Everything is upcast exactly
@@ -139,12 +142,32 @@ def gather_positions(key_cache, value_cache, table_row, positions: np.ndarray, k
     return key_cache[phys, kv_head, off, :], value_cache[phys, kv_head, :, off]
 
 
+def gather_row_scales(scale_pool, table_row, positions, kv_head: int) -> np.ndarray:
+    """The per-row scales of the given token positions of one sequence and KV head:
+    position t's row sits at block table_row[t // bs], offset t % bs of scale_pool
+    [NB, H_kv, bs]."""
+    num_blocks, _, block_size = scale_pool.shape
+    positions = np.asarray(positions, dtype=np.int64)
+    phys = np.asarray(table_row, dtype=np.int64)[positions // block_size]
+    if np.any((phys < 0) | (phys >= num_blocks)):
+        raise IndexError("block table entry outside the pool")
+    return scale_pool[phys, kv_head, positions % block_size]
+
+
 def kv_for(key_cache, value_cache, table_row, num_tokens: int, kv_head: int, dtype: str, quant=None,
            mask=None):
     """float64 K, V of one sequence and KV head, one row per position that holds a token:
     all t < num_tokens, or with mask = (lo, hi) those outside [lo, hi) (keep_positions).
     With quant = (fmt, k_scale, v_scale) the pools hold 8-bit codes and stand for
-    decode(code) * scale (oracle/quant.py); otherwise they hold `dtype` values."""
+    decode(code) * scale (oracle/quant.py); with quant = ("int8_token", k_scales,
+    v_scales) each row has its own scale (decode(code) * the row's scale); otherwise they
+    hold `dtype` values."""
+    if quant is not None and quant[0] == Q.INT8_TOKEN:
+        _, k_scales, v_scales = quant
+        pos = np.arange(num_tokens) if mask is None else keep_positions(num_tokens, int(mask[0]), int(mask[1]))
+        K, V = gather_positions(key_cache, value_cache, table_row, pos, kv_head)
+        return (Q.dequantize_rows_int8(K, gather_row_scales(k_scales, table_row, pos, kv_head)),
+                Q.dequantize_rows_int8(V, gather_row_scales(v_scales, table_row, pos, kv_head)))
     if mask is None:
         if quant is None:
             return gather_kv(key_cache, value_cache, table_row, num_tokens, kv_head, dtype)
@@ -183,7 +206,8 @@ def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scal
 
     query [S, H, D]; key_cache [NB, H_kv, bs, D]; value_cache [NB, H_kv, D, bs];
     block_tables [S, MB]; context_lens [S].  Returns float64 [S, H, D].
-    quant = (fmt, k_scale, v_scale) when the pools hold 8-bit codes; masks = (lo, hi)
+    quant = (fmt, k_scale, v_scale) when the pools hold 8-bit codes with per-pool scales,
+    ("int8_token", k_scales, v_scales) for int8 codes with per-row scales; masks = (lo, hi)
     per-sequence lists of masked positions.
     """
     S, H, D = query.shape

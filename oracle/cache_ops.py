@@ -20,7 +20,10 @@ Pools: key_cache [NB, H_kv, bs, D] (token rows), value_cache [NB, H_kv, D, bs]
 value vector is written down column `offset` of its tile.  Arrays are NumPy
 storage arrays (bf16 as uint16 bits), so the results are bit patterns and
 compare bit-exactly.  8-bit pools hold uint8 codes; their write quantises
-first (reshape_and_cache_quant), their block copy is the same byte copy.
+first (reshape_and_cache_quant), their block copy is the same byte copy.  The
+int8 form with a scale per (token, KV head) keeps those scales in arrays
+[NB, H_kv, bs] beside the code pools (reshape_and_cache_int8_token); a block
+copy copies them with the same copy_blocks.
 """
 from __future__ import annotations
 
@@ -50,6 +53,27 @@ def reshape_and_cache_quant(key, value, key_cache, value_cache, slot_mapping, dt
     v_scale), then written exactly like reshape_and_cache."""
     return reshape_and_cache(Q.quantize(key, dtype, k_scale, fmt), Q.quantize(value, dtype, v_scale, fmt),
                              key_cache, value_cache, slot_mapping)
+
+
+def reshape_and_cache_int8_token(key, value, key_cache, value_cache, k_scales, v_scales, slot_mapping,
+                                 dtype: str):
+    """The slot-mapping write into int8 pools with per-(token, KV head) scales: each new
+    key and value row is quantised on its own (oracle/quant.py quantize_rows_int8), its
+    codes written like reshape_and_cache, its scale at k_scales / v_scales [block, KV head,
+    offset].  Returns copies of the four pools."""
+    kcodes, ksc = Q.quantize_rows_int8(key, dtype)
+    vcodes, vsc = Q.quantize_rows_int8(value, dtype)
+    kc, vc = reshape_and_cache(kcodes, vcodes, key_cache, value_cache, slot_mapping)
+    ks = np.array(k_scales, copy=True)
+    vs = np.array(v_scales, copy=True)
+    block_size = ks.shape[2]
+    for i, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        if slot < 0:
+            continue
+        block, offset = divmod(int(slot), block_size)
+        ks[block, :, offset] = ksc[i]
+        vs[block, :, offset] = vsc[i]
+    return kc, vc, ks, vs
 
 
 def copy_blocks(key_cache, value_cache, pairs):

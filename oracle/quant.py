@@ -23,6 +23,14 @@ What they leave open, and the readings taken here:
   (symmetric, so Q(-y) = -Q(y)); NaN becomes 0.  Signed zeros keep their sign
   in E4M3 (0x00 / 0x80).
 
+A second int8 form keeps one scale per (token, KV head) instead of one per
+pool, the per-token form the xdnf.cn article's §2.3/§6.3 name among the
+quantisation choices: each new key row and each new value row of D elements
+gets s = max_d |x_d| / 127 (float32 division) and codes Q(x_d / s), so its
+largest element maps to +-127.  A row of zeros has s = 0 and codes 0.  Rows
+must be finite (a NaN row's codes are not specified).  The cache then stands
+for decode(code) * s of that row.
+
 The E4M3 encoder is a brute-force nearest-value search over the code table,
 built from the format's definition; the int8 encoder is the nearest integer.
 Pools are uint8 arrays holding the codes, with the layouts of the
@@ -33,6 +41,7 @@ from __future__ import annotations
 import numpy as np
 
 FORMATS = ("fp8_e4m3", "int8")
+INT8_TOKEN = "int8_token"  # int8 codes with one float32 scale per (token, KV head)
 E4M3_MAX = 448.0
 INT8_MAX = 127
 
@@ -124,3 +133,21 @@ def quantize(x, dtype: str, scale: float, fmt: str) -> np.ndarray:
 def dequantize(codes, scale: float, fmt: str) -> np.ndarray:
     """float64 values the codes stand for: decode(code) * scale (scale as float32)."""
     return decode(codes, fmt) * float(np.float32(scale))
+
+
+def quantize_rows_int8(x, dtype: str):
+    """Per-row int8: for each row (last axis) s = max |x| / 127 in float32 and codes
+    Q_int8(x / s) (float32 quotient, nearest with ties to even, saturating at +-127); a
+    row of zeros gets s = 0 and codes 0.  Returns (codes uint8 [..., D], scales float32 [...])."""
+    x32 = to_f32(x, dtype)
+    amax = np.max(np.abs(x32), axis=-1)
+    scales = (amax / np.float32(INT8_MAX)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        quot = (x32 / scales[..., None]).astype(np.float32)
+    codes = np.where(scales[..., None] > 0, _int8_encode(quot), np.uint8(0)).astype(np.uint8)
+    return codes, scales
+
+
+def dequantize_rows_int8(codes, scales) -> np.ndarray:
+    """float64 values of per-row int8 codes: decode(code) * s of the row."""
+    return decode(codes, "int8") * np.asarray(scales, dtype=np.float32).astype(np.float64)[..., None]

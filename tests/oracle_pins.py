@@ -553,6 +553,139 @@ QUANT_PINS = [check_e4m3_special_values, check_e4m3_table_vs_torch, check_e4m3_e
               check_e4m3_round_trip, check_e4m3_saturation, check_int8_encode, check_quantize_division,
               check_quant_attention_lossless, check_quant_write_round_trip]
 
+# ----------------------------------------------------------------------------
+# int8 with one scale per (token, KV head)
+
+def check_int8_rows_closed_forms(seed=51):
+    """Per-row int8 codes: the largest |element| of a row maps to +-127 with its sign, every
+    element is within half a code step (s / 2) of code * s, a row of zeros has scale 0 and
+    codes 0, and a row of whole multiples of 2^k whose largest is 127 * 2^k comes back exactly."""
+    from oracle import quant as Q
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((40, 64)) * rng.uniform(0.01, 50, size=(40, 1))).astype(np.float32)
+    codes, sc = Q.quantize_rows_int8(x, "f32")
+    vals = Q.decode(codes, "int8")
+    for r in range(x.shape[0]):
+        j = int(np.argmax(np.abs(x[r])))
+        assert vals[r, j] == (127.0 if x[r, j] > 0 else -127.0), r
+        assert np.max(np.abs(x[r] - vals[r] * float(sc[r]))) <= 0.50001 * float(sc[r]), r
+        assert np.max(np.abs(vals[r])) == 127.0
+    c0, s0 = Q.quantize_rows_int8(np.zeros((3, 8), np.float32), "f32")
+    assert not c0.any() and not s0.any()
+    k = np.array([-7, -3, 0, 2, 5], dtype=np.float64)
+    row = np.concatenate([rng.integers(-126, 127, size=30), [127]]).astype(np.float64)
+    for e in k:
+        xs = (row * 2.0 ** e).astype(np.float32)[None, :]
+        c, s_ = Q.quantize_rows_int8(xs, "f32")
+        assert float(s_[0]) == 2.0 ** e
+        assert np.array_equal(Q.dequantize_rows_int8(c, s_), xs.astype(np.float64))
+    # bf16 and fp16 inputs are widened exactly first
+    xb = np.array([[0x3F80, 0xC000, 0x3E80]], dtype=np.uint16)   # 1, -2, 0.25
+    cb, sb = Q.quantize_rows_int8(xb, "bf16")
+    assert float(sb[0]) == float(np.float32(2.0) / np.float32(127)) and Q.decode(cb, "int8")[0, 1] == -127.0
+
+
+def check_int8_rows_vs_torch(seed=53):
+    """Per-row int8 codes and scales equal torch's float32 amax / 127 and round-half-even of
+    the quotient, clamped to +-127, on normal rows, rows with ties and fp16 rows."""
+    import torch
+    from oracle import quant as Q
+    rng = np.random.default_rng(seed)
+    rows = [rng.standard_normal((50, 128)).astype(np.float32)]
+    tie = np.zeros((4, 16), np.float32)
+    tie[:, 0] = 127.0
+    tie[:, 1:] = np.arange(15, dtype=np.float32) + 0.5        # quotients k + 0.5 exactly
+    rows.append(tie)
+    rows.append(rng.standard_normal((20, 64)).astype(np.float16).astype(np.float32))
+    for x in rows:
+        codes, sc = Q.quantize_rows_int8(x, "f32")
+        t = torch.from_numpy(x)
+        ts = t.abs().amax(dim=-1) / torch.tensor(127.0, dtype=torch.float32)
+        tq = torch.clamp(torch.round(t / ts[:, None]), -127, 127).to(torch.int64)
+        assert np.array_equal(sc, ts.numpy())
+        assert np.array_equal(Q.decode(codes, "int8").astype(np.int64), tq.numpy())
+
+
+def _token_pools(seed, NB, Hkv, bs, D):
+    """int8 code pools and per-row power-of-two scales, and the float32 pools of the values
+    they stand for (exact)."""
+    from oracle import quant as Q
+    rng = np.random.default_rng(seed)
+    kc = rng.integers(0, 256, size=(NB, Hkv, bs, D)).astype(np.uint8)
+    vc = rng.integers(0, 256, size=(NB, Hkv, D, bs)).astype(np.uint8)
+    ks = (2.0 ** rng.integers(-9, -4, size=(NB, Hkv, bs))).astype(np.float32)
+    vs = (2.0 ** rng.integers(-9, -4, size=(NB, Hkv, bs))).astype(np.float32)
+    kf = (Q.decode(kc, "int8") * ks[..., None]).astype(np.float32)
+    vf = (Q.decode(vc, "int8") * vs[:, :, None, :]).astype(np.float32)
+    return kc, vc, ks, vs, kf, vf
+
+
+def check_int8_token_attention_lossless(seed=57):
+    """Attention over int8 pools with a scale per (token, KV head) equals attention over the
+    float32 pools holding exactly code * scale of each row: MHA and GQA, permuted tables,
+    a mask, and every row of decode_one."""
+    from oracle import quant as Q
+    for S, H, Hkv, D, bs in ((3, 8, 2, 32, 16), (2, 4, 4, 64, 32)):
+        NB = 12
+        kc, vc, ks, vs, kf, vf = _token_pools(seed + H, NB, Hkv, bs, D)
+        rng = np.random.default_rng(seed)
+        tables = np.stack([rng.permutation(NB)[:4] for _ in range(S)]).astype(np.int32)
+        ctx = [1, 3 * bs + 5, 4 * bs][:S]
+        q = normal_host((S, H, D), seed + 1, "f32")
+        quant = (Q.INT8_TOKEN, ks, vs)
+        want = A.paged_decode(q, kf, vf, tables, ctx, 0.3, "f32")
+        got = A.paged_decode(q, kc, vc, tables, ctx, 0.3, "f32", quant=quant)
+        assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
+        lo, hi = [0] * S, [min(9, c) for c in ctx]
+        want = A.paged_decode(q, kf, vf, tables, ctx, 0.3, "f32", masks=(lo, hi))
+        got = A.paged_decode(q, kc, vc, tables, ctx, 0.3, "f32", quant=quant, masks=(lo, hi))
+        assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
+        full = A.paged_decode(q, kc, vc, tables, ctx, 0.3, "f32", quant=quant)
+        for s in range(S):
+            for h in range(H):
+                row = A.decode_one(q[s], kc, vc, tables[s], ctx[s], h, H, 0.3, "f32", quant=quant)
+                assert np.array_equal(row, full[s, h]), (s, h)
+
+
+def check_int8_token_write_round_trip(seed=59):
+    """The per-row quantising write: every written row reads back within half a code step of
+    its input, with its scale at (block, KV head, offset) of the scale arrays and its largest
+    element at +-127; slots < 0 and every other row and scale are left as they were."""
+    from oracle import quant as Q
+    NB, Hkv, bs, D = 6, 2, 16, 32
+    rng = np.random.default_rng(seed)
+    kc = rng.integers(0, 256, size=(NB, Hkv, bs, D)).astype(np.uint8)
+    vc = rng.integers(0, 256, size=(NB, Hkv, D, bs)).astype(np.uint8)
+    ks = rng.uniform(0.01, 0.1, size=(NB, Hkv, bs)).astype(np.float32)
+    vs = rng.uniform(0.01, 0.1, size=(NB, Hkv, bs)).astype(np.float32)
+    T = 5
+    key = normal_host((T, Hkv, D), seed + 1, "bf16")
+    val = normal_host((T, Hkv, D), seed + 2, "bf16")
+    slots = np.array([3, 17, -1, 95, 40], dtype=np.int32)
+    kc2, vc2, ks2, vs2 = C.reshape_and_cache_int8_token(key, val, kc, vc, ks, vs, slots, "bf16")
+    touched = np.zeros((NB, bs), bool)
+    for i, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        b, o = divmod(int(slot), bs)
+        touched[b, o] = True
+        for h in range(Hkv):
+            for rows, codes, scale in ((key, kc2[b, h, o], ks2[b, h, o]), (val, vc2[b, h, :, o], vs2[b, h, o])):
+                x = A.to_f64(rows[i, h], "bf16")
+                got = Q.decode(codes, "int8") * float(scale)
+                assert np.max(np.abs(got - x)) <= 0.50001 * float(scale)
+                assert np.max(np.abs(Q.decode(codes, "int8"))) == 127.0
+    for b in range(NB):
+        for o in range(bs):
+            if not touched[b, o]:
+                assert np.array_equal(kc2[b, :, o], kc[b, :, o]) and np.array_equal(vc2[b, :, :, o], vc[b, :, :, o])
+                assert np.array_equal(ks2[b, :, o], ks[b, :, o]) and np.array_equal(vs2[b, :, o], vs[b, :, o])
+
+
+TOKEN_PINS = [check_int8_rows_closed_forms, check_int8_rows_vs_torch, check_int8_token_attention_lossless,
+              check_int8_token_write_round_trip]
+
+
 
 # ----------------------------------------------------------------------------
 # prefix caching ("PagedAttention 实现细节" §3.2)

@@ -8,6 +8,7 @@ import pytest
 
 from oracle import allocator as AL
 from oracle import attention as A
+from oracle import cache_ops as C
 from oracle import quant as Q
 from tests import oracle_pins as P
 
@@ -270,6 +271,55 @@ QUANT_MUTANTS = [
 def test_quant_mutant_is_caught(monkeypatch, mod, name, bad):
     monkeypatch.setattr(mod, name, bad)
     assert _caught(P.QUANT_PINS), f"no pin caught the planted mistake in {name}"
+
+
+def _rows_mean_scale(x, dtype, _orig=Q.quantize_rows_int8):
+    # scale from the mean magnitude instead of the largest
+    import numpy as np
+    x32 = Q.to_f32(x, dtype)
+    sc = (np.mean(np.abs(x32), axis=-1) / np.float32(127)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        codes = Q.encode(x32 / sc[..., None], "int8")
+    return codes, sc
+
+
+def _rows_scale_255(x, dtype):
+    # the full byte range instead of the symmetric 127
+    import numpy as np
+    x32 = Q.to_f32(x, dtype)
+    sc = (np.max(np.abs(x32), axis=-1) / np.float32(255)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        codes = Q.encode(x32 / sc[..., None], "int8")
+    return codes, sc
+
+
+def _rows_dequant_ignores_scale(codes, scales):
+    return Q.decode(codes, "int8") * 0.01
+
+
+def _row_scales_of_next_head(scale_pool, table_row, positions, kv_head, _orig=A.gather_row_scales):
+    return _orig(scale_pool, table_row, positions, (kv_head + 1) % scale_pool.shape[1])
+
+
+def _token_write_keeps_old_scales(key, value, kc, vc, ks, vs, slots, dtype, _orig=C.reshape_and_cache_int8_token):
+    kc2, vc2, _, _ = _orig(key, value, kc, vc, ks, vs, slots, dtype)
+    return kc2, vc2, ks.copy(), vs.copy()
+
+
+TOKEN_MUTANTS = [
+    (Q, "quantize_rows_int8", _rows_mean_scale),
+    (Q, "quantize_rows_int8", _rows_scale_255),
+    (Q, "dequantize_rows_int8", _rows_dequant_ignores_scale),
+    (A, "gather_row_scales", _row_scales_of_next_head),
+    (C, "reshape_and_cache_int8_token", _token_write_keeps_old_scales),
+]
+
+
+@pytest.mark.parametrize("mod,name,bad", TOKEN_MUTANTS, ids=[f"{n}:{b.__name__}" for _, n, b in TOKEN_MUTANTS])
+def test_token_scale_mutant_is_caught(monkeypatch, mod, name, bad):
+    """Planted mistakes in the per-(token, KV head) int8 form: each fails a pin."""
+    monkeypatch.setattr(mod, name, bad)
+    assert _caught(P.TOKEN_PINS), f"no pin caught the planted mistake in {name}"
 
 
 def test_quant_table_mutant_is_caught(monkeypatch):

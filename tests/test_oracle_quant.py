@@ -9,3 +9,8 @@ from tests import oracle_pins as P
 @pytest.mark.parametrize("pin", P.QUANT_PINS, ids=[p.__name__ for p in P.QUANT_PINS])
 def test_quant_pin(pin):
     pin()
+
+
+@pytest.mark.parametrize("pin", P.TOKEN_PINS, ids=[p.__name__ for p in P.TOKEN_PINS])
+def test_token_scale_pin(pin):
+    pin()
