@@ -10,14 +10,16 @@ One step = the whole hot path over one batch:
   (pa_decode_append).  Workloads 6 and 7 keep the pools as 8-bit codes (FP8 E4M3 /
   int8 with per-pool scales): pa_reshape_and_cache_quant quantises the new K/V and
   pa_decode_quant decodes.  Workload 8 appends 4 tokens per sequence and verifies them
-  in one pa_decode_multi launch (4 causal query tokens per sequence).
+  in one pa_decode_multi launch (4 causal query tokens per sequence).  Workload 9 keeps
+  int8 codes with one scale per (token, KV head) in each block's tiles: the write
+  quantises every new row with its own scale.
 
 Default workload: 64 sequences, 32 query / 32 KV heads of dimension 128, fp16,
 block size 16, contexts uniform in [256, 2048] (a LLaMA-7B-like layer), pool of
 8192 blocks in shuffled order.  Inputs are synthetic (seeded normals) and
 resident in HBM before the timed region.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload 1..7] [--path single|split]
+  python bench.py [--steps K] [--warmup W] [--workload 1..9] [--path single|split]
 """
 from __future__ import annotations
 
@@ -57,7 +59,7 @@ def parse(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9])
     ap.add_argument("--path", choices=["auto", "single", "split", "shared"], default=None,
                     help="decode path: pa_decode_auto (the library picks), pa_decode, pa_decode_split, or "
                          "pa_decode_shared (groups of sequences sharing leading blocks, from "
@@ -398,9 +400,16 @@ class Bench:
         if self.quant and args.fused_write:
             raise SystemExit("--fused-write has no 8-bit form: 8-bit pools are written by "
                              "pa_reshape_and_cache_quant")
+        # int8 pools with a scale per (token, KV head): each tile holds its codes, then its
+        # rows' scales (pa.token_pool); written in two launches (pa_upload, then the write)
+        self.rows = w.kv_format == "int8_token"
         if self.quant:
             self.kc = synth.normal_codes_device(k_shape, seeds["key_cache"], w.kv_format)
             self.vc = synth.normal_codes_device(v_shape, seeds["value_cache"], w.kv_format)
+            if self.rows:
+                sc_shape = (w.num_blocks, Hkv, bs)
+                self.kc = pa.pack_token_pool(self.kc, synth.row_scales_device(sc_shape, seeds["key_scales"]))
+                self.vc = pa.pack_token_pool(self.vc, synth.row_scales_device(sc_shape, seeds["value_scales"]))
         else:
             self.kc = synth.normal_device(k_shape, seeds["key_cache"], w.dtype)
             self.vc = synth.normal_device(v_shape, seeds["value_cache"], w.dtype)
@@ -468,6 +477,8 @@ class Bench:
         self.pool_owner = [None] * TIMING_SETS  # the timing entry each set's pending result goes to
         self.elem = synth.ELEM_BYTES[w.dtype]
         self.kv_elem = 1 if self.quant else self.elem
+        # KV bytes per token: every element once, plus (row scales) one fp32 scale per K and V row
+        self.kv_bytes_token = 2 * Hkv * (D * self.kv_elem + (4 if self.rows else 0))
         torch.cuda.synchronize()
 
     def step(self, k: int, timing: list | None, instrument: bool = False):
@@ -511,7 +522,7 @@ class Bench:
         fused = self.path == "auto" and self.args.fused_write
         # One launch for the upload and the K/V write when no copy-on-write pair must come
         # between them (the write may land in a block the copy fills).
-        one_launch = not npairs and not fused and not self.args.separate_upload
+        one_launch = not npairs and not fused and not self.args.separate_upload and not self.rows
         if one_launch:
             mark()
             pa.pa_upload_and_cache(b["idx_d"], b["idx_h"], self.newk[r], self.newv[r], self.kc, self.vc,
@@ -666,14 +677,19 @@ class Bench:
         remap = -np.ones(w.num_blocks, dtype=np.int32)
         remap[used] = np.arange(len(used), dtype=np.int32)
         idx = torch.from_numpy(used.astype(np.int64)).to(self.dev)
-        if self.quant:
+        if self.rows:
+            kc, ks = (t.cpu().numpy() for t in self.pa.unpack_token_pool(self.kc.index_select(0, idx),
+                                                                          w.block_size, w.head_dim, "key"))
+            vc, vs = (t.cpu().numpy() for t in self.pa.unpack_token_pool(self.vc.index_select(0, idx),
+                                                                          w.block_size, w.head_dim, "value"))
+        elif self.quant:
             kc = self.kc.index_select(0, idx).cpu().numpy()
             vc = self.vc.index_select(0, idx).cpu().numpy()
         else:
             kc = synth.to_numpy(self.kc.index_select(0, idx), w.dtype)
             vc = synth.to_numpy(self.vc.index_select(0, idx), w.dtype)
         q = synth.to_numpy(self.q, w.dtype)
-        quant = (w.kv_format, w.k_scale, w.v_scale) if self.quant else None
+        quant = ((w.kv_format, ks, vs) if self.rows else (w.kv_format, w.k_scale, w.v_scale)) if self.quant else None
         qstart = self.qstart.cpu().numpy()
         t2 = np.where(tabs >= 0, remap[np.maximum(tabs, 0)], -1)
         passes, tokens = 0, 0
@@ -725,7 +741,7 @@ def main():
     e = bench.elem
     timed = [t for t in timing if t[0] is not None]  # the steps whose decode was timed
     kv_tokens = sum(t[1] for t in timing)
-    kv_bytes_token = 2 * w.num_kv_heads * w.head_dim * bench.kv_elem
+    kv_bytes_token = bench.kv_bytes_token
     qo_bytes = 2 * w.num_seqs * w.query_len * w.num_heads * w.head_dim * e
 
     def alg_bytes(t):
@@ -763,7 +779,7 @@ def main():
                    "kv_write": "fused into the decode (pa_decode_append)" if args.fused_write
                    else ("upload and write in one launch (pa_upload_and_cache) when the step has no "
                          "copy-on-write pair, else pa_upload, pa_copy_blocks, write"
-                         if not args.separate_upload else "pa_upload, then the write (two launches)"),
+                         if not (args.separate_upload or bench.rows) else "pa_upload, then the write (two launches)"),
                    "partition_size": args.partition if "split" in bench.path_ran else None,
                    "launch_order": bench.order, "kv_cache_policy": "cached" if bench.cached else "stream",
                    "cow_pairs_per_step": sum(t[3] for t in timing) / len(timing)},

@@ -99,16 +99,18 @@ typedef enum pa_status {
 } pa_status;
 
 /* Element types.  PA_F32, PA_F16 and PA_BF16 are model types (query, out,
- * new K/V rows, 16-bit and 32-bit pools).  PA_FP8_E4M3 and PA_INT8 are the
- * 8-bit KV code types of the quantised cache (see pa_reshape_and_cache_quant):
- * they are valid only as kv_dtype of the *_quant calls and as the dtype of
- * pa_copy_blocks on 8-bit pools. */
+ * new K/V rows, 16-bit and 32-bit pools).  PA_FP8_E4M3, PA_INT8 and
+ * PA_INT8_TOKEN are the 8-bit KV code types of the quantised cache (see
+ * pa_reshape_and_cache_quant): they are valid only as kv_dtype of the calls
+ * that take one and as the dtype of pa_copy_blocks / pa_swap_blocks on 8-bit
+ * pools. */
 typedef enum pa_dtype {
   PA_F32 = 0,
   PA_F16 = 1,
   PA_BF16 = 2,
   PA_FP8_E4M3 = 3, /* OCP FP8 E4M3 ("fn"): bias 7, 3 mantissa bits, max 448, NaN 0x7F/0xFF */
-  PA_INT8 = 4      /* two's-complement int8 */
+  PA_INT8 = 4,     /* two's-complement int8, one scale per pool */
+  PA_INT8_TOKEN = 5 /* int8 with one fp32 scale per (token, KV head), kept in the block's tiles */
 } pa_dtype;
 
 /* Decode flags (bit mask).  By default K/V rows are read with a streaming
@@ -389,7 +391,9 @@ pa_status pa_upload(void* dst, const void* src, size_t nbytes, void* stream);
  * `dtype` at the slots slot_mapping[0..num_tokens), which it reads straight
  * from page-locked host memory (typically inside src).  kv_dtype == dtype:
  * the write of pa_reshape_and_cache; PA_FP8_E4M3 / PA_INT8: the quantising
- * write of pa_reshape_and_cache_quant with k_scale, v_scale.  The two parts
+ * write of pa_reshape_and_cache_quant with k_scale, v_scale (PA_INT8_TOKEN is
+ * not taken here: PA_ERR_UNSUPPORTED; use pa_upload, then
+ * pa_reshape_and_cache_quant).  The two parts
  * are independent: nothing in dst may be needed by the write, and a write
  * into a block that a copy-on-write pair of the same step copies must wait
  * for that copy (use pa_upload, pa_copy_blocks, then the write).  The call
@@ -577,7 +581,8 @@ pa_status pa_lse_reduce(void* out, const void* workspace, size_t workspace_bytes
  * inside the interval cost nothing when it covers the start of the context.
  * A sequence with every token masked gets a zero row.  Pools are `dtype`
  * (kv_dtype == dtype, the scales ignored) or 8-bit codes (kv_dtype
- * PA_FP8_E4M3 / PA_INT8 with k_scale, v_scale, as pa_decode_quant).  Path,
+ * PA_FP8_E4M3 / PA_INT8 with k_scale, v_scale, or PA_INT8_TOKEN, as
+ * pa_decode_quant).  Path,
  * flags (PA_DECODE_CACHED_KV, PA_DECODE_SPLIT), workspace, *path and errors
  * as in pa_decode_quant; under PA_DEBUG only blocks with an unmasked token
  * are validated. */
@@ -682,22 +687,42 @@ pa_status pa_decode_shared(void* out, const void* query, const void* key_cache, 
  *     Q rounding to nearest with ties to even.  E4M3: finite values beyond
  *     +-448 and +-inf saturate to +-448, NaN is stored as 0x7F, zeros keep
  *     their sign.  INT8: saturate to [-127, 127], NaN is stored as 0.
- * pa_copy_blocks copies 8-bit pools with dtype = kv_dtype. */
+ * PA_INT8_TOKEN keeps a scale per (token, KV head) instead ([XDNF] §2.3/§6.3
+ * name per-token int8 among the choices): each new key row and each new value
+ * row of head_dim elements gets s = max |x| / 127 (fp32 division) and codes
+ * Q(x / s) with Q as for PA_INT8, so its largest element is stored as +-127;
+ * a row of zeros has s = 0.  Rows must be finite (a NaN row's codes and scale
+ * are not specified).  The scales live in the pools themselves: each
+ * (block, KV head) tile is its block_size * head_dim codes (laid out as
+ * above) followed by block_size fp32 scales, the scale of token row o at byte
+ * block_size * head_dim + 4 o of the tile, the scales padded to a whole
+ * 128-byte line (PA_TOKEN_TILE_BYTES) so every tile's code rows stay
+ * line-aligned; a pool is [num_blocks, num_kv_heads, PA_TOKEN_TILE_BYTES]
+ * bytes, and block copies and swaps move the scales with the codes.  With PA_INT8_TOKEN the k_scale and v_scale arguments are
+ * not used.
+ * pa_copy_blocks and pa_swap_blocks copy 8-bit pools with dtype = kv_dtype. */
+
+/* Bytes of one (block, KV head) tile of a PA_INT8_TOKEN pool. */
+#define PA_TOKEN_TILE_BYTES(block_size, head_dim) \
+  ((block_size) * (head_dim) + ((block_size) * 4 + 127) / 128 * 128)
 
 /* The slot-mapping write of pa_reshape_and_cache into 8-bit pools: every
  * element of key[i, h, :] (of type dtype: PA_F32, PA_F16 or PA_BF16) is
  * quantised with k_scale and stored at key_cache[s / bs, h, s % bs, :]; value
  * rows likewise with v_scale at value_cache[s / bs, h, :, s % bs].  kv_dtype
- * selects the code format.  Slots, skipping, races and errors as in
- * pa_reshape_and_cache; k_scale and v_scale must be finite and > 0
- * (PA_ERR_INVALID_ARG).  Bit-exact (integer codes). */
+ * selects the code format; PA_INT8_TOKEN quantises each (token, KV head) row
+ * with its own scale and stores the scale in its tile (see above).  Slots,
+ * skipping, races and errors as in pa_reshape_and_cache; k_scale and v_scale
+ * must be finite and > 0 (PA_ERR_INVALID_ARG) unless kv_dtype is
+ * PA_INT8_TOKEN.  Bit-exact (integer codes and their scales). */
 pa_status pa_reshape_and_cache_quant(const void* key, const void* value, void* key_cache, void* value_cache,
                                      const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pa_dtype dtype,
                                      pa_dtype kv_dtype, float k_scale, float v_scale, void* stream);
 
 /* Paged decode attention over 8-bit pools: pa_decode's definition with
- * K_t = decode(key code) * k_scale and V_t = decode(value code) * v_scale.
+ * K_t = decode(key code) * k_scale and V_t = decode(value code) * v_scale
+ * (PA_INT8_TOKEN: times the scale of K_t's and V_t's own rows).
  * query and out are PA_F16 or PA_BF16 (dtype); the codes are widened exactly
  * to dtype on the fly, the scales folded into the logit scale and the output.
  * Path: the single pass when workspace is NULL; the split path (partials +

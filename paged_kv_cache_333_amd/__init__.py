@@ -56,11 +56,11 @@ PA_OK = 0
 STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_NO_FREE_BLOCKS", 3: "PA_ERR_UNKNOWN_SEQ",
           4: "PA_ERR_SEQ_EXISTS", 5: "PA_ERR_UNSUPPORTED", 6: "PA_ERR_BAD_TABLE",
           7: "PA_ERR_WORKSPACE_TOO_SMALL", 8: "PA_ERR_HIP", 9: "PA_ERR_UNKNOWN_PREFIX"}
-PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3, 4
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3, PA_INT8, PA_INT8_TOKEN = 0, 1, 2, 3, 4, 5
 PA_DECODE_CACHED_KV = 1
 PA_DECODE_SPLIT = 2
 DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
-KV_FORMATS = {"fp8_e4m3": PA_FP8_E4M3, "int8": PA_INT8}
+KV_FORMATS = {"fp8_e4m3": PA_FP8_E4M3, "int8": PA_INT8, "int8_token": PA_INT8_TOKEN}
 
 _i32, _u32, _i64, _f32, _vp, _sz = C.c_int32, C.c_uint32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
 _pi32, _pi64 = C.POINTER(C.c_int32), C.POINTER(C.c_int64)
@@ -189,8 +189,21 @@ def _stream(stream):
     return _torch().cuda.current_stream().cuda_stream
 
 
-def _pool_dims(key_cache, value_cache):
-    """(NB, H_kv, bs, D) from key_cache [NB, H_kv, bs, D]; value_cache must be [NB, H_kv, D, bs]."""
+def _pool_dims(key_cache, value_cache, head_dim=None):
+    """(NB, H_kv, bs, D) from key_cache [NB, H_kv, bs, D]; value_cache must be [NB, H_kv, D, bs].
+    Pools of int8 codes with a scale per (token, KV head) are uint8 [NB, H_kv, tile] (see
+    token_pool): their head_dim must be given, bs follows from it."""
+    if key_cache.dim() == 3:
+        NB, H_kv, tile = key_cache.shape
+        if head_dim is None:
+            raise ValueError("pools of int8 codes with row scales need head_dim")
+        bs = next((b for b in (16, 32) if token_tile_bytes(b, head_dim) == tile), None)
+        if bs is None or tuple(value_cache.shape) != tuple(key_cache.shape) or \
+                key_cache.element_size() != 1 or value_cache.element_size() != 1:
+            raise ValueError(f"row-scaled int8 pools must both be uint8 [num_blocks, num_kv_heads, "
+                             f"token_tile_bytes(block_size, {head_dim})]; got {tuple(key_cache.shape)} and "
+                             f"{tuple(value_cache.shape)}")
+        return NB, H_kv, bs, head_dim
     NB, H_kv, bs, D = key_cache.shape
     if tuple(value_cache.shape) != (NB, H_kv, D, bs) or value_cache.dtype != key_cache.dtype:
         raise ValueError(f"value_cache must be [num_blocks, num_kv_heads, head_dim, block_size] = "
@@ -208,12 +221,56 @@ def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, strea
                                     _dtype_code(key_cache), _stream(stream)), "pa_reshape_and_cache")
 
 
-def pa_copy_blocks(key_cache, value_cache, pairs, stream=None, num_pairs=None):
+def token_tile_bytes(block_size: int, head_dim: int) -> int:
+    """Bytes of one (block, KV head) tile of a row-scaled int8 pool (PA_TOKEN_TILE_BYTES): the
+    block_size * head_dim codes, then block_size float32 scales padded to a 128-byte line."""
+    return block_size * head_dim + (block_size * 4 + 127) // 128 * 128
+
+
+def token_pool(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, device="cuda"):
+    """A zeroed pool of int8 codes with a scale per (token, KV head) (kv_format "int8_token"):
+    uint8 [num_blocks, num_kv_heads, token_tile_bytes(block_size, head_dim)], each (block, KV
+    head) tile its codes (keys [block_size, head_dim], values [head_dim, block_size]) followed
+    by block_size float32 scales, one per token row, and padding to a 128-byte line."""
+    torch = _torch()
+    return torch.zeros((num_blocks, num_kv_heads, token_tile_bytes(block_size, head_dim)), dtype=torch.uint8,
+                       device=device)
+
+
+def pack_token_pool(codes, scales):
+    """A row-scaled int8 pool from its parts: codes uint8 [NB, H_kv, bs, D] (keys) or
+    [NB, H_kv, D, bs] (values) and scales float32 [NB, H_kv, bs]; the padding is zero."""
+    torch = _torch()
+    NB, H_kv = codes.shape[:2]
+    bs = scales.shape[2]
+    D = codes.shape[2] * codes.shape[3] // bs
+    pool = torch.zeros((NB, H_kv, token_tile_bytes(bs, D)), dtype=torch.uint8, device=codes.device)
+    pool[:, :, :bs * D] = codes.reshape(NB, H_kv, -1)
+    pool[:, :, bs * D:bs * D + 4 * bs] = scales.contiguous().view(torch.uint8).reshape(NB, H_kv, -1)
+    return pool
+
+
+def unpack_token_pool(pool, block_size: int, head_dim: int, kind: str):
+    """(codes, scales) of a row-scaled int8 pool: kind "key" gives codes [NB, H_kv, bs, D],
+    "value" [NB, H_kv, D, bs]; scales float32 [NB, H_kv, bs]."""
+    NB, H_kv, tile = pool.shape
+    nc = block_size * head_dim
+    if tile != token_tile_bytes(block_size, head_dim) or kind not in ("key", "value"):
+        raise ValueError("not a row-scaled int8 pool of this block size and head_dim, or kind not key/value")
+    shape = (NB, H_kv, block_size, head_dim) if kind == "key" else (NB, H_kv, head_dim, block_size)
+    codes = pool[:, :, :nc].reshape(shape)
+    scales = pool[:, :, nc:nc + 4 * block_size].contiguous().view(_torch().float32)
+    return codes, scales
+
+
+def pa_copy_blocks(key_cache, value_cache, pairs, stream=None, num_pairs=None, head_dim=None):
     """pairs int32 [P, 2] (src, dst) on the device; num_pairs may cover a prefix of it.
-    8-bit pools (one-byte elements) are copied as such."""
-    NB, H_kv, bs, D = _pool_dims(key_cache, value_cache)
+    8-bit pools (one-byte elements) are copied as such; row-scaled int8 pools (3-D, see
+    token_pool) need head_dim and are copied with their scales."""
+    NB, H_kv, bs, D = _pool_dims(key_cache, value_cache, head_dim)
     P = pairs.shape[0] if num_pairs is None else num_pairs
-    code = PA_FP8_E4M3 if key_cache.element_size() == 1 else _dtype_code(key_cache)
+    code = (PA_INT8_TOKEN if key_cache.dim() == 3 else PA_FP8_E4M3) if key_cache.element_size() == 1 \
+        else _dtype_code(key_cache)
     _check(lib.pa_copy_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(pairs), P, NB, H_kv, D, bs,
                               code, _stream(stream)), "pa_copy_blocks")
 
@@ -224,6 +281,10 @@ def _kv_format(key_cache, kv_format):
     torch = _torch()
     if key_cache.element_size() != 1:
         raise TypeError(f"8-bit pools expected, got {key_cache.dtype}")
+    if key_cache.dim() == 3:  # the row-scaled int8 layout
+        if kv_format not in (None, "int8_token"):
+            raise ValueError("3-D pools hold int8 codes with row scales (kv_format 'int8_token')")
+        return PA_INT8_TOKEN
     if kv_format is None:
         kv_format = {torch.float8_e4m3fn: "fp8_e4m3", torch.int8: "int8"}.get(key_cache.dtype)
         if kv_format is None:
@@ -234,8 +295,9 @@ def _kv_format(key_cache, kv_format):
 def pa_reshape_and_cache_quant(key, value, key_cache, value_cache, slot_mapping, k_scale: float, v_scale: float,
                                kv_format=None, stream=None):
     """The slot-mapping write into 8-bit pools: key, value [T, H_kv, D] (f32/f16/bf16) are
-    stored as codes of x / k_scale and x / v_scale."""
-    NB, H_kv, bs, D = _pool_dims(key_cache, value_cache)
+    stored as codes of x / k_scale and x / v_scale (row-scaled int8 pools: each row with its
+    own scale, k_scale and v_scale unused)."""
+    NB, H_kv, bs, D = _pool_dims(key_cache, value_cache, key.shape[-1])
     _check(lib.pa_reshape_and_cache_quant(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
                                           _ptr(slot_mapping), slot_mapping.numel(), NB, H_kv, D, bs,
                                           _dtype_code(key), _kv_format(key_cache, kv_format), k_scale, v_scale,
@@ -250,7 +312,7 @@ def pa_upload_and_cache(dst, src, key, value, key_cache, value_cache, slot_mappi
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != nbytes:
         raise ValueError("pa_upload_and_cache: dst and src differ in size")
-    NB, H_kv, bs, D = _pool_dims(key_cache, value_cache)
+    NB, H_kv, bs, D = _pool_dims(key_cache, value_cache, key.shape[-1])
     kv = _kv_format(key_cache, kv_format) if key_cache.element_size() == 1 else _dtype_code(key_cache)
     _check(lib.pa_upload_and_cache(_ptr(dst), _ptr(src), nbytes, _ptr(key), _ptr(value), _ptr(key_cache),
                                    _ptr(value_cache), _ptr(slot_mapping_host), slot_mapping_host.numel(), NB, H_kv,
@@ -259,16 +321,17 @@ def pa_upload_and_cache(dst, src, key, value, key_cache, value_cache, slot_mappi
 
 
 def pa_swap_blocks(dst_key_cache, dst_value_cache, src_key_cache, src_value_cache, pairs, stream=None,
-                   num_pairs=None):
+                   num_pairs=None, head_dim=None):
     """Whole-block copies pairs[p] = (src id, dst id) between two pools of the same block shape,
     each on the device or in pinned host memory (swap out: device -> host; swap in: host ->
     device).  pairs: int32 [P, 2] on the device or pinned."""
-    NB_d, H_kv, bs, D = _pool_dims(dst_key_cache, dst_value_cache)
-    NB_s = _pool_dims(src_key_cache, src_value_cache)[0]
-    if tuple(src_key_cache.shape[1:]) != (H_kv, bs, D) or src_key_cache.dtype != dst_key_cache.dtype:
+    NB_d, H_kv, bs, D = _pool_dims(dst_key_cache, dst_value_cache, head_dim)
+    NB_s = _pool_dims(src_key_cache, src_value_cache, head_dim)[0]
+    if tuple(src_key_cache.shape[1:]) != tuple(dst_key_cache.shape[1:]) or src_key_cache.dtype != dst_key_cache.dtype:
         raise ValueError("source and destination pools differ in block shape or dtype")
     P = pairs.shape[0] if num_pairs is None else num_pairs
-    code = PA_FP8_E4M3 if dst_key_cache.element_size() == 1 else _dtype_code(dst_key_cache)
+    code = (PA_INT8_TOKEN if dst_key_cache.dim() == 3 else PA_FP8_E4M3) if dst_key_cache.element_size() == 1 \
+        else _dtype_code(dst_key_cache)
     _check(lib.pa_swap_blocks(_ptr(dst_key_cache), _ptr(dst_value_cache), _ptr(src_key_cache),
                               _ptr(src_value_cache), _ptr(pairs), P, NB_s, NB_d, H_kv, D, bs, code,
                               _stream(stream)), "pa_swap_blocks")
@@ -311,7 +374,7 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, ma
     seq_order: optional device int32 [S] launch order (see pa_order_longest_first);
     cached_kv: read K/V with the default cache policy (pools with shared blocks)."""
     S, H, D = query.shape
-    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache)
+    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache, query.shape[-1])
     _check(lib.pa_decode(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
                          _ptr(context_lens), _opt(seq_order), S, H, H_kv, D, bs, block_tables.shape[1], NB,
                          max_context_len, scale, _dtype_code(query), PA_DECODE_CACHED_KV if cached_kv else 0,
@@ -328,7 +391,7 @@ def pa_decode_split(out, query, key_cache, value_cache, block_tables, context_le
                     cached_kv: bool = False):
     """As pa_decode; workspace is a device tensor of at least pa_decode_split_workspace_bytes bytes."""
     S, H, D = query.shape
-    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache)
+    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache, query.shape[-1])
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib.pa_decode_split(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
                                _ptr(block_tables), _ptr(context_lens), _opt(seq_order), S, H, H_kv, D, bs,
@@ -345,7 +408,7 @@ def pa_decode_split_static(out, query, key_cache, value_cache, block_tables, con
     """As pa_decode_split, with the partials in the library's static per-device workspace
     (PA_STATIC_SCRATCH_BYTES): no workspace argument, no allocation."""
     S, H, D = query.shape
-    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache)
+    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache, query.shape[-1])
     _check(lib.pa_decode_split_static(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
                                       _ptr(block_tables), _ptr(context_lens), _opt(seq_order), S, H, H_kv, D, bs,
                                       block_tables.shape[1], NB, max_context_len, scale, _dtype_code(query),
@@ -359,7 +422,7 @@ def pa_decode_auto(out, query, key_cache, value_cache, block_tables, context_len
     """pa_decode or pa_decode_split, chosen by the library for this launch; returns
     "single" or "split"."""
     S, H, D = query.shape
-    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache)
+    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache, query.shape[-1])
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     path = C.c_int32(-1)
     _check(lib.pa_decode_auto(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
@@ -376,7 +439,7 @@ def pa_decode_append(out, query, key, value, slot_mapping, key_cache, value_cach
     """pa_reshape_and_cache of one new token per sequence (key, value [S, H_kv, D] at
     slot_mapping [S]) fused into pa_decode_auto; returns "single" or "split"."""
     S, H, D = query.shape
-    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache)
+    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache, query.shape[-1])
     if tuple(key.shape) != (S, H_kv, D) or tuple(value.shape) != (S, H_kv, D) or slot_mapping.numel() != S:
         raise ValueError("key/value must be [num_seqs, num_kv_heads, head_dim] and slot_mapping [num_seqs]")
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -397,7 +460,7 @@ def pa_decode_quant(out, query, key_cache, value_cache, block_tables, context_le
     output.  Single pass without a workspace; split with split=True; else the pa_decode_auto
     rule.  Returns "single" or "split"."""
     S, H, D = query.shape
-    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache)
+    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache, query.shape[-1])
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     flags = (PA_DECODE_CACHED_KV if cached_kv else 0) | (PA_DECODE_SPLIT if split else 0)
     path = C.c_int32(-1)
@@ -418,7 +481,7 @@ def pa_decode_masked(out, query, key_cache, value_cache, block_tables, context_l
     8-bit pools (K = code * k_scale, V = code * v_scale).  Single pass without a workspace; split
     with split=True; else the pa_decode_auto rule.  Returns "single" or "split"."""
     S, H, D = query.shape
-    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache)
+    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache, query.shape[-1])
     kv = _kv_format(key_cache, kv_format) if key_cache.element_size() == 1 else _dtype_code(key_cache)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     flags = (PA_DECODE_CACHED_KV if cached_kv else 0) | (PA_DECODE_SPLIT if split else 0)
@@ -446,7 +509,7 @@ def pa_decode_multi(out, query, key_cache, value_cache, block_tables, context_le
     "single" or "split"."""
     T, H, D = query.shape
     S = context_lens.numel()
-    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache)
+    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache, query.shape[-1])
     if query_start.numel() != S + 1:
         raise ValueError("query_start must hold num_seqs + 1 offsets")
     kv = _kv_format(key_cache, kv_format) if key_cache.element_size() == 1 else _dtype_code(key_cache)
@@ -483,7 +546,7 @@ def pa_decode_shared(out, query, key_cache, value_cache, block_tables, context_l
     each group's shared prefix is read once for all its members, then each sequence's own
     tokens, merged.  Same result as pa_decode; workspace of pa_decode_shared_workspace_bytes."""
     S, H, D = query.shape
-    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache)
+    NB, H_kv, bs, _ = _pool_dims(key_cache, value_cache, query.shape[-1])
     kv = _kv_format(key_cache, kv_format) if key_cache.element_size() == 1 else _dtype_code(key_cache)
     nbytes = workspace.numel() * workspace.element_size()
     flags = PA_DECODE_CACHED_KV if cached_kv else 0

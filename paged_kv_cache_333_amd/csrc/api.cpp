@@ -36,7 +36,15 @@ bool debug_mode() {
 
 int elem_bytes(pa_dtype dt) { return dt == PA_F32 ? 4 : dt == PA_F16 || dt == PA_BF16 ? 2 : 1; }
 
-bool is_code_type(pa_dtype dt) { return dt == PA_FP8_E4M3 || dt == PA_INT8; }
+bool is_code_type(pa_dtype dt) { return dt == PA_FP8_E4M3 || dt == PA_INT8 || dt == PA_INT8_TOKEN; }
+
+// Bytes of one (block, KV head) tile of a pool of element type dt: its
+// elements, then (PA_INT8_TOKEN) one fp32 scale per token row, padded to a
+// whole 128-byte line.
+int64_t tile_bytes(pa_dtype dt, int32_t head_dim, int32_t block_size) {
+  return static_cast<int64_t>(block_size) * head_dim * elem_bytes(dt) +
+         (dt == PA_INT8_TOKEN ? (static_cast<int64_t>(block_size) * 4 + 127) / 128 * 128 : 0);
+}
 
 pa_status check_scales(float k_scale, float v_scale) {
   // finite and positive (NaN fails the comparisons)
@@ -344,8 +352,8 @@ pa_status pa_reshape_and_cache_quant(const void* key, const void* value, void* k
                                      pa_dtype kv_dtype, float k_scale, float v_scale, void* stream) {
   pa_status s = check_shape(dtype, head_dim, block_size);
   if (s != PA_OK) return s;
-  if (!is_code_type(kv_dtype)) return fail(PA_ERR_UNSUPPORTED, "kv_dtype must be PA_FP8_E4M3 or PA_INT8");
-  if ((s = check_scales(k_scale, v_scale)) != PA_OK) return s;
+  if (!is_code_type(kv_dtype)) return fail(PA_ERR_UNSUPPORTED, "kv_dtype must be an 8-bit code type");
+  if (kv_dtype != PA_INT8_TOKEN && (s = check_scales(k_scale, v_scale)) != PA_OK) return s;
   if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0)
     return fail(PA_ERR_INVALID_ARG, "negative size or zero heads");
   if (num_tokens == 0) return PA_OK;
@@ -356,6 +364,10 @@ pa_status pa_reshape_and_cache_quant(const void* key, const void* value, void* k
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (debug_mode() && (s = debug_check_slots(slot_mapping, num_tokens, num_blocks, block_size, st)) != PA_OK)
     return s;
+  if (kv_dtype == PA_INT8_TOKEN)
+    return finish(pa::launch_reshape_and_cache_rows(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                                                    num_blocks, num_kv_heads, head_dim, block_size, dtype, st),
+                  st, "pa_reshape_and_cache_quant");
   return finish(pa::launch_reshape_and_cache_quant(key, value, key_cache, value_cache, slot_mapping, num_tokens,
                                                    num_blocks, num_kv_heads, head_dim, block_size, dtype, kv_dtype,
                                                    k_scale, v_scale, st),
@@ -389,7 +401,7 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* pair
     for (int32_t b : dsts)
       if (srcs.count(b)) return fail(PA_ERR_BAD_TABLE, "a copy destination is also a source");
   }
-  const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
+  const int64_t block_bytes = num_kv_heads * tile_bytes(dtype, head_dim, block_size);
   return finish(pa::launch_copy_blocks(key_cache, value_cache, pairs, num_pairs, num_blocks, block_bytes, st),
                 st, "pa_copy_blocks");
 }
@@ -435,7 +447,7 @@ pa_status pa_swap_blocks(void* dst_key_cache, void* dst_value_cache, const void*
   if (kdk < 0 || kdv < 0 || ksk < 0 || ksv < 0 || kp < 0)
     return fail(PA_ERR_INVALID_ARG, "pools and pairs must be device memory or page-locked host memory");
   if (kdk != kdv || ksk != ksv) return fail(PA_ERR_INVALID_ARG, "K and V pools of one side must live together");
-  const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
+  const int64_t block_bytes = num_kv_heads * tile_bytes(dtype, head_dim, block_size);
   hipStream_t st = static_cast<hipStream_t>(stream);
   return finish(pa::launch_swap_blocks(const_cast<void*>(dk), const_cast<void*>(dv), sk, sv,
                                        static_cast<const int32_t*>(pv), num_pairs, num_src_blocks, num_dst_blocks,
@@ -474,8 +486,10 @@ pa_status pa_upload_and_cache(void* dst, const void* src, size_t nbytes, const v
   pa_status s = check_shape(dtype, head_dim, block_size);
   if (s != PA_OK) return s;
   const bool quant = is_code_type(kv_dtype);
+  if (kv_dtype == PA_INT8_TOKEN)
+    return fail(PA_ERR_UNSUPPORTED, "per-row int8 pools are written by pa_reshape_and_cache_quant");
   if (!quant && kv_dtype != dtype)
-    return fail(PA_ERR_UNSUPPORTED, "kv_dtype must equal dtype, or be PA_FP8_E4M3 / PA_INT8");
+    return fail(PA_ERR_UNSUPPORTED, "kv_dtype must equal dtype, or be an 8-bit code type");
   if (quant && (s = check_scales(k_scale, v_scale)) != PA_OK) return s;
   if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0)
     return fail(PA_ERR_INVALID_ARG, "negative size or zero heads");
@@ -676,11 +690,11 @@ pa_status pa_decode_masked(void* out, const void* query, const void* key_cache, 
   if (is_code_type(kv_dtype)) {
     if (dtype != PA_F16 && dtype != PA_BF16)
       return fail(PA_ERR_UNSUPPORTED, "8-bit pools decode with PA_F16 or PA_BF16 queries");
-    if ((s = check_scales(k_scale, v_scale)) != PA_OK) return s;
-    a.k_scale = k_scale;
-    a.v_scale = v_scale;
+    if (kv_dtype != PA_INT8_TOKEN && (s = check_scales(k_scale, v_scale)) != PA_OK) return s;
+    a.k_scale = kv_dtype == PA_INT8_TOKEN ? 1.0f : k_scale;  // per-row scales come from the pools
+    a.v_scale = kv_dtype == PA_INT8_TOKEN ? 1.0f : v_scale;
   } else if (kv_dtype != dtype) {
-    return fail(PA_ERR_UNSUPPORTED, "kv_dtype must equal dtype, or be PA_FP8_E4M3 / PA_INT8");
+    return fail(PA_ERR_UNSUPPORTED, "kv_dtype must equal dtype, or be an 8-bit code type");
   }
   if ((mask_lo == nullptr) != (mask_hi == nullptr))
     return fail(PA_ERR_INVALID_ARG, "mask_lo and mask_hi must both be given or both be NULL");
@@ -732,11 +746,11 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache, c
   if (is_code_type(kv_dtype)) {
     if (dtype != PA_F16 && dtype != PA_BF16)
       return fail(PA_ERR_UNSUPPORTED, "8-bit pools decode with PA_F16 or PA_BF16 queries");
-    if ((s = check_scales(k_scale, v_scale)) != PA_OK) return s;
-    a.k_scale = k_scale;
-    a.v_scale = v_scale;
+    if (kv_dtype != PA_INT8_TOKEN && (s = check_scales(k_scale, v_scale)) != PA_OK) return s;
+    a.k_scale = kv_dtype == PA_INT8_TOKEN ? 1.0f : k_scale;  // per-row scales come from the pools
+    a.v_scale = kv_dtype == PA_INT8_TOKEN ? 1.0f : v_scale;
   } else if (kv_dtype != dtype) {
-    return fail(PA_ERR_UNSUPPORTED, "kv_dtype must equal dtype, or be PA_FP8_E4M3 / PA_INT8");
+    return fail(PA_ERR_UNSUPPORTED, "kv_dtype must equal dtype, or be an 8-bit code type");
   }
   if (num_query_tokens < 0 || max_query_len < 1 || max_query_len > 4096)
     return fail(PA_ERR_INVALID_ARG, "num_query_tokens >= 0 and 1 <= max_query_len <= 4096");
@@ -883,11 +897,11 @@ pa_status pa_decode_shared(void* out, const void* query, const void* key_cache, 
   if (is_code_type(kv_dtype)) {
     if (dtype != PA_F16 && dtype != PA_BF16)
       return fail(PA_ERR_UNSUPPORTED, "8-bit pools decode with PA_F16 or PA_BF16 queries");
-    if ((s = check_scales(k_scale, v_scale)) != PA_OK) return s;
-    a.k_scale = k_scale;
-    a.v_scale = v_scale;
+    if (kv_dtype != PA_INT8_TOKEN && (s = check_scales(k_scale, v_scale)) != PA_OK) return s;
+    a.k_scale = kv_dtype == PA_INT8_TOKEN ? 1.0f : k_scale;  // per-row scales come from the pools
+    a.v_scale = kv_dtype == PA_INT8_TOKEN ? 1.0f : v_scale;
   } else if (kv_dtype != dtype) {
-    return fail(PA_ERR_UNSUPPORTED, "kv_dtype must equal dtype, or be PA_FP8_E4M3 / PA_INT8");
+    return fail(PA_ERR_UNSUPPORTED, "kv_dtype must equal dtype, or be an 8-bit code type");
   }
   if (flags & ~uint32_t(PA_DECODE_CACHED_KV)) return fail(PA_ERR_INVALID_ARG, "unknown flag bits");
   if (max_group_size < 1 || max_group_size > 4096)
@@ -957,14 +971,14 @@ pa_status pa_decode_quant(void* out, const void* query, const void* key_cache, c
                           num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
                           max_context_len, scale, dtype, flags);
   a.kv_dtype = kv_dtype;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
+  a.k_scale = kv_dtype == PA_INT8_TOKEN ? 1.0f : k_scale;  // per-row scales come from the pools
+  a.v_scale = kv_dtype == PA_INT8_TOKEN ? 1.0f : v_scale;
   pa_status s = check_decode_args(a);
   if (s != PA_OK) return s;
   if (dtype != PA_F16 && dtype != PA_BF16)
     return fail(PA_ERR_UNSUPPORTED, "8-bit pools decode with PA_F16 or PA_BF16 queries");
-  if (!is_code_type(kv_dtype)) return fail(PA_ERR_UNSUPPORTED, "kv_dtype must be PA_FP8_E4M3 or PA_INT8");
-  if ((s = check_scales(k_scale, v_scale)) != PA_OK) return s;
+  if (!is_code_type(kv_dtype)) return fail(PA_ERR_UNSUPPORTED, "kv_dtype must be an 8-bit code type");
+  if (kv_dtype != PA_INT8_TOKEN && (s = check_scales(k_scale, v_scale)) != PA_OK) return s;
   if (flags & ~uint32_t(PA_DECODE_CACHED_KV | PA_DECODE_SPLIT))
     return fail(PA_ERR_INVALID_ARG, "unknown flag bits");
   a.flags = flags & PA_DECODE_CACHED_KV;

@@ -252,6 +252,76 @@ __device__ __forceinline__ void write_tile_quant(const WriteArgs& a, int64_t tok
   }
 }
 
+// One model-type element at p, as fp32 (exact).
+__device__ __forceinline__ float element_at(TF32, const char* p) {
+  return __builtin_bit_cast(float, *reinterpret_cast<const uint32_t*>(p));
+}
+__device__ __forceinline__ float element_at(TF16, const char* p) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(p)));
+}
+__device__ __forceinline__ float element_at(TBF16, const char* p) {
+  return __builtin_bit_cast(float, static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(p)) << 16);
+}
+
+// The slot-mapping write into int8 pools with one scale per (token, KV head)
+// (the per-token int8 form of the xdnf.cn article's §2.3/§6.3).  One wave per
+// (token, KV head): its key row and its value row each get s = max |x| / 127
+// (fp32 division) and codes to_code(x / s) (nearest, ties to even,
+// saturating at +-127); a row of zeros gets s = 0 and codes 0.  Lane l holds
+// elements EL l .. EL l + EL - 1; the row's max comes from a butterfly of lane
+// exchanges.  The key codes go to the token's row of the key tile, the value
+// codes one byte each down column `offset` of the value tile, and the two
+// scales to byte BS * D + 4 offset of their tiles (each tile holds its codes,
+// then one fp32 scale per token row, padded to a 128-byte line).  Slots
+// outside the pool write nothing.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void reshape_and_cache_rows_kernel(WriteArgs a) {
+  constexpr int EL = D / 64;
+  constexpr int E = T::kBytes;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // token * H_kv + head
+  if (row >= static_cast<int64_t>(a.num_tokens) * a.num_kv_heads) return;
+  const int64_t tok = row / a.num_kv_heads;
+  const int32_t h = static_cast<int32_t>(row - tok * a.num_kv_heads);
+  const int64_t slot = a.slots[tok];
+  if (slot < 0 || slot >= a.num_slots) return;
+  const int64_t blk = slot / a.block_size;
+  const int64_t off = slot - blk * a.block_size;
+  // bytes per tile: the codes, then the rows' scales padded to a whole 128-byte line
+  const int64_t tb = static_cast<int64_t>(a.block_size) * D + (a.block_size * 4 + 127) / 128 * 128;
+  char* kt = a.key_cache + (blk * a.num_kv_heads + h) * tb;
+  char* vt = a.value_cache + (blk * a.num_kv_heads + h) * tb;
+  float xk[EL], xv[EL];
+  float mk = 0.f, mv = 0.f;
+#pragma unroll
+  for (int i = 0; i < EL; ++i) {
+    const int64_t src = (row * D + EL * lane + i) * E;
+    xk[i] = element_at(T{}, a.key + src);
+    xv[i] = element_at(T{}, a.value + src);
+    mk = fmaxf(mk, fabsf(xk[i]));
+    mv = fmaxf(mv, fabsf(xv[i]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mk = fmaxf(mk, __shfl_xor(mk, o));
+    mv = fmaxf(mv, __shfl_xor(mv, o));
+  }
+  const float sk = mk / 127.0f;
+  const float sv = mv / 127.0f;
+#pragma unroll
+  for (int i = 0; i < EL; ++i) {
+    const int d = EL * lane + i;
+    const uint32_t ck = sk > 0.f ? to_code(TI8{}, xk[i] / sk) : 0u;
+    const uint32_t cv = sv > 0.f ? to_code(TI8{}, xv[i] / sv) : 0u;
+    reinterpret_cast<uint8_t*>(kt)[off * D + d] = static_cast<uint8_t>(ck);
+    reinterpret_cast<uint8_t*>(vt)[static_cast<int64_t>(d) * a.block_size + off] = static_cast<uint8_t>(cv);
+  }
+  if (lane == 0) {
+    *reinterpret_cast<float*>(kt + static_cast<int64_t>(a.block_size) * D + 4 * off) = sk;
+    *reinterpret_cast<float*>(vt + static_cast<int64_t>(a.block_size) * D + 4 * off) = sv;
+  }
+}
+
 // W::template run<HOST_SLOTS, NT>(a, idx, hs) is one of the two element-wise writes above,
 // W::run_tile(a, tok, h0, h1, slot) the matching whole-tile write.
 template <int E>
@@ -579,6 +649,29 @@ hipError_t launch_reshape_and_cache_quant(const void* key, const void* value, vo
                                        num_kv_heads, head_dim, block_size, k_scale, v_scale),
                             chunks, stream},
                   dtype, kv_dtype);
+}
+
+hipError_t launch_reshape_and_cache_rows(const void* key, const void* value, void* key_cache, void* value_cache,
+                                         const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pa_dtype dtype,
+                                         hipStream_t stream) {
+  const int64_t rows = static_cast<int64_t>(num_tokens) * num_kv_heads;
+  if (rows == 0) return hipSuccess;
+  const WriteArgs a = write_args(key, value, key_cache, value_cache, slot_mapping, num_tokens, num_blocks,
+                                 num_kv_heads, head_dim, block_size, 1.f, 1.f);
+  const dim3 grid(static_cast<uint32_t>((rows + 3) / 4));
+#define PA_ROWS(T, D) launch_kernel(reshape_and_cache_rows_kernel<T, D>, grid, dim3(256), stream, a)
+  if (head_dim == 64) {
+    if (dtype == PA_F32) PA_ROWS(TF32, 64);
+    else if (dtype == PA_F16) PA_ROWS(TF16, 64);
+    else PA_ROWS(TBF16, 64);
+  } else {
+    if (dtype == PA_F32) PA_ROWS(TF32, 128);
+    else if (dtype == PA_F16) PA_ROWS(TF16, 128);
+    else PA_ROWS(TBF16, 128);
+  }
+#undef PA_ROWS
+  return hipGetLastError();
 }
 
 hipError_t launch_upload_and_cache(void* dst, const void* src_device_view, int64_t nbytes, const void* key,

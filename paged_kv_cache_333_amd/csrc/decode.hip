@@ -23,6 +23,8 @@ hipError_t by_dtype(const LaunchOp& op, pa_dtype dt, pa_dtype kv, bool split, bo
   if (kv == PA_FP8_E4M3 && dt == PA_BF16) return dispatch_e4m3_bf16(op, split, append, d, bs, gt);
   if (kv == PA_INT8 && dt == PA_F16) return dispatch_i8_f16(op, split, append, d, bs, gt);
   if (kv == PA_INT8 && dt == PA_BF16) return dispatch_i8_bf16(op, split, append, d, bs, gt);
+  if (kv == PA_INT8_TOKEN && dt == PA_F16) return dispatch_i8t_f16(op, split, append, d, bs, gt);
+  if (kv == PA_INT8_TOKEN && dt == PA_BF16) return dispatch_i8t_bf16(op, split, append, d, bs, gt);
   return hipErrorInvalidValue;
 }
 
@@ -39,6 +41,8 @@ hipError_t occupancy_by_dtype(int* per_cu, pa_dtype dt, pa_dtype kv, int d, int 
   if (kv == PA_FP8_E4M3 && dt == PA_BF16) return occupancy_e4m3_bf16(per_cu, d, bs, gt);
   if (kv == PA_INT8 && dt == PA_F16) return occupancy_i8_f16(per_cu, d, bs, gt);
   if (kv == PA_INT8 && dt == PA_BF16) return occupancy_i8_bf16(per_cu, d, bs, gt);
+  if (kv == PA_INT8_TOKEN && dt == PA_F16) return occupancy_i8t_f16(per_cu, d, bs, gt);
+  if (kv == PA_INT8_TOKEN && dt == PA_BF16) return occupancy_i8t_bf16(per_cu, d, bs, gt);
   return hipErrorInvalidValue;
 }
 

@@ -44,6 +44,18 @@
 // column's causal limit in the last steps, and value rows are zeroed only past
 // the tile's furthest limit.
 //
+// int8 pools with a scale per (token, KV head) (storage type TI8T): each tile
+// holds its codes, then the fp32 scales of its bs token rows, padded to a
+// 128-byte line (an unpadded 16-row tile would leave half of all code rows
+// straddling two lines: back to back, the decode measured 117 instead of
+// 110 us).  With the
+// step's other loads, lane i loads the key scale and the value scale of the
+// step's token i; lane (q, n) takes those of its tokens 16 q + e from lane e
+// of its row (a DPP row broadcast), so the scales cost two registers in
+// flight.  The key scale multiplies the lane's logit of that token, and the
+// value scale its weight p before P.V (the running sum l stays unscaled), so
+// the codes still go to the matrix cores widened as they are.
+//
 // Logits are kept in base-2 units (scale folded with log2 e) so the hardware
 // exp2 is used.  Tokens past the context are masked by select (never by
 // multiplying by 0), and their value columns are zeroed before the product,
@@ -223,6 +235,7 @@ template <typename T, typename S, int D, int BS, int GT, bool SPLIT, bool CACHED
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void decode_kernel(DecodeParams a) {
   constexpr int NC = GT;
   constexpr bool Q8 = S::kBytes == 1;  // 8-bit codes
+  constexpr bool ROWS = row_scaled<S>::value;  // a scale per (token, KV head) in each tile
   constexpr int EPL = T::kEPL;       // compute elements per 16-byte chunk
   constexpr int E = T::kBytes;
   constexpr int SE = S::kEPL;        // stored elements per 16-byte load
@@ -235,6 +248,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   constexpr int NV = D / 16;         // value loads per step, 16 output dims each
   constexpr int PV = TPL / EPL;      // P.V products per 16 output dims (2 for 8-bit codes)
   constexpr int NBS = TS > BS ? TS / BS : 1;  // blocks touched by one step
+  // bytes of one (block, KV head) tile: its codes or elements, then (ROWS) its rows' scales,
+  // padded to a whole 128-byte line so every tile's rows stay line-aligned
+  constexpr int64_t KT = static_cast<int64_t>(BS) * D * SB + (ROWS ? (BS * 4 + 127) / 128 * 128 : 0);
   // P.V runs in TP: the query type, except over 8-bit pools, whose codes are
   // exact in fp16 (and P is in [0, 1]): fp16 there, one product per chunk
   // instead of bf16's high part + residual, and the cheaper fp16 widening.
@@ -246,6 +262,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   static_assert(!(Q8 && APPEND), "the fused write stores model-type rows");
   static_assert(NBS <= 4 && KL * SE * 4 == D && KV * EPL * 4 == D, "step shape");
   static_assert(TPL % BS == 0 || BS % TPL == 0, "a lane's tokens never straddle a block boundary");
+  static_assert(!ROWS || (TPL == 16 && TS == 64), "row scales: one token of the step per lane, 16 per row");
 
   const int lane = threadIdx.x & 63;
   // wave-uniform: keeps the step loop and the table lookups in scalar registers
@@ -490,17 +507,29 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
 #pragma unroll
     for (int tau = 0; tau < NT; ++tau) {
       const int x = off0 + TPL * (n >> 2) + 4 * tau + (n & 3);
-      const char* kp = a.kc + (((kblk * hkv + kvh) * BS + (x - bik * BS)) * D) * SB + q * 16;
+      const char* kp = a.kc + (kblk * hkv + kvh) * KT + ((x - bik * BS) * D) * SB + q * 16;
 #pragma unroll
       for (int l = 0; l < KL; ++l) kr[tau][l] = CACHED ? load16(kp + l * 64) : load16_stream(kp + l * 64);
     }
     // V columns: lane (q, n) supplies dim 16v + n of tokens TPL q .. TPL q + TPL-1.
     u32x4 vr[NV];
+    float ks1 = 1.f, vs1 = 1.f;  // (ROWS) the key and value scales of the step's token `lane`
+    if constexpr (ROWS) {
+      const int x = off0 + lane;
+      const int bi = NBS == 1 ? 0 : x / BS;
+      const int64_t sc = (pick(bi) * hkv + kvh) * KT + static_cast<int64_t>(BS) * D + (x - bi * BS) * 4;
+      // streaming like the codes (plain loads that miss allocate L2 lines: measured 140 instead
+      // of 108 us for the row-scaled LLaMA-7B-like decode after a cache flush)
+      const float* kp1 = reinterpret_cast<const float*>(a.kc + sc);
+      const float* vp1 = reinterpret_cast<const float*>(a.vc + sc);
+      ks1 = CACHED ? *kp1 : __builtin_nontemporal_load(kp1);
+      vs1 = CACHED ? *vp1 : __builtin_nontemporal_load(vp1);
+    }
     {
       const int x = off0 + TPL * q;
       const int bi = NBS == 1 ? 0 : x / BS;
       const int64_t phys = pick(bi);  // bi < NBS: TPL q < TS
-      const char* vp = a.vc + (((phys * hkv + kvh) * D + n) * BS + (x - bi * BS)) * SB;
+      const char* vp = a.vc + (phys * hkv + kvh) * KT + (n * BS + (x - bi * BS)) * SB;
 #pragma unroll
       for (int v = 0; v < NV; ++v)
         vr[v] = CACHED ? load16(vp + v * 16 * BS * SB) : load16_stream(vp + v * 16 * BS * SB);
@@ -547,7 +576,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     for (int tau = 0; tau < NT; ++tau)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float v = c[tau][j] * a.scale_log2;
+        float v = c[tau][j] * a.scale_log2;
+        if constexpr (ROWS) v *= row_bcast(ks1, 4 * tau + j);  // the scale of token TPL q + 4 tau + j
         const bool ok = !ragged || ((use >> (4 * tau + j)) & 1u);
         z[4 * tau + j] = ok ? v : kNegInf;
         mx = fmaxf(mx, z[4 * tau + j]);
@@ -566,6 +596,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       ps += p[e];
     }
     l_run = l_run * alpha + ps;
+    if constexpr (ROWS) {
+      // weights of the value codes: p times the value row's scale; a token no column
+      // uses (its scale may be anything) weighs exactly 0
+#pragma unroll
+      for (int e = 0; e < TPL; ++e) {
+        const float sv = row_bcast(vs1, e);
+        p[e] = !ragged || ((vuse >> e) & 1u) ? p[e] * sv : 0.f;
+      }
+    }
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
       // acc[.][j] belongs to column (4q + j) % NC; its factor sits in a lane
       // of the same row whose column is that one.
@@ -901,6 +940,8 @@ hipError_t dispatch_e4m3_f16(const LaunchOp& op, bool split, bool append, int d,
 hipError_t dispatch_e4m3_bf16(const LaunchOp& op, bool split, bool append, int d, int bs, int gt);
 hipError_t dispatch_i8_f16(const LaunchOp& op, bool split, bool append, int d, int bs, int gt);
 hipError_t dispatch_i8_bf16(const LaunchOp& op, bool split, bool append, int d, int bs, int gt);
+hipError_t dispatch_i8t_f16(const LaunchOp& op, bool split, bool append, int d, int bs, int gt);
+hipError_t dispatch_i8t_bf16(const LaunchOp& op, bool split, bool append, int d, int bs, int gt);
 hipError_t occupancy_f32(int* per_cu, int d, int bs, int gt);
 hipError_t occupancy_f16(int* per_cu, int d, int bs, int gt);
 hipError_t occupancy_bf16(int* per_cu, int d, int bs, int gt);
@@ -908,6 +949,8 @@ hipError_t occupancy_e4m3_f16(int* per_cu, int d, int bs, int gt);
 hipError_t occupancy_e4m3_bf16(int* per_cu, int d, int bs, int gt);
 hipError_t occupancy_i8_f16(int* per_cu, int d, int bs, int gt);
 hipError_t occupancy_i8_bf16(int* per_cu, int d, int bs, int gt);
+hipError_t occupancy_i8t_f16(int* per_cu, int d, int bs, int gt);
+hipError_t occupancy_i8t_bf16(int* per_cu, int d, int bs, int gt);
 
 template <typename T, typename S = T>
 hipError_t dispatch_t(const LaunchOp& op, bool split, bool append, int d, int bs, int gt) {

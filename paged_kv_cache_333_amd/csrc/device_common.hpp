@@ -34,6 +34,20 @@ struct TI8 {
   static constexpr int kBytes = 1;
   static constexpr int kEPL = 16;
 };
+// int8 codes with one fp32 scale per (token, KV head): each (block, KV head)
+// tile holds its bs * D codes, then the bs scales of its token rows.
+struct TI8T {
+  static constexpr int kBytes = 1;
+  static constexpr int kEPL = 16;
+};
+template <typename S>
+struct row_scaled {
+  static constexpr bool value = false;
+};
+template <>
+struct row_scaled<TI8T> {
+  static constexpr bool value = true;
+};
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -155,6 +169,7 @@ __device__ __forceinline__ u32x4 bits_mask_8(uint32_t bits) {
 }
 __device__ __forceinline__ u32x4 bits_mask(TE4M3, uint32_t bits) { return bits_mask_8(bits); }
 __device__ __forceinline__ u32x4 bits_mask(TI8, uint32_t bits) { return bits_mask_8(bits); }
+__device__ __forceinline__ u32x4 bits_mask(TI8T, uint32_t bits) { return bits_mask_8(bits); }
 
 // ---------------------------------------------------------------------------
 // 8-bit codes -> fp16/bf16, exactly.  widen() turns one chunk of 16 codes into
@@ -208,6 +223,11 @@ __device__ __forceinline__ void widen(TI8, T, u32x4 raw, u32x4& lo, u32x4& hi) {
              i8_pair<true>(T{}, raw[3])};
 }
 
+template <typename T>
+__device__ __forceinline__ void widen(TI8T, T, u32x4 raw, u32x4& lo, u32x4& hi) {
+  widen(TI8{}, T{}, raw, lo, hi);
+}
+
 // ---------------------------------------------------------------------------
 // fp32 -> 8-bit code, round to nearest even (the quantising write).
 
@@ -256,6 +276,35 @@ __device__ __forceinline__ float quad_bcast(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
                                                                J | (J << 2) | (J << 4) | (J << 6), 0xf, 0xf,
                                                                false));
+}
+
+// Value of lane J of this lane's row of 16 (DPP row_newbcast:J).
+template <int J>
+__device__ __forceinline__ float row_bcast_lane(float x) {
+  static_assert(J >= 0 && J < 16, "a lane of the row");
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J, 0xf, 0xf,
+                                                               false));
+}
+// The same with the lane given by an expression that unrolling makes constant.
+__device__ __forceinline__ float row_bcast(float x, int j) {
+  switch (j) {
+    case 0: return row_bcast_lane<0>(x);
+    case 1: return row_bcast_lane<1>(x);
+    case 2: return row_bcast_lane<2>(x);
+    case 3: return row_bcast_lane<3>(x);
+    case 4: return row_bcast_lane<4>(x);
+    case 5: return row_bcast_lane<5>(x);
+    case 6: return row_bcast_lane<6>(x);
+    case 7: return row_bcast_lane<7>(x);
+    case 8: return row_bcast_lane<8>(x);
+    case 9: return row_bcast_lane<9>(x);
+    case 10: return row_bcast_lane<10>(x);
+    case 11: return row_bcast_lane<11>(x);
+    case 12: return row_bcast_lane<12>(x);
+    case 13: return row_bcast_lane<13>(x);
+    case 14: return row_bcast_lane<14>(x);
+    default: return row_bcast_lane<15>(x);
+  }
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

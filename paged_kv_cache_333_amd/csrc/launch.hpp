@@ -78,6 +78,12 @@ hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t*
                               int32_t num_pairs, int32_t num_blocks, int64_t block_bytes,
                               hipStream_t stream);
 hipError_t launch_upload(void* dst, const void* src_device_view, int64_t nbytes, hipStream_t stream);
+// The quantising write into int8 pools with a scale per (token, KV head)
+// (PA_INT8_TOKEN): each row's scale computed from the row, stored in its tile.
+hipError_t launch_reshape_and_cache_rows(const void* key, const void* value, void* key_cache, void* value_cache,
+                                         const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pa_dtype dtype,
+                                         hipStream_t stream);
 // pa_upload and the slot-mapping write (plain or quantising) in one launch; the
 // slots are read from page-locked host memory (its device view).
 hipError_t launch_upload_and_cache(void* dst, const void* src_device_view, int64_t nbytes, const void* key,

@@ -22,6 +22,8 @@ dimension 128, blocks of 16 or 32 tokens, contexts up to 2048 and beyond):
                    k_scale 0.031, v_scale 0.029
   8 llama7b-fp16-verify4  workload 2's shapes (own draw) with 4 query tokens per sequence
                    (a speculative verification pass of 4 draft tokens)
+  9 llama7b-int8tok  workload 2's shapes (own draw) with int8 pools holding one float32
+                   scale per (token, KV head), fp16 query/output
 
 Draw order for workload k (numpy PCG64, seed 1000+k): context lengths, then the
 pool's initial free order (a permutation), then (workload 5) the suffix
@@ -33,6 +35,8 @@ code scale of CODE_SIGMA (N(0, CODE_SIGMA^2) in code units) and rounded onto
 the code grid: torch's float8_e4m3fn cast after clamping to +-448, or the
 nearest integer clamped to +-127; `normal_codes_host` / `normal_codes_device`.
 With scale ~ 1 / CODE_SIGMA the values they stand for are about N(0, 1).
+Pools with a scale per (token, KV head) take their scales from `row_scales_host` /
+`row_scales_device`: uniform in [0.75, 1.25] / CODE_SIGMA, one per row.
 """
 from __future__ import annotations
 
@@ -43,8 +47,8 @@ import numpy as np
 
 DTYPES = ("f32", "f16", "bf16")
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
-KV_FORMATS = ("fp8_e4m3", "int8")
-CODE_SIGMA = {"fp8_e4m3": 64.0, "int8": 32.0}
+KV_FORMATS = ("fp8_e4m3", "int8", "int8_token")
+CODE_SIGMA = {"fp8_e4m3": 64.0, "int8": 32.0, "int8_token": 32.0}
 
 
 @dataclass
@@ -92,7 +96,7 @@ def _ceil_div(a: int, b: int) -> int:
 
 
 def workload(key: int) -> Workload:
-    """Shapes, context lengths and pool free order of workload `key` (1..5)."""
+    """Shapes, context lengths and pool free order of workload `key` (1..9)."""
     rng = rng_for(key)
     if key == 1:
         w = Workload(1, "tiny-fp32-mha", "f32", 4, 4, 4, 64, 16)
@@ -148,6 +152,10 @@ def workload(key: int) -> Workload:
     if key == 8:
         w = workload_shapes_like(2, key, rng)
         w.name, w.query_len = "llama7b-fp16-verify4", 4
+        return w
+    if key == 9:
+        w = workload_shapes_like(2, key, rng)
+        w.name, w.kv_format = "llama7b-int8tok", "int8_token"
         return w
     raise ValueError(f"unknown workload {key}")
 
@@ -251,11 +259,28 @@ def normal_codes_device(shape, seed: int, fmt: str, device="cuda"):
     return _codes(x, fmt)
 
 
+def row_scales_host(shape, seed: int) -> np.ndarray:
+    """float32 scales, one per (block, KV head, token row): uniform in [0.75, 1.25] / 32,
+    from numpy PCG64(seed)."""
+    rng = np.random.default_rng(seed)
+    return ((np.float32(0.75) + np.float32(0.5) * rng.random(size=shape, dtype=np.float32))
+            / np.float32(CODE_SIGMA["int8_token"])).astype(np.float32)
+
+
+def row_scales_device(shape, seed: int, device="cuda"):
+    """The same distribution from torch's generator on `device`."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    u = torch.rand(shape, generator=g, device=device, dtype=torch.float32)
+    return (0.75 + 0.5 * u) / CODE_SIGMA["int8_token"]
+
+
 def _codes(x, fmt: str):
     import torch
     if fmt == "fp8_e4m3":
         return x.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
-    if fmt == "int8":
+    if fmt in ("int8", "int8_token"):
         return x.round().clamp(-127.0, 127.0).to(torch.int8).view(torch.uint8)
     raise ValueError(fmt)
 
@@ -264,4 +289,5 @@ def tensor_seeds(key: int) -> dict:
     """Derived seeds for the tensor contents of workload `key`."""
     base = 1000 + key
     return {"key_cache": base * 16 + 1, "value_cache": base * 16 + 2, "query": base * 16 + 3,
-            "new_key": base * 16 + 4, "new_value": base * 16 + 5}
+            "new_key": base * 16 + 4, "new_value": base * 16 + 5, "key_scales": base * 16 + 6,
+            "value_scales": base * 16 + 7}

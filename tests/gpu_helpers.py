@@ -86,6 +86,16 @@ def renumber_slots(used: np.ndarray, slots, block_size):
     return np.where(slots >= 0, blk.astype(np.int64) * block_size + slots % block_size, -1).astype(np.int32)
 
 
+def fetch_token_blocks(pool, used: np.ndarray, block_size: int, head_dim: int, kind: str):
+    """(codes, scales) host copies of the listed blocks of a row-scaled int8 pool."""
+    import torch
+
+    import paged_kv_cache_333_amd as pa
+    t = pool.index_select(0, torch.from_numpy(used).to(pool.device))
+    codes, scales = pa.unpack_token_pool(t, block_size, head_dim, kind)
+    return codes.cpu().numpy(), scales.cpu().numpy()
+
+
 def fetch_blocks(pool, used: np.ndarray, dtype: str, quant: bool):
     """Host storage copy of pool[used] (8-bit pools: uint8 codes; bf16: uint16 bits)."""
     import torch

@@ -19,7 +19,8 @@ import synth
 from oracle import allocator as AL
 from oracle import attention as A
 from oracle import cache_ops as OC
-from tests.gpu_helpers import assert_close, fetch_blocks, out_to_f64, renumber, renumber_slots, used_blocks
+from tests.gpu_helpers import (assert_close, fetch_blocks, fetch_token_blocks, out_to_f64, renumber, renumber_slots,
+                               used_blocks)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +50,7 @@ def same_bits(a, b, dtype, quant):
     return np.array_equal(a.view(BITS[dtype]), b.view(BITS[dtype]))
 
 
-@pytest.mark.parametrize("key", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("key", [1, 2, 3, 4, 5, 6, 7, 8, 9])
 def test_bench_step_every_row(key):
     print(f"bench step, workload {key}", flush=True)
     args = bench.parse(["--workload", str(key), "--steps", "1", "--warmup", "0", "--no-cpu-baseline"])
@@ -57,6 +58,7 @@ def test_bench_step_every_row(key):
     w = b.w
     S, L, bs = w.num_seqs, w.query_len, w.block_size
     quant = bool(w.kv_format)
+    rows = w.kv_format == "int8_token"
 
     ora = oracle_allocator(w)
     slots, pairs = ora.seq_append_slots(list(range(S)) * L)
@@ -64,8 +66,14 @@ def test_bench_step_every_row(key):
     if key == 5:
         assert len(pairs) > 0, "the parallel-sampling step copies shared last blocks"
     used = used_blocks(tabs, lens, bs, [x for p in pairs for x in p])
-    kc0 = fetch_blocks(b.kc, used, w.dtype, quant)
-    vc0 = fetch_blocks(b.vc, used, w.dtype, quant)
+
+    def fetch_pools():
+        if rows:
+            return (fetch_token_blocks(b.kc, used, bs, w.head_dim, "key"),
+                    fetch_token_blocks(b.vc, used, bs, w.head_dim, "value"))
+        return fetch_blocks(b.kc, used, w.dtype, quant), fetch_blocks(b.vc, used, w.dtype, quant)
+
+    kc0, vc0 = fetch_pools()
 
     b.step(0, None)
     torch.cuda.synchronize()
@@ -78,22 +86,34 @@ def test_bench_step_every_row(key):
 
     nk = synth.to_numpy(b.newk[0], w.dtype)
     nv = synth.to_numpy(b.newv[0], w.dtype)
-    kc, vc = OC.copy_blocks(kc0, vc0, renumber(used, np.array(pairs, dtype=np.int64).reshape(-1)).reshape(-1, 2))
+    pr = renumber(used, np.array(pairs, dtype=np.int64).reshape(-1)).reshape(-1, 2)
     rs = renumber_slots(used, slots, bs)
-    if quant:
-        kc, vc = OC.reshape_and_cache_quant(nk, nv, kc, vc, rs, w.dtype, w.kv_format, w.k_scale, w.v_scale)
+    kc1, vc1 = fetch_pools()
+    if rows:
+        (kc, ks), (vc, vs) = kc0, vc0
+        kc, vc = OC.copy_blocks(kc, vc, pr)
+        ks, vs = OC.copy_blocks(ks, vs, pr)
+        kc, vc, ks, vs = OC.reshape_and_cache_int8_token(nk, nv, kc, vc, ks, vs, rs, w.dtype)
+        assert np.array_equal(kc1[0], kc) and np.array_equal(vc1[0], vc), "codes after the step"
+        assert np.array_equal(kc1[1].view(np.uint32), ks.view(np.uint32)), "key scales after the step"
+        assert np.array_equal(vc1[1].view(np.uint32), vs.view(np.uint32)), "value scales after the step"
+        qarg = (w.kv_format, ks, vs)
     else:
-        kc, vc = OC.reshape_and_cache(nk, nv, kc, vc, rs)
-    assert same_bits(fetch_blocks(b.kc, used, w.dtype, quant), kc, w.dtype, quant), "key pool after the step"
-    assert same_bits(fetch_blocks(b.vc, used, w.dtype, quant), vc, w.dtype, quant), "value pool after the step"
+        kc, vc = OC.copy_blocks(kc0, vc0, pr)
+        if quant:
+            kc, vc = OC.reshape_and_cache_quant(nk, nv, kc, vc, rs, w.dtype, w.kv_format, w.k_scale, w.v_scale)
+        else:
+            kc, vc = OC.reshape_and_cache(nk, nv, kc, vc, rs)
+        assert same_bits(kc1, kc, w.dtype, quant), "key pool after the step"
+        assert same_bits(vc1, vc, w.dtype, quant), "value pool after the step"
+        qarg = (w.kv_format, w.k_scale, w.v_scale) if quant else None
 
     q = synth.to_numpy(b.q, w.dtype)
     t2 = renumber(used, tabs)
     if L > 1:
         ref = A.paged_decode_multi(q, kc, vc, t2, lens, b.qstart.cpu().numpy(), w.scale, w.dtype)
     else:
-        ref = A.paged_decode(q, kc, vc, t2, lens, w.scale, w.dtype,
-                             quant=(w.kv_format, w.k_scale, w.v_scale) if quant else None)
+        ref = A.paged_decode(q, kc, vc, t2, lens, w.scale, w.dtype, quant=qarg)
     path = "+".join(sorted(b.path_ran))
     assert_close(out_to_f64(b.out, w.dtype), ref, w.dtype, f"workload {key} bench step ({path}), every row")
     if key == 5:
