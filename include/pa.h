@@ -220,14 +220,17 @@ pa_status pa_order_longest_first(const int32_t* context_lens, int32_t n, int32_t
 
 /* Groups for pa_decode_shared, from host block tables (host int32
  * [n, max_blocks]) and context lengths (host [n]).  Consecutive sequences whose
- * first table entry is the same block form a candidate group (the branches of
- * a fork sit next to each other in a batch built in fork order); its prefix P
- * is the number of leading table entries every member shares with the first
- * member, times block_size, capped at the members' shortest context.  A
- * candidate with P below one block becomes groups of one (P = 0).  Writes
- * group_start (host [n + 1], from 0 to n), prefix_len (host [n]),
- * *num_groups and *max_group_size (1 when no group has two members; 0 for
- * n = 0).  PA_ERR_INVALID_ARG on a null pointer or a negative size. */
+ * first table entry is the same block form a group when there are at least two
+ * (the branches of a fork sit next to each other in a batch built in fork
+ * order); a sequence alone is a group of one with prefix 0.  A group's row is
+ * its longest member (the first of them); each member's prefix P_i is the
+ * number of leading table entries it shares with the row, times block_size,
+ * capped at its context, and the row's own prefix is its whole context.
+ * Forked branches that each copied their last block on a write share every
+ * other block, so P_i covers all but that block.  Writes group_start (host
+ * [n + 1], from 0 to n), prefix_len (host [n]), *num_groups and
+ * *max_group_size (1 when no group has two members; 0 for n = 0).
+ * PA_ERR_INVALID_ARG on a null pointer or a negative size. */
 pa_status pa_shared_prefix_groups(const int32_t* tables, const int32_t* context_lens, int32_t n, int32_t max_blocks,
                                   int32_t block_size, int32_t* group_start, int32_t* prefix_len,
                                   int32_t* num_groups, int32_t* max_group_size);
@@ -630,10 +633,12 @@ pa_status pa_decode_multi(void* out, const void* query, const void* key_cache, c
 /* Workspace of pa_decode_shared: room for the three arrays of
  * pa_decode_split_workspace_bytes for num_seqs rows with partitions of an
  * eighth of max_context_len rounded up to 64 tokens (eight partitions, the
- * most a call uses), then one int32 per sequence at the next 256-byte
- * boundary (the prefix length the first pass used).  A call lays the three
- * arrays out from the start for the partition count it picks (see
- * pa_decode_shared), at most eight.  Returns 0 on an invalid argument. */
+ * most a call uses); at the next 256-byte boundaries each sequence's own-token
+ * partial, m and l (fp32 [num_seqs, num_heads] each) and o (fp32 [num_seqs,
+ * num_heads, head_dim]); then, in the last 4 * num_seqs bytes, one int32 per
+ * sequence (the prefix length its partitions covered).  A call lays the
+ * three partition arrays out from the start for the partition count it picks
+ * (see pa_decode_shared), at most eight.  Returns 0 on an invalid argument. */
 size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                         int32_t max_context_len);
 
@@ -645,21 +650,25 @@ size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int
  *   group_start: device int32 [num_groups + 1], from 0 to num_seqs, increasing:
  *     sequences group_start[g] .. group_start[g+1] - 1 form group g (at most
  *     max_group_size of them; a sequence sharing nothing is a group of one).
- *   prefix_len: device int32 [num_seqs], the same P for every member of a
- *     group, 0 <= P <= each member's context length, and the first ceil(P/bs)
- *     table entries of every member equal to its group's first member's.
- * Two launches: the first reads each group's first P tokens once, with the
- * members' queries as the columns of the q.K tile, into per-member partials;
- * the second decodes each sequence's own tokens P .. n-1 (the prefix's blocks
- * are not read) and merges the two by the log-sum-exp rule.  The first
- * launch cuts each group's prefix into P partitions of max_context_len / P
- * (rounded up to 64 tokens), one wave each, P in 1..8 chosen so that the
- * launch fills whole rounds of the workgroups the device holds at once;
- * PA_SHARED_PARTS=1..8 (read on every call) forces P.  A member whose
- * prefix_len differs from its group's, and every member of a group larger
- * than max_group_size, get NaN rows; sequences outside every
- * group, or groups that do not share the blocks they claim, give undefined
- * values (all of this is rejected under PA_DEBUG).  Pools, scales, kv_dtype
+ *   prefix_len: device int32 [num_seqs], each member's prefix P_i,
+ *     0 <= P_i <= its context length; the first ceil(P_i / bs) table entries
+ *     of every member equal those of its group's row, the member with the
+ *     largest P_i (the first of them), e.g. from pa_shared_prefix_groups.
+ * One launch, then the merge.  The launch's first wave items read each
+ * group's prefixes once: a tile of members reads up to its longest P_i
+ * through the table row of the member that has it, with the members'
+ * queries as the columns of the q.K tile and each member's column seeing
+ * only its own first P_i tokens, into per-member partials; its remaining
+ * items read each sequence's own tokens P_i .. n-1 (one wave per sequence and
+ * head tile; the prefix's blocks are not read) into one more partial.  The
+ * merge combines them by the log-sum-exp rule.  Each prefix is cut into P
+ * partitions of max_context_len / P (rounded up to 64 tokens), one wave
+ * each, P in 1..8 chosen so that the prefix items fill whole rounds of the
+ * workgroups the device holds at once; PA_SHARED_PARTS=1..8 (read on every
+ * call) forces P.  Every member of a group larger than max_group_size gets
+ * NaN rows; sequences outside every group, or members that do not share the
+ * blocks they claim, give undefined values (all of this is rejected under
+ * PA_DEBUG).  Pools, scales, kv_dtype
  * and errors as in pa_decode_masked; flags: PA_DECODE_CACHED_KV only;
  * workspace: at least pa_decode_shared_workspace_bytes, 256-byte aligned. */
 pa_status pa_decode_shared(void* out, const void* query, const void* key_cache, const void* value_cache,

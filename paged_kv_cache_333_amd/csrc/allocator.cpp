@@ -783,25 +783,25 @@ pa_status pa_shared_prefix_groups(const int32_t* tables, const int32_t* context_
     int32_t stop = i + 1;
     if (used(i) > 0)
       while (stop < n && used(stop) > 0 && row(stop)[0] == row(i)[0]) ++stop;
-    // tokens every member holds in the same blocks
-    int64_t common = used(i), shortest = std::max(context_lens[i], 0);
-    for (int32_t m = i + 1; m < stop; ++m) {
-      int32_t j = 0;
-      const int32_t lim = std::min(used(m), used(i));
-      while (j < lim && row(m)[j] == row(i)[j]) ++j;
-      common = std::min<int64_t>(common, j);
-      shortest = std::min<int64_t>(shortest, std::max(context_lens[m], 0));
-    }
-    const int64_t p = std::min<int64_t>(common * block_size, shortest);
-    if (stop - i > 1 && p >= block_size) {
+    if (stop - i > 1) {
+      // the group's row: its longest member (the first of them); each member's prefix is
+      // the leading blocks it shares with that row, capped at its context (the row's own
+      // prefix is its whole context)
+      int32_t r = i;
+      for (int32_t m = i + 1; m < stop; ++m)
+        if (context_lens[m] > context_lens[r]) r = m;
       group_start[groups++] = i;
-      for (int32_t m = i; m < stop; ++m) prefix_len[m] = static_cast<int32_t>(p);
-      widest = std::max(widest, stop - i);
-    } else {  // nothing worth sharing: groups of one
       for (int32_t m = i; m < stop; ++m) {
-        group_start[groups++] = m;
-        prefix_len[m] = 0;
+        const int64_t n_m = std::max(context_lens[m], 0);
+        int32_t j = 0;
+        const int32_t lim = std::min(used(m), used(r));
+        while (j < lim && row(m)[j] == row(r)[j]) ++j;
+        prefix_len[m] = static_cast<int32_t>(m == r ? n_m : std::min<int64_t>(static_cast<int64_t>(j) * block_size, n_m));
       }
+      widest = std::max(widest, stop - i);
+    } else {  // nothing shared: a group of one
+      group_start[groups++] = i;
+      prefix_len[i] = 0;
     }
     i = stop;
   }

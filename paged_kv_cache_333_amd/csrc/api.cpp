@@ -829,11 +829,11 @@ static int32_t partition_of(int32_t max_context_len, int32_t parts) {
   return static_cast<int32_t>(p < 64 ? 64 : p);
 }
 
-// The smallest partition pass 1 of pa_decode_shared uses (kMaxPrior = 8
-// pieces): the workspace is sized for it.
+// The smallest partition of the prefixes pa_decode_shared uses (8 pieces of
+// the longest context): the workspace is sized for it.
 static int32_t shared_partition_min(int32_t max_context_len) { return partition_of(max_context_len, 8); }
 
-// Partition of the shared prefixes in pass 1.  Each unit of the pass (a
+// Partition of the shared prefixes.  Each prefix unit of the launch (a
 // group and head tile) cuts the longest context into P pieces, one wave
 // each, and the launch packs the waves four to a workgroup across units, so
 // no P leaves a wave idle.  P in 1..8 minimises the estimated time: the
@@ -871,14 +871,34 @@ static int32_t shared_partition(const pa::DecodeArgs& a, int32_t num_groups, int
   return partition_of(a.max_context_len, best);
 }
 
+// Workspace of the shared-prefix decode: the prefix partials (sized for the
+// smallest partition, whatever partition a call takes), the own-token partials
+// m, l [S x H] and o [S x H x D], then the prefix length each sequence's
+// partials covered, one int per sequence, at the end.
+struct SharedSizes {
+  int64_t own_m, own_l, own_o, len_off, total;
+};
+static bool shared_sizes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
+                  SharedSizes* out) {
+  SplitSizes z;
+  if (!split_sizes(num_seqs, num_heads, head_dim, max_context_len, shared_partition_min(max_context_len), &z))
+    return false;
+  const int64_t rows = static_cast<int64_t>(num_seqs) * num_heads;
+  out->own_m = align256(z.total);
+  out->own_l = align256(out->own_m + rows * 4);
+  out->own_o = align256(out->own_l + rows * 4);
+  out->len_off = align256(out->own_o + rows * head_dim * 4);
+  out->total = out->len_off + static_cast<int64_t>(num_seqs) * 4;
+  return true;
+}
+
 }  // namespace
 
 size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                         int32_t max_context_len) {
-  SplitSizes z;
-  if (!split_sizes(num_seqs, num_heads, head_dim, max_context_len, shared_partition_min(max_context_len), &z))
-    return 0;
-  return static_cast<size_t>(align256(z.total) + static_cast<int64_t>(num_seqs) * 4);
+  SharedSizes z;
+  if (!shared_sizes(num_seqs, num_heads, head_dim, max_context_len, &z)) return 0;
+  return static_cast<size_t>(z.total);
 }
 
 pa_status pa_decode_shared(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -910,25 +930,26 @@ pa_status pa_decode_shared(void* out, const void* query, const void* key_cache, 
   if (num_groups < 1 || num_groups > num_seqs)
     return fail(PA_ERR_INVALID_ARG, "the groups must partition the sequences: 1 <= num_groups <= num_seqs");
   if (!group_start || !prefix_len) return fail(PA_ERR_INVALID_ARG, "null group_start or prefix_len");
-  SplitSizes z;
+  SharedSizes zs;
   // the workspace is checked against the size pa_decode_shared_workspace_bytes
   // returns (the smallest partition), whatever partition this call uses
-  if (!split_sizes(num_seqs, num_heads, head_dim, max_context_len, shared_partition_min(max_context_len), &z))
+  if (!shared_sizes(num_seqs, num_heads, head_dim, max_context_len, &zs))
     return fail(PA_ERR_INVALID_ARG, "workspace sizes");
-  const int64_t len_off = align256(z.total);  // the prefix lengths sit here whatever the partition
-  const int64_t need = len_off + static_cast<int64_t>(num_seqs) * 4;
+  const int64_t need = zs.total;
   if (static_cast<int64_t>(workspace_bytes) < need)
     return fail(PA_ERR_WORKSPACE_TOO_SMALL,
                 "need " + std::to_string(need) + " bytes, got " + std::to_string(workspace_bytes));
   const int32_t part = shared_partition(a, num_groups, max_group_size);
-  if (!split_sizes(num_seqs, num_heads, head_dim, max_context_len, part, &z))
-    return fail(PA_ERR_INVALID_ARG, "workspace sizes");
   pa::SplitLayout ws;
   if ((s = make_layout(workspace, workspace_bytes, num_seqs, num_heads, head_dim, max_context_len, part, &ws)) !=
       PA_OK)
     return s;
   ws.rows = num_seqs;
-  int32_t* ws_len = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + len_off);
+  char* base = static_cast<char*>(workspace);
+  ws.own_m = reinterpret_cast<float*>(base + zs.own_m);
+  ws.own_l = reinterpret_cast<float*>(base + zs.own_l);
+  ws.own_o = reinterpret_cast<float*>(base + zs.own_o);
+  int32_t* ws_len = reinterpret_cast<int32_t*>(base + zs.len_off);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (debug_mode()) {
     if ((s = debug_check_tables(a, st)) != PA_OK) return s;
@@ -943,16 +964,18 @@ pa_status pa_decode_shared(void* out, const void* query, const void* key_cache, 
       const int32_t lead = gs[g], stop = gs[g + 1];
       if (stop <= lead || stop - lead > max_group_size)
         return fail(PA_ERR_BAD_TABLE, "group " + std::to_string(g) + " empty or above max_group_size");
-      const int32_t nb = (pl[lead] + block_size - 1) / block_size;
+      int32_t r = lead;  // the group's row: the member with the largest prefix_len, the first of them
+      for (int32_t i = lead + 1; i < stop; ++i)
+        if (pl[i] > pl[r]) r = i;
       for (int32_t i = lead; i < stop; ++i) {
-        if (pl[i] != pl[lead] || pl[i] < 0 || pl[i] > ctx[i])
-          return fail(PA_ERR_BAD_TABLE, "prefix_len of sequence " + std::to_string(i) +
-                                            " differs from its group's or lies outside [0, its context]");
+        if (pl[i] < 0 || pl[i] > ctx[i])
+          return fail(PA_ERR_BAD_TABLE, "prefix_len of sequence " + std::to_string(i) + " lies outside [0, its context]");
+        const int32_t nb = (pl[i] + block_size - 1) / block_size;
         for (int32_t j = 0; j < nb; ++j)
           if (tab[static_cast<size_t>(i) * max_blocks_per_seq + j] !=
-              tab[static_cast<size_t>(lead) * max_blocks_per_seq + j])
+              tab[static_cast<size_t>(r) * max_blocks_per_seq + j])
             return fail(PA_ERR_BAD_TABLE, "sequence " + std::to_string(i) + " does not share block " +
-                                              std::to_string(j) + " of its group's prefix");
+                                              std::to_string(j) + " with its group's row");
       }
     }
   }

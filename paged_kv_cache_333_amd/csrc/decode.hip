@@ -191,47 +191,46 @@ hipError_t launch_decode_multi(const DecodeArgs& x, const int32_t* query_start, 
 hipError_t launch_decode_shared(const DecodeArgs& x, const int32_t* group_start, int32_t num_groups,
                                 int32_t max_group, const int32_t* prefix_len, const SplitLayout& ws, int32_t* ws_len,
                                 hipStream_t stream) {
-  if (ws.num_parts > kMaxPrior) return hipErrorInvalidValue;  // the merge takes at most kMaxPrior partitions
   const bool cached = (x.flags & PA_DECODE_CACHED_KV) != 0;
-  // Pass 1: each group's shared prefix, read once for all its members (their
-  // queries are the columns of the tile), into per-member partials.
+  // One flat launch.  Its first wave items read each group's shared prefix once for all
+  // its members (their queries are the columns of the tile) into per-member partials; the
+  // rest read each sequence's own tokens after its prefix, one wave per (sequence, head
+  // tile), into one more partial.  Short own items fill in behind the long prefix items.
   DecodeArgs g = x;
   g.num_seqs = num_groups;
   g.context_lens = prefix_len;  // read at each group's first member
   g.seq_order = nullptr;
   g.mask_lo = g.mask_hi = nullptr;
-  DecodeParams p1 = make_params(g);
-  p1.shared = 1;
-  p1.q_start = group_start;
-  p1.num_q_rows = x.num_seqs;
+  DecodeParams p = make_params(g);
+  p.shared = 1;
+  p.q_start = group_start;
+  p.num_q_rows = x.num_seqs;
   int nc = 1, lg = 0, chunks = 1;
   multi_tile(x.num_heads / x.num_kv_heads, max_group, &nc, &lg, &chunks);
-  p1.col_heads_log2 = lg;
-  p1.q_chunks = chunks;
-  p1.ws_m = ws.m;
-  p1.ws_l = ws.l;
-  p1.ws_o = ws.o;
-  p1.part_size = ws.partition_size;
-  p1.num_parts = ws.num_parts;
-  p1.flat = 1;  // the partition count need not be a multiple of the waves per workgroup
-  p1.ws_len = ws_len;
-  hipError_t e = by_dtype(LaunchOp{p1, num_groups, cached, stream}, x.dtype, x.kv_dtype, true, false, x.head_dim,
+  p.col_heads_log2 = lg;
+  p.q_chunks = chunks;
+  p.ws_m = ws.m;
+  p.ws_l = ws.l;
+  p.ws_o = ws.o;
+  p.part_size = ws.partition_size;
+  p.num_parts = ws.num_parts;
+  p.flat = 1;  // the partition count need not be a multiple of the waves per workgroup
+  p.ws_len = ws_len;
+  const int64_t tiles = x.num_heads >> lg;
+  p.n_lead = static_cast<int32_t>(static_cast<int64_t>(num_groups) * tiles * chunks * ws.num_parts);
+  p.n_own = static_cast<int32_t>(static_cast<int64_t>(x.num_seqs) * tiles);
+  p.own_ctx = x.context_lens;
+  p.own_lo = prefix_len;
+  p.own_m = ws.own_m;
+  p.own_l = ws.own_l;
+  p.own_o = ws.own_o;
+  hipError_t e = by_dtype(LaunchOp{p, num_groups, cached, stream}, x.dtype, x.kv_dtype, true, false, x.head_dim,
                           x.block_size, nc);
   if (e != hipSuccess) return e;
-  // Pass 2: every sequence over its own tokens (the prefix masked, its blocks
-  // not read), merged with its prefix partials.
-  DecodeArgs o = x;
-  o.mask_lo = nullptr;
-  o.mask_hi = prefix_len;
-  DecodeParams p2 = make_params(o);
-  p2.prior_m = ws.m;
-  p2.prior_l = ws.l;
-  p2.prior_o = ws.o;
-  p2.prior_len = ws_len;
-  p2.prior_parts = ws.num_parts;
-  p2.prior_part_size = ws.partition_size;
-  return by_dtype(LaunchOp{p2, x.num_seqs, cached, stream}, x.dtype, x.kv_dtype, false, false, x.head_dim,
-                  x.block_size, group_tile(x.num_heads / x.num_kv_heads));
+  // per (sequence, head): the prefix's partitions, then the own tokens' partial; a sequence
+  // whose prefix length differs from the one its group's partitions covered gets NaN
+  return launch_lse_reduce(x.out, ws, ws_len, nullptr, x.num_seqs, x.num_heads, x.head_dim, p.len_limit, x.dtype,
+                           stream, ExtraPartial{ws.own_m, ws.own_l, ws.own_o, prefix_len});
 }
 
 hipError_t multi_pass_shape(const DecodeArgs& x, int32_t max_query_len, int64_t* workgroups, int64_t* resident) {
@@ -259,11 +258,29 @@ hipError_t single_pass_shape(const DecodeArgs& x, int64_t* workgroups, int64_t* 
 
 hipError_t launch_lse_reduce(void* out, const SplitLayout& ws, const int32_t* ctx, const int32_t* order,
                              int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t len_limit,
-                             pa_dtype dt, hipStream_t stream) {
+                             pa_dtype dt, hipStream_t stream, ExtraPartial extra) {
+  if (ws.num_parts + (extra.m ? 1 : 0) <= kSmallParts) {
+    // few partials per row: one wave per (row, head)
+    const dim3 grid(static_cast<uint32_t>((static_cast<int64_t>(num_seqs) * num_heads + 3) / 4));
+#define PA_MERGE(T, D)                                                                                   \
+  launch_kernel(lse_merge_small_kernel<T, D>, grid, dim3(256), stream, out, ws.m, ws.l, ws.o, ctx, order, \
+                num_seqs, num_heads, len_limit, ws.partition_size, ws.num_parts, extra)
+    if (head_dim == 64) {
+      if (dt == PA_F32) PA_MERGE(TF32, 64);
+      else if (dt == PA_F16) PA_MERGE(TF16, 64);
+      else PA_MERGE(TBF16, 64);
+    } else {
+      if (dt == PA_F32) PA_MERGE(TF32, 128);
+      else if (dt == PA_F16) PA_MERGE(TF16, 128);
+      else PA_MERGE(TBF16, 128);
+    }
+#undef PA_MERGE
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<uint32_t>(num_seqs) * num_heads, static_cast<uint32_t>(head_dim / 32));
 #define PA_REDUCE(T, D)                                                                          \
   launch_kernel(lse_reduce_kernel<T, D>, grid, dim3(256), stream, out, ws.m, ws.l, ws.o, \
-                     ctx, order, num_seqs, num_heads, len_limit, ws.partition_size, ws.num_parts)
+                     ctx, order, num_seqs, num_heads, len_limit, ws.partition_size, ws.num_parts, extra)
   if (head_dim == 64) {
     if (dt == PA_F32) PA_REDUCE(TF32, 64);
     else if (dt == PA_F16) PA_REDUCE(TF16, 64);

@@ -87,7 +87,6 @@
 namespace pa {
 
 constexpr int kWaves = 4;
-constexpr int kMaxPrior = 8;  // partitions of a prior partial (the shared-prefix pass)
 
 struct DecodeParams {
   void* out;
@@ -109,21 +108,12 @@ struct DecodeParams {
   const int32_t* q_start;
   int32_t num_q_rows;  // rows of q/out when q_start is set
   // Shared-prefix pass (with q_start, split): "sequence" s is a group of
-  // sequences q_start[s] .. q_start[s+1]-1 whose first ctx[q_start[s]] tokens
-  // are the same blocks; the q_start[s] row of the tables addresses them, every
-  // member's query sees all of them (no causal limit), and the partials land
-  // in the members' rows.
+  // sequences q_start[s] .. q_start[s+1]-1; member i's first ctx[i] tokens sit
+  // in the same blocks as those of the member with the largest ctx (its prefix
+  // length); a tile of members reads up to its longest prefix through that
+  // member's table row, each member's query seeing its own ctx[i] tokens, and
+  // the partials land in the members' rows.
   int32_t shared;
-  // A prior partial per (sequence, head), merged into a single-pass result:
-  // the shared-prefix pass's partitions of the masked positions [0, mask_hi)
-  // (prior_len: the prefix length that pass used, per sequence; it must equal
-  // mask_hi, else the row is NaN).  Null: none.
-  const float* prior_m;
-  const float* prior_l;
-  const float* prior_o;
-  const int32_t* prior_len;
-  int32_t prior_parts;
-  int32_t prior_part_size;
   int32_t col_heads_log2;
   int32_t q_chunks;
   int32_t* ws_len;
@@ -144,6 +134,18 @@ struct DecodeParams {
   // partition count that kWaves does not divide leaves no wave idle.  Never
   // with the fused write.
   int32_t flat;
+  // Flat launch of the shared-prefix decode, nonzero: wave items n_lead .. n_lead + n_own - 1
+  // (after the groups' prefix partitions) are each query row's own tokens: item n_lead + u
+  // takes row u / tiles (tiles = num_heads / 2^col_heads_log2) and its head tile u % tiles,
+  // reads [own_lo[row], own_ctx[row]) of the row's own table, and writes its partial (m, l,
+  // o) to own_m / own_l [row x heads] and own_o [row x heads x D].
+  int32_t n_lead;
+  int32_t n_own;
+  const int32_t* own_ctx;
+  const int32_t* own_lo;
+  float* own_m;
+  float* own_l;
+  float* own_o;
   float scale_log2;    // scale * k_scale * log2(e)
   float v_scale;       // multiplies the output (8-bit value pools; 1 otherwise)
   // fused slot-mapping write (pa_decode_append): new K/V rows [num_seqs, H_kv, D]
@@ -278,24 +280,32 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int per_slot = groups * a.q_chunks;
   int unit = static_cast<int>(blockIdx.x);
   int flat_part = 0;
+  bool own = false;  // a query row's own tokens after the shared prefixes (DecodeParams::n_lead)
   if constexpr (SPLIT && !APPEND) {
     if (a.flat) {  // see DecodeParams::flat
       const int item = static_cast<int>(blockIdx.x) * kWaves + wave;
-      unit = item / a.num_parts;
-      flat_part = item - unit * a.num_parts;
+      if (a.n_lead > 0 && item >= a.n_lead) {
+        own = true;
+        unit = item - a.n_lead;
+      } else {
+        unit = item / a.num_parts;
+        flat_part = item - unit * a.num_parts;
+      }
     }
   }
-  const int slot = unit / per_slot;
-  if (slot >= a.num_seqs) return;  // a flat launch's last workgroup: waves past the last unit
-  const int grp = (unit - slot * per_slot) / a.q_chunks;
-  const int chunk = unit - slot * per_slot - grp * a.q_chunks;
+  // an own item's "sequence" is a query row of the batch, its unit (row, head tile)
+  const int slot = own ? unit / groups : unit / per_slot;
+  const int rows = own ? a.num_q_rows : a.num_seqs;
+  if (slot >= rows) return;  // a flat launch's last workgroup: waves past the last unit
+  const int grp = own ? unit - slot * groups : (unit - slot * per_slot) / a.q_chunks;
+  const int chunk = own ? 0 : unit - slot * per_slot - grp * a.q_chunks;
   const int h0 = grp << lg_h;
   // Workgroups start in blockIdx order; with a longest-first order the long
   // sequences start first and the short ones fill in behind them.
-  const int s = a.order ? a.order[slot] : slot;
-  if (static_cast<uint32_t>(s) >= static_cast<uint32_t>(a.num_seqs)) return;
+  const int s = a.order && !own ? a.order[slot] : slot;
+  if (static_cast<uint32_t>(s) >= static_cast<uint32_t>(rows)) return;
   int qs = s, L = 1;  // the sequence's query rows qs .. qs + L - 1
-  if (a.q_start) {
+  if (a.q_start && !own) {
     qs = a.q_start[s];
     L = a.q_start[s + 1] - qs;
     if (qs < 0 || L < 0 || qs > a.num_q_rows - L) return;  // a span outside the rows: no output
@@ -303,50 +313,50 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int tok0 = chunk * col_toks;
   if (tok0 >= L) return;  // no query token for this workgroup
   const int kvh = h0 / (a.num_heads / a.num_kv_heads);
-  const bool shared = a.shared != 0;  // a group's shared prefix (see DecodeParams)
-  const int nctx = a.ctx[shared ? qs : s];
+  const bool shared = a.shared != 0 && !own;  // a group's shared prefix (see DecodeParams)
+  // A shared tile's members each read their own first ctx[member] tokens (their prefix
+  // lengths differ); the tile reads up to the longest of them from the table row of the
+  // member that has it (the first such), whose blocks hold every member's prefix.
+  int sh_lo = 0, sh_hi = 0, sh_row = qs;
+  if (shared) {
+    sh_lo = 0x7fffffff;
+    sh_hi = -1;
+    const int i_end = min(tok0 + col_toks, L);
+    for (int i = tok0; i < i_end; ++i) {  // wave-uniform: scalar loads
+      const int e = a.ctx[qs + i];
+      if (e > sh_hi) {
+        sh_hi = e;
+        sh_row = qs + i;
+      }
+      sh_lo = min(sh_lo, e);
+    }
+  }
+  const int nctx = own ? a.own_ctx[s] : shared ? sh_hi : a.ctx[s];
   // (an empty context is valid for plain decode: a zero row; a span of query
   // tokens must lie inside the context)
   // (a group with more members than the launch's tiles cover is invalid as a
   // whole: its members get no partials, and the merge sees a -1 length)
-  const bool bad_len = nctx < 0 || nctx > a.len_limit || (a.q_start && !shared && L > nctx) ||
-                       (shared && L > a.q_chunks * col_toks);
+  const bool bad_len = nctx < 0 || nctx > a.len_limit || (a.q_start && !shared && !own && L > nctx) ||
+                       (shared && (sh_lo < 0 || L > a.q_chunks * col_toks)) ||
+                       (own && (a.own_lo[s] < 0 || a.own_lo[s] > nctx));
   // Causal limits: query token i sits at position nctx - L + i and sees the
   // positions before nctx - L + i + 1.  This lane's column, and the tile's
-  // nearest and furthest limits (all nctx for one token per sequence, and for
-  // the members of a shared prefix).
+  // nearest and furthest limits (all nctx for one token per sequence; each
+  // member's own prefix length for the members of a shared tile).
   const int my_tok = tok0 + ((n % NC) >> lg_h);
   const int lim_base = shared ? nctx : nctx - L + 1;
-  const int lane_lim = shared ? nctx : lim_base + min(my_tok, L - 1);
-  const int tile_lim_lo = shared ? nctx : lim_base + tok0;
-  const int tile_lim_hi = shared ? nctx : lim_base + min(tok0 + col_toks, L) - 1;
+  const int lane_lim = shared ? a.ctx[qs + min(my_tok, L - 1)] : lim_base + min(my_tok, L - 1);
+  const int tile_lim_lo = shared ? sh_lo : lim_base + tok0;
+  const int tile_lim_hi = shared ? sh_hi : lim_base + min(tok0 + col_toks, L) - 1;
   int mlo = 0, mhi = 0;  // masked positions; empty unless mask_lo < mask_hi (mask_lo null: 0)
   if (!APPEND && a.mask_hi) {
     mlo = a.mask_lo ? a.mask_lo[s] : 0;
     mhi = a.mask_hi[s];
     if (mhi <= mlo) mlo = mhi = 0;
   }
-  // a prior partial covers [0, mhi); it must be the one the shared pass made
-  const bool use_prior = !SPLIT && a.prior_m && mlo == 0 && mhi > 0;
-  const bool prior_bad = use_prior && (mhi > nctx || a.prior_len[s] != mhi);
-  // Its partitions that hold tokens (only for a valid prefix: mhi <= nctx <=
-  // len_limit lies within them), and this thread's share of their m and l,
-  // loaded now so that the loads overlap the main loop: thread t < NC *
-  // kMaxPrior takes column t / kMaxPrior, partition t % kMaxPrior.
-  const int prior_np = use_prior && !prior_bad && !bad_len
-                           ? min(min((mhi + a.prior_part_size - 1) / a.prior_part_size, a.prior_parts), kMaxPrior)
-                           : 0;
-  float pre_m = kNegInf, pre_l = 0.f;
-  if (prior_np > 0) {
-    const int pg = static_cast<int>(threadIdx.x) / kMaxPrior;
-    const int pp = static_cast<int>(threadIdx.x) - pg * kMaxPrior;
-    const int ptok = tok0 + (pg >> lg_h);
-    if (pg < NC && pp < prior_np && ptok < L) {
-      const int64_t idx =
-          (static_cast<int64_t>(qs + ptok) * a.num_heads + h0 + (pg & (col_heads - 1))) * a.prior_parts + pp;
-      pre_m = a.prior_m[idx] * 1.4426950408889634f;  // base-2 units, like m_run
-      pre_l = a.prior_l[idx];
-    }
+  if (own) {  // the row's shared prefix is masked: its tokens come from the group's partitions
+    mlo = 0;
+    mhi = bad_len ? 0 : a.own_lo[s];
   }
 
   // Single pass: the workgroup's waves share the context, wave w taking steps
@@ -356,12 +366,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int t_all = bad_len ? 0 : tile_lim_hi;  // the tile's range is [0, t_all)
   int t_begin = 0, t_end = t_all, part = 0;
   if constexpr (SPLIT) {
-    part = !APPEND && a.flat ? flat_part : static_cast<int>(blockIdx.y) * kWaves + wave;
-    t_begin = part * a.part_size;
-    t_end = min(t_begin + a.part_size, t_end);
+    // an own item reads its whole range [own_lo, nctx) in one wave
+    part = own ? 0 : !APPEND && a.flat ? flat_part : static_cast<int>(blockIdx.y) * kWaves + wave;
+    t_begin = own ? 0 : part * a.part_size;
+    t_end = own ? t_end : min(t_begin + a.part_size, t_end);
     // the merge needs each query row's context length (any head group writes the same)
-    if (a.ws_len && part == 0 && grp == 0 && q == 0 && n < NC && (n & (col_heads - 1)) == 0 && my_tok < L)
-      a.ws_len[qs + my_tok] = bad_len ? -1 : (shared ? nctx : lim_base + my_tok);
+    if (!own && a.ws_len && part == 0 && grp == 0 && q == 0 && n < NC && (n & (col_heads - 1)) == 0 && my_tok < L)
+      a.ws_len[qs + my_tok] = bad_len ? -1 : (shared ? lane_lim : lim_base + my_tok);
     if (shared && a.ws_len && part == 0 && grp == 0 && chunk == 0) {
       // members past the last tile of the launch: no workgroup computes them
       for (int i = a.q_chunks * col_toks + lane; i < L; i += 64) a.ws_len[qs + i] = -1;
@@ -371,7 +382,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   if constexpr (APPEND)
     fresh.template prepare<BS, TS, SPLIT>(a, s, kvh, nctx, bad_len, t_begin, t_end, wave, lane);
   if constexpr (SPLIT) {
-    if (bad_len || t_begin >= t_all) {  // nothing to read in this partition (no barrier follows)
+    // nothing to read in this partition (no barrier follows); an own item always writes its
+    // partial (no token: m = -inf, l = 0; an invalid row: NaN)
+    if (!own && (bad_len || t_begin >= t_all)) {
       if constexpr (APPEND) {
         if (fresh.pending) fresh.template commit<BS>(a, lane);
       }
@@ -382,7 +395,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int st_skip = mlo <= t_begin && mhi > t_begin ? (min(mhi, t_end) - t_begin) / TS : 0;
   const int st_first = st_skip + (SPLIT ? 0 : wave);
   const int b_end = (t_end + BS - 1) / BS;
-  const int32_t* trow = a.tables + static_cast<int64_t>(shared ? qs : s) * a.max_blocks;
+  const int32_t* trow = a.tables + static_cast<int64_t>(shared ? sh_row : s) * a.max_blocks;
 
   // Q operand of q.K: lane (q, n) holds column n % NC (a padding column past
   // the last query token repeats it), the dims its key chunks hold: chunk
@@ -405,7 +418,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   f32x4 acc[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int bad = 0;
+  int bad = own && bad_len ? 1 : 0;
 
   const int n_steps = (t_end - t_begin + TS - 1) / TS;
   const int64_t hkv = a.num_kv_heads;
@@ -680,7 +693,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       const int g = 4 * q + j;  // first replica of each column
       const int64_t r = g < NC ? out_row(g) : -1;
       if (r >= 0) {
-        float* o = a.ws_o + (r * a.num_parts + part) * D + n;
+        float* o = own ? a.own_o + r * D + n : a.ws_o + (r * a.num_parts + part) * D + n;
 #pragma unroll
         for (int v = 0; v < NV; ++v)
           o[16 * v] = bad ? qnan : (lg[j] == 0.f ? 0.f : acc[v][j] / lg[j] * a.v_scale);  // 0: all masked
@@ -688,9 +701,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     }
     const int64_t rn = q == 0 && n < NC ? out_row(n) : -1;
     if (rn >= 0) {
-      const int64_t idx = rn * a.num_parts + part;
-      a.ws_m[idx] = m_run * 0.6931471805599453f;  // back to natural-log units
-      a.ws_l[idx] = bad ? qnan : l_run;
+      const int64_t idx = own ? rn : rn * a.num_parts + part;
+      (own ? a.own_m : a.ws_m)[idx] = m_run * 0.6931471805599453f;  // back to natural-log units
+      (own ? a.own_l : a.ws_l)[idx] = bad ? qnan : l_run;
     }
     return;
   }
@@ -710,12 +723,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       for (int v = 0; v < NV; ++v) sm_acc[wave][g][16 * v + n] = acc[v][j];
     }
   }
-  __shared__ float sm_pm[NC][kMaxPrior];  // prior partitions: m (base 2) and l; -inf and 0 past prior_np
-  __shared__ float sm_pl[NC][kMaxPrior];
-  if (prior_np > 0 && threadIdx.x < NC * kMaxPrior) {
-    sm_pm[threadIdx.x / kMaxPrior][threadIdx.x % kMaxPrior] = pre_m;
-    sm_pl[threadIdx.x / kMaxPrior][threadIdx.x % kMaxPrior] = pre_l;
-  }
   const int any_bad = __syncthreads_or(bad);
 
   for (int i = threadIdx.x; i < NC * D; i += kWaves * 64) {
@@ -724,19 +731,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     const int tok = tok0 + (g >> lg_h);
     if (tok >= L) continue;  // a padding column
     const int64_t sh = static_cast<int64_t>(qs + tok) * a.num_heads + h0 + (g & (col_heads - 1));
-    float po[kMaxPrior];  // the prior partitions' o for this element, all loads in flight at once
-    if (prior_np > 0) {
-#pragma unroll
-      for (int p = 0; p < kMaxPrior; ++p)
-        po[p] = p < prior_np ? a.prior_o[(sh * a.prior_parts + p) * D + d] : 0.f;
-    }
     float M = kNegInf;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][g]);
-    if (prior_np > 0) {
-#pragma unroll
-      for (int p = 0; p < kMaxPrior; ++p) M = fmaxf(M, sm_pm[g][p]);
-    }
     const float Mu = M == kNegInf ? 0.f : M;
     float Lsum = 0.f, A = 0.f;
 #pragma unroll
@@ -745,19 +742,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       Lsum = __builtin_fmaf(sm_l[w][g], wt, Lsum);
       A = __builtin_fmaf(sm_acc[w][g][d], wt, A);
     }
-    if (prior_np > 0) {
-#pragma unroll
-      for (int p = 0; p < kMaxPrior; ++p) {
-        // o_p is acc_p / l_p with v_scale applied; A is in unscaled acc units.  A
-        // partition with no token (l = 0) has no weight.
-        const float lp = sm_pl[g][p];
-        const float wt = lp == 0.f ? 0.f : lp * fast_exp2(sm_pm[g][p] - Mu);
-        Lsum += wt;
-        A = __builtin_fmaf(po[p] / a.v_scale, wt, A);
-      }
-    }
-    const float val = any_bad || bad_len || prior_bad ? __builtin_nanf("")
-                                                      : (Lsum > 0.f ? A / Lsum * a.v_scale : 0.f);
+    const float val = any_bad || bad_len ? __builtin_nanf("") : (Lsum > 0.f ? A / Lsum * a.v_scale : 0.f);
     store_elem(T{}, a.out, sh * D + d, val);
   }
 }
@@ -772,6 +757,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
 // partition rows are then brought to the common max and summed across lanes
 // and, for the four waves, through LDS.  The summation order depends only on
 // the partition count, not on timing.
+//
+// With an extra partial (x, the shared-prefix decode's own tokens), row (s, h)
+// merges its partitions and then (x.m, x.l, x.o)[s, h], as one more partition;
+// and x.expect[s] must equal ctx[s] (the prefix the partitions covered), else
+// the row is NaN.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float* __restrict__ ws_m,
                                                          const float* __restrict__ ws_l,
@@ -779,7 +769,7 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float*
                                                          const int32_t* __restrict__ ctx,
                                                          const int32_t* __restrict__ order, int32_t num_seqs,
                                                          int32_t num_heads, int32_t len_limit,
-                                                         int32_t part_size, int32_t num_parts) {
+                                                         int32_t part_size, int32_t num_parts, ExtraPartial x) {
   static_assert(D % 32 == 0, "dims in slices of 32");
   constexpr float kLog2e = 1.4426950408889634f;
   constexpr float kNegInf = -__builtin_huge_valf();
@@ -792,11 +782,12 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float*
   const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
   const int d_lo = 32 * static_cast<int>(blockIdx.y);
   const int n = ctx[s];
-  if (n < 0 || n > len_limit) {
+  if (n < 0 || n > len_limit || (x.expect && x.expect[s] != n)) {
     if (threadIdx.x < 32) store_elem(T{}, out, sh * D + d_lo + threadIdx.x, __builtin_nanf(""));
     return;
   }
   const int np = (n + part_size - 1) / part_size;
+  const int nt = np + (x.m ? 1 : 0);  // the partitions, then the extra partial
   const float* mp = ws_m + sh * num_parts;
   const float* lp = ws_l + sh * num_parts;
   const float* op = ws_o + sh * num_parts * D + d_lo + 4 * (threadIdx.x & 7);
@@ -805,7 +796,7 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float*
   const int wave = threadIdx.x >> 6;
 
   float m = kNegInf, L = 0.f, A[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int base = 0; base < np; base += kRows * kRound) {
+  for (int base = 0; base < nt; base += kRows * kRound) {
     float mv[kRound], lv[kRound];
     float4 ov[kRound];
 #pragma unroll
@@ -815,6 +806,10 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float*
         mv[u] = mp[p];
         lv[u] = lp[p];
         ov[u] = *reinterpret_cast<const float4*>(op + static_cast<int64_t>(p) * D);
+      } else if (p == np && x.m) {
+        mv[u] = x.m[sh];
+        lv[u] = x.l[sh];
+        ov[u] = *reinterpret_cast<const float4*>(x.o + sh * D + d_lo + 4 * (threadIdx.x & 7));
       } else {
         mv[u] = kNegInf;
         lv[u] = 0.f;
@@ -877,6 +872,76 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float*
 }
 
 
+// The same merge for rows of few partials (at most kSmallParts, the extra one
+// included): one wave per (row, head), lane l holding dims EL l .. EL l + EL - 1
+// (EL = D / 64), every partial's loads issued at once.  The rule and the
+// handling of empty and invalid partials are those of lse_reduce_kernel; the
+// summation runs in partition order.
+constexpr int kSmallParts = 16;
+template <typename T, int D>
+__global__ __launch_bounds__(256) void lse_merge_small_kernel(void* out, const float* __restrict__ ws_m,
+                                                              const float* __restrict__ ws_l,
+                                                              const float* __restrict__ ws_o,
+                                                              const int32_t* __restrict__ ctx,
+                                                              const int32_t* __restrict__ order, int32_t num_seqs,
+                                                              int32_t num_heads, int32_t len_limit, int32_t part_size,
+                                                              int32_t num_parts, ExtraPartial x) {
+  constexpr int EL = D / 64;
+  constexpr float kLog2e = 1.4426950408889634f;
+  constexpr float kNegInf = -__builtin_huge_valf();
+  const int lane = threadIdx.x & 63;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (item >= static_cast<int64_t>(num_seqs) * num_heads) return;
+  const int slot = static_cast<int>(item / num_heads);
+  const int h = static_cast<int>(item - static_cast<int64_t>(slot) * num_heads);
+  const int s = order ? order[slot] : slot;
+  if (static_cast<uint32_t>(s) >= static_cast<uint32_t>(num_seqs)) return;
+  const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
+  const int n = ctx[s];
+  const int np = n >= 0 && n <= len_limit ? (n + part_size - 1) / part_size : 0;
+  const int nt = np + (x.m ? 1 : 0);
+  if (n < 0 || n > len_limit || (x.expect && x.expect[s] != n) || nt > kSmallParts) {
+#pragma unroll
+    for (int i = 0; i < EL; ++i) store_elem(T{}, out, sh * D + EL * lane + i, __builtin_nanf(""));
+    return;
+  }
+  float mv[kSmallParts], lv[kSmallParts], ov[kSmallParts][EL];
+#pragma unroll
+  for (int p = 0; p < kSmallParts; ++p) {
+    mv[p] = kNegInf;
+    lv[p] = 0.f;
+#pragma unroll
+    for (int i = 0; i < EL; ++i) ov[p][i] = 0.f;
+    if (p < np) {
+      mv[p] = ws_m[sh * num_parts + p];
+      lv[p] = ws_l[sh * num_parts + p];
+#pragma unroll
+      for (int i = 0; i < EL; ++i) ov[p][i] = ws_o[(sh * num_parts + p) * D + EL * lane + i];
+    } else if (p == np && x.m) {
+      mv[p] = x.m[sh];
+      lv[p] = x.l[sh];
+#pragma unroll
+      for (int i = 0; i < EL; ++i) ov[p][i] = x.o[sh * D + EL * lane + i];
+    }
+  }
+  float M = kNegInf;
+#pragma unroll
+  for (int p = 0; p < kSmallParts; ++p) M = fmaxf(M, mv[p]);
+  float L = 0.f, A[EL];
+#pragma unroll
+  for (int i = 0; i < EL; ++i) A[i] = 0.f;
+#pragma unroll
+  for (int p = 0; p < kSmallParts; ++p) {
+    // a partition with no token (l = 0, m = -inf: all masked) has no weight
+    const float w = lv[p] == 0.f ? 0.f : lv[p] * fast_exp2((mv[p] - M) * kLog2e);
+    L += w;
+#pragma unroll
+    for (int i = 0; i < EL; ++i) A[i] = __builtin_fmaf(w, ov[p][i], A[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < EL; ++i) store_elem(T{}, out, sh * D + EL * lane + i, L == 0.f ? 0.f : A[i] / L);
+}
+
 // The kernel instance for (dtype, head_dim, block_size, heads per workgroup)
 // is chosen at run time; Op::run<T, D, BS, GT, SPLIT>() does the work with it.
 struct LaunchOp {
@@ -888,7 +953,7 @@ struct LaunchOp {
   hipError_t run() const {
     const int64_t units = static_cast<int64_t>(num_seqs) * (p.num_heads >> p.col_heads_log2) * p.q_chunks;
     const bool flat = SPLIT && !APPEND && p.flat;
-    const uint32_t gx = static_cast<uint32_t>(flat ? (units * p.num_parts + kWaves - 1) / kWaves : units);
+    const uint32_t gx = static_cast<uint32_t>(flat ? (units * p.num_parts + p.n_own + kWaves - 1) / kWaves : units);
     const uint32_t gy = SPLIT && !flat ? static_cast<uint32_t>((p.num_parts + kWaves - 1) / kWaves) : 1u;
     if (cached)
       launch_kernel(decode_kernel<T, S, D, BS, GT, SPLIT, true, APPEND>, dim3(gx, gy), dim3(kWaves * 64), stream, p);

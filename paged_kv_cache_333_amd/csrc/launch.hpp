@@ -62,6 +62,20 @@ struct SplitLayout {
   int32_t partition_size;
   int32_t num_parts;
   int32_t rows = 0;  // rows of the partials (sequences; query rows for several query tokens)
+  // the shared-prefix decode's own-token partials, one per (row, head): m, l [rows x heads],
+  // o [rows x heads x head_dim]
+  float* own_m = nullptr;
+  float* own_l = nullptr;
+  float* own_o = nullptr;
+};
+
+// One more partial per (row, head) for the log-sum-exp merge, and the context
+// length each row's partitions must have covered (see lse_reduce_kernel).
+struct ExtraPartial {
+  const float* m = nullptr;
+  const float* l = nullptr;
+  const float* o = nullptr;
+  const int32_t* expect = nullptr;
 };
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,
@@ -116,9 +130,9 @@ hipError_t launch_decode_multi(const DecodeArgs& a, const int32_t* query_start, 
 hipError_t multi_pass_shape(const DecodeArgs& a, int32_t max_query_len, int64_t* workgroups, int64_t* resident);
 // Groups of sequences sharing their first prefix_len tokens' blocks: sequences
 // group_start[g] .. group_start[g+1]-1, prefix_len per sequence (equal within a
-// group).  Pass 1 reads each group's prefix once into per-member partials
-// (ws, one int per sequence in ws_len); pass 2 decodes each sequence's own
-// tokens and merges.
+// group).  One flat launch reads each group's prefix once into per-member
+// partials (ws, one int per sequence in ws_len) and each sequence's own tokens
+// into one more partial (ws.own_*); the merge combines them.
 hipError_t launch_decode_shared(const DecodeArgs& a, const int32_t* group_start, int32_t num_groups,
                                 int32_t max_group, const int32_t* prefix_len, const SplitLayout& ws, int32_t* ws_len,
                                 hipStream_t stream);
@@ -128,6 +142,6 @@ hipError_t launch_decode_shared(const DecodeArgs& a, const int32_t* group_start,
 hipError_t static_scratch(void** ptr);
 hipError_t launch_lse_reduce(void* out, const SplitLayout& ws, const int32_t* context_lens,
                              const int32_t* seq_order, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                             int32_t len_limit, pa_dtype dtype, hipStream_t stream);
+                             int32_t len_limit, pa_dtype dtype, hipStream_t stream, ExtraPartial extra = {});
 
 }  // namespace pa

@@ -238,11 +238,13 @@ def test_shared_prefix_decode_validation_rejects_before_launch():
     assert _shared(ws=16) == 1               # not 256-byte aligned
     assert _shared(D=96) == 5
     assert _shared(kv=pa.PA_FP8_E4M3, ks=0.0) == 1
-    # m and l (4 x 32 rows of one 64-token partition, each padded to 256 bytes), o, then
-    # one int per sequence
-    assert pa.pa_decode_shared_workspace_bytes(4, 32, 128, 64) == 512 + 512 + 4 * 32 * 128 * 4 + 4 * 4
+    # m and l (4 x 32 rows of one 64-token partition, each padded to 256 bytes), o; the
+    # own-token partials m, l (4 x 32 each) and o; then one int per sequence
+    own = 512 + 512 + 4 * 32 * 128 * 4
+    assert pa.pa_decode_shared_workspace_bytes(4, 32, 128, 64) == 512 + 512 + 4 * 32 * 128 * 4 + own + 4 * 4
     # 4096 tokens: eight partitions of 512
-    assert pa.pa_decode_shared_workspace_bytes(4, 32, 128, 4096) == 4096 + 4096 + 4 * 32 * 8 * 128 * 4 + 4 * 4
+    assert pa.pa_decode_shared_workspace_bytes(4, 32, 128, 4096) == \
+        4096 + 4096 + 4 * 32 * 8 * 128 * 4 + own + 4 * 4
     assert pa.pa_decode_shared_workspace_bytes(-1, 32, 128, 64) == 0
 
 

@@ -282,30 +282,34 @@ def test_random_swap_and_window_ops_bit_exact(seed):
     same_host_state(c2, o2)
 
 
-def _groups_reference(tables, lens, bs):
-    """Shared-prefix groups written out from their definition in include/pa.h."""
+def _groups_reference(rows, lens, bs):
+    """The grouping written out: consecutive sequences whose first block is the same form a
+    group when there are at least two; its row is its longest member (the first of them);
+    each member's prefix is the number of leading table entries it shares with the row,
+    times bs, capped at its context (the row's is its whole context)."""
     n = len(lens)
-    used = [min(-(-max(c, 0) // bs), len(tables[i])) for i, c in enumerate(lens)]
+    used = [min(-(-max(x, 0) // bs), len(rows[0]) if rows else 0) for x in lens]
     gs, pl, widest = [], [0] * n, 1 if n else 0
     i = 0
     while i < n:
         stop = i + 1
-        while used[i] and stop < n and used[stop] and tables[stop][0] == tables[i][0]:
-            stop += 1
-        shared = []
-        for m in range(i, stop):
-            k = 0
-            while k < min(used[m], used[i]) and tables[m][k] == tables[i][k]:
-                k += 1
-            shared.append(k)
-        p = min(min(shared) * bs, min(max(lens[m], 0) for m in range(i, stop)))
-        if stop - i > 1 and p >= bs:
+        if used[i] > 0:
+            while stop < n and used[stop] > 0 and rows[stop][0] == rows[i][0]:
+                stop += 1
+        if stop - i > 1:
+            r = i
+            for m in range(i + 1, stop):
+                if lens[m] > lens[r]:
+                    r = m
             gs.append(i)
             for m in range(i, stop):
-                pl[m] = p
+                k = 0
+                while k < min(used[m], used[r]) and rows[m][k] == rows[r][k]:
+                    k += 1
+                pl[m] = max(lens[m], 0) if m == r else min(k * bs, max(lens[m], 0))
             widest = max(widest, stop - i)
         else:
-            gs.extend(range(i, stop))
+            gs.append(i)
         i = stop
     return gs + [n], pl, len(gs), widest
 
@@ -314,7 +318,8 @@ def _groups_reference(tables, lens, bs):
 def test_shared_prefix_groups_match_definition(seed):
     """Random families of forked sequences (shared leading blocks, then own blocks), loners
     and empty sequences: the C++ grouping equals the definition, and every member's first
-    P tokens sit in the same (block, offset) as its group's first member's."""
+    P tokens sit in the same (block, offset) as those of its group's member with the largest
+    P (the first of them), the row the decode reads the group through."""
     rng = np.random.default_rng(seed)
     bs = int(rng.choice([16, 32]))
     tables, lens = [], []
@@ -344,17 +349,19 @@ def test_shared_prefix_groups_match_definition(seed):
     gs, pl, ng, mg = got
     assert gs[0] == 0 and gs[-1] == len(lens) and all(a < b for a, b in zip(gs, gs[1:]))
     for g in range(ng):
-        lead = gs[g]
-        for m in range(gs[g], gs[g + 1]):
-            assert pl[m] == pl[lead] <= lens[m]
+        members = range(gs[g], gs[g + 1])
+        row = max(members, key=lambda m: (pl[m], -m))
+        for m in members:
+            assert 0 <= pl[m] <= max(lens[m], 0)
             for t in range(pl[m]):
-                assert rows[m][t // bs] == rows[lead][t // bs]
+                assert rows[m][t // bs] == rows[row][t // bs]
 
 
 def test_shared_prefix_groups_of_a_forked_batch():
     """Parallel sampling through the allocator: three parents of 100, 64 and 40 tokens forked
     into 3, 2 and 1 branches; each branch appends its own tokens (copy-on-write of the last
-    block).  The families become the groups; a single branch is a group of one."""
+    block).  The families become the groups, read through their first branch; the others
+    share every block but their own last one; a single branch is a group of one."""
     bs = 16
     al = pa.Allocator(200, bs)
     sid = 0
@@ -371,8 +378,10 @@ def test_shared_prefix_groups_of_a_forked_batch():
     tabs, lens = al.build_block_tables(ids, 16)
     gs, pl, ng, mg = pa.pa_shared_prefix_groups(tabs, lens, bs)
     # 100 tokens: 6 full blocks shared, the 7th copied on the first append; 64 tokens: 4 full blocks
+    # shared, the 5th each branch's own; a group's first branch (the longest, by index on ties)
+    # is its row and has its whole context as its prefix
     assert (gs, ng, mg) == ([0, 3, 5, 6], 3, 3)
-    assert pl == [96, 96, 96, 64, 64, 0]
+    assert pl == [105, 96, 96, 69, 64, 0]
 
 
 def test_pa_log_dumps_tables(monkeypatch, capfd):

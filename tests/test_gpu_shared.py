@@ -1,11 +1,12 @@
 """GPU parity of the shared-prefix decode (pa_decode_shared): families of forked sequences
-that share their leading blocks, read once per family, then each sequence's own tokens,
-merged.  Against the float64 oracle's plain decode (the definition does not change) for
-every model dtype and both 8-bit formats, head groups 1 to 8, families of 1 to 17
-members (more members than the 16 columns of a tile), members whose context ends inside
-the shared blocks, long prefixes over several partitions, empty sequences; groups from
-pa_shared_prefix_groups and hand-made shorter prefixes; a member whose prefix length
-differs from its group's gets NaN rows.  Unused rows of the pools are poisoned."""
+that share their leading blocks, read once per family with each member seeing its own
+prefix, then each sequence's own tokens, merged.  Against the float64 oracle's plain decode
+(the definition does not change) for every model dtype and both 8-bit formats, head groups
+1 to 8, families of 1 to 17 members (more members than the 16 columns of a tile), members
+whose context ends inside the shared blocks, long prefixes over several partitions, empty
+sequences; groups from pa_shared_prefix_groups, hand-made shorter prefixes and members of
+one group with different prefixes; a prefix beyond its member's context gives that
+member NaN rows.  Unused rows of the pools are poisoned."""
 import zlib
 
 import numpy as np
@@ -140,15 +141,22 @@ def test_shorter_hand_made_prefixes(dt):
         assert_close(run_shared(c, dv, (gs, pl2, ng, mg)), ref, dt, f"prefix cut to {cut}")
 
 
-def test_member_with_a_different_prefix_length_gets_nan_rows():
+def test_members_with_different_prefixes():
+    """A member's prefix may be any length its blocks share with its group's row: members of
+    one group cut to 32 and to 5 tokens (the rest read from their own blocks) match the
+    oracle; a prefix longer than the member's context gives that member NaN rows only."""
     c = make_case(5, "f16", None, 4, 4, 64, 16)
     gs, pl, ng, mg = pa.pa_shared_prefix_groups(c["tables"].tolist(), c["ctx"], 16)
-    assert pl[1] == 48
-    pl[1] = 32                                   # the group's first member says 48
-    got = run_shared(c, dev(c), (gs, pl, ng, mg))
-    assert np.all(np.isnan(got[1]))
+    assert pl[:5] == [48, 48, 48, 88, 48]     # the family's row is its longest member, 88 tokens
+    pl[1] = 32
+    pl[2] = 5
     ref = oracle(c)
-    ok = [s for s in range(c["S"]) if s != 1]
+    got = run_shared(c, dev(c), (gs, pl, ng, mg))
+    assert_close(got, ref, "f16", "different prefixes")
+    pl[4] = 60                                   # beyond its 48 tokens
+    got = run_shared(c, dev(c), (gs, pl, ng, mg))
+    assert np.all(np.isnan(got[4]))
+    ok = [s for s in range(c["S"]) if s != 4]
     assert_close(got[ok], ref[ok], "f16", "the other sequences")
 
 
