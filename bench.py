@@ -89,6 +89,7 @@ def parse(argv=None):
                          "half written by one pa_copy_blocks launch over a scratch pool; at least 512 MiB written "
                          "is twice the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--json-out", metavar="PATH", help="also write the result line to PATH")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain copy of known size instead (pa_copy_blocks, 1 GiB read + 1 GiB written "
@@ -177,7 +178,9 @@ def measure_swap(launches: int = 10):
 # rocprofv3: kernel trace + HBM counters of the decode kernel, scaled by the same
 # counters read on a plain copy of known size (pa_copy_blocks moving 1 GiB).
 
-PROFILE_STEPS = {"trace": (20, 5, 50), "counters": (3, 2, 5)}  # (steps, warmup, decode reps)
+# (steps, warmup, decode reps): the bench's defaults, so that the repetitions decode the same
+# inputs as a default bench run's (the last step's); the counter runs take fewer repetitions
+PROFILE_STEPS = {"trace": (50, 10, 50), "counters": (50, 10, 10)}
 REP_WARM = 5  # untimed repetitions before each timed set in Bench.kernel_timing
 
 
@@ -194,7 +197,7 @@ def profile_commands(workload: int, outdir: str, path: str | None) -> list[str]:
     ts, tw, tr = PROFILE_STEPS["trace"]
     cs, cw, cr = PROFILE_STEPS["counters"]
     cmds = [f"rocprofv3 --kernel-trace --stats -f csv -d {outdir}/trace -o run -- "
-            f"{bench}{sel} --steps {ts} --warmup {tw} --decode-reps {tr}"]
+            f"{bench}{sel} --steps {ts} --warmup {tw} --decode-reps {tr} --json-out {outdir}/trace/bench.json"]
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
         cmds.append(f"rocprofv3 --pmc {ctr} -f csv -d {outdir}/{ctr.lower()} -o run -- "
                     f"{bench}{sel} --steps {cs} --warmup {cw} --decode-reps {cr}")
@@ -216,18 +219,26 @@ def _csv_rows(folder: str, suffix: str):
     return rows
 
 
-def _counter_per_dispatch(folder: str, counter: str, kernel_substr: str) -> tuple[float, int]:
+def _counter_per_dispatch(folder: str, counter: str, kernel_substr: str,
+                          pick: tuple[int, int] | None = None) -> tuple[float, int]:
     """Mean over dispatches of `counter` (summed over its rows per dispatch) for kernels whose
-    name contains kernel_substr."""
+    name contains kernel_substr; with pick = (first, count), over those dispatches only, counted
+    in dispatch order among the matching ones."""
     per = {}
     for r in _csv_rows(folder, "counter_collection.csv"):
         if r.get("counter_name") != counter or kernel_substr not in r.get("kernel_name", ""):
             continue
-        d = r.get("dispatch_id") or r.get("correlation_id")
+        d = int(r.get("dispatch_id") or r.get("correlation_id"))
         per[d] = per.get(d, 0.0) + float(r["counter_value"])
     if not per:
         raise SystemExit(f"no {counter} rows for *{kernel_substr}* under {folder}")
-    return sum(per.values()) / len(per), len(per)
+    vals = [per[d] for d in sorted(per)]
+    if pick is not None:
+        if len(vals) < pick[0] + pick[1]:
+            raise SystemExit(f"{len(vals)} *{kernel_substr}* dispatches under {folder}, expected at least "
+                             f"{pick[0] + pick[1]}")
+        vals = vals[pick[0]:pick[0] + pick[1]]
+    return sum(vals) / len(vals), len(vals)
 
 
 def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
@@ -242,18 +253,17 @@ def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
     dec = [r for r in stats if decode in r["name"]]
     if not dec:
         raise SystemExit("decode kernel missing from the kernel trace")
-    # the shared-prefix path launches the decode kernel twice per call (the groups' prefixes,
-    # then the sequences' own tokens): its figures are per call, both launches together
-    per_call = 2 if w_path == "shared" else 1
-    if per_call == 2 and len(dec) < 2:
-        raise SystemExit("the shared-prefix path's two decode launches are not both in the trace")
-    dec_avg_ns = sum(float(r["averagens"]) for r in dec[:per_call])
+    # one decode launch per call on every path (the split and shared-prefix paths merge in a
+    # second kernel, listed on its own in the trace)
+    if len(dec) != 1:
+        raise SystemExit(f"{len(dec)} decode kernel instances in the trace, expected one")
+    dec_avg_ns = float(dec[0]["averagens"])
     # per-dispatch durations of the decode kernel, in dispatch order: the step loop's decodes,
     # then the flushed repetitions, then the back-to-back ones (each set after REP_WARM untimed)
     trace = [r for r in _csv_rows(os.path.join(outdir, "trace"), "kernel_trace.csv") if decode in r["kernel_name"]]
     trace.sort(key=lambda r: int(r["dispatch_id"]))
     durs = [(int(r["end_timestamp"]) - int(r["start_timestamp"])) / 1e3 for r in trace]
-    calls = [sum(durs[i:i + per_call]) for i in range(0, len(durs) - per_call + 1, per_call)]
+    calls = durs
     ts, tw, tr = PROFILE_STEPS["trace"]
     if len(calls) != ts + tw + 2 * (tr + REP_WARM):
         raise SystemExit(f"{len(calls)} decode calls in the trace, expected {ts + tw + 2 * (tr + REP_WARM)}")
@@ -262,13 +272,21 @@ def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
               "flushed": calls[a + REP_WARM:a + REP_WARM + tr],
               "back to back": calls[a + 2 * REP_WARM + tr:]}
     copy_bytes = 8192 // 2 * 32 * 16 * 128 * 2 * 2   # calibrate_copy: read (= written) per launch
+    cs, cw, cr = PROFILE_STEPS["counters"]
+    flushed_reps = (cs + cw + REP_WARM, cr)  # the counter runs' flushed repetitions
     scale, meas = {}, {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
         ck, cn = _counter_per_dispatch(os.path.join(outdir, f"copy_{ctr.lower()}"), ctr, "copy_blocks_kernel")
         scale[ctr] = copy_bytes / (ck * 1024.0)
-        meas[ctr] = _counter_per_dispatch(os.path.join(outdir, ctr.lower()), ctr, decode)
-        meas[ctr] = (meas[ctr][0] * per_call, meas[ctr][1] // per_call, ck, cn)
+        meas[ctr] = _counter_per_dispatch(os.path.join(outdir, ctr.lower()), ctr, decode, flushed_reps)
+        meas[ctr] = (meas[ctr][0], meas[ctr][1], ck, cn)
     traffic = sum(meas[c][0] * 1024.0 * scale[c] for c in meas)
+    # the traced bench run's own line: the same decodes timed by its HIP events, and their bytes
+    with open(os.path.join(outdir, "trace", "bench.json"), encoding="utf-8") as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    alg = line["decode_alg_bytes"]
+    ev_med = line["decode_us"]["flushed"]["median"]
+    rp_med = percentiles(phases["flushed"])["median"]
     key = f"workload{workload}-{w_path}"
     try:
         with open(TRAFFIC_FILE, encoding="utf-8") as f:
@@ -279,7 +297,8 @@ def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
                 "fetch_kib_per_dispatch": meas["FETCH_SIZE"][0], "write_kib_per_dispatch": meas["WRITE_SIZE"][0],
                 "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"],
                 "rocprof_decode_avg_us": dec_avg_ns / 1e3,
-                "rocprof_decode_flushed_median_us": percentiles(phases["flushed"])["median"]}
+                "rocprof_decode_flushed_median_us": rp_med, "events_call_flushed_median_us": ev_med,
+                "alg_bytes_per_launch": alg}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w", encoding="utf-8") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
@@ -297,25 +316,30 @@ def summarize_profile(workload: int, outdir: str, path: str | None) -> None:
         name = r["name"] if len(r["name"]) < 90 else r["name"][:87] + "..."
         out.append(f"| `{name}` | {r['calls']} | {float(r['averagens']) / 1e3:.2f} | "
                    f"{float(r['minns']) / 1e3:.2f} | {float(r['maxns']) / 1e3:.2f} | {float(r['percentage']):.1f} |")
-    out += ["", "Decode " + ("call (both launches)" if per_call == 2 else "kernel") +
-            " duration per dispatch in the trace, by phase of the run:", "",
+    out += ["", "Decode kernel duration per dispatch in the trace, by phase of the run:", "",
             "| phase | dispatches | median us | p10 us | p90 us |", "|---|---|---|---|---|"]
     for name, v in phases.items():
         st = percentiles(v)
         out.append(f"| {name} | {st['n']} | {st['median']:.2f} | {st['p10']:.2f} | {st['p90']:.2f} |")
-    out += ["", "## HBM counters (--pmc, one counter per run, KiB per dispatch)", "",
-            "| counter | decode kernel" + (" (both launches of a call)" if per_call == 2 else "") +
-            " | " + ("calls" if per_call == 2 else "dispatches") + " | copy kernel (1 GiB each way) | dispatches | scale |",
+    merge = [r for r in stats if "lse_" in r["name"]]
+    merge_us = float(merge[0]["averagens"]) / 1e3 if merge else 0.0
+    out += ["", f"The traced run's own bench line times the same flushed decode calls by HIP events at a median "
+                f"of {ev_med:.2f} us (decode kernel"
+                + (f" and merge, {merge_us:.2f} us average in the trace" if merge else "") + f"). Algorithmic bytes "
+                f"of one call on these inputs: {alg / 1e6:.2f} MB, so {alg / ev_med / 1e3:.0f} GB/s by the events "
+                f"and {alg / (rp_med + merge_us) / 1e3:.0f} GB/s by the trace.", ""]
+    out += ["## HBM counters (--pmc, one counter per run, KiB per dispatch)", "",
+            f"Averaged over the {cr} flushed repetitions of each counter run (the last step's inputs, as above).", "",
+            "| counter | decode kernel | dispatches | copy kernel (1 GiB each way) | dispatches | scale |",
             "|---|---|---|---|---|---|"]
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         v, n, ck, cn = meas[c]
         out.append(f"| {c} | {v:.1f} | {n} | {ck:.1f} | {cn} | {scale[c]:.4f} |")
-    unit = "call (both launches)" if per_call == 2 else "launch"
-    out += ["", f"Scaled HBM traffic per decode {unit}: **{traffic / 1e6:.2f} MB** "
+    out += ["", f"Scaled HBM traffic per decode launch: **{traffic / 1e6:.2f} MB**, {traffic / alg:.3f} of the "
+                f"algorithmic bytes "
                 f"(fetch {meas['FETCH_SIZE'][0] * 1024 * scale['FETCH_SIZE'] / 1e6:.2f} MB + write "
                 f"{meas['WRITE_SIZE'][0] * 1024 * scale['WRITE_SIZE'] / 1e6:.2f} MB); "
-                f"average decode duration in the trace {dec_avg_ns / 1e3:.2f} us"
-                + (" (the two launches' averages added)." if per_call == 2 else ".")]
+                f"average decode duration in the trace {dec_avg_ns / 1e3:.2f} us."]
     print("\n".join(out))
 
 
@@ -799,6 +823,10 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = bench.cpu_baseline(args.cpu_seconds)
     print(json.dumps(res), flush=True)
+    if args.json_out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.json_out)), exist_ok=True)
+        with open(args.json_out, "w", encoding="utf-8") as f:
+            f.write(json.dumps(res) + "\n")
 
 
 if __name__ == "__main__":
