@@ -277,10 +277,11 @@ hipError_t launch_lse_reduce(void* out, const SplitLayout& ws, const int32_t* ct
 #undef PA_MERGE
     return hipGetLastError();
   }
+  if (extra.m) return hipErrorInvalidValue;  // the extra partial comes with few partitions only
   const dim3 grid(static_cast<uint32_t>(num_seqs) * num_heads, static_cast<uint32_t>(head_dim / 32));
 #define PA_REDUCE(T, D)                                                                          \
   launch_kernel(lse_reduce_kernel<T, D>, grid, dim3(256), stream, out, ws.m, ws.l, ws.o, \
-                     ctx, order, num_seqs, num_heads, len_limit, ws.partition_size, ws.num_parts, extra)
+                     ctx, order, num_seqs, num_heads, len_limit, ws.partition_size, ws.num_parts)
   if (head_dim == 64) {
     if (dt == PA_F32) PA_REDUCE(TF32, 64);
     else if (dt == PA_F16) PA_REDUCE(TF16, 64);

@@ -757,11 +757,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
 // partition rows are then brought to the common max and summed across lanes
 // and, for the four waves, through LDS.  The summation order depends only on
 // the partition count, not on timing.
-//
-// With an extra partial (x, the shared-prefix decode's own tokens), row (s, h)
-// merges its partitions and then (x.m, x.l, x.o)[s, h], as one more partition;
-// and x.expect[s] must equal ctx[s] (the prefix the partitions covered), else
-// the row is NaN.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float* __restrict__ ws_m,
                                                          const float* __restrict__ ws_l,
@@ -769,7 +764,7 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float*
                                                          const int32_t* __restrict__ ctx,
                                                          const int32_t* __restrict__ order, int32_t num_seqs,
                                                          int32_t num_heads, int32_t len_limit,
-                                                         int32_t part_size, int32_t num_parts, ExtraPartial x) {
+                                                         int32_t part_size, int32_t num_parts) {
   static_assert(D % 32 == 0, "dims in slices of 32");
   constexpr float kLog2e = 1.4426950408889634f;
   constexpr float kNegInf = -__builtin_huge_valf();
@@ -782,12 +777,11 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float*
   const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
   const int d_lo = 32 * static_cast<int>(blockIdx.y);
   const int n = ctx[s];
-  if (n < 0 || n > len_limit || (x.expect && x.expect[s] != n)) {
+  if (n < 0 || n > len_limit) {
     if (threadIdx.x < 32) store_elem(T{}, out, sh * D + d_lo + threadIdx.x, __builtin_nanf(""));
     return;
   }
   const int np = (n + part_size - 1) / part_size;
-  const int nt = np + (x.m ? 1 : 0);  // the partitions, then the extra partial
   const float* mp = ws_m + sh * num_parts;
   const float* lp = ws_l + sh * num_parts;
   const float* op = ws_o + sh * num_parts * D + d_lo + 4 * (threadIdx.x & 7);
@@ -796,7 +790,7 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float*
   const int wave = threadIdx.x >> 6;
 
   float m = kNegInf, L = 0.f, A[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int base = 0; base < nt; base += kRows * kRound) {
+  for (int base = 0; base < np; base += kRows * kRound) {
     float mv[kRound], lv[kRound];
     float4 ov[kRound];
 #pragma unroll
@@ -806,10 +800,6 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float*
         mv[u] = mp[p];
         lv[u] = lp[p];
         ov[u] = *reinterpret_cast<const float4*>(op + static_cast<int64_t>(p) * D);
-      } else if (p == np && x.m) {
-        mv[u] = x.m[sh];
-        lv[u] = x.l[sh];
-        ov[u] = *reinterpret_cast<const float4*>(x.o + sh * D + d_lo + 4 * (threadIdx.x & 7));
       } else {
         mv[u] = kNegInf;
         lv[u] = 0.f;
@@ -877,6 +867,11 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float*
 // (EL = D / 64), every partial's loads issued at once.  The rule and the
 // handling of empty and invalid partials are those of lse_reduce_kernel; the
 // summation runs in partition order.
+//
+// With an extra partial (x, the shared-prefix decode's own tokens), row (s, h)
+// merges its partitions and then (x.m, x.l, x.o)[s, h], as one more partition;
+// and x.expect[s] must equal ctx[s] (the prefix the partitions covered), else
+// the row is NaN.
 constexpr int kSmallParts = 16;
 template <typename T, int D>
 __global__ __launch_bounds__(256) void lse_merge_small_kernel(void* out, const float* __restrict__ ws_m,

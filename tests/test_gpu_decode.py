@@ -163,6 +163,61 @@ def test_lse_reduce_many_partitions_and_empty_ones(D):
     assert np.array_equal(got[4], np.zeros((H, D)))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_lse_reduce_few_partitions_empty_and_invalid_rows(D, dt):
+    """The merge alone on rows of at most 16 partitions (the one-wave merge): partitions
+    with no token (l = 0, m = -inf) first, in the middle and last; the largest m in any
+    of them; a row whose partitions are all empty gives zeros; a row with no partition
+    (length 0) gives zeros; a length above the bound or below 0 gives NaN."""
+    S, H, ps = 7, 3, 32
+    max_ctx = ps * 12
+    ctx = [max_ctx, max_ctx - 31, ps * 5 + 1, 1, max_ctx, 0, max_ctx + 1]
+    lay = pa.split_layout(S, H, D, max_ctx, ps)
+    P = lay["parts"]
+    assert P <= 16
+    rng = np.random.default_rng(100 + D)
+    m = rng.normal(size=(S, H, P)) * 3
+    m[0, :, 0] += 25           # the max in the first partition
+    m[1, :, 11] += 25          # in the last
+    m[2, :, 3] += 25           # in the middle
+    l_ = rng.uniform(1, 60, size=(S, H, P))
+    empty = np.zeros((S, H, P), dtype=bool)
+    empty[0, :, 1] = empty[0, :, 11] = True
+    empty[1, :, 0] = empty[1, :, 5] = True
+    empty[2, :, 2] = True
+    empty[4] = True            # a row with no token in any partition
+    l_[empty] = 0.0
+    m[empty] = -np.inf
+    o = rng.normal(size=(S, H, P, D))
+    o[empty] = 0.0
+    buf = np.zeros(lay["total"] // 4, dtype=np.float32)
+    buf[: S * H * P] = m.ravel()
+    buf[lay["off_l"] // 4: lay["off_l"] // 4 + S * H * P] = l_.ravel()
+    buf[lay["off_o"] // 4:] = o.ravel()
+    ws = torch.from_numpy(buf).cuda()
+    lens = torch.tensor(ctx, dtype=torch.int32).cuda()
+    out = torch.full((S, H, D), 7.0, dtype=TD[dt], device="cuda")
+    pa.pa_lse_reduce(out, ws, lens, max_ctx, ps)
+    torch.cuda.synchronize()
+    got = out_to_f64(out, dt)
+    for s in range(4):
+        np_ = -(-ctx[s] // ps)
+        for h in range(H):
+            ref = A.lse_merge(m[s, h, :np_].astype(np.float32).astype(np.float64),
+                              l_[s, h, :np_].astype(np.float32).astype(np.float64),
+                              o[s, h, :np_].astype(np.float32).astype(np.float64))
+            assert_close(got[s, h], ref, dt, f"{dt} seq {s} head {h}")
+    assert np.array_equal(got[4], np.zeros((H, D))), "all partitions empty"
+    assert np.array_equal(got[5], np.zeros((H, D))), "length 0"
+    assert np.isnan(got[6]).all(), "length above the bound"
+    lens[6] = -3
+    out.fill_(7.0)
+    pa.pa_lse_reduce(out, ws, lens, max_ctx, ps)
+    torch.cuda.synchronize()
+    assert np.isnan(out_to_f64(out, dt)[6]).all(), "negative length"
+
+
 def test_tiny_fp32_workload_before_and_after_the_write():
     """Workload 1: contexts {1,16,17,45}; then one new token per sequence is written and the
     decode runs over {2,17,18,46} including it."""
