@@ -66,6 +66,9 @@ def parse(argv=None):
                          "pa_shared_prefix_groups each step); default: shared for the parallel-sampling "
                          "workload (5), auto otherwise")
     ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="run the workload with this block size instead (8, 16, 32 or 64): same contexts, a "
+                         "pool of the same token capacity, its free order drawn again")
     ap.add_argument("--fused-write", action="store_true",
                     help="write the new K/V inside the decode launch (pa_decode_append, auto path) instead of "
                          "pa_reshape_and_cache before it; measured no faster per step, so off by default")
@@ -376,6 +379,10 @@ class Bench:
         self.np, self.torch, self.pa, self.synth = np, torch, pa, synth
         self.args = args
         self.w = w = synth.workload(args.workload)
+        if args.block_size and args.block_size != w.block_size:
+            if args.workload in (1, 5):
+                raise SystemExit("--block-size applies to the growing workloads (2-4, 6-9)")
+            self.w = w = synth.with_block_size(w, args.block_size)
         self.path = args.path = default_path(args.workload, args.path)
         self.path_ran = set()
         shared = args.workload == 5
@@ -806,7 +813,9 @@ def main():
                          if not (args.separate_upload or bench.rows) else "pa_upload, then the write (two launches)"),
                    "partition_size": args.partition if "split" in bench.path_ran else None,
                    "launch_order": bench.order, "kv_cache_policy": "cached" if bench.cached else "stream",
-                   "cow_pairs_per_step": sum(t[3] for t in timing) / len(timing)},
+                   "cow_pairs_per_step": sum(t[3] for t in timing) / len(timing),
+                   # KV slots holding a token, over the slots of the blocks the tables hold (last step)
+                   "kv_slot_utilization": timing[-1][1] / max(1, timing[-1][2] * w.block_size)},
         "decode_kernel_us": stats["flushed"]["median"] * 1e3,
         "decode_us": {k: {q: (v * 1e3 if q != "n" else v) for q, v in st.items()} for k, st in stats.items()},
         "decode_timing": (f"median, p10, p90 of HIP events attached to the decode's kernels: 'flushed' = "

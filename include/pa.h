@@ -35,8 +35,9 @@
  *                   apart, so it touches every 128-byte line of its tile, and
  *                   the decode that follows pays 8-16 us for rereading those
  *                   lines at the LLaMA-7B-like shapes (64 sequences x 32 heads).
- *                   pa_upload_and_cache narrows that with a whole-tile write for
- *                   32-token blocks and non-temporal stores for 16-token blocks.
+ *                   pa_upload_and_cache narrows that with a whole-tile write
+ *                   where a value row is 64 bytes (or 32 bytes of 8-bit codes)
+ *                   and non-temporal stores otherwise.
  *
  * Beyond the pages' problem interface (query, pools, block_tables,
  * context_lens, scale), the decode calls take two more arguments: seq_order
@@ -53,8 +54,9 @@
  * groups; num_heads must be a multiple of num_kv_heads).
  *
  * Supported shapes: dtype f32, f16, bf16 (8-bit pools: see the quantised KV
- * cache below); head_dim 64 or 128; block_size 16 or 32.  Other values
- * return PA_ERR_UNSUPPORTED.
+ * cache below); head_dim 64 or 128; block_size 16 or 32, and with head_dim
+ * 128 also 8 or 64 (the block sizes 8-64 of [SRC-1] §五;
+ * 8-bit pools: 16, 32 or 64).  Other values return PA_ERR_UNSUPPORTED.
  *
  * Streams: device calls enqueue work on `stream` (a hipStream_t; NULL is the
  * null stream) and return without synchronising.  The library allocates no
@@ -402,12 +404,13 @@ pa_status pa_upload(void* dst, const void* src, size_t nbytes, void* stream);
  * for that copy (use pa_upload, pa_copy_blocks, then the write).  The call
  * also reads slot_mapping on the host, so it must hold its final values when
  * the call is made.  When no two tokens' slots fall in one block (a decode
- * step appending one token per sequence) and block_size is 32, the write
+ * step appending one token per sequence) and a value tile's dim row is 64
+ * bytes (block_size x element bytes; or 32 bytes of 8-bit codes), the write
  * stores each written value tile whole (every cache line of the tile, the
- * other columns unchanged) rather than one element per dim row; with
- * 16-token blocks and model-type pools it stores the elements with
- * non-temporal stores.  The result is the same.  PA_TILE_WRITE=always /
- * never overrides the block-size rule
+ * other columns unchanged) rather than one element per dim row; otherwise,
+ * for model-type pools, it stores the elements with non-temporal stores.
+ * The result is the same.  PA_TILE_WRITE=always / never overrides the
+ * row-size rule
  * (never the one-token-per-block condition).  Errors as in pa_upload and the
  * write it stands for.  Bit-exact. */
 pa_status pa_upload_and_cache(void* dst, const void* src, size_t nbytes, const void* key, const void* value,

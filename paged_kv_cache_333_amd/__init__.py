@@ -197,7 +197,7 @@ def _pool_dims(key_cache, value_cache, head_dim=None):
         NB, H_kv, tile = key_cache.shape
         if head_dim is None:
             raise ValueError("pools of int8 codes with row scales need head_dim")
-        bs = next((b for b in (16, 32) if token_tile_bytes(b, head_dim) == tile), None)
+        bs = next((b for b in (16, 32, 64) if token_tile_bytes(b, head_dim) == tile), None)
         if bs is None or tuple(value_cache.shape) != tuple(key_cache.shape) or \
                 key_cache.element_size() != 1 or value_cache.element_size() != 1:
             raise ValueError(f"row-scaled int8 pools must both be uint8 [num_blocks, num_kv_heads, "

@@ -57,19 +57,27 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Form of pa_upload_and_cache's write when every token has a block of its
 // own.  The whole-tile form rewrites each written value tile in full lines
-// instead of one element per dim row.  Measured on full decode steps: with
-// 32-token blocks it shortens the step (GQA bf16 216 -> 200 us, the decode
-// after it running at its clean-cache speed); with 16-token blocks the step
-// is the same either way, the time the shorter write saves reappearing in
-// the decode that follows, so the element-wise form stays there, with
-// non-temporal stores (see put in cache_ops.hip).
+// instead of one element per dim row.  What decides is the bytes of one dim
+// row of a value tile (block_size * element bytes), measured on full decode
+// steps:
+//   64 bytes: tiles (16-bit, 32-token blocks: GQA bf16 step 216 -> 200 us, the
+//     decode after it running at its clean-cache speed; 8-bit, 64-token blocks:
+//     int8 GQA 132.5 -> 117.9 us, FP8 130.7 -> 127.9 us);
+//   32 bytes of codes: tiles (8-bit, 32-token blocks: int8 GQA 130 -> 123 us);
+//   32 bytes of 16-bit elements, 16 bytes: the same either way (the time the
+//     shorter write saves reappears in the decode), so the element-wise form
+//     stays, with non-temporal stores for model-type pools (see put in
+//     cache_ops.hip);
+//   128 bytes (16-bit, 64-token blocks): the element-wise form (tiles made the
+//     LLaMA-7B-like step 219 -> 248 us).
 // PA_TILE_WRITE=always / never overrides the rule (read on every call); the
 // whole-tile form is never used when two tokens share a block.
-bool tile_write_wanted(int32_t block_size) {
+bool tile_write_wanted(int32_t block_size, int32_t elem_bytes) {
   const char* v = std::getenv("PA_TILE_WRITE");
   if (v && std::strcmp(v, "always") == 0) return true;
   if (v && std::strcmp(v, "never") == 0) return false;
-  return block_size >= 32;
+  const int32_t row = block_size * elem_bytes;
+  return row == 64 || (elem_bytes == 1 && row == 32);
 }
 
 pa_status hip_fail(hipError_t e, const char* what) {
@@ -79,7 +87,15 @@ pa_status hip_fail(hipError_t e, const char* what) {
 pa_status check_shape(pa_dtype dt, int32_t head_dim, int32_t block_size) {
   if (dt != PA_F32 && dt != PA_F16 && dt != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype");
   if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
-  if (block_size != 16 && block_size != 32) return fail(PA_ERR_UNSUPPORTED, "block_size must be 16 or 32");
+  if (block_size != 16 && block_size != 32 && !(head_dim == 128 && (block_size == 8 || block_size == 64)))
+    return fail(PA_ERR_UNSUPPORTED, "block_size must be 16 or 32, or 8 or 64 with head_dim 128");
+  return PA_OK;
+}
+
+// A decode step over 8-bit codes spans 64 tokens, at most four blocks: no 8-token blocks.
+pa_status check_code_block(pa_dtype kv_dtype, int32_t block_size) {
+  if (is_code_type(kv_dtype) && block_size == 8)
+    return fail(PA_ERR_UNSUPPORTED, "8-bit pools need block_size 16, 32 or 64");
   return PA_OK;
 }
 
@@ -108,6 +124,7 @@ pa_status fetch(std::vector<T>& host, const T* dev, size_t n, hipStream_t st) {
 pa_status check_decode_args(const pa::DecodeArgs& a) {
   pa_status s = check_shape(a.dtype, a.head_dim, a.block_size);
   if (s != PA_OK) return s;
+  if ((s = check_code_block(a.kv_dtype, a.block_size)) != PA_OK) return s;
   if (a.num_seqs < 0 || a.num_heads <= 0 || a.num_kv_heads <= 0 || a.max_blocks_per_seq < 0 ||
       a.num_blocks < 0 || a.max_context_len < 0)
     return fail(PA_ERR_INVALID_ARG, "negative size or zero heads");
@@ -353,6 +370,7 @@ pa_status pa_reshape_and_cache_quant(const void* key, const void* value, void* k
   pa_status s = check_shape(dtype, head_dim, block_size);
   if (s != PA_OK) return s;
   if (!is_code_type(kv_dtype)) return fail(PA_ERR_UNSUPPORTED, "kv_dtype must be an 8-bit code type");
+  if ((s = check_code_block(kv_dtype, block_size)) != PA_OK) return s;
   if (kv_dtype != PA_INT8_TOKEN && (s = check_scales(k_scale, v_scale)) != PA_OK) return s;
   if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0)
     return fail(PA_ERR_INVALID_ARG, "negative size or zero heads");
@@ -485,6 +503,7 @@ pa_status pa_upload_and_cache(void* dst, const void* src, size_t nbytes, const v
                               float k_scale, float v_scale, pa_dtype dtype, pa_dtype kv_dtype, void* stream) {
   pa_status s = check_shape(dtype, head_dim, block_size);
   if (s != PA_OK) return s;
+  if ((s = check_code_block(kv_dtype, block_size)) != PA_OK) return s;
   const bool quant = is_code_type(kv_dtype);
   if (kv_dtype == PA_INT8_TOKEN)
     return fail(PA_ERR_UNSUPPORTED, "per-row int8 pools are written by pa_reshape_and_cache_quant");
@@ -523,7 +542,8 @@ pa_status pa_upload_and_cache(void* dst, const void* src, size_t nbytes, const v
   // quantising write's one-byte non-temporal stores made the FP8 step slower, 125 -> 130 us); else
   // plain element-wise stores
   const bool own_blocks = num_tokens > 0 && pa::one_token_per_block(slot_mapping, num_tokens, num_blocks, block_size);
-  const int32_t form = !own_blocks ? 0 : tile_write_wanted(block_size) ? 2 : quant ? 0 : 1;
+  const int32_t elem = quant ? 1 : dtype == PA_F32 ? 4 : 2;
+  const int32_t form = !own_blocks ? 0 : tile_write_wanted(block_size, elem) ? 2 : quant ? 0 : 1;
   return finish(pa::launch_upload_and_cache(dst, src_view, static_cast<int64_t>(nbytes), key, value, key_cache,
                                             value_cache, static_cast<const int32_t*>(slots_view), num_tokens,
                                             num_blocks, num_kv_heads, head_dim, block_size, dtype, kv_dtype,

@@ -525,6 +525,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       for (int l = 0; l < KL; ++l) kr[tau][l] = CACHED ? load16(kp + l * 64) : load16_stream(kp + l * 64);
     }
     // V columns: lane (q, n) supplies dim 16v + n of tokens TPL q .. TPL q + TPL-1.
+    // A block longer than a step (16-bit and fp32 elements with 64-token blocks)
+    // spreads each 128-byte line of a value row over several steps, which other
+    // waves read at about the same time: those loads keep the line in the L2 for
+    // them (64-token fp16 blocks, decode inside the step 207 instead of 224 us;
+    // after a cache flush, though, 245 instead of 222 us).
+    constexpr bool V_CACHED = CACHED || BS > TS;
     u32x4 vr[NV];
     float ks1 = 1.f, vs1 = 1.f;  // (ROWS) the key and value scales of the step's token `lane`
     if constexpr (ROWS) {
@@ -545,7 +551,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       const char* vp = a.vc + (phys * hkv + kvh) * KT + (n * BS + (x - bi * BS)) * SB;
 #pragma unroll
       for (int v = 0; v < NV; ++v)
-        vr[v] = CACHED ? load16(vp + v * 16 * BS * SB) : load16_stream(vp + v * 16 * BS * SB);
+        vr[v] = V_CACHED ? load16(vp + v * 16 * BS * SB) : load16_stream(vp + v * 16 * BS * SB);
     }
     // All of the step's loads are issued before any of them is consumed.
     __builtin_amdgcn_sched_barrier(0);
@@ -987,6 +993,10 @@ hipError_t by_shape(const Op& op, int d, int bs, int gt) {
   if (d == 64 && bs == 32) return by_group<T, S, 64, 32, SPLIT, APPEND>(op, gt);
   if (d == 128 && bs == 16) return by_group<T, S, 128, 16, SPLIT, APPEND>(op, gt);
   if (d == 128 && bs == 32) return by_group<T, S, 128, 32, SPLIT, APPEND>(op, gt);
+  if (d == 128 && bs == 64) return by_group<T, S, 128, 64, SPLIT, APPEND>(op, gt);
+  if constexpr (S::kBytes != 1) {  // a step of 8-bit codes (64 tokens) would span eight 8-token blocks
+    if (d == 128 && bs == 8) return by_group<T, S, 128, 8, SPLIT, APPEND>(op, gt);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -176,6 +176,21 @@ def workload_shapes_like(base: int, key: int, rng: np.random.Generator) -> Workl
     return w
 
 
+def with_block_size(w: Workload, block_size: int) -> Workload:
+    """Workload w with another block size: the same contexts, a pool of the same token capacity
+    (num_blocks * block_size kept, rounded up) and a free order drawn again, from a seed of
+    the workload and the block size."""
+    import dataclasses
+    v = dataclasses.replace(w)
+    v.block_size = block_size
+    v.num_blocks = _ceil_div(w.num_blocks * w.block_size, block_size)
+    v.free_order = np.random.default_rng(
+        np.random.SeedSequence([1000 + w.key, block_size])).permutation(v.num_blocks).astype(np.int32)
+    if w.partition_size:
+        v.partition_size = max(w.partition_size, block_size)
+    return v
+
+
 def pool_shapes(w: Workload):
     """Shapes of the key pool [NB, H_kv, bs, D] and the value pool [NB, H_kv, D, bs]."""
     return ((w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim),

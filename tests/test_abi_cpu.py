@@ -64,7 +64,9 @@ def _decode(**kw):
 
 def test_decode_validation_rejects_before_launch():
     assert _decode(D=96) == 5
-    assert _decode(bs=8) == 5
+    assert _decode(bs=8, D=64) == 5   # 8- and 64-token blocks come with head_dim 128 only
+    assert _decode(bs=64, D=64) == 5
+    assert _decode(bs=12) == 5
     assert _decode(dt=7) == 5
     assert _decode(H=6, Hkv=4) == 1
     assert _decode(Hkv=0) == 1
@@ -147,6 +149,9 @@ def test_decode_quant_validation_rejects_before_launch():
     assert _decode_quant(flags=pa.PA_DECODE_SPLIT, ps=24)[0] == 1  # not a multiple of block_size
     assert _decode_quant(flags=pa.PA_DECODE_SPLIT, ps=512) == (0, 1)
     assert _decode_quant(D=96)[0] == 5
+    assert _decode_quant(bs=64) == (0, 0)
+    assert _decode_quant(bs=8)[0] == 5               # a 64-token step of codes spans at most four blocks
+    assert _decode_quant(bs=8, kv=pa.PA_INT8_TOKEN)[0] == 5
 
 
 def test_reshape_quant_validation_rejects_before_launch():
@@ -166,6 +171,9 @@ def test_reshape_quant_validation_rejects_before_launch():
     assert call(T=-1) == 1
     assert call(T=3, k=0) == 1
     assert call(T=3, kc=8) == 1                     # not 16-byte aligned
+    assert call(D=128, bs=64) == 0
+    assert call(D=128, bs=8) == 5                   # 8-bit pools: no 8-token blocks
+    assert call(D=128, bs=8, kv=pa.PA_INT8_TOKEN) == 5
 
 
 def test_copy_blocks_accepts_8bit_pools():

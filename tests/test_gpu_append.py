@@ -74,6 +74,8 @@ def _run_both(c, key, val, slots, split_ps=None):
 
 FAMILIES = [(dt, D, bs, H, Hkv) for dt in ("f32", "f16", "bf16") for D in (64, 128) for bs in (16, 32)
             for (H, Hkv) in ((4, 4), (16, 4), (16, 1), (32, 1))]
+FAMILIES += [(dt, 128, bs, H, Hkv) for dt in ("f32", "f16", "bf16") for bs in (8, 64)
+             for (H, Hkv) in ((4, 4), (16, 1))]
 
 
 @pytest.mark.parametrize("dt,D,bs,H,Hkv", FAMILIES, ids=lambda v: str(v))

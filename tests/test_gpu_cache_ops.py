@@ -12,7 +12,8 @@ from tests.gpu_helpers import DeviceWorkload
 pytestmark = pytest.mark.gpu
 
 SHAPES = [("f32", 64, 16, 4), ("f16", 128, 16, 32), ("bf16", 128, 32, 8), ("f16", 64, 32, 2),
-          ("bf16", 64, 16, 1), ("f32", 128, 32, 3)]
+          ("bf16", 64, 16, 1), ("f32", 128, 32, 3), ("f16", 128, 8, 4), ("bf16", 128, 64, 2),
+          ("f32", 128, 8, 2), ("f32", 128, 64, 1)]
 
 
 def _dev(a, dtype):
@@ -161,7 +162,8 @@ def test_upload_rejects_pageable_source_without_launching():
 
 
 @pytest.mark.parametrize("dtype,D,bs,Hkv,fmt", [s + (None,) for s in SHAPES] +
-                         [("f16", 128, 16, 8, "fp8_e4m3"), ("bf16", 64, 32, 2, "int8"), ("f32", 128, 16, 4, "fp8_e4m3")])
+                         [("f16", 128, 16, 8, "fp8_e4m3"), ("bf16", 64, 32, 2, "int8"), ("f32", 128, 16, 4, "fp8_e4m3"),
+                          ("bf16", 128, 64, 2, "int8")])
 @pytest.mark.parametrize("form", ["rule", "always"])
 def test_upload_and_cache_equals_upload_then_write(dtype, D, bs, Hkv, fmt, form, monkeypatch):
     """One launch: the index block arrives bit for bit and the write (slots read from the
@@ -221,7 +223,9 @@ _NAN_BITS = {"f32": (np.uint32, 0x7FC0_0123), "f16": (np.uint16, 0x7E05), "bf16"
                          [("f16", 128, 16, 8, "fp8_e4m3", 17), ("bf16", 64, 32, 2, "int8", 17),
                           ("f32", 128, 32, 4, "fp8_e4m3", 17), ("bf16", 128, 16, 8, "int8", 17),
                           ("f16", 128, 16, 32, None, 256), ("f16", 128, 32, 32, None, 300),
-                          ("bf16", 128, 32, 8, "int8", 300), ("f32", 64, 16, 3, None, 257)])
+                          ("bf16", 128, 32, 8, "int8", 300), ("f32", 64, 16, 3, None, 257),
+                          ("f16", 128, 64, 4, "fp8_e4m3", 17), ("f16", 128, 8, 32, None, 256),
+                          ("bf16", 128, 64, 8, None, 300)])
 @pytest.mark.parametrize("form", ["always", "rule", "never"])
 def test_upload_and_cache_one_token_per_block(dtype, D, bs, Hkv, fmt, T, form, monkeypatch):
     """Every token in a block of its own, as in a decode step that appends one token per

@@ -82,6 +82,9 @@ def oracle(c):
 # shapes spanning every built kernel family: dtype x head_dim x block_size x group tile
 FAMILIES = [(dt, D, bs, H, Hkv) for dt in ("f32", "f16", "bf16") for D in (64, 128) for bs in (16, 32)
             for (H, Hkv) in ((4, 4), (8, 4), (16, 4), (16, 2), (6, 2))]
+# 8- and 64-token blocks (head_dim 128): a step spans four blocks, or half a block
+FAMILIES += [(dt, 128, bs, H, Hkv) for dt in ("f32", "f16", "bf16") for bs in (8, 64)
+             for (H, Hkv) in ((4, 4), (16, 4), (16, 2))]
 
 
 @pytest.mark.parametrize("dt,D,bs,H,Hkv", FAMILIES, ids=lambda v: str(v))

@@ -123,9 +123,11 @@ def mask_set(bs):
 
 
 @pytest.mark.parametrize("dt,fmt", KINDS, ids=lambda v: str(v))
-@pytest.mark.parametrize("D,bs", [(64, 16), (128, 32), (128, 16)])
+@pytest.mark.parametrize("D,bs", [(64, 16), (128, 32), (128, 16), (128, 8), (128, 64)])
 @pytest.mark.parametrize("H,Hkv", [(4, 4), (8, 2)])
 def test_masked_decode_families(dt, fmt, D, bs, H, Hkv):
+    if fmt and bs == 8:
+        pytest.skip("8-bit pools take no 8-token blocks (rejected on the host, tested on the CPU)")
     ms = mask_set(bs)
     ctx, lo, hi = [m[0] for m in ms], [m[1] for m in ms], [m[2] for m in ms]
     c = make_case(zlib.crc32(repr((dt, fmt, D, bs, H, Hkv)).encode()) % 10000, dt, fmt, H, Hkv, D, bs, ctx, lo,

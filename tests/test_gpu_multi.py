@@ -99,9 +99,11 @@ SPANS = (1, 1, 4, 7, 16, 3, 16, 0)   # one token, a few, a full tile, the whole 
 
 
 @pytest.mark.parametrize("dt,fmt", KINDS, ids=lambda v: str(v))
-@pytest.mark.parametrize("D,bs", [(64, 16), (128, 32), (128, 16)])
+@pytest.mark.parametrize("D,bs", [(64, 16), (128, 32), (128, 16), (128, 8), (128, 64)])
 @pytest.mark.parametrize("H,Hkv", [(4, 4), (8, 2), (16, 2), (6, 2)])
 def test_multi_families(dt, fmt, D, bs, H, Hkv):
+    if fmt and bs == 8:
+        pytest.skip("8-bit pools take no 8-token blocks (rejected on the host, tested on the CPU)")
     c = make_case(zlib.crc32(repr((dt, fmt, D, bs, H, Hkv)).encode()) % 10000, dt, fmt, H, Hkv, D, bs, CTX, SPANS)
     dv = dev(c)
     ref = oracle(c)

@@ -92,6 +92,7 @@ def oracle(c):
 
 FAMILIES = [(fmt, dt, D, bs, H, Hkv) for fmt in FMTS for dt in ("f16", "bf16") for D in (64, 128)
             for bs in (16, 32) for (H, Hkv) in ((4, 4), (8, 4), (16, 4), (16, 2), (6, 2))]
+FAMILIES += [(fmt, dt, 128, 64, H, Hkv) for fmt in FMTS for dt in ("f16", "bf16") for (H, Hkv) in ((4, 4), (16, 2))]
 
 
 @pytest.mark.parametrize("fmt,dt,D,bs,H,Hkv", FAMILIES, ids=lambda v: str(v))
@@ -184,7 +185,7 @@ def special_rows(dtype, shape, seed, fmt):
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("D,bs", [(64, 16), (64, 32), (128, 16), (128, 32)])
+@pytest.mark.parametrize("D,bs", [(64, 16), (64, 32), (128, 16), (128, 32), (128, 64)])
 def test_quant_write_bit_exact(fmt, dt, D, bs):
     seed = zlib.crc32(repr((fmt, dt, D, bs)).encode()) % 10000
     rng = np.random.default_rng(seed)

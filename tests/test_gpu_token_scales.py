@@ -74,7 +74,7 @@ def u32(a):
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("D,bs", [(64, 16), (128, 16), (128, 32)])
+@pytest.mark.parametrize("D,bs", [(64, 16), (128, 16), (128, 32), (128, 64)])
 def test_row_write_bit_exact(dt, D, bs):
     NB, Hkv, T = 12, 2, 7
     seed = zlib.crc32(repr((dt, D, bs)).encode()) % 10000
@@ -107,6 +107,7 @@ def test_row_write_bit_exact(dt, D, bs):
 
 FAMILIES = [(dt, D, bs, H, Hkv) for dt in ("f16", "bf16") for D in (64, 128) for bs in (16, 32)
             for (H, Hkv) in ((4, 4), (8, 2), (16, 2))]
+FAMILIES += [(dt, 128, 64, H, Hkv) for dt in ("f16", "bf16") for (H, Hkv) in ((4, 4), (16, 2))]
 
 
 @pytest.mark.parametrize("dt,D,bs,H,Hkv", FAMILIES, ids=lambda v: str(v))
