@@ -797,3 +797,6 @@ class Allocator:
         _check(lib.pa_allocator_get_stats(self._h, C.byref(st)), "pa_allocator_get_stats")
         return {"blocks_allocated": st.blocks_allocated, "blocks_freed": st.blocks_freed,
                 "cow_copies": st.cow_copies}
+
+
+from .cache import PagedAttention  # noqa: E402  (the object interface over the calls above)
