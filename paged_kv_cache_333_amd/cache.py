@@ -9,7 +9,9 @@ the library's calls and adds nothing to what they compute:
   - key/value pools on the device, keys [num_blocks, num_kv_heads, block_size, head_dim],
     values [num_blocks, num_kv_heads, head_dim, block_size];
   - per forward(): the allocator's append, pa_upload of the step's index data, pa_copy_blocks
-    for copy-on-write pairs, pa_reshape_and_cache of the new tokens' K/V and pa_decode_auto.
+    for copy-on-write pairs, pa_reshape_and_cache of the new tokens' K/V, and pa_decode_auto,
+    or pa_decode_shared when requests forked from one parent sit side by side in the batch
+    (their common blocks are then read once for all of them).
 Calls are enqueued on torch's current stream, as every call of the binding.  One instance
 is used from one host thread.
 """
@@ -19,8 +21,9 @@ import math
 
 import numpy as np
 
-from . import (Allocator, pa_copy_blocks, pa_decode_auto, pa_decode_split_workspace_bytes, pa_order_longest_first,
-               pa_reshape_and_cache, pa_upload)
+from . import (Allocator, pa_copy_blocks, pa_decode_auto, pa_decode_shared, pa_decode_shared_workspace_bytes,
+               pa_decode_split_workspace_bytes, pa_order_longest_first, pa_reshape_and_cache,
+               pa_shared_prefix_groups, pa_upload)
 
 
 class PagedAttention:
@@ -95,7 +98,9 @@ class PagedAttention:
         """One decode step.  For every request a slot is appended (a shared, partly filled last
         block is first copied), the new token's K/V rows key/value [S, num_kv_heads, head_dim]
         are written there, and query [S, num_heads, head_dim] attends over the request's
-        context including that token.  Returns out [S, num_heads, head_dim]."""
+        context including that token.  Returns out [S, num_heads, head_dim].  Requests that
+        share their leading blocks (forks of one parent) and are passed next to each other are
+        decoded with those blocks read once."""
         torch = self._torch
         ids = [int(r) for r in request_ids]
         S = len(ids)
@@ -110,13 +115,18 @@ class PagedAttention:
         bs = self.block_size
         max_blocks = max(-(-n // bs) for n in lens_now) + 1
         tables, lens = self.allocator.build_block_tables(ids, max_blocks)
-        order = pa_order_longest_first(lens)
-        # one pinned buffer, one upload: slots | pairs | tables | lengths | launch order
+        group_start, prefix_len, num_groups, widest = pa_shared_prefix_groups(tables, lens, bs)
+        shared = widest > 1
+        # shared prefixes keep the batch order (groups are runs of neighbours); else longest first
+        order = list(range(S)) if shared else pa_order_longest_first(lens)
+        # one pinned buffer, one upload: slots | pairs | tables | lengths | launch order | groups
         P = len(pairs)
-        host = np.concatenate([np.asarray(slots, dtype=np.int32),
-                               np.asarray(pairs, dtype=np.int32).reshape(-1),
-                               np.asarray(tables, dtype=np.int32).reshape(-1),
-                               np.asarray(lens, dtype=np.int32), np.asarray(order, dtype=np.int32)])
+        parts = [np.asarray(slots, dtype=np.int32), np.asarray(pairs, dtype=np.int32).reshape(-1),
+                 np.asarray(tables, dtype=np.int32).reshape(-1), np.asarray(lens, dtype=np.int32),
+                 np.asarray(order, dtype=np.int32)]
+        if shared:
+            parts += [np.asarray(group_start, dtype=np.int32), np.asarray(prefix_len, dtype=np.int32)]
+        host = np.concatenate(parts)
         staging = self._stage(host)
         dev = torch.empty(host.size, dtype=torch.int32, device=self.device)
         pa_upload(dev, staging)
@@ -132,15 +142,28 @@ class PagedAttention:
         lens_d = dev[o:o + S]
         o += S
         order_d = dev[o:o + S]
+        o += S
+        if shared:
+            gs_d = dev[o:o + num_groups + 1]
+            o += num_groups + 1
+            pl_d = dev[o:o + S]
         if P:
             pa_copy_blocks(self.key_cache, self.value_cache, pairs_d)
         pa_reshape_and_cache(key.contiguous(), value.contiguous(), self.key_cache, self.value_cache, slots_d)
         max_ctx = max_blocks * bs
-        need = pa_decode_split_workspace_bytes(S, self.num_heads, self.head_dim, max_ctx, self.partition_size)
+        if shared:
+            need = pa_decode_shared_workspace_bytes(S, self.num_heads, self.head_dim, max_ctx)
+        else:
+            need = pa_decode_split_workspace_bytes(S, self.num_heads, self.head_dim, max_ctx, self.partition_size)
         if self._workspace is None or self._workspace.numel() < need:
             self._workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
-        pa_decode_auto(out, query.contiguous(), self.key_cache, self.value_cache, tables_d, lens_d, max_ctx,
-                       self.scale, self.partition_size, self._workspace, seq_order=order_d)
+        if shared:
+            pa_decode_shared(out, query.contiguous(), self.key_cache, self.value_cache, tables_d, lens_d, gs_d, pl_d,
+                             num_groups, widest, max_ctx, self.scale, self._workspace)
+        else:
+            pa_decode_auto(out, query.contiguous(), self.key_cache, self.value_cache, tables_d, lens_d, max_ctx,
+                           self.scale, self.partition_size, self._workspace, seq_order=order_d)
+        self.last_path = "shared" if shared else "auto"
         return out
 
     def _stage(self, host: np.ndarray):

@@ -30,7 +30,8 @@ def contiguous_reference(q, rows, H, Hkv, scale, dt):
 
 
 @pytest.mark.parametrize("dt,H,Hkv,bs", [("f16", 8, 2, 16), ("bf16", 4, 4, 32), ("f16", 16, 1, 8)])
-def test_steps_match_contiguous_attention(dt, H, Hkv, bs):
+@pytest.mark.parametrize("batch", [(1, 2, 3, 4), (1, 2, 4, 3)], ids=["fork apart", "fork beside its parent"])
+def test_steps_match_contiguous_attention(dt, H, Hkv, bs, batch):
     D, NB = 128, 64
     m = pa.PagedAttention(H, D, block_size=bs, num_blocks=NB, num_kv_heads=Hkv, dtype=synth.torch_dtype(dt))
     mirror = {}
@@ -50,7 +51,7 @@ def test_steps_match_contiguous_attention(dt, H, Hkv, bs):
         if step == 4:
             m.free(1)
             del mirror[1]
-        ids = sorted(mirror)
+        ids = [r for r in batch if r in mirror]
         S = len(ids)
         q = synth.normal_host((S, H, D), 100 + 3 * step, dt)
         k = synth.normal_host((S, Hkv, D), 101 + 3 * step, dt)
@@ -58,6 +59,8 @@ def test_steps_match_contiguous_attention(dt, H, Hkv, bs):
         before = m.allocator.stats()["cow_copies"]
         out = m.forward(ids, synth.to_torch(q, dt).cuda(), synth.to_torch(k, dt).cuda(), synth.to_torch(v, dt).cuda())
         copies += m.allocator.stats()["cow_copies"] - before
+        # a fork passed beside its parent is decoded with their common blocks read once
+        assert m.last_path == ("shared" if step >= 2 and batch == (1, 2, 4, 3) else "auto")
         torch.cuda.synchronize()
         for i, r in enumerate(ids):
             mirror[r][0].append(k[i])
