@@ -9,9 +9,14 @@ the library's calls and adds nothing to what they compute:
   - key/value pools on the device, keys [num_blocks, num_kv_heads, block_size, head_dim],
     values [num_blocks, num_kv_heads, head_dim, block_size];
   - per forward(): the allocator's append, pa_upload of the step's index data, pa_copy_blocks
-    for copy-on-write pairs, pa_reshape_and_cache of the new tokens' K/V, and pa_decode_auto,
-    or pa_decode_shared when requests forked from one parent sit side by side in the batch
-    (their common blocks are then read once for all of them).
+    for copy-on-write pairs, pa_reshape_and_cache of the new tokens' K/V, and the decode:
+    pa_decode_masked when a request has positions without a token (a cached prefix's hole, or
+    a sliding window's dropped tokens), else pa_decode_shared when requests forked from one
+    parent sit side by side in the batch (their common blocks then read once for all of them),
+    else pa_decode_auto;
+  - prefix caching ("PagedAttention 实现细节" §3.2: requests with the same prompt prefix share
+    its blocks) and a sliding window (the "滑动窗口" of the §六 feature list), through the
+    allocator's prefix entries and window release.
 Calls are enqueued on torch's current stream, as every call of the binding.  One instance
 is used from one host thread.
 """
@@ -21,9 +26,9 @@ import math
 
 import numpy as np
 
-from . import (Allocator, pa_copy_blocks, pa_decode_auto, pa_decode_shared, pa_decode_shared_workspace_bytes,
-               pa_decode_split_workspace_bytes, pa_order_longest_first, pa_reshape_and_cache,
-               pa_shared_prefix_groups, pa_upload)
+from . import (Allocator, pa_copy_blocks, pa_decode_auto, pa_decode_masked, pa_decode_shared,
+               pa_decode_shared_workspace_bytes, pa_decode_split_workspace_bytes, pa_order_longest_first,
+               pa_reshape_and_cache, pa_shared_prefix_groups, pa_upload)
 
 
 class PagedAttention:
@@ -57,6 +62,7 @@ class PagedAttention:
         self._staging = None   # pinned int32 host buffer of the last step's index data
         self._staged = None    # event after that buffer's upload
         self._workspace = None
+        self._prefix_of = {}   # request -> the cached prefix it took a use of
 
     # -- requests ------------------------------------------------------------------
     def allocate(self, request_id: int, seq_len: int):
@@ -68,13 +74,52 @@ class PagedAttention:
         self.allocator.seq_fork(parent_id, child_id)
 
     def free(self, request_id: int):
+        """Release the request's blocks, and its use of a cached prefix (the prefix's blocks
+        return to the pool when its last user is freed)."""
         self.allocator.seq_free(request_id)
+        pid = self._prefix_of.pop(request_id, None)
+        if pid is not None:
+            self.allocator.prefix_release(pid)
 
     def context_len(self, request_id: int) -> int:
         return self.allocator.seq_len(request_id)
 
     def block_table(self, request_id: int) -> list:
         return self.allocator.block_table(request_id)
+
+    # -- prefix caching and sliding window -------------------------------------------
+    def allocate_with_prefix(self, request_id: int, prefix_tokens, own_len: int):
+        """A request whose prompt starts with `prefix_tokens` (token ids), cached by content: the
+        first request with this prefix takes its blocks (hit False: store its K/V once with
+        store_prefix), later ones share them (hit True).  The request's own own_len prompt
+        tokens start at the block boundary after the prefix; the positions in between hold no
+        token and decode skips them.  The request holds a use of the prefix until free().
+        Returns (prefix_id, hit, position of the first own token)."""
+        pid, hit = self.allocator.prefix_get_or_create(prefix_tokens)
+        try:
+            self.allocator.seq_create_with_prefix(request_id, pid, own_len)
+        except Exception:
+            self.allocator.prefix_release(pid)
+            raise
+        self._prefix_of[request_id] = pid
+        start = -(-len(prefix_tokens) // self.block_size) * self.block_size
+        return pid, hit, start
+
+    def store_prefix(self, prefix_id: int, key, value):
+        """Write a cached prefix's K/V rows [prefix length, num_kv_heads, head_dim] into its blocks."""
+        torch = self._torch
+        blocks, n, _ = self.allocator.prefix_info(prefix_id)
+        if key.shape[0] != n or value.shape[0] != n:
+            raise ValueError(f"the prefix holds {n} tokens")
+        bs = self.block_size
+        slots = torch.tensor([blocks[p // bs] * bs + p % bs for p in range(n)], dtype=torch.int32,
+                             device=self.device)
+        pa_reshape_and_cache(key.contiguous(), value.contiguous(), self.key_cache, self.value_cache, slots)
+
+    def set_window(self, request_id: int, window: int):
+        """Attend over the request's last `window` tokens from now on; the blocks wholly before
+        them return to the pool."""
+        self.allocator.seq_set_window(request_id, window)
 
     # -- K/V of stored tokens --------------------------------------------------------
     def store(self, request_id: int, key, value, start: int = 0):
@@ -98,9 +143,10 @@ class PagedAttention:
         """One decode step.  For every request a slot is appended (a shared, partly filled last
         block is first copied), the new token's K/V rows key/value [S, num_kv_heads, head_dim]
         are written there, and query [S, num_heads, head_dim] attends over the request's
-        context including that token.  Returns out [S, num_heads, head_dim].  Requests that
-        share their leading blocks (forks of one parent) and are passed next to each other are
-        decoded with those blocks read once."""
+        context including that token (positions without a token, a cached prefix's hole or
+        what a sliding window dropped, left out).  Returns out [S, num_heads, head_dim].
+        Requests that share their leading blocks (forks of one parent) and are passed next to
+        each other are decoded with those blocks read once."""
         torch = self._torch
         ids = [int(r) for r in request_ids]
         S = len(ids)
@@ -115,8 +161,10 @@ class PagedAttention:
         bs = self.block_size
         max_blocks = max(-(-n // bs) for n in lens_now) + 1
         tables, lens = self.allocator.build_block_tables(ids, max_blocks)
+        lo, hi = self.allocator.masks(ids)
+        masked = any(h > l for l, h in zip(lo, hi))
         group_start, prefix_len, num_groups, widest = pa_shared_prefix_groups(tables, lens, bs)
-        shared = widest > 1
+        shared = widest > 1 and not masked
         # shared prefixes keep the batch order (groups are runs of neighbours); else longest first
         order = list(range(S)) if shared else pa_order_longest_first(lens)
         # one pinned buffer, one upload: slots | pairs | tables | lengths | launch order | groups
@@ -126,6 +174,8 @@ class PagedAttention:
                  np.asarray(order, dtype=np.int32)]
         if shared:
             parts += [np.asarray(group_start, dtype=np.int32), np.asarray(prefix_len, dtype=np.int32)]
+        if masked:
+            parts += [np.asarray(lo, dtype=np.int32), np.asarray(hi, dtype=np.int32)]
         host = np.concatenate(parts)
         staging = self._stage(host)
         dev = torch.empty(host.size, dtype=torch.int32, device=self.device)
@@ -147,6 +197,10 @@ class PagedAttention:
             gs_d = dev[o:o + num_groups + 1]
             o += num_groups + 1
             pl_d = dev[o:o + S]
+            o += S
+        if masked:
+            lo_d = dev[o:o + S]
+            hi_d = dev[o + S:o + 2 * S]
         if P:
             pa_copy_blocks(self.key_cache, self.value_cache, pairs_d)
         pa_reshape_and_cache(key.contiguous(), value.contiguous(), self.key_cache, self.value_cache, slots_d)
@@ -157,13 +211,17 @@ class PagedAttention:
             need = pa_decode_split_workspace_bytes(S, self.num_heads, self.head_dim, max_ctx, self.partition_size)
         if self._workspace is None or self._workspace.numel() < need:
             self._workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
-        if shared:
+        if masked:
+            pa_decode_masked(out, query.contiguous(), self.key_cache, self.value_cache, tables_d, lens_d, lo_d, hi_d,
+                             max_ctx, self.scale, partition_size=self.partition_size, workspace=self._workspace,
+                             seq_order=order_d)
+        elif shared:
             pa_decode_shared(out, query.contiguous(), self.key_cache, self.value_cache, tables_d, lens_d, gs_d, pl_d,
                              num_groups, widest, max_ctx, self.scale, self._workspace)
         else:
             pa_decode_auto(out, query.contiguous(), self.key_cache, self.value_cache, tables_d, lens_d, max_ctx,
                            self.scale, self.partition_size, self._workspace, seq_order=order_d)
-        self.last_path = "shared" if shared else "auto"
+        self.last_path = "masked" if masked else "shared" if shared else "auto"
         return out
 
     def _stage(self, host: np.ndarray):

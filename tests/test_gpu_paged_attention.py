@@ -81,3 +81,52 @@ def test_store_refuses_a_shared_block():
     k = torch.zeros((4, 4, 64), dtype=torch.float16, device="cuda")
     with pytest.raises(ValueError):
         m.store(2, k, k, start=16)
+
+
+def test_cached_prefix_and_sliding_window_steps():
+    """Two requests on one cached 40-token prefix (the second a hit, its blocks shared; each
+    request's own tokens after the block boundary), and a third request with a sliding window
+    of 20 tokens, decoded together over four steps against contiguous attention over the
+    prefix then the own tokens, and over the window's last 20 tokens."""
+    dt, H, Hkv, D, bs, NB = "f16", 8, 2, 128, 16, 64
+    m = pa.PagedAttention(H, D, block_size=bs, num_blocks=NB, num_kv_heads=Hkv, dtype=torch.float16)
+    prefix = list(range(1000, 1040))
+    pk = synth.normal_host((40, Hkv, D), 200, dt)
+    pv = synth.normal_host((40, Hkv, D), 201, dt)
+    mirror, window = {}, {}
+    pid, hit, start = m.allocate_with_prefix(1, prefix, 10)
+    assert not hit and start == 48
+    m.store_prefix(pid, synth.to_torch(pk, dt).cuda(), synth.to_torch(pv, dt).cuda())
+    pid2, hit2, _ = m.allocate_with_prefix(2, prefix, 5)
+    assert hit2 and pid2 == pid
+    for r, n, seed in ((1, 10, 210), (2, 5, 220)):
+        k = synth.normal_host((n, Hkv, D), seed, dt)
+        v = synth.normal_host((n, Hkv, D), seed + 1, dt)
+        m.store(r, synth.to_torch(k, dt).cuda(), synth.to_torch(v, dt).cuda(), start=start)
+        mirror[r] = (list(pk) + list(k), list(pv) + list(v))
+    k = synth.normal_host((60, Hkv, D), 230, dt)
+    v = synth.normal_host((60, Hkv, D), 231, dt)
+    m.allocate(3, 60)
+    m.store(3, synth.to_torch(k, dt).cuda(), synth.to_torch(v, dt).cuda())
+    m.set_window(3, 20)
+    mirror[3] = (list(k), list(v))
+    window[3] = 20
+    ids = [1, 2, 3]
+    for step in range(4):
+        q = synth.normal_host((3, H, D), 300 + 3 * step, dt)
+        kn = synth.normal_host((3, Hkv, D), 301 + 3 * step, dt)
+        vn = synth.normal_host((3, Hkv, D), 302 + 3 * step, dt)
+        out = m.forward(ids, synth.to_torch(q, dt).cuda(), synth.to_torch(kn, dt).cuda(), synth.to_torch(vn, dt).cuda())
+        torch.cuda.synchronize()
+        assert m.last_path == "masked"
+        for i, r in enumerate(ids):
+            mirror[r][0].append(kn[i])
+            mirror[r][1].append(vn[i])
+        rows = [(mirror[r][0][-window[r]:], mirror[r][1][-window[r]:]) if r in window else mirror[r] for r in ids]
+        ref = contiguous_reference(q, rows, H, Hkv, m.scale, dt)
+        assert_close(out_to_f64(out, dt), ref, dt, f"step {step}")
+    m.free(1)
+    assert m.allocator.prefix_info(pid)[2] == 1, "request 2 still uses the prefix"
+    for r in (2, 3):
+        m.free(r)
+    assert m.allocator.num_free_blocks() == NB
