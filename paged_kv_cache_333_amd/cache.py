@@ -16,7 +16,9 @@ the library's calls and adds nothing to what they compute:
     else pa_decode_auto;
   - prefix caching ("PagedAttention 实现细节" §3.2: requests with the same prompt prefix share
     its blocks) and a sliding window (the "滑动窗口" of the §六 feature list), through the
-    allocator's prefix entries and window release.
+    allocator's prefix entries and window release;
+  - swapping requests to a pinned host pool and back ("PagedAttention 实现细节" §3.4: the cache
+    engine's CPU-side pool), through the allocator's swap and pa_swap_blocks.
 Calls are enqueued on torch's current stream, as every call of the binding.  One instance
 is used from one host thread.
 """
@@ -28,7 +30,7 @@ import numpy as np
 
 from . import (Allocator, pa_copy_blocks, pa_decode_auto, pa_decode_masked, pa_decode_shared,
                pa_decode_shared_workspace_bytes, pa_decode_split_workspace_bytes, pa_order_longest_first,
-               pa_reshape_and_cache, pa_shared_prefix_groups, pa_upload)
+               pa_reshape_and_cache, pa_shared_prefix_groups, pa_swap_blocks, pa_upload)
 
 
 class PagedAttention:
@@ -36,11 +38,12 @@ class PagedAttention:
 
     num_kv_heads defaults to num_heads (multi-head); query head h reads KV head
     h // (num_heads // num_kv_heads).  scale defaults to float32(1 / sqrt(head_dim)).
-    partition_size is the split path's partition, used when pa_decode_auto takes it."""
+    partition_size is the split path's partition, used when pa_decode_auto takes it.
+    num_host_blocks > 0 adds a pinned host pool of that many blocks for swap_out / swap_in."""
 
     def __init__(self, num_heads: int, head_dim: int, block_size: int = 16, num_blocks: int = 1024,
                  num_kv_heads: int | None = None, dtype=None, device="cuda", scale: float | None = None,
-                 partition_size: int = 512):
+                 partition_size: int = 512, num_host_blocks: int = 0):
         import torch
         self._torch = torch
         self.num_heads = num_heads
@@ -59,6 +62,13 @@ class PagedAttention:
         self.value_cache = torch.zeros((num_blocks, self.num_kv_heads, head_dim, block_size), dtype=self.dtype,
                                        device=self.device)
         self.allocator = Allocator(num_blocks, block_size)
+        self.host_key_cache = self.host_value_cache = None
+        if num_host_blocks > 0:
+            self.host_key_cache = torch.zeros((num_host_blocks, self.num_kv_heads, block_size, head_dim),
+                                              dtype=self.dtype, pin_memory=True)
+            self.host_value_cache = torch.zeros((num_host_blocks, self.num_kv_heads, head_dim, block_size),
+                                                dtype=self.dtype, pin_memory=True)
+            self.allocator.set_host_pool(num_host_blocks)
         self._staging = None   # pinned int32 host buffer of the last step's index data
         self._staged = None    # event after that buffer's upload
         self._workspace = None
@@ -120,6 +130,29 @@ class PagedAttention:
         """Attend over the request's last `window` tokens from now on; the blocks wholly before
         them return to the pool."""
         self.allocator.seq_set_window(request_id, window)
+
+    # -- swap -------------------------------------------------------------------------
+    def swap_out(self, request_ids):
+        """Move the requests (forks of one parent move together) to the host pool; their device
+        blocks return to the pool.  A swapped request can be swapped in or freed."""
+        self._swap(self.allocator.seq_swap_out, request_ids, to_host=True)
+
+    def swap_in(self, request_ids):
+        """Bring swapped requests back into device blocks."""
+        self._swap(self.allocator.seq_swap_in, request_ids, to_host=False)
+
+    def _swap(self, move, request_ids, to_host: bool):
+        torch = self._torch
+        if self.host_key_cache is None:
+            raise ValueError("no host pool: construct with num_host_blocks > 0")
+        pairs = move([int(r) for r in request_ids])
+        if not pairs:
+            return
+        pairs_d = torch.tensor(pairs, dtype=torch.int32, device=self.device)
+        if to_host:
+            pa_swap_blocks(self.host_key_cache, self.host_value_cache, self.key_cache, self.value_cache, pairs_d)
+        else:
+            pa_swap_blocks(self.key_cache, self.value_cache, self.host_key_cache, self.host_value_cache, pairs_d)
 
     # -- K/V of stored tokens --------------------------------------------------------
     def store(self, request_id: int, key, value, start: int = 0):

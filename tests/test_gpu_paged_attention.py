@@ -130,3 +130,56 @@ def test_cached_prefix_and_sliding_window_steps():
     for r in (2, 3):
         m.free(r)
     assert m.allocator.num_free_blocks() == NB
+
+
+def test_swap_out_reuse_and_swap_in():
+    """A request is swapped out to the host pool, its device blocks are taken and written by a
+    new request, and it is swapped back in: every step, before and after, matches contiguous
+    attention, the swapped request's included ("PagedAttention 实现细节" §3.4)."""
+    dt, H, Hkv, D, bs, NB = "bf16", 4, 2, 64, 16, 12
+    m = pa.PagedAttention(H, D, block_size=bs, num_blocks=NB, num_kv_heads=Hkv, dtype=torch.bfloat16,
+                          num_host_blocks=8)
+    mirror = {}
+    seed = 500
+
+    def add(r, n):
+        nonlocal seed
+        k = synth.normal_host((n, Hkv, D), seed, dt)
+        v = synth.normal_host((n, Hkv, D), seed + 1, dt)
+        seed += 2
+        m.allocate(r, n)
+        m.store(r, synth.to_torch(k, dt).cuda(), synth.to_torch(v, dt).cuda())
+        mirror[r] = (list(k), list(v))
+
+    def step(ids, tag):
+        nonlocal seed
+        S = len(ids)
+        q = synth.normal_host((S, H, D), seed, dt)
+        kn = synth.normal_host((S, Hkv, D), seed + 1, dt)
+        vn = synth.normal_host((S, Hkv, D), seed + 2, dt)
+        seed += 3
+        out = m.forward(ids, synth.to_torch(q, dt).cuda(), synth.to_torch(kn, dt).cuda(),
+                        synth.to_torch(vn, dt).cuda())
+        torch.cuda.synchronize()
+        for i, r in enumerate(ids):
+            mirror[r][0].append(kn[i])
+            mirror[r][1].append(vn[i])
+        ref = contiguous_reference(q, [mirror[r] for r in ids], H, Hkv, m.scale, dt)
+        assert_close(out_to_f64(out, dt), ref, dt, tag)
+
+    add(1, 30)
+    add(2, 45)
+    step([1, 2], "both on the device")
+    m.swap_out([2])
+    assert m.allocator.num_free_blocks() == NB - 2            # request 1's two blocks remain
+    add(3, 100)                                               # takes (and overwrites) request 2's blocks
+    step([1, 3], "request 2 on the host")
+    for r in (3,):
+        m.free(r)
+        del mirror[r]
+    m.swap_in([2])
+    step([2, 1], "request 2 back")
+    step([1, 2], "and once more")
+    for r in list(mirror):
+        m.free(r)
+    assert m.allocator.num_free_blocks() == NB
