@@ -18,7 +18,10 @@ the library's calls and adds nothing to what they compute:
     its blocks) and a sliding window (the "滑动窗口" of the §六 feature list), through the
     allocator's prefix entries and window release;
   - swapping requests to a pinned host pool and back ("PagedAttention 实现细节" §3.4: the cache
-    engine's CPU-side pool), through the allocator's swap and pa_swap_blocks.
+    engine's CPU-side pool), through the allocator's swap and pa_swap_blocks;
+  - 8-bit pools (the int8 KV cache beside paging of the xdnf.cn article, §2.3 and §6.3): FP8
+    E4M3 or int8 codes with one scale per pool, or int8 with a scale per (token, KV head),
+    written by pa_reshape_and_cache_quant and decoded by the calls above or pa_decode_quant.
 Calls are enqueued on torch's current stream, as every call of the binding.  One instance
 is used from one host thread.
 """
@@ -28,9 +31,12 @@ import math
 
 import numpy as np
 
-from . import (Allocator, pa_copy_blocks, pa_decode_auto, pa_decode_masked, pa_decode_shared,
+from . import (Allocator, pa_copy_blocks, pa_decode_auto, pa_decode_masked, pa_decode_quant, pa_decode_shared,
                pa_decode_shared_workspace_bytes, pa_decode_split_workspace_bytes, pa_order_longest_first,
-               pa_reshape_and_cache, pa_shared_prefix_groups, pa_swap_blocks, pa_upload)
+               pa_reshape_and_cache, pa_reshape_and_cache_quant, pa_shared_prefix_groups, pa_swap_blocks,
+               pa_upload, token_tile_bytes)
+
+KV_FORMATS = (None, "fp8_e4m3", "int8", "int8_token")
 
 
 class PagedAttention:
@@ -39,11 +45,16 @@ class PagedAttention:
     num_kv_heads defaults to num_heads (multi-head); query head h reads KV head
     h // (num_heads // num_kv_heads).  scale defaults to float32(1 / sqrt(head_dim)).
     partition_size is the split path's partition, used when pa_decode_auto takes it.
-    num_host_blocks > 0 adds a pinned host pool of that many blocks for swap_out / swap_in."""
+    num_host_blocks > 0 adds a pinned host pool of that many blocks for swap_out / swap_in.
+    kv_format "fp8_e4m3" or "int8" stores codes of K / k_scale and V / v_scale (uint8 pools of
+    the same shapes); "int8_token" stores int8 codes with a scale per (token, KV head) in each
+    tile (uint8 [num_blocks, num_kv_heads, token_tile_bytes(block_size, head_dim)] pools, the
+    scale arguments unused).  8-bit pools take fp16 or bf16 queries and blocks of 16, 32 or 64."""
 
     def __init__(self, num_heads: int, head_dim: int, block_size: int = 16, num_blocks: int = 1024,
                  num_kv_heads: int | None = None, dtype=None, device="cuda", scale: float | None = None,
-                 partition_size: int = 512, num_host_blocks: int = 0):
+                 partition_size: int = 512, num_host_blocks: int = 0, kv_format: str | None = None,
+                 k_scale: float = 1.0, v_scale: float = 1.0):
         import torch
         self._torch = torch
         self.num_heads = num_heads
@@ -57,22 +68,40 @@ class PagedAttention:
         self.device = torch.device(device)
         self.scale = float(np.float32(1.0 / math.sqrt(head_dim))) if scale is None else float(scale)
         self.partition_size = partition_size
-        self.key_cache = torch.zeros((num_blocks, self.num_kv_heads, block_size, head_dim), dtype=self.dtype,
-                                     device=self.device)
-        self.value_cache = torch.zeros((num_blocks, self.num_kv_heads, head_dim, block_size), dtype=self.dtype,
-                                       device=self.device)
+        if kv_format not in KV_FORMATS:
+            raise ValueError(f"kv_format must be one of {KV_FORMATS}")
+        if kv_format and (self.dtype not in (torch.float16, torch.bfloat16) or block_size not in (16, 32, 64)):
+            raise ValueError("8-bit pools take fp16 or bf16 queries and blocks of 16, 32 or 64 tokens")
+        self.kv_format = kv_format
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
+        self.key_cache, self.value_cache = self._pools(num_blocks, device=self.device)
         self.allocator = Allocator(num_blocks, block_size)
         self.host_key_cache = self.host_value_cache = None
         if num_host_blocks > 0:
-            self.host_key_cache = torch.zeros((num_host_blocks, self.num_kv_heads, block_size, head_dim),
-                                              dtype=self.dtype, pin_memory=True)
-            self.host_value_cache = torch.zeros((num_host_blocks, self.num_kv_heads, head_dim, block_size),
-                                                dtype=self.dtype, pin_memory=True)
+            self.host_key_cache, self.host_value_cache = self._pools(num_host_blocks, pin_memory=True)
             self.allocator.set_host_pool(num_host_blocks)
         self._staging = None   # pinned int32 host buffer of the last step's index data
         self._staged = None    # event after that buffer's upload
         self._workspace = None
         self._prefix_of = {}   # request -> the cached prefix it took a use of
+
+    def _pools(self, n: int, **where):
+        """Zeroed key and value pools of n blocks (on the device, or pinned on the host)."""
+        torch = self._torch
+        Hkv, bs, D = self.num_kv_heads, self.block_size, self.head_dim
+        if self.kv_format == "int8_token":
+            shape = (n, Hkv, token_tile_bytes(bs, D))
+            return torch.zeros(shape, dtype=torch.uint8, **where), torch.zeros(shape, dtype=torch.uint8, **where)
+        dt = torch.uint8 if self.kv_format else self.dtype
+        return (torch.zeros((n, Hkv, bs, D), dtype=dt, **where), torch.zeros((n, Hkv, D, bs), dtype=dt, **where))
+
+    def _write(self, key, value, slots):
+        """The slot-mapping write of K/V rows [n, num_kv_heads, head_dim] (quantising into 8-bit pools)."""
+        if self.kv_format:
+            pa_reshape_and_cache_quant(key.contiguous(), value.contiguous(), self.key_cache, self.value_cache, slots,
+                                       self.k_scale, self.v_scale, kv_format=self.kv_format)
+        else:
+            pa_reshape_and_cache(key.contiguous(), value.contiguous(), self.key_cache, self.value_cache, slots)
 
     # -- requests ------------------------------------------------------------------
     def allocate(self, request_id: int, seq_len: int):
@@ -124,7 +153,7 @@ class PagedAttention:
         bs = self.block_size
         slots = torch.tensor([blocks[p // bs] * bs + p % bs for p in range(n)], dtype=torch.int32,
                              device=self.device)
-        pa_reshape_and_cache(key.contiguous(), value.contiguous(), self.key_cache, self.value_cache, slots)
+        self._write(key, value, slots)
 
     def set_window(self, request_id: int, window: int):
         """Attend over the request's last `window` tokens from now on; the blocks wholly before
@@ -149,10 +178,13 @@ class PagedAttention:
         if not pairs:
             return
         pairs_d = torch.tensor(pairs, dtype=torch.int32, device=self.device)
+        D = self.head_dim
         if to_host:
-            pa_swap_blocks(self.host_key_cache, self.host_value_cache, self.key_cache, self.value_cache, pairs_d)
+            pa_swap_blocks(self.host_key_cache, self.host_value_cache, self.key_cache, self.value_cache, pairs_d,
+                           head_dim=D)
         else:
-            pa_swap_blocks(self.key_cache, self.value_cache, self.host_key_cache, self.host_value_cache, pairs_d)
+            pa_swap_blocks(self.key_cache, self.value_cache, self.host_key_cache, self.host_value_cache, pairs_d,
+                           head_dim=D)
 
     # -- K/V of stored tokens --------------------------------------------------------
     def store(self, request_id: int, key, value, start: int = 0):
@@ -169,7 +201,7 @@ class PagedAttention:
                 raise ValueError(f"block {table[j]} of request {request_id} is shared: it cannot be written")
         slots = torch.tensor([table[p // bs] * bs + p % bs for p in range(start, start + n)], dtype=torch.int32,
                              device=self.device)
-        pa_reshape_and_cache(key.contiguous(), value.contiguous(), self.key_cache, self.value_cache, slots)
+        self._write(key, value, slots)
 
     # -- one decode step ---------------------------------------------------------------
     def forward(self, request_ids, query, key, value):
@@ -235,8 +267,8 @@ class PagedAttention:
             lo_d = dev[o:o + S]
             hi_d = dev[o + S:o + 2 * S]
         if P:
-            pa_copy_blocks(self.key_cache, self.value_cache, pairs_d)
-        pa_reshape_and_cache(key.contiguous(), value.contiguous(), self.key_cache, self.value_cache, slots_d)
+            pa_copy_blocks(self.key_cache, self.value_cache, pairs_d, head_dim=self.head_dim)
+        self._write(key, value, slots_d)
         max_ctx = max_blocks * bs
         if shared:
             need = pa_decode_shared_workspace_bytes(S, self.num_heads, self.head_dim, max_ctx)
@@ -244,16 +276,21 @@ class PagedAttention:
             need = pa_decode_split_workspace_bytes(S, self.num_heads, self.head_dim, max_ctx, self.partition_size)
         if self._workspace is None or self._workspace.numel() < need:
             self._workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+        q = query.contiguous()
+        kc, vc, fmt, ks, vs = self.key_cache, self.value_cache, self.kv_format, self.k_scale, self.v_scale
         if masked:
-            pa_decode_masked(out, query.contiguous(), self.key_cache, self.value_cache, tables_d, lens_d, lo_d, hi_d,
-                             max_ctx, self.scale, partition_size=self.partition_size, workspace=self._workspace,
+            pa_decode_masked(out, q, kc, vc, tables_d, lens_d, lo_d, hi_d, max_ctx, self.scale, ks, vs,
+                             kv_format=fmt, partition_size=self.partition_size, workspace=self._workspace,
                              seq_order=order_d)
         elif shared:
-            pa_decode_shared(out, query.contiguous(), self.key_cache, self.value_cache, tables_d, lens_d, gs_d, pl_d,
-                             num_groups, widest, max_ctx, self.scale, self._workspace)
+            pa_decode_shared(out, q, kc, vc, tables_d, lens_d, gs_d, pl_d, num_groups, widest, max_ctx, self.scale,
+                             self._workspace, ks, vs, kv_format=fmt)
+        elif fmt:  # the pa_decode_auto rule over 8-bit pools
+            pa_decode_quant(out, q, kc, vc, tables_d, lens_d, max_ctx, self.scale, ks, vs, kv_format=fmt,
+                            partition_size=self.partition_size, workspace=self._workspace, seq_order=order_d)
         else:
-            pa_decode_auto(out, query.contiguous(), self.key_cache, self.value_cache, tables_d, lens_d, max_ctx,
-                           self.scale, self.partition_size, self._workspace, seq_order=order_d)
+            pa_decode_auto(out, q, kc, vc, tables_d, lens_d, max_ctx, self.scale, self.partition_size,
+                           self._workspace, seq_order=order_d)
         self.last_path = "masked" if masked else "shared" if shared else "auto"
         return out
 

@@ -2,7 +2,8 @@
 fork, forward, free) over several decode steps, against attention over each request's K/V
 kept contiguous on the host ("PagedAttention 实现细节" §3.1: the paged cache computes what a
 contiguous cache computes).  A fork in the middle makes the next step copy a shared, partly
-filled last block (§3.3)."""
+filled last block (§3.3).  8-bit pools are checked against attention over the rows their
+codes stand for (the oracle's quantisation of each stored row)."""
 import numpy as np
 import pytest
 import torch
@@ -10,19 +11,21 @@ import torch
 import paged_kv_cache_333_amd as pa
 import synth
 from oracle import attention as A
+from oracle import quant as Q
 from tests.gpu_helpers import assert_close, out_to_f64
 
 pytestmark = pytest.mark.gpu
 
 
-def contiguous_reference(q, rows, H, Hkv, scale, dt):
-    """out[i, h] = attention of q[i, h] over request i's rows (K, V [n, Hkv, D] in order)."""
+def contiguous_reference(q, rows, H, Hkv, scale, dt, kv_f64=False):
+    """out[i, h] = attention of q[i, h] over request i's rows (K, V [n, Hkv, D] in order; of
+    storage type dt, or float64 values with kv_f64)."""
     S, _, D = q.shape
     out = np.zeros((S, H, D))
     sig = A.scale_f64(scale)
     for i, (ks, vs) in enumerate(rows):
-        K = A.to_f64(np.stack(ks), dt)
-        V = A.to_f64(np.stack(vs), dt)
+        K = np.stack(ks).astype(np.float64) if kv_f64 else A.to_f64(np.stack(ks), dt)
+        V = np.stack(vs).astype(np.float64) if kv_f64 else A.to_f64(np.stack(vs), dt)
         for h in range(H):
             g = A.kv_head_of(h, H, Hkv)
             out[i, h] = A.attend(A.to_f64(q[i, h], dt), K[:, g, :], V[:, g, :], sig)
@@ -180,6 +183,75 @@ def test_swap_out_reuse_and_swap_in():
     m.swap_in([2])
     step([2, 1], "request 2 back")
     step([1, 2], "and once more")
+    for r in list(mirror):
+        m.free(r)
+    assert m.allocator.num_free_blocks() == NB
+
+
+def stored_rows(k, v, dt, fmt, ks, vs):
+    """The float64 rows [n, Hkv, D] that 8-bit pools hold for K/V rows k, v of type dt."""
+    if fmt == "int8_token":
+        kq, kscale = Q.quantize_rows_int8(k, dt)
+        vq, vscale = Q.quantize_rows_int8(v, dt)
+        return Q.dequantize_rows_int8(kq, kscale), Q.dequantize_rows_int8(vq, vscale)
+    return Q.dequantize(Q.quantize(k, dt, ks, fmt), ks, fmt), Q.dequantize(Q.quantize(v, dt, vs, fmt), vs, fmt)
+
+
+@pytest.mark.parametrize("dt,fmt,bs", [("f16", "fp8_e4m3", 16), ("bf16", "int8", 32), ("f16", "int8_token", 16),
+                                       ("bf16", "int8_token", 64)])
+def test_8bit_pools_fork_window_and_swap(dt, fmt, bs):
+    """The object over 8-bit pools: prompts stored by the quantising write, a fork decoded
+    beside its parent (shared prefix, copy-on-write of the quantised last block), a sliding
+    window (masked), a swap out and back in, and plain steps, each against attention over
+    the dequantised rows."""
+    H, Hkv, D, NB = 8, 2, 128, 48
+    ks, vs = 0.04, 0.035
+    m = pa.PagedAttention(H, D, block_size=bs, num_blocks=NB, num_kv_heads=Hkv, dtype=synth.torch_dtype(dt),
+                          num_host_blocks=16, kv_format=fmt, k_scale=ks, v_scale=vs)
+    mirror, window = {}, {}
+    seed = 700
+    for r, n in {1: 37, 2: 2 * bs + 5, 3: 3}.items():
+        k = synth.normal_host((n, Hkv, D), seed, dt)
+        v = synth.normal_host((n, Hkv, D), seed + 1, dt)
+        seed += 2
+        m.allocate(r, n)
+        m.store(r, synth.to_torch(k, dt).cuda(), synth.to_torch(v, dt).cuda())
+        kq, vq = stored_rows(k, v, dt, fmt, ks, vs)
+        mirror[r] = (list(kq), list(vq))
+    # (step, event, batch, expected decode path)
+    plan = [(0, None, [1, 2, 3], "auto"),
+            (1, "fork", [1, 2, 4, 3], "shared"),
+            (2, None, [1, 2, 4, 3], "shared"),
+            (3, "swap out", [1, 3], "auto"),
+            (4, "swap in", [3, 2, 4, 1], "shared"),
+            (5, "window", [1, 2, 4, 3], "masked"),
+            (6, None, [1, 2, 4, 3], "masked")]
+    for step, event, ids, path in plan:
+        if event == "fork":
+            m.fork(2, 4)
+            mirror[4] = (list(mirror[2][0]), list(mirror[2][1]))
+        elif event == "swap out":
+            m.swap_out([2, 4])   # a parent and its fork move together
+        elif event == "swap in":
+            m.swap_in([2, 4])
+        elif event == "window":
+            m.set_window(3, 2)
+            window[3] = 2
+        S = len(ids)
+        q = synth.normal_host((S, H, D), 800 + 3 * step, dt)
+        kn = synth.normal_host((S, Hkv, D), 801 + 3 * step, dt)
+        vn = synth.normal_host((S, Hkv, D), 802 + 3 * step, dt)
+        out = m.forward(ids, synth.to_torch(q, dt).cuda(), synth.to_torch(kn, dt).cuda(),
+                        synth.to_torch(vn, dt).cuda())
+        torch.cuda.synchronize()
+        assert m.last_path == path, (step, m.last_path)
+        kq, vq = stored_rows(kn, vn, dt, fmt, ks, vs)
+        for i, r in enumerate(ids):
+            mirror[r][0].append(kq[i])
+            mirror[r][1].append(vq[i])
+        rows = [(mirror[r][0][-window[r]:], mirror[r][1][-window[r]:]) if r in window else mirror[r] for r in ids]
+        ref = contiguous_reference(q, rows, H, Hkv, m.scale, dt, kv_f64=True)
+        assert_close(out_to_f64(out, dt), ref, dt, f"step {step} ({event or 'no event'})")
     for r in list(mirror):
         m.free(r)
     assert m.allocator.num_free_blocks() == NB
