@@ -548,12 +548,14 @@ pa_status pa_decode_auto(void* out, const void* query, const void* key_cache, co
  *     but the decode may read that block's old or new contents (a race).
  *   key_cache, value_cache: written (one key row and one value column per
  *     sequence and KV head) and read.
- * The wave that reads the new token's step writes it and makes the writes
- * visible before loading that step, so the write costs no extra launch.  When
- * num_heads / num_kv_heads is above 16 (several workgroups per KV head) the
- * two operations run as two launches.  Other arguments, the path choice,
- * *path and the errors are those of pa_decode_auto; under PA_DEBUG the slots
- * are validated as in pa_reshape_and_cache. */
+ * The decode does not wait for the write: the wave whose step holds token
+ * context_lens[s] - 1 takes its key row and value column from key / value
+ * directly (when slot_mapping[s] is inside the pool; otherwise it reads the
+ * pool there, as the write-then-decode order would), and workgroups after the
+ * decode's own in the same launch store the new rows.  Output and pools are
+ * bit-identical to the two calls.  Other arguments, the path choice, *path and
+ * the errors are those of pa_decode_auto; under PA_DEBUG the slots are
+ * validated as in pa_reshape_and_cache. */
 pa_status pa_decode_append(void* out, const void* query, const void* key, const void* value,
                            const int32_t* slot_mapping, void* key_cache, void* value_cache,
                            const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,

@@ -1,6 +1,8 @@
 // Host-side launchers of the paged decode kernels (decode_kernel.hpp): the
 // single pass, the split pass plus its log-sum-exp merge, the fused
 // slot-mapping write, and the occupancy query behind pa_decode_auto.
+#include <algorithm>
+
 #include "decode_kernel.hpp"
 
 namespace pa {
@@ -112,22 +114,14 @@ hipError_t launch_decode_split(const DecodeArgs& x, const SplitLayout& ws, hipSt
 
 hipError_t launch_decode_append(const DecodeArgs& x, const void* new_k, const void* new_v, const int32_t* slots,
                                 const SplitLayout* ws, hipStream_t stream) {
-  const int group = x.num_heads / x.num_kv_heads;
-  const int gt = group_tile(group);
-  if (gt != group) {
-    // A KV head spans several workgroups, which cannot order one writer
-    // before the other readers: write first, then decode.
-    hipError_t e = launch_reshape_and_cache(new_k, new_v, const_cast<void*>(x.key_cache),
-                                            const_cast<void*>(x.value_cache), slots, x.num_seqs, x.num_blocks,
-                                            x.num_kv_heads, x.head_dim, x.dtype == PA_F32 ? 4 : 2, x.block_size,
-                                            stream);
-    if (e != hipSuccess) return e;
-    return ws ? launch_decode_split(x, *ws, stream) : launch_decode(x, stream);
-  }
+  const int gt = group_tile(x.num_heads / x.num_kv_heads);
   DecodeParams p = make_params(x);
   p.new_k = static_cast<const char*>(new_k);
   p.new_v = static_cast<const char*>(new_v);
   p.slots = slots;
+  // one (sequence, KV head) pair per writing wave, at most 1024 workgroups (then several each)
+  const int64_t pairs = static_cast<int64_t>(x.num_seqs) * x.num_kv_heads;
+  p.append_wgs = static_cast<int32_t>(std::min<int64_t>((pairs + kWaves - 1) / kWaves, 1024));
   if (ws) {
     p.ws_m = ws->m;
     p.ws_l = ws->l;

@@ -148,85 +148,58 @@ struct DecodeParams {
   float* own_o;
   float scale_log2;    // scale * k_scale * log2(e)
   float v_scale;       // multiplies the output (8-bit value pools; 1 otherwise)
-  // fused slot-mapping write (pa_decode_append): new K/V rows [num_seqs, H_kv, D]
-  // and the slot of each sequence's new token
+  // fused slot-mapping write (pa_decode_append): new K/V rows [num_seqs, H_kv, D],
+  // the slot of each sequence's new token, and the workgroups after the decode's
+  // own that store them
   const char* new_k;
   const char* new_v;
   const int32_t* slots;
+  int32_t append_wgs;
 };
 
-// The fused slot-mapping write of pa_decode_append.  The new token of sequence
-// s sits at position p = ctx - 1, which exactly one wave of the launch reads
-// (the owner of p's step, or of p's partition); that wave writes the token's
-// key row and value column into the pools itself.  When no wave reads p (an
-// empty or invalid context) wave 0 of the first workgroup writes.  Slots
-// outside the pool write nothing, as in pa_reshape_and_cache.
+// The fused slot-mapping write of pa_decode_append.  The decode does not wait
+// for the new tokens to reach the pools: the wave whose step holds position
+// p = ctx - 1 of a sequence takes that token's key row and value column from
+// the new rows themselves (a lane's key row is loaded from the new row instead
+// of the pool; the value element of p is put into the lane's value chunk after
+// its load), so its products see exactly what the pools will hold.  The
+// stores are made by append_wgs extra workgroups at the end of the grid, which
+// start as the decode's last workgroups drain.  A decode wave may load the
+// lines they write at the same time: every byte it keeps there is unchanged by
+// the write, and the byte of p it replaces.  A slot outside the pool (or
+// negative) writes nothing and the decode then reads the pool at p, as
+// pa_reshape_and_cache followed by the decode would.
 //
-// The writer loads the new row when it starts (prepare) but stores it only
-// after its first step's loads are in flight (commit), so the write adds no
-// round trip ahead of the streaming; the step that reads p waits for the
-// stores first (a workgroup-scope fence: writer and reader are one wave).
-template <typename T, int D>
-struct AppendRow {
-  static constexpr int kPerLane = (D + 63) / 64;
+// Wave i of the writers stores (sequence, KV head) pairs i, i + waves, ...:
+// the key row as one contiguous run, the value column element by element,
+// both non-temporal (no partly written line stays in the L2 for the next
+// reader to pay for).
+template <typename T, int D, int BS>
+__device__ __forceinline__ void write_new_rows(const DecodeParams& a, int wg) {
   typedef typename std::conditional<T::kBytes == 4, uint32_t, uint16_t>::type word_t;
-  word_t k[kPerLane], v[kPerLane];
-  int64_t k_base = 0, v_base = 0;  // element offsets of the key row / value column (offset 0 of each)
-  bool pending = false;
-  int read_step = -1;  // this wave's step that reads p, or -1
-
-  template <int BS, int TS, bool SPLIT>
-  __device__ __forceinline__ void prepare(const DecodeParams& a, int s, int kvh, int nctx, bool bad_len,
-                                          int t_begin, int t_end, int wave, int lane) {
-    const int p = nctx - 1;
-    const bool readable = !bad_len && p >= 0;
-    bool writer;
-    if (readable) {
-      writer = p >= t_begin && p < t_end;
-      if (writer) {
-        const int st_p = (p - t_begin) / TS;
-        writer = SPLIT || st_p % kWaves == wave;
-        if (writer) read_step = st_p;
-      }
-    } else {
-      writer = wave == 0 && (!SPLIT || blockIdx.y == 0);
-    }
-    if (!writer) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t pairs = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads;
+  const int64_t pool_slots = static_cast<int64_t>(a.num_blocks) * BS;
+  const word_t* nk = reinterpret_cast<const word_t*>(a.new_k);
+  const word_t* nv = reinterpret_cast<const word_t*>(a.new_v);
+  word_t* kc = reinterpret_cast<word_t*>(const_cast<char*>(a.kc));
+  word_t* vc = reinterpret_cast<word_t*>(const_cast<char*>(a.vc));
+  for (int64_t i = static_cast<int64_t>(wg) * kWaves + wave; i < pairs;
+       i += static_cast<int64_t>(a.append_wgs) * kWaves) {
+    const int s = static_cast<int>(i / a.num_kv_heads);
+    const int h = static_cast<int>(i - static_cast<int64_t>(s) * a.num_kv_heads);
     const int64_t slot = a.slots[s];
-    if (slot < 0 || slot >= static_cast<int64_t>(a.num_blocks) * BS) return;  // the read sees the old row
+    if (slot < 0 || slot >= pool_slots) continue;
     const int64_t blk = slot / BS, off = slot - blk * BS;
-    const int64_t tile = blk * a.num_kv_heads + kvh;
-    k_base = (tile * BS + off) * D;
-    v_base = tile * D * BS + off;
-    const int64_t src = (static_cast<int64_t>(s) * a.num_kv_heads + kvh) * D;
-    const word_t* nk = reinterpret_cast<const word_t*>(a.new_k);
-    const word_t* nv = reinterpret_cast<const word_t*>(a.new_v);
+    const int64_t tile = blk * a.num_kv_heads + h;
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-      const int d = lane + 64 * i;
-      if (d < D) {
-        k[i] = nk[src + d];
-        v[i] = nv[src + d];
-      }
+    for (int d = lane; d < D; d += 64) {
+      __builtin_nontemporal_store(nk[i * D + d], kc + (tile * BS + off) * D + d);
+      __builtin_nontemporal_store(nv[i * D + d], vc + (tile * D + d) * BS + off);
     }
-    pending = true;
   }
-
-  template <int BS>
-  __device__ __forceinline__ void commit(const DecodeParams& a, int lane) {
-    word_t* kc = reinterpret_cast<word_t*>(const_cast<char*>(a.kc));
-    word_t* vc = reinterpret_cast<word_t*>(const_cast<char*>(a.vc));
-#pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-      const int d = lane + 64 * i;
-      if (d < D) {
-        kc[k_base + d] = k[i];
-        vc[v_base + static_cast<int64_t>(d) * BS] = v[i];
-      }
-    }
-    pending = false;
-  }
-};
+}
 
 // T is the query/output type and the type the matrix cores compute in; S is
 // the pools' storage type: T itself, or an 8-bit code type (TE4M3, TI8) whose
@@ -278,6 +251,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const int col_toks = NC >> lg_h;
   const int groups = a.num_heads >> lg_h;
   const int per_slot = groups * a.q_chunks;
+  if constexpr (APPEND) {  // the workgroups after the decode's own store the new rows
+    const int64_t n_units = static_cast<int64_t>(a.num_seqs) * per_slot;
+    if (static_cast<int64_t>(blockIdx.x) >= n_units) {
+      if (blockIdx.y + 1 == gridDim.y) write_new_rows<T, D, BS>(a, static_cast<int>(blockIdx.x - n_units));
+      return;
+    }
+  }
   int unit = static_cast<int>(blockIdx.x);
   int flat_part = 0;
   bool own = false;  // a query row's own tokens after the shared prefixes (DecodeParams::n_lead)
@@ -378,18 +358,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       for (int i = a.q_chunks * col_toks + lane; i < L; i += 64) a.ws_len[qs + i] = -1;
     }
   }
-  AppendRow<T, D> fresh;  // the fused slot-mapping write (pa_decode_append)
-  if constexpr (APPEND)
-    fresh.template prepare<BS, TS, SPLIT>(a, s, kvh, nctx, bad_len, t_begin, t_end, wave, lane);
+  // pa_decode_append: position p = nctx - 1 is taken from the new rows (write_new_rows)
+  // when the new token has a slot in the pool; -1 otherwise
+  int fresh_p = -1;
+  if constexpr (APPEND) {
+    const int64_t slot = a.slots[s];
+    if (!bad_len && nctx > 0 && slot >= 0 && slot < static_cast<int64_t>(a.num_blocks) * BS) fresh_p = nctx - 1;
+  }
   if constexpr (SPLIT) {
     // nothing to read in this partition (no barrier follows); an own item always writes its
     // partial (no token: m = -inf, l = 0; an invalid row: NaN)
-    if (!own && (bad_len || t_begin >= t_all)) {
-      if constexpr (APPEND) {
-        if (fresh.pending) fresh.template commit<BS>(a, lane);
-      }
-      return;
-    }
+    if (!own && (bad_len || t_begin >= t_all)) return;
   }
   // steps wholly inside a mask that covers the start of the range are skipped
   const int st_skip = mlo <= t_begin && mhi > t_begin ? (min(mhi, t_end) - t_begin) / TS : 0;
@@ -477,17 +456,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       bad = 1;
       continue;
     }
-    if constexpr (APPEND) {
-      if (st == fresh.read_step) {
-        // This step holds the token this wave writes.  Writer and reader are
-        // the same wave, so workgroup scope suffices: the stores complete
-        // before the loads issue.  (Agent scope would write back and
-        // invalidate the whole L2 of the XCD, once per workgroup.)
-        if (fresh.pending) fresh.template commit<BS>(a, lane);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      }
-    }
     {
       int32_t live = ph[0];
 #pragma unroll
@@ -516,11 +484,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     // nonzero only when NBS == 1), so the row's block does not depend on tau.
     const int bik = NBS == 1 ? 0 : (off0 + TPL * (n >> 2)) / BS;
     const int64_t kblk = pick(bik);
+    // (pa_decode_append) the step holds the new token p (wave-uniform)
+    const bool has_fresh = APPEND && fresh_p >= t0 && fresh_p < t0 + TS;
+    const int64_t fresh_row = (static_cast<int64_t>(s) * hkv + kvh) * D;  // of the new rows, in elements
     u32x4 kr[NT][KL];
 #pragma unroll
     for (int tau = 0; tau < NT; ++tau) {
       const int x = off0 + TPL * (n >> 2) + 4 * tau + (n & 3);
-      const char* kp = a.kc + (kblk * hkv + kvh) * KT + ((x - bik * BS) * D) * SB + q * 16;
+      const char* kp = has_fresh && t0 + (x - off0) == fresh_p
+                           ? a.new_k + fresh_row * E + q * 16
+                           : a.kc + (kblk * hkv + kvh) * KT + ((x - bik * BS) * D) * SB + q * 16;
 #pragma unroll
       for (int l = 0; l < KL; ++l) kr[tau][l] = CACHED ? load16(kp + l * 64) : load16_stream(kp + l * 64);
     }
@@ -553,11 +526,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       for (int v = 0; v < NV; ++v)
         vr[v] = V_CACHED ? load16(vp + v * 16 * BS * SB) : load16_stream(vp + v * 16 * BS * SB);
     }
+    // (pa_decode_append) dims 16 v + n of the new token's value row, for the lanes whose
+    // tokens hold p
+    typedef typename std::conditional<E == 4, uint32_t, uint16_t>::type word_t;
+    word_t fv[APPEND ? NV : 1];
+    if constexpr (APPEND) {
+      if (has_fresh) {
+        const word_t* nv = reinterpret_cast<const word_t*>(a.new_v) + fresh_row + n;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) fv[v] = nv[16 * v];
+      }
+    }
     // All of the step's loads are issued before any of them is consumed.
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (APPEND) {
-      if (fresh.pending) fresh.template commit<BS>(a, lane);  // first step: behind its loads
-    }
 
     f32x4 c[NT];
 #pragma unroll
@@ -646,6 +627,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     u32x4 phi[PV], plo[PV];
 #pragma unroll
     for (int u = 0; u < PV; ++u) pack_p(TP{}, p + EPL * u, phi[u], plo[u]);
+    if constexpr (APPEND) {
+      const int e = fresh_p - t0 - TPL * q;  // the lane's element holding p, if any
+      if (has_fresh && e >= 0 && e < TPL) {
+        const int wi = E == 4 ? e : e >> 1;
+        const uint32_t sh = E == 4 ? 0u : static_cast<uint32_t>(e & 1) * 16u;
+        const uint32_t hole = E == 4 ? 0u : ~(0xFFFFu << sh);
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i == wi) vr[v][i] = (vr[v][i] & hole) | (static_cast<uint32_t>(fv[v]) << sh);
+      }
+    }
     if (ragged) {
       const u32x4 keep = bits_mask(S{}, vuse);
 #pragma unroll
@@ -664,10 +658,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
         if constexpr (SPLIT_P) acc[v] = mma(TP{}, plo[u], vc[u], acc[v]);
       }
     }
-  }
-
-  if constexpr (APPEND) {
-    if (fresh.pending) fresh.template commit<BS>(a, lane);  // a writer whose range has no step
   }
 
   // the four lanes of a column summed disjoint tokens with a common max
@@ -954,7 +944,8 @@ struct LaunchOp {
   hipError_t run() const {
     const int64_t units = static_cast<int64_t>(num_seqs) * (p.num_heads >> p.col_heads_log2) * p.q_chunks;
     const bool flat = SPLIT && !APPEND && p.flat;
-    const uint32_t gx = static_cast<uint32_t>(flat ? (units * p.num_parts + p.n_own + kWaves - 1) / kWaves : units);
+    const uint32_t gx = static_cast<uint32_t>(flat ? (units * p.num_parts + p.n_own + kWaves - 1) / kWaves
+                                                   : units + (APPEND ? p.append_wgs : 0));
     const uint32_t gy = SPLIT && !flat ? static_cast<uint32_t>((p.num_parts + kWaves - 1) / kWaves) : 1u;
     if (cached)
       launch_kernel(decode_kernel<T, S, D, BS, GT, SPLIT, true, APPEND>, dim3(gx, gy), dim3(kWaves * 64), stream, p);
