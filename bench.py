@@ -440,8 +440,8 @@ class Bench:
             self.vc = synth.normal_codes_device(v_shape, seeds["value_cache"], w.kv_format)
             if self.rows:
                 sc_shape = (w.num_blocks, Hkv, bs)
-                self.kc = pa.pack_token_pool(self.kc, synth.row_scales_device(sc_shape, seeds["key_scales"]))
-                self.vc = pa.pack_token_pool(self.vc, synth.row_scales_device(sc_shape, seeds["value_scales"]))
+                self.kc, self.vc = pa.pack_token_pools(self.kc, synth.row_scales_device(sc_shape, seeds["key_scales"]),
+                                                       self.vc, synth.row_scales_device(sc_shape, seeds["value_scales"]))
         else:
             self.kc = synth.normal_device(k_shape, seeds["key_cache"], w.dtype)
             self.vc = synth.normal_device(v_shape, seeds["value_cache"], w.dtype)
@@ -708,10 +708,8 @@ class Bench:
         remap[used] = np.arange(len(used), dtype=np.int32)
         idx = torch.from_numpy(used.astype(np.int64)).to(self.dev)
         if self.rows:
-            kc, ks = (t.cpu().numpy() for t in self.pa.unpack_token_pool(self.kc.index_select(0, idx),
-                                                                          w.block_size, w.head_dim, "key"))
-            vc, vs = (t.cpu().numpy() for t in self.pa.unpack_token_pool(self.vc.index_select(0, idx),
-                                                                          w.block_size, w.head_dim, "value"))
+            kc, ks, vc, vs = (t.cpu().numpy() for t in self.pa.unpack_token_pools(
+                self.kc.index_select(0, idx), self.vc.index_select(0, idx), w.block_size, w.head_dim))
         elif self.quant:
             kc = self.kc.index_select(0, idx).cpu().numpy()
             vc = self.vc.index_select(0, idx).cpu().numpy()

@@ -708,12 +708,17 @@ pa_status pa_decode_shared(void* out, const void* query, const void* key_cache, 
  * a row of zeros has s = 0.  Rows must be finite (a NaN row's codes and scale
  * are not specified).  The scales live in the pools themselves: each
  * (block, KV head) tile is its block_size * head_dim codes (laid out as
- * above) followed by block_size fp32 scales, the scale of token row o at byte
- * block_size * head_dim + 4 o of the tile, the scales padded to a whole
- * 128-byte line (PA_TOKEN_TILE_BYTES) so every tile's code rows stay
- * line-aligned; a pool is [num_blocks, num_kv_heads, PA_TOKEN_TILE_BYTES]
- * bytes, and block copies and swaps move the scales with the codes.  With PA_INT8_TOKEN the k_scale and v_scale arguments are
- * not used.
+ * above) followed by a scale area of whole 128-byte lines
+ * (PA_TOKEN_TILE_BYTES; every tile's code rows stay line-aligned), and a pool
+ * is [num_blocks, num_kv_heads, PA_TOKEN_TILE_BYTES] bytes.  With
+ * block_size 16 the key and value scales of a (block, KV head) share the key
+ * tile's area, which is one line: the key scale of token row o at byte
+ * 16 * head_dim + 4 o, its value scale at byte 16 * head_dim + 64 + 4 o, and
+ * the value tile's area is unused (the decode then fetches one scale line per
+ * block, not two half-used ones).  With larger blocks each tile's area holds
+ * the scales of its own rows, row o's at byte block_size * head_dim + 4 o.
+ * Block copies and swaps move whole tiles, scales included.  With
+ * PA_INT8_TOKEN the k_scale and v_scale arguments are not used.
  * pa_copy_blocks and pa_swap_blocks copy 8-bit pools with dtype = kv_dtype. */
 
 /* Bytes of one (block, KV head) tile of a PA_INT8_TOKEN pool. */

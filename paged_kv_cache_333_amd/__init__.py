@@ -223,44 +223,58 @@ def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, strea
 
 def token_tile_bytes(block_size: int, head_dim: int) -> int:
     """Bytes of one (block, KV head) tile of a row-scaled int8 pool (PA_TOKEN_TILE_BYTES): the
-    block_size * head_dim codes, then block_size float32 scales padded to a 128-byte line."""
+    block_size * head_dim codes, then a scale area of whole 128-byte lines."""
     return block_size * head_dim + (block_size * 4 + 127) // 128 * 128
+
+
+def token_scale_offsets(block_size: int, head_dim: int):
+    """Where a row-scaled int8 block keeps its scales: (byte of the key scales in the key tile,
+    byte of the value scales, True if those sit in the key tile).  With 16-token blocks both
+    sets share the key tile's one scale line; otherwise each tile holds its own."""
+    area = block_size * head_dim
+    paired = 8 * block_size <= (block_size * 4 + 127) // 128 * 128
+    return area, (area + 4 * block_size if paired else area), paired
 
 
 def token_pool(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, device="cuda"):
     """A zeroed pool of int8 codes with a scale per (token, KV head) (kv_format "int8_token"):
     uint8 [num_blocks, num_kv_heads, token_tile_bytes(block_size, head_dim)], each (block, KV
     head) tile its codes (keys [block_size, head_dim], values [head_dim, block_size]) followed
-    by block_size float32 scales, one per token row, and padding to a 128-byte line."""
+    by its scale area (token_scale_offsets)."""
     torch = _torch()
     return torch.zeros((num_blocks, num_kv_heads, token_tile_bytes(block_size, head_dim)), dtype=torch.uint8,
                        device=device)
 
 
-def pack_token_pool(codes, scales):
-    """A row-scaled int8 pool from its parts: codes uint8 [NB, H_kv, bs, D] (keys) or
-    [NB, H_kv, D, bs] (values) and scales float32 [NB, H_kv, bs]; the padding is zero."""
+def pack_token_pools(k_codes, k_scales, v_codes, v_scales):
+    """Row-scaled int8 key and value pools from their parts: codes uint8 [NB, H_kv, bs, D]
+    (keys) and [NB, H_kv, D, bs] (values), scales float32 [NB, H_kv, bs]; unused bytes zero."""
     torch = _torch()
-    NB, H_kv = codes.shape[:2]
-    bs = scales.shape[2]
-    D = codes.shape[2] * codes.shape[3] // bs
-    pool = torch.zeros((NB, H_kv, token_tile_bytes(bs, D)), dtype=torch.uint8, device=codes.device)
-    pool[:, :, :bs * D] = codes.reshape(NB, H_kv, -1)
-    pool[:, :, bs * D:bs * D + 4 * bs] = scales.contiguous().view(torch.uint8).reshape(NB, H_kv, -1)
-    return pool
+    NB, H_kv, bs, D = k_codes.shape
+    ko, vo, paired = token_scale_offsets(bs, D)
+    kp = torch.zeros((NB, H_kv, token_tile_bytes(bs, D)), dtype=torch.uint8, device=k_codes.device)
+    vp = torch.zeros_like(kp)
+    kp[:, :, :bs * D] = k_codes.reshape(NB, H_kv, -1)
+    vp[:, :, :bs * D] = v_codes.reshape(NB, H_kv, -1)
+    kp[:, :, ko:ko + 4 * bs] = k_scales.contiguous().view(torch.uint8).reshape(NB, H_kv, -1)
+    (kp if paired else vp)[:, :, vo:vo + 4 * bs] = v_scales.contiguous().view(torch.uint8).reshape(NB, H_kv, -1)
+    return kp, vp
 
 
-def unpack_token_pool(pool, block_size: int, head_dim: int, kind: str):
-    """(codes, scales) of a row-scaled int8 pool: kind "key" gives codes [NB, H_kv, bs, D],
-    "value" [NB, H_kv, D, bs]; scales float32 [NB, H_kv, bs]."""
-    NB, H_kv, tile = pool.shape
-    nc = block_size * head_dim
-    if tile != token_tile_bytes(block_size, head_dim) or kind not in ("key", "value"):
-        raise ValueError("not a row-scaled int8 pool of this block size and head_dim, or kind not key/value")
-    shape = (NB, H_kv, block_size, head_dim) if kind == "key" else (NB, H_kv, head_dim, block_size)
-    codes = pool[:, :, :nc].reshape(shape)
-    scales = pool[:, :, nc:nc + 4 * block_size].contiguous().view(_torch().float32)
-    return codes, scales
+def unpack_token_pools(key_pool, value_pool, block_size: int, head_dim: int):
+    """(key codes [NB, H_kv, bs, D], key scales [NB, H_kv, bs], value codes [NB, H_kv, D, bs],
+    value scales [NB, H_kv, bs]) of a pair of row-scaled int8 pools."""
+    NB, H_kv, tile = key_pool.shape
+    bs, D = block_size, head_dim
+    if tile != token_tile_bytes(bs, D) or tuple(value_pool.shape) != tuple(key_pool.shape):
+        raise ValueError("not a pair of row-scaled int8 pools of this block size and head_dim")
+    ko, vo, paired = token_scale_offsets(bs, D)
+    f32 = _torch().float32
+    kc = key_pool[:, :, :bs * D].reshape(NB, H_kv, bs, D)
+    vc = value_pool[:, :, :bs * D].reshape(NB, H_kv, D, bs)
+    ks = key_pool[:, :, ko:ko + 4 * bs].contiguous().view(f32)
+    vs = (key_pool if paired else value_pool)[:, :, vo:vo + 4 * bs].contiguous().view(f32)
+    return kc, ks, vc, vs
 
 
 def pa_copy_blocks(key_cache, value_cache, pairs, stream=None, num_pairs=None, head_dim=None):

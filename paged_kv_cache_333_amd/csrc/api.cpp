@@ -39,8 +39,7 @@ int elem_bytes(pa_dtype dt) { return dt == PA_F32 ? 4 : dt == PA_F16 || dt == PA
 bool is_code_type(pa_dtype dt) { return dt == PA_FP8_E4M3 || dt == PA_INT8 || dt == PA_INT8_TOKEN; }
 
 // Bytes of one (block, KV head) tile of a pool of element type dt: its
-// elements, then (PA_INT8_TOKEN) one fp32 scale per token row, padded to a
-// whole 128-byte line.
+// elements, then (PA_INT8_TOKEN) a scale area of whole 128-byte lines.
 int64_t tile_bytes(pa_dtype dt, int32_t head_dim, int32_t block_size) {
   return static_cast<int64_t>(block_size) * head_dim * elem_bytes(dt) +
          (dt == PA_INT8_TOKEN ? (static_cast<int64_t>(block_size) * 4 + 127) / 128 * 128 : 0);

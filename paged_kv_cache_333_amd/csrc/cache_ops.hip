@@ -270,10 +270,11 @@ __device__ __forceinline__ float element_at(TBF16, const char* p) {
 // saturating at +-127); a row of zeros gets s = 0 and codes 0.  Lane l holds
 // elements EL l .. EL l + EL - 1; the row's max comes from a butterfly of lane
 // exchanges.  The key codes go to the token's row of the key tile, the value
-// codes one byte each down column `offset` of the value tile, and the two
-// scales to byte BS * D + 4 offset of their tiles (each tile holds its codes,
-// then one fp32 scale per token row, padded to a 128-byte line).  Slots
-// outside the pool write nothing.
+// codes one byte each down column `offset` of the value tile, the key scale to
+// byte BS * D + 4 offset of the key tile, and the value scale to byte
+// BS * D + 4 BS + 4 offset of the key tile when the block's scales are paired
+// there (token_scales_paired), else to byte BS * D + 4 offset of the value
+// tile.  Slots outside the pool write nothing.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void reshape_and_cache_rows_kernel(WriteArgs a) {
   constexpr int EL = D / 64;
@@ -287,8 +288,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_rows_kernel(WriteArgs a
   if (slot < 0 || slot >= a.num_slots) return;
   const int64_t blk = slot / a.block_size;
   const int64_t off = slot - blk * a.block_size;
-  // bytes per tile: the codes, then the rows' scales padded to a whole 128-byte line
-  const int64_t tb = static_cast<int64_t>(a.block_size) * D + (a.block_size * 4 + 127) / 128 * 128;
+  // bytes per tile: the codes, then the scale area
+  const int64_t tb = static_cast<int64_t>(a.block_size) * D + token_scale_area(a.block_size);
   char* kt = a.key_cache + (blk * a.num_kv_heads + h) * tb;
   char* vt = a.value_cache + (blk * a.num_kv_heads + h) * tb;
   float xk[EL], xv[EL];
@@ -317,8 +318,10 @@ __global__ __launch_bounds__(256) void reshape_and_cache_rows_kernel(WriteArgs a
     reinterpret_cast<uint8_t*>(vt)[static_cast<int64_t>(d) * a.block_size + off] = static_cast<uint8_t>(cv);
   }
   if (lane == 0) {
-    *reinterpret_cast<float*>(kt + static_cast<int64_t>(a.block_size) * D + 4 * off) = sk;
-    *reinterpret_cast<float*>(vt + static_cast<int64_t>(a.block_size) * D + 4 * off) = sv;
+    const int64_t area = static_cast<int64_t>(a.block_size) * D;
+    *reinterpret_cast<float*>(kt + area + 4 * off) = sk;
+    char* vs = token_scales_paired(a.block_size) ? kt + area + 4 * a.block_size : vt + area;
+    *reinterpret_cast<float*>(vs + 4 * off) = sv;
   }
 }
 

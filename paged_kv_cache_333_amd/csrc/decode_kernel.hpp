@@ -45,10 +45,11 @@
 // the tile's furthest limit.
 //
 // int8 pools with a scale per (token, KV head) (storage type TI8T): each tile
-// holds its codes, then the fp32 scales of its bs token rows, padded to a
-// 128-byte line (an unpadded 16-row tile would leave half of all code rows
-// straddling two lines: back to back, the decode measured 117 instead of
-// 110 us).  With the
+// holds its codes, then a scale area of whole 128-byte lines (an unpadded
+// 16-row tile would leave half of all code rows straddling two lines: back to
+// back, the decode measured 117 instead of 110 us); with 16-token blocks the
+// key and value scales of a block share the key tile's one scale line
+// (device_common.hpp, TI8T).  With the
 // step's other loads, lane i loads the key scale and the value scale of the
 // step's token i; lane (q, n) takes those of its tokens 16 q + e from lane e
 // of its row (a DPP row broadcast), so the scales cost two registers in
@@ -223,9 +224,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   constexpr int NV = D / 16;         // value loads per step, 16 output dims each
   constexpr int PV = TPL / EPL;      // P.V products per 16 output dims (2 for 8-bit codes)
   constexpr int NBS = TS > BS ? TS / BS : 1;  // blocks touched by one step
-  // bytes of one (block, KV head) tile: its codes or elements, then (ROWS) its rows' scales,
-  // padded to a whole 128-byte line so every tile's rows stay line-aligned
-  constexpr int64_t KT = static_cast<int64_t>(BS) * D * SB + (ROWS ? (BS * 4 + 127) / 128 * 128 : 0);
+  // bytes of one (block, KV head) tile: its codes or elements, then (ROWS) the scale area
+  // (whole 128-byte lines, so every tile's rows stay line-aligned); PAIRED: the key tile's
+  // area holds the value scales too (TI8T)
+  constexpr int64_t KT = static_cast<int64_t>(BS) * D * SB + (ROWS ? token_scale_area(BS) : 0);
+  constexpr bool PAIRED = ROWS && token_scales_paired(BS);
   // P.V runs in TP: the query type, except over 8-bit pools, whose codes are
   // exact in fp16 (and P is in [0, 1]): fp16 there, one product per chunk
   // instead of bf16's high part + residual, and the cheaper fp16 widening.
@@ -513,7 +516,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       // streaming like the codes (plain loads that miss allocate L2 lines: measured 140 instead
       // of 108 us for the row-scaled LLaMA-7B-like decode after a cache flush)
       const float* kp1 = reinterpret_cast<const float*>(a.kc + sc);
-      const float* vp1 = reinterpret_cast<const float*>(a.vc + sc);
+      const float* vp1 = reinterpret_cast<const float*>(PAIRED ? a.kc + sc + 4 * BS : a.vc + sc);
       ks1 = CACHED ? *kp1 : __builtin_nontemporal_load(kp1);
       vs1 = CACHED ? *vp1 : __builtin_nontemporal_load(vp1);
     }

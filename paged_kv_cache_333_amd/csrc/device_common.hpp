@@ -35,11 +35,19 @@ struct TI8 {
   static constexpr int kEPL = 16;
 };
 // int8 codes with one fp32 scale per (token, KV head): each (block, KV head)
-// tile holds its bs * D codes, then the bs scales of its token rows.
+// tile holds its bs * D codes, then a scale area of whole 128-byte lines (so
+// every tile's code rows stay line-aligned).  When the key and value scales of
+// a block fit in one such area together (16-token blocks: 2 x 64 bytes in one
+// line), the key tile's area holds the key scales, then the value scales, and
+// the value tile's area is unused: a reader fetches one scale line per block
+// instead of two half-used ones.  Otherwise each tile's area holds the scales
+// of its own rows.
 struct TI8T {
   static constexpr int kBytes = 1;
   static constexpr int kEPL = 16;
 };
+__host__ __device__ constexpr int64_t token_scale_area(int bs) { return (static_cast<int64_t>(bs) * 4 + 127) / 128 * 128; }
+__host__ __device__ constexpr bool token_scales_paired(int bs) { return 8 * static_cast<int64_t>(bs) <= token_scale_area(bs); }
 template <typename S>
 struct row_scaled {
   static constexpr bool value = false;

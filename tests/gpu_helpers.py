@@ -86,14 +86,16 @@ def renumber_slots(used: np.ndarray, slots, block_size):
     return np.where(slots >= 0, blk.astype(np.int64) * block_size + slots % block_size, -1).astype(np.int32)
 
 
-def fetch_token_blocks(pool, used: np.ndarray, block_size: int, head_dim: int, kind: str):
-    """(codes, scales) host copies of the listed blocks of a row-scaled int8 pool."""
+def fetch_token_blocks(key_pool, value_pool, used: np.ndarray, block_size: int, head_dim: int):
+    """(key codes, key scales, value codes, value scales) host copies of the listed blocks of a
+    pair of row-scaled int8 pools."""
     import torch
 
     import paged_kv_cache_333_amd as pa
-    t = pool.index_select(0, torch.from_numpy(used).to(pool.device))
-    codes, scales = pa.unpack_token_pool(t, block_size, head_dim, kind)
-    return codes.cpu().numpy(), scales.cpu().numpy()
+    idx = torch.from_numpy(used).to(key_pool.device)
+    parts = pa.unpack_token_pools(key_pool.index_select(0, idx), value_pool.index_select(0, idx), block_size,
+                                  head_dim)
+    return tuple(t.cpu().numpy() for t in parts)
 
 
 def fetch_blocks(pool, used: np.ndarray, dtype: str, quant: bool):

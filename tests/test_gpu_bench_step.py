@@ -69,8 +69,8 @@ def test_bench_step_every_row(key):
 
     def fetch_pools():
         if rows:
-            return (fetch_token_blocks(b.kc, used, bs, w.head_dim, "key"),
-                    fetch_token_blocks(b.vc, used, bs, w.head_dim, "value"))
+            kc, ks, vc, vs = fetch_token_blocks(b.kc, b.vc, used, bs, w.head_dim)
+            return (kc, ks), (vc, vs)
         return fetch_blocks(b.kc, used, w.dtype, quant), fetch_blocks(b.vc, used, w.dtype, quant)
 
     kc0, vc0 = fetch_pools()

@@ -41,14 +41,12 @@ def pools_host(seed, NB, Hkv, bs, D, used=None):
 
 
 def to_device(kc, vc, ks, vs):
-    kd = pa.pack_token_pool(torch.from_numpy(kc).cuda(), torch.from_numpy(ks).cuda())
-    vd = pa.pack_token_pool(torch.from_numpy(vc).cuda(), torch.from_numpy(vs).cuda())
-    return kd, vd
+    return pa.pack_token_pools(torch.from_numpy(kc).cuda(), torch.from_numpy(ks).cuda(),
+                               torch.from_numpy(vc).cuda(), torch.from_numpy(vs).cuda())
 
 
 def from_device(kd, vd, bs, D):
-    kc, ks = (t.cpu().numpy() for t in pa.unpack_token_pool(kd, bs, D, "key"))
-    vc, vs = (t.cpu().numpy() for t in pa.unpack_token_pool(vd, bs, D, "value"))
+    kc, ks, vc, vs = (t.cpu().numpy() for t in pa.unpack_token_pools(kd, vd, bs, D))
     return kc, vc, ks, vs
 
 
@@ -151,8 +149,7 @@ def test_row_copy_and_swap_move_the_scales():
     out_pairs = np.array([[11, 0], [19, 5], [4, 7]], dtype=np.int32)
     pa.pa_swap_blocks(hk, hv, kd, vd, torch.from_numpy(out_pairs).cuda(), head_dim=D)
     torch.cuda.synchronize()
-    hkc, hks = (t.numpy() for t in pa.unpack_token_pool(hk, bs, D, "key"))
-    hvc, hvs = (t.numpy() for t in pa.unpack_token_pool(hv, bs, D, "value"))
+    hkc, hks, hvc, hvs = (t.numpy() for t in pa.unpack_token_pools(hk, hv, bs, D))
     wk, wv = OC.swap_blocks(np.zeros((NH, Hkv, bs, D), np.uint8), np.zeros((NH, Hkv, D, bs), np.uint8), gk, gv,
                             out_pairs)
     wks, wvs = OC.swap_blocks(np.zeros((NH, Hkv, bs), np.float32), np.zeros((NH, Hkv, bs), np.float32), gks, gvs,
