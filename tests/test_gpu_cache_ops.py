@@ -28,7 +28,9 @@ def test_reshape_and_cache_bit_exact(dtype, D, bs, Hkv):
     vc = synth.normal_host((NB, Hkv, D, bs), 2, dtype)
     key = synth.normal_host((T, Hkv, D), 3, dtype)
     val = synth.normal_host((T, Hkv, D), 4, dtype)
-    slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int32)
+    # distinct slots (two tokens on one slot race, by the call's definition); the pool's last
+    # slot is kept out of the draw and given to token 7
+    slots = rng.choice(NB * bs - 1, size=T, replace=False).astype(np.int32)
     slots[[0, 5, 36]] = -1               # padding tokens are skipped
     slots[7] = NB * bs - 1               # last slot of the pool
     ek, ev = C.reshape_and_cache(key, val, kc, vc, slots)
