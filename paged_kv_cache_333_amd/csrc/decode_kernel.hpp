@@ -130,9 +130,14 @@ struct DecodeParams {
   int32_t part_size;   // split only
   int32_t num_parts;   // split only
   // Split only, nonzero: a flat launch.  Wave item blockIdx.x * kWaves + wave
-  // is partition item % num_parts of unit item / num_parts (a unit is what
-  // blockIdx.x is otherwise: a (sequence, head group, query chunk)), so a
-  // partition count that kWaves does not divide leaves no wave idle.  Never
+  // below n_lead is partition item / units of unit item % units (units =
+  // n_lead / num_parts, the launch's (sequence, head group, query chunk)
+  // units, what blockIdx.x is otherwise), so a partition count that kWaves
+  // does not divide leaves no wave idle.  The items go partition by partition:
+  // with one resident round, the k-th workgroup a compute unit receives takes
+  // partition k, and the last (the shortest, and the youngest, which the
+  // memory system serves last) ends sooner than in unit order.  (With n_lead
+  // 0, item is partition item % num_parts of unit item / num_parts.)  Never
   // with the fused write.
   int32_t flat;
   // Flat launch of the shared-prefix decode, nonzero: wave items n_lead .. n_lead + n_own - 1
@@ -270,6 +275,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       if (a.n_lead > 0 && item >= a.n_lead) {
         own = true;
         unit = item - a.n_lead;
+      } else if (a.n_lead > 0) {
+        const int units = a.n_lead / a.num_parts;  // n_lead = units x num_parts
+        flat_part = item / units;
+        unit = item - flat_part * units;
       } else {
         unit = item / a.num_parts;
         flat_part = item - unit * a.num_parts;
