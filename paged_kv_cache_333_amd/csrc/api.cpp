@@ -852,20 +852,34 @@ static int32_t partition_of(int32_t max_context_len, int32_t parts) {
 // the longest context): the workspace is sized for it.
 static int32_t shared_partition_min(int32_t max_context_len) { return partition_of(max_context_len, 8); }
 
+// A piece of the longest context for P shared-prefix partitions: 15 % longer
+// than an even cut (then rounded up to 64 tokens), so the last partition is
+// the shortest.  The launch places partitions in order (partition-major: the
+// k-th workgroup a compute unit receives takes partition k), and the last
+// workgroup on a compute unit is served last.  On the parallel-sampling
+// workload (P = 3) pieces of 832 (even), 896, 960, 1024 and 1088 tokens gave
+// calls of 202.7, 200.6, 200.2, 202.8 and 207.0 us flushed.
+static int32_t shared_piece(int32_t max_context_len, int32_t parts) {
+  const int64_t piece = (static_cast<int64_t>(max_context_len) * 23 + 20 * parts - 1) / (20 * parts);
+  const int64_t p = (piece + 63) / 64 * 64;
+  return static_cast<int32_t>(p < 64 ? 64 : p);
+}
+
 // Partition of the shared prefixes.  Each prefix unit of the launch (a
-// group and head tile) cuts the longest context into P pieces, one wave
-// each, and the launch packs the waves four to a workgroup across units, so
-// no P leaves a wave idle.  P in 1..8 minimises the estimated time: the
-// rounds of resident workgroups the launch needs, times the tokens of one
-// wave plus 64 for its fixed costs.  On the parallel-sampling workload
-// (1024 units, 768 workgroups resident) that is P = 3, one round; the
-// earlier fixed P = 8 needed 2048 workgroups, and its third round ran two
-// thirds empty.  PA_SHARED_PARTS=1..8 overrides the rule (read on every call).
+// group and head tile) cuts the longest context into P pieces
+// (shared_piece), one wave each, and the launch packs the waves four to a
+// workgroup across units, so no P leaves a wave idle.  P in 1..8 minimises
+// the estimated time: the rounds of resident workgroups the launch needs,
+// times the tokens of one wave plus 64 for its fixed costs.  On the
+// parallel-sampling workload (1024 units, 768 workgroups resident) that is
+// P = 3, one round; the earlier fixed P = 8 needed 2048 workgroups, and its
+// third round ran two thirds empty.  PA_SHARED_PARTS=1..8 overrides the rule
+// (read on every call).  Every piece is at least shared_partition_min's.
 static int32_t shared_partition(const pa::DecodeArgs& a, int32_t num_groups, int32_t max_group_size) {
   const char* v = std::getenv("PA_SHARED_PARTS");
   if (v) {
     const int forced = std::atoi(v);
-    if (forced >= 1 && forced <= 8) return partition_of(a.max_context_len, forced);
+    if (forced >= 1 && forced <= 8) return shared_piece(a.max_context_len, forced);
   }
   pa::DecodeArgs g = a;
   g.num_seqs = num_groups;
@@ -877,7 +891,7 @@ static int32_t shared_partition(const pa::DecodeArgs& a, int32_t num_groups, int
   int32_t best = 8;
   int64_t best_cost = -1;
   for (int32_t parts = 1; parts <= 8; ++parts) {
-    const int64_t piece = partition_of(a.max_context_len, parts);
+    const int64_t piece = shared_piece(a.max_context_len, parts);
     const int64_t used = (static_cast<int64_t>(a.max_context_len) + piece - 1) / piece;  // pieces with tokens
     const int64_t workgroups = (units * used + 3) / 4;
     const int64_t rounds = (workgroups + resident - 1) / resident;
@@ -887,7 +901,7 @@ static int32_t shared_partition(const pa::DecodeArgs& a, int32_t num_groups, int
       best = parts;
     }
   }
-  return partition_of(a.max_context_len, best);
+  return shared_piece(a.max_context_len, best);
 }
 
 // Workspace of the shared-prefix decode: the prefix partials (sized for the
