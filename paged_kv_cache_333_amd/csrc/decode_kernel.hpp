@@ -879,7 +879,9 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(void* out, const float*
 // With an extra partial (x, the shared-prefix decode's own tokens), row (s, h)
 // merges its partitions and then (x.m, x.l, x.o)[s, h], as one more partition;
 // and x.expect[s] must equal ctx[s] (the prefix the partitions covered), else
-// the row is NaN.
+// the row is NaN.  Every slot a row can hold (num_parts of them, and the extra
+// partial) is loaded together with the row's length, which then only selects
+// among them: one round trip per row, not two.
 constexpr int kSmallParts = 16;
 template <typename T, int D>
 __global__ __launch_bounds__(256) void lse_merge_small_kernel(void* out, const float* __restrict__ ws_m,
@@ -900,14 +902,9 @@ __global__ __launch_bounds__(256) void lse_merge_small_kernel(void* out, const f
   const int s = order ? order[slot] : slot;
   if (static_cast<uint32_t>(s) >= static_cast<uint32_t>(num_seqs)) return;
   const int64_t sh = static_cast<int64_t>(s) * num_heads + h;
-  const int n = ctx[s];
-  const int np = n >= 0 && n <= len_limit ? (n + part_size - 1) / part_size : 0;
-  const int nt = np + (x.m ? 1 : 0);
-  if (n < 0 || n > len_limit || (x.expect && x.expect[s] != n) || nt > kSmallParts) {
-#pragma unroll
-    for (int i = 0; i < EL; ++i) store_elem(T{}, out, sh * D + EL * lane + i, __builtin_nanf(""));
-    return;
-  }
+  // the slots, loaded before the length is known (num_parts is uniform; a slot past the
+  // row's partitions is in the workspace and is left out of the sums below)
+  const int slots = min(num_parts, kSmallParts);
   float mv[kSmallParts], lv[kSmallParts], ov[kSmallParts][EL];
 #pragma unroll
   for (int p = 0; p < kSmallParts; ++p) {
@@ -915,31 +912,52 @@ __global__ __launch_bounds__(256) void lse_merge_small_kernel(void* out, const f
     lv[p] = 0.f;
 #pragma unroll
     for (int i = 0; i < EL; ++i) ov[p][i] = 0.f;
-    if (p < np) {
+    if (p < slots) {
       mv[p] = ws_m[sh * num_parts + p];
       lv[p] = ws_l[sh * num_parts + p];
 #pragma unroll
       for (int i = 0; i < EL; ++i) ov[p][i] = ws_o[(sh * num_parts + p) * D + EL * lane + i];
-    } else if (p == np && x.m) {
-      mv[p] = x.m[sh];
-      lv[p] = x.l[sh];
-#pragma unroll
-      for (int i = 0; i < EL; ++i) ov[p][i] = x.o[sh * D + EL * lane + i];
     }
   }
-  float M = kNegInf;
+  float xm = kNegInf, xl = 0.f, xo[EL];
 #pragma unroll
-  for (int p = 0; p < kSmallParts; ++p) M = fmaxf(M, mv[p]);
+  for (int i = 0; i < EL; ++i) xo[i] = 0.f;
+  if (x.m) {
+    xm = x.m[sh];
+    xl = x.l[sh];
+#pragma unroll
+    for (int i = 0; i < EL; ++i) xo[i] = x.o[sh * D + EL * lane + i];
+  }
+  const int n = ctx[s];
+  const int np = n >= 0 && n <= len_limit ? (n + part_size - 1) / part_size : 0;
+  const int nt = np + (x.m ? 1 : 0);
+  if (n < 0 || n > len_limit || (x.expect && x.expect[s] != n) || nt > kSmallParts || np > slots) {
+#pragma unroll
+    for (int i = 0; i < EL; ++i) store_elem(T{}, out, sh * D + EL * lane + i, __builtin_nanf(""));
+    return;
+  }
+  // partitions 0 .. np-1, then the extra partial
+  float M = xm;
+#pragma unroll
+  for (int p = 0; p < kSmallParts; ++p) M = p < np ? fmaxf(M, mv[p]) : M;
   float L = 0.f, A[EL];
 #pragma unroll
   for (int i = 0; i < EL; ++i) A[i] = 0.f;
 #pragma unroll
   for (int p = 0; p < kSmallParts; ++p) {
-    // a partition with no token (l = 0, m = -inf: all masked) has no weight
-    const float w = lv[p] == 0.f ? 0.f : lv[p] * fast_exp2((mv[p] - M) * kLog2e);
+    if (p < np) {  // (wave-uniform) a slot past the row's partitions may hold anything, NaN included
+      // a partition with no token (l = 0, m = -inf: all masked) has no weight
+      const float w = lv[p] == 0.f ? 0.f : lv[p] * fast_exp2((mv[p] - M) * kLog2e);
+      L += w;
+#pragma unroll
+      for (int i = 0; i < EL; ++i) A[i] = __builtin_fmaf(w, ov[p][i], A[i]);
+    }
+  }
+  {
+    const float w = xl == 0.f ? 0.f : xl * fast_exp2((xm - M) * kLog2e);
     L += w;
 #pragma unroll
-    for (int i = 0; i < EL; ++i) A[i] = __builtin_fmaf(w, ov[p][i], A[i]);
+    for (int i = 0; i < EL; ++i) A[i] = __builtin_fmaf(w, xo[i], A[i]);
   }
 #pragma unroll
   for (int i = 0; i < EL; ++i) store_elem(T{}, out, sh * D + EL * lane + i, L == 0.f ? 0.f : A[i] / L);

@@ -128,7 +128,7 @@ def test_split_merge_over_more_than_256_partitions(D):
 def test_lse_reduce_many_partitions_and_empty_ones(D):
     """The merge alone on 600-partition rows: the largest m in the first, the middle or the
     last round of loads; partitions with no token (l = 0, m = -inf) anywhere; a row with
-    no token at all gives zeros."""
+    no token at all gives zeros; slots past a row's partitions hold NaN."""
     S, H, ps = 5, 2, 16
     max_ctx = ps * 600
     ctx = [max_ctx, max_ctx, max_ctx - 5, ps * 300 + 1, max_ctx]
@@ -147,6 +147,11 @@ def test_lse_reduce_many_partitions_and_empty_ones(D):
     m[empty] = -np.inf
     o = rng.normal(size=(S, H, P, D))
     o[empty] = 0.0
+    for s, n in enumerate(ctx):  # slots past a row's partitions: the merge must leave them out
+        if 0 <= n <= max_ctx:
+            past = -(-n // ps)
+            m[s, :, past:] = l_[s, :, past:] = np.nan
+            o[s, :, past:] = np.nan
     buf = np.zeros(lay["total"] // 4, dtype=np.float32)
     buf[: S * H * P] = m.ravel()
     buf[lay["off_l"] // 4: lay["off_l"] // 4 + S * H * P] = l_.ravel()
@@ -172,7 +177,8 @@ def test_lse_reduce_few_partitions_empty_and_invalid_rows(D, dt):
     """The merge alone on rows of at most 16 partitions (the one-wave merge): partitions
     with no token (l = 0, m = -inf) first, in the middle and last; the largest m in any
     of them; a row whose partitions are all empty gives zeros; a row with no partition
-    (length 0) gives zeros; a length above the bound or below 0 gives NaN."""
+    (length 0) gives zeros; a length above the bound or below 0 gives NaN.  Slots past a
+    row's partitions hold NaN: the merge loads them early and must leave them out."""
     S, H, ps = 7, 3, 32
     max_ctx = ps * 12
     ctx = [max_ctx, max_ctx - 31, ps * 5 + 1, 1, max_ctx, 0, max_ctx + 1]
@@ -194,6 +200,11 @@ def test_lse_reduce_few_partitions_empty_and_invalid_rows(D, dt):
     m[empty] = -np.inf
     o = rng.normal(size=(S, H, P, D))
     o[empty] = 0.0
+    for s, n in enumerate(ctx):  # slots past a row's partitions: the merge must leave them out
+        if 0 <= n <= max_ctx:
+            past = -(-n // ps)
+            m[s, :, past:] = l_[s, :, past:] = np.nan
+            o[s, :, past:] = np.nan
     buf = np.zeros(lay["total"] // 4, dtype=np.float32)
     buf[: S * H * P] = m.ravel()
     buf[lay["off_l"] // 4: lay["off_l"] // 4 + S * H * P] = l_.ravel()
