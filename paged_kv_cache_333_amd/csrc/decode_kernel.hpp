@@ -539,10 +539,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
         vr[v] = V_CACHED ? load16(vp + v * 16 * BS * SB) : load16_stream(vp + v * 16 * BS * SB);
     }
     // (pa_decode_append) dims 16 v + n of the new token's value row, for the lanes whose
-    // tokens hold p
+    // tokens hold p; loaded with the step's other loads, except for fp32 (there they are
+    // loaded where they are put in, since holding them through the loads spills registers)
     typedef typename std::conditional<E == 4, uint32_t, uint16_t>::type word_t;
+    constexpr bool EARLY_FRESH = E != 4;
     word_t fv[APPEND ? NV : 1];
-    if constexpr (APPEND) {
+    if constexpr (APPEND && EARLY_FRESH) {
       if (has_fresh) {
         const word_t* nv = reinterpret_cast<const word_t*>(a.new_v) + fresh_row + n;
 #pragma unroll
@@ -642,6 +644,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     if constexpr (APPEND) {
       const int e = fresh_p - t0 - TPL * q;  // the lane's element holding p, if any
       if (has_fresh && e >= 0 && e < TPL) {
+        if constexpr (!EARLY_FRESH) {
+          const word_t* nv = reinterpret_cast<const word_t*>(a.new_v) + fresh_row + n;
+#pragma unroll
+          for (int v = 0; v < NV; ++v) fv[v] = nv[16 * v];
+        }
         const int wi = E == 4 ? e : e >> 1;
         const uint32_t sh = E == 4 ? 0u : static_cast<uint32_t>(e & 1) * 16u;
         const uint32_t hole = E == 4 ? 0u : ~(0xFFFFu << sh);
