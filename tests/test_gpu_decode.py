@@ -79,9 +79,10 @@ def oracle(c):
     return A.paged_decode(c["q"], c["kc"], c["vc"], c["tables"], c["ctx"], scale_for(c["D"]), c["dtype"])
 
 
-# shapes spanning every built kernel family: dtype x head_dim x block_size x group tile
+# shapes spanning every built kernel family: dtype x head_dim x block_size x group tile (groups of
+# 1, 2, 4, 8 and 16 heads per workgroup; group 32 as two tiles of 16, group 5 as five tiles of 1)
 FAMILIES = [(dt, D, bs, H, Hkv) for dt in ("f32", "f16", "bf16") for D in (64, 128) for bs in (16, 32)
-            for (H, Hkv) in ((4, 4), (8, 4), (16, 4), (16, 2), (6, 2))]
+            for (H, Hkv) in ((4, 4), (8, 4), (16, 4), (16, 2), (6, 2), (32, 2), (64, 2), (10, 2))]
 # 8- and 64-token blocks (head_dim 128): a step spans four blocks, or half a block
 FAMILIES += [(dt, 128, bs, H, Hkv) for dt in ("f32", "f16", "bf16") for bs in (8, 64)
              for (H, Hkv) in ((4, 4), (16, 4), (16, 2))]

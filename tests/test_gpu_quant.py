@@ -91,7 +91,7 @@ def oracle(c):
 
 
 FAMILIES = [(fmt, dt, D, bs, H, Hkv) for fmt in FMTS for dt in ("f16", "bf16") for D in (64, 128)
-            for bs in (16, 32) for (H, Hkv) in ((4, 4), (8, 4), (16, 4), (16, 2), (6, 2))]
+            for bs in (16, 32) for (H, Hkv) in ((4, 4), (8, 4), (16, 4), (16, 2), (6, 2), (32, 2))]
 FAMILIES += [(fmt, dt, 128, 64, H, Hkv) for fmt in FMTS for dt in ("f16", "bf16") for (H, Hkv) in ((4, 4), (16, 2))]
 
 

@@ -21,6 +21,10 @@ from tests.gpu_helpers import DeviceWorkload, assert_close, out_to_f64, scale_fo
 pytestmark = pytest.mark.gpu
 
 KINDS = [("f32", None), ("f16", None), ("bf16", None), ("f16", "fp8_e4m3"), ("bf16", "int8")]
+# (element type, 8-bit format, head_dim, block size); 8-bit pools take no 8-token blocks (the host
+# rejects them, tested on the CPU)
+POOL_CASES = [(dt, fmt, D, bs) for D, bs in [(64, 16), (128, 32), (128, 16), (128, 8), (128, 64)]
+              for dt, fmt in KINDS if not (fmt and bs == 8)]
 POISON_CODE = {"fp8_e4m3": 0x7F, "int8": 0x80}
 
 # (blocks shared by the family at block size 16, context length of each member in tokens)
@@ -112,12 +116,9 @@ def oracle(c):
     return A.paged_decode(c["q"], c["kc"], c["vc"], c["tables"], c["ctx"], scale_for(c["D"]), c["dt"], quant=quant)
 
 
-@pytest.mark.parametrize("dt,fmt", KINDS, ids=lambda v: str(v))
-@pytest.mark.parametrize("D,bs", [(64, 16), (128, 32), (128, 16), (128, 8), (128, 64)])
-@pytest.mark.parametrize("H,Hkv", [(4, 4), (8, 2), (16, 2)])
+@pytest.mark.parametrize("dt,fmt,D,bs", POOL_CASES, ids=lambda v: str(v))
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (8, 2), (16, 2), (32, 2)])
 def test_shared_prefix_families(dt, fmt, D, bs, H, Hkv):
-    if fmt and bs == 8:
-        pytest.skip("8-bit pools take no 8-token blocks (rejected on the host, tested on the CPU)")
     c = make_case(zlib.crc32(repr((dt, fmt, D, bs, H, Hkv)).encode()) % 10000, dt, fmt, H, Hkv, D, bs)
     groups = pa.pa_shared_prefix_groups(c["tables"].tolist(), c["ctx"], bs)
     assert groups[2] < c["S"] and groups[3] == 17      # the families were found

@@ -104,7 +104,7 @@ def test_row_write_bit_exact(dt, D, bs):
 
 
 FAMILIES = [(dt, D, bs, H, Hkv) for dt in ("f16", "bf16") for D in (64, 128) for bs in (16, 32)
-            for (H, Hkv) in ((4, 4), (8, 2), (16, 2))]
+            for (H, Hkv) in ((4, 4), (8, 2), (16, 2), (32, 2))]
 FAMILIES += [(dt, 128, 64, H, Hkv) for dt in ("f16", "bf16") for (H, Hkv) in ((4, 4), (16, 2))]
 
 
