@@ -13,8 +13,8 @@ import torch
 import paged_kv_cache_333_amd as pa
 import synth
 from oracle import attention as A
-from tests.gpu_helpers import (DeviceWorkload, assert_close, out_to_f64, renumber, renumber_slots, scale_for,
-                               used_blocks, fetch_blocks)
+from tests.gpu_helpers import (DeviceWorkload, assert_close, fp32_logit_term, out_to_f64, renumber, renumber_slots,
+                               scale_for, used_blocks, fetch_blocks)
 
 pytestmark = pytest.mark.gpu
 
@@ -376,6 +376,63 @@ def test_identical_keys_give_mean_of_v_and_ctx1_gives_v0():
             assert np.max(np.abs(got[s, h] - V.mean(axis=0))) <= 1e-5
             if n == 1:
                 assert np.array_equal(got[s, h], V[0])
+
+
+def _as_dtype(x, dt):
+    """float64 values rounded to the storage type dt (numpy storage array, bf16 as bits)."""
+    return synth.to_numpy(torch.from_numpy(np.asarray(x, dtype=np.float32)).to(TD[dt]), dt)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+def test_wide_logit_ranges_and_late_maxima(dt):
+    """Logits spanning about +-360 (softmax weights from 1 down to far below fp32's smallest
+    value): every key of a token is one constant a_t, every query element of a head one
+    constant b_h, so logit = scale * D * a_t * b_h.  Sequence 0 rises along the context (a
+    new running maximum at every step, each one rescaling what came before), sequence 1
+    falls (the maximum is the first token), sequence 2 is random with one spike in the
+    middle, sequence 3 holds one large constant (every weight equal: the mean of V).  Heads
+    take b = 8, -8, 2, 0.25, so the same keys rise for one head and fall for another."""
+    S, H, Hkv, D, bs = 4, 8, 2, 128, 16
+    ctx = (300, 300, 300, 131)
+    c = make_case(71, dt, S, H, Hkv, D, bs, ctx)
+    rng = np.random.default_rng(72)
+    a = [np.linspace(-4, 4, ctx[0]), np.linspace(4, -4, ctx[1]), rng.uniform(-4, 4, ctx[2]), np.full(ctx[3], 6.0)]
+    a[2][157] = 8.0
+    kc = c["kc"].copy()
+    for si in range(S):
+        for t in range(ctx[si]):
+            for g in range(Hkv):
+                kc[c["tables"][si, t // bs], g, t % bs, :] = _as_dtype(np.full(D, a[si][t] * (1 - 2 * g)), dt)
+    q = np.stack([np.stack([np.full(D, b) for b in (8.0, -8.0, 2.0, 0.25) * (H // 4)])] * S)
+    c["kc"], c["q"] = kc, _as_dtype(q, dt)
+    dv = to_dev(c)
+    ref = oracle(c)
+    extra = 0.0
+    if dt == "f32":  # 1e-5 is out of fp32's reach at these logits: add the term their rounding allows
+        qf = A.to_f64(c["q"], dt)
+        x2 = max(abs(b * a_t) for b in (8.0, 0.25) for arr in a for a_t in (arr.min(), arr.max()))
+        x2 *= D * scale_for(D) * np.log2(np.e)
+        extra = fp32_logit_term(x2, float(np.max(np.abs(A.to_f64(c["vc"], dt)))))
+        assert qf.max() == 8.0 and 1e-4 < extra < 5e-3
+    assert_close(run_decode(c, dv), ref, dt, "single", extra)
+    assert_close(run_decode(c, dv, split=64), ref, dt, "split", extra)
+    assert_close(run_decode(c, dv, split=16), ref, dt, "split, one block per partition", extra)
+
+
+def test_many_sequences_large_grid():
+    """8 192 short sequences (empty to 40 tokens) of 4 heads: 32 768 workgroups in the
+    single pass, every row against the oracle, in index order and longest first."""
+    S = 8192
+    rng = np.random.default_rng(73)
+    ctx = tuple(int(n) for n in rng.integers(0, 41, S))
+    c = make_case(74, "f16", S, 4, 4, 64, 16, ctx, extra_blocks=3)
+    dv = to_dev(c)
+    ref = oracle(c)
+    single = run_decode(c, dv)
+    assert_close(single, ref, "f16", "single")
+    order = pa.pa_order_longest_first(list(ctx))
+    assert np.array_equal(run_decode(c, dv, order=order), single)
+    assert_close(run_decode(c, dv, split=16), ref, "f16", "split")
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
