@@ -460,6 +460,10 @@ def test_invalid_device_indices_give_nan_rows_without_faulting():
     for split in (None, 32):
         got = run_decode(c2, dv2, split=split)
         assert np.all(np.isnan(got[1])) and not np.any(np.isnan(got[0]))
+    dv2["ctx"] = torch.tensor([-3, 20], dtype=torch.int32).cuda()       # a negative length
+    for split in (None, 32):
+        got = run_decode(c2, dv2, split=split)
+        assert np.all(np.isnan(got[0])) and not np.any(np.isnan(got[1]))
 
 
 def test_bad_launch_order_entries_do_not_fault():
