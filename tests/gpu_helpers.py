@@ -48,6 +48,24 @@ def fp32_logit_term(max_abs_logit2: float, max_abs_v: float) -> float:
     return math.log(2.0) * 2 * 4 * u * max_abs_logit2 * 2 * max_abs_v
 
 
+def max_abs_logit2(q, key_cache, tables, ctx, bs, dtype, scale) -> float:
+    """An upper bound of |base-2 logit| (scale * log2 e * q.k) over every query row of q
+    [rows, H, D] and every stored token of every sequence (all pairs, not only those a call
+    forms), from the host values of a model-type key pool [NB, H_kv, bs, D]."""
+    kv = A.to_f64(key_cache, dtype)
+    H, Hkv = q.shape[1], kv.shape[1]
+    qf = A.to_f64(q, dtype)
+    rows = [kv[tables[s, t // bs], :, t % bs, :] for s, n in enumerate(ctx) for t in range(n)]
+    if not rows or qf.size == 0:
+        return 0.0
+    K = np.stack(rows)                       # [tokens, H_kv, D]
+    best = 0.0
+    for h in range(H):
+        g = A.kv_head_of(h, H, Hkv)
+        best = max(best, float(np.max(np.abs(qf[:, h, :] @ K[:, g, :].T))))
+    return best * scale * math.log2(math.e)
+
+
 def log_parity(what: str, dtype: str, err: np.ndarray, tol: np.ndarray):
     path = os.environ.get("PA_PARITY_LOG")
     if not path or err.size == 0:

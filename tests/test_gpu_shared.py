@@ -16,7 +16,7 @@ import torch
 import paged_kv_cache_333_amd as pa
 import synth
 from oracle import attention as A
-from tests.gpu_helpers import DeviceWorkload, assert_close, out_to_f64, scale_for
+from tests.gpu_helpers import DeviceWorkload, assert_close, fp32_logit_term, max_abs_logit2, out_to_f64, scale_for
 
 pytestmark = pytest.mark.gpu
 
@@ -96,7 +96,7 @@ def dev(c):
                 ctx=torch.tensor(c["ctx"], dtype=torch.int32, device=d))
 
 
-def run_shared(c, dv, groups, cached=False):
+def run_shared(c, dv, groups, cached=False, scale=None):
     gs, pl, ng, mg = groups
     max_ctx = c["MB"] * c["bs"]
     ws = torch.empty(pa.pa_decode_shared_workspace_bytes(c["S"], c["H"], c["D"], max_ctx), dtype=torch.uint8,
@@ -105,8 +105,9 @@ def run_shared(c, dv, groups, cached=False):
     out = torch.full_like(dv["q"], 7.0)
     pa.pa_decode_shared(out, dv["q"], dv["kc"], dv["vc"], dv["tab"], dv["ctx"],
                         torch.tensor(gs, dtype=torch.int32, device="cuda"),
-                        torch.tensor(pl, dtype=torch.int32, device="cuda"), ng, mg, max_ctx, scale_for(c["D"]), ws,
-                        c["ks"], c["vs"], kv_format=c["fmt"], cached_kv=cached)
+                        torch.tensor(pl, dtype=torch.int32, device="cuda"), ng, mg, max_ctx,
+                        scale_for(c["D"]) if scale is None else scale, ws, c["ks"], c["vs"], kv_format=c["fmt"],
+                        cached_kv=cached)
     torch.cuda.synchronize()
     return out_to_f64(out, c["dt"])
 
@@ -230,3 +231,59 @@ def test_every_forced_partition_count(parts, dt, fmt, monkeypatch):
     assert c["ws"][-4 * S:].view(torch.int32).cpu().tolist() == list(groups[1])
     monkeypatch.delenv("PA_SHARED_PARTS")
     assert_close(run_shared(c, dv, groups), ref, dt, "automatic partition count")
+
+
+RANDOM_CASES, WIDE_CASES, WIDE_GAIN = 48, 16, 40.0
+
+
+def draw_families(case):
+    """A random shared-prefix case: pool format, head shape, 1-5 families of 1-19 members
+    sharing 0-29 leading blocks (counted at 16 tokens; make_case rescales them), members
+    ending before, inside or after the shared blocks, and a forced partition count 1-8 or
+    the automatic one (0)."""
+    rng = np.random.default_rng(8800 + case)
+    fmt = [None, None, "fp8_e4m3", "int8"][int(rng.integers(4))]
+    dt = ["f16", "bf16"][int(rng.integers(2))] if fmt else ["f32", "f16", "bf16"][int(rng.integers(3))]
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32] + ([64] if D == 128 else []) + ([8] if D == 128 and not fmt else [])))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    fams = []
+    for _ in range(int(rng.integers(1, 6))):
+        shared = int(rng.integers(0, 30))
+        lens = [int(rng.integers(max(0, 16 * shared - 24), 16 * shared + 120)) for _ in range(int(rng.integers(1, 20)))]
+        fams.append((shared, lens))
+    return dict(fmt=fmt, dt=dt, D=D, bs=bs, Hkv=Hkv, H=Hkv * G, fams=fams, parts=int(rng.integers(0, 9)))
+
+
+def run_family_case(case, gain, monkeypatch):
+    d = draw_families(case)
+    print(f"shared-prefix case {case} (scale x {gain}): {d}", flush=True)
+    c = make_case(8800 + case, d["dt"], d["fmt"], d["H"], d["Hkv"], d["D"], d["bs"], families=d["fams"])
+    groups = pa.pa_shared_prefix_groups(c["tables"].tolist(), c["ctx"], c["bs"])
+    scale = float(np.float32(scale_for(c["D"]) * gain))
+    quant = (c["fmt"], c["ks"], c["vs"]) if c["fmt"] else None
+    ref = A.paged_decode(c["q"], c["kc"], c["vc"], c["tables"], c["ctx"], scale, c["dt"], quant=quant)
+    if d["parts"]:
+        monkeypatch.setenv("PA_SHARED_PARTS", str(d["parts"]))
+    got = run_shared(c, dev(c), groups, scale=scale)
+    extra = 0.0
+    if c["dt"] == "f32" and gain != 1.0:
+        vals = A.to_f64(c["vc"], "f32")
+        extra = fp32_logit_term(max_abs_logit2(c["q"], c["kc"], c["tables"], c["ctx"], c["bs"], "f32", scale),
+                                float(np.max(np.abs(vals[np.isfinite(vals)]))))
+    assert_close(got, ref, c["dt"], f"shared-prefix case {case} x {gain}", extra)
+
+
+@pytest.mark.parametrize("case", range(RANDOM_CASES))
+def test_random_families_match_the_oracle(case, monkeypatch):
+    """Seeded random shared-prefix cases (draw_families), every row against the oracle."""
+    run_family_case(case, 1.0, monkeypatch)
+
+
+@pytest.mark.parametrize("case", range(WIDE_CASES))
+def test_random_families_with_wide_logits(case, monkeypatch):
+    """The first random cases again with the softmax scale 40 times larger: the prefix
+    partitions and the own tokens' partial then hold maxima hundreds apart, which the merge
+    must rescale without overflow or loss."""
+    run_family_case(case, WIDE_GAIN, monkeypatch)
