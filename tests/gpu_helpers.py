@@ -48,6 +48,17 @@ def fp32_logit_term(max_abs_logit2: float, max_abs_v: float) -> float:
     return math.log(2.0) * 2 * 4 * u * max_abs_logit2 * 2 * max_abs_v
 
 
+def output_rounding_term(ref: np.ndarray, dtype: str) -> np.ndarray:
+    """Half an ulp of the output type at |ref|: what rounding the exact result to that type
+    moves it by.  tolerance() includes it for bf16 outputs everywhere; fp16 and fp32 outputs
+    add it only in the wide-logit cases, whose outputs approach single value rows (|out| up
+    to 5, where the fp16 half-ulp is 1.95e-3, all but 5e-5 of the stated 2e-3)."""
+    if dtype == "bf16":
+        return np.zeros(np.shape(ref))
+    mag = np.maximum(np.abs(ref), 2.0 ** -14)
+    return 0.5 * np.exp2(np.floor(np.log2(mag)) - MANT[dtype])
+
+
 def max_abs_logit2(q, key_cache, tables, ctx, bs, dtype, scale) -> float:
     """An upper bound of |base-2 logit| (scale * log2 e * q.k) over every query row of q
     [rows, H, D] and every stored token of every sequence (all pairs, not only those a call

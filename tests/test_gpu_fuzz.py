@@ -12,8 +12,10 @@ number, so a failing case is reproduced by its id.
 
 The first 64 cases run a second time with the softmax scale 40 times larger: logits of
 tens to hundreds, so most weights underflow and the running maximum jumps between steps,
-partitions and masked spans.  fp32 outputs there add the error that rounding such logits
-to fp32 allows (gpu_helpers.fp32_logit_term, from the largest logit of the case)."""
+partitions and masked spans.  Their outputs approach single value rows, so fp16 and fp32
+outputs there add half an ulp of the output type at |ref| (gpu_helpers.output_rounding_term,
+included for bf16 everywhere), and fp32 outputs the error that rounding such logits to fp32
+allows (gpu_helpers.fp32_logit_term, from the largest logit of the case)."""
 import numpy as np
 import pytest
 import torch
@@ -21,7 +23,8 @@ import torch
 import paged_kv_cache_333_amd as pa
 import synth
 from oracle import attention as A
-from tests.gpu_helpers import assert_close, fp32_logit_term, max_abs_logit2, out_to_f64, scale_for
+from tests.gpu_helpers import (assert_close, fp32_logit_term, max_abs_logit2, out_to_f64, output_rounding_term,
+                               scale_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -150,7 +153,9 @@ def run_case(case, gain):
                 pa.pa_decode(out, qd, kc, vc, tab, lens, c["max_ctx"], scale)
     torch.cuda.synchronize()
     extra = 0.0
+    if gain != 1.0:
+        extra = output_rounding_term(ref, c["dt"])
     if c["dt"] == "f32" and gain != 1.0:
-        extra = fp32_logit_term(max_abs_logit2(q, c["kc"], c["tables"], c["ctx"], c["bs"], "f32", scale),
+        extra = extra + fp32_logit_term(max_abs_logit2(q, c["kc"], c["tables"], c["ctx"], c["bs"], "f32", scale),
                                 float(np.max(np.abs(A.to_f64(c["vc"], "f32")))))
     assert_close(out_to_f64(out, c["dt"]), ref, c["dt"], f"fuzz case {case} x {gain} ({c['path']})", extra)

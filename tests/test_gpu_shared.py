@@ -16,7 +16,8 @@ import torch
 import paged_kv_cache_333_amd as pa
 import synth
 from oracle import attention as A
-from tests.gpu_helpers import DeviceWorkload, assert_close, fp32_logit_term, max_abs_logit2, out_to_f64, scale_for
+from tests.gpu_helpers import (DeviceWorkload, assert_close, fp32_logit_term, max_abs_logit2, out_to_f64,
+                               output_rounding_term, scale_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -267,10 +268,10 @@ def run_family_case(case, gain, monkeypatch):
     if d["parts"]:
         monkeypatch.setenv("PA_SHARED_PARTS", str(d["parts"]))
     got = run_shared(c, dev(c), groups, scale=scale)
-    extra = 0.0
+    extra = 0.0 if gain == 1.0 else output_rounding_term(ref, c["dt"])
     if c["dt"] == "f32" and gain != 1.0:
         vals = A.to_f64(c["vc"], "f32")
-        extra = fp32_logit_term(max_abs_logit2(c["q"], c["kc"], c["tables"], c["ctx"], c["bs"], "f32", scale),
+        extra = extra + fp32_logit_term(max_abs_logit2(c["q"], c["kc"], c["tables"], c["ctx"], c["bs"], "f32", scale),
                                 float(np.max(np.abs(vals[np.isfinite(vals)]))))
     assert_close(got, ref, c["dt"], f"shared-prefix case {case} x {gain}", extra)
 

@@ -20,7 +20,7 @@ import paged_kv_cache_333_amd as pa
 import synth
 from oracle import attention as A
 from oracle import cache_ops as OC
-from tests.gpu_helpers import assert_close, out_to_f64, scale_for
+from tests.gpu_helpers import assert_close, out_to_f64, output_rounding_term, scale_for
 
 pytestmark = pytest.mark.gpu
 
@@ -222,3 +222,76 @@ def test_row_pools_are_refused_by_the_one_launch_write():
     with pytest.raises(pa.PAError) as e:
         pa.pa_upload_and_cache(dst, host, k, k, kd, vd, host[:2], kv_format=TOKEN)
     assert e.value.code == "PA_ERR_UNSUPPORTED"
+
+
+ROW_CASES = 48
+
+
+@pytest.mark.parametrize("case", range(ROW_CASES))
+def test_random_row_scaled_cases(case):
+    """Seeded random cases over row-scaled int8 pools: fp16/bf16 queries, head_dim, block
+    size 16-64, KV heads, head groups 1-16, 1-6 ragged contexts, a partition of 1-4 blocks,
+    and one of single pass, split, masked (single or split; a random hole or window per
+    sequence) or several causal query tokens (single or split); every fourth case with the
+    softmax scale 40 times larger (outputs then approach single value rows: fp16 outputs add half
+    an fp16 ulp at |ref|, as bf16 outputs do everywhere).  Against the oracle over the values the
+    rows stand for."""
+    rng = np.random.default_rng(9500 + case)
+    dt = ["f16", "bf16"][int(rng.integers(2))]
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32] + ([64] if D == 128 else [])))
+    Hkv = int(rng.choice([1, 2, 4]))
+    H = Hkv * int(rng.choice([1, 2, 3, 4, 8, 16]))
+    ctx = [[0, 1, bs - 1, bs, bs + 1, int(rng.integers(2, 12 * bs))][int(rng.integers(6))]
+           for _ in range(int(rng.integers(1, 7)))]
+    path = ["single", "split", "masked", "masked-split", "multi", "multi-split"][int(rng.integers(6))]
+    ps = bs * int(rng.integers(1, 5))
+    gain = 40.0 if case % 4 == 3 else 1.0
+    print(f"row-scaled case {case}: {dt} D={D} bs={bs} H={H}/{Hkv} ctx={ctx} {path} ps={ps} x{gain}", flush=True)
+    S = len(ctx)
+    tables, NB, MB, used = tables_for(9500 + case, ctx, bs)
+    kc, vc, ks, vs = pools_host(9600 + case, NB, Hkv, bs, D, used)
+    kd, vd = to_device(kc, vc, ks, vs)
+    tab, cl = torch.from_numpy(tables).cuda(), torch.tensor(ctx, dtype=torch.int32).cuda()
+    max_ctx = MB * bs
+    scale = float(np.float32(scale_for(D) * gain))
+    split = path.endswith("split")
+    quant = (TOKEN, ks, vs)
+    if path.startswith("multi"):
+        spans = [int(rng.integers(0, min(n, 9) + 1)) for n in ctx]
+        if sum(spans) == 0:
+            spans[int(np.argmax(ctx))] = min(1, max(ctx))
+    if path.startswith("multi") and sum(spans) > 0:
+        qst = np.concatenate([[0], np.cumsum(spans)]).astype(np.int32)
+        T = int(qst[-1])
+        q = synth.normal_host((T, H, D), 9700 + case, dt)
+        ref = A.paged_decode_multi(q, kc, vc, tables, ctx, qst, scale, dt, quant=quant)
+        qd = synth.to_torch(q, dt).cuda()
+        out = torch.full_like(qd, 7.0)
+        ws = torch.empty(pa.pa_decode_multi_workspace_bytes(T, H, D, max_ctx, ps), dtype=torch.uint8,
+                         device="cuda") if split else None
+        pa.pa_decode_multi(out, qd, kd, vd, tab, cl, torch.from_numpy(qst).cuda(), max(spans), max_ctx, scale,
+                           kv_format=TOKEN, partition_size=ps, workspace=ws, split=split)
+    else:
+        q = synth.normal_host((S, H, D), 9700 + case, dt)
+        qd = synth.to_torch(q, dt).cuda()
+        out = torch.full_like(qd, 7.0)
+        ws = torch.empty(pa.pa_decode_split_workspace_bytes(S, H, D, max_ctx, ps), dtype=torch.uint8,
+                         device="cuda") if split else None
+        if path.startswith("masked"):
+            lo, hi = [], []
+            for n in ctx:
+                a = int(rng.integers(0, n + 1))
+                lo.append(a)
+                hi.append(int(rng.integers(a, n + 1)))
+            ref = A.paged_decode(q, kc, vc, tables, ctx, scale, dt, quant=quant, masks=(lo, hi))
+            pa.pa_decode_masked(out, qd, kd, vd, tab, cl, torch.tensor(lo, dtype=torch.int32).cuda(),
+                                torch.tensor(hi, dtype=torch.int32).cuda(), max_ctx, scale, kv_format=TOKEN,
+                                partition_size=ps, workspace=ws, split=split)
+        else:
+            ref = A.paged_decode(q, kc, vc, tables, ctx, scale, dt, quant=quant)
+            pa.pa_decode_quant(out, qd, kd, vd, tab, cl, max_ctx, scale, 1.0, 1.0, kv_format=TOKEN,
+                               partition_size=ps, workspace=ws, split=split)
+    torch.cuda.synchronize()
+    extra = 0.0 if gain == 1.0 else output_rounding_term(ref, dt)
+    assert_close(out_to_f64(out, dt), ref, dt, f"row-scaled case {case} ({path}, x{gain})", extra)
