@@ -35,7 +35,8 @@
 //   * P.V: out^T tile C[m][d'] = sum_t P[m][t] V[t][d'], one product per 16
 //     output dims; P never leaves the registers that computed it.  For bf16,
 //     P is split into a bf16 high part and a bf16 residual (two products) so
-//     the weights keep ~16 significant bits; fp16 P keeps 11.
+//     the weights keep ~16 significant bits; fp16 P keeps 11, and over
+//     row-scaled pools an fp16 high part and residual (~22 bits).
 // Each KV element is loaded once per workgroup; the NC columns share it.
 //
 // Several query tokens per sequence (speculative verification): query token i
@@ -238,7 +239,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   // exact in fp16 (and P is in [0, 1]): fp16 there, one product per chunk
   // instead of bf16's high part + residual, and the cheaper fp16 widening.
   using TP = typename std::conditional<Q8, TF16, T>::type;
-  constexpr bool SPLIT_P = std::is_same<TP, TBF16>::value;
+  // Weights enter P.V as a high part plus a residual (two products) for bf16, whose 8
+  // bits would cost accuracy everywhere, and for row-scaled pools, whose weights carry
+  // each token's value scale: in one fp16 product even a token holding all the weight
+  // would be off by up to 2^-12 of its value.
+  constexpr bool SPLIT_P = std::is_same<TP, TBF16>::value || ROWS;
   constexpr float kNegInf = -__builtin_huge_valf();
   static_assert(NC >= 1 && NC <= 16 && (NC & (NC - 1)) == 0, "columns per tile");
   static_assert(Q8 ? T::kBytes == 2 : std::is_same<T, S>::value, "8-bit pools decode in fp16/bf16");
@@ -640,7 +645,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     // P in chunks of the compute type: chunk u holds tokens TPL q + EPL u ..
     u32x4 phi[PV], plo[PV];
 #pragma unroll
-    for (int u = 0; u < PV; ++u) pack_p(TP{}, p + EPL * u, phi[u], plo[u]);
+    for (int u = 0; u < PV; ++u) {
+      if constexpr (SPLIT_P)
+        pack_p_split(TP{}, p + EPL * u, phi[u], plo[u]);
+      else
+        pack_p(TP{}, p + EPL * u, phi[u], plo[u]);
+    }
     if constexpr (APPEND) {
       const int e = fresh_p - t0 - TPL * q;  // the lane's element holding p, if any
       if (has_fresh && e >= 0 && e < TPL) {

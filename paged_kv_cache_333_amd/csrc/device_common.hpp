@@ -147,6 +147,18 @@ __device__ __forceinline__ void pack_p(TBF16, const float* p, u32x4& hi, u32x4& 
   hi = __builtin_bit_cast(u32x4, h);
   lo = __builtin_bit_cast(u32x4, l);
 }
+// fp16 high part and fp16 residual of 8 weights (about 22 significant bits between them).
+__device__ __forceinline__ void pack_p_split(TF16, const float* p, u32x4& hi, u32x4& lo) {
+  f16x8 h, l;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = static_cast<_Float16>(p[e]);
+    l[e] = static_cast<_Float16>(p[e] - static_cast<float>(h[e]));
+  }
+  hi = __builtin_bit_cast(u32x4, h);
+  lo = __builtin_bit_cast(u32x4, l);
+}
+__device__ __forceinline__ void pack_p_split(TBF16, const float* p, u32x4& hi, u32x4& lo) { pack_p(TBF16{}, p, hi, lo); }
 
 // Low k bits set (k clamped to [0, 32]).
 __device__ __forceinline__ uint32_t low_bits(int k) { return k <= 0 ? 0u : k >= 32 ? ~0u : (1u << k) - 1u; }
