@@ -522,10 +522,12 @@ pa_status pa_decode_split_static(void* out, const void* query, const void* key_c
  *   would idle while a few workgroups walk long contexts) and max_context_len
  *   spans at least 4 partitions;
  *   otherwise the single pass (pa_decode).
- * Same arguments and error behaviour as pa_decode_split.  workspace may be
- * NULL, or smaller than pa_decode_split_workspace_bytes for this shape: then
- * the single pass runs.  *path (may be NULL) receives 0 for the single pass
- * and 1 for split.  Both paths agree within the stated tolerances. */
+ * Arguments as pa_decode_split; the errors are those of the path that runs.
+ * The split runs only when it can: with workspace NULL or smaller than
+ * pa_decode_split_workspace_bytes for this shape, or a partition_size that
+ * pa_decode_split refuses, the single pass runs.  *path (may be NULL)
+ * receives 0 for the single pass and 1 for split.  Both paths agree within
+ * the stated tolerances. */
 pa_status pa_decode_auto(void* out, const void* query, const void* key_cache, const void* value_cache,
                          const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_order,
                          int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -260,3 +260,72 @@ def test_set_launch_events_accepts_null_and_needs_no_device():
     """The measurement hook only stores the events for the next call on this thread."""
     assert pa.lib.pa_set_launch_events(None, None) == 0
     pa.pa_set_launch_events(None, None)
+
+
+def test_other_entry_points_validate_before_launch():
+    """Calls whose arguments are wrong return an error status before any device work
+    (no GPU here), and calls with nothing to do return PA_OK."""
+    L, path = pa.lib, C.c_int32(-7)
+    base = dict(out=16, q=16, kc=16, vc=16, tab=16, ctx=16, S=2, H=32, Hkv=32, D=128, bs=16, MB=4, NB=8,
+                maxlen=64, scale=0.1, dt=F, flags=0, ps=512)
+
+    def auto(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.pa_decode_auto(a["out"], a["q"], a["kc"], a["vc"], a["tab"], a["ctx"], None, a["S"], a["H"], a["Hkv"],
+                                a["D"], a["bs"], a["MB"], a["NB"], a["maxlen"], a["scale"], a["dt"], a["flags"],
+                                a["ps"], None, 0, C.byref(path), None)
+
+    def append(**kw):
+        a = dict(base, key=16, value=16, slots=16)
+        a.update(kw)
+        return L.pa_decode_append(a["out"], a["q"], a["key"], a["value"], a["slots"], a["kc"], a["vc"], a["tab"],
+                                  a["ctx"], None, a["S"], a["H"], a["Hkv"], a["D"], a["bs"], a["MB"], a["NB"],
+                                  a["maxlen"], a["scale"], a["dt"], a["flags"], a["ps"], None, 0, C.byref(path), None)
+
+    def static(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.pa_decode_split_static(a["out"], a["q"], a["kc"], a["vc"], a["tab"], a["ctx"], None, a["S"], a["H"],
+                                        a["Hkv"], a["D"], a["bs"], a["MB"], a["NB"], a["maxlen"], a["scale"], a["dt"],
+                                        a["flags"], a["ps"], None)
+
+    assert auto(D=96) == 5 and auto(q=0) == 1 and auto(flags=2) == 1 and auto(H=6, Hkv=4) == 1
+    assert auto(S=0, out=0, q=0) == 0
+    assert append(D=96) == 5 and append(key=0) == 1 and append(slots=0) == 1 and append(flags=2) == 1
+    assert append(dt=pa.PA_FP8_E4M3) == 5                      # the fused write stores model-type rows
+    assert append(S=0, out=0, q=0, key=0, value=0, slots=0) == 0
+    assert static(D=96) == 5 and static(ps=24) == 1
+    assert static(S=100000, maxlen=131072) == 7                # beyond the library's static workspace
+    assert static(S=0, out=0, q=0) == 0
+
+    def swap(**kw):
+        a = dict(dk=16, dv=16, sk=16, sv=16, pairs=16, n=2, ns=8, nd=8, Hkv=4, D=64, bs=16, dt=F)
+        a.update(kw)
+        return L.pa_swap_blocks(a["dk"], a["dv"], a["sk"], a["sv"], a["pairs"], a["n"], a["ns"], a["nd"], a["Hkv"],
+                                a["D"], a["bs"], a["dt"], None)
+
+    assert swap(D=96) == 5 and swap(dt=7) == 5 and swap(pairs=0) == 1 and swap(n=-1) == 1
+    assert swap(ns=0) == 1                                     # pools that are neither device nor pinned memory
+    assert swap(n=0, pairs=0) == 0
+
+    assert L.pa_upload(0, 16, 64, None) == 1
+    assert L.pa_upload(16, 16, 6, None) == 1                   # whole 4-byte words only
+    assert L.pa_upload(0, 0, 0, None) == 0
+
+    def upload_and_cache(**kw):
+        a = dict(dst=16, src=16, nb=64, key=16, value=16, kc=16, vc=16, slots=16, T=2, NB=8, Hkv=4, D=64, bs=16,
+                 dt=F, kv=F)
+        a.update(kw)
+        return L.pa_upload_and_cache(a["dst"], a["src"], a["nb"], a["key"], a["value"], a["kc"], a["vc"], a["slots"],
+                                     a["T"], a["NB"], a["Hkv"], a["D"], a["bs"], 1.0, 1.0, a["dt"], a["kv"], None)
+
+    assert upload_and_cache(D=96) == 5 and upload_and_cache(T=-1) == 1
+    assert upload_and_cache(kv=pa.PA_BF16) == 5                # kv_dtype neither dtype nor an 8-bit code type
+    assert upload_and_cache() == 1                             # src is not page-locked host memory
+
+    g, pl, ng, mg = (C.c_int32 * 4)(), (C.c_int32 * 3)(), C.c_int32(), C.c_int32()
+    assert L.pa_shared_prefix_groups(None, None, 3, 4, 16, g, pl, C.byref(ng), C.byref(mg)) == 1
+    for name in ("pa_decode_auto", "pa_decode_append", "pa_decode_split_static", "pa_swap_blocks", "pa_upload",
+                 "pa_upload_and_cache", "pa_shared_prefix_groups"):
+        assert name in header_functions()
