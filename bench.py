@@ -749,8 +749,9 @@ def main():
         summarize_profile(args.workload, args.summarize_profile, args.path)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path shards by "
-              "sequence or KV head with no exchange; this build runs on a single MI355X)", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the decode shards by "
+              "sequence or KV head with no exchange between GPUs, so one GPU's share is the measured unit)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

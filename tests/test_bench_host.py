@@ -31,3 +31,15 @@ def test_steps_that_fit_caps_at_the_steps_asked_for():
     assert bench.steps_that_fit(w.context_lens, w.block_size, w.num_blocks, w.query_len, 60) == 60
     assert bench.steps_that_fit([15], 16, 1, 1, 5) == 1  # one more token opens a second block
     assert bench.steps_that_fit([16], 16, 1, 1, 5) == 0
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    """bench.py measures one GPU: any other --gpus exits with status 2 and says why, before
+    touching the GPU."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=root, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and "--gpus 2" in r.stderr
