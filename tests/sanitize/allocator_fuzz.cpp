@@ -4,7 +4,7 @@
 // calls alike: unknown and duplicate ids, exhausted pools, out-of-range
 // blocks, undersized output buffers, clones, prefixes, swaps, windows, the
 // shared-prefix grouping and the launch order.  The sanitizers report memory
-// and undefined-behaviour errors; the driver itself checks that every block is
+// and undefined-behaviour errors; this program itself checks that every block is
 // either free or referenced and that no call returns an unknown status.
 #include <cstdint>
 #include <cstdio>
