@@ -329,3 +329,21 @@ def test_other_entry_points_validate_before_launch():
     for name in ("pa_decode_auto", "pa_decode_append", "pa_decode_split_static", "pa_swap_blocks", "pa_upload",
                  "pa_upload_and_cache", "pa_shared_prefix_groups"):
         assert name in header_functions()
+
+
+def test_import_fails_loudly_without_the_library(tmp_path):
+    """The binding has no fallback: a package without libpa.so refuses to import, naming the
+    missing file and how to build it."""
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.join(ROOT, "paged_kv_cache_333_amd")
+    dst = tmp_path / "paged_kv_cache_333_amd"
+    dst.mkdir()
+    for name in os.listdir(src):
+        if name.endswith(".py"):
+            shutil.copy(os.path.join(src, name), dst / name)
+    r = subprocess.run([sys.executable, "-c", "import paged_kv_cache_333_amd"], cwd=tmp_path, capture_output=True,
+                       text=True, env=dict(os.environ, PYTHONPATH=str(tmp_path)), timeout=120)
+    assert r.returncode != 0
+    assert "libpa.so is missing" in r.stderr and "build" in r.stderr
